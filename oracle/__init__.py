@@ -1,0 +1,151 @@
+"""CPU oracle for the speculative-decoding verification step (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``liboracle.so`` (built from
+``spec_oracle.c`` by :func:`build`) with ctypes and numpy; it shares no code
+with the HIP library.
+
+Every function is a plain fp64 restatement of the method; see the header of
+``spec_oracle.c`` for the passages followed, the readings taken and the error
+rules.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib: Optional[ctypes.CDLL] = None
+
+F32 = 0
+BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (fp64, IEEE semantics, OpenMP over batch rows)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wno-unknown-pragmas", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        L.oracle_verify_chain.argtypes = [P, I, P, P, P, I, I, I, D, I, P, P, P, P, P, P, P, P]
+        L.oracle_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P]
+        L.oracle_accept_rate.argtypes = [P, I, P, I, I, I, D, I, P]
+        L.oracle_target_dist.argtypes = [P, I, I, D, I, P]
+        L.oracle_draft_dist.argtypes = [P, I, D, I, P]
+        L.oracle_argmax_row.argtypes = [P, I, I]
+        L.oracle_set_variant.argtypes = [I]
+        for f in ("oracle_verify_chain", "oracle_verify_tree_greedy", "oracle_accept_rate",
+                  "oracle_target_dist", "oracle_draft_dist", "oracle_argmax_row",
+                  "oracle_max_threads"):
+            getattr(L, f).restype = I
+        L.oracle_set_variant.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def _logits_arr(logits: np.ndarray, dtype: int) -> np.ndarray:
+    want = np.uint16 if dtype == BF16 else np.float32
+    return np.ascontiguousarray(logits, dtype=want)
+
+
+def set_variant(v: int) -> None:
+    """Plant a deliberate mistake (tests of the pins only); 0 restores the method."""
+    lib().oracle_set_variant(int(v))
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
+
+
+def verify_chain(logits, dtype, draft_probs, draft_tokens, uniforms, temperature, top_k):
+    """Chain verification; returns a dict of numpy arrays (see spec_oracle.c)."""
+    z = _logits_arr(logits, dtype)
+    B, K1, V = z.shape
+    K = K1 - 1
+    q = np.ascontiguousarray(draft_probs, dtype=np.float32).reshape(B, K, V)
+    x = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, K)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, K + 1)
+    out = dict(tokens=np.empty((B, K + 1), np.int32), accept_len=np.empty(B, np.int32),
+               pk=np.empty((B, K)), qk=np.empty((B, K)), S=np.empty(B), py=np.empty(B),
+               m_test=np.empty((B, K)), m_draw=np.empty(B))
+    rc = lib().oracle_verify_chain(_p(z), dtype, _p(q), _p(x), _p(u), B, K, V, float(temperature),
+                                   int(top_k), _p(out["tokens"]), _p(out["accept_len"]),
+                                   _p(out["pk"]), _p(out["qk"]), _p(out["S"]), _p(out["py"]),
+                                   _p(out["m_test"]), _p(out["m_draw"]))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_chain rejected its arguments ({rc})")
+    return out
+
+
+def verify_tree_greedy(logits, dtype, node_tokens, parents):
+    z = _logits_arr(logits, dtype)
+    B, N, V = z.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    tok = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(B, N)
+    depth = np.zeros(N, dtype=np.int64)
+    for n in range(1, N):
+        depth[n] = depth[par[n]] + 1
+    D = int(depth.max())
+    out = dict(path=np.empty((B, D + 1), np.int32), tokens=np.empty((B, D + 1), np.int32),
+               accept_len=np.empty(B, np.int32))
+    rc = lib().oracle_verify_tree_greedy(_p(z), dtype, _p(tok), _p(par), B, N, V, _p(out["path"]),
+                                         _p(out["tokens"]), _p(out["accept_len"]))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree_greedy rejected its arguments ({rc})")
+    return out
+
+
+def accept_rate(logits, dtype, draft_probs, temperature, top_k):
+    z = _logits_arr(logits, dtype)
+    B, K1, V = z.shape
+    K = K1 - 1
+    q = np.ascontiguousarray(draft_probs, dtype=np.float32).reshape(B, K, V)
+    a = np.empty((B, K))
+    rc = lib().oracle_accept_rate(_p(z), dtype, _p(q), B, K, V, float(temperature), int(top_k), _p(a))
+    if rc != 0:
+        raise ValueError(f"oracle_accept_rate rejected its arguments ({rc})")
+    return a
+
+
+def target_dist(row, dtype, temperature, top_k):
+    """p' of one logit row (fp64, length V); None if the row is invalid."""
+    z = _logits_arr(row, dtype).reshape(-1)
+    p = np.empty(z.shape[0])
+    bad = lib().oracle_target_dist(_p(z), dtype, z.shape[0], float(temperature), int(top_k), _p(p))
+    return None if bad else p
+
+
+def draft_dist(row, temperature, top_k):
+    """q' of one row of draft probabilities (fp64); None if invalid."""
+    q = np.ascontiguousarray(row, dtype=np.float32).reshape(-1)
+    out = np.empty(q.shape[0])
+    bad = lib().oracle_draft_dist(_p(q), q.shape[0], float(temperature), int(top_k), _p(out))
+    return None if bad else out
+
+
+def argmax_row(row, dtype) -> int:
+    z = _logits_arr(row, dtype).reshape(-1)
+    return int(lib().oracle_argmax_row(_p(z), dtype, z.shape[0]))

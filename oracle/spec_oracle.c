@@ -1,0 +1,431 @@
+/*
+ * spec_oracle.c -- CPU oracle for the verification step of speculative decoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The product path (the HIP
+ * library and its Python binding) never calls it, and it shares no code,
+ * header, table or helper with that path.
+ *
+ * Everything is plain and slow on purpose: full-vocabulary fp64 arrays, a
+ * full sort for top-k, sequential index-ascending sums.  Each function states
+ * the passage it follows.  Sources (cited by page title and section):
+ *   [LEV]  "064 · 投机解码：小模型先起草，大模型怎样并行验收而不改变分布" (notes on
+ *          Leviathan, Kalman, Matias, ICML 2023): section 二 (a(x), r(x),
+ *          alpha = sum min(p,q) = 1 - TV, the two-token example, the note that
+ *          p and q carry the sampling transforms), section 三 (the per-position
+ *          loop: test, residual draw, bonus draw).
+ *   [EAG]  "投机解码与 EAGLE": section 二 (the exactness rule, the greedy
+ *          rule for temperature 0, E[tokens]); the EAGLE part (tree drafts,
+ *          longest accepted branch).
+ *   [E2]   "EAGLE-2: Faster Inference of Language Models with Dynamic Draft
+ *          Trees": section 2.1 (acceptance min(1, p/p_hat), residual
+ *          norm(max(0, p - p_hat)), discard the rest).
+ *   [P10]  "Việc giải mã giả định và EAGLE-3": step 2 (residual with the
+ *          zero-sum fallback to the target distribution).
+ *
+ * Notation: p = target, q = draft (as in [LEV] and [EAG]).
+ *
+ * Readings taken where the pages leave a step open (all listed with reasons
+ * in the design notes of the repository):
+ *   - strict "u < min(1, ratio)";
+ *   - test k consumes u[k]; the single final draw (residual or bonus)
+ *     consumes u[K];
+ *   - the final draw is an inverse CDF over token indices in ascending order:
+ *     y = min{ i : u*S < C_i }, C_i the inclusive prefix sum of r; if no i
+ *     qualifies (rounding) y is the largest i with r_i > 0;
+ *   - zero residual mass: draw from the target distribution ([P10]);
+ *   - q(x) = 0 for the drafted token: accept iff p(x) > 0;
+ *   - top-k keeps exactly k entries, ordered by value descending and index
+ *     ascending; temperature on a draft given as probabilities is
+ *     q^(1/T) renormalised over its own top-k;
+ *   - with T = 1 and no top-k the draft probabilities are used as given;
+ *   - greedy (T = 0) ties go to the lowest index; the tree's "longest path"
+ *     is the deepest accepted node, lowest node index on ties.
+ *
+ * Error rules (a batch row with an error gets accept_len = -1 and -1 tokens):
+ *   E1 a target row holds NaN, or (sampling mode) +inf or only -inf values;
+ *   E2 a draft / node token lies outside [0, V);
+ *   E3 a draft probability that is read is NaN, negative or +inf;
+ *   E4 transformed draft row with zero kept mass;
+ *   E5 a uniform outside [0, 1) (sampling mode).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Deliberate-mistake switch used only by the tests that show the pins bite:
+ * 0 = the method as stated; 1 = on rejection re-sample from p instead of the
+ * residual (the "naive" variant of [LEV] section 二); 2 = bonus token drawn
+ * from p_{K-1} instead of p_K; 3 = ratio written q/p instead of p/q. */
+static int g_variant = 0;
+void oracle_set_variant(int v) { g_variant = v; }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static double load_logit(const void* row, int dtype, int i) {
+    if (dtype == ORC_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t*)row)[i]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float*)row)[i];
+}
+
+/* Ordering used by top-k: larger value first, then smaller index. */
+typedef struct { double v; int i; } vi_t;
+static int cmp_desc_then_index(const void* a, const void* b) {
+    const vi_t* x = (const vi_t*)a;
+    const vi_t* y = (const vi_t*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->i > y->i) - (x->i < y->i);
+}
+
+static int topk_enabled(int top_k, int V) { return top_k > 0 && top_k < V; }
+
+/* Marks the top_k entries of vals (value desc, index asc) in keep[]. */
+static void mark_topk(const double* vals, int V, int top_k, unsigned char* keep) {
+    vi_t* tmp = (vi_t*)malloc(sizeof(vi_t) * (size_t)V);
+    for (int i = 0; i < V; ++i) { tmp[i].v = vals[i]; tmp[i].i = i; }
+    qsort(tmp, (size_t)V, sizeof(vi_t), cmp_desc_then_index);
+    memset(keep, 0, (size_t)V);
+    for (int t = 0; t < top_k; ++t) keep[tmp[t].i] = 1;
+    free(tmp);
+}
+
+/* Index of the largest value, lowest index among equals; -1 if a NaN is present.
+ * [EAG] section 二, greedy rule. */
+int oracle_argmax_row(const void* row, int dtype, int V) {
+    int best = 0;
+    double bv = load_logit(row, dtype, 0);
+    if (isnan(bv)) return -1;
+    for (int i = 1; i < V; ++i) {
+        double v = load_logit(row, dtype, i);
+        if (isnan(v)) return -1;
+        if (v > bv) { bv = v; best = i; }
+    }
+    return best;
+}
+
+int oracle_argmax_f32(const float* row, int V) { return oracle_argmax_row(row, ORC_F32, V); }
+
+/* Target distribution p' of one logit row under temperature T > 0 and top-k:
+ * x = z/T, keep set S (all, or the top_k of x), p'_i = exp(x_i - m) / sum_S exp(x_j - m)
+ * on S and 0 elsewhere ([LEV] section 二: p must already carry the temperature and
+ * truncation).  Returns 0, or 1 when the row is invalid (E1). */
+int oracle_target_dist(const void* row, int dtype, int V, double T, int top_k, double* p) {
+    if (V <= 0 || !(T > 0.0)) return 1;
+    double* x = (double*)malloc(sizeof(double) * (size_t)V);
+    unsigned char* keep = (unsigned char*)malloc((size_t)V);
+    int bad = 0;
+    double m = -INFINITY;
+    for (int i = 0; i < V; ++i) {
+        double z = load_logit(row, dtype, i);
+        if (isnan(z) || z == INFINITY) bad = 1;
+        x[i] = z / T;
+    }
+    if (!bad) {
+        if (topk_enabled(top_k, V)) mark_topk(x, V, top_k, keep);
+        else memset(keep, 1, (size_t)V);
+        for (int i = 0; i < V; ++i)
+            if (keep[i] && x[i] > m) m = x[i];
+        if (m == -INFINITY) bad = 1;
+    }
+    if (!bad) {
+        double Z = 0.0;
+        for (int i = 0; i < V; ++i) {
+            p[i] = keep[i] ? exp(x[i] - m) : 0.0;
+            Z += p[i];
+        }
+        for (int i = 0; i < V; ++i) p[i] /= Z;
+    }
+    free(x);
+    free(keep);
+    return bad;
+}
+
+/* Draft distribution q' of one row of draft probabilities.
+ * T == 1 and no top-k: q as given.  Otherwise w_i = q_i^(1/T), keep the top_k of w,
+ * q' = w / sum_kept w ([LEV] section 二; temperature applied to both p and q).
+ * Returns 0, or 1 when invalid (E3, E4). */
+int oracle_draft_dist(const float* q, int V, double T, int top_k, double* out) {
+    if (V <= 0 || !(T > 0.0)) return 1;
+    for (int i = 0; i < V; ++i) {
+        double v = (double)q[i];
+        if (isnan(v) || v < 0.0 || v == INFINITY) return 1;
+    }
+    if (T == 1.0 && !topk_enabled(top_k, V)) {
+        for (int i = 0; i < V; ++i) out[i] = (double)q[i];
+        return 0;
+    }
+    double* w = (double*)malloc(sizeof(double) * (size_t)V);
+    unsigned char* keep = (unsigned char*)malloc((size_t)V);
+    for (int i = 0; i < V; ++i) w[i] = (q[i] > 0.0f) ? pow((double)q[i], 1.0 / T) : 0.0;
+    if (topk_enabled(top_k, V)) mark_topk(w, V, top_k, keep);
+    else memset(keep, 1, (size_t)V);
+    double s = 0.0;
+    for (int i = 0; i < V; ++i) s += keep[i] ? w[i] : 0.0;
+    int bad = !(s > 0.0);
+    if (!bad)
+        for (int i = 0; i < V; ++i) out[i] = keep[i] ? w[i] / s : 0.0;
+    free(w);
+    free(keep);
+    return bad;
+}
+
+/* Inverse-CDF draw over r[0..V) with total S (index-ascending). */
+static int draw_index(const double* r, int V, double S, double u, double* margin) {
+    double t = u * S, c = 0.0, prev = 0.0;
+    for (int i = 0; i < V; ++i) {
+        prev = c;
+        c += r[i];
+        if (t < c) {
+            double a = t - prev, b = c - t;
+            *margin = (a < b ? a : b) / S;
+            return i;
+        }
+    }
+    for (int i = V - 1; i >= 0; --i)
+        if (r[i] > 0.0) { *margin = 0.0; return i; }
+    *margin = 0.0;
+    return V - 1;
+}
+
+static int u_ok(float u) { return u >= 0.0f && u < 1.0f; }
+static int q_ok(float v) { return !(isnan(v) || v < 0.0f || v == INFINITY); }
+
+/*
+ * Chain verification for B independent rows ([LEV] section 三; [EAG] section 二;
+ * [E2] section 2.1).  Layouts (row-major):
+ *   logits [B][K+1][V] (bf16 bits or f32), q [B][K][V] f32, x [B][K] i32, u [B][K+1] f32.
+ * Outputs: tokens [B][K+1] (-1 padded), accept_len [B] (-1 on error),
+ *   pk, qk [B][K]: p'_k(x_k), q'_k(x_k) for every k (NaN where undefined);
+ *   S [B]: mass of the final-draw distribution before normalising; py [B]: r_y/S;
+ *   m_test [B][K]: |u_k - min(1, ratio_k)| for tests performed (NaN otherwise);
+ *   m_draw [B]: distance of u*S to the nearest edge of the chosen cell, over S.
+ * Greedy mode (T == 0): argmax comparisons; pk = 1 if x_k is the argmax else 0,
+ * qk = NaN, S = py = 1, margins = +inf (the decisions are exact).
+ */
+int oracle_verify_chain(const void* logits, int dtype, const float* q, const int32_t* x,
+                        const float* u, int B, int K, int V, double T, int top_k,
+                        int32_t* tokens, int32_t* accept_len, double* pk, double* qk,
+                        double* S_out, double* py_out, double* m_test, double* m_draw) {
+    if (B <= 0 || K <= 0 || V <= 0 || !(T >= 0.0) || isinf(T)) return -1;
+    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    const int greedy = (T == 0.0);
+    const int transformed = !(T == 1.0 && !topk_enabled(top_k, V));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        const char* zb = (const char*)logits + (size_t)b * (K + 1) * V * esz;
+        const float* qb = q + (size_t)b * K * V;
+        const int32_t* xb = x + (size_t)b * K;
+        const float* ub = u + (size_t)b * (K + 1);
+        int32_t* tb = tokens + (size_t)b * (K + 1);
+        double *pkb = pk + (size_t)b * K, *qkb = qk + (size_t)b * K, *mtb = m_test + (size_t)b * K;
+        for (int k = 0; k <= K; ++k) tb[k] = -1;
+        for (int k = 0; k < K; ++k) { pkb[k] = NAN; qkb[k] = NAN; mtb[k] = NAN; }
+        S_out[b] = NAN; py_out[b] = NAN; m_draw[b] = NAN;
+        accept_len[b] = -1;
+        int err = 0;
+        for (int k = 0; k < K; ++k) if (xb[k] < 0 || xb[k] >= V) err = 1;   /* E2 */
+        if (greedy) {
+            int g[K + 1];
+            for (int k = 0; k <= K && !err; ++k) {
+                g[k] = oracle_argmax_row(zb + (size_t)k * V * esz, dtype, V);
+                if (g[k] < 0) err = 1;                                            /* E1 */
+            }
+            if (err) continue;
+            int j = K;
+            for (int k = 0; k < K; ++k) {
+                pkb[k] = (xb[k] == g[k]) ? 1.0 : 0.0;
+                mtb[k] = INFINITY;
+            }
+            for (int k = 0; k < K; ++k) if (xb[k] != g[k]) { j = k; break; }
+            for (int k = 0; k < j; ++k) tb[k] = xb[k];
+            tb[j] = g[j];
+            accept_len[b] = j;
+            S_out[b] = 1.0; py_out[b] = 1.0; m_draw[b] = INFINITY;
+            continue;
+        }
+        for (int k = 0; k <= K; ++k) if (!u_ok(ub[k])) err = 1;                  /* E5 */
+        if (err) continue;
+        double* p = (double*)malloc(sizeof(double) * (size_t)(K + 1) * V);
+        double* qq = (double*)malloc(sizeof(double) * (size_t)V * (transformed ? K : 1));
+        double* r = (double*)malloc(sizeof(double) * (size_t)V);
+        for (int k = 0; k <= K && !err; ++k)
+            if (oracle_target_dist(zb + (size_t)k * V * esz, dtype, V, T, top_k, p + (size_t)k * V))
+                err = 1;                                                           /* E1 */
+        if (transformed)
+            for (int k = 0; k < K && !err; ++k)
+                if (oracle_draft_dist(qb + (size_t)k * V, V, T, top_k, qq + (size_t)k * V))
+                    err = 1;                                                       /* E3, E4 */
+        if (!transformed)
+            for (int k = 0; k < K; ++k) if (!q_ok(qb[(size_t)k * V + xb[k]])) err = 1;   /* E3 */
+        if (!err) {
+            for (int k = 0; k < K; ++k) {
+                pkb[k] = p[(size_t)k * V + xb[k]];
+                qkb[k] = transformed ? qq[(size_t)k * V + xb[k]] : (double)qb[(size_t)k * V + xb[k]];
+            }
+            /* Ratio tests left to right, stop at the first rejection. */
+            int j = K;
+            for (int k = 0; k < K; ++k) {
+                double a = pkb[k], c = qkb[k], ratio;
+                if (g_variant == 3) { double t = a; a = c; c = t; }
+                if (c > 0.0) ratio = a / c;
+                else ratio = a > 0.0 ? INFINITY : 0.0;
+                double thr = ratio < 1.0 ? ratio : 1.0;
+                mtb[k] = fabs((double)ub[k] - thr);
+                if (!((double)ub[k] < thr)) { j = k; break; }
+            }
+            /* Final draw with u[K]: residual at the rejected position, else bonus. */
+            const double* pj = p + (size_t)j * V;
+            double S = 0.0;
+            if (j < K && g_variant != 1) {
+                const float* qrow = qb + (size_t)j * V;
+                if (!transformed)
+                    for (int i = 0; i < V; ++i) if (!q_ok(qrow[i])) err = 1;      /* E3 */
+                for (int i = 0; i < V && !err; ++i) {
+                    double qi = transformed ? qq[(size_t)j * V + i] : (double)qrow[i];
+                    double d = pj[i] - qi;
+                    r[i] = d > 0.0 ? d : 0.0;
+                    S += r[i];
+                }
+                if (!err && !(S > 0.0)) {                                         /* [P10] */
+                    S = 0.0;
+                    for (int i = 0; i < V; ++i) { r[i] = pj[i]; S += r[i]; }
+                }
+            } else {
+                const double* src = (j == K && g_variant == 2) ? p + (size_t)(K - 1) * V : pj;
+                for (int i = 0; i < V; ++i) { r[i] = src[i]; S += r[i]; }
+            }
+            if (!err) {
+                double md;
+                int y = draw_index(r, V, S, (double)ub[K], &md);
+                for (int k = 0; k < j; ++k) tb[k] = xb[k];
+                tb[j] = y;
+                accept_len[b] = j;
+                S_out[b] = S;
+                py_out[b] = r[y] / S;
+                m_draw[b] = md;
+            } else {
+                for (int k = 0; k < K; ++k) { pkb[k] = NAN; qkb[k] = NAN; mtb[k] = NAN; }
+            }
+        }
+        free(p);
+        free(qq);
+        free(r);
+    }
+    return 0;
+}
+
+/*
+ * Greedy verification of a static draft tree ([EAG] greedy rule and tree drafts;
+ * [E2] section 2.2 verification stage).  logits [B][N][V]: row n is the target's
+ * distribution after the path to node n; node_tokens [B][N] (entry 0 ignored);
+ * parents [N] with parents[0] = -1 and 0 <= parents[i] < i.  Node n (n > 0) is
+ * accepted iff its parent is accepted and its token equals the argmax of the
+ * parent's row.  The chosen node is the deepest accepted node (lowest index on
+ * ties); the output is its path and the bonus argmax of its own row.
+ * out_path, out_tokens [B][D+1] (-1 padded), accept_len [B] = depth (-1 on error).
+ */
+int oracle_verify_tree_greedy(const void* logits, int dtype, const int32_t* node_tokens,
+                              const int32_t* parents, int B, int N, int V,
+                              int32_t* out_path, int32_t* out_tokens, int32_t* accept_len) {
+    if (B <= 0 || N <= 0 || V <= 0 || parents[0] != -1) return -1;
+    int D = 0;
+    int* depth = (int*)malloc(sizeof(int) * (size_t)N);
+    depth[0] = 0;
+    for (int n = 1; n < N; ++n) {
+        if (parents[n] < 0 || parents[n] >= n) { free(depth); return -1; }
+        depth[n] = depth[parents[n]] + 1;
+        if (depth[n] > D) D = depth[n];
+    }
+    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        const char* zb = (const char*)logits + (size_t)b * N * V * esz;
+        const int32_t* tk = node_tokens + (size_t)b * N;
+        int32_t* op = out_path + (size_t)b * (D + 1);
+        int32_t* ot = out_tokens + (size_t)b * (D + 1);
+        for (int d = 0; d <= D; ++d) { op[d] = -1; ot[d] = -1; }
+        accept_len[b] = -1;
+        int* g = (int*)malloc(sizeof(int) * (size_t)N);
+        unsigned char* acc = (unsigned char*)malloc((size_t)N);
+        int err = 0;
+        for (int n = 1; n < N; ++n) if (tk[n] < 0 || tk[n] >= V) err = 1;        /* E2 */
+        for (int n = 0; n < N && !err; ++n) {
+            g[n] = oracle_argmax_row(zb + (size_t)n * V * esz, dtype, V);
+            if (g[n] < 0) err = 1;                                                 /* E1 */
+        }
+        if (!err) {
+            int best = 0;
+            acc[0] = 1;
+            for (int n = 1; n < N; ++n) {
+                acc[n] = acc[parents[n]] && tk[n] == g[parents[n]];
+                if (acc[n] && depth[n] > depth[best]) best = n;
+            }
+            int d = depth[best];
+            for (int n = best, t = d; t >= 0; n = parents[n], --t) op[t] = n;
+            for (int t = 1; t <= d; ++t) ot[t - 1] = tk[op[t]];
+            ot[d] = g[best];
+            accept_len[b] = d;
+        }
+        free(g);
+        free(acc);
+    }
+    free(depth);
+    return 0;
+}
+
+/*
+ * Acceptance rate alpha[b][k] = sum_i min(p'_k(i), q'_k(i)) for k < K ([LEV]
+ * section 二: the overlap mass of the two transformed distributions).
+ * Greedy (T == 0): 1 if the argmax of the target row equals the argmax of the
+ * draft row, else 0.  NaN for an invalid row.
+ */
+int oracle_accept_rate(const void* logits, int dtype, const float* q, int B, int K, int V,
+                       double T, int top_k, double* alpha) {
+    if (B <= 0 || K <= 0 || V <= 0 || !(T >= 0.0) || isinf(T)) return -1;
+    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int b = 0; b < B; ++b) {
+        for (int k = 0; k < K; ++k) {
+            const char* zrow = (const char*)logits + ((size_t)b * (K + 1) + k) * V * esz;
+            const float* qrow = q + ((size_t)b * K + k) * V;
+            double* out = alpha + (size_t)b * K + k;
+            if (T == 0.0) {
+                int gp = oracle_argmax_row(zrow, dtype, V);
+                int gq = oracle_argmax_f32(qrow, V);
+                *out = (gp < 0 || gq < 0) ? NAN : (gp == gq ? 1.0 : 0.0);
+                continue;
+            }
+            double* p = (double*)malloc(sizeof(double) * (size_t)V);
+            double* qq = (double*)malloc(sizeof(double) * (size_t)V);
+            if (oracle_target_dist(zrow, dtype, V, T, top_k, p) ||
+                oracle_draft_dist(qrow, V, T, top_k, qq)) {
+                *out = NAN;
+            } else {
+                double s = 0.0;
+                for (int i = 0; i < V; ++i) s += p[i] < qq[i] ? p[i] : qq[i];
+                *out = s;
+            }
+            free(p);
+            free(qq);
+        }
+    }
+    return 0;
+}
