@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verification step on one MI355X.
+
+A step is one spec_verify_chain call over one batch of synthetic inputs that
+already sit in HBM.  The default workload is the chain verification with
+B=64, K=7, V=128256 (bf16 target logits, fp32 draft probabilities,
+temperature 0.7, top-k 50 on both distributions).  Several copies of the
+inputs are rotated so that the working set exceeds the 256 MB Infinity Cache.
+
+Prints ONE JSON line: verified token-rows/s (B*(K+1) per step), the step
+time, the dominant kernel's achieved HBM bandwidth against the 8 TB/s peak
+(timed live with HIP events around that kernel on the call's stream), the
+hardware-counter traffic recorded under profiles/ when it matches the current
+kernel source, and the CPU oracle's throughput on the host cores.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2|4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBS = 8000.0
+METRIC = "verified token-rows/s and achieved HBM GB/s (% of peak), V=128256, B=64, K=7"
+
+WORKLOADS = {
+    2: dict(name="chain verify B=64 K=7 V=128256, bf16 target logits, fp32 draft probs, T=0.7, top_k=50",
+            kernel="topk_chunk_kernel", copies=4, oracle_rows=64),
+    4: dict(name="chain verify B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
+            kernel="rowstats_kernel", copies=1, oracle_rows=32),
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("common.hpp", "internal.hpp", "topk.hip", "rowstats.hip", "verify.hip", "api.hip"):
+        with open(os.path.join(ROOT, "rejection_sampling_verify_10_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when the summary is absent or was taken on another kernel source."""
+    path = os.path.join(ROOT, "profiles", f"counters_workload{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b) or m_sha.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int) -> float:
+    """Bytes the dominant kernel must move per launch (see the design notes)."""
+    if workload == 2:
+        # every target row (bf16) and every draft row (fp32) once; per chunk a sorted list
+        # of top_k (value, index) pairs plus count and flags written
+        chunks = B * (K + 1) * 4 + B * K * 8
+        return B * (K + 1) * V * 2 + B * K * V * 4 + chunks * (top_k * 8 + 8)
+    # row statistics: every target row once, 24 bytes of statistics per row written
+    return B * (K + 1) * V * 2 + B * (K + 1) * 24
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the verification step shards over the batch with no "
+              "exchange, so there is no multi-GPU path to time (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_10_amd as R
+    from rejection_sampling_verify_10_amd import workloads as W
+
+    wl = WORKLOADS[args.workload]
+    R.lib()                                   # fails loudly without the HIP library
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    ci = W.config(args.workload, seed=args.seed)
+    B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
+    log(f"workload {args.workload}: {wl['name']} (inputs drawn in {time.time() - t0:.1f} s)")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    base = [to_dev(ci.logits), to_dev(ci.draft_probs), to_dev(ci.draft_tokens), to_dev(ci.uniforms)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(wl["copies"] - 1)]
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = torch.empty(R.chain_workspace_bytes(B, K, V, ci.dtype, T, top_k) + 256, dtype=torch.uint8, device=dev)
+    in_bytes = sum(t.numel() * t.element_size() for t in base)
+    log(f"{wl['copies']} input copies x {in_bytes / 1e6:.1f} MB resident")
+
+    def step(i: int) -> None:
+        z, q, x, u = sets[i % len(sets)]
+        R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Events around the dominant kernel of every timed step (recorded by the library on
+    # the call's stream), and around the whole timed region.
+    kstart = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    kstop = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in kstart + kstop:
+        e.record()
+    torch.cuda.synchronize()
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for i in range(args.steps):
+        R.profile_next_call(kstart[i], kstop[i])
+        step(args.warmup + i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_begin.elapsed_time(t_end) / args.steps
+    k_ms = sum(a.elapsed_time(b) for a, b in zip(kstart, kstop)) / args.steps
+    value = B * (K + 1) / (ms_step * 1e-3)
+    alg = algorithmic_bytes(args.workload, B, K, V, top_k)
+    achieved = alg / (k_ms * 1e-3) / 1e9
+    step_alg_gbs = (alg if args.workload == 2 else alg) / (ms_step * 1e-3) / 1e9
+    al = alen.cpu().numpy()
+    log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
+        f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak); accept_len histogram {np.bincount(al, minlength=K + 1).tolist()}")
+    traffic = counter_traffic(args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = min(wl["oracle_rows"], B)
+        t0 = time.perf_counter()
+        oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
+                            ci.uniforms[:rows], T, top_k)
+        dt = time.perf_counter() - t0
+        cpu = {"value": rows * (K + 1) / dt, "unit": "token-rows/s", "cores": oracle.max_threads(),
+               "kind": "oracle",
+               "sample": f"first {rows} of {B} batch rows ({rows * (K + 1)} token-rows) of the same workload, "
+                         f"fp64 C oracle, OpenMP over batch rows, {dt:.2f} s wall"}
+        log(f"oracle: {cpu['value']:.0f} token-rows/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "token-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16/f32 in, f32 select, f64 probabilities" if args.workload == 2 else "bf16 in, f32 exp, f64 draw",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
+                   "input_copies": wl["copies"], "parallelism": "single GPU"},
+        "step_algorithmic_GBps": step_alg_gbs,
+        "roofline": {"bound": "hbm", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

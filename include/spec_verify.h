@@ -1,0 +1,177 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) library for the verification
+ * step of speculative decoding.
+ *
+ * The method (p = target, q = draft):
+ *   - "投机解码与 EAGLE", section 二 (exactness rule; temperature-0 greedy rule);
+ *   - "064 · 投机解码：小模型先起草，大模型怎样并行验收而不改变分布",
+ *     section 二 (acceptance a(x) = min(1, p(x)/q(x)); residual
+ *     r(x) = max(0, p(x) - q(x)) / sum max(0, p - q); p and q must carry the
+ *     temperature / top-k transforms; acceptance rate alpha = sum min(p, q)),
+ *     section 三 (the per-position loop: test, stop at the first rejection
+ *     and draw from the residual, or draw a bonus token from p_{K+1});
+ *   - "EAGLE-2: Faster Inference of Language Models with Dynamic Draft
+ *     Trees", section 2.1 (same rule), section 2.2 (tree drafts verified in one
+ *     pass; the longest accepted branch wins).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments except `parents_host` are DEVICE pointers, row-major
+ *     and contiguous.  Every buffer is owned by the caller; the library
+ *     allocates nothing, keeps no pointer after returning and holds no global
+ *     mutable state (calls on different streams may run concurrently as long as
+ *     they use different workspaces).
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.  Inputs must stay valid and
+ *     outputs must not be read until the stream has reached the call.
+ *   - `workspace` is device scratch of at least the size reported by the
+ *     matching *_workspace_bytes function, 256-byte aligned; it is used only
+ *     during the call's kernels (no state is carried between calls).
+ *   - Logit rows are bfloat16 (SPEC_BF16, raw bits) or float32 (SPEC_F32).
+ *     Draft probabilities are float32.  Uniforms are float32 in [0, 1).
+ *   - Host-detectable argument errors return a negative code and launch
+ *     nothing.  Bad DATA never aborts a call: the affected batch row gets
+ *     accept_len = -1 and all its output tokens (and path entries) = -1,
+ *     under these rules:
+ *       E1 a target row that is read contains NaN, or (sampling mode) +inf, or
+ *          only -inf values;
+ *       E2 a draft / node token outside [0, V);
+ *       E3 a draft probability that is read is NaN, negative or +inf (with
+ *          T = 1 and no top-k only q[x_k] and, after a rejection at j, row j
+ *          are read; otherwise all K draft rows are read);
+ *       E4 a transformed draft row keeps zero mass;
+ *       E5 a uniform outside [0, 1) (sampling mode).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+
+enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = -1,        /* bad sizes, pointers, dtype, temperature, parents */
+    SPEC_EWORKSPACE = -2,    /* workspace missing, misaligned or too small */
+    SPEC_ELAUNCH = -3,       /* a kernel launch failed (hipGetLastError) */
+    SPEC_EUNSUPPORTED = -4   /* valid request outside this build's limits */
+};
+
+/* Limits of this build: K <= SPEC_MAX_K draft positions, N <= SPEC_MAX_NODES
+ * tree nodes, top_k <= SPEC_TOPK_MAX when top-k is active, V < 2^24 and V <=
+ * SPEC_MAX_V. */
+#define SPEC_MAX_K 63
+#define SPEC_MAX_NODES 64
+#define SPEC_TOPK_MAX 64
+#define SPEC_MAX_V (1 << 20)
+
+/* Human-readable text for a return code (static storage). */
+const char* spec_error_string(int code);
+
+/* Workspace sizes (bytes) for the calls below with the same arguments; 0 if the
+ * arguments are invalid.  Sizes depend only on the arguments. */
+size_t spec_chain_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k);
+size_t spec_tree_workspace_bytes(int B, int N, int V, spec_dtype_t dtype);
+size_t spec_accept_rate_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k);
+
+/*
+ * spec_verify_chain -- batched verification of B drafted chains of K tokens.
+ *
+ * For each batch row b (independently):
+ *   p'_k = softmax(z_k / T) over the top_k largest logits of row k (all V when
+ *          top-k is off), zero elsewhere; k = 0..K.
+ *   q'_k = q_k as given when T == 1 and top-k is off; otherwise q_k^(1/T)
+ *          renormalised over the top_k largest entries of q_k.
+ *   Test k = 0, 1, ...: accept x_k iff u_k < min(1, p'_k(x_k) / q'_k(x_k))
+ *   (q'_k(x_k) = 0: accept iff p'_k(x_k) > 0); stop at the first rejection j.
+ *   Final draw with u_K: at j < K from r = max(0, p'_j - q'_j) (if r has zero
+ *   mass, from p'_j), at j = K from p'_K; the token is the smallest index i
+ *   with u_K * S < C_i (C the inclusive prefix sum of r in index order, S its
+ *   total).
+ *   Top-k sets are exact: k entries, larger value first, lower index on ties.
+ * Greedy mode (temperature == 0): accept while x_k equals the argmax of row k
+ * (lowest index on ties), then emit the argmax of the first mismatching row
+ * (or of row K); draft_probs and uniforms are not read (may be NULL).
+ *
+ *   target_logits [B][K+1][V]  dtype                   device, read
+ *   draft_probs   [B][K][V]    float32                 device, read (rows sum to ~1)
+ *   draft_tokens  [B][K]       int32                   device, read
+ *   uniforms      [B][K+1]     float32 in [0,1)        device, read
+ *   temperature   >= 0, finite (0 = greedy); top_k <= 0 or >= V disables top-k
+ *   out_tokens    [B][K+1]     int32                   device, written: x_0..x_{j-1}, y, then -1
+ *   out_accept_len[B]          int32                   device, written: j in [0,K], -1 on error
+ *   out_diag      [B][2K+2]    float32, may be NULL    device, written:
+ *                 [k] = p'_k(x_k), [K+k] = q'_k(x_k) for k < K,
+ *                 [2K] = mass of the final-draw distribution before
+ *                 normalisation (residual mass, or 1 for p'), [2K+1] = the
+ *                 drawn token's probability under it.
+ * Returns SPEC_OK or a negative code.
+ */
+int spec_verify_chain(const void* target_logits, spec_dtype_t dtype,
+                      const float* draft_probs, const int32_t* draft_tokens,
+                      const float* uniforms, int B, int K, int V,
+                      float temperature, int top_k,
+                      int32_t* out_tokens, int32_t* out_accept_len, float* out_diag,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * spec_verify_tree_greedy -- greedy verification of a static draft tree.
+ *
+ * Node 0 is the root; parents_host[0] = -1 and 0 <= parents_host[n] < n
+ * (nodes in topological, e.g. breadth-first, order).  Row n of the logits is
+ * the target's next-token distribution after the path to node n.  Node n > 0 is
+ * accepted iff its parent is accepted and node_tokens[b][n] equals the argmax
+ * of the parent's row (lowest index on ties).  The result is the deepest
+ * accepted node n* (lowest node index on ties), its root-to-n* path and the
+ * bonus token argmax(row n*).  D = the tree's maximum depth.
+ *
+ *   target_logits [B][N][V]    dtype                   device, read
+ *   node_tokens   [B][N]       int32                   device, read ([b][0] ignored)
+ *   parents_host  [N]          int32                   HOST, read during the call only
+ *   out_path      [B][D+1]     int32                   device, written: node ids root..n*, then -1
+ *   out_tokens    [B][D+1]     int32                   device, written: accepted tokens, bonus, then -1
+ *   out_accept_len[B]          int32                   device, written: depth of n*, -1 on error
+ */
+int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype,
+                            const int32_t* node_tokens, const int32_t* parents_host,
+                            int B, int N, int V,
+                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * spec_accept_rate -- alpha[b][k] = sum_i min(p'_k(i), q'_k(i)) for k < K, with
+ * p' and q' transformed as in spec_verify_chain (rows 0..K-1 of the logits are
+ * read; row K is not).  Greedy (temperature == 0): 1 if the argmax of target
+ * row k equals the argmax of draft row k, else 0.  An invalid row gives NaN.
+ *
+ *   target_logits [B][K+1][V], draft_probs [B][K][V] (device, read)
+ *   out_alpha     [B][K]       float32                 device, written
+ */
+int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                     int B, int K, int V, float temperature, int top_k,
+                     float* out_alpha, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Instrumentation.
+ *
+ * spec_profile_events: the next verification call made BY THIS HOST THREAD
+ * records `start_event` immediately before and `stop_event` immediately after
+ * its dominant (vocabulary-streaming) kernel, on its stream; both are
+ * hipEvent_t created by the caller.  The request is consumed by that call.
+ *
+ * spec_copy_probe: plain device-to-device copy of `bytes` (multiple of 16,
+ * 16-byte aligned pointers) by a streaming kernel, for calibrating hardware
+ * byte counters against a known traffic.
+ */
+int spec_profile_events(void* start_event, void* stop_event);
+int spec_copy_probe(const void* src, void* dst, size_t bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

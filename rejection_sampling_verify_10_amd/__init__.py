@@ -1,0 +1,231 @@
+"""Verification step of speculative decoding on MI355X (gfx950).
+
+Thin ctypes binding over ``libspecverify.so`` (see ``include/spec_verify.h``):
+it checks tensor placement and dtypes, allocates outputs and the workspace
+with torch, and passes raw device pointers plus torch's current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+CPU path.  If the library is missing the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_TOPK_MAX = 64
+SPEC_MAX_K = 63
+SPEC_MAX_NODES = 64
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class SpecError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SpecError(f"{LIB_PATH} is missing: build it with "
+                            "`python -m rejection_sampling_verify_10_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.spec_error_string.argtypes = [I]
+        L.spec_error_string.restype = ctypes.c_char_p
+        L.spec_chain_workspace_bytes.argtypes = [I, I, I, I, F, I]
+        L.spec_chain_workspace_bytes.restype = Z
+        L.spec_tree_workspace_bytes.argtypes = [I, I, I, I]
+        L.spec_tree_workspace_bytes.restype = Z
+        L.spec_accept_rate_workspace_bytes.argtypes = [I, I, I, I, F, I]
+        L.spec_accept_rate_workspace_bytes.restype = Z
+        L.spec_verify_chain.argtypes = [P, I, P, P, P, I, I, I, F, I, P, P, P, P, Z, P]
+        L.spec_verify_chain.restype = I
+        L.spec_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, Z, P]
+        L.spec_verify_tree_greedy.restype = I
+        L.spec_accept_rate.argtypes = [P, I, P, I, I, I, F, I, P, P, Z, P]
+        L.spec_accept_rate.restype = I
+        L.spec_profile_events.argtypes = [P, P]
+        L.spec_profile_events.restype = I
+        L.spec_copy_probe.argtypes = [P, P, Z, P]
+        L.spec_copy_probe.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise SpecError(f"{what}: {lib().spec_error_string(rc).decode()} ({rc})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _shape(t: Optional[torch.Tensor], name: str, shape: Tuple[int, ...]) -> None:
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device: torch.device,
+               given: Optional[torch.Tensor] = None) -> Tuple[int, Optional[torch.Tensor]]:
+    if nbytes == 0:
+        return 0, None
+    if given is not None:
+        _dev(given, "workspace", torch.uint8)
+        if given.numel() < nbytes + 256:
+            raise ValueError(f"workspace needs {nbytes + 256} bytes, got {given.numel()}")
+        return (given.data_ptr() + 255) // 256 * 256, given
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    p = ws.data_ptr()
+    return (p + 255) // 256 * 256, ws
+
+
+def chain_workspace_bytes(B: int, K: int, V: int, dtype: int, temperature: float, top_k: int) -> int:
+    return int(lib().spec_chain_workspace_bytes(B, K, V, dtype, float(temperature), int(top_k)))
+
+
+def tree_workspace_bytes(B: int, N: int, V: int, dtype: int) -> int:
+    return int(lib().spec_tree_workspace_bytes(B, N, V, dtype))
+
+
+def accept_rate_workspace_bytes(B: int, K: int, V: int, dtype: int, temperature: float, top_k: int) -> int:
+    return int(lib().spec_accept_rate_workspace_bytes(B, K, V, dtype, float(temperature), int(top_k)))
+
+
+def verify_chain(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor],
+                 draft_tokens: torch.Tensor, uniforms: Optional[torch.Tensor],
+                 temperature: float = 1.0, top_k: int = 0, *, diag: bool = False,
+                 out: Optional[Tuple[torch.Tensor, ...]] = None, workspace: Optional[torch.Tensor] = None):
+    """Batched chain verification (``spec_verify_chain``).
+
+    target_logits [B, K+1, V] bf16/f32, draft_probs [B, K, V] f32, draft_tokens [B, K] int32,
+    uniforms [B, K+1] f32.  Returns (tokens [B, K+1] int32, accept_len [B] int32) and, with
+    ``diag=True``, a third tensor [B, 2K+2] f32.  Asynchronous on the current stream.
+    ``out`` reuses output tensors; ``workspace`` (uint8, at least the size reported by
+    :func:`chain_workspace_bytes` + 256) avoids the per-call allocation.
+    """
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    _shape(draft_probs, "draft_probs", (B, K, V))
+    _shape(draft_tokens, "draft_tokens", (B, K))
+    _shape(uniforms, "uniforms", (B, K + 1))
+    if float(temperature) != 0.0 and (draft_probs is None or uniforms is None):
+        raise ValueError("sampling verification needs draft_probs and uniforms")
+    z = _dev(target_logits, "target_logits")
+    q = _dev(draft_probs, "draft_probs", torch.float32) if draft_probs is not None else None
+    x = _dev(draft_tokens, "draft_tokens", torch.int32)
+    u = _dev(uniforms, "uniforms", torch.float32) if uniforms is not None else None
+    if out is not None:
+        _shape(out[0], "out tokens", (B, K + 1))
+        _shape(out[1], "out accept_len", (B,))
+        if diag:
+            _shape(out[2], "out diag", (B, 2 * K + 2))
+        _dev(out[0], "out tokens", torch.int32)
+        _dev(out[1], "out accept_len", torch.int32)
+        if diag:
+            _dev(out[2], "out diag", torch.float32)
+    if out is None:
+        tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        dg = torch.empty((B, 2 * K + 2), dtype=torch.float32, device=dev) if diag else None
+    else:
+        tokens, alen = out[0], out[1]
+        dg = out[2] if diag else None
+    need = chain_workspace_bytes(B, K, V, code, temperature, top_k)
+    wp, ws = _workspace(need, dev, workspace)
+    rc = lib().spec_verify_chain(z, code, q, x, u, B, K, V, float(temperature), int(top_k),
+                                 tokens.data_ptr(), alen.data_ptr(), dg.data_ptr() if dg is not None else None,
+                                 wp, need, _stream(dev))
+    _check(rc, "spec_verify_chain")
+    return (tokens, alen, dg) if diag else (tokens, alen)
+
+
+def verify_tree_greedy(target_logits: torch.Tensor, node_tokens: torch.Tensor, parents: Sequence[int]):
+    """Greedy static-tree verification (``spec_verify_tree_greedy``).
+
+    target_logits [B, N, V], node_tokens [B, N] int32, parents: N host ints.
+    Returns (path [B, D+1], tokens [B, D+1], accept_len [B]) int32 tensors.
+    """
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    _shape(node_tokens, "node_tokens", (B, N))
+    if len(parents) != N:
+        raise ValueError(f"parents must have {N} entries")
+    par = (ctypes.c_int32 * N)(*[int(p) for p in parents])
+    depth = [0] * N
+    for n in range(1, N):
+        depth[n] = depth[int(parents[n])] + 1 if 0 <= int(parents[n]) < n else 0
+    D = max(depth)
+    path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+    toks = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    need = tree_workspace_bytes(B, N, V, code)
+    wp, ws = _workspace(need, dev)
+    rc = lib().spec_verify_tree_greedy(_dev(target_logits, "target_logits"), code,
+                                       _dev(node_tokens, "node_tokens", torch.int32), par, B, N, V,
+                                       path.data_ptr(), toks.data_ptr(), alen.data_ptr(), wp, need, _stream(dev))
+    _check(rc, "spec_verify_tree_greedy")
+    return path, toks, alen
+
+
+def accept_rate(target_logits: torch.Tensor, draft_probs: torch.Tensor, temperature: float = 1.0,
+                top_k: int = 0) -> torch.Tensor:
+    """alpha[b, k] = sum min(p'_k, q'_k) (``spec_accept_rate``); returns [B, K] f32."""
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    _shape(draft_probs, "draft_probs", (B, K, V))
+    alpha = torch.empty((B, K), dtype=torch.float32, device=dev)
+    need = accept_rate_workspace_bytes(B, K, V, code, temperature, top_k)
+    wp, ws = _workspace(need, dev)
+    rc = lib().spec_accept_rate(_dev(target_logits, "target_logits"), code,
+                                _dev(draft_probs, "draft_probs", torch.float32), B, K, V,
+                                float(temperature), int(top_k), alpha.data_ptr(), wp, need, _stream(dev))
+    _check(rc, "spec_accept_rate")
+    return alpha
+
+
+def profile_next_call(start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
+    """Bracket the dominant kernel of this thread's next verification call with two events."""
+    _check(lib().spec_profile_events(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)),
+           "spec_profile_events")
+
+
+def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Plain streaming copy kernel (for calibrating hardware byte counters)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(lib().spec_copy_probe(_dev(src, "src"), _dev(dst, "dst"), n, _stream(src.device)), "spec_copy_probe")

@@ -1,0 +1,483 @@
+// C ABI entry points: argument checks, workspace carving, launch sequencing.
+// Every call only enqueues kernels on the caller's stream.
+
+#include <math.h>
+#include <string.h>
+
+#include "../../include/spec_verify.h"
+#include "common.hpp"
+#include "internal.hpp"
+
+using namespace sv;
+
+namespace {
+
+static_assert(SPEC_TOPK_MAX == kTopkMax, "top-k list width");
+static_assert(SPEC_MAX_V == kMaxV, "vocabulary limit");
+
+thread_local hipEvent_t t_prof_start = nullptr;
+thread_local hipEvent_t t_prof_stop = nullptr;
+
+struct ProfileScope {
+    hipStream_t s;
+    hipEvent_t start, stop;
+    explicit ProfileScope(hipStream_t st) : s(st), start(t_prof_start), stop(t_prof_stop) {
+        t_prof_start = t_prof_stop = nullptr;
+    }
+    void before() const { if (start) (void)hipEventRecord(start, s); }
+    void after() const { if (stop) (void)hipEventRecord(stop, s); }
+};
+
+// Bump allocator over the caller's workspace (or a size counter when base is null).
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T> T* take(size_t n) {
+        off = (off + 255) & ~static_cast<size_t>(255);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += n * sizeof(T);
+        return p;
+    }
+};
+
+bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
+int esz_of(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+RowStats carve_rowstats(Carver& c, size_t R) {
+    RowStats st;
+    st.m = c.take<float>(R);
+    st.Z = c.take<double>(R);
+    st.arg = c.take<int32_t>(R);
+    st.zx = c.take<float>(R);
+    st.flags = c.take<uint32_t>(R);
+    return st;
+}
+
+struct TopkBufs {
+    int Ct, chunk_t, Cd, chunk_d;
+    float* vals;
+    int32_t* idx;
+    int32_t* cnt;
+    uint32_t* flags;
+    int32_t* row_idx;
+    double* row_p;
+    int32_t* row_cnt;
+    uint32_t* row_flags;
+};
+
+TopkBufs carve_topk(Carver& c, int dtype, int V, size_t Rt, size_t Rd) {
+    TopkBufs t;
+    topk_chunking(V, esz_of(dtype), &t.Ct, &t.chunk_t);
+    topk_chunking(V, 4, &t.Cd, &t.chunk_d);
+    const size_t units = Rt * t.Ct + Rd * t.Cd;
+    t.vals = c.take<float>(units * kTopkMax);
+    t.idx = c.take<int32_t>(units * kTopkMax);
+    t.cnt = c.take<int32_t>(units);
+    t.flags = c.take<uint32_t>(units);
+    const size_t rows = Rt + Rd;
+    t.row_idx = c.take<int32_t>(rows * kTopkMax);
+    t.row_p = c.take<double>(rows * kTopkMax);
+    t.row_cnt = c.take<int32_t>(rows);
+    t.row_flags = c.take<uint32_t>(rows);
+    return t;
+}
+
+// Chunks per row must fit the row-merge kernel (<= 16).
+bool topk_shape_ok(int dtype, int V) {
+    int c1, e1, c2, e2;
+    topk_chunking(V, esz_of(dtype), &c1, &e1);
+    topk_chunking(V, 4, &c2, &e2);
+    return c1 <= 16 && c2 <= 16;
+}
+
+int check_common(const void* logits, int dtype, int B, int K, int V, float T) {
+    if (!logits) return SPEC_EINVAL;
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EINVAL;
+    if (B < 1 || K < 1 || V < 1) return SPEC_EINVAL;
+    if (!(T >= 0.f) || isinf(T)) return SPEC_EINVAL;
+    if (!aligned(logits, esz_of(dtype))) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || V > SPEC_MAX_V) return SPEC_EUNSUPPORTED;
+    if (static_cast<long>(B) * (K + 1) > (1L << 30)) return SPEC_EUNSUPPORTED;
+    return SPEC_OK;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+    if (need == 0) return SPEC_OK;
+    if (!ws || !aligned(ws, 256) || have < need) return SPEC_EWORKSPACE;
+    return SPEC_OK;
+}
+
+// Plans the chain call into `c`; returns the workspace size.
+struct ChainPlan {
+    int mode;   // 0 dense, 1 top-k, 2 greedy
+    RowStats st;
+    double* qsum;
+    uint32_t* qflags;
+    TopkBufs tk;
+};
+
+ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {
+    ChainPlan p{};
+    const size_t Rt = static_cast<size_t>(B) * (K + 1), Rd = static_cast<size_t>(B) * K;
+    if (T == 0.f) {
+        p.mode = 2;
+        p.st = carve_rowstats(c, Rt);
+    } else if (topk_active(top_k, V)) {
+        p.mode = 1;
+        p.tk = carve_topk(c, dtype, V, Rt, Rd);
+    } else {
+        p.mode = 0;
+        p.st = carve_rowstats(c, Rt);
+        if (T != 1.f) {
+            p.qsum = c.take<double>(Rd);
+            p.qflags = c.take<uint32_t>(Rd);
+        }
+    }
+    return p;
+}
+
+struct AlphaPlan {
+    int mode;   // 0 dense, 1 top-k, 2 greedy
+    RowStats st, qst;
+    double* qsum;
+    uint32_t* qflags;
+    TopkBufs tk;
+};
+
+AlphaPlan plan_alpha(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {
+    AlphaPlan p{};
+    const size_t R = static_cast<size_t>(B) * K;
+    if (T == 0.f) {
+        p.mode = 2;
+        p.st = carve_rowstats(c, R);
+        p.qst = carve_rowstats(c, R);
+    } else if (topk_active(top_k, V)) {
+        p.mode = 1;
+        p.tk = carve_topk(c, dtype, V, R, R);
+    } else {
+        p.mode = 0;
+        p.st = carve_rowstats(c, R);
+        if (T != 1.f) {
+            p.qsum = c.take<double>(R);
+            p.qflags = c.take<uint32_t>(R);
+        }
+    }
+    return p;
+}
+
+RowStatsArgs rowstats_args(const void* base, int dtype, int V, int rows_per_batch, int batch_stride, int B,
+                           bool argmax, float T, const int32_t* gather, int gather_K, const RowStats& out) {
+    RowStatsArgs a{};
+    a.base = base;
+    a.dtype = dtype;
+    a.V = V;
+    a.rows_per_batch = rows_per_batch;
+    a.batch_stride = batch_stride;
+    a.R = B * rows_per_batch;
+    a.argmax_mode = argmax ? 1 : 0;
+    a.scale = argmax ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(T));
+    a.invT = argmax ? 0.0 : 1.0 / static_cast<double>(T);
+    a.gather_tokens = gather;
+    a.gather_K = gather_K;
+    a.out = out;
+    return a;
+}
+
+TopkChunkArgs topk_chunk_args(const void* target, const float* draft, int dtype, int V, int top_k, int Rt,
+                              int rows_per_batch, int batch_stride, int Rd, const TopkBufs& t) {
+    TopkChunkArgs a{};
+    a.target = target;
+    a.draft = draft;
+    a.dtype = dtype;
+    a.V = V;
+    a.top_k = top_k;
+    a.Rt = Rt;
+    a.Ct = t.Ct;
+    a.chunk_t = t.chunk_t;
+    a.Rd = Rd;
+    a.Cd = t.Cd;
+    a.chunk_d = t.chunk_d;
+    a.target_rows_per_batch = rows_per_batch;
+    a.target_batch_stride = batch_stride;
+    a.vals = t.vals;
+    a.idx = t.idx;
+    a.cnt = t.cnt;
+    a.flags = t.flags;
+    return a;
+}
+
+TopkRowsArgs topk_rows_args(const TopkBufs& t, int Rt, int Rd, int top_k, float T) {
+    TopkRowsArgs a{};
+    a.chunk_vals = t.vals;
+    a.chunk_idx = t.idx;
+    a.chunk_cnt = t.cnt;
+    a.chunk_flags = t.flags;
+    a.Rt = Rt;
+    a.Ct = t.Ct;
+    a.Rd = Rd;
+    a.Cd = t.Cd;
+    a.top_k = top_k;
+    a.invT = 1.0 / static_cast<double>(T);
+    a.draft_identity = (T == 1.f) ? 1 : 0;
+    a.row_idx = t.row_idx;
+    a.row_p = t.row_p;
+    a.row_cnt = t.row_cnt;
+    a.row_flags = t.row_flags;
+    return a;
+}
+
+#define SV_TRY(expr)                                  \
+    do {                                              \
+        if ((expr) != hipSuccess) return SPEC_ELAUNCH; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_error_string(int code) {
+    switch (code) {
+        case SPEC_OK: return "ok";
+        case SPEC_EINVAL: return "invalid argument";
+        case SPEC_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case SPEC_ELAUNCH: return "kernel launch failed";
+        case SPEC_EUNSUPPORTED: return "outside the limits of this build";
+        default: return "unknown error";
+    }
+}
+
+size_t spec_chain_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k) {
+    int dummy;
+    (void)dummy;
+    if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return 0;
+    if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || !(temperature >= 0.f) || isinf(temperature)) return 0;
+    Carver c(nullptr);
+    plan_chain(c, B, K, V, dtype, temperature, top_k);
+    return (c.off + 255) & ~static_cast<size_t>(255);
+}
+
+size_t spec_tree_workspace_bytes(int B, int N, int V, spec_dtype_t dtype) {
+    if (B < 1 || N < 1 || N > SPEC_MAX_NODES || V < 1 || V > SPEC_MAX_V) return 0;
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return 0;
+    Carver c(nullptr);
+    carve_rowstats(c, static_cast<size_t>(B) * N);
+    return (c.off + 255) & ~static_cast<size_t>(255);
+}
+
+size_t spec_accept_rate_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k) {
+    if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return 0;
+    if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || !(temperature >= 0.f) || isinf(temperature)) return 0;
+    Carver c(nullptr);
+    plan_alpha(c, B, K, V, dtype, temperature, top_k);
+    return (c.off + 255) & ~static_cast<size_t>(255);
+}
+
+int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                      float temperature, int top_k, int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    int rc = check_common(target_logits, dtype, B, K, V, temperature);
+    if (rc) return rc;
+    const bool greedy = temperature == 0.f;
+    if (!draft_tokens || !out_tokens || !out_accept_len) return SPEC_EINVAL;
+    if (!greedy && (!draft_probs || !uniforms)) return SPEC_EINVAL;
+    if (!aligned(draft_tokens, 4) || !aligned(out_tokens, 4) || !aligned(out_accept_len, 4)) return SPEC_EINVAL;
+    if ((draft_probs && !aligned(draft_probs, 4)) || (uniforms && !aligned(uniforms, 4)) ||
+        (out_diag && !aligned(out_diag, 4)))
+        return SPEC_EINVAL;
+    if (!greedy && topk_active(top_k, V)) {
+        if (top_k > SPEC_TOPK_MAX || !topk_shape_ok(dtype, V)) return SPEC_EUNSUPPORTED;
+    }
+    const size_t need = spec_chain_workspace_bytes(B, K, V, dtype, temperature, top_k);
+    rc = check_workspace(workspace, workspace_bytes, need);
+    if (rc) return rc;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfileScope prof(s);
+    Carver c(workspace);
+    ChainPlan p = plan_chain(c, B, K, V, dtype, temperature, top_k);
+
+    ChainArgs ca{};
+    ca.logits = target_logits;
+    ca.dtype = dtype;
+    ca.q = draft_probs;
+    ca.x = draft_tokens;
+    ca.u = uniforms;
+    ca.B = B;
+    ca.K = K;
+    ca.V = V;
+    ca.T = temperature;
+    ca.invT = greedy ? 0.0 : 1.0 / static_cast<double>(temperature);
+    ca.transformed = (!greedy && temperature != 1.f) ? 1 : 0;
+    ca.out_tokens = out_tokens;
+    ca.out_accept_len = out_accept_len;
+    ca.out_diag = out_diag;
+
+    if (p.mode == 2) {
+        ca.st = p.st;
+        RowStatsArgs ra = rowstats_args(target_logits, dtype, V, K + 1, K + 1, B, true, 0.f, nullptr, 0, p.st);
+        prof.before();
+        SV_TRY(launch_rowstats(ra, s));
+        prof.after();
+        SV_TRY(launch_chain_greedy(ca, s));
+    } else if (p.mode == 1) {
+        const int Rt = B * (K + 1), Rd = B * K;
+        TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, V, top_k, Rt, K + 1, K + 1, Rd, p.tk);
+        prof.before();
+        SV_TRY(launch_topk_chunks(ta, s));
+        prof.after();
+        SV_TRY(launch_topk_rows(topk_rows_args(p.tk, Rt, Rd, top_k, temperature), s));
+        ca.row_idx = p.tk.row_idx;
+        ca.row_p = p.tk.row_p;
+        ca.row_cnt = p.tk.row_cnt;
+        ca.row_flags = p.tk.row_flags;
+        SV_TRY(launch_chain_topk(ca, s));
+    } else {
+        ca.st = p.st;
+        RowStatsArgs ra =
+            rowstats_args(target_logits, dtype, V, K + 1, K + 1, B, false, temperature, draft_tokens, K, p.st);
+        prof.before();
+        SV_TRY(launch_rowstats(ra, s));
+        prof.after();
+        if (ca.transformed) {
+            PowerSumArgs pa{draft_probs, V, B * K, static_cast<float>(1.0 / temperature), p.qsum, p.qflags};
+            SV_TRY(launch_power_sums(pa, s));
+            ca.qsum = p.qsum;
+            ca.qflags = p.qflags;
+        }
+        SV_TRY(launch_chain_dense(ca, s));
+    }
+    return SPEC_OK;
+}
+
+int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype, const int32_t* node_tokens,
+                            const int32_t* parents_host, int B, int N, int V, int32_t* out_path,
+                            int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+    if (!target_logits || !node_tokens || !parents_host || !out_path || !out_tokens || !out_accept_len)
+        return SPEC_EINVAL;
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EINVAL;
+    if (B < 1 || N < 1 || V < 1) return SPEC_EINVAL;
+    if (N > SPEC_MAX_NODES || V > SPEC_MAX_V) return SPEC_EUNSUPPORTED;
+    if (!aligned(target_logits, esz_of(dtype)) || !aligned(node_tokens, 4) || !aligned(out_path, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_accept_len, 4))
+        return SPEC_EINVAL;
+    TreeArgs ta{};
+    if (parents_host[0] != -1) return SPEC_EINVAL;
+    int depth[SPEC_MAX_NODES];
+    depth[0] = 0;
+    int D = 0;
+    ta.parents[0] = -1;
+    for (int n = 1; n < N; ++n) {
+        const int p = parents_host[n];
+        if (p < 0 || p >= n) return SPEC_EINVAL;
+        depth[n] = depth[p] + 1;
+        if (depth[n] > D) D = depth[n];
+        ta.parents[n] = static_cast<int16_t>(p);
+    }
+    const size_t need = spec_tree_workspace_bytes(B, N, V, dtype);
+    int rc = check_workspace(workspace, workspace_bytes, need);
+    if (rc) return rc;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfileScope prof(s);
+    Carver c(workspace);
+    RowStats st = carve_rowstats(c, static_cast<size_t>(B) * N);
+    RowStatsArgs ra = rowstats_args(target_logits, dtype, V, N, N, B, true, 0.f, nullptr, 0, st);
+    prof.before();
+    SV_TRY(launch_rowstats(ra, s));
+    prof.after();
+    ta.node_tokens = node_tokens;
+    ta.B = B;
+    ta.N = N;
+    ta.V = V;
+    ta.D = D;
+    ta.st = st;
+    ta.out_path = out_path;
+    ta.out_tokens = out_tokens;
+    ta.out_accept_len = out_accept_len;
+    SV_TRY(launch_tree(ta, s));
+    return SPEC_OK;
+}
+
+int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float* draft_probs, int B, int K,
+                     int V, float temperature, int top_k, float* out_alpha, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
+    int rc = check_common(target_logits, dtype, B, K, V, temperature);
+    if (rc) return rc;
+    if (!draft_probs || !out_alpha || !aligned(draft_probs, 4) || !aligned(out_alpha, 4)) return SPEC_EINVAL;
+    const bool greedy = temperature == 0.f;
+    if (!greedy && topk_active(top_k, V)) {
+        if (top_k > SPEC_TOPK_MAX || !topk_shape_ok(dtype, V)) return SPEC_EUNSUPPORTED;
+    }
+    const size_t need = spec_accept_rate_workspace_bytes(B, K, V, dtype, temperature, top_k);
+    rc = check_workspace(workspace, workspace_bytes, need);
+    if (rc) return rc;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfileScope prof(s);
+    Carver c(workspace);
+    AlphaPlan p = plan_alpha(c, B, K, V, dtype, temperature, top_k);
+    AlphaArgs aa{};
+    aa.logits = target_logits;
+    aa.dtype = dtype;
+    aa.q = draft_probs;
+    aa.B = B;
+    aa.K = K;
+    aa.V = V;
+    aa.scale = greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+    aa.invT = greedy ? 0.f : static_cast<float>(1.0 / static_cast<double>(temperature));
+    aa.transformed = (!greedy && temperature != 1.f) ? 1 : 0;
+    aa.out_alpha = out_alpha;
+    if (p.mode == 2) {
+        prof.before();
+        SV_TRY(launch_rowstats(rowstats_args(target_logits, dtype, V, K, K + 1, B, true, 0.f, nullptr, 0, p.st), s));
+        prof.after();
+        SV_TRY(launch_rowstats(rowstats_args(draft_probs, SPEC_F32, V, K, K, B, true, 0.f, nullptr, 0, p.qst), s));
+        aa.st = p.st;
+        aa.qst = p.qst;
+        SV_TRY(launch_alpha_greedy(aa, s));
+    } else if (p.mode == 1) {
+        const int R = B * K;
+        TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, V, top_k, R, K, K + 1, R, p.tk);
+        prof.before();
+        SV_TRY(launch_topk_chunks(ta, s));
+        prof.after();
+        SV_TRY(launch_topk_rows(topk_rows_args(p.tk, R, R, top_k, temperature), s));
+        aa.row_idx = p.tk.row_idx;
+        aa.row_p = p.tk.row_p;
+        aa.row_cnt = p.tk.row_cnt;
+        aa.row_flags = p.tk.row_flags;
+        SV_TRY(launch_alpha_topk(aa, s));
+    } else {
+        prof.before();
+        SV_TRY(launch_rowstats(
+            rowstats_args(target_logits, dtype, V, K, K + 1, B, false, temperature, nullptr, 0, p.st), s));
+        prof.after();
+        aa.st = p.st;
+        if (aa.transformed) {
+            PowerSumArgs pa{draft_probs, V, B * K, static_cast<float>(1.0 / temperature), p.qsum, p.qflags};
+            SV_TRY(launch_power_sums(pa, s));
+            aa.qsum = p.qsum;
+            aa.qflags = p.qflags;
+        }
+        SV_TRY(launch_alpha_dense(aa, s));
+    }
+    return SPEC_OK;
+}
+
+int spec_profile_events(void* start_event, void* stop_event) {
+    t_prof_start = static_cast<hipEvent_t>(start_event);
+    t_prof_stop = static_cast<hipEvent_t>(stop_event);
+    return SPEC_OK;
+}
+
+int spec_copy_probe(const void* src, void* dst, size_t bytes, void* hip_stream) {
+    if (!src || !dst || bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return SPEC_EINVAL;
+    if (launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(hip_stream)) != hipSuccess) return SPEC_ELAUNCH;
+    return SPEC_OK;
+}
+
+}  // extern "C"

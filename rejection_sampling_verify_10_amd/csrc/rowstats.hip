@@ -1,0 +1,260 @@
+// Row statistics over the vocabulary: one pass over each logit row.
+//
+// Softmax mode gives the row maximum m and Z = sum_i exp((z_i - m)/T), the
+// normaliser of the target distribution p' = softmax(z/T) ("064 · 投机解码",
+// section 二: p must carry the temperature).  Argmax mode gives the lowest
+// index of the maximum, the greedy rule of "投机解码与 EAGLE", section 二.
+//
+// The rows are HBM-bound: each is read once with 16-byte non-temporal loads,
+// four vectors in flight per thread.  Inside a thread the sum is accumulated
+// in fp32 against a running maximum (rescaled once per tile of 4 vectors);
+// the 256 per-thread partials are combined in fp64 with exact per-thread
+// rescaling, so Z carries the accuracy of the fp32 exponentials.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace sv {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ u32x4 neg_inf_vec(int dt) {
+    const uint32_t w = dt ? 0xff80ff80u : 0xff800000u;
+    return u32x4{w, w, w, w};
+}
+
+template <int DT>
+__device__ __forceinline__ void softmax_row_vec(const char* row, int V, float scale, float& m, float& s) {
+    using E = Elem<DT>;
+    const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+    const int nvec = V / E::kPerVec;
+    float acc[kUnroll] = {0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    for (int base = 0; base < nvec; base += kThreads * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = base + u * kThreads + threadIdx.x;
+            v[u] = (i < nvec) ? load_stream(rv + i) : neg_inf_vec(DT);
+        }
+        float tmax = m;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < E::kPerVec; ++e) tmax = fmaxf(tmax, E::get(v[u], e));
+        if (tmax > m) {
+            const float f = __builtin_amdgcn_exp2f((m - tmax) * scale);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) acc[u] *= f;
+            m = tmax;
+        }
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < E::kPerVec; ++e)
+                    acc[u] += __builtin_amdgcn_exp2f((E::get(v[u], e) - m) * scale);
+        } else {
+            // Everything seen so far is -inf (or padding); only a NaN may matter.
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < E::kPerVec; ++e)
+                    if (E::get(v[u], e) != E::get(v[u], e)) acc[0] = NAN;
+        }
+    }
+    s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <int DT>
+__device__ __forceinline__ void softmax_row_scalar(const char* row, int V, float scale, float& m, float& s) {
+    m = -INFINITY;
+    s = 0.f;
+    for (int i = threadIdx.x; i < V; i += kThreads) {
+        const float z = Elem<DT>::scalar(row, i);
+        if (z > m) {
+            s *= __builtin_amdgcn_exp2f((m - z) * scale);
+            m = z;
+        }
+        if (m != -INFINITY) s += __builtin_amdgcn_exp2f((z - m) * scale);
+        else if (z != z) s = NAN;
+    }
+}
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void argmax_row(const char* row, int V, float& best, int& bi, uint32_t& nan) {
+    using E = Elem<DT>;
+    best = -INFINITY;
+    bi = 0x7fffffff;
+    nan = 0;
+    if (VEC) {
+        const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+        const int nvec = V / E::kPerVec;
+        for (int base = 0; base < nvec; base += kThreads * kUnroll) {
+            u32x4 v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = base + u * kThreads + threadIdx.x;
+                v[u] = (i < nvec) ? load_stream(rv + i) : neg_inf_vec(DT);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i0 = (base + u * kThreads + threadIdx.x) * E::kPerVec;
+#pragma unroll
+                for (int e = 0; e < E::kPerVec; ++e) {
+                    const float z = E::get(v[u], e);
+                    nan |= (z != z);
+                    if (z > best) { best = z; bi = i0 + e; }
+                }
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < V; i += kThreads) {
+            const float z = E::scalar(row, i);
+            nan |= (z != z);
+            if (z > best) { best = z; bi = i; }
+        }
+    }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
+    __shared__ float s_m[kThreads / kWave];
+    __shared__ double s_z[kThreads / kWave];
+    __shared__ int s_i[kThreads / kWave];
+    __shared__ uint32_t s_f[kThreads / kWave];
+
+    const int r = blockIdx.x;
+    const int b = r / a.rows_per_batch;
+    const int k = r - b * a.rows_per_batch;
+    const long mem_row = static_cast<long>(b) * a.batch_stride + k;
+    const char* row = static_cast<const char*>(a.base) + mem_row * a.V * Elem<DT>::kBytes;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+
+    if (a.argmax_mode) {
+        float best;
+        int bi;
+        uint32_t nan;
+        argmax_row<DT, VEC>(row, a.V, best, bi, nan);
+        wave_argmax(best, bi);
+        nan = wave_or(nan);
+        if (lane == 0) { s_m[wid] = best; s_i[wid] = bi; s_f[wid] = nan; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < kThreads / kWave; ++w) {
+                if (precedes(s_m[w], s_i[w], best, bi)) { best = s_m[w]; bi = s_i[w]; }
+                nan |= s_f[w];
+            }
+            // Every element was -inf: the lowest index, 0, is the argmax.
+            if (bi == 0x7fffffff) bi = 0;
+            a.out.m[r] = best;
+            a.out.arg[r] = bi;
+            a.out.flags[r] = nan ? kFlagInvalid : 0u;
+        }
+        return;
+    }
+
+    float m, s;
+    if (VEC) softmax_row_vec<DT>(row, a.V, a.scale, m, s);
+    else softmax_row_scalar<DT>(row, a.V, a.scale, m, s);
+
+    float M = wave_max(m);
+    if (lane == 0) s_m[wid] = M;
+    __syncthreads();
+    M = s_m[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) M = fmaxf(M, s_m[w]);
+    // Rescale each thread's partial to the row maximum in fp64.
+    double c = static_cast<double>(s) * exp((static_cast<double>(m) - static_cast<double>(M)) * a.invT);
+    c = wave_sum(c);
+    if (lane == 0) s_z[wid] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double Z = 0.0;
+        for (int w = 0; w < kThreads / kWave; ++w) Z += s_z[w];
+        a.out.m[r] = M;
+        a.out.Z[r] = Z;
+        a.out.flags[r] = (Z >= 1.0 && Z < INFINITY) ? 0u : kFlagInvalid;
+        if (a.out.zx) {
+            float zx = NAN;
+            if (a.gather_tokens && k < a.gather_K) {
+                const int x = a.gather_tokens[static_cast<long>(b) * a.gather_K + k];
+                if (x >= 0 && x < a.V) zx = Elem<DT>::scalar(row, x);
+            }
+            a.out.zx[r] = zx;
+        }
+    }
+}
+
+// sum_i q_i^(1/T) of a draft-probability row, plus validity (E3, E4).
+__global__ __launch_bounds__(kThreads) void power_sums_kernel(PowerSumArgs a) {
+    __shared__ double s_z[kThreads / kWave];
+    __shared__ uint32_t s_f[kThreads / kWave];
+    const float* row = a.q + static_cast<long>(blockIdx.x) * a.V;
+    double acc = 0.0;
+    float part = 0.f;
+    uint32_t bad = 0;
+    int n = 0;
+    for (int i = threadIdx.x; i < a.V; i += kThreads) {
+        const float v = row[i];
+        bad |= !(v >= 0.f && v < INFINITY);
+        part += (v > 0.f) ? __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(v) * a.invT) : 0.f;
+        if (++n == 64) { acc += part; part = 0.f; n = 0; }
+    }
+    acc += part;
+    acc = wave_sum(acc);
+    bad = wave_or(bad);
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    if (lane == 0) { s_z[wid] = acc; s_f[wid] = bad; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double S = 0.0;
+        uint32_t f = 0;
+        for (int w = 0; w < kThreads / kWave; ++w) { S += s_z[w]; f |= s_f[w]; }
+        a.S[blockIdx.x] = S;
+        a.flags[blockIdx.x] = (f || !(S > 0.0)) ? kFlagInvalid : 0u;
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         size_t n) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        __builtin_nontemporal_store(load_stream(src + i), dst + i);
+}
+
+}  // namespace
+
+hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s) {
+    const bool vec = vec_ok(a.base, a.V, a.dtype ? 2 : 4);
+    dim3 grid(a.R), block(kThreads);
+    if (a.dtype == 1) {
+        if (vec) hipLaunchKernelGGL((rowstats_kernel<1, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((rowstats_kernel<1, false>), grid, block, 0, s, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((rowstats_kernel<0, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((rowstats_kernel<0, false>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_power_sums(const PowerSumArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(power_sums_kernel, dim3(a.R), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s) {
+    const size_t n = bytes / 16;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_probe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -121,6 +121,10 @@ def _softmax64(a: np.ndarray) -> np.ndarray:
 def _draft_sampler_cdf(zd_row: np.ndarray, T: float, top_k: int) -> np.ndarray:
     """Cumulative sum of the draft model's own sampling distribution (float64)."""
     V = zd_row.shape[0]
+    if T == 0.0:                        # greedy draft: its argmax
+        w = np.zeros(V, dtype=np.float64)
+        w[int(np.argmax(zd_row))] = 1.0
+        return np.cumsum(w)
     if T == 1.0 and not (0 < top_k < V):
         w = _softmax64(zd_row)
     else:

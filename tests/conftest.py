@@ -19,3 +19,12 @@ def orc():
     oracle.lib()
     yield oracle
     oracle.set_variant(0)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built_library():
+    """Build the HIP library in-tree if it is missing (normally built beforehand)."""
+    import rejection_sampling_verify_10_amd as R
+    if not os.path.exists(R.LIB_PATH):
+        from rejection_sampling_verify_10_amd import build
+        build.build()

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports what include/spec_verify.h declares, and rejects bad
+arguments on the host before touching a GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+EINVAL, EWORKSPACE, EUNSUPPORTED = -1, -2, -4
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    import rejection_sampling_verify_10_amd as R
+    if not os.path.exists(R.LIB_PATH):
+        from rejection_sampling_verify_10_amd import build
+        build.build()
+    return R.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(L):
+    names = declared_functions()
+    assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_accept_rate"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_error_strings(L):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert L.spec_error_string(code)
+
+
+def _chain(L, **kw):
+    a = dict(z=FAKE, dtype=1, q=FAKE, x=FAKE, u=FAKE, B=4, K=3, V=1000, T=1.0, top_k=0,
+             tok=FAKE, alen=FAKE, diag=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.spec_verify_chain(a["z"], a["dtype"], a["q"], a["x"], a["u"], a["B"], a["K"], a["V"], a["T"],
+                               a["top_k"], a["tok"], a["alen"], a["diag"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_chain_argument_checks(L):
+    assert _chain(L, B=0) == EINVAL
+    assert _chain(L, K=0) == EINVAL
+    assert _chain(L, V=0) == EINVAL
+    assert _chain(L, dtype=2) == EINVAL
+    assert _chain(L, T=-1.0) == EINVAL
+    assert _chain(L, T=float("inf")) == EINVAL
+    assert _chain(L, T=float("nan")) == EINVAL
+    assert _chain(L, z=None) == EINVAL
+    assert _chain(L, q=None) == EINVAL
+    assert _chain(L, u=None) == EINVAL
+    assert _chain(L, z=FAKE + 1) == EINVAL                  # bf16 rows need 2-byte alignment
+    assert _chain(L, K=64) == EUNSUPPORTED
+    assert _chain(L, V=(1 << 20) + 1) == EUNSUPPORTED
+    assert _chain(L, top_k=65, T=0.7) == EUNSUPPORTED
+    assert _chain(L, top_k=50, T=0.7, V=300000) == EUNSUPPORTED
+    assert _chain(L, wsb=16) == EWORKSPACE
+    assert _chain(L, ws=None) == EWORKSPACE
+    assert _chain(L, ws=FAKE + 8) == EWORKSPACE
+
+
+def test_tree_argument_checks(L):
+    par = (ctypes.c_int32 * 4)(-1, 0, 0, 1)
+    bad1 = (ctypes.c_int32 * 4)(0, 0, 0, 1)
+    bad2 = (ctypes.c_int32 * 4)(-1, 0, 3, 1)
+
+    def call(p, N=4, B=2, ws=FAKE, wsb=1 << 30):
+        return L.spec_verify_tree_greedy(FAKE, 1, FAKE, p, B, N, 1000, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert call(bad1) == EINVAL
+    assert call(bad2) == EINVAL
+    assert call(par, B=0) == EINVAL
+    assert call(par, wsb=8) == EWORKSPACE
+    big = (ctypes.c_int32 * 65)(*([-1] + list(range(64))))
+    assert call(big, N=65) == EUNSUPPORTED
+
+
+def test_accept_rate_argument_checks(L):
+    def call(**kw):
+        a = dict(z=FAKE, q=FAKE, B=2, K=3, V=1000, T=1.0, top_k=0, out=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return L.spec_accept_rate(a["z"], 1, a["q"], a["B"], a["K"], a["V"], a["T"], a["top_k"], a["out"],
+                                  a["ws"], a["wsb"], None)
+    assert call(q=None) == EINVAL
+    assert call(out=None) == EINVAL
+    assert call(K=0) == EINVAL
+    assert call(top_k=100, T=0.5) == EUNSUPPORTED
+    assert call(wsb=0) == EWORKSPACE
+
+
+def test_workspace_sizes(L):
+    import rejection_sampling_verify_10_amd as R
+    a = R.chain_workspace_bytes(64, 7, 128256, 1, 0.7, 50)
+    b = R.chain_workspace_bytes(128, 7, 128256, 1, 0.7, 50)
+    assert 0 < a < b and a % 256 == 0
+    assert R.chain_workspace_bytes(0, 7, 128256, 1, 0.7, 50) == 0
+    assert R.chain_workspace_bytes(8, 5, 32000, 1, 1.0, 0) > 0
+    assert R.chain_workspace_bytes(8, 5, 32000, 1, 0.0, 0) > 0
+    assert R.tree_workspace_bytes(32, 27, 32000, 1) > 0
+    assert R.accept_rate_workspace_bytes(8, 5, 32000, 1, 0.7, 50) > 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import rejection_sampling_verify_10_amd as R
+    z = torch.zeros(2, 4, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        R.verify_chain(z, torch.zeros(2, 3, 16), torch.zeros(2, 3, dtype=torch.int32),
+                       torch.zeros(2, 4), 1.0, 0)
+    with pytest.raises(ValueError):                       # shape mismatch caught before any launch
+        R.verify_chain(z, torch.zeros(2, 3, 15), torch.zeros(2, 3, dtype=torch.int32),
+                       torch.zeros(2, 4), 1.0, 0)

@@ -1,0 +1,170 @@
+"""Parity of spec_verify_chain (HIP, through the C ABI) with the CPU oracle."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from parity import compare_chain, log_tally, run_gpu_chain, run_oracle_chain, Tally
+from rejection_sampling_verify_10_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def R():
+    import torch
+    import rejection_sampling_verify_10_amd as R
+    assert torch.cuda.is_available(), "GPU test without a GPU"
+    R.lib()
+    return R
+
+
+def check(R, orc, ci, name, rows=None, diag=True):
+    print(f"[case] {name}: B={ci.B} K={ci.K} V={ci.V} dtype={ci.dtype} T={ci.temperature} top_k={ci.top_k}",
+          flush=True)
+    tok, alen, dg = run_gpu_chain(R, ci, diag=diag)[:3]
+    o = run_oracle_chain(orc, ci, rows)
+    t = compare_chain(o, tok, alen, dg, ci.K, greedy=ci.temperature == 0.0, rows=rows)
+    log_tally(name, t)
+    t.check()
+    return t, tok, alen
+
+
+# ------------------------------------------------------------------ the five workloads (chain ones)
+
+def test_workload0_fp32_v1000(R, orc):
+    """B=1, K=4, V=1000 fp32, T=1: 256 independent batch rows of the same recipe."""
+    total = Tally()
+    for seed in range(2):
+        t, _, _ = check(R, orc, W.config(0, seed, B=256), f"c0 seed {seed}")
+        total.add(t)
+    total.check()
+
+
+def test_workload1_bf16_v32000(R, orc):
+    for seed in range(3):
+        check(R, orc, W.config(1, seed), f"c1 seed {seed}")
+    check(R, orc, W.config(1, 9, B=64), "c1 B=64")
+
+
+def test_workload2_topk_reduced_batch(R, orc):
+    check(R, orc, W.config(2, 0, B=8), "c2 B=8")
+
+
+@pytest.mark.slow
+def test_workload2_topk_full(R, orc):
+    """B=64, K=7, V=128256, T=0.7, top_k=50: every batch row against the oracle."""
+    t, _, alen = check(R, orc, W.config(2, 1), "c2 full")
+    hist = np.bincount(alen[alen >= 0], minlength=8)
+    print(f"[c2] accept_len histogram {hist.tolist()}", flush=True)
+
+
+def test_workload4_reduced_batch(R, orc):
+    check(R, orc, W.config(4, 0, B=16), "c4 B=16")
+
+
+@pytest.mark.slow
+def test_workload4_full_sampled(R, orc):
+    """B=512, K=8, V=128256: the full launch, checked on 48 sampled batch rows."""
+    ci = W.config(4, 2)
+    rows = np.random.default_rng(5).choice(ci.B, 48, replace=False)
+    rows.sort()
+    t, _, alen = check(R, orc, ci, "c4 full (48 sampled rows)", rows=rows)
+    hist = np.bincount(alen[alen >= 0], minlength=9)
+    print(f"[c4] accept_len histogram {hist.tolist()}", flush=True)
+
+
+# ------------------------------------------------------------------ modes and shapes
+
+@pytest.mark.parametrize("T,top_k", [(0.0, 0), (0.5, 0), (1.7, 0), (1.0, 20), (0.7, 64), (1.3, 1)])
+def test_transforms(R, orc, T, top_k):
+    ci = W.with_transform(W.config(1, 4, B=6, V=4096), temperature=T, top_k=top_k)
+    check(R, orc, ci, f"transform T={T} k={top_k}")
+
+
+@pytest.mark.parametrize("V,dtype", [(1, 1), (3, 0), (7, 1), (1001, 1), (1001, 0), (5000, 0), (50257, 1),
+                                     (4096 * 3 + 8, 1)])
+@pytest.mark.parametrize("T,top_k", [(1.0, 0), (0.8, 0), (0.7, 5), (0.0, 0)])
+def test_ragged_vocab(R, orc, V, dtype, T, top_k):
+    """Vocabularies that are not a multiple of the 16-byte vector (scalar paths) or of a tile."""
+    base = W.make_chain(5, 3, V, dtype=dtype, temperature=T, top_k=top_k, sigma=W.sigma_const(0.7),
+                        config_id=90, seed=V)
+    check(R, orc, base, f"ragged V={V}")
+
+
+@pytest.mark.parametrize("K", [1, 2, 16, 63])
+def test_chain_lengths(R, orc, K):
+    ci = W.make_chain(4, K, 2048, dtype=W.DTYPE_BF16, temperature=1.0, top_k=0, sigma=W.sigma_const(0.3),
+                      config_id=91, seed=K)
+    check(R, orc, ci, f"K={K}")
+    ci2 = W.with_transform(ci, temperature=0.7, top_k=10)
+    check(R, orc, ci2, f"K={K} top-k")
+
+
+def test_ties_at_topk_boundary_and_argmax(R, orc):
+    """Coarsely rounded logits give many equal values at the k-th position and at the max."""
+    ci = W.config(2, 3, B=8, V=32000)
+    z = W.bf16_bits_to_f32(ci.logits)
+    zr = W.f32_to_bf16_bits(np.round(z * 2) / 2)
+    ci = dataclasses.replace(ci, logits=zr)
+    check(R, orc, ci, "ties top-k")
+    check(R, orc, W.with_transform(ci, temperature=0.0, top_k=0), "ties greedy")
+    check(R, orc, W.with_transform(ci, temperature=0.9, top_k=3), "ties top-3")
+
+
+def test_error_rows(R, orc):
+    ci = W.make_chain(10, 3, 1024, dtype=W.DTYPE_BF16, temperature=1.0, top_k=0, sigma=W.sigma_const(0.5),
+                      config_id=92, seed=0)
+    z = ci.logits.copy()
+    q = ci.draft_probs.copy()
+    x = ci.draft_tokens.copy()
+    u = ci.uniforms.copy()
+    z[1, 3, 17] = 0x7FC0             # NaN in row K (always read)
+    z[2, 0, 5] = 0x7F80              # +inf
+    z[3, 2, :] = 0xFF80              # a row of -inf
+    x[4, 1] = 1024                   # token out of range
+    u[5, 3] = 1.0                    # uniform out of range
+    q[6, 0, x[6, 0]] = np.nan        # gathered draft probability NaN
+    ci = dataclasses.replace(ci, logits=z, draft_probs=q, draft_tokens=x, uniforms=u)
+    for T, k in [(1.0, 0), (0.6, 0), (0.7, 8), (0.0, 0)]:
+        t, tok, alen = check(R, orc, W.with_transform(ci, temperature=T, top_k=k), f"errors T={T} k={k}")
+        assert alen[1] == -1
+        if T != 0.0:
+            assert np.all(alen[[1, 2, 3, 4, 5]] == -1)
+
+
+def test_zero_residual_falls_back_to_target(R, orc):
+    """q = 1.5 p' everywhere: a rejection leaves max(0, p' - q) = 0, so the draw uses p'."""
+    V, K, B = 512, 2, 64
+    rng = np.random.default_rng(7)
+    z = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    p = np.exp(z - z.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    q = (1.5 * p[:, :K]).astype(np.float32)
+    x = np.stack([[rng.choice(V, p=p[b, k]) for k in range(K)] for b in range(B)]).astype(np.int32)
+    u = rng.random((B, K + 1), dtype=np.float32)
+    ci = W.ChainInputs(B, K, V, W.DTYPE_F32, 1.0, 0, z, q, x, u, np.zeros(B))
+    t, _, alen = check(R, orc, ci, "zero residual")
+    assert np.any(alen < K)
+
+
+def test_draft_probability_zero_and_uniform_edges(R, orc):
+    ci = W.make_chain(16, 3, 777, dtype=W.DTYPE_F32, temperature=1.0, top_k=0, sigma=W.sigma_const(1.0),
+                      config_id=93, seed=0)
+    q = ci.draft_probs.copy()
+    u = ci.uniforms.copy()
+    for b in range(0, 16, 3):
+        q[b, 0, ci.draft_tokens[b, 0]] = 0.0       # q(x) = 0: accepted iff p'(x) > 0
+    u[1::4] = 0.0
+    u[2::4] = np.nextafter(np.float32(1), np.float32(0))
+    ci = dataclasses.replace(ci, draft_probs=q, uniforms=u)
+    check(R, orc, ci, "q(x)=0 and u edges")
+
+
+def test_deterministic(R, orc):
+    ci = W.config(2, 5, B=8)
+    a = run_gpu_chain(R, ci)
+    b = run_gpu_chain(R, ci)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y, equal_nan=True)

@@ -1,0 +1,123 @@
+"""Parity of spec_verify_tree_greedy and spec_accept_rate with the CPU oracle."""
+
+import dataclasses
+import itertools
+
+import numpy as np
+import pytest
+
+from parity import PROB_TOL, nan_equal_close, to_torch
+from rejection_sampling_verify_10_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def R():
+    import torch
+    import rejection_sampling_verify_10_amd as R
+    assert torch.cuda.is_available(), "GPU test without a GPU"
+    R.lib()
+    return R
+
+
+def run_tree(R, orc, ti, name):
+    import torch
+    print(f"[case] {name}: B={ti.B} N={ti.N} V={ti.V}", flush=True)
+    path, toks, alen = R.verify_tree_greedy(to_torch(ti.logits), to_torch(ti.node_tokens), ti.parents.tolist())
+    torch.cuda.synchronize()
+    path, toks, alen = path.cpu().numpy(), toks.cpu().numpy(), alen.cpu().numpy()
+    o = orc.verify_tree_greedy(ti.logits, ti.dtype, ti.node_tokens, ti.parents)
+    assert np.array_equal(alen, o["accept_len"]), name
+    assert np.array_equal(path, o["path"]), name
+    assert np.array_equal(toks, o["tokens"]), name
+    print(f"[tree] {name}: accepted depth histogram {np.bincount(alen[alen >= 0]).tolist()}", flush=True)
+    return alen
+
+
+def test_workload3_tree_full(R, orc):
+    """B=32, 27-node static tree (depth 5), V=32000 bf16: bit-exact paths, tokens, lengths."""
+    for seed in range(3):
+        run_tree(R, orc, W.config(3, seed), f"c3 seed {seed}")
+
+
+def test_tree_ties_and_small_vocab(R, orc):
+    ti = W.config(3, 7, B=16, V=5000)
+    z = W.bf16_bits_to_f32(ti.logits)
+    ti2 = dataclasses.replace(ti, logits=W.f32_to_bf16_bits(np.round(z)))     # many equal maxima
+    run_tree(R, orc, ti2, "tree ties")
+    rng = np.random.default_rng(3)
+    for parents in ([-1, 0, 0, 1, 1, 2], [-1, 0, 1, 2], [-1], list(range(-1, 63))):
+        parents = np.array(parents, np.int32)
+        N = len(parents)
+        V = 3
+        combos = list(itertools.islice(itertools.product(range(V), repeat=N - 1), 200))
+        B = len(combos)
+        assigns = np.array(combos, np.int32).reshape(B, N - 1)
+        z = np.round(rng.standard_normal((B, N, V)) * 2).astype(np.float32)
+        tok = np.concatenate([np.full((B, 1), -1, np.int32), assigns], 1)
+        run_tree(R, orc, W.TreeInputs(B, N, V, W.DTYPE_F32, z, tok, parents), f"tree N={N}")
+
+
+def test_tree_error_rows(R, orc):
+    ti = W.config(3, 1, B=6, V=1000)
+    z = ti.logits.copy()
+    tok = ti.node_tokens.copy()
+    z[1, 5, 3] = 0x7FC0
+    tok[2, 7] = 1000
+    tok[3, 4] = -5
+    alen = run_tree(R, orc, dataclasses.replace(ti, logits=z, node_tokens=tok), "tree errors")
+    assert np.all(alen[1:4] == -1)
+
+
+def run_alpha(R, orc, ci, name):
+    import torch
+    print(f"[case] {name}: B={ci.B} K={ci.K} V={ci.V} T={ci.temperature} top_k={ci.top_k}", flush=True)
+    a = R.accept_rate(to_torch(ci.logits), to_torch(ci.draft_probs), ci.temperature, ci.top_k)
+    torch.cuda.synchronize()
+    a = a.cpu().numpy()
+    o = orc.accept_rate(ci.logits, ci.dtype, ci.draft_probs, ci.temperature, ci.top_k)
+    nan_equal_close(a, o, PROB_TOL if ci.temperature != 0.0 else 0.0)
+    return a
+
+
+@pytest.mark.parametrize("cid,T,top_k", [(0, 1.0, 0), (1, 1.0, 0), (1, 0.0, 0), (1, 1.5, 0), (1, 0.7, 50),
+                                         (2, 0.7, 50), (4, 1.0, 0)])
+def test_accept_rate(R, orc, cid, T, top_k):
+    ci = W.config(cid, 0, B=(8 if cid in (2, 4) else None))
+    a = run_alpha(R, orc, W.with_transform(ci, temperature=T, top_k=top_k), f"alpha c{cid}")
+    assert np.all((a >= 0) & (a <= 1 + 1e-6))
+
+
+def test_accept_rate_ragged_and_errors(R, orc):
+    ci = W.make_chain(6, 3, 1001, dtype=W.DTYPE_BF16, temperature=1.0, top_k=0, sigma=W.sigma_const(0.5),
+                      config_id=94, seed=0)
+    z = ci.logits.copy()
+    q = ci.draft_probs.copy()
+    z[1, 0, 4] = 0x7FC0
+    q[2, 1, 9] = -1.0
+    ci = dataclasses.replace(ci, logits=z, draft_probs=q)
+    for T, k in [(1.0, 0), (0.8, 0), (0.7, 7), (0.0, 0)]:
+        a = run_alpha(R, orc, W.with_transform(ci, temperature=T, top_k=k), f"alpha ragged T={T} k={k}")
+        assert np.isnan(a[1, 0])
+
+
+def test_mean_accept_len_matches_alpha_products(R, orc):
+    """E[accept_len] = sum_k prod_{i<=k} alpha_i, from the GPU's own two entry points:
+    4096 calls' worth of rows of workload 0 drawn with fresh draft tokens and uniforms."""
+    import torch
+    ci = W.config(0, 11)
+    n = 4096
+    rng = np.random.default_rng(12)
+    K, V = ci.K, ci.V
+    z = np.ascontiguousarray(np.broadcast_to(ci.logits[0], (n, K + 1, V)))
+    q = np.ascontiguousarray(np.broadcast_to(ci.draft_probs[0], (n, K, V)))
+    x = np.stack([rng.choice(V, size=n, p=q[0, k].astype(np.float64) / q[0, k].astype(np.float64).sum())
+                  for k in range(K)], 1).astype(np.int32)
+    u = rng.random((n, K + 1), dtype=np.float32)
+    tok, alen = R.verify_chain(to_torch(z), to_torch(q), to_torch(x), to_torch(u), 1.0, 0)
+    alpha = R.accept_rate(to_torch(ci.logits[:1]), to_torch(ci.draft_probs[:1]), 1.0, 0)
+    torch.cuda.synchronize()
+    alen = alen.cpu().numpy()
+    expect = np.sum(np.cumprod(alpha.cpu().numpy()[0].astype(np.float64)))
+    assert abs(alen.mean() - expect) <= 4 * alen.std() / np.sqrt(n)
