@@ -75,6 +75,27 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int) -> floa
     return B * (K + 1) * V * 2 + B * (K + 1) * 24
 
 
+def copy_probe(R, torch, args) -> int:
+    """Plain device copy of 512 MiB per launch (bytes read = bytes written = 512 MiB)."""
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        R.copy_probe(src, dst)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        R.copy_probe(src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "us_per_launch": us,
+                      "GBps_read_plus_write": 2 * n / us / 1e3}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +104,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time the library's plain copy kernel on 512 MiB instead (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -96,8 +119,10 @@ def main() -> int:
     import rejection_sampling_verify_10_amd as R
     from rejection_sampling_verify_10_amd import workloads as W
 
-    wl = WORKLOADS[args.workload]
     R.lib()                                   # fails loudly without the HIP library
+    if args.copy_probe:
+        return copy_probe(R, torch, args)
+    wl = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
@@ -115,7 +140,7 @@ def main() -> int:
     sets = [base] + [[t.clone() for t in base] for _ in range(wl["copies"] - 1)]
     tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     alen = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = torch.empty(R.chain_workspace_bytes(B, K, V, ci.dtype, T, top_k) + 256, dtype=torch.uint8, device=dev)
+    ws = R.new_workspace(R.chain_workspace_bytes(B, K, V, ci.dtype, T, top_k), dev)
     in_bytes = sum(t.numel() * t.element_size() for t in base)
     log(f"{wl['copies']} input copies x {in_bytes / 1e6:.1f} MB resident")
 

@@ -24,8 +24,11 @@
  *     and the call returns without synchronising.  Inputs must stay valid and
  *     outputs must not be read until the stream has reached the call.
  *   - `workspace` is device scratch of at least the size reported by the
- *     matching *_workspace_bytes function, 256-byte aligned; it is used only
- *     during the call's kernels (no state is carried between calls).
+ *     matching *_workspace_bytes function, 256-byte aligned.  It must be
+ *     zero-filled before its first use (spec_workspace_init, or any zeroing
+ *     allocation); every call leaves it in that reusable state (its completion
+ *     counters return to zero), so zeroing once is enough.  A workspace serves
+ *     one call at a time: calls that may overlap need separate workspaces.
  *   - Logit rows are bfloat16 (SPEC_BF16, raw bits) or float32 (SPEC_F32).
  *     Draft probabilities are float32.  Uniforms are float32 in [0, 1).
  *   - Host-detectable argument errors return a negative code and launch
@@ -154,6 +157,10 @@ int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype,
 int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
                      int B, int K, int V, float temperature, int top_k,
                      float* out_alpha, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Zero-fills `workspace_bytes` (a multiple of 4) of a 256-byte aligned workspace
+ * with a fill kernel on hip_stream (no memset node, so it may be captured). */
+int spec_workspace_init(void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * Instrumentation.

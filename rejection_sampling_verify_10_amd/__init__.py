@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.spec_accept_rate.restype = I
         L.spec_profile_events.argtypes = [P, P]
         L.spec_profile_events.restype = I
+        L.spec_workspace_init.argtypes = [P, Z, P]
+        L.spec_workspace_init.restype = I
         L.spec_copy_probe.argtypes = [P, P, Z, P]
         L.spec_copy_probe.restype = I
         _lib = L
@@ -103,7 +105,7 @@ def _workspace(nbytes: int, device: torch.device,
         if given.numel() < nbytes + 256:
             raise ValueError(f"workspace needs {nbytes + 256} bytes, got {given.numel()}")
         return (given.data_ptr() + 255) // 256 * 256, given
-    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
     p = ws.data_ptr()
     return (p + 255) // 256 * 256, ws
 
@@ -129,8 +131,9 @@ def verify_chain(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor
     target_logits [B, K+1, V] bf16/f32, draft_probs [B, K, V] f32, draft_tokens [B, K] int32,
     uniforms [B, K+1] f32.  Returns (tokens [B, K+1] int32, accept_len [B] int32) and, with
     ``diag=True``, a third tensor [B, 2K+2] f32.  Asynchronous on the current stream.
-    ``out`` reuses output tensors; ``workspace`` (uint8, at least the size reported by
-    :func:`chain_workspace_bytes` + 256) avoids the per-call allocation.
+    ``out`` reuses output tensors; ``workspace`` (uint8, zero-filled before its first
+    use, at least the size reported by :func:`chain_workspace_bytes` + 256) avoids the
+    per-call allocation; calls leave it reusable.
     """
     B, K1, V = target_logits.shape
     K = K1 - 1
@@ -215,6 +218,11 @@ def accept_rate(target_logits: torch.Tensor, draft_probs: torch.Tensor, temperat
                                 float(temperature), int(top_k), alpha.data_ptr(), wp, need, _stream(dev))
     _check(rc, "spec_accept_rate")
     return alpha
+
+
+def new_workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A zero-filled workspace tensor for the ``workspace=`` argument."""
+    return torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
 
 
 def profile_next_call(start: torch.cuda.Event, stop: torch.cuda.Event) -> None:

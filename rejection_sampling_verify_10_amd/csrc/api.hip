@@ -55,33 +55,35 @@ RowStats carve_rowstats(Carver& c, size_t R) {
     return st;
 }
 
-struct TopkBufs {
-    int Ct, chunk_t, Cd, chunk_d;
-    float* vals;
-    int32_t* idx;
-    int32_t* cnt;
-    uint32_t* flags;
-    int32_t* row_idx;
-    double* row_p;
-    int32_t* row_cnt;
-    uint32_t* row_flags;
-};
-
-TopkBufs carve_topk(Carver& c, int dtype, int V, size_t Rt, size_t Rd) {
-    TopkBufs t;
+// Chunk lists for B batch rows of P positions, K of which carry a draft row.
+TopkLists carve_topk(Carver& c, int dtype, int V, int B, int P, int K, int top_k, float T) {
+    TopkLists t{};
     topk_chunking(V, esz_of(dtype), &t.Ct, &t.chunk_t);
     topk_chunking(V, 4, &t.Cd, &t.chunk_d);
-    const size_t units = Rt * t.Ct + Rd * t.Cd;
+    t.Ub = static_cast<long>(P) * t.Ct + static_cast<long>(K) * t.Cd;
+    const size_t units = static_cast<size_t>(B) * t.Ub;
     t.vals = c.take<float>(units * kTopkMax);
     t.idx = c.take<int32_t>(units * kTopkMax);
     t.cnt = c.take<int32_t>(units);
     t.flags = c.take<uint32_t>(units);
-    const size_t rows = Rt + Rd;
-    t.row_idx = c.take<int32_t>(rows * kTopkMax);
-    t.row_p = c.take<double>(rows * kTopkMax);
-    t.row_cnt = c.take<int32_t>(rows);
-    t.row_flags = c.take<uint32_t>(rows);
+    t.top_k = top_k;
+    t.draft_identity = (T == 1.f) ? 1 : 0;
+    t.invT = T > 0.f ? 1.0 / static_cast<double>(T) : 0.0;
     return t;
+}
+
+TopkChunkArgs topk_chunk_args(const void* target, const float* draft, int dtype, int B, int K, int V, int P,
+                              const TopkLists& t) {
+    TopkChunkArgs a{};
+    a.target = target;
+    a.draft = draft;
+    a.dtype = dtype;
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.P = P;
+    a.l = t;
+    return a;
 }
 
 // Chunks per row must fit the row-merge kernel (<= 16).
@@ -115,7 +117,8 @@ struct ChainPlan {
     RowStats st;
     double* qsum;
     uint32_t* qflags;
-    TopkBufs tk;
+    TopkLists tk;
+    PosRecord* rec;
 };
 
 ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {
@@ -126,7 +129,8 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
         p.st = carve_rowstats(c, Rt);
     } else if (topk_active(top_k, V)) {
         p.mode = 1;
-        p.tk = carve_topk(c, dtype, V, Rt, Rd);
+        p.tk = carve_topk(c, dtype, V, B, K + 1, K, top_k, T);
+        p.rec = c.take<PosRecord>(Rt);
     } else {
         p.mode = 0;
         p.st = carve_rowstats(c, Rt);
@@ -135,6 +139,7 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
             p.qflags = c.take<uint32_t>(Rd);
         }
     }
+    (void)Rd;
     return p;
 }
 
@@ -143,7 +148,7 @@ struct AlphaPlan {
     RowStats st, qst;
     double* qsum;
     uint32_t* qflags;
-    TopkBufs tk;
+    TopkLists tk;
 };
 
 AlphaPlan plan_alpha(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {
@@ -155,7 +160,7 @@ AlphaPlan plan_alpha(Carver& c, int B, int K, int V, int dtype, float T, int top
         p.qst = carve_rowstats(c, R);
     } else if (topk_active(top_k, V)) {
         p.mode = 1;
-        p.tk = carve_topk(c, dtype, V, R, R);
+        p.tk = carve_topk(c, dtype, V, B, K, K, top_k, T);
     } else {
         p.mode = 0;
         p.st = carve_rowstats(c, R);
@@ -185,49 +190,6 @@ RowStatsArgs rowstats_args(const void* base, int dtype, int V, int rows_per_batc
     return a;
 }
 
-TopkChunkArgs topk_chunk_args(const void* target, const float* draft, int dtype, int V, int top_k, int Rt,
-                              int rows_per_batch, int batch_stride, int Rd, const TopkBufs& t) {
-    TopkChunkArgs a{};
-    a.target = target;
-    a.draft = draft;
-    a.dtype = dtype;
-    a.V = V;
-    a.top_k = top_k;
-    a.Rt = Rt;
-    a.Ct = t.Ct;
-    a.chunk_t = t.chunk_t;
-    a.Rd = Rd;
-    a.Cd = t.Cd;
-    a.chunk_d = t.chunk_d;
-    a.target_rows_per_batch = rows_per_batch;
-    a.target_batch_stride = batch_stride;
-    a.vals = t.vals;
-    a.idx = t.idx;
-    a.cnt = t.cnt;
-    a.flags = t.flags;
-    return a;
-}
-
-TopkRowsArgs topk_rows_args(const TopkBufs& t, int Rt, int Rd, int top_k, float T) {
-    TopkRowsArgs a{};
-    a.chunk_vals = t.vals;
-    a.chunk_idx = t.idx;
-    a.chunk_cnt = t.cnt;
-    a.chunk_flags = t.flags;
-    a.Rt = Rt;
-    a.Ct = t.Ct;
-    a.Rd = Rd;
-    a.Cd = t.Cd;
-    a.top_k = top_k;
-    a.invT = 1.0 / static_cast<double>(T);
-    a.draft_identity = (T == 1.f) ? 1 : 0;
-    a.row_idx = t.row_idx;
-    a.row_p = t.row_p;
-    a.row_cnt = t.row_cnt;
-    a.row_flags = t.row_flags;
-    return a;
-}
-
 #define SV_TRY(expr)                                  \
     do {                                              \
         if ((expr) != hipSuccess) return SPEC_ELAUNCH; \
@@ -249,8 +211,6 @@ const char* spec_error_string(int code) {
 }
 
 size_t spec_chain_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k) {
-    int dummy;
-    (void)dummy;
     if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return 0;
     if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || !(temperature >= 0.f) || isinf(temperature)) return 0;
     Carver c(nullptr);
@@ -323,16 +283,12 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
         prof.after();
         SV_TRY(launch_chain_greedy(ca, s));
     } else if (p.mode == 1) {
-        const int Rt = B * (K + 1), Rd = B * K;
-        TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, V, top_k, Rt, K + 1, K + 1, Rd, p.tk);
+        TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K + 1, p.tk);
         prof.before();
         SV_TRY(launch_topk_chunks(ta, s));
         prof.after();
-        SV_TRY(launch_topk_rows(topk_rows_args(p.tk, Rt, Rd, top_k, temperature), s));
-        ca.row_idx = p.tk.row_idx;
-        ca.row_p = p.tk.row_p;
-        ca.row_cnt = p.tk.row_cnt;
-        ca.row_flags = p.tk.row_flags;
+        ca.tk = p.tk;
+        ca.rec = p.rec;
         SV_TRY(launch_chain_topk(ca, s));
     } else {
         ca.st = p.st;
@@ -429,6 +385,7 @@ int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float*
     aa.V = V;
     aa.scale = greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
     aa.invT = greedy ? 0.f : static_cast<float>(1.0 / static_cast<double>(temperature));
+    aa.T = temperature;
     aa.transformed = (!greedy && temperature != 1.f) ? 1 : 0;
     aa.out_alpha = out_alpha;
     if (p.mode == 2) {
@@ -440,16 +397,11 @@ int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float*
         aa.qst = p.qst;
         SV_TRY(launch_alpha_greedy(aa, s));
     } else if (p.mode == 1) {
-        const int R = B * K;
-        TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, V, top_k, R, K, K + 1, R, p.tk);
+        TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K, p.tk);
         prof.before();
         SV_TRY(launch_topk_chunks(ta, s));
         prof.after();
-        SV_TRY(launch_topk_rows(topk_rows_args(p.tk, R, R, top_k, temperature), s));
-        aa.row_idx = p.tk.row_idx;
-        aa.row_p = p.tk.row_p;
-        aa.row_cnt = p.tk.row_cnt;
-        aa.row_flags = p.tk.row_flags;
+        aa.tk = p.tk;
         SV_TRY(launch_alpha_topk(aa, s));
     } else {
         prof.before();
@@ -471,6 +423,13 @@ int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float*
 int spec_profile_events(void* start_event, void* stop_event) {
     t_prof_start = static_cast<hipEvent_t>(start_event);
     t_prof_stop = static_cast<hipEvent_t>(stop_event);
+    return SPEC_OK;
+}
+
+int spec_workspace_init(void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes % 4 != 0) return SPEC_EINVAL;
+    if (launch_zero_fill(workspace, workspace_bytes, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return SPEC_ELAUNCH;
     return SPEC_OK;
 }
 

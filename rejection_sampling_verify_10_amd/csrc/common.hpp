@@ -40,25 +40,80 @@ template <> struct Elem<1> {
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
+// Value of lane (lane ^ j) for j in {1, 2, 4, 8, 16, 32}, on the VALU: DPP quad
+// permutes (1, 2), row shifts (4), a row rotate (8) and the gfx950 lane-swap
+// instructions (16, 32).  All 64 lanes must be active.  j must fold to a
+// constant (the networks below are fully unrolled).
+__device__ __forceinline__ int xshfl_i(int v, int j) {
+    const int lane = threadIdx.x & 63;
+    switch (j) {
+        case 1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);     // quad_perm [1,0,3,2]
+        case 2: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);     // quad_perm [2,3,0,1]
+        case 4: {
+            const int up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, false);  // row_shl:4
+            const int dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
+            return (lane & 4) ? dn : up;
+        }
+        case 8: return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);    // row_ror:8
+        case 16: {
+            const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+            return (lane & 16) ? static_cast<int>(r[0]) : static_cast<int>(r[1]);
+        }
+        default: {
+            const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+            return (lane & 32) ? static_cast<int>(r[0]) : static_cast<int>(r[1]);
+        }
+    }
+}
+__device__ __forceinline__ unsigned xshfl(unsigned v, int j) { return static_cast<unsigned>(xshfl_i(static_cast<int>(v), j)); }
+__device__ __forceinline__ int xshfl(int v, int j) { return xshfl_i(v, j); }
+__device__ __forceinline__ float xshfl(float v, int j) { return __int_as_float(xshfl_i(__float_as_int(v), j)); }
+__device__ __forceinline__ double xshfl(double v, int j) {
+    const long long b = __double_as_longlong(v);
+    const int lo = xshfl_i(static_cast<int>(b), j);
+    const int hi = xshfl_i(static_cast<int>(b >> 32), j);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+// Value of lane 63 - lane (the wave reversed): xor 63 composed of the steps above.
+template <typename T> __device__ __forceinline__ T xrev(T v) {
+#pragma unroll
+    for (int j = 1; j < 64; j <<= 1) v = xshfl(v, j);
+    return v;
+}
+// Broadcast from a wave-uniform lane (v_readlane).
+__device__ __forceinline__ int bcast(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float bcast(float v, int lane) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane)); }
+__device__ __forceinline__ double bcast(double v, int lane) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
 // Wave-wide reductions (all lanes receive the result).
 template <typename T> __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    for (int o = 32; o > 0; o >>= 1) v += xshfl(v, o);
     return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, xshfl(v, o));
     return v;
 }
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, xshfl(v, o));
+    return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, xshfl(v, o));
     return v;
 }
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+    for (int o = 32; o > 0; o >>= 1) v |= xshfl(v, o);
     return v;
 }
 
@@ -82,8 +137,8 @@ __device__ __forceinline__ bool precedes(float va, int ia, float vb, int ib) {
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        float ov = __shfl_xor(v, o, kWave);
-        int oi = __shfl_xor(i, o, kWave);
+        float ov = xshfl(v, o);
+        int oi = xshfl(i, o);
         if (precedes(ov, oi, v, i)) { v = ov; i = oi; }
     }
 }
@@ -95,7 +150,7 @@ __device__ __forceinline__ float wave_sort_desc(float v) {
     for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            float o = __shfl_xor(v, j, kWave);
+            float o = xshfl(v, j);
             // descending overall: block direction flips with (lane & k)
             bool up = ((lane & k) == 0);
             bool lower = ((lane & j) == 0);
@@ -104,6 +159,68 @@ __device__ __forceinline__ float wave_sort_desc(float v) {
         }
     }
     return v;
+}
+
+}  // namespace sv
+
+namespace sv {
+
+// ---- wave-level bitonic networks over (value, index) pairs, one pair per lane ----
+//
+// Order: larger value first, lower index on equal values (a strict total order
+// for distinct indices).  Empty slots hold (-inf, kNoIndex) and sort last.
+
+constexpr int kNoIndex = 0x7fffffff;
+
+__device__ __forceinline__ float maximum3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);   // NaN-propagating
+}
+__device__ __forceinline__ float minimum3(float a, float b, float c) {
+    return __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c);
+}
+
+// Keeps in this lane the first (keep_first) or the second of {mine, lane^j's}.
+__device__ __forceinline__ void cx_pair(float& v, int& i, int j, bool keep_first) {
+    const float ov = xshfl(v, j);
+    const int oi = xshfl(i, j);
+    const bool mine = precedes(v, i, ov, oi);
+    if (keep_first ? !mine : mine) { v = ov; i = oi; }
+}
+
+// Full sort of the 64 pairs of the wave (lane 0 = first).
+__device__ __forceinline__ void wave_sort_pairs(float& v, int& i) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const bool up = (lane & k) == 0 || k == kWave;
+            cx_pair(v, i, j, ((lane & j) == 0) == up);
+        }
+    }
+}
+
+// (v,i) and (w,wi) each sorted (lane 0 first): leaves in (v,i) the first 64 of their
+// union, sorted.  Pairing lane l of one list with lane 63-l of the other gives a
+// bitonic sequence holding the 64 winners; a bitonic merge sorts it.
+__device__ __forceinline__ void wave_merge_pairs(float& v, int& i, float w, int wi) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float rw = xrev(w);
+    const int ri = xrev(wi);
+    if (!precedes(v, i, rw, ri)) { v = rw; i = ri; }
+#pragma unroll
+    for (int j = kWave >> 1; j > 0; j >>= 1) cx_pair(v, i, j, (lane & j) == 0);
+}
+
+// Values only, descending.
+__device__ __forceinline__ void wave_merge_desc(float& v, float w) {
+    const int lane = threadIdx.x & (kWave - 1);
+    v = fmaxf(v, xrev(w));
+#pragma unroll
+    for (int j = kWave >> 1; j > 0; j >>= 1) {
+        const float o = xshfl(v, j);
+        v = ((lane & j) == 0) ? fmaxf(v, o) : fminf(v, o);
+    }
 }
 
 }  // namespace sv

@@ -40,34 +40,40 @@ struct PowerSumArgs {       // sum_i q_i^(1/T) per draft row (transformed dense 
     uint32_t* flags;        // [R]
 };
 
-struct TopkChunkArgs {
-    const void* target;     // [Rt][V] dtype
-    const float* draft;     // [Rd][V] f32 (may be null when Rd == 0)
-    int dtype;
-    int V;
-    int top_k;
-    int Rt, Ct, chunk_t;    // target rows, chunks per target row, elements per target chunk
-    int Rd, Cd, chunk_d;
-    int target_rows_per_batch, target_batch_stride;   // maps row index -> memory row
-    float* vals;            // [units][kTopkMax]
-    int32_t* idx;           // [units][kTopkMax]
+// Sorted per-chunk top-k lists (topk.hip).  Units are ordered by batch row b,
+// then position k; position k owns Ct target chunks followed, when k has a
+// draft row, by Cd draft chunks: unit_base(b, k) = b*Ub + k*(Ct + Cd).
+struct TopkLists {
+    float* vals;            // [units][kTopkMax], entries past cnt are ignored
+    int32_t* idx;
     int32_t* cnt;           // [units]
-    uint32_t* flags;        // [units]
+    uint32_t* flags;
+    int Ct, Cd;             // chunks per target / draft row
+    int chunk_t, chunk_d;   // elements per target / draft chunk
+    long Ub;                // units per batch row
+    int top_k;
+    int draft_identity;     // T == 1: q^(1/T) = q exactly
+    double invT;
+    __host__ __device__ long unit_base(int b, int k) const {
+        return static_cast<long>(b) * Ub + static_cast<long>(k) * (Ct + Cd);
+    }
 };
 
-struct TopkRowsArgs {
-    const float* chunk_vals;
-    const int32_t* chunk_idx;
-    const int32_t* chunk_cnt;
-    const uint32_t* chunk_flags;
-    int Rt, Ct, Rd, Cd;
-    int top_k;
-    double invT;
-    int draft_identity;     // T == 1: q^(1/T) = q exactly
-    int32_t* row_idx;       // [rows][kTopkMax], index-ascending
-    double* row_p;          // [rows][kTopkMax]
-    int32_t* row_cnt;       // [rows]
-    uint32_t* row_flags;    // [rows]
+// Result of one position of a chain (top-k path): written by the position's
+// workgroup, read by the per-batch-row combine kernel.
+struct PosRecord {
+    int32_t accept, y, bad, pad;
+    float pk, qk, S, py;
+};
+
+// One launch of the top-k selection: B batch rows of P positions (K+1 for a
+// chain, K for the acceptance rate); positions k < K carry a draft row.
+struct TopkChunkArgs {
+    const void* target;     // logits [B][K+1][V] (dtype)
+    const float* draft;     // [B][K][V]
+    int dtype;
+    int B, K, V, P;
+    TopkLists l;
 };
 
 struct ChainArgs {
@@ -82,11 +88,8 @@ struct ChainArgs {
     RowStats st;            // dense / greedy statistics for rows b*(K+1)+k
     const double* qsum;     // dense transformed: [B*K] sum q^(1/T) (fp32-accurate)
     const uint32_t* qflags;
-    // top-k path
-    const int32_t* row_idx;
-    const double* row_p;
-    const int32_t* row_cnt;
-    const uint32_t* row_flags;
+    TopkLists tk;           // top-k path
+    PosRecord* rec;         // [B][K+1]
     int32_t* out_tokens;
     int32_t* out_accept_len;
     float* out_diag;
@@ -109,15 +112,13 @@ struct AlphaArgs {
     int B, K, V;
     float scale;            // log2(e)/T
     float invT;
+    double T;
     int transformed;
     RowStats st;            // target rows (b, k<K), dense or argmax
     RowStats qst;           // greedy: argmax of draft rows
     const double* qsum;
     const uint32_t* qflags;
-    const int32_t* row_idx;
-    const double* row_p;
-    const int32_t* row_cnt;
-    const uint32_t* row_flags;
+    TopkLists tk;
     float* out_alpha;
 };
 
@@ -130,15 +131,15 @@ inline bool vec_ok(const void* p, int V, int esz) {
 hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s);
 hipError_t launch_power_sums(const PowerSumArgs& a, hipStream_t s);
 hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s);
-hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s);
+hipError_t launch_chain_topk(const ChainArgs& a, hipStream_t s);   // positions + combine
+hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_chain_dense(const ChainArgs& a, hipStream_t s);
-hipError_t launch_chain_topk(const ChainArgs& a, hipStream_t s);
 hipError_t launch_chain_greedy(const ChainArgs& a, hipStream_t s);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t s);
 hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s);
-hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_alpha_greedy(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
 
 // Chunking of a row for the top-k selection kernel: chunks of at most
 // kChunkBytes, equal sizes rounded up to whole 16-byte vectors.

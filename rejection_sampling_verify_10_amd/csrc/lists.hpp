@@ -1,0 +1,127 @@
+// Wave-level operations on the sorted per-chunk top-k lists: merge a row's
+// chunk lists, turn the kept values into the transformed distribution, look
+// tokens up and draw by inverse CDF in index order.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace sv {
+
+__device__ __forceinline__ bool u_ok(float u) { return u >= 0.f && u < 1.f; }
+__device__ __forceinline__ bool q_ok(float v) { return v >= 0.f && v < INFINITY; }
+
+constexpr int kMaxRowChunks = 16;
+
+// Merges the C (<= 16) sorted chunk lists of a row (workspace units unit0 ..
+// unit0+C-1): lane l ends with the l-th ranked (value, index) of their union.
+// Every load is issued before any count is used (a list owns all kTopkMax
+// slots); a pairwise tree keeps the merges of one level independent.  Returns
+// the total number of entries; flags collects the chunks' flags.
+__device__ __forceinline__ int merge_global_lists(const TopkLists& t, long unit0, int C, float& v, int& i,
+                                                  uint32_t& flags) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float w[kMaxRowChunks];
+    int wi[kMaxRowChunks];
+    int n[kMaxRowChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxRowChunks; ++c) {
+        if (c < C) {
+            const long u = unit0 + c;
+            n[c] = t.cnt[u];
+            flags |= t.flags[u];
+            w[c] = t.vals[u * kTopkMax + lane];
+            wi[c] = t.idx[u * kTopkMax + lane];
+        }
+    }
+    int total = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxRowChunks; ++c) {
+        if (c < C) {
+            total += n[c];
+            if (lane >= n[c]) { w[c] = -INFINITY; wi[c] = kNoIndex; }
+        }
+    }
+#pragma unroll
+    for (int step = 1; step < kMaxRowChunks; step <<= 1) {
+#pragma unroll
+        for (int c = 0; c + step < kMaxRowChunks; c += 2 * step)
+            if (c + step < C) wave_merge_pairs(w[c], wi[c], w[c + step], wi[c + step]);
+    }
+    v = w[0];
+    i = wi[0];
+    return total;
+}
+
+// Sorts (index, probability) pairs by index ascending (empty lanes carry kNoIndex).
+__device__ __forceinline__ void wave_sort_by_index(int& i, double& p) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int oi = xshfl(i, j);
+            const double op = xshfl(p, j);
+            const bool up = (lane & k) == 0 || k == kWave;
+            const bool keep_small = ((lane & j) == 0) == up;
+            if (keep_small ? (oi < i) : (oi > i)) { i = oi; p = op; }
+        }
+    }
+}
+
+// From a row's ranked top entries (lane l = l-th, kk kept) to its transformed
+// distribution in index order: p' = softmax(z/T) over the kept logits (target)
+// or q' = q^(1/T) renormalised over the kept probabilities (draft).  Returns
+// false when the row is unusable (E1 / E3 / E4).
+__device__ __forceinline__ bool kept_distribution(float v, int idx_in, int kk, bool valid, bool draft,
+                                                  double invT, bool identity, int& idx, double& p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float v0 = bcast(v, 0);
+    const bool have = lane < kk;
+    double w = 0.0;
+    bool ok = valid && kk > 0;
+    if (!draft) {
+        ok = ok && v0 > -INFINITY && v0 < INFINITY;
+        if (have) w = exp((static_cast<double>(v) - static_cast<double>(v0)) * invT);
+    } else {
+        ok = ok && v0 < INFINITY;
+        if (have && v > 0.f) w = identity ? static_cast<double>(v) : pow(static_cast<double>(v), invT);
+    }
+    const double Z = wave_sum(w);
+    ok = ok && Z > 0.0 && Z < INFINITY;
+    p = have ? w / Z : 0.0;
+    idx = have ? idx_in : kNoIndex;
+    wave_sort_by_index(idx, p);
+    return ok;
+}
+
+// Probability of token x in an index-sorted list held one entry per lane.
+__device__ __forceinline__ double lane_lookup(int idx, double p, int x) {
+    const unsigned long long m = __ballot(idx == x);
+    if (!m) return 0.0;
+    return bcast(p, __ffsll(static_cast<long long>(m)) - 1);
+}
+
+// Probability of token x in an index-sorted LDS list of n entries (0 if absent).
+__device__ __forceinline__ double lds_lookup(const int* sidx, const double* sp, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sidx[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return (lo < n && sidx[lo] == x) ? sp[lo] : 0.0;
+}
+
+// Inverse-CDF draw over an index-sorted list of weights r (one per lane) with
+// target u*S: first lane whose inclusive prefix exceeds the target; rounding
+// fallback = last lane with a positive weight.  Returns the lane.
+__device__ __forceinline__ int lane_draw(double r, bool have, double target) {
+    const double C = wave_inclusive_scan(r);
+    const unsigned long long hit = __ballot(have && r > 0.0 && target < C);
+    if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
+    const unsigned long long pos = __ballot(have && r > 0.0);
+    return pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+}
+
+}  // namespace sv

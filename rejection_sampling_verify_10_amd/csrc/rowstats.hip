@@ -227,7 +227,23 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* __restrict
         __builtin_nontemporal_store(load_stream(src + i), dst + i);
 }
 
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* __restrict__ dst, size_t n) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        dst[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s) {
+    const size_t n = bytes / 4;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(dst), n);
+    return hipGetLastError();
+}
 
 hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s) {
     const bool vec = vec_ok(a.base, a.V, a.dtype ? 2 : 4);

@@ -1,4 +1,4 @@
-// Exact top-k of logit rows and draft-probability rows.
+// Exact top-k of logit rows and draft-probability rows: per-chunk selection.
 //
 // The sampling transforms must be applied to both distributions before the
 // ratio test ("064 · 投机解码", section 二).  Top-k keeps exactly k entries,
@@ -6,23 +6,24 @@
 // (z/T for logits, q^(1/T) for probabilities), so the kept set is selected on
 // the raw values and only the k survivors are ever exponentiated.
 //
-// Stage 1 (topk_chunk_kernel): each workgroup owns one <= 64 KiB chunk of a
-// row and holds it in registers (16 x 16-byte vectors per thread).
-//   - Every thread keeps the maximum of each of its vectors.
-//   - tau = the smallest, over the 4 waves, of each wave's ceil(k/4)-th
-//     largest thread maximum.  At least k distinct elements (those maxima) are
-//     >= tau, so every element of the chunk's top-k is >= tau.
-//   - Elements >= tau (typically ~1.5k of 16-32k) go to an LDS list; each
-//     candidate's rank is the number of candidates that precede it, which
-//     writes the chunk's top-k already sorted.  A list that overflows the LDS
-//     capacity (heavy ties, -inf rows) takes an exact bisection on the value
-//     order plus an index-ordered scan of the tied values instead.
-// Stage 2 (topk_rows_kernel): one workgroup per row merges its chunks' sorted
-// lists by rank (binary search in the other lists), applies the transform to
-// the k survivors in fp64 and writes (index, probability) sorted by index.
+// topk_chunk_kernel: one workgroup per <= 64 KiB chunk of a target or draft row,
+// held in registers (16 x 16-byte non-temporal vectors per thread).  Per chunk:
+//   - Per vector, a NaN-propagating maximum (v_maximum3_f32): 1.5 VALU ops per
+//     bf16 element, 0.5 per fp32 element; the thread maximum carries NaN.
+//   - tau = the exact k-th largest of the 256 thread maxima (each wave sorts
+//     its 64 maxima; every wave merges the four sorted lists).  At least k
+//     distinct elements (those maxima) are >= tau, so the chunk's top-k are.
+//   - Elements >= tau (about k + 10 of 16-32k) go to LDS; one wave sorts them
+//     with a bitonic network, 64 at a time, merging blocks if there are more.
+//     A list that overflows LDS (heavy ties, -inf rows) switches to an exact
+//     bisection on the value order plus an index-ordered scan of the ties.
+// Chunk lists go to the workspace, units ordered by batch row and position
+// (position k: Ct target chunks, then Cd draft chunks when k has a draft row),
+// and the verification kernels merge them.  No workgroup waits for another.
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "lists.hpp"
 
 namespace sv {
 
@@ -33,13 +34,18 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kSlots = 16;
 constexpr int kCap = 1024;
 
+constexpr int kStage = kWave;             // staged (lane, vector) pairs per wave
+
 struct ChunkSmem {
-    float cv[kCap];
+    float cv[kCap];                      // candidates of the chunk
     int32_t ci[kCap];
-    float tau[kWaves];
+    uint32_t tkey[kThreads];             // ordered keys of the thread maxima
+    u32x4 stage[kWaves][kStage];         // vectors whose maximum reaches tau
+    int32_t stage_vi[kWaves][kStage];
     int32_t red[kWaves];
     int32_t cnt;
-    uint32_t flags;
+    uint32_t flags, overflow;
+    float tau;
 };
 
 __device__ __forceinline__ uint32_t ordered_key(float v) {
@@ -47,6 +53,9 @@ __device__ __forceinline__ uint32_t ordered_key(float v) {
     if (v == 0.f) v = 0.f;                 // -0 and +0 are equal values
     const uint32_t b = __float_as_uint(v);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 __device__ __forceinline__ int block_sum(int v, ChunkSmem& sm) {
@@ -60,7 +69,7 @@ __device__ __forceinline__ int block_sum(int v, ChunkSmem& sm) {
     return t;
 }
 
-// Exclusive prefix of v over the threads of the block; returns the block total in *total.
+// Exclusive prefix of v over the threads of the block; the block total in *total.
 __device__ __forceinline__ int block_exclusive(int v, ChunkSmem& sm, int* total) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     int incl = v;
@@ -82,36 +91,14 @@ __device__ __forceinline__ int block_exclusive(int v, ChunkSmem& sm, int* total)
     return before + incl - v;
 }
 
-template <int DT, bool VEC>
-__device__ __forceinline__ u32x4 load_slot(const char* row, long e0, long end) {
-    using E = Elem<DT>;
-    if (VEC) return load_stream(reinterpret_cast<const u32x4*>(row + e0 * E::kBytes));
-    u32x4 v;
-    if (DT == 1) {
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(row);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = (e0 + 2 * w < end) ? h[e0 + 2 * w] : 0xff80u;
-            const uint32_t hi = (e0 + 2 * w + 1 < end) ? h[e0 + 2 * w + 1] : 0xff80u;
-            v[w] = lo | (hi << 16);
-        }
-    } else {
-        const uint32_t* f = reinterpret_cast<const uint32_t*>(row);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) v[w] = (e0 + w < end) ? f[e0 + w] : 0xff800000u;
-    }
-    return v;
-}
-
 __device__ __forceinline__ float load_elem(const char* row, int dt, long i) {
     return dt ? Elem<1>::scalar(row, i) : Elem<0>::scalar(row, i);
 }
 
-// Exact top-k candidates of a chunk when the tau filter lets too many through
-// (heavy ties, -inf rows): bisection for the k-th largest value in the total
-// order, then every larger element plus the lowest-index elements equal to it.
-// Re-reads the chunk from memory; leaves the candidates in sm and returns
-// their number (<= top_k).
+// Exact candidates when the tau filter lets too many through: bisection for the
+// k-th largest value in the total order, then every larger element plus the
+// lowest-index elements equal to it.  Re-reads the chunk; leaves the candidates
+// in sm and returns their number (<= top_k).
 __device__ __noinline__ int chunk_exact(const char* row, int dt, long start, int len, int top_k, ChunkSmem& sm) {
     const int tid = threadIdx.x;
     uint32_t lo = 0u, hi = 0xffffffffu;
@@ -159,84 +146,194 @@ __device__ __noinline__ int chunk_exact(const char* row, int dt, long start, int
     return sm.cnt;
 }
 
-// Selects the chunk's top-k; writes the sorted list to (ov, oi) and returns the count.
 template <int DT, bool VEC>
-__device__ __forceinline__ void chunk_topk(const char* row, long start, int len, int top_k, bool is_draft, float* ov,
-                           int32_t* oi, int32_t* ocnt, uint32_t* oflag, ChunkSmem& sm) {
+__device__ __forceinline__ u32x4 load_slot(const char* row, long e0, long end) {
+    using E = Elem<DT>;
+    if (VEC) return load_stream(reinterpret_cast<const u32x4*>(row + e0 * E::kBytes));
+    u32x4 v;
+    if (DT == 1) {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(row);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = (e0 + 2 * w < end) ? h[e0 + 2 * w] : 0xff80u;
+            const uint32_t hi = (e0 + 2 * w + 1 < end) ? h[e0 + 2 * w + 1] : 0xff80u;
+            v[w] = lo | (hi << 16);
+        }
+    } else {
+        const uint32_t* f = reinterpret_cast<const uint32_t*>(row);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v[w] = (e0 + w < end) ? f[e0 + w] : 0xff800000u;
+    }
+    return v;
+}
+
+// Maximum (NaN-propagating) of one 16-byte vector.
+template <int DT>
+__device__ __forceinline__ float vec_max(const u32x4& d) {
+    if (DT == 1) {
+        const float a = bf16_lo(d[0]), b = bf16_hi(d[0]), c = bf16_lo(d[1]), e = bf16_hi(d[1]);
+        const float f = bf16_lo(d[2]), g = bf16_hi(d[2]), h = bf16_lo(d[3]), k = bf16_hi(d[3]);
+        return maximum3(maximum3(a, b, c), maximum3(e, f, g), __builtin_elementwise_maximum(h, k));
+    }
+    return maximum3(__uint_as_float(d[0]), __uint_as_float(d[1]),
+                    __builtin_elementwise_maximum(__uint_as_float(d[2]), __uint_as_float(d[3])));
+}
+__device__ __forceinline__ float vec_min_f32(const u32x4& d) {
+    return minimum3(__uint_as_float(d[0]), __uint_as_float(d[1]),
+                    __builtin_elementwise_minimum(__uint_as_float(d[2]), __uint_as_float(d[3])));
+}
+
+// Loads one chunk (len elements from `start`) into registers: vector vi = s*256 + tid.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_chunk(const char* row, long start, int len, u32x4 (&d)[kSlots]) {
+    using E = Elem<DT>;
+    constexpr int EPV = E::kPerVec;
+    const u32x4* vbase = reinterpret_cast<const u32x4*>(row + start * E::kBytes);
+    const int nvec = (len + EPV - 1) / EPV;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        const int vi = s * kThreads + static_cast<int>(threadIdx.x);
+        d[s] = u32x4{0u, 0u, 0u, 0u};
+        if (vi < nvec)
+            d[s] = VEC ? load_stream(vbase + vi)
+                       : load_slot<DT, false>(row, start + static_cast<long>(vi) * EPV, start + len);
+    }
+}
+
+// Top-k of one register-resident chunk, left sorted in list slot `slot`.
+template <int DT, bool VEC>
+__device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row, long start, int len, int top_k,
+                                             bool is_draft, float* ov, int32_t* oi, int32_t* ocnt,
+                                             uint32_t* oflag, ChunkSmem& sm) {
     using E = Elem<DT>;
     constexpr int EPV = E::kPerVec;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wid = tid / kWave;
-    const long end = start + len;
-
-    // Vector vi (= s*256 + tid) of the chunk holds elements [vi*EPV, vi*EPV + EPV).
-    const u32x4* vbase = reinterpret_cast<const u32x4*>(row + start * E::kBytes);
     const int nvec = (len + EPV - 1) / EPV;
-    u32x4 d[kSlots];
     float gmax[kSlots];
-    float tmax = -INFINITY;
-    uint32_t bad = 0;
+    float tmax = -INFINITY, tmin = INFINITY;
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
         const int vi = s * kThreads + tid;
-        const bool valid = vi < nvec;
-        if (VEC) d[s] = valid ? load_stream(vbase + vi) : u32x4{0u, 0u, 0u, 0u};
-        else d[s] = valid ? load_slot<DT, false>(row, start + static_cast<long>(vi) * EPV, end) : u32x4{0u, 0u, 0u, 0u};
-        float g = -INFINITY;
-        if (valid) {
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const float v = E::get(d[s], e);
-                g = fmaxf(g, v);
-                bad |= (v != v);
-                if (is_draft) bad |= (v < 0.f) & (VEC || vi * EPV + e < len);
-            }
-        }
-        gmax[s] = g;
-        tmax = fmaxf(tmax, g);
-    }
-
-    // Lower bound on the chunk's k-th largest value.
-    const int kw = (top_k + kWaves - 1) / kWaves;
-    const float sorted = wave_sort_desc(tmax);
-    const float tw = __shfl(sorted, kw - 1, kWave);
-    bad = wave_or(bad);
-    if (tid == 0) { sm.cnt = 0; sm.flags = 0; }
-    if (lane == 0) sm.tau[wid] = tw;
-    __syncthreads();
-    if (lane == 0 && bad) atomicOr(&sm.flags, kFlagInvalid);
-    float tau = sm.tau[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) tau = fminf(tau, sm.tau[w]);
-
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        if (gmax[s] >= tau) {
-            const int i0 = (s * kThreads + tid) * EPV;
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const float v = E::get(d[s], e);
-                if (v >= tau && i0 + e < len) {
-                    const int p = atomicAdd(&sm.cnt, 1);
-                    if (p < kCap) { sm.cv[p] = v; sm.ci[p] = static_cast<int32_t>(start) + i0 + e; }
+        gmax[s] = -INFINITY;
+        if (vi < nvec) {
+            gmax[s] = vec_max<DT>(d[s]);
+            if (is_draft) {
+                // the -inf padding of a partial vector must not enter the minimum
+                if (VEC || (vi + 1) * EPV <= len) {
+                    tmin = __builtin_elementwise_minimum(tmin, vec_min_f32(d[s]));
+                } else {
+                    for (int e = 0; e < EPV; ++e)
+                        if (vi * EPV + e < len) tmin = __builtin_elementwise_minimum(tmin, E::get(d[s], e));
                 }
             }
+        }
+        tmax = __builtin_elementwise_maximum(tmax, gmax[s]);
+    }
+    // The widened values are cheaper to recompute for the few candidate vectors
+    // than to keep live: hide the raw registers' provenance from the compiler.
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) asm volatile("" : "+v"(d[s]));
+    // NaN anywhere (E1/E3) or a negative draft probability (E3) flags the chunk.
+    uint32_t bad = (tmax != tmax) || (is_draft && !(tmin >= 0.f));
+    bad = wave_or(bad);
+    if (tmax != tmax) tmax = -INFINITY;
+
+    // tau: the top_k-th largest of the 256 thread maxima, by bisection on their
+    // ordered keys in wave 0 (4 keys per lane; counts are ballot popcounts).
+    sm.tkey[tid] = ordered_key(tmax);
+    if (tid == 0) { sm.cnt = 0; sm.flags = 0; sm.overflow = 0; }
+    __syncthreads();
+    if (lane == 0 && bad) atomicOr(&sm.flags, kFlagInvalid);
+    if (wid == 0) {
+        const uint32_t k0 = sm.tkey[lane], k1 = sm.tkey[lane + 64], k2 = sm.tkey[lane + 128], k3 = sm.tkey[lane + 192];
+        uint32_t lo = 0u, hi = 0xffffffffu;
+        while (lo < hi) {
+            const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
+            const int c = __popcll(__ballot(k0 >= mid)) + __popcll(__ballot(k1 >= mid)) +
+                          __popcll(__ballot(k2 >= mid)) + __popcll(__ballot(k3 >= mid));
+            if (c >= top_k) lo = mid;
+            else hi = mid - 1u;
+        }
+        if (lane == 0) sm.tau = lo == 0u ? -INFINITY : key_value(lo);
+    }
+    __syncthreads();
+    const float tau = sm.tau;
+
+    // Stage the vectors whose maximum reaches tau (about k + 10 per chunk) in
+    // wave-private LDS, then let each lane check one staged vector's elements.
+    int staged = 0;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        const bool pass = gmax[s] >= tau;
+        const unsigned long long bal = __ballot(pass);
+        if (bal) {
+            const int p = staged + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+            if (pass && p < kStage) {
+                sm.stage[wid][p] = d[s];
+                sm.stage_vi[wid][p] = s * kThreads + tid;
+            }
+            staged += __popcll(bal);
+        }
+    }
+    if (staged > kStage) {
+        if (lane == 0) sm.overflow = 1;
+    } else if (staged > 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const bool mine = lane < staged;
+        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+        int vi = 0;
+        if (mine) {
+            w = sm.stage[wid][lane];
+            vi = sm.stage_vi[wid][lane];
+        }
+        int base = 0;
+        int total = 0;
+        bool take[EPV];
+        unsigned long long tb[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float v = E::get(w, e);
+            take[e] = mine && v >= tau && vi * EPV + e < len;
+            tb[e] = __ballot(take[e]);
+            total += __popcll(tb[e]);
+        }
+        if (lane == 0) base = atomicAdd(&sm.cnt, total);
+        base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const int p = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tb[e] >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tb[e]), 0u));
+            if (take[e] && p < kCap) {
+                sm.cv[p] = E::get(w, e);
+                sm.ci[p] = static_cast<int32_t>(start) + vi * EPV + e;
+            }
+            base += __popcll(tb[e]);
         }
     }
     __syncthreads();
     int n = sm.cnt;
-    if (n > kCap) n = chunk_exact(row, DT, start, len, top_k, sm);
+    if (n > kCap || sm.overflow) n = chunk_exact(row, DT, start, len, top_k, sm);
+    if (wid != 0) return;
 
-    // Rank selection: position = number of candidates that precede this one.
-    for (int c = tid; c < n; c += kThreads) {
-        const float v = sm.cv[c];
-        const int i = sm.ci[c];
-        int rank = 0;
-        for (int j = 0; j < n; ++j) rank += precedes(sm.cv[j], sm.ci[j], v, i);
-        if (rank < top_k) { ov[rank] = v; oi[rank] = i; }
+    // One wave: sort 64 candidates at a time and merge the blocks.
+    float v = lane < n ? sm.cv[lane] : -INFINITY;
+    int i = lane < n ? sm.ci[lane] : kNoIndex;
+    wave_sort_pairs(v, i);
+    for (int base = kWave; base < n; base += kWave) {
+        float w = base + lane < n ? sm.cv[base + lane] : -INFINITY;
+        int wi = base + lane < n ? sm.ci[base + lane] : kNoIndex;
+        wave_sort_pairs(w, wi);
+        wave_merge_pairs(v, i, w, wi);
     }
-    if (tid == 0) {
-        *ocnt = n < top_k ? n : top_k;
+    const int kk = n < top_k ? n : top_k;
+    ov[lane] = v;                       // every slot: past kk the entries are ignored
+    oi[lane] = i;
+    if (lane == 0) {
+        *ocnt = kk;
         *oflag = sm.flags;
     }
 }
@@ -244,116 +341,30 @@ __device__ __forceinline__ void chunk_topk(const char* row, long start, int len,
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkChunkArgs a) {
     __shared__ ChunkSmem sm;
-    const int unit = blockIdx.x;
-    const int Ut = a.Rt * a.Ct;
-    float* ov = a.vals + static_cast<long>(unit) * kTopkMax;
-    int32_t* oi = a.idx + static_cast<long>(unit) * kTopkMax;
-    if (unit < Ut) {
-        const int rt = unit / a.Ct, c = unit - rt * a.Ct;
-        const int b = rt / a.target_rows_per_batch, k = rt - b * a.target_rows_per_batch;
-        const long mem_row = static_cast<long>(b) * a.target_batch_stride + k;
-        const char* row = static_cast<const char*>(a.target) + mem_row * a.V * Elem<DT>::kBytes;
-        const long start = static_cast<long>(c) * a.chunk_t;
-        const int len = static_cast<int>(min(static_cast<long>(a.chunk_t), a.V - start));
-        chunk_topk<DT, VEC>(row, start, len, a.top_k, false, ov, oi, a.cnt + unit, a.flags + unit, sm);
+    const long unit = blockIdx.x;
+    const TopkLists& t = a.l;
+    const int b = static_cast<int>(unit / t.Ub);
+    const long local = unit - static_cast<long>(b) * t.Ub;
+    const int PB = t.Ct + t.Cd;
+    int k = static_cast<int>(local / PB);
+    if (k > a.K) k = a.K;
+    const int within = static_cast<int>(local - static_cast<long>(k) * PB);
+    float* ov = t.vals + unit * kTopkMax;
+    int32_t* oi = t.idx + unit * kTopkMax;
+    u32x4 d[kSlots];
+    if (within < t.Ct) {
+        const char* row = static_cast<const char*>(a.target) + (static_cast<long>(b) * (a.K + 1) + k) * a.V * Elem<DT>::kBytes;
+        const long start = static_cast<long>(within) * t.chunk_t;
+        const int len = static_cast<int>(min(static_cast<long>(t.chunk_t), a.V - start));
+        load_chunk<DT, VEC>(row, start, len, d);
+        select_chunk<DT, VEC>(d, row, start, len, t.top_k, false, ov, oi, t.cnt + unit, t.flags + unit, sm);
     } else {
-        const int u = unit - Ut;
-        const int rd = u / a.Cd, c = u - rd * a.Cd;
-        const char* row = reinterpret_cast<const char*>(a.draft + static_cast<long>(rd) * a.V);
-        const long start = static_cast<long>(c) * a.chunk_d;
-        const int len = static_cast<int>(min(static_cast<long>(a.chunk_d), a.V - start));
-        chunk_topk<0, VEC>(row, start, len, a.top_k, true, ov, oi, a.cnt + unit, a.flags + unit, sm);
-    }
-}
-
-constexpr int kMaxChunks = 16;
-
-__global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkRowsArgs a) {
-    __shared__ float lv[kMaxChunks * kTopkMax];
-    __shared__ int32_t li[kMaxChunks * kTopkMax];
-    __shared__ int32_t lcnt[kMaxChunks], loff[kMaxChunks + 1];
-    __shared__ float sel_v[kTopkMax];
-    __shared__ int32_t sel_i[kTopkMax];
-    __shared__ uint32_t s_flags;
-
-    const int r = blockIdx.x;
-    const bool draft = r >= a.Rt;
-    const int C = draft ? a.Cd : a.Ct;
-    const long unit0 = draft ? static_cast<long>(a.Rt) * a.Ct + static_cast<long>(r - a.Rt) * a.Cd
-                             : static_cast<long>(r) * a.Ct;
-    const int tid = threadIdx.x;
-    if (tid == 0) {
-        uint32_t f = 0;
-        int off = 0;
-        for (int c = 0; c < C; ++c) {
-            lcnt[c] = a.chunk_cnt[unit0 + c];
-            loff[c] = off;
-            off += lcnt[c];
-            f |= a.chunk_flags[unit0 + c];
-        }
-        loff[C] = off;
-        s_flags = f;
-    }
-    __syncthreads();
-    const int n = loff[C];
-    for (int t = tid; t < C * kTopkMax; t += kThreads) {
-        const int c = t / kTopkMax, p = t - c * kTopkMax;
-        if (p < lcnt[c]) {
-            lv[loff[c] + p] = a.chunk_vals[(unit0 + c) * kTopkMax + p];
-            li[loff[c] + p] = a.chunk_idx[(unit0 + c) * kTopkMax + p];
-        }
-    }
-    __syncthreads();
-    // Merge by rank: own position plus, in every other list, the number of
-    // entries that precede this one (lists are sorted, so binary search).
-    for (int t = tid; t < n; t += kThreads) {
-        int c = 0;
-        while (t >= loff[c + 1]) ++c;
-        const float v = lv[t];
-        const int i = li[t];
-        int rank = t - loff[c];
-        for (int o = 0; o < C; ++o) {
-            if (o == c) continue;
-            int lo = loff[o], hi = loff[o + 1];
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (precedes(lv[mid], li[mid], v, i)) lo = mid + 1;
-                else hi = mid;
-            }
-            rank += lo - loff[o];
-        }
-        if (rank < a.top_k) { sel_v[rank] = v; sel_i[rank] = i; }
-    }
-    __syncthreads();
-    if (tid >= kWave) return;
-    const int kk = n < a.top_k ? n : a.top_k;
-    const int l = tid;
-    const bool have = l < kk;
-    const float v = have ? sel_v[l] : 0.f;
-    const int idx = have ? sel_i[l] : 0x7fffffff;
-    const float v0 = sel_v[0];
-    uint32_t flags = s_flags;
-    double w = 0.0;
-    if (!draft) {
-        if (kk == 0 || !(v0 > -INFINITY && v0 < INFINITY)) flags |= kFlagInvalid;
-        if (have) w = exp((static_cast<double>(v) - static_cast<double>(v0)) * a.invT);
-    } else {
-        if (kk == 0 || v0 == INFINITY) flags |= kFlagInvalid;
-        if (have && v > 0.f) w = a.draft_identity ? static_cast<double>(v) : pow(static_cast<double>(v), a.invT);
-    }
-    const double Z = wave_sum(w);
-    if (!(Z > 0.0 && Z < INFINITY)) flags |= kFlagInvalid;
-    const double p = w / Z;
-    // Order by token index for the inverse-CDF draw.
-    int pos = 0;
-    for (int t = 0; t < kk; ++t) pos += sel_i[t] < idx;
-    if (have) {
-        a.row_idx[static_cast<long>(r) * kTopkMax + pos] = idx;
-        a.row_p[static_cast<long>(r) * kTopkMax + pos] = p;
-    }
-    if (l == 0) {
-        a.row_cnt[r] = kk;
-        a.row_flags[r] = flags;
+        const int c = within - t.Ct;
+        const char* row = reinterpret_cast<const char*>(a.draft + (static_cast<long>(b) * a.K + k) * a.V);
+        const long start = static_cast<long>(c) * t.chunk_d;
+        const int len = static_cast<int>(min(static_cast<long>(t.chunk_d), a.V - start));
+        load_chunk<0, VEC>(row, start, len, d);
+        select_chunk<0, VEC>(d, row, start, len, t.top_k, true, ov, oi, t.cnt + unit, t.flags + unit, sm);
     }
 }
 
@@ -361,8 +372,8 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(TopkRowsArgs a) {
 
 hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s) {
     const int esz = a.dtype ? 2 : 4;
-    const bool vec = vec_ok(a.target, a.V, esz) && (a.Rd == 0 || vec_ok(a.draft, a.V, 4));
-    const unsigned units = static_cast<unsigned>(a.Rt * a.Ct + a.Rd * a.Cd);
+    const bool vec = vec_ok(a.target, a.V, esz) && vec_ok(a.draft, a.V, 4);
+    const unsigned units = static_cast<unsigned>(static_cast<long>(a.B) * a.l.Ub);
     if (units == 0) return hipSuccess;
     if (a.dtype == 1) {
         if (vec) hipLaunchKernelGGL((topk_chunk_kernel<1, true>), dim3(units), dim3(kThreads), 0, s, a);
@@ -371,13 +382,6 @@ hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s) {
         if (vec) hipLaunchKernelGGL((topk_chunk_kernel<0, true>), dim3(units), dim3(kThreads), 0, s, a);
         else hipLaunchKernelGGL((topk_chunk_kernel<0, false>), dim3(units), dim3(kThreads), 0, s, a);
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
-    const unsigned rows = static_cast<unsigned>(a.Rt + a.Rd);
-    if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "lists.hpp"
 
 namespace sv {
 
@@ -29,8 +30,6 @@ constexpr int kEPT = 8;                                   // elements per thread
 constexpr int kTile = kDrawThreads * kEPT;                // 4096
 constexpr int kMaxTiles = (kMaxV + kTile - 1) / kTile;
 
-__device__ __forceinline__ bool u_ok(float u) { return u >= 0.f && u < 1.f; }
-__device__ __forceinline__ bool q_ok(float v) { return v >= 0.f && v < INFINITY; }
 
 // Loads 8 consecutive logits starting at i0 (multiple of 8); -inf beyond V.
 template <int DT, bool VEC>
@@ -92,7 +91,7 @@ __device__ __forceinline__ double block_sum_d(double v, DrawSmem& sm) {
 
 __device__ __forceinline__ int block_min_i(int v, DrawSmem& sm) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+    for (int o = 32; o > 0; o >>= 1) v = min(v, xshfl(v, o));
     __syncthreads();
     if ((threadIdx.x & (kWave - 1)) == 0) sm.ired[threadIdx.x / kWave] = v;
     __syncthreads();
@@ -371,100 +370,6 @@ __global__ __launch_bounds__(kDrawThreads) void chain_dense_kernel(ChainArgs a) 
     }
 }
 
-// Top-k rows: every list holds <= 64 (index, probability) entries sorted by index.
-__device__ __forceinline__ double list_lookup(const int32_t* idx, const double* p, int cnt, int tok) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const bool hit = lane < cnt && idx[lane] == tok;
-    const unsigned long long m = __ballot(hit);
-    if (!m) return 0.0;
-    const int src = __ffsll(static_cast<long long>(m)) - 1;
-    return __shfl(hit ? p[lane] : 0.0, src, kWave);
-}
-
-__global__ __launch_bounds__(kWave) void chain_topk_kernel(ChainArgs a) {
-    const int b = blockIdx.x;
-    const int K = a.K, V = a.V;
-    const int lane = threadIdx.x;
-    const long rbase = static_cast<long>(b) * (K + 1);      // target list rows
-    const long dbase = static_cast<long>(b) * K;            // draft list rows (offset by B*(K+1))
-    const long drow0 = static_cast<long>(a.B) * (K + 1);
-    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
-
-    bool bad = false;
-    if (lane <= K) {
-        bad |= a.row_flags[rbase + lane] != 0u;
-        bad |= !u_ok(a.u[rbase + lane]);
-    }
-    if (lane < K) {
-        bad |= a.row_flags[drow0 + dbase + lane] != 0u;
-        const int x = a.x[dbase + lane];
-        bad |= (x < 0 || x >= V);
-    }
-    if (__ballot(bad)) {
-        for (int t = lane; t <= K; t += kWave) a.out_tokens[rbase + t] = -1;
-        if (lane == 0) a.out_accept_len[b] = -1;
-        if (diag) for (int t = lane; t < 2 * K + 2; t += kWave) diag[t] = NAN;
-        return;
-    }
-    int j = K;
-    for (int k = 0; k < K; ++k) {
-        const int x = a.x[dbase + k];
-        const long tr = rbase + k, dr = drow0 + dbase + k;
-        const double pk = list_lookup(a.row_idx + tr * kTopkMax, a.row_p + tr * kTopkMax, a.row_cnt[tr], x);
-        const double qk = list_lookup(a.row_idx + dr * kTopkMax, a.row_p + dr * kTopkMax, a.row_cnt[dr], x);
-        double ratio;
-        if (qk > 0.0) ratio = pk / qk;
-        else ratio = pk > 0.0 ? INFINITY : 0.0;
-        const double thr = ratio < 1.0 ? ratio : 1.0;
-        if (diag && lane == 0) { diag[k] = static_cast<float>(pk); diag[K + k] = static_cast<float>(qk); }
-        if (j == K && !(static_cast<double>(a.u[rbase + k]) < thr)) j = k;
-    }
-    // Final draw over the index-sorted target list of row j.
-    const long tr = rbase + j;
-    const int cnt = a.row_cnt[tr];
-    const bool have = lane < cnt;
-    const int idx = have ? a.row_idx[tr * kTopkMax + lane] : 0x7fffffff;
-    const double p = have ? a.row_p[tr * kTopkMax + lane] : 0.0;
-    double r = p;
-    double S;
-    if (j < K) {
-        const long dr = drow0 + dbase + j;
-        const int qc = a.row_cnt[dr];
-        double qv = 0.0;
-        for (int t = 0; t < qc; ++t)
-            if (a.row_idx[dr * kTopkMax + t] == idx) qv = a.row_p[dr * kTopkMax + t];
-        r = have ? fmax(p - qv, 0.0) : 0.0;
-        S = wave_sum(r);
-        if (!(S > 0.0)) { r = p; S = wave_sum(p); }
-    } else {
-        S = wave_sum(p);
-    }
-    const double C = wave_inclusive_scan(r);
-    const double target = static_cast<double>(a.u[rbase + K]) * S;
-    const unsigned long long hit = __ballot(have && r > 0.0 && target < C);
-    int src;
-    if (hit) src = __ffsll(static_cast<long long>(hit)) - 1;
-    else {
-        const unsigned long long pos = __ballot(have && r > 0.0);
-        src = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
-    }
-    const int y = __shfl(idx, src, kWave);
-    const double ry = __shfl(r, src, kWave);
-    for (int t = lane; t <= K; t += kWave) {
-        int tok = -1;
-        if (t < j) tok = a.x[dbase + t];
-        else if (t == j) tok = y;
-        a.out_tokens[rbase + t] = tok;
-    }
-    if (lane == 0) {
-        a.out_accept_len[b] = j;
-        if (diag) {
-            diag[2 * K] = static_cast<float>(S);
-            diag[2 * K + 1] = static_cast<float>(ry / S);
-        }
-    }
-}
-
 // Greedy chain: argmax comparisons only.
 __global__ void chain_greedy_kernel(ChainArgs a) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -526,8 +431,7 @@ __global__ __launch_bounds__(kWave) void tree_kernel(TreeArgs a) {
     }
     // Deepest accepted node, lowest index on ties.
     int key = (node && acc) ? (depth << 8) | (255 - n) : -1;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, kWave));
+    key = wave_max_int(key);
     const int best = 255 - (key & 255);
     const int dbest = key >> 8;
     const int gbest = __shfl(g, best, kWave);
@@ -581,23 +485,148 @@ __global__ __launch_bounds__(256) void alpha_dense_kernel(AlphaArgs a) {
     }
 }
 
-__global__ __launch_bounds__(kWave) void alpha_topk_kernel(AlphaArgs a) {
-    const int r = blockIdx.x;                      // b*K + k
-    const int lane = threadIdx.x;
-    const long tr = r, dr = static_cast<long>(a.B) * a.K + r;
-    const int cnt = a.row_cnt[tr];
-    const bool have = lane < cnt;
-    const int idx = have ? a.row_idx[tr * kTopkMax + lane] : -1;
-    const double p = have ? a.row_p[tr * kTopkMax + lane] : 0.0;
-    const int qc = a.row_cnt[dr];
-    double qv = 0.0;
-    for (int t = 0; t < qc; ++t)
-        if (a.row_idx[dr * kTopkMax + t] == idx) qv = a.row_p[dr * kTopkMax + t];
-    const double s = wave_sum(have ? fmin(p, qv) : 0.0);
-    if (lane == 0) {
-        const bool bad = a.row_flags[tr] != 0u || a.row_flags[dr] != 0u;
-        a.out_alpha[r] = bad ? NAN : static_cast<float>(s);
+// ---- top-k path: merge the chunk lists of each position, test, draw, combine ----
+
+// Kept distribution of row (b, k): target (draft = false) or draft.
+__device__ __forceinline__ bool position_row(const TopkLists& t, int b, int k, bool draft, int& idx, double& p,
+                                             int& kk) {
+    const long unit0 = t.unit_base(b, k) + (draft ? t.Ct : 0);
+    float v;
+    int i;
+    uint32_t flags = 0;
+    const int tot = merge_global_lists(t, unit0, draft ? t.Cd : t.Ct, v, i, flags);
+    kk = tot < t.top_k ? tot : t.top_k;
+    return kept_distribution(v, i, kk, flags == 0u, draft, t.invT, draft && t.draft_identity, idx, p);
+}
+
+// One workgroup of two waves per position (b, k): wave 0 merges target row k's
+// chunk lists, wave 1 draft row k's, in parallel; wave 0 then runs test k and
+// draws the token that would be emitted if k were the first rejection (the bonus
+// token for k = K).  One position per workgroup spreads the work over the chip.
+__global__ __launch_bounds__(2 * kWave) void chain_topk_position_kernel(ChainArgs a) {
+    __shared__ int32_t sidx[kWave];
+    __shared__ double sp[kWave];
+    __shared__ int32_t skd, sok;
+    const int K = a.K, V = a.V;
+    const int b = blockIdx.x / (K + 1), k = blockIdx.x - b * (K + 1);
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const long rbase = static_cast<long>(b) * (K + 1);
+    const TopkLists& t = a.tk;
+    int it = kNoIndex, kt = 0;
+    double pt = 0.0;
+    bool ok = false;
+    if (wid == 0) {
+        ok = position_row(t, b, k, false, it, pt, kt);
+    } else if (k < K) {
+        int id, kd;
+        double pd;
+        const bool okd = position_row(t, b, k, true, id, pd, kd);
+        sidx[lane] = id;
+        sp[lane] = pd;
+        if (lane == 0) { skd = kd; sok = okd; }
     }
+    __syncthreads();
+    if (wid != 0) return;
+    const float uK = a.u[rbase + K];
+    ok = ok && u_ok(a.u[rbase + k]) && u_ok(uK);
+    double r = pt, px = 0.0, qx = 0.0;
+    bool accept = false;
+    if (k < K) {
+        const int x = a.x[static_cast<long>(b) * K + k];
+        ok = ok && sok && x >= 0 && x < V;
+        px = lane_lookup(it, pt, x);
+        qx = lds_lookup(sidx, sp, skd, x);
+        double ratio;
+        if (qx > 0.0) ratio = px / qx;
+        else ratio = px > 0.0 ? INFINITY : 0.0;
+        const double thr = ratio < 1.0 ? ratio : 1.0;
+        accept = static_cast<double>(a.u[rbase + k]) < thr;
+        const double q = lane < kt ? lds_lookup(sidx, sp, skd, it) : 0.0;
+        r = lane < kt ? fmax(pt - q, 0.0) : 0.0;
+    }
+    double S = wave_sum(r);
+    if (!(S > 0.0)) {                       // zero residual: draw from p'_k
+        r = pt;
+        S = wave_sum(pt);
+    }
+    const int src = lane_draw(r, lane < kt, static_cast<double>(uK) * S);
+    const int y = bcast(it, src);
+    const double ry = bcast(r, src);
+    if (lane == 0) {
+        PosRecord rc;
+        rc.accept = accept;
+        rc.y = y;
+        rc.bad = !ok;
+        rc.pad = 0;
+        rc.pk = static_cast<float>(px);
+        rc.qk = static_cast<float>(qx);
+        rc.S = static_cast<float>(S);
+        rc.py = static_cast<float>(ry / S);
+        a.rec[rbase + k] = rc;
+    }
+}
+
+// Per batch row: first rejection j from the position records, emitted tokens
+// x_0..x_{j-1}, y_j, accept_len = j.  One wave per batch row.
+__global__ __launch_bounds__(4 * kWave) void chain_topk_combine_kernel(ChainArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (b >= a.B) return;
+    const int K = a.K;
+    const long rb = static_cast<long>(b) * (K + 1);
+    bool bad = false;
+    for (int k = lane; k <= K; k += kWave) bad |= a.rec[rb + k].bad != 0;
+    const bool err = __ballot(bad) != 0ull;
+    int j = K;
+    for (int base = 0; base < K; base += kWave) {
+        const int k = base + lane;
+        const unsigned long long rm = __ballot(k < K && !a.rec[rb + k].accept);
+        if (rm) { j = base + __ffsll(static_cast<long long>(rm)) - 1; break; }
+    }
+    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
+    for (int k = lane; k <= K; k += kWave) {
+        int tok = -1;
+        if (!err) tok = k < j ? a.x[static_cast<long>(b) * K + k] : (k == j ? a.rec[rb + j].y : -1);
+        a.out_tokens[rb + k] = tok;
+        if (diag && k < K) {
+            diag[k] = err ? NAN : a.rec[rb + k].pk;
+            diag[K + k] = err ? NAN : a.rec[rb + k].qk;
+        }
+    }
+    if (lane == 0) {
+        a.out_accept_len[b] = err ? -1 : j;
+        if (diag) {
+            diag[2 * K] = err ? NAN : a.rec[rb + j].S;
+            diag[2 * K + 1] = err ? NAN : a.rec[rb + j].py;
+        }
+    }
+}
+
+// alpha over the kept sets: one workgroup of two waves per (b, k).
+__global__ __launch_bounds__(2 * kWave) void alpha_topk_kernel(AlphaArgs a) {
+    __shared__ int32_t sidx[kWave];
+    __shared__ double sp[kWave];
+    __shared__ int32_t skd, sok;
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const long r = blockIdx.x;                                  // b*K + k
+    const int b = static_cast<int>(r / a.K), k = static_cast<int>(r - static_cast<long>(b) * a.K);
+    int it = kNoIndex, kt = 0;
+    double pt = 0.0;
+    bool ok = false;
+    if (wid == 0) ok = position_row(a.tk, b, k, false, it, pt, kt);
+    else {
+        int id, kd;
+        double pd;
+        const bool okd = position_row(a.tk, b, k, true, id, pd, kd);
+        sidx[lane] = id;
+        sp[lane] = pd;
+        if (lane == 0) { skd = kd; sok = okd; }
+    }
+    __syncthreads();
+    if (wid != 0) return;
+    const double q = lane < kt ? lds_lookup(sidx, sp, skd, it) : 0.0;
+    const double s = wave_sum(lane < kt ? fmin(pt, q) : 0.0);
+    if (lane == 0) a.out_alpha[r] = (ok && sok) ? static_cast<float>(s) : NAN;
 }
 
 __global__ void alpha_greedy_kernel(AlphaArgs a) {
@@ -622,11 +651,6 @@ hipError_t launch_chain_dense(const ChainArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_chain_topk(const ChainArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(chain_topk_kernel, dim3(a.B), dim3(kWave), 0, s, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_chain_greedy(const ChainArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(chain_greedy_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a);
     return hipGetLastError();
@@ -644,8 +668,16 @@ hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_chain_topk(const ChainArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(chain_topk_position_kernel, dim3(a.B * (a.K + 1)), dim3(2 * kWave), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chain_topk_combine_kernel, dim3((a.B + 3) / 4), dim3(4 * kWave), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(alpha_topk_kernel, dim3(a.B * a.K), dim3(kWave), 0, s, a);
+    hipLaunchKernelGGL(alpha_topk_kernel, dim3(a.B * a.K), dim3(2 * kWave), 0, s, a);
     return hipGetLastError();
 }
 
