@@ -43,17 +43,21 @@ def log(msg: str) -> None:
 
 
 def kernel_source_digest() -> str:
+    """Digest of every kernel source (csrc/*.hip, *.hpp): counter figures taken on other
+    sources are stale."""
     h = hashlib.sha256()
-    for f in ("common.hpp", "internal.hpp", "topk.hip", "rowstats.hip", "verify.hip", "api.hip"):
-        with open(os.path.join(ROOT, "rejection_sampling_verify_10_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "rejection_sampling_verify_10_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
 def counter_traffic(workload: int):
     """HBM bytes per launch of the dominant kernel from the committed counter summary,
     or None when the summary is absent or was taken on another kernel source."""
-    path = os.path.join(ROOT, "profiles", f"counters_workload{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{WORKLOADS[workload]['kernel']}_workload{workload}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
