@@ -100,6 +100,25 @@ def copy_probe(R, torch, args) -> int:
     return 0
 
 
+def read_probe_gbps(R, torch, dev) -> float:
+    """Achievable streaming-read bandwidth: the library's read-only probe over 1 GiB
+    (four times the Infinity Cache), 20 launches timed together."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        R.read_probe(src, sink)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(20):
+        R.read_probe(src, sink)
+    b.record()
+    torch.cuda.synchronize()
+    return n / (a.elapsed_time(b) * 1e-3 / 20) / 1e9
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +201,8 @@ def main() -> int:
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak); accept_len histogram {np.bincount(al, minlength=K + 1).tolist()}")
     traffic = counter_traffic(args.workload)
+    probe = read_probe_gbps(R, torch, dev)
+    log(f"read probe {probe:.0f} GB/s; {wl['kernel']} at {100 * achieved / probe:.1f}% of it")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -215,7 +236,8 @@ def main() -> int:
         "step_algorithmic_GBps": step_alg_gbs,
         "roofline": {"bound": "hbm", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg},
+                     "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg,
+                     "read_probe_GBps": probe, "frac_of_read_probe": achieved / probe},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

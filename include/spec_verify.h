@@ -173,9 +173,15 @@ int spec_workspace_init(void* workspace, size_t workspace_bytes, void* hip_strea
  * spec_copy_probe: plain device-to-device copy of `bytes` (multiple of 16,
  * 16-byte aligned pointers) by a streaming kernel, for calibrating hardware
  * byte counters against a known traffic.
+ *
+ * spec_read_probe: reads `bytes` (multiple of 16, 16-byte aligned) of device
+ * memory once with the same 16-byte non-temporal loads as the verification
+ * kernels and writes nothing but, at most, one word to `sink` (4 bytes of device
+ * memory, contents meaningless): the achievable streaming-read bandwidth.
  */
 int spec_profile_events(void* start_event, void* stop_event);
 int spec_copy_probe(const void* src, void* dst, size_t bytes, void* hip_stream);
+int spec_read_probe(const void* src, size_t bytes, void* sink, void* hip_stream);
 
 #ifdef __cplusplus
 }

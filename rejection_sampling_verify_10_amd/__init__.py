@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.spec_workspace_init.restype = I
         L.spec_copy_probe.argtypes = [P, P, Z, P]
         L.spec_copy_probe.restype = I
+        L.spec_read_probe.argtypes = [P, Z, P, P]
+        L.spec_read_probe.restype = I
         _lib = L
     return _lib
 
@@ -237,3 +239,9 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst is smaller than src")
     _check(lib().spec_copy_probe(_dev(src, "src"), _dev(dst, "dst"), n, _stream(src.device)), "spec_copy_probe")
+
+
+def read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read-only streaming kernel over src (achievable HBM read bandwidth)."""
+    n = src.numel() * src.element_size()
+    _check(lib().spec_read_probe(_dev(src, "src"), n, _dev(sink, "sink"), _stream(src.device)), "spec_read_probe")

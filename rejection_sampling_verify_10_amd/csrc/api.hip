@@ -119,7 +119,10 @@ struct ChainPlan {
     uint32_t* qflags;
     TopkLists tk;
     PosRecord* rec;
+    DenseParts dp;
 };
+
+int dense_chunks(int V) { return (V + kDenseChunk - 1) / kDenseChunk; }
 
 ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {
     ChainPlan p{};
@@ -138,8 +141,13 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
             p.qsum = c.take<double>(Rd);
             p.qflags = c.take<uint32_t>(Rd);
         }
+        const size_t P = static_cast<size_t>(B) * dense_chunks(V);
+        p.dp.C = dense_chunks(V);
+        p.dp.pe = c.take<double>(P);
+        p.dp.pr = c.take<double>(P);
+        p.dp.pq = c.take<double>(P);
+        p.dp.pflag = c.take<uint32_t>(P);
     }
-    (void)Rd;
     return p;
 }
 
@@ -250,6 +258,7 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
     if (!greedy && topk_active(top_k, V)) {
         if (top_k > SPEC_TOPK_MAX || !topk_shape_ok(dtype, V)) return SPEC_EUNSUPPORTED;
     }
+    if (static_cast<long>(B) * dense_chunks(V) > 0x7fffffffL) return SPEC_EUNSUPPORTED;
     const size_t need = spec_chain_workspace_bytes(B, K, V, dtype, temperature, top_k);
     rc = check_workspace(workspace, workspace_bytes, need);
     if (rc) return rc;
@@ -303,7 +312,7 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
             ca.qsum = p.qsum;
             ca.qflags = p.qflags;
         }
-        SV_TRY(launch_chain_dense(ca, s));
+        SV_TRY(launch_chain_dense(ca, p.dp, s));
     }
     return SPEC_OK;
 }
@@ -436,6 +445,12 @@ int spec_workspace_init(void* workspace, size_t workspace_bytes, void* hip_strea
 int spec_copy_probe(const void* src, void* dst, size_t bytes, void* hip_stream) {
     if (!src || !dst || bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return SPEC_EINVAL;
     if (launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(hip_stream)) != hipSuccess) return SPEC_ELAUNCH;
+    return SPEC_OK;
+}
+
+int spec_read_probe(const void* src, size_t bytes, void* sink, void* hip_stream) {
+    if (!src || !sink || bytes % 16 != 0 || !aligned(src, 16) || !aligned(sink, 4)) return SPEC_EINVAL;
+    if (launch_read_probe(src, bytes, sink, static_cast<hipStream_t>(hip_stream)) != hipSuccess) return SPEC_ELAUNCH;
     return SPEC_OK;
 }
 

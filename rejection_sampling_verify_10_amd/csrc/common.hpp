@@ -111,6 +111,11 @@ __device__ __forceinline__ int wave_max_int(int v) {
     for (int o = 32; o > 0; o >>= 1) v = max(v, xshfl(v, o));
     return v;
 }
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, xshfl(v, o));
+    return v;
+}
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v |= xshfl(v, o);

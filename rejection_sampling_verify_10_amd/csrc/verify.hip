@@ -8,13 +8,10 @@
 // rejected draw the bonus token from p'_K.  The draw is an inverse CDF over
 // token indices in ascending order driven by u_K.
 //
-// Dense rows: the K tests are independent of each other, so they run in
-// parallel lanes and the first rejection is a ballot.  The final draw touches
-// one target row (and one draft row) per batch entry; it is recomputed in fp64
-// so that its CDF boundaries sit ~1e-16 from the exact ones: pass A sums
-// exp((z - m)/T) per 4096-element tile, pass B (residual only) sums
-// max(0, p' - q') per tile, then the tile holding u*S is rescanned element by
-// element.
+// The K tests are independent of each other, so they run in parallel lanes
+// and the first rejection is a ballot.  This file holds the greedy chain, the
+// static tree, the acceptance rate and the top-k chain finish; the dense final
+// draw is in dense.hip.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -23,352 +20,6 @@
 namespace sv {
 
 namespace {
-
-constexpr int kDrawThreads = 512;
-constexpr int kDrawWaves = kDrawThreads / kWave;
-constexpr int kEPT = 8;                                   // elements per thread per tile
-constexpr int kTile = kDrawThreads * kEPT;                // 4096
-constexpr int kMaxTiles = (kMaxV + kTile - 1) / kTile;
-
-
-// Loads 8 consecutive logits starting at i0 (multiple of 8); -inf beyond V.
-template <int DT, bool VEC>
-__device__ __forceinline__ void load8_logits(const char* row, int i0, int V, float out[kEPT]) {
-    using E = Elem<DT>;
-    if (VEC && DT == 1) {
-        if (i0 + 8 <= V) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(row + static_cast<long>(i0) * 2);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) out[e] = E::get(v, e);
-            return;
-        }
-    }
-    if (VEC && DT == 0) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + static_cast<long>(i0) * 4);
-        if (i0 + 8 <= V) {
-            const u32x4 a = p[0], b = p[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { out[e] = __uint_as_float(a[e]); out[4 + e] = __uint_as_float(b[e]); }
-            return;
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e) out[e] = (i0 + e < V) ? E::scalar(row, i0 + e) : -INFINITY;
-}
-
-template <bool VEC>
-__device__ __forceinline__ void load8_probs(const float* row, int i0, int V, float out[kEPT]) {
-    if (VEC && i0 + 8 <= V) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + i0);
-        const u32x4 a = p[0], b = p[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { out[e] = __uint_as_float(a[e]); out[4 + e] = __uint_as_float(b[e]); }
-        return;
-    }
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e) out[e] = (i0 + e < V) ? row[i0 + e] : 0.f;
-}
-
-struct DrawSmem {
-    double wsum[kMaxTiles][kDrawWaves];
-    double tsum[kMaxTiles];
-    double red[kDrawWaves];
-    int ired[kDrawWaves];
-    int j, err, tile, y, tail, bad;
-    double zp, zq, total, target, before;
-};
-
-__device__ __forceinline__ double block_sum_d(double v, DrawSmem& sm) {
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & (kWave - 1)) == 0) sm.red[threadIdx.x / kWave] = v;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int w = 0; w < kDrawWaves; ++w) t += sm.red[w];
-    return t;
-}
-
-__device__ __forceinline__ int block_min_i(int v, DrawSmem& sm) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, xshfl(v, o));
-    __syncthreads();
-    if ((threadIdx.x & (kWave - 1)) == 0) sm.ired[threadIdx.x / kWave] = v;
-    __syncthreads();
-    int t = sm.ired[0];
-#pragma unroll
-    for (int w = 1; w < kDrawWaves; ++w) t = min(t, sm.ired[w]);
-    return t;
-}
-
-__device__ __forceinline__ int block_max_i(int v, DrawSmem& sm) { return -block_min_i(-v, sm); }
-
-// Weight of element i in the final-draw distribution.
-//   mode 0: e_i = exp((z_i - m)/T)            (bonus, or zero-residual fallback)
-//   mode 1: max(0, e_i/Zp - q'_i)             (residual)
-struct DrawRow {
-    const char* z;
-    const float* q;
-    int V;
-    double m, invT, inv_zp, inv_zq;
-    int transformed;
-};
-
-template <int DT, bool VEC>
-__device__ __forceinline__ void tile_weights(const DrawRow& r, int mode, int i0, double w[kEPT], bool& bad) {
-    float z[kEPT];
-    load8_logits<DT, VEC>(r.z, i0, r.V, z);
-    if (mode == 0) {
-#pragma unroll
-        for (int e = 0; e < kEPT; ++e) w[e] = exp((static_cast<double>(z[e]) - r.m) * r.invT);
-        return;
-    }
-    float q[kEPT];
-    load8_probs<VEC>(r.q, i0, r.V, q);
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
-        bad |= (i0 + e < r.V) && !q_ok(q[e]);
-        const double p = exp((static_cast<double>(z[e]) - r.m) * r.invT) * r.inv_zp;
-        double qq = static_cast<double>(q[e]);
-        if (r.transformed) qq = (q[e] > 0.f) ? pow(qq, r.invT) * r.inv_zq : 0.0;
-        const double d = p - qq;
-        w[e] = d > 0.0 ? d : 0.0;
-    }
-}
-
-// Per-tile sums of the weights (mode) into sm.tsum; returns the total.  *qbad
-// becomes true (block-uniformly) when a draft probability read is invalid (E3).
-template <int DT, bool VEC>
-__device__ double tile_sums(const DrawRow& r, int mode, int ntiles, DrawSmem& sm, bool* qbad) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    bool bad = false;
-    if (threadIdx.x == 0) sm.bad = 0;
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        double w[kEPT];
-        tile_weights<DT, VEC>(r, mode, t * kTile + threadIdx.x * kEPT, w, bad);
-        double s = 0.0;
-#pragma unroll
-        for (int e = 0; e < kEPT; ++e) s += w[e];
-        s = wave_sum(s);
-        if (lane == 0) sm.wsum[t][wid] = s;
-    }
-    if (__ballot(bad) && lane == 0) atomicOr(&sm.bad, 1);
-    __syncthreads();
-    for (int t = threadIdx.x; t < ntiles; t += kDrawThreads) {
-        double s = 0.0;
-#pragma unroll
-        for (int w = 0; w < kDrawWaves; ++w) s += sm.wsum[t][w];
-        sm.tsum[t] = s;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double tot = 0.0;
-        for (int t = 0; t < ntiles; ++t) tot += sm.tsum[t];
-        sm.total = tot;
-    }
-    __syncthreads();
-    if (qbad) *qbad = sm.bad != 0;
-    return sm.total;
-}
-
-// Inverse CDF: smallest index i with target < C_i, C the index-ascending
-// inclusive prefix of the weights; rounding fallback = last positive weight.
-template <int DT, bool VEC>
-__device__ int draw_from(const DrawRow& r, int mode, int ntiles, double target, DrawSmem& sm, double* wy) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    if (threadIdx.x == 0) {
-        double before = 0.0;
-        int tile = -1, tail = -1;
-        for (int t = 0; t < ntiles; ++t) {
-            if (sm.tsum[t] > 0.0) tail = t;
-            if (tile < 0 && target < before + sm.tsum[t]) { tile = t; break; }
-            before += sm.tsum[t];
-        }
-        if (tile < 0) {
-            for (int t = ntiles - 1; t >= 0; --t) if (sm.tsum[t] > 0.0) { tail = t; break; }
-        }
-        sm.tile = tile;
-        sm.tail = tail;
-        sm.before = before;
-    }
-    __syncthreads();
-    const int tile = sm.tile;
-    const int t_use = tile >= 0 ? tile : (sm.tail >= 0 ? sm.tail : 0);
-    double w[kEPT];
-    const int i0 = t_use * kTile + threadIdx.x * kEPT;
-    bool unused = false;
-    tile_weights<DT, VEC>(r, mode, i0, w, unused);
-    int found = 0x7fffffff;
-    int lastpos = -1;
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e) if (w[e] > 0.0 && i0 + e < r.V) lastpos = i0 + e;
-    if (tile >= 0) {
-        double s = 0.0;
-#pragma unroll
-        for (int e = 0; e < kEPT; ++e) s += w[e];
-        // exclusive scan of the thread sums across the block
-        double incl = s;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            double t = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += t;
-        }
-        if (lane == kWave - 1) sm.red[wid] = incl;
-        __syncthreads();
-        double base = sm.before;
-        for (int x = 0; x < wid; ++x) base += sm.red[x];
-        double c = base + incl - s;
-#pragma unroll
-        for (int e = 0; e < kEPT; ++e) {
-            c += w[e];
-            if (found == 0x7fffffff && target < c && w[e] > 0.0) found = i0 + e;
-        }
-    }
-    int y = block_min_i(found, sm);
-    if (y == 0x7fffffff) y = block_max_i(lastpos, sm);
-    // weight of the drawn token
-    double my = 0.0;
-#pragma unroll
-    for (int e = 0; e < kEPT; ++e) if (i0 + e == y) my = w[e];
-    *wy = block_sum_d(my, sm);
-    return y;
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kDrawThreads) void chain_dense_kernel(ChainArgs a) {
-    __shared__ DrawSmem sm;
-    const int b = blockIdx.x;
-    const int K = a.K, V = a.V;
-    const int tid = threadIdx.x;
-    const long rbase = static_cast<long>(b) * (K + 1);
-    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
-
-    if (tid < kWave) {
-        const int k = tid;
-        bool bad = false, rej = false;
-        double pk = NAN, qk = NAN;
-        if (k <= K) {
-            bad |= (a.st.flags[rbase + k] != 0u);
-            bad |= !u_ok(a.u[rbase + k]);
-        }
-        if (k < K) {
-            const int x = a.x[static_cast<long>(b) * K + k];
-            bad |= (x < 0 || x >= V);
-            if (x >= 0 && x < V) {
-                const float qx = a.q[(static_cast<long>(b) * K + k) * V + x];
-                bad |= !q_ok(qx);
-                if (a.transformed) bad |= (a.qflags[static_cast<long>(b) * K + k] != 0u);
-                const double zx = static_cast<double>(a.st.zx[rbase + k]);
-                pk = exp((zx - static_cast<double>(a.st.m[rbase + k])) * a.invT) / a.st.Z[rbase + k];
-                qk = static_cast<double>(qx);
-                if (a.transformed)
-                    qk = (qx > 0.f) ? pow(qk, a.invT) / a.qsum[static_cast<long>(b) * K + k] : 0.0;
-                double ratio;
-                if (qk > 0.0) ratio = pk / qk;
-                else ratio = pk > 0.0 ? INFINITY : 0.0;
-                const double thr = ratio < 1.0 ? ratio : 1.0;
-                rej = !(static_cast<double>(a.u[rbase + k]) < thr);
-            }
-        }
-        const unsigned long long bm = __ballot(bad);
-        const unsigned long long rm = __ballot(rej && k < K);
-        const int j = rm ? __ffsll(static_cast<long long>(rm)) - 1 : K;
-        if (diag && k < K) {
-            diag[k] = bm ? NAN : static_cast<float>(pk);
-            diag[K + k] = bm ? NAN : static_cast<float>(qk);
-        }
-        if (tid == 0) {
-            sm.j = j;
-            sm.err = bm != 0ull;
-        }
-    }
-    __syncthreads();
-    const int j = sm.j;
-    if (sm.err) {
-        for (int t = tid; t <= K; t += kDrawThreads) a.out_tokens[rbase + t] = -1;
-        if (tid == 0) {
-            a.out_accept_len[b] = -1;
-            if (diag) { diag[2 * K] = NAN; diag[2 * K + 1] = NAN; }
-        }
-        return;
-    }
-
-    const long zrow = rbase + j;
-    DrawRow r;
-    r.z = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
-    r.q = (j < K) ? a.q + (static_cast<long>(b) * K + j) * V : nullptr;
-    r.V = V;
-    r.m = static_cast<double>(a.st.m[zrow]);
-    r.invT = a.invT;
-    r.transformed = a.transformed;
-    const int ntiles = (V + kTile - 1) / kTile;
-
-    // Pass A: exact normaliser of p'_j.
-    const double zp = tile_sums<DT, VEC>(r, 0, ntiles, sm, nullptr);
-    r.inv_zp = 1.0 / zp;
-    r.inv_zq = 1.0;
-    int mode = 0;
-    double W = zp;
-    bool qbad = false;
-    if (j < K) {
-        if (a.transformed) {
-            // Exact normaliser of q'_j = q_j^(1/T) / sum q_j^(1/T) (top-k is off here).
-            double zq = 0.0;
-            bool badq = false;
-            for (int i = tid; i < V; i += kDrawThreads) {
-                const float v = r.q[i];
-                badq |= !q_ok(v);
-                if (v > 0.f) zq += pow(static_cast<double>(v), a.invT);
-            }
-            const unsigned long long bq = __ballot(badq);
-            if ((tid & (kWave - 1)) == 0) sm.ired[tid / kWave] = bq != 0ull;
-            zq = block_sum_d(zq, sm);
-            for (int w = 0; w < kDrawWaves; ++w) qbad |= sm.ired[w] != 0;
-            qbad |= !(zq > 0.0);
-            r.inv_zq = 1.0 / zq;
-        }
-        __syncthreads();
-        bool badb = false;
-        const double S = tile_sums<DT, VEC>(r, 1, ntiles, sm, &badb);
-        qbad |= badb;
-        if (!qbad) {
-            if (S > 0.0) {
-                mode = 1;
-                W = S;
-            } else {
-                __syncthreads();
-                tile_sums<DT, VEC>(r, 0, ntiles, sm, nullptr);   // restore the p' tile sums
-            }
-        }
-    }
-    if (qbad) {
-        for (int t = tid; t <= K; t += kDrawThreads) a.out_tokens[rbase + t] = -1;
-        if (tid == 0) {
-            a.out_accept_len[b] = -1;
-            if (diag)
-                for (int k = 0; k < 2 * K + 2; ++k) diag[k] = NAN;
-        }
-        return;
-    }
-    const double target = static_cast<double>(a.u[rbase + K]) * W;
-    double wy;
-    const int y = draw_from<DT, VEC>(r, mode, ntiles, target, sm, &wy);
-
-    for (int t = tid; t <= K; t += kDrawThreads) {
-        int tok = -1;
-        if (t < j) tok = a.x[static_cast<long>(b) * K + t];
-        else if (t == j) tok = y;
-        a.out_tokens[rbase + t] = tok;
-    }
-    if (tid == 0) {
-        a.out_accept_len[b] = j;
-        if (diag) {
-            diag[2 * K] = static_cast<float>(mode == 1 ? W : W / zp);
-            diag[2 * K + 1] = static_cast<float>(wy / W);
-        }
-    }
-}
 
 // Greedy chain: argmax comparisons only.
 __global__ void chain_greedy_kernel(ChainArgs a) {
@@ -637,19 +288,6 @@ __global__ void alpha_greedy_kernel(AlphaArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_chain_dense(const ChainArgs& a, hipStream_t s) {
-    const int esz = a.dtype ? 2 : 4;
-    const bool vec = vec_ok(a.logits, a.V, esz) && vec_ok(a.q, a.V, 4);
-    if (a.dtype == 1) {
-        if (vec) hipLaunchKernelGGL((chain_dense_kernel<1, true>), dim3(a.B), dim3(kDrawThreads), 0, s, a);
-        else hipLaunchKernelGGL((chain_dense_kernel<1, false>), dim3(a.B), dim3(kDrawThreads), 0, s, a);
-    } else {
-        if (vec) hipLaunchKernelGGL((chain_dense_kernel<0, true>), dim3(a.B), dim3(kDrawThreads), 0, s, a);
-        else hipLaunchKernelGGL((chain_dense_kernel<0, false>), dim3(a.B), dim3(kDrawThreads), 0, s, a);
-    }
-    return hipGetLastError();
-}
 
 hipError_t launch_chain_greedy(const ChainArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(chain_greedy_kernel, dim3((a.B + 63) / 64), dim3(64), 0, s, a);
