@@ -2,6 +2,7 @@
 // Every call only enqueues kernels on the caller's stream.
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/spec_verify.h"
@@ -119,10 +120,22 @@ struct ChainPlan {
     uint32_t* qflags;
     TopkLists tk;
     PosRecord* rec;
-    DenseParts dp;
 };
 
-int dense_chunks(int V) { return (V + kDenseChunk - 1) / kDenseChunk; }
+// Relative half-width of the brackets the dense draw puts around the row
+// normalisers it takes from the row statistics (fp32 terms: within ~1e-6; the
+// draft power sums of a transformed draft: within ~1e-5).  Any width gives the
+// same result (a normaliser outside its bracket makes the draw recompute the
+// row exactly); it only sets how often that slow path runs.  The environment
+// variable SPEC_VERIFY_DENSE_BRACKET overrides it (0 forces the slow path).
+double dense_bracket(bool transformed) {
+    const char* env = getenv("SPEC_VERIFY_DENSE_BRACKET");
+    if (env && *env) {
+        const double v = atof(env);
+        if (v >= 0.0 && v < 0.5) return v;
+    }
+    return transformed ? 3e-5 : 4e-6;
+}
 
 ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {
     ChainPlan p{};
@@ -141,12 +154,6 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
             p.qsum = c.take<double>(Rd);
             p.qflags = c.take<uint32_t>(Rd);
         }
-        const size_t P = static_cast<size_t>(B) * dense_chunks(V);
-        p.dp.C = dense_chunks(V);
-        p.dp.pe = c.take<double>(P);
-        p.dp.pr = c.take<double>(P);
-        p.dp.pq = c.take<double>(P);
-        p.dp.pflag = c.take<uint32_t>(P);
     }
     return p;
 }
@@ -258,7 +265,6 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
     if (!greedy && topk_active(top_k, V)) {
         if (top_k > SPEC_TOPK_MAX || !topk_shape_ok(dtype, V)) return SPEC_EUNSUPPORTED;
     }
-    if (static_cast<long>(B) * dense_chunks(V) > 0x7fffffffL) return SPEC_EUNSUPPORTED;
     const size_t need = spec_chain_workspace_bytes(B, K, V, dtype, temperature, top_k);
     rc = check_workspace(workspace, workspace_bytes, need);
     if (rc) return rc;
@@ -312,7 +318,7 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
             ca.qsum = p.qsum;
             ca.qflags = p.qflags;
         }
-        SV_TRY(launch_chain_dense(ca, p.dp, s));
+        SV_TRY(launch_chain_dense(ca, dense_bracket(ca.transformed != 0), s));
     }
     return SPEC_OK;
 }

@@ -10,22 +10,35 @@
 // total; if rounding leaves no such i, the last index with positive weight.
 //
 // About 8% of draws on a wide (perplexity ~180) target distribution have a
-// CDF boundary within 1e-5 of u*S, so the row is recomputed in fp64 end to end:
-// one fp64 exponential per element (a table-driven exponential, below), fp64
-// weights and sums.  The one row per batch entry is split into chunks of 8192
-// elements spread over the whole chip, in three launches:
-//   dense_sum_kernel       per chunk: sum_i exp((z_i - m)/T) (and, when the
-//                          draft is transformed, sum_i q_i^(1/T)) in fp64;
-//   dense_residual_kernel  per chunk (rows with a rejection): sum of the
-//                          residual weights given the exact row normalisers;
-//                          invalid draft probabilities flag the chunk (E3);
-//   dense_draw_kernel      per batch entry: picks the chunk holding u*S from
-//                          the chunk sums, rescans that chunk element by
-//                          element and writes the outputs.
-// Every kernel derives the first rejection j from the row statistics itself
-// (one wave, K+1 lanes), so no kernel waits for another workgroup.
+// CDF boundary within 1e-5 of u*S, so the draw is computed in fp64 end to end
+// (one table-driven fp64 exponential per element, fp64 weights and sums).
+//
+// One pass over row j, although the residual needs the exact normaliser
+// Zp = sum_i e_i (e_i = exp((z_i - m)/T)) before any weight is known: the row
+// statistics give Zp' (fp32 terms, within ~1e-6).  With iz = 1/Zp' and
+// d_i = e_i*iz - w_i (w_i = q'_i, the draft weight), the pass sums per chunk
+// of 4096 elements
+//     E = sum e_i,   R = sum max(0, d_i),   P = sum_{d_i > 0} w_i,
+// and lists the elements with |d_i| within a relative delta of zero
+// ("undecided").  For every other element the sign of e_i/Zp - w_i equals
+// that of d_i as long as Zp lies in Zp'(1 -+ delta), and there the residual is
+// rho*d_i + (rho - 1)*w_i with rho = Zp'/Zp, so the chunk's residual mass is
+//     rho*R + (rho - 1)*P + (exact share of the listed elements),
+// with Zp = sum E known after the pass.  P only scales a term of relative size
+// delta, so its terms are fp32.  The bracket is checked afterwards (else, and
+// when the list overflowed, a second pass recomputes the chunk sums exactly),
+// so the result never depends on the accuracy of Zp'.  A transformed draft
+// (T != 1) brackets its normaliser Zq the same way.
+//
+// dense_row_kernel: one workgroup of 512 threads per batch entry.  Wave 0 runs
+// the K ratio tests on the row statistics (lanes k = 0..K); the workgroup then
+// streams row j chunk by chunk, loading chunk c+1 while it computes chunk c,
+// keeps the chunk sums in LDS, and finishes with the draw: the chunk holding
+// u*S, rescanned element by element.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -35,52 +48,83 @@ namespace sv {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kEPT = kDenseChunk / kThreads;        // 32 elements per thread per chunk
+constexpr int kEPT = kDenseChunk / kThreads;        // 8 elements per thread per chunk
 constexpr int kSub = kEPT / 8;                      // 8-element groups per thread
+constexpr int kMaxChunks = (kMaxV + kDenseChunk - 1) / kDenseChunk;
+constexpr int kListCap = 64;                        // undecided elements per row
 
-// exp(x) for x <= 0 in fp64, by Tang's table-driven method (ACM TOMS 15(2),
-// 1989): x = N ln2/64 + r with N = round(64 x / ln2) and |r| <= ln2/128, so
-// exp(x) = 2^(N div 64) * 2^((N mod 64)/64) * exp(r); exp(r) - 1 is its Taylor
-// series to r^6 (truncation < 3e-20 relative).  tbl[t] = 2^(t/64).  Arguments
-// below -800 give 0 (as exp does in double); x = -inf is such an argument.
-__device__ __forceinline__ double exp_nonpos(double x, const double* tbl) {
-    constexpr double kInvStep = 92.33248261689366;           // 64 / ln 2
-    constexpr double kStepHi = 0x1.62e42fefa39efp-7;         // ln 2 / 64, leading part
-    constexpr double kStepLo = 0x1.abc9e3b39803fp-62;        // ln 2 / 64 - kStepHi
-    x = fmax(x, -800.0);
-    const double n = __builtin_rint(x * kInvStep);
+// exp(x) for x <= 0 in fp64 by Tang's table-driven method (ACM TOMS 15(2),
+// 1989), with 256 table entries.  The caller passes y = x * 256/ln2 (folded
+// into one fma with the temperature and the row maximum); with N = round(y)
+// and f = y - N (exact), exp(x) = 2^(N div 256) * 2^((N mod 256)/256) * e^(f ln2/256),
+// |f ln2/256| <= 0.00136, and e^t - 1 is its Taylor series to t^4 (truncation
+// < 4e-17 relative).  tbl[k] = 2^(k/256).  y below -800*256/ln2 gives 0 (as exp
+// does in double); y = -inf is such an argument.
+//
+// The constants arrive as kernel arguments: they then sit in scalar registers
+// and feed v_fma_f64 directly, instead of being rebuilt in vector registers
+// for every element.
+struct ExpConsts {
+    double scale;        // 256 / ln 2
+    double floor;        // -800 * scale
+    double b1, b2, b3, b4;   // (ln2/256)^k / k!
+};
+inline ExpConsts exp_consts() {
+    ExpConsts k;
+    k.scale = 0x1.71547652b82fep+8;
+    k.floor = -800.0 * k.scale;
+    k.b1 = 0x1.62e42fefa39efp-9;
+    k.b2 = 0x1.ebfbdff82c58fp-19;
+    k.b3 = 0x1.c6b08d704a0c0p-29;
+    k.b4 = 0x1.3b2ab6fba4e77p-39;
+    return k;
+}
+constexpr int kTableSize = 256;
+
+__device__ __forceinline__ double exp_scaled(double y, const double* tbl, const ExpConsts& k) {
+    y = fmax(y, k.floor);
+    const double n = __builtin_rint(y);
     const int N = static_cast<int>(n);
-    double r = fma(-n, kStepHi, x);
-    r = fma(-n, kStepLo, r);
-    double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
-    p = fma(r, p, 1.0 / 24.0);
-    p = fma(r, p, 1.0 / 6.0);
-    p = fma(r, p, 0.5);
-    p = fma(r, p, 1.0);
-    p *= r;                                                  // exp(r) - 1
-    const double t = tbl[N & 63];
-    return ldexp(fma(t, p, t), N >> 6);
+    const double f = y - n;
+    double p = fma(f, k.b4, k.b3);
+    p = fma(p, f, k.b2);
+    p = fma(p, f, k.b1);
+    p *= f;                                                  // e^(f ln2/256) - 1
+    const double t = tbl[N & (kTableSize - 1)];
+    return ldexp(fma(t, p, t), N >> 8);
 }
 
-__device__ __forceinline__ void fill_exp_table(double* tbl) {
-    if (threadIdx.x < 64) tbl[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) * (1.0 / 64.0));
+// y for exp((z - m)/T): one fma per element with k1 = scale/T, mk1 = -m*k1.
+struct ExpArg {
+    double k1, mk1;
+};
+__device__ __forceinline__ ExpArg exp_arg(double m, double invT, const ExpConsts& k) {
+    const double k1 = invT * k.scale;
+    return ExpArg{k1, -m * k1};
+}
+__device__ __forceinline__ double exp_of(float z, const ExpArg& g, const double* tbl, const ExpConsts& k) {
+    return exp_scaled(fma(static_cast<double>(z), g.k1, g.mk1), tbl, k);
 }
 
-// Eight consecutive logits from i0 (a multiple of 8); -inf past V.
+// Eight consecutive logits from i0 (a multiple of 8); -inf past V.  With VEC
+// the row is 16-byte aligned and V a multiple of the vector length, so each
+// vector lies wholly inside or wholly past the row.
 template <int DT, bool VEC, bool NT>
 __device__ __forceinline__ void load8_z(const char* row, int i0, int V, float out[8]) {
     using E = Elem<DT>;
-    if (VEC && i0 + 8 <= V) {
+    if (VEC) {
         const u32x4* p = reinterpret_cast<const u32x4*>(row + static_cast<long>(i0) * E::kBytes);
+        constexpr uint32_t ninf = DT == 1 ? 0xff80ff80u : 0xff800000u;
+        const u32x4 pad = u32x4{ninf, ninf, ninf, ninf};
         if (DT == 1) {
-            const u32x4 v = NT ? load_stream(p) : p[0];
+            const u32x4 v = (i0 < V) ? (NT ? load_stream(p) : p[0]) : pad;
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[e] = E::get(v, e);
         } else {
-            const u32x4 a = NT ? load_stream(p) : p[0];
-            const u32x4 b = NT ? load_stream(p + 1) : p[1];
+            const u32x4 a = (i0 < V) ? (NT ? load_stream(p) : p[0]) : pad;
+            const u32x4 b = (i0 + 4 < V) ? (NT ? load_stream(p + 1) : p[1]) : pad;
 #pragma unroll
             for (int e = 0; e < 4; ++e) { out[e] = __uint_as_float(a[e]); out[4 + e] = __uint_as_float(b[e]); }
         }
@@ -93,10 +137,11 @@ __device__ __forceinline__ void load8_z(const char* row, int i0, int V, float ou
 // Eight consecutive draft probabilities from i0; 0 past V.
 template <bool VEC, bool NT>
 __device__ __forceinline__ void load8_q(const float* row, int i0, int V, float out[8]) {
-    if (VEC && i0 + 8 <= V) {
+    if (VEC) {
         const u32x4* p = reinterpret_cast<const u32x4*>(row + i0);
-        const u32x4 a = NT ? load_stream(p) : p[0];
-        const u32x4 b = NT ? load_stream(p + 1) : p[1];
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+        const u32x4 a = (i0 < V) ? (NT ? load_stream(p) : p[0]) : zero;
+        const u32x4 b = (i0 + 4 < V) ? (NT ? load_stream(p + 1) : p[1]) : zero;
 #pragma unroll
         for (int e = 0; e < 4; ++e) { out[e] = __uint_as_float(a[e]); out[4 + e] = __uint_as_float(b[e]); }
         return;
@@ -105,13 +150,79 @@ __device__ __forceinline__ void load8_q(const float* row, int i0, int V, float o
     for (int e = 0; e < 8; ++e) out[e] = (i0 + e < V) ? row[i0 + e] : 0.f;
 }
 
-// Ratio tests of batch row b from the row statistics (lanes k = 0..K of wave 0):
-// sets *j (first rejection, K if none) and *err (E1..E5); writes p'_k(x_k) and
-// q'_k(x_k) to diag when given.  Call from the whole of wave 0.
+// The same eight elements kept packed as loaded (bf16 pairs or fp32 words): half
+// the registers of the widened values for bf16.  kZW vectors hold 8 logits.
+template <int DT> struct Raw8 {
+    static constexpr int kZW = DT == 1 ? 1 : 2;
+    u32x4 z[kZW];
+    u32x4 q[2];
+    __device__ __forceinline__ float zf(int e) const {
+        return DT == 1 ? Elem<1>::get(z[0], e) : __uint_as_float(z[e >> 2][e & 3]);
+    }
+    __device__ __forceinline__ float qf(int e) const { return __uint_as_float(q[e >> 2][e & 3]); }
+};
+// GUARD: the vectors may lie past the row's end.  Loads are then issued from a
+// clamped (valid) address and replaced by padding, so that no load sits behind a
+// branch and the wait for one buffer does not also wait for the other.
+template <int DT, bool VEC, bool GUARD>
+__device__ __forceinline__ void load8_raw(const char* zrow, const float* qrow, bool with_q, int i0, int V,
+                                          Raw8<DT>& r) {
+    constexpr uint32_t ninf = DT == 1 ? 0xff80ff80u : 0xff800000u;
+    const u32x4 pad = u32x4{ninf, ninf, ninf, ninf};
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+    if (VEC) {
+        const u32x4* pz = reinterpret_cast<const u32x4*>(zrow);
+        const u32x4* pq = reinterpret_cast<const u32x4*>(qrow);
+        constexpr int zv = 8 / Raw8<DT>::kZW;              // elements per z vector
+        if (!GUARD) {
+#pragma unroll
+            for (int w = 0; w < Raw8<DT>::kZW; ++w) r.z[w] = load_stream(pz + (i0 + w * zv) / zv);
+            if (with_q) {
+                r.q[0] = load_stream(pq + i0 / 4);
+                r.q[1] = load_stream(pq + i0 / 4 + 1);
+            }
+            return;
+        }
+#pragma unroll
+        for (int w = 0; w < Raw8<DT>::kZW; ++w) {
+            const int i = i0 + w * zv;
+            const u32x4 v = load_stream(pz + (i < V ? i : 0) / zv);
+            r.z[w] = i < V ? v : pad;
+        }
+        if (with_q) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const int i = i0 + 4 * w;
+                const u32x4 v = load_stream(pq + (i < V ? i : 0) / 4);
+                r.q[w] = i < V ? v : zero;
+            }
+        }
+        return;
+    }
+    float z[8], q[8];
+    load8_z<DT, false, false>(zrow, i0, V, z);
+    if (DT == 1) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            r.z[0][w] = (__float_as_uint(z[2 * w]) >> 16) | (__float_as_uint(z[2 * w + 1]) & 0xffff0000u);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.z[e >> 2][e & 3] = __float_as_uint(z[e]);
+    }
+    if (with_q) {
+        load8_q<false, false>(qrow, i0, V, q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.q[e >> 2][e & 3] = __float_as_uint(q[e]);
+    }
+}
+
+// Ratio tests of one batch row from the row statistics, lanes k = 0..K of a
+// wave: sets j (first rejection, K if none) and err (E1, E2, E3 at x_k, E5);
+// writes p'_k(x_k) and q'_k(x_k) to diag when given.
 template <bool TR>
-__device__ __forceinline__ void first_reject(const ChainArgs& a, int b, float* diag, int* j_out, int* err_out) {
+__device__ __forceinline__ void first_reject(const ChainArgs& a, int b, float* diag, int& j_out, bool& err_out) {
     const int K = a.K, V = a.V;
-    const int k = threadIdx.x;
+    const int k = threadIdx.x & (kWave - 1);
     const long rbase = static_cast<long>(b) * (K + 1);
     bool bad = false, rej = false;
     double pk = NAN, qk = NAN;
@@ -143,10 +254,8 @@ __device__ __forceinline__ void first_reject(const ChainArgs& a, int b, float* d
         diag[k] = bm ? NAN : static_cast<float>(pk);
         diag[K + k] = bm ? NAN : static_cast<float>(qk);
     }
-    if (k == 0) {
-        *j_out = rm ? __ffsll(static_cast<long long>(rm)) - 1 : K;
-        *err_out = bm != 0ull;
-    }
+    j_out = rm ? __ffsll(static_cast<long long>(rm)) - 1 : K;
+    err_out = bm != 0ull;
 }
 
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -160,246 +269,326 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
     return t;
 }
 
-// Sum over a batch row's chunks, in chunk order (the same order in every kernel).
-__device__ __forceinline__ double chunk_total(const double* part, long base, int C) {
-    double s = 0.0;
-    for (int c = 0; c < C; ++c) s += part[base + c];
-    return s;
-}
-
-template <int DT, bool VEC, bool TR>
-__global__ __launch_bounds__(kThreads) void dense_sum_kernel(ChainArgs a, DenseParts d) {
-    __shared__ double tbl[64];
-    __shared__ double red[2][kWaves];
-    __shared__ int s_j, s_err;
-    const long blk = blockIdx.x;
-    const int b = static_cast<int>(blk / d.C);
-    const int c = static_cast<int>(blk - static_cast<long>(b) * d.C);
-    fill_exp_table(tbl);
-    if (threadIdx.x < kWave) first_reject<TR>(a, b, nullptr, &s_j, &s_err);
-    __syncthreads();
-    if (s_err) return;
-    const int j = s_j, K = a.K, V = a.V;
-    const long zrow = static_cast<long>(b) * (K + 1) + j;
-    const char* zr = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
-    const double m = static_cast<double>(a.st.m[zrow]);
-    const int start = c * kDenseChunk;
-    float z[kSub][8];
-#pragma unroll
-    for (int g = 0; g < kSub; ++g) load8_z<DT, VEC, true>(zr, start + (g * kThreads + threadIdx.x) * 8, V, z[g]);
-    double acc = 0.0;
-#pragma unroll
-    for (int g = 0; g < kSub; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += exp_nonpos((static_cast<double>(z[g][e]) - m) * a.invT, tbl);
-    double accq = 0.0;
-    if (TR && j < K) {
-        const float* qr = a.q + (static_cast<long>(b) * K + j) * V;
-#pragma unroll 1
-        for (int g = 0; g < kSub; ++g) {
-            float q[8];
-            load8_q<VEC, true>(qr, start + (g * kThreads + threadIdx.x) * 8, V, q);
-#pragma unroll 1
-            for (int e = 0; e < 8; ++e)
-                if (q[e] > 0.f) accq += pow(static_cast<double>(q[e]), a.invT);
-        }
-    }
-    acc = block_sum(acc, red[0]);
-    if (TR) accq = block_sum(accq, red[1]);
-    if (threadIdx.x == 0) {
-        d.pe[blk] = acc;
-        if (TR) d.pq[blk] = accq;
-    }
-}
-
-// Residual weight max(0, e_i/Zp - q'_i), q'_i = q_i or (TR) q_i^(1/T)/Zq.
+// Draft weight w_i: q_i, or q_i^(1/T) when the draft is transformed (0 stays 0).
 template <bool TR>
-__device__ __forceinline__ double residual_w(double e, float q, double invZp, double invT, double invZq) {
-    double qq = static_cast<double>(q);
-    if (TR) qq = (q > 0.f) ? pow(qq, invT) * invZq : 0.0;
-    const double r = e * invZp - qq;
-    return r > 0.0 ? r : 0.0;
+__device__ __forceinline__ double draft_w(float q, double invT) {
+    if (!TR) return static_cast<double>(q);
+    return q > 0.f ? pow(static_cast<double>(q), invT) : 0.0;
 }
 
-template <int DT, bool VEC, bool TR>
-__global__ __launch_bounds__(kThreads) void dense_residual_kernel(ChainArgs a, DenseParts d) {
-    __shared__ double tbl[64];
-    __shared__ double red[kWaves];
-    __shared__ int s_j, s_err;
-    const long blk = blockIdx.x;
-    const int b = static_cast<int>(blk / d.C);
-    const int c = static_cast<int>(blk - static_cast<long>(b) * d.C);
-    fill_exp_table(tbl);
-    if (threadIdx.x < kWave) first_reject<TR>(a, b, nullptr, &s_j, &s_err);
-    __syncthreads();
-    const int j = s_j, K = a.K, V = a.V;
-    if (s_err || j == K) return;
-    const long zrow = static_cast<long>(b) * (K + 1) + j;
-    const char* zr = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
-    const float* qr = a.q + (static_cast<long>(b) * K + j) * V;
-    const double m = static_cast<double>(a.st.m[zrow]);
-    const long pbase = static_cast<long>(b) * d.C;
-    const double invZp = 1.0 / chunk_total(d.pe, pbase, d.C);
-    const double invZq = TR ? 1.0 / chunk_total(d.pq, pbase, d.C) : 1.0;
-    const int start = c * kDenseChunk;
-    float z[kSub][8], q[kSub][8];
-#pragma unroll
-    for (int g = 0; g < kSub; ++g) {
-        const int i0 = start + (g * kThreads + threadIdx.x) * 8;
-        load8_z<DT, VEC, true>(zr, i0, V, z[g]);
-        load8_q<VEC, true>(qr, i0, V, q[g]);
-    }
-    double acc = 0.0;
-    bool bad = false;
-    auto one = [&](int g, int e) {
-        const int i = start + (g * kThreads + threadIdx.x) * 8 + e;
-        bad |= (i < V) && !q_ok(q[g][e]);
-        const double ex = exp_nonpos((static_cast<double>(z[g][e]) - m) * a.invT, tbl);
-        acc += residual_w<TR>(ex, q[g][e], invZp, a.invT, invZq);
-    };
-    if constexpr (TR) {
-        // q^(1/T) in fp64 is long: one element at a time keeps the registers in check.
-#pragma unroll
-        for (int g = 0; g < kSub; ++g)
-#pragma unroll 1
-            for (int e = 0; e < 8; ++e) one(g, e);
-    } else {
-#pragma unroll
-        for (int g = 0; g < kSub; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) one(g, e);
-    }
-    const unsigned long long bb = __ballot(bad);
-    acc = block_sum(acc, red);
-    __shared__ uint32_t s_bad;
-    if (threadIdx.x == 0) s_bad = 0;
-    __syncthreads();
-    if ((threadIdx.x & (kWave - 1)) == 0 && bb) atomicOr(&s_bad, 1u);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        d.pr[blk] = acc;
-        d.pflag[blk] = s_bad;
-    }
+// True when Z lies strictly inside Zapprox(1 -+ delta), with room for rounding.
+__device__ __forceinline__ bool in_bracket(double Z, double Zapprox, double delta) {
+    return Z > Zapprox * (1.0 - delta) * (1.0 + 1e-12) && Z < Zapprox * (1.0 + delta) * (1.0 - 1e-12);
 }
 
+struct RowSmem {
+    double tbl[kTableSize];
+    double we[kMaxChunks][kWaves];     // per-wave chunk sums: E
+    double wr[kMaxChunks][kWaves];     //   R (or the exact residual in the second pass)
+    float wp[kMaxChunks][kWaves];      //   P
+    double part[kMaxChunks];           // chunk weights of the draw
+    double pe[kMaxChunks];             // chunk sums of e
+    int32_t li[kListCap];              // undecided elements
+    double le[kListCap], lw[kListCap];
+    double red[kWaves];
+    int ired[kWaves];
+    int n_list, j, err, chunk, fallback;
+    uint32_t qbad;
+    double before;
+};
+
 template <int DT, bool VEC, bool TR>
-__global__ __launch_bounds__(kThreads, 2) void dense_draw_kernel(ChainArgs a, DenseParts d) {
-    __shared__ double tbl[64];
-    __shared__ double red[kWaves];
-    __shared__ int ired[kWaves];
-    __shared__ int s_j, s_err, s_chunk, s_fallback;
-    __shared__ double s_before;
+__global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, double bracket, ExpConsts ek) {
+    __shared__ RowSmem sm;
     const int b = blockIdx.x;
-    const int K = a.K, V = a.V, C = d.C;
+    const int K = a.K, V = a.V;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int C = (V + kDenseChunk - 1) / kDenseChunk;
+    const int C_full = V / kDenseChunk;              // chunks wholly inside the row
     const long rbase = static_cast<long>(b) * (K + 1);
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
-    fill_exp_table(tbl);
-    if (tid < kWave) first_reject<TR>(a, b, diag, &s_j, &s_err);
-    __syncthreads();
-    const int j = s_j;
-    const long pbase = static_cast<long>(b) * C;
-    bool err = s_err != 0;
-    double Zp = 1.0, Zq = 1.0, S = 0.0;
-    if (!err) {
-        Zp = chunk_total(d.pe, pbase, C);
-        if (j < K) {
-            S = chunk_total(d.pr, pbase, C);
-            for (int c = 0; c < C; ++c) err |= d.pflag[pbase + c] != 0u;
-            if (TR) {
-                Zq = chunk_total(d.pq, pbase, C);
-                err |= !(Zq > 0.0);
-            }
-        }
+
+    if (tid < kWave) {
+        int j;
+        bool err;
+        first_reject<TR>(a, b, diag, j, err);
+        if (tid == 0) { sm.j = j; sm.err = err; sm.n_list = 0; sm.qbad = 0; }
     }
-    if (err) {
+    for (int t = tid; t < kTableSize; t += kThreads) sm.tbl[t] = exp2(static_cast<double>(t) * (1.0 / kTableSize));
+    __syncthreads();
+    const int j = sm.j;
+    auto fail_row = [&]() {
         for (int t = tid; t <= K; t += kThreads) a.out_tokens[rbase + t] = -1;
         if (tid == 0) a.out_accept_len[b] = -1;
         if (diag)
             for (int t = tid; t < 2 * K + 2; t += kThreads) diag[t] = NAN;
-        return;
+    };
+    if (sm.err) { fail_row(); return; }
+
+    const bool res = j < K;
+    const long zrow = rbase + j;
+    const long qrow = static_cast<long>(b) * K + (res ? j : 0);
+    const char* zr = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
+    const float* qr = a.q + qrow * V;
+    const double* tbl = sm.tbl;
+    const ExpArg g = exp_arg(static_cast<double>(a.st.m[zrow]), a.invT, ek);
+    const double Zp_ap = a.st.Z[zrow];
+    const double Zq_ap = (TR && res) ? a.qsum[qrow] : 1.0;
+    const double iz = 1.0 / Zp_ap, iq = TR ? 1.0 / Zq_ap : 1.0;
+    // |d| > tol*(e*iz + w') (w' = w*iq, tol >= delta/(1 - delta) plus rounding room)
+    // fixes the sign of the residual over the brackets; since e*iz = d + w' this
+    // holds whenever |d| > tol2*w'.
+    const double tol = bracket * (1.0 + 2.0 * bracket) + 1e-12;
+    const double tol2 = 2.0 * tol / (1.0 - tol);
+
+    // ---- one pass over row j ----
+    double sq_tot = 0.0;                   // transformed draft: sum w over the thread's elements
+    auto body = [&](auto res_tag) {
+        constexpr bool RES = decltype(res_tag)::value;
+        using Buf = Raw8<DT>[kSub];
+        auto load = [&](int c, Buf& rb, auto guard_tag) {
+            constexpr bool GUARD = decltype(guard_tag)::value;
+#pragma unroll
+            for (int s = 0; s < kSub; ++s)
+                load8_raw<DT, VEC, GUARD>(zr, qr, RES, c * kDenseChunk + (s * kThreads + tid) * 8, V, rb[s]);
+        };
+        auto compute = [&](int c, Buf& rb) {
+            double se = 0.0, sr = 0.0;
+            float sp = 0.f, qmin = 0.f, qmax = 0.f;
+            bool und = false;
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) {
+                if (RES) {
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        qmin = minimum3(qmin, rb[s].qf(e), rb[s].qf(e + 1));
+                        qmax = maximum3(qmax, rb[s].qf(e), rb[s].qf(e + 1));
+                    }
+                }
+                auto one = [&](int e) {
+                    const double ex = exp_of(rb[s].zf(e), g, tbl, ek);
+                    se += ex;
+                    if (RES) {
+                        const float qv = rb[s].qf(e);
+                        const double w = draft_w<TR>(qv, a.invT);
+                        if (TR) sq_tot += w;
+                        const double wq = TR ? w * iq : w;
+                        const double dd = fma(ex, iz, -wq);
+                        sr += fmax(dd, 0.0);
+                        sp += dd > 0.0 ? (TR ? static_cast<float>(w) : qv) : 0.f;
+                        und |= fabs(dd) <= tol2 * wq;
+                    }
+                };
+                if (TR) {
+#pragma unroll 1
+                    for (int e = 0; e < 8; ++e) one(e);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) one(e);
+                }
+            }
+            if (RES) {
+                if (__ballot(!(qmin >= 0.f && qmax < INFINITY)) && lane == 0) atomicOr(&sm.qbad, 1u);
+                // Undecided elements are rare (about one per row): list them in a
+                // wave-uniform branch, re-reading the thread's elements of the chunk.
+                if (__ballot(und) && und) {
+#pragma unroll 1
+                    for (int k = 0; k < kEPT; ++k) {
+                        const int i = c * kDenseChunk + ((k >> 3) * kThreads + tid) * 8 + (k & 7);
+                        if (i >= V) break;
+                        const double ex = exp_of(Elem<DT>::scalar(zr, i), g, tbl, ek);
+                        const double w = draft_w<TR>(qr[i], a.invT);
+                        const double wq = TR ? w * iq : w;
+                        const double dd = fma(ex, iz, -wq);
+                        if (fabs(dd) <= tol2 * wq) {
+                            const int p = atomicAdd(&sm.n_list, 1);
+                            if (p < kListCap) { sm.li[p] = i; sm.le[p] = ex; sm.lw[p] = w; }
+                        }
+                    }
+                }
+            }
+            se = wave_sum(se);
+            if (RES) {
+                sr = wave_sum(sr);
+                sp = wave_sum(sp);
+            }
+            if (lane == 0) {
+                sm.we[c][wid] = se;
+                sm.wr[c][wid] = sr;
+                sm.wp[c][wid] = sp;
+            }
+        };
+        // Full chunks: chunk c+1 is in flight while chunk c is computed (two register
+        // buffers).  The loads are unconditional (indices clamped to the last full
+        // chunk; the surplus loads are discarded) so that the wait for one buffer
+        // does not also wait for the other.  The partial last chunk comes after.
+        Buf ra, rn;
+        if (C_full > 0) load(0, ra, std::false_type{});
+#pragma unroll 1
+        for (int c = 0; c < C_full; c += 2) {
+            load(min(c + 1, C_full - 1), rn, std::false_type{});
+            __builtin_amdgcn_sched_barrier(0);     // keep the prefetch ahead of the compute
+            compute(c, ra);
+            load(min(c + 2, C_full - 1), ra, std::false_type{});
+            __builtin_amdgcn_sched_barrier(0);
+            if (c + 1 < C_full) compute(c + 1, rn);
+        }
+        if (C_full < C) {
+            load(C_full, ra, std::true_type{});
+            compute(C_full, ra);
+        }
+    };
+    if (res) body(std::true_type{});
+    else body(std::false_type{});
+    __syncthreads();
+    for (int c = tid; c < C; c += kThreads) {
+        double e = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) e += sm.we[c][w];
+        sm.pe[c] = e;
     }
-    const bool residual = j < K && S > 0.0;
+    __syncthreads();
+    double Zp = 0.0;
+    for (int c = 0; c < C; ++c) Zp += sm.pe[c];
+    const double invZp = 1.0 / Zp;
+    double Zq = 1.0;
+    if (TR && res) Zq = block_sum(sq_tot, sm.red);   // exact normaliser of the transformed draft
+    double S = 0.0;
+    bool residual = false;
+    if (res) {
+        if (sm.qbad || (TR && !(Zq > 0.0))) { fail_row(); return; }
+        const double invZq = 1.0 / Zq;
+        const bool exact_ok = sm.n_list <= kListCap && in_bracket(Zp, Zp_ap, bracket) &&
+                              (!TR || in_bracket(Zq, Zq_ap, bracket));
+        if (exact_ok) {
+            // over d > 0 the residual e/Zp - w/Zq is rho*d + kap*w, rho = Zp'/Zp
+            const double rho = Zp_ap * invZp;
+            const double kap = TR ? rho * iq - invZq : (Zp_ap - Zp) * invZp;
+            const int n = sm.n_list;
+            for (int c = tid; c < C; c += kThreads) {
+                double r = 0.0;
+                float pp = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) { r += sm.wr[c][w]; pp += sm.wp[c][w]; }
+                double pc = rho * r + kap * static_cast<double>(pp);
+                for (int t = 0; t < n; ++t) {
+                    if (sm.li[t] / kDenseChunk != c) continue;
+                    const double e = sm.le[t], w = sm.lw[t];
+                    const double wq = TR ? w * iq : w;
+                    const double dd = fma(e, iz, -wq);
+                    const double rr = e * invZp - w * invZq;
+                    pc += (rr > 0.0 ? rr : 0.0) - (dd > 0.0 ? rho * dd + kap * w : 0.0);
+                }
+                sm.part[c] = pc > 0.0 ? pc : 0.0;
+            }
+        } else {
+            // Exact chunk sums (a normaliser outside its bracket or the list overflowed):
+            // never expected, always correct.
+#pragma unroll 1
+            for (int c = 0; c < C; ++c) {
+                double sr = 0.0;
+#pragma unroll 1
+                for (int s = 0; s < kSub; ++s) {
+                    const int i0 = c * kDenseChunk + (s * kThreads + tid) * 8;
+                    float z[8], q[8];
+                    load8_z<DT, VEC, false>(zr, i0, V, z);
+                    load8_q<VEC, false>(qr, i0, V, q);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const double rr = exp_of(z[e], g, tbl, ek) * invZp - draft_w<TR>(q[e], a.invT) * invZq;
+                        sr += rr > 0.0 ? rr : 0.0;
+                    }
+                }
+                sr = block_sum(sr, sm.red);
+                if (tid == 0) sm.part[c] = sr;
+            }
+        }
+        __syncthreads();
+        for (int c = 0; c < C; ++c) S += sm.part[c];
+        __syncthreads();
+        residual = S > 0.0;
+    }
+    if (!residual) {
+        for (int c = tid; c < C; c += kThreads) sm.part[c] = sm.pe[c];
+        __syncthreads();
+    }
+    const double invZq = 1.0 / Zq;
+
+    // ---- draw: the chunk holding u*W, then its elements ----
     const double W = residual ? S : Zp;
-    const double* part = residual ? d.pr : d.pe;
     const double target = static_cast<double>(a.u[rbase + K]) * W;
     if (tid == 0) {
         double before = 0.0;
         int chunk = -1, last = 0;
         for (int c = 0; c < C; ++c) {
-            const double pc = part[pbase + c];
+            const double pc = sm.part[c];
             if (target < before + pc) { chunk = c; break; }
             before += pc;
             if (pc > 0.0) last = c;
         }
-        s_fallback = chunk < 0;
-        if (chunk < 0) {        // rounding: u*W at or past the total
-            chunk = last;
-            before = 0.0;       // unused
-        }
-        s_chunk = chunk;
-        s_before = before;
+        sm.fallback = chunk < 0;     // rounding: u*W at or past the total
+        sm.chunk = chunk < 0 ? last : chunk;
+        sm.before = before;
     }
     __syncthreads();
-    const int chunk = s_chunk;
-    const bool fallback = s_fallback != 0;
+    const int chunk = sm.chunk;
+    const bool fallback = sm.fallback != 0;
 
-    // Rescan the chunk: thread t holds elements [t*32, t*32 + 32) of it.
-    const long zrow = rbase + j;
-    const char* zr = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
-    const float* qr = residual ? a.q + (static_cast<long>(b) * K + j) * V : nullptr;
-    const double m = static_cast<double>(a.st.m[zrow]);
-    const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
-    const int i0 = chunk * kDenseChunk + tid * kEPT;
-    // Two passes over the thread's 32 elements (recomputing beats holding 32
-    // doubles): thread sums, then the crossing after the block's prefix.
-    auto weights8 = [&](int g, double wt[8]) {
+    // Weights of 8 consecutive elements from i0: exp (p' draw) or residual.
+    auto weights8 = [&](int i0, double wt[8]) {
         float z[8], q[8];
-        load8_z<DT, VEC, false>(zr, i0 + 8 * g, V, z);
-        if (residual) load8_q<VEC, false>(qr, i0 + 8 * g, V, q);
+        load8_z<DT, VEC, false>(zr, i0, V, z);
+        if (residual) load8_q<VEC, false>(qr, i0, V, q);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const double ex = exp_nonpos((static_cast<double>(z[e]) - m) * a.invT, tbl);
-            wt[e] = residual ? residual_w<TR>(ex, q[e], invZp, a.invT, invZq) : ex;
-            if (i0 + 8 * g + e >= V) wt[e] = 0.0;
+            const double ex = exp_of(z[e], g, tbl, ek);
+            double w = ex;
+            if (residual) {
+                w = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
+                w = w > 0.0 ? w : 0.0;
+            }
+            wt[e] = (i0 + e < V) ? w : 0.0;
         }
     };
+    // Thread t holds elements [t*8, t*8 + 8) of the chunk.  Two passes
+    // (recomputing beats holding 16 doubles): thread sums, then the crossing.
+    const int i0 = chunk * kDenseChunk + tid * kEPT;
     double s = 0.0, wlast = 0.0;
     int lastpos = -1;
 #pragma unroll 1
-    for (int g = 0; g < kSub; ++g) {
+    for (int sub = 0; sub < kSub; ++sub) {
         double wt[8];
-        weights8(g, wt);
+        weights8(i0 + 8 * sub, wt);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             s += wt[e];
-            if (wt[e] > 0.0) { lastpos = i0 + 8 * g + e; wlast = wt[e]; }
+            if (wt[e] > 0.0) { lastpos = i0 + 8 * sub + e; wlast = wt[e]; }
         }
     }
-    // Exclusive prefix of the thread sums in index order.
     double incl = s;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
         const double t = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += t;
     }
-    if (lane == kWave - 1) red[wid] = incl;
     __syncthreads();
-    double cum = s_before;
-    for (int x = 0; x < wid; ++x) cum += red[x];
+    if (lane == kWave - 1) sm.red[wid] = incl;
+    __syncthreads();
+    double cum = sm.before;
+    for (int x = 0; x < wid; ++x) cum += sm.red[x];
     cum += incl - s;
     int found = 0x7fffffff;
     double wfound = 0.0;
     // Threads whose span ends past u*W rescan; the smallest crossing wins.
     if (!fallback && target < cum + s) {
 #pragma unroll 1
-        for (int g = 0; g < kSub && found == 0x7fffffff; ++g) {
+        for (int sub = 0; sub < kSub && found == 0x7fffffff; ++sub) {
             double wt[8];
-            weights8(g, wt);
+            weights8(i0 + 8 * sub, wt);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 cum += wt[e];
-                if (found == 0x7fffffff && wt[e] > 0.0 && target < cum) { found = i0 + 8 * g + e; wfound = wt[e]; }
+                if (found == 0x7fffffff && wt[e] > 0.0 && target < cum) { found = i0 + 8 * sub + e; wfound = wt[e]; }
             }
         }
     }
@@ -407,16 +596,16 @@ __global__ __launch_bounds__(kThreads, 2) void dense_draw_kernel(ChainArgs a, De
     int y = wave_min_int(found);
     const int lp = wave_max_int(lastpos);
     __syncthreads();
-    if (lane == 0) { ired[wid] = y; red[wid] = static_cast<double>(lp); }
+    if (lane == 0) { sm.ired[wid] = y; sm.red[wid] = static_cast<double>(lp); }
     __syncthreads();
-    y = ired[0];
-    int lpb = static_cast<int>(red[0]);
+    y = sm.ired[0];
+    int lpb = static_cast<int>(sm.red[0]);
 #pragma unroll
-    for (int x = 1; x < kWaves; ++x) { y = min(y, ired[x]); lpb = max(lpb, static_cast<int>(red[x])); }
+    for (int x = 1; x < kWaves; ++x) { y = min(y, sm.ired[x]); lpb = max(lpb, static_cast<int>(sm.red[x])); }
     const bool crossed = y != 0x7fffffff;
     if (!crossed) y = lpb;
     const double my = crossed ? (found == y ? wfound : 0.0) : (lastpos == y ? wlast : 0.0);
-    const double wy = block_sum(my, red);
+    const double wy = block_sum(my, sm.red);
 
     for (int t = tid; t <= K; t += kThreads) {
         int tok = -1;
@@ -434,29 +623,22 @@ __global__ __launch_bounds__(kThreads, 2) void dense_draw_kernel(ChainArgs a, De
 }
 
 template <int DT, bool VEC, bool TR>
-hipError_t dense_launch(const ChainArgs& a, const DenseParts& d, unsigned chunks, hipStream_t s) {
-    hipLaunchKernelGGL((dense_sum_kernel<DT, VEC, TR>), dim3(chunks), dim3(kThreads), 0, s, a, d);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dense_residual_kernel<DT, VEC, TR>), dim3(chunks), dim3(kThreads), 0, s, a, d);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dense_draw_kernel<DT, VEC, TR>), dim3(a.B), dim3(kThreads), 0, s, a, d);
+hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s) {
+    hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR>), dim3(a.B), dim3(kThreads), 0, s, a, bracket, exp_consts());
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_chain_dense(const ChainArgs& a, const DenseParts& d, hipStream_t s) {
+hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s) {
     const int esz = a.dtype ? 2 : 4;
     const bool vec = vec_ok(a.logits, a.V, esz) && vec_ok(a.q, a.V, 4);
-    const unsigned chunks = static_cast<unsigned>(static_cast<long>(a.B) * d.C);
     if (a.dtype == 1) {
-        if (vec) return a.transformed ? dense_launch<1, true, true>(a, d, chunks, s) : dense_launch<1, true, false>(a, d, chunks, s);
-        return a.transformed ? dense_launch<1, false, true>(a, d, chunks, s) : dense_launch<1, false, false>(a, d, chunks, s);
+        if (vec) return a.transformed ? dense_launch<1, true, true>(a, bracket, s) : dense_launch<1, true, false>(a, bracket, s);
+        return a.transformed ? dense_launch<1, false, true>(a, bracket, s) : dense_launch<1, false, false>(a, bracket, s);
     }
-    if (vec) return a.transformed ? dense_launch<0, true, true>(a, d, chunks, s) : dense_launch<0, true, false>(a, d, chunks, s);
-    return a.transformed ? dense_launch<0, false, true>(a, d, chunks, s) : dense_launch<0, false, false>(a, d, chunks, s);
+    if (vec) return a.transformed ? dense_launch<0, true, true>(a, bracket, s) : dense_launch<0, true, false>(a, bracket, s);
+    return a.transformed ? dense_launch<0, false, true>(a, bracket, s) : dense_launch<0, false, false>(a, bracket, s);
 }
 
 }  // namespace sv

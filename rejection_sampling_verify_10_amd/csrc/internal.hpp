@@ -95,16 +95,8 @@ struct ChainArgs {
     float* out_diag;
 };
 
-// Per-chunk fp64 sums of the dense final draw (dense.hip): chunks of kDenseChunk
-// elements of the one row per batch entry that the draw uses; [B][C] each.
-constexpr int kDenseChunk = 8192;
-struct DenseParts {
-    double* pe;             // sum exp((z - m)/T) over the chunk
-    double* pr;             // sum of residual weights max(0, p' - q')
-    double* pq;             // transformed draft: sum q^(1/T)
-    uint32_t* pflag;        // invalid draft probability in the chunk (E3)
-    int C;                  // chunks per row
-};
+// Dense final draw (dense.hip): rows are cut into chunks of kDenseChunk elements.
+constexpr int kDenseChunk = 4096;
 
 struct TreeArgs {
     const int32_t* node_tokens;
@@ -144,7 +136,9 @@ hipError_t launch_power_sums(const PowerSumArgs& a, hipStream_t s);
 hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s);
 hipError_t launch_chain_topk(const ChainArgs& a, hipStream_t s);   // positions + combine
 hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
-hipError_t launch_chain_dense(const ChainArgs& a, const DenseParts& d, hipStream_t s);   // sum, residual, draw
+// bracket: relative half-width of the brackets put around the row statistics'
+// normalisers (any value gives the same result; it sets how often the slow path runs)
+hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s);
 hipError_t launch_chain_greedy(const ChainArgs& a, hipStream_t s);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t s);
 hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s);

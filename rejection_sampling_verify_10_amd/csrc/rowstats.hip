@@ -227,20 +227,25 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* __restrict
         __builtin_nontemporal_store(load_stream(src + i), dst + i);
 }
 
-// Read-only streaming probe: every 16-byte vector once, non-temporal, four in
-// flight per thread over a grid-stride loop.  The xor of the data decides a
-// store that practically never happens, so the loads cannot be dropped.
+// Read-only streaming probe: every 16-byte vector once, non-temporal.  Each
+// workgroup reads runs of 4 x 256 consecutive vectors (16 KiB), striding over
+// the buffer by the grid.  The xor of the data decides a store that practically
+// never happens, so the loads cannot be dropped.
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ src, size_t n,
                                                          uint32_t* __restrict__ sink) {
-    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    constexpr int kU = 4;
+    const size_t stride = static_cast<size_t>(gridDim.x) * 256 * kU;
     u32x4 acc = u32x4{0u, 0u, 0u, 0u};
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        const u32x4 a = load_stream(src + i), b = load_stream(src + i + stride);
-        const u32x4 c = load_stream(src + i + 2 * stride), d = load_stream(src + i + 3 * stride);
-        acc ^= (a ^ b) ^ (c ^ d);
+    for (size_t base = static_cast<size_t>(blockIdx.x) * 256 * kU; base < n; base += stride) {
+        u32x4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const size_t i = base + static_cast<size_t>(u) * 256 + threadIdx.x;
+            v[u] = i < n ? load_stream(src + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= v[u];
     }
-    for (; i < n; i += stride) acc ^= load_stream(src + i);
     const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
     if (x == 0x9e3779b9u) sink[0] = x;
 }
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* __restrict__ d
 hipError_t launch_read_probe(const void* src, size_t bytes, void* sink, hipStream_t s) {
     const size_t n = bytes / 16;
     size_t blocks = (n + 1023) / 1024;
-    if (blocks > 1024) blocks = 1024;
+    if (blocks > 2048) blocks = 2048;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                        static_cast<const u32x4*>(src), n, static_cast<uint32_t*>(sink));

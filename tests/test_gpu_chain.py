@@ -168,3 +168,16 @@ def test_deterministic(R, orc):
     b = run_gpu_chain(R, ci)
     for x, y in zip(a[:3], b[:3]):
         assert np.array_equal(x, y, equal_nan=True)
+
+
+@pytest.mark.parametrize("bracket", ["0", "1e-3", "0.3"])
+def test_dense_draw_bracket_widths(R, orc, bracket, monkeypatch):
+    """The dense draw brackets the row normalisers; any width must give the same tokens.
+
+    0 makes every bracket miss (the draw recomputes each rejected row exactly); wide
+    brackets leave many residual elements undecided (lists fill up and overflow)."""
+    monkeypatch.setenv("SPEC_VERIFY_DENSE_BRACKET", bracket)
+    check(R, orc, W.config(1, 5), f"c1 bracket {bracket}")
+    check(R, orc, W.config(4, 3, B=12), f"c4 B=12 bracket {bracket}")
+    check(R, orc, W.with_transform(W.config(1, 6, B=6, V=20000), temperature=0.6, top_k=0),
+          f"T=0.6 bracket {bracket}")
