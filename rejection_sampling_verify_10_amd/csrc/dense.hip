@@ -281,13 +281,41 @@ __device__ __forceinline__ bool in_bracket(double Z, double Zapprox, double delt
     return Z > Zapprox * (1.0 - delta) * (1.0 + 1e-12) && Z < Zapprox * (1.0 + delta) * (1.0 - 1e-12);
 }
 
+// Inclusive sums within each 16-lane row (DPP row shifts, zero fill): lane 16r+15
+// ends with the sum of row r.
+__device__ __forceinline__ double row_scan(double v) {
+    auto step = [&](auto ctrl_tag) {
+        constexpr int kCtrl = decltype(ctrl_tag)::value;
+        const long long bits = __double_as_longlong(v);
+        const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), kCtrl, 0xF, 0xF, true);
+        const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), kCtrl, 0xF, 0xF, true);
+        v += __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+    };
+    step(std::integral_constant<int, 0x111>{});   // row_shr:1
+    step(std::integral_constant<int, 0x112>{});   // row_shr:2
+    step(std::integral_constant<int, 0x114>{});   // row_shr:4
+    step(std::integral_constant<int, 0x118>{});   // row_shr:8
+    return v;
+}
+__device__ __forceinline__ float row_scan(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true));
+    return v;
+}
+// Chunk partials live in dynamic LDS, summed in slot order after the pass: 4 row
+// sums per wave (32 slots per chunk) while C <= 128 (48 KiB), else one wave sum per
+// wave (8 slots; longer rows, fewer slots, the same 48 KiB bound).
+constexpr int kRowSlots = kWaves * 4;
+__host__ __device__ inline int dense_slots(int C) { return C <= 128 ? kRowSlots : kWaves; }
+inline size_t dense_dyn_lds(int C) {
+    return static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float));
+}
+
 struct RowSmem {
     double tbl[kTableSize];
-    double we[kMaxChunks][kWaves];     // per-wave chunk sums: E
-    double wr[kMaxChunks][kWaves];     //   R (or the exact residual in the second pass)
-    float wp[kMaxChunks][kWaves];      //   P
     double part[kMaxChunks];           // chunk weights of the draw
-    double pe[kMaxChunks];             // chunk sums of e
     int32_t li[kListCap];              // undecided elements
     double le[kListCap], lw[kListCap];
     double red[kWaves];
@@ -300,11 +328,15 @@ struct RowSmem {
 template <int DT, bool VEC, bool TR>
 __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, double bracket, ExpConsts ek) {
     __shared__ RowSmem sm;
+    extern __shared__ double dyn_lds[];
     const int b = blockIdx.x;
     const int K = a.K, V = a.V;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
     const int C = (V + kDenseChunk - 1) / kDenseChunk;
     const int C_full = V / kDenseChunk;              // chunks wholly inside the row
+    const int nslots = dense_slots(C);
+    double* pr = dyn_lds;                            // [C][nslots]: R (residual rows) or E
+    float* pp = reinterpret_cast<float*>(dyn_lds + static_cast<long>(C) * nslots);   // [C][nslots]: P
     const long rbase = static_cast<long>(b) * (K + 1);
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
 
@@ -343,6 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
 
     // ---- one pass over row j ----
     double sq_tot = 0.0;                   // transformed draft: sum w over the thread's elements
+    double se_tot = 0.0;                   // residual rows: sum e over the thread's elements
     auto body = [&](auto res_tag) {
         constexpr bool RES = decltype(res_tag)::value;
         using Buf = Raw8<DT>[kSub];
@@ -407,15 +440,25 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
                     }
                 }
             }
-            se = wave_sum(se);
-            if (RES) {
-                sr = wave_sum(sr);
-                sp = wave_sum(sp);
-            }
-            if (lane == 0) {
-                sm.we[c][wid] = se;
-                sm.wr[c][wid] = sr;
-                sm.wp[c][wid] = sp;
+            // Per chunk the residual rows need R and P; E only as a row total (kept per
+            // lane).  The bonus rows need E per chunk.
+            if (RES) se_tot += se;
+            double v = RES ? sr : se;
+            if (nslots == kRowSlots) {
+                const int slot = c * kRowSlots + wid * 4 + (lane >> 4);
+                v = row_scan(v);
+                if (RES) sp = row_scan(sp);
+                if ((lane & 15) == 15) {
+                    pr[slot] = v;
+                    if (RES) pp[slot] = sp;
+                }
+            } else {
+                v = wave_sum(v);
+                if (RES) sp = wave_sum(sp);
+                if (lane == 0) {
+                    pr[c * kWaves + wid] = v;
+                    if (RES) pp[c * kWaves + wid] = sp;
+                }
             }
         };
         // Full chunks: chunk c+1 is in flight while chunk c is computed (two register
@@ -441,23 +484,51 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
     if (res) body(std::true_type{});
     else body(std::false_type{});
     __syncthreads();
-    for (int c = tid; c < C; c += kThreads) {
-        double e = 0.0;
+
+    // Exact chunk sums of e (RESID false) or of the residual (true) by a second pass.
+    auto exact_chunks = [&](bool resid, double invZp, double invZq) {
+#pragma unroll 1
+        for (int c = 0; c < C; ++c) {
+            double sc = 0.0;
+#pragma unroll 1
+            for (int s = 0; s < kSub; ++s) {
+                const int i0 = c * kDenseChunk + (s * kThreads + tid) * 8;
+                float z[8], q[8];
+                load8_z<DT, VEC, false>(zr, i0, V, z);
+                if (resid) load8_q<VEC, false>(qr, i0, V, q);
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) e += sm.we[c][w];
-        sm.pe[c] = e;
-    }
-    __syncthreads();
-    double Zp = 0.0;
-    for (int c = 0; c < C; ++c) Zp += sm.pe[c];
-    const double invZp = 1.0 / Zp;
-    double Zq = 1.0;
-    if (TR && res) Zq = block_sum(sq_tot, sm.red);   // exact normaliser of the transformed draft
-    double S = 0.0;
+                for (int e = 0; e < 8; ++e) {
+                    const double ex = exp_of(z[e], g, tbl, ek);
+                    if (resid) {
+                        const double rr = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
+                        sc += rr > 0.0 ? rr : 0.0;
+                    } else {
+                        sc += ex;
+                    }
+                }
+            }
+            sc = block_sum(sc, sm.red);
+            if (tid == 0) sm.part[c] = sc;
+        }
+        __syncthreads();
+    };
+
+    double Zp = 0.0, Zq = 1.0, S = 0.0;
     bool residual = false;
-    if (res) {
+    if (!res) {
+        for (int c = tid; c < C; c += kThreads) {
+            double e = 0.0;
+#pragma unroll
+            for (int w = 0; w < nslots; ++w) e += pr[c * nslots + w];
+            sm.part[c] = e;
+        }
+        __syncthreads();
+        for (int c = 0; c < C; ++c) Zp += sm.part[c];
+    } else {
+        Zp = block_sum(se_tot, sm.red);
+        if (TR) Zq = block_sum(sq_tot, sm.red);      // exact normaliser of the transformed draft
         if (sm.qbad || (TR && !(Zq > 0.0))) { fail_row(); return; }
-        const double invZq = 1.0 / Zq;
+        const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
         const bool exact_ok = sm.n_list <= kListCap && in_bracket(Zp, Zp_ap, bracket) &&
                               (!TR || in_bracket(Zq, Zq_ap, bracket));
         if (exact_ok) {
@@ -467,10 +538,9 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
             const int n = sm.n_list;
             for (int c = tid; c < C; c += kThreads) {
                 double r = 0.0;
-                float pp = 0.f;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) { r += sm.wr[c][w]; pp += sm.wp[c][w]; }
-                double pc = rho * r + kap * static_cast<double>(pp);
+                float psum = 0.f;
+                for (int w = 0; w < nslots; ++w) { r += pr[c * nslots + w]; psum += pp[c * nslots + w]; }
+                double pc = rho * r + kap * static_cast<double>(psum);
                 for (int t = 0; t < n; ++t) {
                     if (sm.li[t] / kDenseChunk != c) continue;
                     const double e = sm.le[t], w = sm.lw[t];
@@ -481,38 +551,23 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
                 }
                 sm.part[c] = pc > 0.0 ? pc : 0.0;
             }
+            __syncthreads();
         } else {
-            // Exact chunk sums (a normaliser outside its bracket or the list overflowed):
-            // never expected, always correct.
-#pragma unroll 1
-            for (int c = 0; c < C; ++c) {
-                double sr = 0.0;
-#pragma unroll 1
-                for (int s = 0; s < kSub; ++s) {
-                    const int i0 = c * kDenseChunk + (s * kThreads + tid) * 8;
-                    float z[8], q[8];
-                    load8_z<DT, VEC, false>(zr, i0, V, z);
-                    load8_q<VEC, false>(qr, i0, V, q);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const double rr = exp_of(z[e], g, tbl, ek) * invZp - draft_w<TR>(q[e], a.invT) * invZq;
-                        sr += rr > 0.0 ? rr : 0.0;
-                    }
-                }
-                sr = block_sum(sr, sm.red);
-                if (tid == 0) sm.part[c] = sr;
-            }
+            // A normaliser outside its bracket or the list overflowed: never expected,
+            // always correct.
+            exact_chunks(true, invZp, invZq);
         }
-        __syncthreads();
         for (int c = 0; c < C; ++c) S += sm.part[c];
         __syncthreads();
         residual = S > 0.0;
+        if (!residual) {
+            // zero residual: the draw falls back to p'_j, whose chunk sums this pass skipped
+            exact_chunks(false, 0.0, 0.0);
+            Zp = 0.0;
+            for (int c = 0; c < C; ++c) Zp += sm.part[c];
+        }
     }
-    if (!residual) {
-        for (int c = tid; c < C; c += kThreads) sm.part[c] = sm.pe[c];
-        __syncthreads();
-    }
-    const double invZq = 1.0 / Zq;
+    const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
 
     // ---- draw: the chunk holding u*W, then its elements ----
     const double W = residual ? S : Zp;
@@ -624,7 +679,9 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
 
 template <int DT, bool VEC, bool TR>
 hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s) {
-    hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR>), dim3(a.B), dim3(kThreads), 0, s, a, bracket, exp_consts());
+    const int C = (a.V + kDenseChunk - 1) / kDenseChunk;
+    hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR>), dim3(a.B), dim3(kThreads),
+                       static_cast<unsigned>(dense_dyn_lds(C)), s, a, bracket, exp_consts());
     return hipGetLastError();
 }
 

@@ -181,3 +181,11 @@ def test_dense_draw_bracket_widths(R, orc, bracket, monkeypatch):
     check(R, orc, W.config(4, 3, B=12), f"c4 B=12 bracket {bracket}")
     check(R, orc, W.with_transform(W.config(1, 6, B=6, V=20000), temperature=0.6, top_k=0),
           f"T=0.6 bracket {bracket}")
+
+
+@pytest.mark.parametrize("V,T", [(600000, 1.0), (600000, 0.8), (524288, 1.0)])
+def test_dense_long_rows(R, orc, V, T):
+    """Rows of more than 128 dense chunks (wave-level chunk partials) and exactly 128."""
+    ci = W.make_chain(3, 3, V, dtype=W.DTYPE_BF16, temperature=T, top_k=0, sigma=W.sigma_const(0.6),
+                      config_id=92, seed=V % 1000)
+    check(R, orc, ci, f"dense V={V} T={T}")
