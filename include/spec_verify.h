@@ -43,6 +43,12 @@
  *          are read; otherwise all K draft rows are read);
  *       E4 a transformed draft row keeps zero mass;
  *       E5 a uniform outside [0, 1) (sampling mode).
+ *   - Environment: SPEC_VERIFY_DENSE_BRACKET (a number in [0, 0.5)) sets the
+ *     relative width of the bracket the dense final draw (temperature > 0,
+ *     top-k off) puts around the normalisers taken from its row statistics.
+ *     Results do not depend on it; a normaliser outside its bracket only makes
+ *     the draw recompute that row exactly (0 forces that path, for tests).
+ *     Read on every call; unset or invalid values leave the built-in width.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
