@@ -33,13 +33,23 @@ __device__ __forceinline__ void softmax_row_vec(const char* row, int V, float sc
     const int nvec = V / E::kPerVec;
     float acc[kUnroll] = {0.f, 0.f, 0.f, 0.f};
     m = -INFINITY;
-    for (int base = 0; base < nvec; base += kThreads * kUnroll) {
-        u32x4 v[kUnroll];
+    // Tile t+1 is loaded while tile t is summed (two register buffers), so each
+    // thread keeps 8 vectors in flight instead of 4.  Full tiles load without a
+    // bounds check (the surplus load at the end re-reads the last full tile and
+    // is dropped), so that no load sits behind a branch and waiting for one
+    // buffer does not also wait for the other; the partial last tile comes after.
+    auto load_tile = [&](int base, u32x4 (&v)[kUnroll]) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int i = base + u * kThreads + threadIdx.x;
             v[u] = (i < nvec) ? load_stream(rv + i) : neg_inf_vec(DT);
         }
+    };
+    auto load_full = [&](int base, u32x4 (&v)[kUnroll]) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = load_stream(rv + base + u * kThreads + threadIdx.x);
+    };
+    auto sum_tile = [&](const u32x4 (&v)[kUnroll]) {
         float tmax = m;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
@@ -65,6 +75,24 @@ __device__ __forceinline__ void softmax_row_vec(const char* row, int V, float sc
                 for (int e = 0; e < E::kPerVec; ++e)
                     if (E::get(v[u], e) != E::get(v[u], e)) acc[0] = NAN;
         }
+    };
+    constexpr int kTile = kThreads * kUnroll;
+    const int nfull = nvec / kTile;
+    u32x4 va[kUnroll], vb[kUnroll];
+    int t = 0;
+    if (nfull > 0) {
+        load_full(0, va);
+        for (; t + 1 < nfull; t += 2) {
+            load_full((t + 1) * kTile, vb);
+            sum_tile(va);
+            load_full(min(t + 2, nfull - 1) * kTile, va);
+            sum_tile(vb);
+        }
+        if (t < nfull) sum_tile(va);
+    }
+    if (nfull * kTile < nvec) {
+        load_tile(nfull * kTile, va);
+        sum_tile(va);
     }
     s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
