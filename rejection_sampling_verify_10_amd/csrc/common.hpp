@@ -74,6 +74,13 @@ __device__ __forceinline__ double xshfl(double v, int j) {
     const int hi = xshfl_i(static_cast<int>(b >> 32), j);
     return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
 }
+typedef unsigned long long pkey_t;     // (value, index) sort key, see below
+__device__ __forceinline__ pkey_t xshfl(pkey_t v, int j) {
+    const int lo = xshfl_i(static_cast<int>(v), j);
+    const int hi = xshfl_i(static_cast<int>(v >> 32), j);
+    return (static_cast<pkey_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
 // Value of lane 63 - lane (the wave reversed): xor 63 composed of the steps above.
 template <typename T> __device__ __forceinline__ T xrev(T v) {
 #pragma unroll
@@ -107,6 +114,16 @@ __device__ __forceinline__ float wave_min(float v) {
     return v;
 }
 __device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, xshfl(v, o));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, xshfl(v, o));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = max(v, xshfl(v, o));
     return v;
@@ -148,24 +165,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     }
 }
 
-// Sorts one value per lane in descending order (bitonic network over the wave).
-__device__ __forceinline__ float wave_sort_desc(float v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            float o = xshfl(v, j);
-            // descending overall: block direction flips with (lane & k)
-            bool up = ((lane & k) == 0);
-            bool lower = ((lane & j) == 0);
-            bool take_max = (up == lower);
-            v = take_max ? fmaxf(v, o) : fminf(v, o);
-        }
-    }
-    return v;
-}
-
 }  // namespace sv
 
 namespace sv {
@@ -173,7 +172,10 @@ namespace sv {
 // ---- wave-level bitonic networks over (value, index) pairs, one pair per lane ----
 //
 // Order: larger value first, lower index on equal values (a strict total order
-// for distinct indices).  Empty slots hold (-inf, kNoIndex) and sort last.
+// for distinct indices).  A pair travels as one 64-bit key whose unsigned order
+// is that order: the order-preserving bits of the value above the complement of
+// the index, so a compare-exchange is one 64-bit compare and two selects.
+// Empty slots hold (-inf, kNoIndex) and sort after every real entry.
 
 constexpr int kNoIndex = 0x7fffffff;
 
@@ -184,48 +186,53 @@ __device__ __forceinline__ float minimum3(float a, float b, float c) {
     return __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c);
 }
 
-// Keeps in this lane the first (keep_first) or the second of {mine, lane^j's}.
-__device__ __forceinline__ void cx_pair(float& v, int& i, int j, bool keep_first) {
-    const float ov = xshfl(v, j);
-    const int oi = xshfl(i, j);
-    const bool mine = precedes(v, i, ov, oi);
-    if (keep_first ? !mine : mine) { v = ov; i = oi; }
+// Order-preserving unsigned key of a float: NaN lowest, -0 folded onto +0.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (v != v) return 0u;
+    if (v == 0.f) v = 0.f;
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float order_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Full sort of the 64 pairs of the wave (lane 0 = first).
-__device__ __forceinline__ void wave_sort_pairs(float& v, int& i) {
+__device__ __forceinline__ pkey_t pair_key(float v, int i) {
+    return (static_cast<pkey_t>(order_key(v)) << 32) | (0xffffffffu - static_cast<uint32_t>(i));
+}
+__device__ __forceinline__ float key_val(pkey_t k) { return order_value(static_cast<uint32_t>(k >> 32)); }
+__device__ __forceinline__ int key_idx(pkey_t k) { return static_cast<int>(0xffffffffu - static_cast<uint32_t>(k)); }
+__device__ __forceinline__ pkey_t empty_key() { return pair_key(-INFINITY, kNoIndex); }
+
+// Keeps in this lane the larger (keep_first) or the smaller of {mine, lane^j's}.
+__device__ __forceinline__ void cx_key(pkey_t& k, int j, bool keep_first) {
+    const pkey_t o = xshfl(k, j);
+    const bool mine = k > o;
+    if (keep_first ? !mine : mine) k = o;
+}
+
+// Full sort of the 64 keys of the wave (lane 0 = first).
+__device__ __forceinline__ void wave_sort_keys(pkey_t& k) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
+    for (int s = 2; s <= kWave; s <<= 1) {
 #pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const bool up = (lane & k) == 0 || k == kWave;
-            cx_pair(v, i, j, ((lane & j) == 0) == up);
+        for (int j = s >> 1; j > 0; j >>= 1) {
+            const bool up = (lane & s) == 0 || s == kWave;
+            cx_key(k, j, ((lane & j) == 0) == up);
         }
     }
 }
 
-// (v,i) and (w,wi) each sorted (lane 0 first): leaves in (v,i) the first 64 of their
-// union, sorted.  Pairing lane l of one list with lane 63-l of the other gives a
-// bitonic sequence holding the 64 winners; a bitonic merge sorts it.
-__device__ __forceinline__ void wave_merge_pairs(float& v, int& i, float w, int wi) {
+// a and b each sorted (lane 0 first): leaves in a the first 64 of their union,
+// sorted.  Pairing lane l of one list with lane 63-l of the other gives a bitonic
+// sequence holding the 64 winners; a bitonic merge sorts it.
+__device__ __forceinline__ void wave_merge_keys(pkey_t& a, pkey_t b) {
     const int lane = threadIdx.x & (kWave - 1);
-    const float rw = xrev(w);
-    const int ri = xrev(wi);
-    if (!precedes(v, i, rw, ri)) { v = rw; i = ri; }
+    const pkey_t rb = xrev(b);
+    a = a > rb ? a : rb;
 #pragma unroll
-    for (int j = kWave >> 1; j > 0; j >>= 1) cx_pair(v, i, j, (lane & j) == 0);
-}
-
-// Values only, descending.
-__device__ __forceinline__ void wave_merge_desc(float& v, float w) {
-    const int lane = threadIdx.x & (kWave - 1);
-    v = fmaxf(v, xrev(w));
-#pragma unroll
-    for (int j = kWave >> 1; j > 0; j >>= 1) {
-        const float o = xshfl(v, j);
-        v = ((lane & j) == 0) ? fmaxf(v, o) : fminf(v, o);
-    }
+    for (int j = kWave >> 1; j > 0; j >>= 1) cx_key(a, j, (lane & j) == 0);
 }
 
 }  // namespace sv

@@ -35,21 +35,22 @@ __device__ __forceinline__ int merge_global_lists(const TopkLists& t, long unit0
         }
     }
     int total = 0;
+    pkey_t k[kMaxRowChunks];
 #pragma unroll
     for (int c = 0; c < kMaxRowChunks; ++c) {
         if (c < C) {
             total += n[c];
-            if (lane >= n[c]) { w[c] = -INFINITY; wi[c] = kNoIndex; }
+            k[c] = lane < n[c] ? pair_key(w[c], wi[c]) : empty_key();
         }
     }
 #pragma unroll
     for (int step = 1; step < kMaxRowChunks; step <<= 1) {
 #pragma unroll
         for (int c = 0; c + step < kMaxRowChunks; c += 2 * step)
-            if (c + step < C) wave_merge_pairs(w[c], wi[c], w[c + step], wi[c + step]);
+            if (c + step < C) wave_merge_keys(k[c], k[c + step]);
     }
-    v = w[0];
-    i = wi[0];
+    v = key_val(k[0]);
+    i = key_idx(k[0]);
     return total;
 }
 

@@ -48,16 +48,6 @@ struct ChunkSmem {
     float tau;
 };
 
-__device__ __forceinline__ uint32_t ordered_key(float v) {
-    if (v != v) return 0u;                 // NaN never selected
-    if (v == 0.f) v = 0.f;                 // -0 and +0 are equal values
-    const uint32_t b = __float_as_uint(v);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
 __device__ __forceinline__ int block_sum(int v, ChunkSmem& sm) {
     v = wave_sum(v);
     __syncthreads();
@@ -105,7 +95,7 @@ __device__ __noinline__ int chunk_exact(const char* row, int dt, long start, int
     while (lo < hi) {
         const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
         int c = 0;
-        for (int i = tid; i < len; i += kThreads) c += ordered_key(load_elem(row, dt, start + i)) >= mid;
+        for (int i = tid; i < len; i += kThreads) c += order_key(load_elem(row, dt, start + i)) >= mid;
         if (block_sum(c, sm) >= top_k) lo = mid;
         else hi = mid - 1u;
     }
@@ -116,7 +106,7 @@ __device__ __noinline__ int chunk_exact(const char* row, int dt, long start, int
     int gt = 0;
     for (int i = tid; i < len; i += kThreads) {
         const float v = load_elem(row, dt, start + i);
-        if (ordered_key(v) > kappa) {
+        if (order_key(v) > kappa) {
             const int p = atomicAdd(&sm.cnt, 1);
             sm.cv[p] = v;
             sm.ci[p] = static_cast<int32_t>(start + i);
@@ -131,7 +121,7 @@ __device__ __noinline__ int chunk_exact(const char* row, int dt, long start, int
         int tie = 0;
         if (i < len) {
             v = load_elem(row, dt, start + i);
-            tie = ordered_key(v) == kappa;
+            tie = order_key(v) == kappa;
         }
         int total;
         const int rank = prior + block_exclusive(tie, sm, &total);
@@ -241,21 +231,29 @@ __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row
 
     // tau: the top_k-th largest of the 256 thread maxima, by bisection on their
     // ordered keys in wave 0 (4 keys per lane; counts are ballot popcounts).
-    sm.tkey[tid] = ordered_key(tmax);
+    sm.tkey[tid] = order_key(tmax);
     if (tid == 0) { sm.cnt = 0; sm.flags = 0; sm.overflow = 0; }
     __syncthreads();
     if (lane == 0 && bad) atomicOr(&sm.flags, kFlagInvalid);
     if (wid == 0) {
         const uint32_t k0 = sm.tkey[lane], k1 = sm.tkey[lane + 64], k2 = sm.tkey[lane + 128], k3 = sm.tkey[lane + 192];
-        uint32_t lo = 0u, hi = 0xffffffffu;
+        // Any key with at least top_k maxima at or above it is a valid threshold;
+        // the search runs between the smallest and largest maximum and stops as
+        // soon as exactly top_k qualify.
+        uint32_t lo = wave_min_u32(min(min(k0, k1), min(k2, k3)));
+        uint32_t hi = wave_max_u32(max(max(k0, k1), max(k2, k3)));
         while (lo < hi) {
             const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
             const int c = __popcll(__ballot(k0 >= mid)) + __popcll(__ballot(k1 >= mid)) +
                           __popcll(__ballot(k2 >= mid)) + __popcll(__ballot(k3 >= mid));
-            if (c >= top_k) lo = mid;
-            else hi = mid - 1u;
+            if (c >= top_k) {
+                lo = mid;
+                if (c == top_k) break;
+            } else {
+                hi = mid - 1u;
+            }
         }
-        if (lane == 0) sm.tau = lo == 0u ? -INFINITY : key_value(lo);
+        if (lane == 0) sm.tau = lo == 0u ? -INFINITY : order_value(lo);
     }
     __syncthreads();
     const float tau = sm.tau;
@@ -320,18 +318,16 @@ __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row
     if (wid != 0) return;
 
     // One wave: sort 64 candidates at a time and merge the blocks.
-    float v = lane < n ? sm.cv[lane] : -INFINITY;
-    int i = lane < n ? sm.ci[lane] : kNoIndex;
-    wave_sort_pairs(v, i);
+    pkey_t key = lane < n ? pair_key(sm.cv[lane], sm.ci[lane]) : empty_key();
+    wave_sort_keys(key);
     for (int base = kWave; base < n; base += kWave) {
-        float w = base + lane < n ? sm.cv[base + lane] : -INFINITY;
-        int wi = base + lane < n ? sm.ci[base + lane] : kNoIndex;
-        wave_sort_pairs(w, wi);
-        wave_merge_pairs(v, i, w, wi);
+        pkey_t w = base + lane < n ? pair_key(sm.cv[base + lane], sm.ci[base + lane]) : empty_key();
+        wave_sort_keys(w);
+        wave_merge_keys(key, w);
     }
     const int kk = n < top_k ? n : top_k;
-    ov[lane] = v;                       // every slot: past kk the entries are ignored
-    oi[lane] = i;
+    ov[lane] = key_val(key);            // every slot: past kk the entries are ignored
+    oi[lane] = key_idx(key);
     if (lane == 0) {
         *ocnt = kk;
         *oflag = sm.flags;
