@@ -56,17 +56,23 @@ RowStats carve_rowstats(Carver& c, size_t R) {
     return st;
 }
 
-// Chunk lists for B batch rows of P positions, K of which carry a draft row.
-TopkLists carve_topk(Carver& c, int dtype, int V, int B, int P, int K, int top_k, float T) {
+// Chunk lists for B batch rows of P positions, K of which carry a draft row:
+// list words for a chain (handed to its finisher workgroups within the launch,
+// zero between calls), value / index arrays for a separate merge kernel.
+TopkLists carve_topk(Carver& c, int dtype, int V, int B, int P, int K, int top_k, float T, bool words) {
     TopkLists t{};
     topk_chunking(V, esz_of(dtype), &t.Ct, &t.chunk_t);
     topk_chunking(V, 4, &t.Cd, &t.chunk_d);
     t.Ub = static_cast<long>(P) * t.Ct + static_cast<long>(K) * t.Cd;
     const size_t units = static_cast<size_t>(B) * t.Ub;
-    t.vals = c.take<float>(units * kTopkMax);
-    t.idx = c.take<int32_t>(units * kTopkMax);
-    t.cnt = c.take<int32_t>(units);
-    t.flags = c.take<uint32_t>(units);
+    if (words) {
+        t.words = c.take<unsigned long long>(units * kTopkMax);
+    } else {
+        t.vals = c.take<float>(units * kTopkMax);
+        t.idx = c.take<int32_t>(units * kTopkMax);
+        t.cnt = c.take<int32_t>(units);
+        t.flags = c.take<uint32_t>(units);
+    }
     t.top_k = top_k;
     t.draft_identity = (T == 1.f) ? 1 : 0;
     t.invT = T > 0.f ? 1.0 / static_cast<double>(T) : 0.0;
@@ -119,7 +125,7 @@ struct ChainPlan {
     double* qsum;
     uint32_t* qflags;
     TopkLists tk;
-    PosRecord* rec;
+    unsigned long long* recw;
 };
 
 // Relative half-width of the brackets the dense draw puts around the row
@@ -145,8 +151,8 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
         p.st = carve_rowstats(c, Rt);
     } else if (topk_active(top_k, V)) {
         p.mode = 1;
-        p.tk = carve_topk(c, dtype, V, B, K + 1, K, top_k, T);
-        p.rec = c.take<PosRecord>(Rt);
+        p.tk = carve_topk(c, dtype, V, B, K + 1, K, top_k, T, true);
+        p.recw = c.take<unsigned long long>(Rt * kRecWords);
     } else {
         p.mode = 0;
         p.st = carve_rowstats(c, Rt);
@@ -175,7 +181,7 @@ AlphaPlan plan_alpha(Carver& c, int B, int K, int V, int dtype, float T, int top
         p.qst = carve_rowstats(c, R);
     } else if (topk_active(top_k, V)) {
         p.mode = 1;
-        p.tk = carve_topk(c, dtype, V, B, K, K, top_k, T);
+        p.tk = carve_topk(c, dtype, V, B, K, K, top_k, T, false);
     } else {
         p.mode = 0;
         p.st = carve_rowstats(c, R);
@@ -298,13 +304,14 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
         prof.after();
         SV_TRY(launch_chain_greedy(ca, s));
     } else if (p.mode == 1) {
-        TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K + 1, p.tk);
-        prof.before();
-        SV_TRY(launch_topk_chunks(ta, s));
-        prof.after();
         ca.tk = p.tk;
-        ca.rec = p.rec;
-        SV_TRY(launch_chain_topk(ca, s));
+        ca.recw = p.recw;
+        TopkChainArgs fa{};
+        fa.sel = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K + 1, p.tk);
+        fa.ch = ca;
+        prof.before();
+        SV_TRY(launch_chain_topk(fa, s));
+        prof.after();
     } else {
         ca.st = p.st;
         RowStatsArgs ra =

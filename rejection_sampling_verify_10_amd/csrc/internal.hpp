@@ -48,6 +48,7 @@ struct TopkLists {
     int32_t* idx;
     int32_t* cnt;           // [units]
     uint32_t* flags;
+    unsigned long long* words;   // chain calls: [units][kTopkMax] list words, zero between calls
     int Ct, Cd;             // chunks per target / draft row
     int chunk_t, chunk_d;   // elements per target / draft chunk
     long Ub;                // units per batch row
@@ -57,13 +58,6 @@ struct TopkLists {
     __host__ __device__ long unit_base(int b, int k) const {
         return static_cast<long>(b) * Ub + static_cast<long>(k) * (Ct + Cd);
     }
-};
-
-// Result of one position of a chain (top-k path): written by the position's
-// workgroup, read by the per-batch-row combine kernel.
-struct PosRecord {
-    int32_t accept, y, bad, pad;
-    float pk, qk, S, py;
 };
 
 // One launch of the top-k selection: B batch rows of P positions (K+1 for a
@@ -89,10 +83,18 @@ struct ChainArgs {
     const double* qsum;     // dense transformed: [B*K] sum q^(1/T) (fp32-accurate)
     const uint32_t* qflags;
     TopkLists tk;           // top-k path
-    PosRecord* rec;         // [B][K+1]
+    unsigned long long* recw;   // top-k chain: [B][K+1][kRecWords] position record words, zero between calls
     int32_t* out_tokens;
     int32_t* out_accept_len;
     float* out_diag;
+};
+
+// A top-k chain in one launch (topk.hip): B*Ub selection units, then the
+// finisher workgroups, finish_groups(K) per batch row (chain_finish.hpp).
+constexpr int kRecWords = 5;    // 64-bit words of a position record
+struct TopkChainArgs {
+    TopkChunkArgs sel;
+    ChainArgs ch;
 };
 
 // Dense final draw (dense.hip): rows are cut into chunks of kDenseChunk elements.
@@ -134,7 +136,7 @@ inline bool vec_ok(const void* p, int V, int esz) {
 hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s);
 hipError_t launch_power_sums(const PowerSumArgs& a, hipStream_t s);
 hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s);
-hipError_t launch_chain_topk(const ChainArgs& a, hipStream_t s);   // positions + combine
+hipError_t launch_chain_topk(const TopkChainArgs& a, hipStream_t s);   // selection + finish
 hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
 // bracket: relative half-width of the brackets put around the row statistics'
 // normalisers (any value gives the same result; it sets how often the slow path runs)

@@ -12,46 +12,56 @@ __device__ __forceinline__ bool u_ok(float u) { return u >= 0.f && u < 1.f; }
 __device__ __forceinline__ bool q_ok(float v) { return v >= 0.f && v < INFINITY; }
 
 constexpr int kMaxRowChunks = 16;
+constexpr int kMergeBatch = 8;
 
 // Merges the C (<= 16) sorted chunk lists of a row (workspace units unit0 ..
 // unit0+C-1): lane l ends with the l-th ranked (value, index) of their union.
-// Every load is issued before any count is used (a list owns all kTopkMax
-// slots); a pairwise tree keeps the merges of one level independent.  Returns
-// the total number of entries; flags collects the chunks' flags.
+// Up to kMergeBatch lists are loaded at once, every load issued before any is
+// used (a list owns all kTopkMax slots), and merged by a pairwise tree whose
+// merges within a level are independent.  Returns the total number of entries;
+// flags collects the chunks' flags.  COH: the lists were written by other
+// workgroups of the running launch (device-scope loads).
+template <bool COH>
 __device__ __forceinline__ int merge_global_lists(const TopkLists& t, long unit0, int C, float& v, int& i,
                                                   uint32_t& flags) {
     const int lane = threadIdx.x & (kWave - 1);
-    float w[kMaxRowChunks];
-    int wi[kMaxRowChunks];
-    int n[kMaxRowChunks];
+    int nl = 0;
+    uint32_t fl = 0u;
+    if (lane < C) {
+        nl = ld<COH>(t.cnt + unit0 + lane);
+        fl = ld<COH>(t.flags + unit0 + lane);
+    }
+    pkey_t acc = empty_key();
+#pragma unroll 1
+    for (int base = 0; base < C; base += kMergeBatch) {
+        float w[kMergeBatch];
+        int wi[kMergeBatch];
 #pragma unroll
-    for (int c = 0; c < kMaxRowChunks; ++c) {
-        if (c < C) {
-            const long u = unit0 + c;
-            n[c] = t.cnt[u];
-            flags |= t.flags[u];
-            w[c] = t.vals[u * kTopkMax + lane];
-            wi[c] = t.idx[u * kTopkMax + lane];
+        for (int c = 0; c < kMergeBatch; ++c) {
+            if (base + c < C) {
+                const long u = unit0 + base + c;
+                w[c] = ld<COH>(t.vals + u * kTopkMax + lane);
+                wi[c] = ld<COH>(t.idx + u * kTopkMax + lane);
+            }
         }
-    }
-    int total = 0;
-    pkey_t k[kMaxRowChunks];
+        if (base == 0) nl = min(max(nl, 0), kTopkMax);
+        pkey_t k[kMergeBatch];
 #pragma unroll
-    for (int c = 0; c < kMaxRowChunks; ++c) {
-        if (c < C) {
-            total += n[c];
-            k[c] = lane < n[c] ? pair_key(w[c], wi[c]) : empty_key();
+        for (int c = 0; c < kMergeBatch; ++c)
+            if (base + c < C) k[c] = lane < bcast(nl, base + c) ? pair_key(w[c], wi[c]) : empty_key();
+#pragma unroll
+        for (int step = 1; step < kMergeBatch; step <<= 1) {
+#pragma unroll
+            for (int c = 0; c + step < kMergeBatch; c += 2 * step)
+                if (base + c + step < C) wave_merge_keys(k[c], k[c + step]);
         }
+        if (base == 0) acc = k[0];
+        else wave_merge_keys(acc, k[0]);
     }
-#pragma unroll
-    for (int step = 1; step < kMaxRowChunks; step <<= 1) {
-#pragma unroll
-        for (int c = 0; c + step < kMaxRowChunks; c += 2 * step)
-            if (c + step < C) wave_merge_keys(k[c], k[c + step]);
-    }
-    v = key_val(k[0]);
-    i = key_idx(k[0]);
-    return total;
+    flags |= wave_or(fl);
+    v = key_val(acc);
+    i = key_idx(acc);
+    return wave_sum(nl);
 }
 
 // Sorts (index, probability) pairs by index ascending (empty lanes carry kNoIndex).
@@ -123,6 +133,21 @@ __device__ __forceinline__ int lane_draw(double r, bool have, double target) {
     if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
     const unsigned long long pos = __ballot(have && r > 0.0);
     return pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+}
+
+// Kept distribution of row (b, k) of a chain or acceptance-rate call: target
+// row (draft = false) or draft row; one wave.  Returns false when the row is
+// unusable.
+template <bool COH>
+__device__ __forceinline__ bool position_row(const TopkLists& t, int b, int k, bool draft, int& idx, double& p,
+                                             int& kk) {
+    const long unit0 = t.unit_base(b, k) + (draft ? t.Ct : 0);
+    float v;
+    int i;
+    uint32_t flags = 0;
+    const int tot = merge_global_lists<COH>(t, unit0, draft ? t.Cd : t.Ct, v, i, flags);
+    kk = tot < t.top_k ? tot : t.top_k;
+    return kept_distribution(v, i, kk, flags == 0u, draft, t.invT, draft && t.draft_identity, idx, p);
 }
 
 }  // namespace sv

@@ -21,6 +21,7 @@
 // (position k: Ct target chunks, then Cd draft chunks when k has a draft row),
 // and the verification kernels merge them.  No workgroup waits for another.
 
+#include "chain_finish.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 #include "lists.hpp"
@@ -35,6 +36,7 @@ constexpr int kSlots = 16;
 constexpr int kCap = 1024;
 
 constexpr int kStage = kWave;             // staged (lane, vector) pairs per wave
+static_assert(kWaves == kFinishWaves, "a finisher workgroup has the selection's block size");
 
 struct ChunkSmem {
     float cv[kCap];                      // candidates of the chunk
@@ -190,11 +192,13 @@ __device__ __forceinline__ void load_chunk(const char* row, long start, int len,
     }
 }
 
-// Top-k of one register-resident chunk, left sorted in list slot `slot`.
-template <int DT, bool VEC>
+// Top-k of one register-resident chunk, left sorted in list slot `slot`: as
+// (ov, oi, ocnt, oflag), or (WORDS) as 64 list words for a finisher workgroup
+// of the same launch (chain_finish.hpp), stored at device scope.
+template <int DT, bool VEC, bool WORDS>
 __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row, long start, int len, int top_k,
                                              bool is_draft, float* ov, int32_t* oi, int32_t* ocnt,
-                                             uint32_t* oflag, ChunkSmem& sm) {
+                                             uint32_t* oflag, unsigned long long* ow, ChunkSmem& sm) {
     using E = Elem<DT>;
     constexpr int EPV = E::kPerVec;
     const int tid = threadIdx.x;
@@ -326,18 +330,38 @@ __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row
         wave_merge_keys(key, w);
     }
     const int kk = n < top_k ? n : top_k;
-    ov[lane] = key_val(key);            // every slot: past kk the entries are ignored
-    oi[lane] = key_idx(key);
-    if (lane == 0) {
-        *ocnt = kk;
-        *oflag = sm.flags;
+    if constexpr (WORDS) {
+        st_agent64(ow + lane, list_word(lane < kk ? key : empty_key(), sm.flags != 0u));
+    } else {
+        ov[lane] = key_val(key);            // every slot: past kk the entries are ignored
+        oi[lane] = key_idx(key);
+        if (lane == 0) {
+            *ocnt = kk;
+            *oflag = sm.flags;
+        }
     }
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkChunkArgs a) {
-    __shared__ ChunkSmem sm;
+// FIN: a chain call; the grid holds B*Ub selection units followed by one
+// finisher workgroup per batch row (chain_finish.hpp).
+template <int DT, bool VEC, bool FIN>
+__global__ __launch_bounds__(kThreads, 4) void topk_chunk_kernel(TopkChainArgs fa) {
+    __shared__ union {
+        ChunkSmem sel;
+        FinishSmem fin;
+    } smu;
+    ChunkSmem& sm = smu.sel;
+    const TopkChunkArgs& a = fa.sel;
     const long unit = blockIdx.x;
+    if constexpr (FIN) {
+        const long units = static_cast<long>(a.B) * a.l.Ub;
+        if (unit >= units) {
+            const int G = finish_groups(a.K);
+            const int f = static_cast<int>(unit - units);
+            chain_finish_group(fa.ch, f / G, f - (f / G) * G, smu.fin);
+            return;
+        }
+    }
     const TopkLists& t = a.l;
     const int b = static_cast<int>(unit / t.Ub);
     const long local = unit - static_cast<long>(b) * t.Ub;
@@ -353,32 +377,45 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkChunkArgs a) {
         const long start = static_cast<long>(within) * t.chunk_t;
         const int len = static_cast<int>(min(static_cast<long>(t.chunk_t), a.V - start));
         load_chunk<DT, VEC>(row, start, len, d);
-        select_chunk<DT, VEC>(d, row, start, len, t.top_k, false, ov, oi, t.cnt + unit, t.flags + unit, sm);
+        select_chunk<DT, VEC, FIN>(d, row, start, len, t.top_k, false, ov, oi, t.cnt + unit, t.flags + unit,
+                                   t.words + unit * kTopkMax, sm);
     } else {
         const int c = within - t.Ct;
         const char* row = reinterpret_cast<const char*>(a.draft + (static_cast<long>(b) * a.K + k) * a.V);
         const long start = static_cast<long>(c) * t.chunk_d;
         const int len = static_cast<int>(min(static_cast<long>(t.chunk_d), a.V - start));
         load_chunk<0, VEC>(row, start, len, d);
-        select_chunk<0, VEC>(d, row, start, len, t.top_k, true, ov, oi, t.cnt + unit, t.flags + unit, sm);
+        select_chunk<0, VEC, FIN>(d, row, start, len, t.top_k, true, ov, oi, t.cnt + unit, t.flags + unit,
+                                  t.words + unit * kTopkMax, sm);
     }
 }
 
 }  // namespace
 
-hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s) {
+template <bool FIN>
+hipError_t launch_selection(const TopkChainArgs& fa, hipStream_t s) {
+    const TopkChunkArgs& a = fa.sel;
     const int esz = a.dtype ? 2 : 4;
     const bool vec = vec_ok(a.target, a.V, esz) && vec_ok(a.draft, a.V, 4);
-    const unsigned units = static_cast<unsigned>(static_cast<long>(a.B) * a.l.Ub);
+    const unsigned units =
+        static_cast<unsigned>(static_cast<long>(a.B) * a.l.Ub + (FIN ? static_cast<long>(a.B) * finish_groups(a.K) : 0));
     if (units == 0) return hipSuccess;
     if (a.dtype == 1) {
-        if (vec) hipLaunchKernelGGL((topk_chunk_kernel<1, true>), dim3(units), dim3(kThreads), 0, s, a);
-        else hipLaunchKernelGGL((topk_chunk_kernel<1, false>), dim3(units), dim3(kThreads), 0, s, a);
+        if (vec) hipLaunchKernelGGL((topk_chunk_kernel<1, true, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
+        else hipLaunchKernelGGL((topk_chunk_kernel<1, false, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
     } else {
-        if (vec) hipLaunchKernelGGL((topk_chunk_kernel<0, true>), dim3(units), dim3(kThreads), 0, s, a);
-        else hipLaunchKernelGGL((topk_chunk_kernel<0, false>), dim3(units), dim3(kThreads), 0, s, a);
+        if (vec) hipLaunchKernelGGL((topk_chunk_kernel<0, true, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
+        else hipLaunchKernelGGL((topk_chunk_kernel<0, false, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
     }
     return hipGetLastError();
 }
+
+hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s) {
+    TopkChainArgs fa{};
+    fa.sel = a;
+    return launch_selection<false>(fa, s);
+}
+
+hipError_t launch_chain_topk(const TopkChainArgs& a, hipStream_t s) { return launch_selection<true>(a, s); }
 
 }  // namespace sv

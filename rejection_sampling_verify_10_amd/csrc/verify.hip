@@ -10,8 +10,8 @@
 //
 // The K tests are independent of each other, so they run in parallel lanes
 // and the first rejection is a ballot.  This file holds the greedy chain, the
-// static tree, the acceptance rate and the top-k chain finish; the dense final
-// draw is in dense.hip.
+// static tree and the acceptance rate; the top-k chain finishes inside its
+// selection launch (chain_finish.hpp) and the dense final draw is in dense.hip.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -136,122 +136,7 @@ __global__ __launch_bounds__(256) void alpha_dense_kernel(AlphaArgs a) {
     }
 }
 
-// ---- top-k path: merge the chunk lists of each position, test, draw, combine ----
-
-// Kept distribution of row (b, k): target (draft = false) or draft.
-__device__ __forceinline__ bool position_row(const TopkLists& t, int b, int k, bool draft, int& idx, double& p,
-                                             int& kk) {
-    const long unit0 = t.unit_base(b, k) + (draft ? t.Ct : 0);
-    float v;
-    int i;
-    uint32_t flags = 0;
-    const int tot = merge_global_lists(t, unit0, draft ? t.Cd : t.Ct, v, i, flags);
-    kk = tot < t.top_k ? tot : t.top_k;
-    return kept_distribution(v, i, kk, flags == 0u, draft, t.invT, draft && t.draft_identity, idx, p);
-}
-
-// One workgroup of two waves per position (b, k): wave 0 merges target row k's
-// chunk lists, wave 1 draft row k's, in parallel; wave 0 then runs test k and
-// draws the token that would be emitted if k were the first rejection (the bonus
-// token for k = K).  One position per workgroup spreads the work over the chip.
-__global__ __launch_bounds__(2 * kWave) void chain_topk_position_kernel(ChainArgs a) {
-    __shared__ int32_t sidx[kWave];
-    __shared__ double sp[kWave];
-    __shared__ int32_t skd, sok;
-    const int K = a.K, V = a.V;
-    const int b = blockIdx.x / (K + 1), k = blockIdx.x - b * (K + 1);
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const long rbase = static_cast<long>(b) * (K + 1);
-    const TopkLists& t = a.tk;
-    int it = kNoIndex, kt = 0;
-    double pt = 0.0;
-    bool ok = false;
-    if (wid == 0) {
-        ok = position_row(t, b, k, false, it, pt, kt);
-    } else if (k < K) {
-        int id, kd;
-        double pd;
-        const bool okd = position_row(t, b, k, true, id, pd, kd);
-        sidx[lane] = id;
-        sp[lane] = pd;
-        if (lane == 0) { skd = kd; sok = okd; }
-    }
-    __syncthreads();
-    if (wid != 0) return;
-    const float uK = a.u[rbase + K];
-    ok = ok && u_ok(a.u[rbase + k]) && u_ok(uK);
-    double r = pt, px = 0.0, qx = 0.0;
-    bool accept = false;
-    if (k < K) {
-        const int x = a.x[static_cast<long>(b) * K + k];
-        ok = ok && sok && x >= 0 && x < V;
-        px = lane_lookup(it, pt, x);
-        qx = lds_lookup(sidx, sp, skd, x);
-        double ratio;
-        if (qx > 0.0) ratio = px / qx;
-        else ratio = px > 0.0 ? INFINITY : 0.0;
-        const double thr = ratio < 1.0 ? ratio : 1.0;
-        accept = static_cast<double>(a.u[rbase + k]) < thr;
-        const double q = lane < kt ? lds_lookup(sidx, sp, skd, it) : 0.0;
-        r = lane < kt ? fmax(pt - q, 0.0) : 0.0;
-    }
-    double S = wave_sum(r);
-    if (!(S > 0.0)) {                       // zero residual: draw from p'_k
-        r = pt;
-        S = wave_sum(pt);
-    }
-    const int src = lane_draw(r, lane < kt, static_cast<double>(uK) * S);
-    const int y = bcast(it, src);
-    const double ry = bcast(r, src);
-    if (lane == 0) {
-        PosRecord rc;
-        rc.accept = accept;
-        rc.y = y;
-        rc.bad = !ok;
-        rc.pad = 0;
-        rc.pk = static_cast<float>(px);
-        rc.qk = static_cast<float>(qx);
-        rc.S = static_cast<float>(S);
-        rc.py = static_cast<float>(ry / S);
-        a.rec[rbase + k] = rc;
-    }
-}
-
-// Per batch row: first rejection j from the position records, emitted tokens
-// x_0..x_{j-1}, y_j, accept_len = j.  One wave per batch row.
-__global__ __launch_bounds__(4 * kWave) void chain_topk_combine_kernel(ChainArgs a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (b >= a.B) return;
-    const int K = a.K;
-    const long rb = static_cast<long>(b) * (K + 1);
-    bool bad = false;
-    for (int k = lane; k <= K; k += kWave) bad |= a.rec[rb + k].bad != 0;
-    const bool err = __ballot(bad) != 0ull;
-    int j = K;
-    for (int base = 0; base < K; base += kWave) {
-        const int k = base + lane;
-        const unsigned long long rm = __ballot(k < K && !a.rec[rb + k].accept);
-        if (rm) { j = base + __ffsll(static_cast<long long>(rm)) - 1; break; }
-    }
-    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
-    for (int k = lane; k <= K; k += kWave) {
-        int tok = -1;
-        if (!err) tok = k < j ? a.x[static_cast<long>(b) * K + k] : (k == j ? a.rec[rb + j].y : -1);
-        a.out_tokens[rb + k] = tok;
-        if (diag && k < K) {
-            diag[k] = err ? NAN : a.rec[rb + k].pk;
-            diag[K + k] = err ? NAN : a.rec[rb + k].qk;
-        }
-    }
-    if (lane == 0) {
-        a.out_accept_len[b] = err ? -1 : j;
-        if (diag) {
-            diag[2 * K] = err ? NAN : a.rec[rb + j].S;
-            diag[2 * K + 1] = err ? NAN : a.rec[rb + j].py;
-        }
-    }
-}
+// ---- top-k acceptance rate (the chain finish is fused into the selection launch) ----
 
 // alpha over the kept sets: one workgroup of two waves per (b, k).
 __global__ __launch_bounds__(2 * kWave) void alpha_topk_kernel(AlphaArgs a) {
@@ -264,11 +149,11 @@ __global__ __launch_bounds__(2 * kWave) void alpha_topk_kernel(AlphaArgs a) {
     int it = kNoIndex, kt = 0;
     double pt = 0.0;
     bool ok = false;
-    if (wid == 0) ok = position_row(a.tk, b, k, false, it, pt, kt);
+    if (wid == 0) ok = position_row<false>(a.tk, b, k, false, it, pt, kt);
     else {
         int id, kd;
         double pd;
-        const bool okd = position_row(a.tk, b, k, true, id, pd, kd);
+        const bool okd = position_row<false>(a.tk, b, k, true, id, pd, kd);
         sidx[lane] = id;
         sp[lane] = pd;
         if (lane == 0) { skd = kd; sok = okd; }
@@ -303,14 +188,6 @@ hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s) {
     const int R = a.B * a.K;
     if (a.dtype == 1) hipLaunchKernelGGL((alpha_dense_kernel<1, false>), dim3(R), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((alpha_dense_kernel<0, false>), dim3(R), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_chain_topk(const ChainArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(chain_topk_position_kernel, dim3(a.B * (a.K + 1)), dim3(2 * kWave), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chain_topk_combine_kernel, dim3((a.B + 3) / 4), dim3(4 * kWave), 0, s, a);
     return hipGetLastError();
 }
 
