@@ -41,12 +41,6 @@ __device__ __forceinline__ pkey_t word_key(unsigned long long w) {
     const int i = idx == kWordNoIndex ? kNoIndex : static_cast<int>(idx);
     return (w & 0xffffffff00000000ull) | (0xffffffffu - static_cast<uint32_t>(i));
 }
-__device__ __forceinline__ void st_agent64(unsigned long long* p, unsigned long long v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned long long ld_agent64(const unsigned long long* p) {
-    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Polls per list batch before a row is given up (each poll sleeps ~256 cycles
 // and waits for a load): about 0.1 s, thousands of times the time between a

@@ -40,37 +40,16 @@ template <> struct Elem<1> {
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
-// Relaxed accesses at device (agent) scope.  They carry the device-coherence
-// bit: a store is written through the XCD's L2 before it counts as complete,
-// and a load does not return a stale cached copy.  Small results pass between
-// workgroups of one launch this way without writing back a whole L2: the
-// producer stores with st_agent, waits for its stores (wait_vm), then counts
-// itself in with add_agent; the workgroup that counts last reads with ld_agent.
-__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+// Relaxed 64-bit accesses at device (agent) scope.  They carry the
+// device-coherence bit: a store is written through the XCD's L2, and a load
+// does not return a stale copy from another XCD's write.  Aligned 8-byte
+// accesses are single-copy atomic, so a word carrying its own valid bit can be
+// handed between workgroups of one launch without any cache write-back.
+__device__ __forceinline__ void st_agent64(unsigned long long* p, unsigned long long v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) { st_agent(reinterpret_cast<uint32_t*>(p), static_cast<uint32_t>(v)); }
-__device__ __forceinline__ void st_agent(float* p, float v) { st_agent(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
-    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
-    return static_cast<int32_t>(ld_agent(reinterpret_cast<const uint32_t*>(p)));
-}
-__device__ __forceinline__ float ld_agent(const float* p) { return __uint_as_float(ld_agent(reinterpret_cast<const uint32_t*>(p))); }
-__device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Waits until every vector memory operation of the wave has completed.
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Plain or device-coherent load / store, chosen at compile time.
-template <bool COH, typename T> __device__ __forceinline__ T ld(const T* p) {
-    if constexpr (COH) return ld_agent(p);
-    else return *p;
-}
-template <bool COH, typename T> __device__ __forceinline__ void st(T* p, T v) {
-    if constexpr (COH) st_agent(p, v);
-    else *p = v;
+__device__ __forceinline__ unsigned long long ld_agent64(const unsigned long long* p) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Value of lane (lane ^ j) for j in {1, 2, 4, 8, 16, 32}, on the VALU: DPP quad

@@ -19,17 +19,15 @@ constexpr int kMergeBatch = 8;
 // Up to kMergeBatch lists are loaded at once, every load issued before any is
 // used (a list owns all kTopkMax slots), and merged by a pairwise tree whose
 // merges within a level are independent.  Returns the total number of entries;
-// flags collects the chunks' flags.  COH: the lists were written by other
-// workgroups of the running launch (device-scope loads).
-template <bool COH>
+// flags collects the chunks' flags.
 __device__ __forceinline__ int merge_global_lists(const TopkLists& t, long unit0, int C, float& v, int& i,
                                                   uint32_t& flags) {
     const int lane = threadIdx.x & (kWave - 1);
     int nl = 0;
     uint32_t fl = 0u;
     if (lane < C) {
-        nl = ld<COH>(t.cnt + unit0 + lane);
-        fl = ld<COH>(t.flags + unit0 + lane);
+        nl = t.cnt[unit0 + lane];
+        fl = t.flags[unit0 + lane];
     }
     pkey_t acc = empty_key();
 #pragma unroll 1
@@ -40,8 +38,8 @@ __device__ __forceinline__ int merge_global_lists(const TopkLists& t, long unit0
         for (int c = 0; c < kMergeBatch; ++c) {
             if (base + c < C) {
                 const long u = unit0 + base + c;
-                w[c] = ld<COH>(t.vals + u * kTopkMax + lane);
-                wi[c] = ld<COH>(t.idx + u * kTopkMax + lane);
+                w[c] = t.vals[u * kTopkMax + lane];
+                wi[c] = t.idx[u * kTopkMax + lane];
             }
         }
         if (base == 0) nl = min(max(nl, 0), kTopkMax);
@@ -138,14 +136,13 @@ __device__ __forceinline__ int lane_draw(double r, bool have, double target) {
 // Kept distribution of row (b, k) of a chain or acceptance-rate call: target
 // row (draft = false) or draft row; one wave.  Returns false when the row is
 // unusable.
-template <bool COH>
 __device__ __forceinline__ bool position_row(const TopkLists& t, int b, int k, bool draft, int& idx, double& p,
                                              int& kk) {
     const long unit0 = t.unit_base(b, k) + (draft ? t.Ct : 0);
     float v;
     int i;
     uint32_t flags = 0;
-    const int tot = merge_global_lists<COH>(t, unit0, draft ? t.Cd : t.Ct, v, i, flags);
+    const int tot = merge_global_lists(t, unit0, draft ? t.Cd : t.Ct, v, i, flags);
     kk = tot < t.top_k ? tot : t.top_k;
     return kept_distribution(v, i, kk, flags == 0u, draft, t.invT, draft && t.draft_identity, idx, p);
 }

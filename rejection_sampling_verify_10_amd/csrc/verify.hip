@@ -149,11 +149,11 @@ __global__ __launch_bounds__(2 * kWave) void alpha_topk_kernel(AlphaArgs a) {
     int it = kNoIndex, kt = 0;
     double pt = 0.0;
     bool ok = false;
-    if (wid == 0) ok = position_row<false>(a.tk, b, k, false, it, pt, kt);
+    if (wid == 0) ok = position_row(a.tk, b, k, false, it, pt, kt);
     else {
         int id, kd;
         double pd;
-        const bool okd = position_row<false>(a.tk, b, k, true, id, pd, kd);
+        const bool okd = position_row(a.tk, b, k, true, id, pd, kd);
         sidx[lane] = id;
         sp[lane] = pd;
         if (lane == 0) { skd = kd; sok = okd; }
