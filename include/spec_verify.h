@@ -26,8 +26,9 @@
  *   - `workspace` is device scratch of at least the size reported by the
  *     matching *_workspace_bytes function, 256-byte aligned.  It must be
  *     zero-filled before its first use (spec_workspace_init, or any zeroing
- *     allocation); every call leaves it in that reusable state (its completion
- *     counters return to zero), so zeroing once is enough.  A workspace serves
+ *     allocation); every call leaves it in that reusable state (the hand-over
+ *     words one call writes are cleared by the same call), so zeroing once is
+ *     enough.  A workspace serves
  *     one call at a time: calls that may overlap need separate workspaces.
  *   - Logit rows are bfloat16 (SPEC_BF16, raw bits) or float32 (SPEC_F32).
  *     Draft probabilities are float32.  Uniforms are float32 in [0, 1).
