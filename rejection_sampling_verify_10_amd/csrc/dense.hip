@@ -54,6 +54,10 @@ constexpr int kEPT = kDenseChunk / kThreads;        // 8 elements per thread per
 constexpr int kSub = kEPT / 8;                      // 8-element groups per thread
 constexpr int kMaxChunks = (kMaxV + kDenseChunk - 1) / kDenseChunk;
 constexpr int kListCap = 64;                        // undecided elements per row
+// Register buffers of the streaming pass: three (two chunks in flight) where the
+// registers allow four waves per SIMD, else two.
+template <bool VEC, bool TR> constexpr int ring_depth() { return (VEC && !TR) ? 3 : 2; }
+template <bool VEC, bool TR> constexpr int min_waves() { return (VEC && !TR) ? 4 : 2; }
 
 // exp(x) for x <= 0 in fp64 by Tang's table-driven method (ACM TOMS 15(2),
 // 1989), with 256 table entries.  The caller passes y = x * 256/ln2 (folded
@@ -108,6 +112,47 @@ __device__ __forceinline__ double exp_of(float z, const ExpArg& g, const double*
     return exp_scaled(fma(static_cast<double>(z), g.k1, g.mk1), tbl, k);
 }
 
+// bfloat16 logits take few distinct values: the pass looks exp((z - m)/T) up in
+// a per-row LDS table holding exp_of of every bf16 value with 2^-20 <= |z| < 256
+// (28 binades of 128 values per sign), so the result is the one exp_of gives.
+// Entry of bit pattern h: sign(h)*kTabSpan + (h & 0x7fff) - kTabLo.  Values
+// outside the table (smaller, larger, zero, inf, NaN) take exp_of.
+constexpr uint32_t kTabLo = 0x3580u;                 // bf16 bits of 2^-20
+constexpr uint32_t kTabSpan = 0x0e00u;               // bits of 256 minus kTabLo
+constexpr int kTabSize = 2 * static_cast<int>(kTabSpan);
+constexpr size_t kTabBytes = kTabSize * sizeof(double);
+
+__device__ __forceinline__ void build_exp_table(double* etab, const ExpArg& g, const double* tbl, const ExpConsts& k) {
+    for (int t = threadIdx.x; t < kTabSize; t += blockDim.x) {
+        const uint32_t h = t < static_cast<int>(kTabSpan) ? kTabLo + t : 0x8000u + kTabLo + (t - kTabSpan);
+        etab[t] = exp_of(__uint_as_float(h << 16), g, tbl, k);
+    }
+}
+
+// exp_of of the 8 bf16 logits of r, from the table where it holds them.
+template <typename R8>
+__device__ __forceinline__ void exp8_table(const R8& r, const double* etab, const ExpArg& g, const double* tbl,
+                                           const ExpConsts& k, double ex[8]) {
+    bool out = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t w = r.z[0][e >> 1];
+        const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xffffu);
+        const uint32_t off = (h & 0x7fffu) - kTabLo;
+        const bool in = off < kTabSpan;
+        out |= !in;
+        ex[e] = etab[(in ? off : 0u) + ((h & 0x8000u) ? kTabSpan : 0u)];
+    }
+    if (__ballot(out)) {            // wave-uniform: rows with logits outside the table
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t w = r.z[0][e >> 1];
+            const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xffffu);
+            if ((h & 0x7fffu) - kTabLo >= kTabSpan) ex[e] = exp_of(r.zf(e), g, tbl, k);
+        }
+    }
+}
+
 // Eight consecutive logits from i0 (a multiple of 8); -inf past V.  With VEC
 // the row is 16-byte aligned and V a multiple of the vector length, so each
 // vector lies wholly inside or wholly past the row.
@@ -160,6 +205,21 @@ template <int DT> struct Raw8 {
         return DT == 1 ? Elem<1>::get(z[0], e) : __uint_as_float(z[e >> 2][e & 3]);
     }
     __device__ __forceinline__ float qf(int e) const { return __uint_as_float(q[e >> 2][e & 3]); }
+    // The same for an index known only at run time (selects, no register indexing).
+    __device__ __forceinline__ static uint32_t pick4(const u32x4& v, int i) {
+        const uint32_t lo = (i & 1) ? v[1] : v[0], hi = (i & 1) ? v[3] : v[2];
+        return (i & 2) ? hi : lo;
+    }
+    __device__ __forceinline__ float zf_at(int e) const {
+        if (DT == 1) {
+            const uint32_t w = pick4(z[0], e >> 1);
+            return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+        }
+        return __uint_as_float((e & 4) ? pick4(z[kZW - 1], e & 3) : pick4(z[0], e & 3));
+    }
+    __device__ __forceinline__ float qf_at(int e) const {
+        return __uint_as_float((e & 4) ? pick4(q[1], e & 3) : pick4(q[0], e & 3));
+    }
 };
 // GUARD: the vectors may lie past the row's end.  Loads are then issued from a
 // clamped (valid) address and replaced by padding, so that no load sits behind a
@@ -309,9 +369,12 @@ __device__ __forceinline__ float row_scan(float v) {
 // wave (8 slots; longer rows, fewer slots, the same 48 KiB bound).
 constexpr int kRowSlots = kWaves * 4;
 __host__ __device__ inline int dense_slots(int C) { return C <= 128 ? kRowSlots : kWaves; }
-inline size_t dense_dyn_lds(int C) {
-    return static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float));
+inline size_t dense_dyn_lds(int C, bool tab) {
+    return (tab ? kTabBytes : 0) + static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float));
 }
+// The exponential table is used when two workgroups still fit a CU's 160 KiB of
+// LDS (bf16 rows of up to 48 chunks).
+constexpr int kTabMaxChunks = 48;
 
 struct RowSmem {
     double tbl[kTableSize];
@@ -325,8 +388,9 @@ struct RowSmem {
     double before;
 };
 
-template <int DT, bool VEC, bool TR>
-__global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, double bracket, ExpConsts ek) {
+template <int DT, bool VEC, bool TR, bool TAB>
+__global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_kernel(ChainArgs a, double bracket, ExpConsts ek) {
+    static_assert(!TAB || DT == 1, "the exponential table is for bf16 logits");
     __shared__ RowSmem sm;
     extern __shared__ double dyn_lds[];
     const int b = blockIdx.x;
@@ -335,8 +399,9 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
     const int C = (V + kDenseChunk - 1) / kDenseChunk;
     const int C_full = V / kDenseChunk;              // chunks wholly inside the row
     const int nslots = dense_slots(C);
-    double* pr = dyn_lds;                            // [C][nslots]: R (residual rows) or E
-    float* pp = reinterpret_cast<float*>(dyn_lds + static_cast<long>(C) * nslots);   // [C][nslots]: P
+    double* etab = dyn_lds;                          // TAB: [kTabSize] exponentials
+    double* pr = dyn_lds + (TAB ? kTabSize : 0);     // [C][nslots]: R (residual rows) or E
+    float* pp = reinterpret_cast<float*>(pr + static_cast<long>(C) * nslots);        // [C][nslots]: P
     const long rbase = static_cast<long>(b) * (K + 1);
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
 
@@ -372,6 +437,10 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
     // holds whenever |d| > tol2*w'.
     const double tol = bracket * (1.0 + 2.0 * bracket) + 1e-12;
     const double tol2 = 2.0 * tol / (1.0 - tol);
+    if constexpr (TAB) {
+        build_exp_table(etab, g, tbl, ek);
+        __syncthreads();
+    }
 
     // ---- one pass over row j ----
     double sq_tot = 0.0;                   // transformed draft: sum w over the thread's elements
@@ -398,8 +467,10 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
                         qmax = maximum3(qmax, rb[s].qf(e), rb[s].qf(e + 1));
                     }
                 }
+                double ext[8];
+                if constexpr (TAB) exp8_table(rb[s], etab, g, tbl, ek, ext);
                 auto one = [&](int e) {
-                    const double ex = exp_of(rb[s].zf(e), g, tbl, ek);
+                    const double ex = TAB ? ext[e] : exp_of(rb[s].zf(e), g, tbl, ek);
                     se += ex;
                     if (RES) {
                         const float qv = rb[s].qf(e);
@@ -423,8 +494,28 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
             if (RES) {
                 if (__ballot(!(qmin >= 0.f && qmax < INFINITY)) && lane == 0) atomicOr(&sm.qbad, 1u);
                 // Undecided elements are rare (about one per row): list them in a
-                // wave-uniform branch, re-reading the thread's elements of the chunk.
-                if (__ballot(und) && und) {
+                // wave-uniform branch.  Untransformed drafts recompute the thread's
+                // elements from the registers (a branch holding loads would make
+                // the compiler wait for every prefetch in flight); transformed
+                // ones re-read them, keeping a single copy of the power function.
+                if constexpr (!TR) {
+                    if (__ballot(und)) {
+#pragma unroll
+                        for (int s2 = 0; s2 < kSub; ++s2) {
+#pragma unroll 1
+                            for (int e = 0; e < 8; ++e) {
+                                const int i = c * kDenseChunk + (s2 * kThreads + tid) * 8 + e;
+                                const double ex = exp_of(rb[s2].zf_at(e), g, tbl, ek);
+                                const double w = static_cast<double>(rb[s2].qf_at(e));
+                                const double dd = fma(ex, iz, -w);
+                                if (und && i < V && fabs(dd) <= tol2 * w) {
+                                    const int p = atomicAdd(&sm.n_list, 1);
+                                    if (p < kListCap) { sm.li[p] = i; sm.le[p] = ex; sm.lw[p] = w; }
+                                }
+                            }
+                        }
+                    }
+                } else if (__ballot(und) && und) {
 #pragma unroll 1
                     for (int k = 0; k < kEPT; ++k) {
                         const int i = c * kDenseChunk + ((k >> 3) * kThreads + tid) * 8 + (k & 7);
@@ -461,24 +552,29 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
                 }
             }
         };
-        // Full chunks: chunk c+1 is in flight while chunk c is computed (two register
-        // buffers).  The loads are unconditional (indices clamped to the last full
-        // chunk; the surplus loads are discarded) so that the wait for one buffer
-        // does not also wait for the other.  The partial last chunk comes after.
-        Buf ra, rn;
-        if (C_full > 0) load(0, ra, std::false_type{});
+        // Full chunks: a ring of kRing register buffers keeps chunks c+1 .. c+kRing-1
+        // in flight while chunk c is computed.  The loads are unconditional (indices
+        // clamped to the last full chunk; the surplus loads are discarded) so that
+        // the wait for one buffer does not also wait for the others.  The partial
+        // last chunk comes after.
+        constexpr int kRing = ring_depth<VEC, TR>();
+        Buf ring[kRing];
+        if (C_full > 0) {
+#pragma unroll
+            for (int r = 0; r < kRing - 1; ++r) load(min(r, C_full - 1), ring[r], std::false_type{});
+        }
 #pragma unroll 1
-        for (int c = 0; c < C_full; c += 2) {
-            load(min(c + 1, C_full - 1), rn, std::false_type{});
-            __builtin_amdgcn_sched_barrier(0);     // keep the prefetch ahead of the compute
-            compute(c, ra);
-            load(min(c + 2, C_full - 1), ra, std::false_type{});
-            __builtin_amdgcn_sched_barrier(0);
-            if (c + 1 < C_full) compute(c + 1, rn);
+        for (int c = 0; c < C_full; c += kRing) {
+#pragma unroll
+            for (int st = 0; st < kRing; ++st) {
+                load(min(c + st + kRing - 1, C_full - 1), ring[(st + kRing - 1) % kRing], std::false_type{});
+                __builtin_amdgcn_sched_barrier(0);     // keep the prefetch ahead of the compute
+                if (st == 0 || c + st < C_full) compute(c + st, ring[st]);
+            }
         }
         if (C_full < C) {
-            load(C_full, ra, std::true_type{});
-            compute(C_full, ra);
+            load(C_full, ring[0], std::true_type{});
+            compute(C_full, ring[0]);
         }
     };
     if (res) body(std::true_type{});
@@ -680,8 +776,15 @@ __global__ __launch_bounds__(kThreads, 2) void dense_row_kernel(ChainArgs a, dou
 template <int DT, bool VEC, bool TR>
 hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s) {
     const int C = (a.V + kDenseChunk - 1) / kDenseChunk;
-    hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR>), dim3(a.B), dim3(kThreads),
-                       static_cast<unsigned>(dense_dyn_lds(C)), s, a, bracket, exp_consts());
+    if constexpr (DT == 1 && VEC && !TR) {
+        if (C <= kTabMaxChunks) {
+            hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR, true>), dim3(a.B), dim3(kThreads),
+                               static_cast<unsigned>(dense_dyn_lds(C, true)), s, a, bracket, exp_consts());
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR, false>), dim3(a.B), dim3(kThreads),
+                       static_cast<unsigned>(dense_dyn_lds(C, false)), s, a, bracket, exp_consts());
     return hipGetLastError();
 }
 
