@@ -9,10 +9,10 @@ inputs are rotated so that the working set exceeds the 256 MB Infinity Cache.
 
 Prints ONE JSON line: verified token-rows/s (B*(K+1) per step) and the step
 time from K timed steps with nothing else on the stream; the dominant kernel's
-achieved HBM bandwidth against the 8 TB/s peak, timed live with HIP events
-that the library records around that kernel on the call's stream during a
-second pass of K steps (event records between kernels add several
-microseconds of queue latency, so they stay out of the step timing); the
+achieved HBM bandwidth against the 8 TB/s peak, timed live with HIP events that
+the library attaches to that kernel's dispatch on the call's stream during a
+second pass of K steps (events between kernels add several microseconds of
+queue latency, so they stay out of the step timing); the
 hardware-counter traffic recorded under profiles/ when it matches the current
 kernel source; and the CPU oracle's throughput on the host cores.
 
@@ -245,8 +245,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg,
-                     "kernel_timing": "HIP events around the kernel on the call's stream, second pass of "
-                                      "the same number of steps",
+                     "kernel_timing": "HIP events attached to the kernel's dispatch (hipExtLaunchKernel) on "
+                                      "the call's stream, second pass of the same number of steps",
                      "read_probe_GBps": probe, "frac_of_read_probe": achieved / probe},
         "cpu_baseline": cpu,
     }

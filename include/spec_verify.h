@@ -173,9 +173,10 @@ int spec_workspace_init(void* workspace, size_t workspace_bytes, void* hip_strea
  * Instrumentation.
  *
  * spec_profile_events: the next verification call made BY THIS HOST THREAD
- * records `start_event` immediately before and `stop_event` immediately after
- * its dominant (vocabulary-streaming) kernel, on its stream; both are
- * hipEvent_t created by the caller.  The request is consumed by that call.
+ * launches its dominant (vocabulary-streaming) kernel with `start_event` and
+ * `stop_event` attached to the dispatch (hipExtLaunchKernel), so that they hold
+ * that kernel's own start and end times; both are hipEvent_t created by the
+ * caller.  The request is consumed by that call.
  *
  * spec_copy_probe: plain device-to-device copy of `bytes` (multiple of 16,
  * 16-byte aligned pointers) by a streaming kernel, for calibrating hardware

@@ -19,14 +19,16 @@ static_assert(SPEC_MAX_V == kMaxV, "vocabulary limit");
 thread_local hipEvent_t t_prof_start = nullptr;
 thread_local hipEvent_t t_prof_stop = nullptr;
 
+// The pending profiling request of this thread, consumed by the call that
+// constructs it and handed to its dominant kernel's launch.
 struct ProfileScope {
-    hipStream_t s;
-    hipEvent_t start, stop;
-    explicit ProfileScope(hipStream_t st) : s(st), start(t_prof_start), stop(t_prof_stop) {
+    Timing t;
+    ProfileScope() {
+        t.start = t_prof_start;
+        t.stop = t_prof_stop;
         t_prof_start = t_prof_stop = nullptr;
     }
-    void before() const { if (start) (void)hipEventRecord(start, s); }
-    void after() const { if (stop) (void)hipEventRecord(stop, s); }
+    Timing timing() const { return t; }
 };
 
 // Bump allocator over the caller's workspace (or a size counter when base is null).
@@ -276,7 +278,7 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
     if (rc) return rc;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    ProfileScope prof(s);
+    ProfileScope prof;
     Carver c(workspace);
     ChainPlan p = plan_chain(c, B, K, V, dtype, temperature, top_k);
 
@@ -299,9 +301,7 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
     if (p.mode == 2) {
         ca.st = p.st;
         RowStatsArgs ra = rowstats_args(target_logits, dtype, V, K + 1, K + 1, B, true, 0.f, nullptr, 0, p.st);
-        prof.before();
-        SV_TRY(launch_rowstats(ra, s));
-        prof.after();
+        SV_TRY(launch_rowstats(ra, s, prof.timing()));
         SV_TRY(launch_chain_greedy(ca, s));
     } else if (p.mode == 1) {
         ca.tk = p.tk;
@@ -309,16 +309,12 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
         TopkChainArgs fa{};
         fa.sel = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K + 1, p.tk);
         fa.ch = ca;
-        prof.before();
-        SV_TRY(launch_chain_topk(fa, s));
-        prof.after();
+        SV_TRY(launch_chain_topk(fa, s, prof.timing()));
     } else {
         ca.st = p.st;
         RowStatsArgs ra =
             rowstats_args(target_logits, dtype, V, K + 1, K + 1, B, false, temperature, draft_tokens, K, p.st);
-        prof.before();
-        SV_TRY(launch_rowstats(ra, s));
-        prof.after();
+        SV_TRY(launch_rowstats(ra, s, prof.timing()));
         if (ca.transformed) {
             PowerSumArgs pa{draft_probs, V, B * K, static_cast<float>(1.0 / temperature), p.qsum, p.qflags};
             SV_TRY(launch_power_sums(pa, s));
@@ -360,13 +356,11 @@ int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype, const
     if (rc) return rc;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    ProfileScope prof(s);
+    ProfileScope prof;
     Carver c(workspace);
     RowStats st = carve_rowstats(c, static_cast<size_t>(B) * N);
     RowStatsArgs ra = rowstats_args(target_logits, dtype, V, N, N, B, true, 0.f, nullptr, 0, st);
-    prof.before();
-    SV_TRY(launch_rowstats(ra, s));
-    prof.after();
+    SV_TRY(launch_rowstats(ra, s, prof.timing()));
     ta.node_tokens = node_tokens;
     ta.B = B;
     ta.N = N;
@@ -395,7 +389,7 @@ int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float*
     if (rc) return rc;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    ProfileScope prof(s);
+    ProfileScope prof;
     Carver c(workspace);
     AlphaPlan p = plan_alpha(c, B, K, V, dtype, temperature, top_k);
     AlphaArgs aa{};
@@ -411,25 +405,20 @@ int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float*
     aa.transformed = (!greedy && temperature != 1.f) ? 1 : 0;
     aa.out_alpha = out_alpha;
     if (p.mode == 2) {
-        prof.before();
-        SV_TRY(launch_rowstats(rowstats_args(target_logits, dtype, V, K, K + 1, B, true, 0.f, nullptr, 0, p.st), s));
-        prof.after();
+        SV_TRY(launch_rowstats(rowstats_args(target_logits, dtype, V, K, K + 1, B, true, 0.f, nullptr, 0, p.st), s,
+                               prof.timing()));
         SV_TRY(launch_rowstats(rowstats_args(draft_probs, SPEC_F32, V, K, K, B, true, 0.f, nullptr, 0, p.qst), s));
         aa.st = p.st;
         aa.qst = p.qst;
         SV_TRY(launch_alpha_greedy(aa, s));
     } else if (p.mode == 1) {
         TopkChunkArgs ta = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K, p.tk);
-        prof.before();
-        SV_TRY(launch_topk_chunks(ta, s));
-        prof.after();
+        SV_TRY(launch_topk_chunks(ta, s, prof.timing()));
         aa.tk = p.tk;
         SV_TRY(launch_alpha_topk(aa, s));
     } else {
-        prof.before();
         SV_TRY(launch_rowstats(
-            rowstats_args(target_logits, dtype, V, K, K + 1, B, false, temperature, nullptr, 0, p.st), s));
-        prof.after();
+            rowstats_args(target_logits, dtype, V, K, K + 1, B, false, temperature, nullptr, 0, p.st), s, prof.timing()));
         aa.st = p.st;
         if (aa.transformed) {
             PowerSumArgs pa{draft_probs, V, B * K, static_cast<float>(1.0 / temperature), p.qsum, p.qflags};

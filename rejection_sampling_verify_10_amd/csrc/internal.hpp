@@ -1,11 +1,24 @@
 // Kernel argument blocks and launchers shared by the library's translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace sv {
+
+// Events that timestamp one kernel launch (taken from the dispatch itself, not
+// from markers queued around it), or none.
+struct Timing {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename... Params, typename... Args>
+inline void launch_timed(const Timing& t, void (*kernel)(Params...), dim3 grid, dim3 block, unsigned shmem,
+                         hipStream_t s, Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, t.start, t.stop, 0u, args...);
+}
 
 // Per-row statistics of a logit row (dense path, greedy path).
 struct RowStats {
@@ -133,10 +146,10 @@ inline bool vec_ok(const void* p, int V, int esz) {
     return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((static_cast<long>(V) * esz) % 16 == 0);
 }
 
-hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s);
+hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_power_sums(const PowerSumArgs& a, hipStream_t s);
-hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s);
-hipError_t launch_chain_topk(const TopkChainArgs& a, hipStream_t s);   // selection + finish
+hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s, Timing t = {});
+hipError_t launch_chain_topk(const TopkChainArgs& a, hipStream_t s, Timing t = {});   // selection + finish
 hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
 // bracket: relative half-width of the brackets put around the row statistics'
 // normalisers (any value gives the same result; it sets how often the slow path runs)

@@ -306,15 +306,15 @@ hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s) {
+hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s, Timing t) {
     const bool vec = vec_ok(a.base, a.V, a.dtype ? 2 : 4);
     dim3 grid(a.R), block(kThreads);
     if (a.dtype == 1) {
-        if (vec) hipLaunchKernelGGL((rowstats_kernel<1, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((rowstats_kernel<1, false>), grid, block, 0, s, a);
+        if (vec) launch_timed(t, rowstats_kernel<1, true>, grid, block, 0, s, a);
+        else launch_timed(t, rowstats_kernel<1, false>, grid, block, 0, s, a);
     } else {
-        if (vec) hipLaunchKernelGGL((rowstats_kernel<0, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((rowstats_kernel<0, false>), grid, block, 0, s, a);
+        if (vec) launch_timed(t, rowstats_kernel<0, true>, grid, block, 0, s, a);
+        else launch_timed(t, rowstats_kernel<0, false>, grid, block, 0, s, a);
     }
     return hipGetLastError();
 }

@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 4) void topk_chunk_kernel(TopkChainArgs f
 }  // namespace
 
 template <bool FIN>
-hipError_t launch_selection(const TopkChainArgs& fa, hipStream_t s) {
+hipError_t launch_selection(const TopkChainArgs& fa, hipStream_t s, Timing t) {
     const TopkChunkArgs& a = fa.sel;
     const int esz = a.dtype ? 2 : 4;
     const bool vec = vec_ok(a.target, a.V, esz) && vec_ok(a.draft, a.V, 4);
@@ -401,21 +401,21 @@ hipError_t launch_selection(const TopkChainArgs& fa, hipStream_t s) {
         static_cast<unsigned>(static_cast<long>(a.B) * a.l.Ub + (FIN ? static_cast<long>(a.B) * finish_groups(a.K) : 0));
     if (units == 0) return hipSuccess;
     if (a.dtype == 1) {
-        if (vec) hipLaunchKernelGGL((topk_chunk_kernel<1, true, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
-        else hipLaunchKernelGGL((topk_chunk_kernel<1, false, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
+        if (vec) launch_timed(t, topk_chunk_kernel<1, true, FIN>, dim3(units), dim3(kThreads), 0, s, fa);
+        else launch_timed(t, topk_chunk_kernel<1, false, FIN>, dim3(units), dim3(kThreads), 0, s, fa);
     } else {
-        if (vec) hipLaunchKernelGGL((topk_chunk_kernel<0, true, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
-        else hipLaunchKernelGGL((topk_chunk_kernel<0, false, FIN>), dim3(units), dim3(kThreads), 0, s, fa);
+        if (vec) launch_timed(t, topk_chunk_kernel<0, true, FIN>, dim3(units), dim3(kThreads), 0, s, fa);
+        else launch_timed(t, topk_chunk_kernel<0, false, FIN>, dim3(units), dim3(kThreads), 0, s, fa);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s) {
+hipError_t launch_topk_chunks(const TopkChunkArgs& a, hipStream_t s, Timing t) {
     TopkChainArgs fa{};
     fa.sel = a;
-    return launch_selection<false>(fa, s);
+    return launch_selection<false>(fa, s, t);
 }
 
-hipError_t launch_chain_topk(const TopkChainArgs& a, hipStream_t s) { return launch_selection<true>(a, s); }
+hipError_t launch_chain_topk(const TopkChainArgs& a, hipStream_t s, Timing t) { return launch_selection<true>(a, s, t); }
 
 }  // namespace sv
