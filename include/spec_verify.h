@@ -36,14 +36,17 @@
  *     nothing.  Bad DATA never aborts a call: the affected batch row gets
  *     accept_len = -1 and all its output tokens (and path entries) = -1,
  *     under these rules:
- *       E1 a target row that is read contains NaN, or (sampling mode) +inf, or
- *          only -inf values;
- *       E2 a draft / node token outside [0, V);
- *       E3 a draft probability that is read is NaN, negative or +inf (with
- *          T = 1 and no top-k only q[x_k] and, after a rejection at j, row j
- *          are read; otherwise all K draft rows are read);
- *       E4 a transformed draft row keeps zero mass;
- *       E5 a uniform outside [0, 1) (sampling mode).
+ *       E1 a target row that is consulted contains NaN, or (sampling mode)
+ *          +inf, or only -inf values;
+ *       E2 a draft / node token outside [0, V) (every token is checked);
+ *       E3 a draft probability that is consulted is NaN, negative or +inf;
+ *       E4 a transformed draft row that is consulted keeps zero mass;
+ *       E5 a uniform outside [0, 1) (sampling mode; every uniform is checked).
+ *     A chain consults position k only when x_0..x_{k-1} were all accepted
+ *     (the left-to-right walk of the method): target rows 0..j, and for the
+ *     draft, q[x_k] for k <= j (T == 1, no top-k) or whole rows 0..j (any
+ *     other transform), plus row j itself for a residual draw; j = first
+ *     rejection (K if none).  A tree consults every node row.
  *   - Environment: SPEC_VERIFY_DENSE_BRACKET (a number in [0, 0.5)) sets the
  *     relative width of the bracket the dense final draw (temperature > 0,
  *     top-k off) puts around the normalisers taken from its row statistics.
@@ -115,7 +118,9 @@ size_t spec_accept_rate_workspace_bytes(int B, int K, int V, spec_dtype_t dtype,
  *   out_tokens    [B][K+1]     int32                   device, written: x_0..x_{j-1}, y, then -1
  *   out_accept_len[B]          int32                   device, written: j in [0,K], -1 on error
  *   out_diag      [B][2K+2]    float32, may be NULL    device, written:
- *                 [k] = p'_k(x_k), [K+k] = q'_k(x_k) for k < K,
+ *                 [k] = p'_k(x_k), [K+k] = q'_k(x_k) for the tested
+ *                 positions k <= j, k < K (NaN for k > j; greedy: [k] = 1 if
+ *                 x_k matched, else 0, and [K+k] = NaN),
  *                 [2K] = mass of the final-draw distribution before
  *                 normalisation (residual mass, or 1 for p'), [2K+1] = the
  *                 drawn token's probability under it.

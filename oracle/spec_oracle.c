@@ -43,11 +43,16 @@
  *     is the deepest accepted node, lowest node index on ties.
  *
  * Error rules (a batch row with an error gets accept_len = -1 and -1 tokens):
- *   E1 a target row holds NaN, or (sampling mode) +inf or only -inf values;
- *   E2 a draft / node token lies outside [0, V);
+ *   E1 a target row the walk consults holds NaN, or (sampling mode) +inf or
+ *      only -inf values;
+ *   E2 a draft / node token lies outside [0, V) (all of them are checked);
  *   E3 a draft probability that is read is NaN, negative or +inf;
- *   E4 transformed draft row with zero kept mass;
- *   E5 a uniform outside [0, 1) (sampling mode).
+ *   E4 a transformed draft row the walk consults keeps zero mass;
+ *   E5 a uniform outside [0, 1) (sampling mode; all of them are checked).
+ * The chain walk consults position k only when every earlier draft token was
+ * accepted ([LEV] section 3): target rows 0..j and the draft rows / entries of
+ * positions 0..j, j the first rejection (K if none).  Tree nodes are verified
+ * together: every node row is consulted.
  */
 #include <math.h>
 #include <stdint.h>
@@ -213,7 +218,8 @@ static int q_ok(float v) { return !(isnan(v) || v < 0.0f || v == INFINITY); }
  * [E2] section 2.1).  Layouts (row-major):
  *   logits [B][K+1][V] (bf16 bits or f32), q [B][K][V] f32, x [B][K] i32, u [B][K+1] f32.
  * Outputs: tokens [B][K+1] (-1 padded), accept_len [B] (-1 on error),
- *   pk, qk [B][K]: p'_k(x_k), q'_k(x_k) for every k (NaN where undefined);
+ *   pk, qk [B][K]: p'_k(x_k), q'_k(x_k) for the positions tested, k <= j
+ *   (NaN past the first rejection and on error);
  *   S [B]: mass of the final-draw distribution before normalising; py [B]: r_y/S;
  *   m_test [B][K]: |u_k - min(1, ratio_k)| for tests performed (NaN otherwise);
  *   m_draw [B]: distance of u*S to the nearest edge of the chosen cell, over S.
@@ -242,21 +248,26 @@ int oracle_verify_chain(const void* logits, int dtype, const float* q, const int
         accept_len[b] = -1;
         int err = 0;
         for (int k = 0; k < K; ++k) if (xb[k] < 0 || xb[k] >= V) err = 1;   /* E2 */
+        /* The walk of [LEV] section 3: position k is examined only after every
+         * earlier draft token was accepted, so the rows of positions past the
+         * first rejection are never consulted (nor checked for E1 / E3 / E4). */
         if (greedy) {
-            int g[K + 1];
-            for (int k = 0; k <= K && !err; ++k) {
-                g[k] = oracle_argmax_row(zb + (size_t)k * V * esz, dtype, V);
-                if (g[k] < 0) err = 1;                                            /* E1 */
-            }
             if (err) continue;
-            int j = K;
-            for (int k = 0; k < K; ++k) {
-                pkb[k] = (xb[k] == g[k]) ? 1.0 : 0.0;
+            int j = K, gj = -1;
+            for (int k = 0; k <= K; ++k) {
+                const int g = oracle_argmax_row(zb + (size_t)k * V * esz, dtype, V);
+                if (g < 0) { err = 1; break; }                                   /* E1 */
+                if (k == K) { gj = g; break; }
+                pkb[k] = (xb[k] == g) ? 1.0 : 0.0;
                 mtb[k] = INFINITY;
+                if (xb[k] != g) { j = k; gj = g; break; }
             }
-            for (int k = 0; k < K; ++k) if (xb[k] != g[k]) { j = k; break; }
+            if (err) {
+                for (int k = 0; k < K; ++k) { pkb[k] = NAN; mtb[k] = NAN; }
+                continue;
+            }
             for (int k = 0; k < j; ++k) tb[k] = xb[k];
-            tb[j] = g[j];
+            tb[j] = gj;
             accept_len[b] = j;
             S_out[b] = 1.0; py_out[b] = 1.0; m_draw[b] = INFINITY;
             continue;
@@ -266,31 +277,34 @@ int oracle_verify_chain(const void* logits, int dtype, const float* q, const int
         double* p = (double*)malloc(sizeof(double) * (size_t)(K + 1) * V);
         double* qq = (double*)malloc(sizeof(double) * (size_t)V * (transformed ? K : 1));
         double* r = (double*)malloc(sizeof(double) * (size_t)V);
-        for (int k = 0; k <= K && !err; ++k)
-            if (oracle_target_dist(zb + (size_t)k * V * esz, dtype, V, T, top_k, p + (size_t)k * V))
+        /* Ratio tests left to right, stop at the first rejection. */
+        int j = K;
+        for (int k = 0; k <= K; ++k) {
+            if (oracle_target_dist(zb + (size_t)k * V * esz, dtype, V, T, top_k, p + (size_t)k * V)) {
                 err = 1;                                                           /* E1 */
-        if (transformed)
-            for (int k = 0; k < K && !err; ++k)
-                if (oracle_draft_dist(qb + (size_t)k * V, V, T, top_k, qq + (size_t)k * V))
+                break;
+            }
+            if (k == K) break;
+            if (transformed) {
+                if (oracle_draft_dist(qb + (size_t)k * V, V, T, top_k, qq + (size_t)k * V)) {
                     err = 1;                                                       /* E3, E4 */
-        if (!transformed)
-            for (int k = 0; k < K; ++k) if (!q_ok(qb[(size_t)k * V + xb[k]])) err = 1;   /* E3 */
+                    break;
+                }
+            } else if (!q_ok(qb[(size_t)k * V + xb[k]])) {
+                err = 1;                                                           /* E3 */
+                break;
+            }
+            pkb[k] = p[(size_t)k * V + xb[k]];
+            qkb[k] = transformed ? qq[(size_t)k * V + xb[k]] : (double)qb[(size_t)k * V + xb[k]];
+            double a = pkb[k], c = qkb[k], ratio;
+            if (g_variant == 3) { double t = a; a = c; c = t; }
+            if (c > 0.0) ratio = a / c;
+            else ratio = a > 0.0 ? INFINITY : 0.0;
+            double thr = ratio < 1.0 ? ratio : 1.0;
+            mtb[k] = fabs((double)ub[k] - thr);
+            if (!((double)ub[k] < thr)) { j = k; break; }
+        }
         if (!err) {
-            for (int k = 0; k < K; ++k) {
-                pkb[k] = p[(size_t)k * V + xb[k]];
-                qkb[k] = transformed ? qq[(size_t)k * V + xb[k]] : (double)qb[(size_t)k * V + xb[k]];
-            }
-            /* Ratio tests left to right, stop at the first rejection. */
-            int j = K;
-            for (int k = 0; k < K; ++k) {
-                double a = pkb[k], c = qkb[k], ratio;
-                if (g_variant == 3) { double t = a; a = c; c = t; }
-                if (c > 0.0) ratio = a / c;
-                else ratio = a > 0.0 ? INFINITY : 0.0;
-                double thr = ratio < 1.0 ? ratio : 1.0;
-                mtb[k] = fabs((double)ub[k] - thr);
-                if (!((double)ub[k] < thr)) { j = k; break; }
-            }
             /* Final draw with u[K]: residual at the rejected position, else bonus. */
             const double* pj = p + (size_t)j * V;
             double S = 0.0;
@@ -321,10 +335,10 @@ int oracle_verify_chain(const void* logits, int dtype, const float* q, const int
                 S_out[b] = S;
                 py_out[b] = r[y] / S;
                 m_draw[b] = md;
-            } else {
-                for (int k = 0; k < K; ++k) { pkb[k] = NAN; qkb[k] = NAN; mtb[k] = NAN; }
             }
         }
+        if (err)
+            for (int k = 0; k < K; ++k) { pkb[k] = NAN; qkb[k] = NAN; mtb[k] = NAN; }
         free(p);
         free(qq);
         free(r);

@@ -118,9 +118,10 @@ __device__ __forceinline__ bool word_row(const TopkLists& t, int b, int k, bool 
 }
 
 // ---- position records: kRecWords words per position (payload in bits 63..32,
-// bit 0 valid): y with accept (bit 2) and bad (bit 1); then p'_k(x_k),
-// q'_k(x_k), the draw's mass S and the drawn token's probability.  Zero
-// between calls.
+// bit 0 valid): y with accept (bit 2), rows unusable (bit 1: E1 / E3 / E4,
+// they count only if the walk reaches the position) and inputs invalid (bit 3:
+// E2 / E5, they always count); then p'_k(x_k), q'_k(x_k), the draw's mass S
+// and the drawn token's probability.  Zero between calls.
 static_assert(kRecWords == 5, "record layout");
 
 // Target wave of position (b, k): test k and the token to emit if k is the
@@ -136,11 +137,10 @@ __device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, in
     const int K = a.K, V = a.V;
     const int lane = threadIdx.x & (kWave - 1);
     const long rbase = static_cast<long>(b) * (K + 1);
-    ok = ok && u_ok(uk) && u_ok(uK);
+    const bool inputs_ok = u_ok(uk) && u_ok(uK) && (k == K || (x >= 0 && x < V));
     double r = pt, px = 0.0, qx = 0.0;
     bool accept = false;
     if (k < K) {
-        ok = ok && x >= 0 && x < V;
         px = lane_lookup(it, pt, x);
         qx = lds_lookup(sidx, sp, kd, x);
         double ratio;
@@ -164,7 +164,7 @@ __device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, in
         uint32_t lo = 1u;
         if (lane == 0) {
             hi = static_cast<uint32_t>(y);
-            lo |= (accept ? 4u : 0u) | (ok ? 0u : 2u);
+            lo |= (accept ? 4u : 0u) | (ok ? 0u : 2u) | (inputs_ok ? 0u : 8u);
         } else if (lane == 1) {
             hi = __float_as_uint(static_cast<float>(px));
         } else if (lane == 2) {
@@ -210,13 +210,16 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
     const int y = static_cast<int>(w[0] >> 32);
     const bool acc = (w[0] & 4ull) != 0ull;
     const bool bad = (w[0] & 2ull) != 0ull;
+    const bool inputs_bad = (w[0] & 8ull) != 0ull;
     const float pk = __uint_as_float(static_cast<uint32_t>(w[1] >> 32));
     const float qk = __uint_as_float(static_cast<uint32_t>(w[2] >> 32));
     const float S = __uint_as_float(static_cast<uint32_t>(w[3] >> 32));
     const float py = __uint_as_float(static_cast<uint32_t>(w[4] >> 32));
-    const bool err = timeout || __ballot(have && bad) != 0ull;
-    const unsigned long long rm = __ballot(lane < K && !acc);
-    const int j = rm ? __ffsll(static_cast<long long>(rm)) - 1 : K;
+    // The walk stops at the first position whose rows are unusable (an error) or
+    // whose draft token is rejected; invalid tokens or uniforms count anywhere.
+    const unsigned long long stop = __ballot(have && (bad || (lane < K && !acc)));
+    const int j = stop ? __ffsll(static_cast<long long>(stop)) - 1 : K;
+    const bool err = timeout || __ballot(have && inputs_bad) != 0ull || (stop && bcast(static_cast<int>(bad), j));
     const int yj = bcast(y, j);
     const float Sj = bcast(S, j), pyj = bcast(py, j);
     if (have) {
@@ -226,8 +229,8 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
     }
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
     if (diag && lane < K) {
-        diag[lane] = err ? NAN : pk;
-        diag[K + lane] = err ? NAN : qk;
+        diag[lane] = (err || lane > j) ? NAN : pk;
+        diag[K + lane] = (err || lane > j) ? NAN : qk;
     }
     if (lane == 0) {
         a.out_accept_len[b] = err ? -1 : j;

@@ -277,26 +277,28 @@ __device__ __forceinline__ void load8_raw(const char* zrow, const float* qrow, b
 }
 
 // Ratio tests of one batch row from the row statistics, lanes k = 0..K of a
-// wave: sets j (first rejection, K if none) and err (E1, E2, E3 at x_k, E5);
-// writes p'_k(x_k) and q'_k(x_k) to diag when given.
+// wave, as the left-to-right walk sees them: j = the first position whose rows
+// are unusable (E1, E3 at x_k, E4: an error) or whose draft token is rejected,
+// K if none; invalid tokens or uniforms (E2, E5) are errors wherever they are.
+// Writes p'_k(x_k) and q'_k(x_k) for k <= j to diag when given (NaN past j).
 template <bool TR>
 __device__ __forceinline__ void first_reject(const ChainArgs& a, int b, float* diag, int& j_out, bool& err_out) {
     const int K = a.K, V = a.V;
     const int k = threadIdx.x & (kWave - 1);
     const long rbase = static_cast<long>(b) * (K + 1);
-    bool bad = false, rej = false;
+    bool rows_bad = false, inputs_bad = false, rej = false;
     double pk = NAN, qk = NAN;
     if (k <= K) {
-        bad |= (a.st.flags[rbase + k] != 0u);
-        bad |= !u_ok(a.u[rbase + k]);
+        rows_bad |= (a.st.flags[rbase + k] != 0u);
+        inputs_bad |= !u_ok(a.u[rbase + k]);
     }
     if (k < K) {
         const int x = a.x[static_cast<long>(b) * K + k];
-        bad |= (x < 0 || x >= V);
+        inputs_bad |= (x < 0 || x >= V);
         if (x >= 0 && x < V) {
             const float qx = a.q[(static_cast<long>(b) * K + k) * V + x];
-            bad |= !q_ok(qx);
-            if (TR) bad |= (a.qflags[static_cast<long>(b) * K + k] != 0u);
+            rows_bad |= !q_ok(qx);
+            if (TR) rows_bad |= (a.qflags[static_cast<long>(b) * K + k] != 0u);
             const double zx = static_cast<double>(a.st.zx[rbase + k]);
             pk = exp((zx - static_cast<double>(a.st.m[rbase + k])) * a.invT) / a.st.Z[rbase + k];
             qk = static_cast<double>(qx);
@@ -308,14 +310,15 @@ __device__ __forceinline__ void first_reject(const ChainArgs& a, int b, float* d
             rej = !(static_cast<double>(a.u[rbase + k]) < thr);
         }
     }
-    const unsigned long long bm = __ballot(bad);
-    const unsigned long long rm = __ballot(rej && k < K);
+    const unsigned long long stop = __ballot(k <= K && (rows_bad || (k < K && rej)));
+    const int j = stop ? __ffsll(static_cast<long long>(stop)) - 1 : K;
+    const bool err = __ballot(inputs_bad) != 0ull || (stop && bcast(static_cast<int>(rows_bad), j) != 0);
     if (diag && k < K) {
-        diag[k] = bm ? NAN : static_cast<float>(pk);
-        diag[K + k] = bm ? NAN : static_cast<float>(qk);
+        diag[k] = (err || k > j) ? NAN : static_cast<float>(pk);
+        diag[K + k] = (err || k > j) ? NAN : static_cast<float>(qk);
     }
-    j_out = rm ? __ffsll(static_cast<long long>(rm)) - 1 : K;
-    err_out = bm != 0ull;
+    j_out = j;
+    err_out = err;
 }
 
 __device__ __forceinline__ double block_sum(double v, double* red) {

@@ -21,7 +21,8 @@ namespace sv {
 
 namespace {
 
-// Greedy chain: argmax comparisons only.
+// Greedy chain: argmax comparisons only, walking positions left to right.  A
+// row's flags count only if the walk reaches it; every token is range-checked.
 __global__ void chain_greedy_kernel(ChainArgs a) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= a.B) return;
@@ -29,10 +30,17 @@ __global__ void chain_greedy_kernel(ChainArgs a) {
     const long rbase = static_cast<long>(b) * (K + 1);
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
     bool bad = false;
-    for (int k = 0; k <= K; ++k) bad |= a.st.flags[rbase + k] != 0u;
     for (int k = 0; k < K; ++k) {
         const int x = a.x[static_cast<long>(b) * K + k];
         bad |= (x < 0 || x >= V);
+    }
+    int j = K;
+    if (!bad) {
+        for (int k = 0; k <= K; ++k) {
+            if (a.st.flags[rbase + k] != 0u) { bad = true; break; }
+            if (k == K) break;
+            if (a.x[static_cast<long>(b) * K + k] != a.st.arg[rbase + k]) { j = k; break; }
+        }
     }
     if (bad) {
         for (int t = 0; t <= K; ++t) a.out_tokens[rbase + t] = -1;
@@ -40,11 +48,11 @@ __global__ void chain_greedy_kernel(ChainArgs a) {
         if (diag) for (int t = 0; t < 2 * K + 2; ++t) diag[t] = NAN;
         return;
     }
-    int j = K;
-    for (int k = 0; k < K; ++k) {
-        const bool match = a.x[static_cast<long>(b) * K + k] == a.st.arg[rbase + k];
-        if (diag) { diag[k] = match ? 1.f : 0.f; diag[K + k] = NAN; }
-        if (!match && j == K) j = k;
+    if (diag) {
+        for (int k = 0; k < K; ++k) {
+            diag[k] = k < j ? 1.f : (k == j ? 0.f : NAN);
+            diag[K + k] = NAN;
+        }
     }
     for (int t = 0; t <= K; ++t)
         a.out_tokens[rbase + t] = t < j ? a.x[static_cast<long>(b) * K + t] : (t == j ? a.st.arg[rbase + j] : -1);

@@ -114,24 +114,47 @@ def test_ties_at_topk_boundary_and_argmax(R, orc):
 
 
 def test_error_rows(R, orc):
-    ci = W.make_chain(10, 3, 1024, dtype=W.DTYPE_BF16, temperature=1.0, top_k=0, sigma=W.sigma_const(0.5),
+    """E1-E5 as the left-to-right walk consults rows: errors in row 0 always count; an
+    error in a later row counts only when the walk reaches it (position 0 forced to
+    accept or to reject by construction)."""
+    ci = W.make_chain(12, 3, 1024, dtype=W.DTYPE_BF16, temperature=1.0, top_k=0, sigma=W.sigma_const(0.5),
                       config_id=92, seed=0)
     z = ci.logits.copy()
     q = ci.draft_probs.copy()
     x = ci.draft_tokens.copy()
     u = ci.uniforms.copy()
-    z[1, 3, 17] = 0x7FC0             # NaN in row K (always read)
+    zf = W.bf16_bits_to_f32(z)
+    V = z.shape[2]
+
+    def force(b, accept):
+        if accept:                       # x_0 = argmax, uniform draft: p'(x_0) >= q'(x_0)
+            x[b, 0] = int(np.argmax(zf[b, 0]))
+            q[b, 0] = 1.0 / V
+        else:                            # x_0 = argmin, draft mass 0.9 on it, u_0 = 0.5
+            x[b, 0] = int(np.argmin(zf[b, 0]))
+            q[b, 0] = 0.1 / (V - 1)
+            q[b, 0, x[b, 0]] = 0.9
+            u[b, 0] = 0.5
+
+    z[1, 0, 17] = 0x7FC0             # NaN in row 0
     z[2, 0, 5] = 0x7F80              # +inf
-    z[3, 2, :] = 0xFF80              # a row of -inf
-    x[4, 1] = 1024                   # token out of range
-    u[5, 3] = 1.0                    # uniform out of range
-    q[6, 0, x[6, 0]] = np.nan        # gathered draft probability NaN
+    z[3, 0, :] = 0xFF80              # a row of -inf
+    x[4, 1] = 1024                   # token out of range (checked everywhere)
+    u[5, 3] = 1.0                    # uniform out of range (checked everywhere)
+    force(6, accept=True)
+    z[6, 1, 9] = 0x7FC0              # NaN in row 1, reached after accepting x_0
+    force(7, accept=False)
+    z[7, 1, 9] = 0x7FC0              # rows past the first rejection are not consulted
+    z[7, 3, 2] = 0x7FC0
+    force(8, accept=False)
+    q[8, 2, x[8, 2]] = np.nan        # draft entry at an untested position
     ci = dataclasses.replace(ci, logits=z, draft_probs=q, draft_tokens=x, uniforms=u)
     for T, k in [(1.0, 0), (0.6, 0), (0.7, 8), (0.0, 0)]:
         t, tok, alen = check(R, orc, W.with_transform(ci, temperature=T, top_k=k), f"errors T={T} k={k}")
-        assert alen[1] == -1
+        assert alen[1] == -1 and alen[4] == -1
         if T != 0.0:
-            assert np.all(alen[[1, 2, 3, 4, 5]] == -1)
+            assert np.all(alen[[1, 2, 3, 4, 5, 6]] == -1)
+            assert alen[7] == 0 and alen[8] == 0
 
 
 def test_zero_residual_falls_back_to_target(R, orc):

@@ -404,25 +404,61 @@ def test_tree_greedy_brute_force(orc):
 # ---------------------------------------------------------------- error rules
 
 def test_error_rules(orc):
+    """E1-E5 on the rows the walk consults ([LEV] section 三: position k is examined only
+    after x_0..x_{k-1} were accepted).  Position 0 is forced to accept or to reject by
+    construction, independently of the oracle: accept when x_0 is the target's argmax and
+    the draft is uniform (p'(x_0) >= q'(x_0)); reject when x_0 is the target's argmin (no
+    target mass under top-k) and the draft puts 0.9 on it, with u_0 = 0.5."""
     rng = np.random.default_rng(81)
-    B, K, V = 8, 3, 50
+    B, K, V = 12, 3, 50
     z = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
     q = scipy.special.softmax(rng.standard_normal((B, K, V)), axis=2).astype(np.float32)
     x = rng.integers(0, V, (B, K)).astype(np.int32)
     u = rng.random((B, K + 1), dtype=np.float32)
-    z[1, 3, 7] = np.nan                 # E1 (row K is read too)
+
+    def force(b, accept):
+        if accept:
+            x[b, 0] = int(np.argmax(z[b, 0]))
+            q[b, 0] = 1.0 / V
+        else:
+            x[b, 0] = int(np.argmin(z[b, 0]))
+            q[b, 0] = 0.1 / (V - 1)
+            q[b, 0, x[b, 0]] = 0.9
+            u[b, 0] = 0.5
+
+    z[1, 0, 7] = np.nan                 # E1 in row 0 (always consulted)
     z[2, 0, 0] = np.inf                 # E1 +inf
-    z[3, 1, :] = -np.inf                # E1 all -inf
-    x[4, 2] = V                         # E2
-    u[5, 0] = 1.0                       # E5
-    for T, top_k in [(1.0, 0), (0.7, 10)]:
+    z[3, 0, :] = -np.inf                # E1 all -inf
+    x[4, 2] = V                         # E2 (every token is checked)
+    u[5, 2] = 1.0                       # E5 (every uniform is checked)
+    force(6, accept=True)
+    z[6, 1, 3] = np.nan                 # E1 in row 1, consulted after accepting x_0
+    force(7, accept=False)
+    z[7, 1, 3] = np.nan                 # not consulted: rejection at 0
+    z[7, K, 0] = np.nan
+    force(8, accept=False)
+    q[8, 2, x[8, 2]] = np.nan           # E3 at an untested position: not read
+    for T, top_k in [(1.0, 0), (0.7, 10), (1.3, 0)]:
         o = orc.verify_chain(z, orc.F32, q, x, u, T, top_k)
-        assert list(o["accept_len"][1:6]) == [-1] * 5
-        assert np.all(o["tokens"][1:6] == -1)
-        assert np.all(o["accept_len"][[0, 6, 7]] >= 0)
+        assert list(o["accept_len"][1:7]) == [-1] * 6, (T, top_k)
+        assert np.all(o["tokens"][1:7] == -1)
+        assert np.all(np.isnan(o["pk"][1:7]))
+        assert o["accept_len"][7] == 0 and o["accept_len"][8] == 0
+        assert np.isnan(o["pk"][7, 1:]).all() and not np.isnan(o["pk"][7, 0])   # nothing past j
+        assert np.all(o["accept_len"][[0, 9, 10, 11]] >= 0)
     q2 = q.copy()
-    q2[6, 1, 3] = -0.5                  # E3 in the transformed mode (whole rows are read)
+    force(9, accept=True)
+    q2[9] = q[9]
+    q2[9, 1, 3] = -0.5                  # E3 in a transformed draft row that is consulted
     o = orc.verify_chain(z, orc.F32, q2, x, u, 0.7, 10)
-    assert o["accept_len"][6] == -1
+    assert o["accept_len"][9] == -1
     og = orc.verify_chain(z, orc.F32, q, x, u, 0.0, 0)
     assert og["accept_len"][1] == -1 and og["accept_len"][2] >= 0   # greedy: NaN only
+    # greedy walk: x_0 != argmax row 0 stops before the NaN of row 1
+    x_g = x.copy()
+    x_g[7, 0] = (int(np.argmax(z[7, 0])) + 1) % V
+    og = orc.verify_chain(z, orc.F32, q, x_g, u, 0.0, 0)
+    assert og["accept_len"][7] == 0 and og["tokens"][7, 0] == int(np.argmax(z[7, 0]))
+    x_g[6, 0] = int(np.argmax(z[6, 0]))
+    og = orc.verify_chain(z, orc.F32, q, x_g, u, 0.0, 0)
+    assert og["accept_len"][6] == -1    # consulted row 1 holds NaN
