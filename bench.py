@@ -37,7 +37,7 @@ WORKLOADS = {
     2: dict(name="chain verify B=64 K=7 V=128256, bf16 target logits, fp32 draft probs, T=0.7, top_k=50",
             kernel="topk_chunk_kernel", copies=4, oracle_rows=64),
     4: dict(name="chain verify B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
-            kernel="rowstats_kernel", copies=1, oracle_rows=32),
+            kernel="dense_walk_kernel", copies=1, oracle_rows=32),
 }
 
 
@@ -71,15 +71,19 @@ def counter_traffic(workload: int):
     return float(m_b.group(1))
 
 
-def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int) -> float:
+def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_len=None) -> float:
     """Bytes the dominant kernel must move per launch (see the design notes)."""
     if workload == 2:
         # every target row (bf16) and every draft row (fp32) once; per chunk a sorted list
         # of top_k (value, index) pairs plus count and flags written
         chunks = B * (K + 1) * 4 + B * K * 8
         return B * (K + 1) * V * 2 + B * K * V * 4 + chunks * (top_k * 8 + 8)
-    # row statistics: every target row once, 24 bytes of statistics per row written
-    return B * (K + 1) * V * 2 + B * (K + 1) * 24
+    # the walk: target rows 0..j of each batch row once, the draft row j when j < K, the
+    # gathered q[x_k], tokens and uniforms read, the outputs written
+    j = [K] * B if accept_len is None else [int(a) for a in accept_len]
+    rows = sum(a + 1 for a in j if a >= 0)
+    drafts = sum(1 for a in j if 0 <= a < K)
+    return rows * V * 2 + drafts * V * 4 + B * (K * 12 + (K + 1) * 4 + (K + 2) * 4)
 
 
 def copy_probe(R, torch, args) -> int:
@@ -202,10 +206,10 @@ def main() -> int:
     torch.cuda.synchronize()
     k_ms = sum(a.elapsed_time(b) for a, b in zip(kstart, kstop)) / args.steps
     value = B * (K + 1) / (ms_step * 1e-3)
-    alg = algorithmic_bytes(args.workload, B, K, V, top_k)
-    achieved = alg / (k_ms * 1e-3) / 1e9
-    step_alg_gbs = (alg if args.workload == 2 else alg) / (ms_step * 1e-3) / 1e9
     al = alen.cpu().numpy()
+    alg = algorithmic_bytes(args.workload, B, K, V, top_k, al)
+    achieved = alg / (k_ms * 1e-3) / 1e9
+    step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak); accept_len histogram {np.bincount(al, minlength=K + 1).tolist()}")
     traffic = counter_traffic(args.workload)

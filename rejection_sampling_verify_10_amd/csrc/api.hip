@@ -310,18 +310,18 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
         fa.sel = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K + 1, p.tk);
         fa.ch = ca;
         SV_TRY(launch_chain_topk(fa, s, prof.timing()));
+    } else if (!ca.transformed) {
+        SV_TRY(launch_chain_walk(ca, dense_bracket(false), s, prof.timing()));
     } else {
         ca.st = p.st;
         RowStatsArgs ra =
             rowstats_args(target_logits, dtype, V, K + 1, K + 1, B, false, temperature, draft_tokens, K, p.st);
         SV_TRY(launch_rowstats(ra, s, prof.timing()));
-        if (ca.transformed) {
-            PowerSumArgs pa{draft_probs, V, B * K, static_cast<float>(1.0 / temperature), p.qsum, p.qflags};
-            SV_TRY(launch_power_sums(pa, s));
-            ca.qsum = p.qsum;
-            ca.qflags = p.qflags;
-        }
-        SV_TRY(launch_chain_dense(ca, dense_bracket(ca.transformed != 0), s));
+        PowerSumArgs pa{draft_probs, V, B * K, static_cast<float>(1.0 / temperature), p.qsum, p.qflags};
+        SV_TRY(launch_power_sums(pa, s));
+        ca.qsum = p.qsum;
+        ca.qflags = p.qflags;
+        SV_TRY(launch_chain_dense(ca, dense_bracket(true), s));
     }
     return SPEC_OK;
 }

@@ -17,7 +17,7 @@
 // Zp = sum_i e_i (e_i = exp((z_i - m)/T)) before any weight is known: the row
 // statistics give Zp' (fp32 terms, within ~1e-6).  With iz = 1/Zp' and
 // d_i = e_i*iz - w_i (w_i = q'_i, the draft weight), the pass sums per chunk
-// of 4096 elements
+// of 8 elements per thread
 //     E = sum e_i,   R = sum max(0, d_i),   P = sum_{d_i > 0} w_i,
 // and lists the elements with |d_i| within a relative delta of zero
 // ("undecided").  For every other element the sign of e_i/Zp - w_i equals
@@ -30,11 +30,18 @@
 // so the result never depends on the accuracy of Zp'.  A transformed draft
 // (T != 1) brackets its normaliser Zq the same way.
 //
-// dense_row_kernel: one workgroup of 512 threads per batch entry.  Wave 0 runs
-// the K ratio tests on the row statistics (lanes k = 0..K); the workgroup then
-// streams row j chunk by chunk, loading chunk c+1 while it computes chunk c,
-// keeps the chunk sums in LDS, and finishes with the draw: the chunk holding
-// u*S, rescanned element by element.
+// One workgroup per batch entry.  dense_walk_kernel (T == 1) walks the
+// positions, computing each target row's statistics just before its test;
+// dense_row_kernel (transformed drafts) takes all rows' statistics from
+// rowstats_kernel and runs the K ratio tests in one wave (lanes k = 0..K).  The
+// workgroup then streams row j chunk by chunk, loading the next chunks while it
+// computes chunk c, keeps the chunk sums in LDS, and finishes with the draw:
+// the chunk holding u*S, rescanned element by element.
+
+//
+// This file is compiled twice (dense_walk.hip, dense_tr.hip), each translation
+// unit holding one of the two kernels; SV_DENSE_THREADS sets the block size (a
+// 1024-thread walk, a whole CU per batch row, measured slower than 512).
 
 #include <math.h>
 
@@ -44,11 +51,16 @@
 #include "internal.hpp"
 #include "lists.hpp"
 
+#ifndef SV_DENSE_THREADS
+#error "define SV_DENSE_THREADS before including dense_impl.hpp"
+#endif
+
 namespace sv {
 
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = SV_DENSE_THREADS;
+constexpr int kDenseChunk = 8 * kThreads;           // elements per chunk: 8 per thread
 constexpr int kWaves = kThreads / kWave;
 constexpr int kEPT = kDenseChunk / kThreads;        // 8 elements per thread per chunk
 constexpr int kSub = kEPT / 8;                      // 8-element groups per thread
@@ -57,7 +69,10 @@ constexpr int kListCap = 64;                        // undecided elements per ro
 // Register buffers of the streaming pass: three (two chunks in flight) where the
 // registers allow four waves per SIMD, else two.
 template <bool VEC, bool TR> constexpr int ring_depth() { return (VEC && !TR) ? 3 : 2; }
-template <bool VEC, bool TR> constexpr int min_waves() { return (VEC && !TR) ? 4 : 2; }
+// Waves per SIMD the registers must allow: a 1024-thread workgroup is four per SIMD.
+template <bool VEC, bool TR> constexpr int min_waves() {
+    return kThreads >= 1024 ? kThreads / kWave / 4 : ((VEC && !TR) ? 4 : 2);
+}
 
 // exp(x) for x <= 0 in fp64 by Tang's table-driven method (ACM TOMS 15(2),
 // 1989), with 256 table entries.  The caller passes y = x * 256/ln2 (folded
@@ -380,6 +395,10 @@ inline size_t dense_dyn_lds(int C, bool tab) {
 constexpr int kTabMaxChunks = 48;
 
 struct RowSmem {
+    float wq[kWave];                   // walk: q[x_k], lane k
+    float wz[kWave];                   //       z[x_k]
+    float wu[kWave];                   //       u_k
+    float wmax[kWaves];                //       per-wave row maxima
     double tbl[kTableSize];
     double part[kMaxChunks];           // chunk weights of the draw
     int32_t li[kListCap];              // undecided elements
@@ -391,12 +410,13 @@ struct RowSmem {
     double before;
 };
 
+// The final draw of batch row b (one workgroup): sm.j / sm.err set, sm.tbl
+// built, sm.n_list = sm.qbad = 0, all visible after a barrier; (m_j, Zp_ap):
+// the maximum and approximate normaliser of target row j.
 template <int DT, bool VEC, bool TR, bool TAB>
-__global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_kernel(ChainArgs a, double bracket, ExpConsts ek) {
+__device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bracket, const ExpConsts& ek,
+                                           RowSmem& sm, double* dyn_lds, float m_j, double Zp_row) {
     static_assert(!TAB || DT == 1, "the exponential table is for bf16 logits");
-    __shared__ RowSmem sm;
-    extern __shared__ double dyn_lds[];
-    const int b = blockIdx.x;
     const int K = a.K, V = a.V;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
     const int C = (V + kDenseChunk - 1) / kDenseChunk;
@@ -407,15 +427,6 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_ke
     float* pp = reinterpret_cast<float*>(pr + static_cast<long>(C) * nslots);        // [C][nslots]: P
     const long rbase = static_cast<long>(b) * (K + 1);
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
-
-    if (tid < kWave) {
-        int j;
-        bool err;
-        first_reject<TR>(a, b, diag, j, err);
-        if (tid == 0) { sm.j = j; sm.err = err; sm.n_list = 0; sm.qbad = 0; }
-    }
-    for (int t = tid; t < kTableSize; t += kThreads) sm.tbl[t] = exp2(static_cast<double>(t) * (1.0 / kTableSize));
-    __syncthreads();
     const int j = sm.j;
     auto fail_row = [&]() {
         for (int t = tid; t <= K; t += kThreads) a.out_tokens[rbase + t] = -1;
@@ -431,8 +442,8 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_ke
     const char* zr = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
     const float* qr = a.q + qrow * V;
     const double* tbl = sm.tbl;
-    const ExpArg g = exp_arg(static_cast<double>(a.st.m[zrow]), a.invT, ek);
-    const double Zp_ap = a.st.Z[zrow];
+    const ExpArg g = exp_arg(static_cast<double>(m_j), a.invT, ek);
+    const double Zp_ap = Zp_row;
     const double Zq_ap = (TR && res) ? a.qsum[qrow] : 1.0;
     const double iz = 1.0 / Zp_ap, iq = TR ? 1.0 / Zq_ap : 1.0;
     // |d| > tol*(e*iz + w') (w' = w*iq, tol >= delta/(1 - delta) plus rounding room)
@@ -776,6 +787,255 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_ke
     }
 }
 
+__device__ __forceinline__ void init_draw_smem(RowSmem& sm) {
+    for (int t = threadIdx.x; t < kTableSize; t += kThreads) sm.tbl[t] = exp2(static_cast<double>(t) * (1.0 / kTableSize));
+    if (threadIdx.x == 0) { sm.n_list = 0; sm.qbad = 0; }
+}
+
+// All rows' statistics precomputed (rowstats_kernel): ratio tests in one wave,
+// then the final draw.
+template <int DT, bool VEC, bool TR, bool TAB>
+__global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_kernel(ChainArgs a, double bracket,
+                                                                                     ExpConsts ek) {
+    __shared__ RowSmem sm;
+    extern __shared__ double dyn_lds[];
+    const int b = blockIdx.x;
+    if (threadIdx.x < kWave) {
+        int j;
+        bool err;
+        first_reject<TR>(a, b, a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * a.K + 2) : nullptr, j, err);
+        if (threadIdx.x == 0) { sm.j = j; sm.err = err; }
+    }
+    init_draw_smem(sm);
+    __syncthreads();
+    const long zrow = static_cast<long>(b) * (a.K + 1) + sm.j;
+    final_draw<DT, VEC, TR, TAB>(a, b, bracket, ek, sm, dyn_lds, a.st.m[zrow], a.st.Z[zrow]);
+}
+
+// ---- the walk: statistics of target rows 0, 1, ... until the first rejection ----
+
+constexpr int kWalkUnroll = 4;   // vectors per thread per tile
+constexpr int kWalkTile = kThreads * kWalkUnroll;
+
+// Workgroup barrier for LDS traffic only: it waits for the wave's LDS operations
+// but not for its global loads, so a prefetch stays in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Per-thread part of a row's statistics: fp32 exponentials against a running
+// maximum (the numerics of rowstats_kernel).
+template <int DT>
+struct RowAcc {
+    float m = -INFINITY;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    __device__ __forceinline__ void add(const u32x4 (&v)[kWalkUnroll], float scale) {
+        using E = Elem<DT>;
+        float tmax = m;
+#pragma unroll
+        for (int u = 0; u < kWalkUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < E::kPerVec; ++e) tmax = fmaxf(tmax, E::get(v[u], e));
+        if (tmax > m) {
+            const float f = __builtin_amdgcn_exp2f((m - tmax) * scale);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= f;
+            m = tmax;
+        }
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < kWalkUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < E::kPerVec; ++e) acc[u & 3] += __builtin_amdgcn_exp2f((E::get(v[u], e) - m) * scale);
+        } else {
+            // everything so far is -inf (or padding): only a NaN matters
+#pragma unroll
+            for (int u = 0; u < kWalkUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < E::kPerVec; ++e)
+                    if (E::get(v[u], e) != E::get(v[u], e)) acc[0] = NAN;
+        }
+    }
+};
+
+// Row maximum M and Z' from the per-thread parts (every thread returns them):
+// partials rescaled to M and summed in fp64.  LDS barriers only.
+template <int DT>
+__device__ __forceinline__ void row_reduce(const RowAcc<DT>& ra, double invT, RowSmem& sm, float& M, double& Z) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const float s = (ra.acc[0] + ra.acc[1]) + (ra.acc[2] + ra.acc[3]);
+    const float wm = wave_max(ra.m);
+    if (lane == 0) sm.wmax[wid] = wm;
+    lds_barrier();
+    M = sm.wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.wmax[w]);
+    double c = static_cast<double>(s) * exp((static_cast<double>(ra.m) - static_cast<double>(M)) * invT);
+    c = wave_sum(c);
+    if (lane == 0) sm.red[wid] = c;
+    lds_barrier();
+    Z = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) Z += sm.red[w];
+    lds_barrier();                 // the slots are reused by the next row
+}
+
+// Chain verification with the draft used as given (T == 1, no top-k): one
+// workgroup per batch row walks the positions left to right ("064 · 投机解码",
+// section 三), reading target row k only once x_0..x_{k-1} are accepted: its
+// statistics, then test k from the gathered z[x_k] and q[x_k].  At the first
+// rejection (or at row K) it draws the emitted token as dense_row_kernel does.
+// The rows are one stream of tiles: the tile after the last of row k (the first
+// of row k+1) is in flight while row k is reduced and tested, and is dropped if
+// the walk stops.
+template <int DT, bool VEC, bool TAB>
+__global__ __launch_bounds__(kThreads, (min_waves<VEC, false>())) void dense_walk_kernel(ChainArgs a, double bracket,
+                                                                                         ExpConsts ek) {
+    using E = Elem<DT>;
+    __shared__ RowSmem sm;
+    extern __shared__ double dyn_lds[];
+    const int b = blockIdx.x;
+    const int K = a.K, V = a.V;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const long rbase = static_cast<long>(b) * (K + 1);
+    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
+    const char* zbase = static_cast<const char*>(a.logits) + rbase * V * E::kBytes;
+    // Tokens and uniforms are checked up front (E2, E5 count anywhere); lane k
+    // gathers q[x_k] and z[x_k].
+    if (tid < kWave) {
+        bool bad = false;
+        float qx = NAN, uk = 0.f, zx = 0.f;
+        if (lane <= K) {
+            uk = a.u[rbase + lane];
+            bad |= !u_ok(uk);
+        }
+        if (lane < K) {
+            const int x = a.x[static_cast<long>(b) * K + lane];
+            bad |= (x < 0 || x >= V);
+            if (x >= 0 && x < V) {
+                qx = a.q[(static_cast<long>(b) * K + lane) * V + x];
+                zx = E::scalar(zbase + static_cast<long>(lane) * V * E::kBytes, x);
+            }
+        }
+        sm.wq[lane] = qx;
+        sm.wz[lane] = zx;
+        sm.wu[lane] = uk;
+        bad = __ballot(bad) != 0ull;
+        if (lane == 0) sm.err = bad;
+    }
+    init_draw_smem(sm);
+    __syncthreads();
+    const float scale = static_cast<float>(1.4426950408889634 * a.invT);
+    bool err = sm.err != 0;
+    int j = K;
+    float mj = 0.f;
+    double Zj = 1.0;
+    // Test k from M, Z of row k: returns true when the walk stops there.
+    auto test = [&](int k, float M, double Z) -> bool {
+        mj = M;
+        Zj = Z;
+        if (!(Z >= 1.0 && Z < INFINITY)) { err = true; return true; }                  // E1
+        if (k == K) return true;
+        const float qx = sm.wq[k];
+        if (!q_ok(qx)) { err = true; return true; }                                     // E3
+        const double pk = exp((static_cast<double>(sm.wz[k]) - static_cast<double>(M)) * a.invT) / Z;
+        const double qk = static_cast<double>(qx);
+        double ratio;
+        if (qk > 0.0) ratio = pk / qk;
+        else ratio = pk > 0.0 ? INFINITY : 0.0;
+        const double thr = ratio < 1.0 ? ratio : 1.0;
+        if (diag && tid == 0) {
+            diag[k] = static_cast<float>(pk);
+            diag[K + k] = static_cast<float>(qk);
+        }
+        if (!(static_cast<double>(sm.wu[k]) < thr)) { j = k; return true; }
+        return false;
+    };
+    if (!err) {
+        if constexpr (VEC) {
+            const int nvec = V / E::kPerVec;
+            const int T_row = (nvec + kWalkTile - 1) / kWalkTile;     // tiles per row, the last maybe partial
+            const bool partial = nvec % kWalkTile != 0;
+            constexpr uint32_t ninf = DT == 1 ? 0xff80ff80u : 0xff800000u;
+            // tile t of row k; indices past the row are clamped to a valid vector
+            auto load = [&](int k, int t, u32x4 (&v)[kWalkUnroll]) {
+                const u32x4* rv = reinterpret_cast<const u32x4*>(zbase + static_cast<long>(k) * V * E::kBytes);
+#pragma unroll
+                for (int u = 0; u < kWalkUnroll; ++u) {
+                    const int i = t * kWalkTile + u * kThreads + tid;
+                    v[u] = load_stream(rv + (i < nvec ? i : nvec - 1));
+                }
+            };
+            int k = 0, t = 0;
+            RowAcc<DT> ra;
+            // One tile: prefetch the next one (the next row's first after the last),
+            // add this one, and at a row's end reduce and test.  Returns true to stop.
+            auto step = [&](u32x4 (&cur)[kWalkUnroll], u32x4 (&nxt)[kWalkUnroll]) -> bool {
+                const bool last = t == T_row - 1;
+                load(last ? min(k + 1, K) : k, last ? 0 : t + 1, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+                if (last && partial) {
+#pragma unroll
+                    for (int u = 0; u < kWalkUnroll; ++u)
+                        if (t * kWalkTile + u * kThreads + tid >= nvec) cur[u] = u32x4{ninf, ninf, ninf, ninf};
+                }
+                ra.add(cur, scale);
+                if (!last) {
+                    ++t;
+                    return false;
+                }
+                float M;
+                double Z;
+                row_reduce<DT>(ra, a.invT, sm, M, Z);
+                if (test(k, M, Z)) return true;
+                ++k;
+                t = 0;
+                ra = RowAcc<DT>();
+                return false;
+            };
+            u32x4 va[kWalkUnroll], vb[kWalkUnroll];
+            load(0, 0, va);
+#pragma unroll 1
+            for (;;) {
+                if (step(va, vb)) break;
+                if (step(vb, va)) break;
+            }
+        } else {
+#pragma unroll 1
+            for (int k = 0; k <= K; ++k) {
+                const char* row = zbase + static_cast<long>(k) * V * E::kBytes;
+                RowAcc<DT> ra;
+                for (int base = 0; base < V; base += kThreads * kWalkUnroll * E::kPerVec) {
+                    u32x4 v[kWalkUnroll];
+#pragma unroll
+                    for (int u = 0; u < kWalkUnroll; ++u) {
+                        const long i0 = base + static_cast<long>(u * kThreads + tid) * E::kPerVec;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            if (DT == 1) {
+                                const uint32_t lo = i0 + 2 * w < V ? static_cast<const uint16_t*>(static_cast<const void*>(row))[i0 + 2 * w] : 0xff80u;
+                                const uint32_t hi = i0 + 2 * w + 1 < V ? static_cast<const uint16_t*>(static_cast<const void*>(row))[i0 + 2 * w + 1] : 0xff80u;
+                                v[u][w] = lo | (hi << 16);
+                            } else {
+                                v[u][w] = i0 + w < V ? reinterpret_cast<const uint32_t*>(row)[i0 + w] : 0xff800000u;
+                            }
+                        }
+                    }
+                    ra.add(v, scale);
+                }
+                float M;
+                double Z;
+                row_reduce<DT>(ra, a.invT, sm, M, Z);
+                if (test(k, M, Z)) break;
+            }
+        }
+    }
+    if (diag && !err)
+        for (int t = j + 1 + tid; t < K; t += kThreads) { diag[t] = NAN; diag[K + t] = NAN; }
+    if (tid == 0) { sm.j = j; sm.err = err; }
+    __syncthreads();
+    final_draw<DT, VEC, false, TAB>(a, b, bracket, ek, sm, dyn_lds, mj, Zj);
+}
+
+#if SV_DENSE_TR
 template <int DT, bool VEC, bool TR>
 hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s) {
     const int C = (a.V + kDenseChunk - 1) / kDenseChunk;
@@ -790,18 +1050,44 @@ hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s) {
                        static_cast<unsigned>(dense_dyn_lds(C, false)), s, a, bracket, exp_consts());
     return hipGetLastError();
 }
+#endif
+
+#if SV_DENSE_WALK
+template <int DT, bool VEC>
+hipError_t walk_launch(const ChainArgs& a, double bracket, hipStream_t s, Timing t) {
+    const int C = (a.V + kDenseChunk - 1) / kDenseChunk;
+    if constexpr (DT == 1 && VEC) {
+        if (C <= kTabMaxChunks) {
+            launch_timed(t, dense_walk_kernel<DT, VEC, true>, dim3(a.B), dim3(kThreads),
+                         static_cast<unsigned>(dense_dyn_lds(C, true)), s, a, bracket, exp_consts());
+            return hipGetLastError();
+        }
+    }
+    launch_timed(t, dense_walk_kernel<DT, VEC, false>, dim3(a.B), dim3(kThreads),
+                 static_cast<unsigned>(dense_dyn_lds(C, false)), s, a, bracket, exp_consts());
+    return hipGetLastError();
+}
+#endif
 
 }  // namespace
 
-hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s) {
+#if SV_DENSE_WALK
+hipError_t launch_chain_walk(const ChainArgs& a, double bracket, hipStream_t s, Timing t) {
     const int esz = a.dtype ? 2 : 4;
     const bool vec = vec_ok(a.logits, a.V, esz) && vec_ok(a.q, a.V, 4);
-    if (a.dtype == 1) {
-        if (vec) return a.transformed ? dense_launch<1, true, true>(a, bracket, s) : dense_launch<1, true, false>(a, bracket, s);
-        return a.transformed ? dense_launch<1, false, true>(a, bracket, s) : dense_launch<1, false, false>(a, bracket, s);
-    }
-    if (vec) return a.transformed ? dense_launch<0, true, true>(a, bracket, s) : dense_launch<0, true, false>(a, bracket, s);
-    return a.transformed ? dense_launch<0, false, true>(a, bracket, s) : dense_launch<0, false, false>(a, bracket, s);
+    if (a.dtype == 1) return vec ? walk_launch<1, true>(a, bracket, s, t) : walk_launch<1, false>(a, bracket, s, t);
+    return vec ? walk_launch<0, true>(a, bracket, s, t) : walk_launch<0, false>(a, bracket, s, t);
 }
+#endif
+
+#if SV_DENSE_TR
+hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s) {
+    // transformed drafts only (T != 1 without top-k); T == 1 takes launch_chain_walk
+    const int esz = a.dtype ? 2 : 4;
+    const bool vec = vec_ok(a.logits, a.V, esz) && vec_ok(a.q, a.V, 4);
+    if (a.dtype == 1) return vec ? dense_launch<1, true, true>(a, bracket, s) : dense_launch<1, false, true>(a, bracket, s);
+    return vec ? dense_launch<0, true, true>(a, bracket, s) : dense_launch<0, false, true>(a, bracket, s);
+}
+#endif
 
 }  // namespace sv

@@ -11,7 +11,7 @@
 // The K tests are independent of each other, so they run in parallel lanes
 // and the first rejection is a ballot.  This file holds the greedy chain, the
 // static tree and the acceptance rate; the top-k chain finishes inside its
-// selection launch (chain_finish.hpp) and the dense final draw is in dense.hip.
+// selection launch (chain_finish.hpp) and the dense path is in dense_impl.hpp.
 
 #include "common.hpp"
 #include "internal.hpp"
