@@ -99,6 +99,18 @@ template <typename T> __device__ __forceinline__ T xrev(T v) {
     for (int j = 1; j < 64; j <<= 1) v = xshfl(v, j);
     return v;
 }
+// Value of lane `src` (any lane, per lane) through the LDS crossbar.
+__device__ __forceinline__ uint32_t lane_gather(uint32_t v, int src) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(v)));
+}
+__device__ __forceinline__ unsigned long long lane_gather(unsigned long long v, int src) {
+    const uint32_t lo = lane_gather(static_cast<uint32_t>(v), src);
+    const uint32_t hi = lane_gather(static_cast<uint32_t>(v >> 32), src);
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ double lane_gather(double v, int src) {
+    return __longlong_as_double(static_cast<long long>(lane_gather(static_cast<unsigned long long>(__double_as_longlong(v)), src)));
+}
 // Broadcast from a wave-uniform lane (v_readlane).
 __device__ __forceinline__ int bcast(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 __device__ __forceinline__ float bcast(float v, int lane) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane)); }
@@ -241,7 +253,7 @@ __device__ __forceinline__ void wave_sort_keys(pkey_t& k) {
 // sequence holding the 64 winners; a bitonic merge sorts it.
 __device__ __forceinline__ void wave_merge_keys(pkey_t& a, pkey_t b) {
     const int lane = threadIdx.x & (kWave - 1);
-    const pkey_t rb = xrev(b);
+    const pkey_t rb = lane_gather(b, kWave - 1 - lane);     // b reversed
     a = a > rb ? a : rb;
 #pragma unroll
     for (int j = kWave >> 1; j > 0; j >>= 1) cx_key(a, j, (lane & j) == 0);

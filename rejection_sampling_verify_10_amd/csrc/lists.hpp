@@ -62,20 +62,25 @@ __device__ __forceinline__ int merge_global_lists(const TopkLists& t, long unit0
     return wave_sum(nl);
 }
 
-// Sorts (index, probability) pairs by index ascending (empty lanes carry kNoIndex).
+// Sorts (index, probability) pairs by index ascending (empty lanes carry kNoIndex):
+// a bitonic network on 32-bit keys (index << 6 | lane, indices < 2^26), then one
+// gather of the probabilities by the lane each key came from.
 __device__ __forceinline__ void wave_sort_by_index(int& i, double& p) {
     const int lane = threadIdx.x & (kWave - 1);
+    constexpr uint32_t kEmpty = 0xffffffc0u;
+    uint32_t key = i == kNoIndex ? (kEmpty | lane) : ((static_cast<uint32_t>(i) << 6) | lane);
 #pragma unroll
     for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const int oi = xshfl(i, j);
-            const double op = xshfl(p, j);
+            const uint32_t o = xshfl(key, j);
             const bool up = (lane & k) == 0 || k == kWave;
             const bool keep_small = ((lane & j) == 0) == up;
-            if (keep_small ? (oi < i) : (oi > i)) { i = oi; p = op; }
+            if (keep_small ? (o < key) : (o > key)) key = o;
         }
     }
+    i = key >= kEmpty ? kNoIndex : static_cast<int>(key >> 6);
+    p = lane_gather(p, static_cast<int>(key & 63u));
 }
 
 // From a row's ranked top entries (lane l = l-th, kk kept) to its transformed
