@@ -1,13 +1,15 @@
 #!/usr/bin/env python3
 """Throughput of the speculative-decoding verification step on one MI355X.
 
-A step is one spec_verify_chain call over one batch of synthetic inputs that
-already sit in HBM.  The default workload is the chain verification with
-B=64, K=7, V=128256 (bf16 target logits, fp32 draft probabilities,
-temperature 0.7, top-k 50 on both distributions).  Several copies of the
-inputs are rotated so that the working set exceeds the 256 MB Infinity Cache.
+A step is one spec_verify_chain call (spec_verify_tree_greedy for --workload 3)
+over one batch of synthetic inputs that already sit in HBM.  The default
+workload is the chain verification with B=64, K=7, V=128256 (bf16 target
+logits, fp32 draft probabilities, temperature 0.7, top-k 50 on both
+distributions).  Several copies of the inputs are rotated so that the working
+set exceeds the 256 MB Infinity Cache.
 
-Prints ONE JSON line: verified token-rows/s (B*(K+1) per step) and the step
+Prints ONE JSON line: verified token-rows/s (B*(K+1) per step; B*N node rows
+for the tree) and the step
 time from K timed steps with nothing else on the stream; the dominant kernel's
 achieved HBM bandwidth against the 8 TB/s peak, timed live with HIP events that
 the library attaches to that kernel's dispatch on the call's stream during a
@@ -16,7 +18,7 @@ queue latency, so they stay out of the step timing); the
 hardware-counter traffic recorded under profiles/ when it matches the current
 kernel source; and the CPU oracle's throughput on the host cores.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2|4]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 0|1|2|3|4]
 """
 
 from __future__ import annotations
@@ -33,11 +35,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified token-rows/s and achieved HBM GB/s (% of peak), V=128256, B=64, K=7"
 
+# The default is the headline workload (2); 0, 1 and 3 are the small configurations, bound by
+# launch latency and reported without a bandwidth bar.  copies: input sets rotated so that
+# the working set exceeds the 256 MB Infinity Cache where it can.
 WORKLOADS = {
+    0: dict(name="chain verify B=1 K=4 V=1000, fp32 target logits, fp32 draft probs, T=1, no top-k",
+            kernel="dense_walk_kernel", copies=1, oracle_rows=1, dtype="f32 in, f32 exp, f64 draw"),
+    1: dict(name="chain verify B=8 K=5 V=32000, bf16 target logits, fp32 draft probs, T=1, no top-k",
+            kernel="dense_walk_kernel", copies=64, oracle_rows=8, dtype="bf16 in, f32 exp, f64 draw"),
     2: dict(name="chain verify B=64 K=7 V=128256, bf16 target logits, fp32 draft probs, T=0.7, top_k=50",
-            kernel="topk_chunk_kernel", copies=4, oracle_rows=64),
+            kernel="topk_chunk_kernel", copies=4, oracle_rows=64,
+            dtype="bf16/f32 in, f32 select, f64 probabilities"),
+    3: dict(name="greedy static-tree verify B=32 N=27 (depth 5) V=32000, bf16 target logits",
+            kernel="rowstats_kernel", copies=10, oracle_rows=32, dtype="bf16 in, exact argmax"),
     4: dict(name="chain verify B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
-            kernel="dense_walk_kernel", copies=1, oracle_rows=32),
+            kernel="dense_walk_kernel", copies=1, oracle_rows=32, dtype="bf16 in, f32 exp, f64 draw"),
 }
 
 
@@ -71,8 +83,12 @@ def counter_traffic(workload: int):
     return float(m_b.group(1))
 
 
-def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_len=None) -> float:
-    """Bytes the dominant kernel must move per launch (see the design notes)."""
+def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_len=None, esz: int = 2) -> float:
+    """Bytes the dominant kernel must move per launch (see the design notes).  For the tree,
+    K is the node count N."""
+    if workload == 3:
+        # the row statistics: every node row once, argmax and flags written
+        return B * K * V * esz + B * K * 12
     if workload == 2:
         # every target row (bf16) and every draft row (fp32) once; per chunk a sorted list
         # of top_k (value, index) pairs plus count and flags written
@@ -83,7 +99,7 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
     j = [K] * B if accept_len is None else [int(a) for a in accept_len]
     rows = sum(a + 1 for a in j if a >= 0)
     drafts = sum(1 for a in j if 0 <= a < K)
-    return rows * V * 2 + drafts * V * 4 + B * (K * 12 + (K + 1) * 4 + (K + 2) * 4)
+    return rows * V * esz + drafts * V * 4 + B * (K * 12 + (K + 1) * 4 + (K + 2) * 4)
 
 
 def copy_probe(R, torch, args) -> int:
@@ -158,7 +174,7 @@ def main() -> int:
 
     t0 = time.time()
     ci = W.config(args.workload, seed=args.seed)
-    B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
+    tree = args.workload == 3
     log(f"workload {args.workload}: {wl['name']} (inputs drawn in {time.time() - t0:.1f} s)")
 
     def to_dev(a):
@@ -166,17 +182,38 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    base = [to_dev(ci.logits), to_dev(ci.draft_probs), to_dev(ci.draft_tokens), to_dev(ci.uniforms)]
+    esz = 2 if ci.dtype == W.DTYPE_BF16 else 4
+    if tree:
+        B, K, V, T, top_k = ci.B, ci.N, ci.V, 0.0, 0
+        depth = [0] * K
+        for n in range(1, K):
+            depth[n] = depth[int(ci.parents[n])] + 1
+        D = max(depth)
+        base = [to_dev(ci.logits), to_dev(ci.node_tokens)]
+        tok = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        ws = R.new_workspace(R.tree_workspace_bytes(B, K, V, ci.dtype), dev)
+        parents = ci.parents.tolist()
+        rows_per_step = B * K                  # node rows verified
+    else:
+        B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
+        base = [to_dev(ci.logits), to_dev(ci.draft_probs), to_dev(ci.draft_tokens), to_dev(ci.uniforms)]
+        tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        ws = R.new_workspace(R.chain_workspace_bytes(B, K, V, ci.dtype, T, top_k), dev)
+        rows_per_step = B * (K + 1)            # token rows verified
     sets = [base] + [[t.clone() for t in base] for _ in range(wl["copies"] - 1)]
-    tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    alen = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = R.new_workspace(R.chain_workspace_bytes(B, K, V, ci.dtype, T, top_k), dev)
     in_bytes = sum(t.numel() * t.element_size() for t in base)
     log(f"{wl['copies']} input copies x {in_bytes / 1e6:.1f} MB resident")
 
     def step(i: int) -> None:
-        z, q, x, u = sets[i % len(sets)]
-        R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
+        if tree:
+            z, nt = sets[i % len(sets)]
+            R.verify_tree_greedy(z, nt, parents, out=(path, tok, alen), workspace=ws)
+        else:
+            z, q, x, u = sets[i % len(sets)]
+            R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -193,8 +230,8 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_step = t_begin.elapsed_time(t_end) / args.steps
 
-    # Kernel pass: K more steps, the library recording events around the dominant
-    # kernel of each on the call's stream.
+    # Kernel pass: K more steps, the library attaching events to the dispatch of the
+    # dominant kernel of each on the call's stream.
     kstart = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     kstop = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for e in kstart + kstop:
@@ -205,13 +242,14 @@ def main() -> int:
         step(args.warmup + args.steps + i)
     torch.cuda.synchronize()
     k_ms = sum(a.elapsed_time(b) for a, b in zip(kstart, kstop)) / args.steps
-    value = B * (K + 1) / (ms_step * 1e-3)
+    value = rows_per_step / (ms_step * 1e-3)
     al = alen.cpu().numpy()
-    alg = algorithmic_bytes(args.workload, B, K, V, top_k, al)
+    alg = algorithmic_bytes(args.workload, B, K, V, top_k, al, esz)
     achieved = alg / (k_ms * 1e-3) / 1e9
     step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
-        f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak); accept_len histogram {np.bincount(al, minlength=K + 1).tolist()}")
+        f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak); accept_len histogram "
+        f"{np.bincount(al[al >= 0], minlength=(K + 1) if not tree else 1).tolist()}")
     traffic = counter_traffic(args.workload)
     probe = read_probe_gbps(R, torch, dev)
     log(f"read probe {probe:.0f} GB/s; {wl['kernel']} at {100 * achieved / probe:.1f}% of it")
@@ -221,12 +259,15 @@ def main() -> int:
         import oracle
         rows = min(wl["oracle_rows"], B)
         t0 = time.perf_counter()
-        oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
-                            ci.uniforms[:rows], T, top_k)
+        if tree:
+            oracle.verify_tree_greedy(ci.logits[:rows], ci.dtype, ci.node_tokens[:rows], ci.parents)
+        else:
+            oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
+                                ci.uniforms[:rows], T, top_k)
         dt = time.perf_counter() - t0
-        cpu = {"value": rows * (K + 1) / dt, "unit": "token-rows/s", "cores": oracle.max_threads(),
+        cpu = {"value": rows * rows_per_step / B / dt, "unit": "token-rows/s", "cores": oracle.max_threads(),
                "kind": "oracle",
-               "sample": f"first {rows} of {B} batch rows ({rows * (K + 1)} token-rows) of the same workload, "
+               "sample": f"first {rows} of {B} batch rows ({rows * rows_per_step // B} token-rows) of the same workload, "
                          f"fp64 C oracle, OpenMP over batch rows, {dt:.2f} s wall"}
         log(f"oracle: {cpu['value']:.0f} token-rows/s on {cpu['cores']} threads")
 
@@ -241,11 +282,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16/f32 in, f32 select, f64 probabilities" if args.workload == 2 else "bf16 in, f32 exp, f64 draw",
+        "dtype": wl["dtype"],
         "data": "synthetic",
-        "config": {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
-                   "input_copies": wl["copies"], "parallelism": "single GPU"},
+        "config": ({"workload": wl["name"], "B": B, "N": K, "V": V, "input_copies": wl["copies"],
+                    "parallelism": "single GPU"} if tree else
+                   {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
+                    "input_copies": wl["copies"], "parallelism": "single GPU"}),
         "step_algorithmic_GBps": step_alg_gbs,
+        "emitted_tokens_per_s": float(np.sum(al[al >= 0] + 1)) / (ms_step * 1e-3),
         "roofline": {"bound": "hbm", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg,

@@ -175,11 +175,13 @@ def verify_chain(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor
     return (tokens, alen, dg) if diag else (tokens, alen)
 
 
-def verify_tree_greedy(target_logits: torch.Tensor, node_tokens: torch.Tensor, parents: Sequence[int]):
+def verify_tree_greedy(target_logits: torch.Tensor, node_tokens: torch.Tensor, parents: Sequence[int], *,
+                       out: Optional[Tuple[torch.Tensor, ...]] = None, workspace: Optional[torch.Tensor] = None):
     """Greedy static-tree verification (``spec_verify_tree_greedy``).
 
     target_logits [B, N, V], node_tokens [B, N] int32, parents: N host ints.
-    Returns (path [B, D+1], tokens [B, D+1], accept_len [B]) int32 tensors.
+    Returns (path [B, D+1], tokens [B, D+1], accept_len [B]) int32 tensors.  ``out`` reuses
+    output tensors and ``workspace`` a workspace, as for :func:`verify_chain`.
     """
     B, N, V = target_logits.shape
     dev = target_logits.device
@@ -192,11 +194,19 @@ def verify_tree_greedy(target_logits: torch.Tensor, node_tokens: torch.Tensor, p
     for n in range(1, N):
         depth[n] = depth[int(parents[n])] + 1 if 0 <= int(parents[n]) < n else 0
     D = max(depth)
-    path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
-    toks = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
-    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out is None:
+        path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        toks = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        path, toks, alen = out
+        _shape(path, "out path", (B, D + 1))
+        _shape(toks, "out tokens", (B, D + 1))
+        _shape(alen, "out accept_len", (B,))
+        for o, n in ((path, "out path"), (toks, "out tokens"), (alen, "out accept_len")):
+            _dev(o, n, torch.int32)
     need = tree_workspace_bytes(B, N, V, code)
-    wp, ws = _workspace(need, dev)
+    wp, ws = _workspace(need, dev, workspace)
     rc = lib().spec_verify_tree_greedy(_dev(target_logits, "target_logits"), code,
                                        _dev(node_tokens, "node_tokens", torch.int32), par, B, N, V,
                                        path.data_ptr(), toks.data_ptr(), alen.data_ptr(), wp, need, _stream(dev))
