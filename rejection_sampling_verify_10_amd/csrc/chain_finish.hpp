@@ -48,9 +48,11 @@ __device__ __forceinline__ pkey_t word_key(unsigned long long w) {
 constexpr int kSpinLimit = 1 << 16;
 
 // Merges the C (<= 16) chunk lists of a row from their words (units unit0 ..
-// unit0+C-1), polling until every word is valid, then clears them.  Lane l
-// ends with the l-th ranked key of the union; returns false on a poll timeout.
-// flagged: some chunk flagged the row.
+// unit0+C-1), polling until every word is valid.  Lane l ends with the l-th
+// ranked key of the union; returns false on a poll timeout.  flagged: some
+// chunk flagged the row.  The caller clears the words (clear_words) once it has
+// no more loads to wait for: the vector memory counter retires in order, so a
+// load issued after these stores would wait for their write-through.
 __device__ __forceinline__ bool merge_words(unsigned long long* words, long unit0, int C, pkey_t& out,
                                             bool& flagged) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -85,7 +87,6 @@ __device__ __forceinline__ bool merge_words(unsigned long long* words, long unit
             if (base + c < C) {
                 fl |= (w[c] & 2ull) != 0ull;
                 k[c] = (w[c] & 1ull) ? word_key(w[c]) : empty_key();
-                st_agent64(p + c * kTopkMax, 0ull);          // ready for the next call
             }
         }
         flagged |= __ballot(fl) != 0ull;
@@ -102,19 +103,43 @@ __device__ __forceinline__ bool merge_words(unsigned long long* words, long unit
     return ok;
 }
 
-// Kept distribution of row (b, k) from the list words; one wave.
-__device__ __forceinline__ bool word_row(const TopkLists& t, int b, int k, bool draft, int& idx, double& p,
-                                         int& kk) {
-    const long unit0 = t.unit_base(b, k) + (draft ? t.Ct : 0);
-    pkey_t key;
-    bool flagged;
-    const bool done = merge_words(t.words, unit0, draft ? t.Cd : t.Ct, key, flagged);
-    // Real (non-empty) entries of the merged list; top_k of them are kept.
-    const int real = static_cast<int>(__popcll(__ballot(key_idx(key) != kNoIndex)));
-    kk = real < t.top_k ? real : t.top_k;
-    return kept_distribution(key_val(key), key_idx(key), kk, done && !flagged, draft, t.invT,
-                             draft && t.draft_identity, idx, p) &&
-           done;
+// Zeroes the words of C lists (units unit0 ..), ready for the next call.
+__device__ __forceinline__ void clear_words(unsigned long long* words, long unit0, int C) {
+    unsigned long long* p = words + unit0 * kTopkMax + (threadIdx.x & (kWave - 1));
+#pragma unroll 1
+    for (int c = 0; c < C; ++c) st_agent64(p + c * kTopkMax, 0ull);
+}
+
+// Kept distribution of a merged row in fp32, one wave: lane l holds the l-th
+// ranked (value v, index) of the row, kk of them kept.  Target rows (draft =
+// false): w_l = exp((v_l - v_0)/T) = 2^((v_l - v_0) * k1), k1 = log2(e)/T.
+// Draft rows: w_l = (v_l / v_0)^(1/T) (v_l / v_0 when T = 1), the same
+// distribution as q^(1/T) renormalised, with every weight in [0, 1].  p_l =
+// w_l / sum w.  Returns false when the row is unusable (E1 / E3 / E4).  fp32
+// keeps the probabilities within a few units in the seventh digit of the fp64
+// values, far inside the 1e-5 agreement the test and draw decisions need.
+__device__ __forceinline__ bool kept_dist32(float v, int idx_in, int kk, bool valid, bool draft, float k1,
+                                            float invT, bool identity, int& idx, float& p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const float v0 = bcast(v, 0);
+    const bool have = lane < kk;
+    float w = 0.f;
+    bool ok = valid && kk > 0;
+    if (!draft) {
+        ok = ok && v0 > -INFINITY && v0 < INFINITY;
+        if (have) w = exp2f((v - v0) * k1);
+    } else {
+        ok = ok && v0 < INFINITY;
+        if (have && v > 0.f) {
+            const float r = v / v0;
+            w = identity ? r : exp2f(log2f(r) * invT);
+        }
+    }
+    const float Z = wave_sum(w);
+    ok = ok && Z > 0.f && Z < INFINITY;
+    p = have ? w / Z : 0.f;
+    idx = have ? idx_in : kNoIndex;
+    return ok;
 }
 
 // ---- position records: kRecWords words per position (payload in bits 63..32,
@@ -124,41 +149,54 @@ __device__ __forceinline__ bool word_row(const TopkLists& t, int b, int k, bool 
 // and the drawn token's probability.  Zero between calls.
 static_assert(kRecWords == 5, "record layout");
 
-// Target wave of position (b, k): test k and the token to emit if k is the
-// first rejection (residual draw, or from p'_k when the residual has no mass;
-// bonus draw for k = K).  (it, pt, kt): the target's kept distribution in index
-// order, one entry per lane; (sidx, sp, kd): the draft's, in LDS.  Stores the
-// position's record words.
-// (uk, uK, x): u_k, u_K and x_k (x unused for k = K), loaded by the caller
-// ahead of the list merges.
-__device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, int k, int it, double pt, int kt,
-                                                   bool ok, const int32_t* sidx, const double* sp, int kd,
-                                                   float uk, float uK, int x) {
+constexpr int kFinishWaves = 4;
+
+struct FinishSmem {
+    pkey_t dkey[kWave];            // wave 2's half of the draft merge
+    int32_t didx[kWave];           // the draft's kept entries, value order
+    float dq[kWave];
+    int32_t tidx[kWave];           // the target's kept indices, value order
+    float qpart[kFinishWaves][kWave];   // q'_k at those indices, from wave w's draft entries
+    int32_t dkd, dok, dbad;
+};
+
+// Wave 0 of position (b, k)'s finisher: test k and the token to emit if k is
+// the first rejection (residual draw, or from p'_k when the residual has no
+// mass; bonus draw for k = K).  (it, pt, kt): the target's kept distribution,
+// ranked by value, one entry per lane; the draft's kept entries and the draft
+// probability at each target entry (fs.qpart, one part per wave) are in LDS.
+// Stores the position's record words.  (uk, uK, x): u_k, u_K and x_k (x unused
+// for k = K).
+__device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, int k, int it, float pt, int kt,
+                                                   bool ok, const FinishSmem& fs, float uk, float uK, int x) {
     const int K = a.K, V = a.V;
     const int lane = threadIdx.x & (kWave - 1);
     const long rbase = static_cast<long>(b) * (K + 1);
     const bool inputs_ok = u_ok(uk) && u_ok(uK) && (k == K || (x >= 0 && x < V));
-    double r = pt, px = 0.0, qx = 0.0;
+    float r = pt, px = 0.f, qx = 0.f;
     bool accept = false;
     if (k < K) {
+        const int kd = fs.dkd;
+        const int di = lane < kd ? fs.didx[lane] : kNoIndex;
+        const float dq = lane < kd ? fs.dq[lane] : 0.f;
         px = lane_lookup(it, pt, x);
-        qx = lds_lookup(sidx, sp, kd, x);
-        double ratio;
-        if (qx > 0.0) ratio = px / qx;
-        else ratio = px > 0.0 ? INFINITY : 0.0;
-        const double thr = ratio < 1.0 ? ratio : 1.0;
-        accept = static_cast<double>(uk) < thr;
-        const double q = lane < kt ? lds_lookup(sidx, sp, kd, it) : 0.0;
-        r = lane < kt ? fmax(pt - q, 0.0) : 0.0;
+        qx = lane_lookup(di, dq, x);
+        float ratio;
+        if (qx > 0.f) ratio = px / qx;
+        else ratio = px > 0.f ? INFINITY : 0.f;
+        accept = uk < fminf(ratio, 1.f);
+        const float q = fmaxf(fmaxf(fs.qpart[0][lane], fs.qpart[1][lane]), fmaxf(fs.qpart[2][lane], fs.qpart[3][lane]));
+        r = lane < kt ? fmaxf(pt - q, 0.f) : 0.f;
     }
-    double S = wave_sum(r);
-    if (!(S > 0.0)) {                       // zero residual: draw from p'_k
+    float S = wave_sum(r);
+    if (!(S > 0.f)) {                       // zero residual: draw from p'_k
         r = pt;
         S = wave_sum(pt);
     }
-    const int src = lane_draw(r, lane < kt, static_cast<double>(uK) * S);
+    r = lane_gather(r, wave_sort_indices(it));     // index order for the draw
+    const int src = lane_draw(r, lane < kt, uK * S);
     const int y = bcast(it, src);
-    const double ry = bcast(r, src);
+    const float ry = bcast(r, src);
     if (lane < kRecWords) {
         uint32_t hi;
         uint32_t lo = 1u;
@@ -166,13 +204,13 @@ __device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, in
             hi = static_cast<uint32_t>(y);
             lo |= (accept ? 4u : 0u) | (ok ? 0u : 2u) | (inputs_ok ? 0u : 8u);
         } else if (lane == 1) {
-            hi = __float_as_uint(static_cast<float>(px));
+            hi = __float_as_uint(px);
         } else if (lane == 2) {
-            hi = __float_as_uint(static_cast<float>(qx));
+            hi = __float_as_uint(qx);
         } else if (lane == 3) {
-            hi = __float_as_uint(static_cast<float>(S));
+            hi = __float_as_uint(S);
         } else {
-            hi = __float_as_uint(static_cast<float>(ry / S));
+            hi = __float_as_uint(ry / S);
         }
         st_agent64(a.recw + (rbase + k) * kRecWords + lane, (static_cast<unsigned long long>(hi) << 32) | lo);
     }
@@ -187,6 +225,8 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
     const long rb = static_cast<long>(b) * (K + 1);
     const bool have = lane <= K;
     unsigned long long* pw = a.recw + (rb + (have ? lane : 0)) * kRecWords;
+    // the draft tokens, loaded before any store of this wave (see merge_words)
+    const int xl = lane < K ? a.x[static_cast<long>(b) * K + lane] : -1;
     unsigned long long w[kRecWords];
 #pragma unroll
     for (int i = 0; i < kRecWords; ++i) w[i] = have ? ld_agent64(pw + i) : 1ull;
@@ -202,10 +242,6 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
 #pragma unroll
         for (int i = 0; i < kRecWords; ++i)
             if ((w[i] & 1ull) == 0ull) w[i] = ld_agent64(pw + i);
-    }
-    if (have) {
-#pragma unroll
-        for (int i = 0; i < kRecWords; ++i) st_agent64(pw + i, 0ull);      // ready for the next call
     }
     const int y = static_cast<int>(w[0] >> 32);
     const bool acc = (w[0] & 4ull) != 0ull;
@@ -224,7 +260,7 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
     const float Sj = bcast(S, j), pyj = bcast(py, j);
     if (have) {
         int tok = -1;
-        if (!err) tok = lane < j ? a.x[static_cast<long>(b) * K + lane] : (lane == j ? yj : -1);
+        if (!err) tok = lane < j ? xl : (lane == j ? yj : -1);
         a.out_tokens[rb + lane] = tok;
     }
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
@@ -239,63 +275,101 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
             diag[2 * K + 1] = err ? NAN : pyj;
         }
     }
+    if (have) {
+#pragma unroll
+        for (int i = 0; i < kRecWords; ++i) st_agent64(pw + i, 0ull);      // ready for the next call
+    }
 }
 
-constexpr int kFinishWaves = 4;
-constexpr int kGroupPositions = kFinishWaves / 2;
+// Finisher workgroups per batch row: one per position.
+__host__ __device__ inline int finish_groups(int K) { return K + 1; }
 
-// Finisher workgroups per batch row: two positions each.
-__host__ __device__ inline int finish_groups(int K) { return (K + 1 + kGroupPositions - 1) / kGroupPositions; }
-
-struct FinishSmem {
-    int32_t sidx[kGroupPositions][kWave];     // the draft rows' kept entries, index order
-    double sp[kGroupPositions][kWave];
-    int32_t skd[kGroupPositions], sok[kGroupPositions];
-};
-
-// Finisher workgroup g of batch row b: positions k = 2g + p (p = 0, 1), wave
-// 2p merging target row k, wave 2p+1 draft row k.  The row's last group then
-// combines the row.
-__device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, int g, FinishSmem& fs) {
+// Finisher workgroup of position (b, k).  Wave 0 merges the target row's chunk
+// lists and forms p'_k; waves 1 and 2 merge the two halves of the draft row's
+// lists (k < K), wave 2 handing its half to wave 1, which forms q'_k.  All four
+// waves then look q'_k up at p'_k's indices, a quarter of the draft entries each,
+// and wave 0 tests x_k, draws, and stores the position's record; wave 3 of
+// position K's workgroup combines the row.
+__device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, int k, FinishSmem& fs) {
     const int K = a.K;
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const int p = wid >> 1;
-    const bool draft_wave = (wid & 1) != 0;
-    const int k = kGroupPositions * g + p;
+    const int lane = threadIdx.x & (kWave - 1), wid = wave_id();
     const TopkLists& t = a.tk;
     // The finish is the launch's critical path once the selection units run
     // out: its waves take precedence over co-resident selection waves.
     __builtin_amdgcn_s_setprio(3);
-    int it = kNoIndex, kt = 0;
-    double pt = 0.0;
-    bool ok = false;
+    const long unit0 = t.unit_base(b, k);
+    const int half = (t.Cd + 1) >> 1;
     float uk = 0.f, uK = 0.f;
     int x = 0;
-    if (k <= K && !draft_wave) {            // issued before the merges
+    pkey_t key = empty_key();
+    bool flagged = false, done = true;
+    if (wid == 0) {
         const long rbase = static_cast<long>(b) * (K + 1);
-        uk = a.u[rbase + k];
+        uk = a.u[rbase + k];                 // issued before the merges
         uK = a.u[rbase + K];
         if (k < K) x = a.x[static_cast<long>(b) * K + k];
-    }
-    if (k <= K) {
-        if (!draft_wave) {
-            ok = word_row(t, b, k, false, it, pt, kt);
-        } else if (k < K) {
-            int id, kd;
-            double pd;
-            const bool okd = word_row(t, b, k, true, id, pd, kd);
-            fs.sidx[p][lane] = id;
-            fs.sp[p][lane] = pd;
-            if (lane == 0) { fs.skd[p] = kd; fs.sok[p] = okd; }
-        } else if (lane == 0) {
-            fs.skd[p] = 0;
-            fs.sok[p] = 1;
+        done = merge_words(t.words, unit0, t.Ct, key, flagged);
+    } else if (wid <= 2 && k < K) {
+        const int c0 = wid == 1 ? 0 : half;
+        const int cn = wid == 1 ? half : t.Cd - half;
+        if (cn > 0) done = merge_words(t.words, unit0 + t.Ct + c0, cn, key, flagged);
+        if (wid == 2) {
+            fs.dkey[lane] = key;
+            if (lane == 0) fs.dbad = flagged || !done;
         }
     }
     __syncthreads();
-    if (k <= K && !draft_wave)
-        position_test_draw(a, b, k, it, pt, kt, ok && fs.sok[p] != 0, fs.sidx[p], fs.sp[p], fs.skd[p], uk, uK, x);
-    if (g == finish_groups(K) - 1 && wid == 0) chain_combine(a, b);
+    int it = kNoIndex, kt = 0;
+    float pt = 0.f;
+    bool ok = false;
+    if (wid == 0) {
+        // real (non-empty) entries of the merged list; top_k of them are kept
+        const int real = static_cast<int>(__popcll(__ballot(key_idx(key) != kNoIndex)));
+        kt = real < t.top_k ? real : t.top_k;
+        ok = kept_dist32(key_val(key), key_idx(key), kt, done && !flagged, false,
+                         static_cast<float>(1.4426950408889634 * t.invT), 0.f, false, it, pt) && done;
+        fs.tidx[lane] = it;
+    } else if (wid == 1 && k < K) {
+        wave_merge_keys(key, fs.dkey[lane]);
+        const int real = static_cast<int>(__popcll(__ballot(key_idx(key) != kNoIndex)));
+        const int kd = real < t.top_k ? real : t.top_k;
+        int di;
+        float dq;
+        const bool okd = kept_dist32(key_val(key), key_idx(key), kd, done && !flagged && !fs.dbad, true, 0.f,
+                                     static_cast<float>(t.invT), t.draft_identity != 0, di, dq);
+        fs.didx[lane] = di;
+        fs.dq[lane] = dq;
+        if (lane == 0) { fs.dkd = kd; fs.dok = okd; }
+    }
+    __syncthreads();
+    if (k < K) {
+        // q'_k at each kept target index: wave w matches draft entries 16w .. 16w+15
+        // (past kd they are (kNoIndex, 0) and match nothing that is kept)
+        const int ti = fs.tidx[lane];
+        const int m0 = wid * 16;
+        float q = 0.f;
+        if (m0 < fs.dkd) {
+            const int di = fs.didx[m0 + (lane & 15)];
+            const float dq = fs.dq[m0 + (lane & 15)];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int dm = __builtin_amdgcn_readlane(di, e);
+                const float qm = bcast(dq, e);
+                q = ti == dm ? qm : q;
+            }
+        }
+        fs.qpart[wid][lane] = q;
+        __syncthreads();
+    }
+    if (wid == 0) {
+        position_test_draw(a, b, k, it, pt, kt, ok && (k == K || fs.dok != 0), fs, uk, uK, x);
+        clear_words(t.words, unit0, t.Ct);
+    } else if (wid <= 2 && k < K) {
+        const int c0 = wid == 1 ? 0 : half;
+        const int cn = wid == 1 ? half : t.Cd - half;
+        clear_words(t.words, unit0 + t.Ct + c0, cn);
+    }
+    if (k == K && wid == 3) chain_combine(a, b);
 }
 
 }  // namespace sv

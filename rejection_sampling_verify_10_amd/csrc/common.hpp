@@ -108,9 +108,15 @@ __device__ __forceinline__ unsigned long long lane_gather(unsigned long long v, 
     const uint32_t hi = lane_gather(static_cast<uint32_t>(v >> 32), src);
     return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
+__device__ __forceinline__ float lane_gather(float v, int src) {
+    return __uint_as_float(lane_gather(__float_as_uint(v), src));
+}
 __device__ __forceinline__ double lane_gather(double v, int src) {
     return __longlong_as_double(static_cast<long long>(lane_gather(static_cast<unsigned long long>(__double_as_longlong(v)), src)));
 }
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value:
+// branches on it then compile to scalar branches instead of exec-mask regions.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave); }
 // Broadcast from a wave-uniform lane (v_readlane).
 __device__ __forceinline__ int bcast(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 __device__ __forceinline__ float bcast(float v, int lane) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane)); }
@@ -174,6 +180,21 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
     return v;
 }
 
+// Inclusive prefix sum across the wave in fp32: row-local steps of 1, 2, 4 and 8
+// lanes (DPP row shifts, lanes shifted in from outside the row read 0), then the
+// totals of the rows below (lanes 15, 31, 47) added in.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));   // row_shr:1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));   // row_shr:2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));   // row_shr:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));   // row_shr:8
+    const float r0 = bcast(v, 15), r1 = bcast(v, 31), r2 = bcast(v, 47);
+    const int row = lane >> 4;
+    const float below = row == 0 ? 0.f : (row == 1 ? r0 : (row == 2 ? r0 + r1 : (r0 + r1) + r2));
+    return v + below;
+}
+
 // (value desc, index asc) ordering: true when (va, ia) comes first.
 __device__ __forceinline__ bool precedes(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
@@ -229,10 +250,13 @@ __device__ __forceinline__ int key_idx(pkey_t k) { return static_cast<int>(0xfff
 __device__ __forceinline__ pkey_t empty_key() { return pair_key(-INFINITY, kNoIndex); }
 
 // Keeps in this lane the larger (keep_first) or the smaller of {mine, lane^j's}.
+// Written as one compare and a select (no branch): take the partner's key when it
+// is larger and the larger is kept, or not larger and the smaller is kept (equal
+// keys make either choice the same).
 __device__ __forceinline__ void cx_key(pkey_t& k, int j, bool keep_first) {
     const pkey_t o = xshfl(k, j);
-    const bool mine = k > o;
-    if (keep_first ? !mine : mine) k = o;
+    const bool take = (o > k) == keep_first;
+    k = take ? o : k;
 }
 
 // Full sort of the 64 keys of the wave (lane 0 = first).

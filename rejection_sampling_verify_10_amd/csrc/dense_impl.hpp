@@ -418,7 +418,7 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
                                            RowSmem& sm, double* dyn_lds, float m_j, double Zp_row) {
     static_assert(!TAB || DT == 1, "the exponential table is for bf16 logits");
     const int K = a.K, V = a.V;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
     const int C = (V + kDenseChunk - 1) / kDenseChunk;
     const int C_full = V / kDenseChunk;              // chunks wholly inside the row
     const int nslots = dense_slots(C);
@@ -860,7 +860,7 @@ struct RowAcc {
 // partials rescaled to M and summed in fp64.  LDS barriers only.
 template <int DT>
 __device__ __forceinline__ void row_reduce(const RowAcc<DT>& ra, double invT, RowSmem& sm, float& M, double& Z) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wid = wave_id();
     const float s = (ra.acc[0] + ra.acc[1]) + (ra.acc[2] + ra.acc[3]);
     const float wm = wave_max(ra.m);
     if (lane == 0) sm.wmax[wid] = wm;

@@ -62,10 +62,10 @@ __device__ __forceinline__ int merge_global_lists(const TopkLists& t, long unit0
     return wave_sum(nl);
 }
 
-// Sorts (index, probability) pairs by index ascending (empty lanes carry kNoIndex):
-// a bitonic network on 32-bit keys (index << 6 | lane, indices < 2^26), then one
-// gather of the probabilities by the lane each key came from.
-__device__ __forceinline__ void wave_sort_by_index(int& i, double& p) {
+// Sorts the wave's indices ascending (empty lanes carry kNoIndex and end up
+// last): a bitonic network on 32-bit keys (index << 6 | lane, indices < 2^26).
+// Returns for each lane the lane its index came from, to gather payloads with.
+__device__ __forceinline__ int wave_sort_indices(int& i) {
     const int lane = threadIdx.x & (kWave - 1);
     constexpr uint32_t kEmpty = 0xffffffc0u;
     uint32_t key = i == kNoIndex ? (kEmpty | lane) : ((static_cast<uint32_t>(i) << 6) | lane);
@@ -76,11 +76,17 @@ __device__ __forceinline__ void wave_sort_by_index(int& i, double& p) {
             const uint32_t o = xshfl(key, j);
             const bool up = (lane & k) == 0 || k == kWave;
             const bool keep_small = ((lane & j) == 0) == up;
-            if (keep_small ? (o < key) : (o > key)) key = o;
+            key = ((o < key) == keep_small) ? o : key;      // a select, no branch
         }
     }
     i = key >= kEmpty ? kNoIndex : static_cast<int>(key >> 6);
-    p = lane_gather(p, static_cast<int>(key & 63u));
+    return static_cast<int>(key & 63u);
+}
+
+// (index, probability) pairs sorted by index ascending.
+template <typename P>
+__device__ __forceinline__ void wave_sort_by_index(int& i, P& p) {
+    p = lane_gather(p, wave_sort_indices(i));
 }
 
 // From a row's ranked top entries (lane l = l-th, kk kept) to its transformed
@@ -109,10 +115,11 @@ __device__ __forceinline__ bool kept_distribution(float v, int idx_in, int kk, b
     return ok;
 }
 
-// Probability of token x in an index-sorted list held one entry per lane.
-__device__ __forceinline__ double lane_lookup(int idx, double p, int x) {
+// Probability of token x in a list held one entry per lane (0 if absent).
+template <typename P>
+__device__ __forceinline__ P lane_lookup(int idx, P p, int x) {
     const unsigned long long m = __ballot(idx == x);
-    if (!m) return 0.0;
+    if (!m) return P(0);
     return bcast(p, __ffsll(static_cast<long long>(m)) - 1);
 }
 
@@ -130,11 +137,12 @@ __device__ __forceinline__ double lds_lookup(const int* sidx, const double* sp, 
 // Inverse-CDF draw over an index-sorted list of weights r (one per lane) with
 // target u*S: first lane whose inclusive prefix exceeds the target; rounding
 // fallback = last lane with a positive weight.  Returns the lane.
-__device__ __forceinline__ int lane_draw(double r, bool have, double target) {
-    const double C = wave_inclusive_scan(r);
-    const unsigned long long hit = __ballot(have && r > 0.0 && target < C);
+template <typename P>
+__device__ __forceinline__ int lane_draw(P r, bool have, P target) {
+    const P C = wave_inclusive_scan(r);
+    const unsigned long long hit = __ballot(have && r > P(0) && target < C);
     if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
-    const unsigned long long pos = __ballot(have && r > 0.0);
+    const unsigned long long pos = __ballot(have && r > P(0));
     return pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
 }
 

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
     const long mem_row = static_cast<long>(b) * a.batch_stride + k;
     const char* row = static_cast<const char*>(a.base) + mem_row * a.V * Elem<DT>::kBytes;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wid = threadIdx.x / kWave;
+    const int wid = wave_id();
 
     if (a.argmax_mode) {
         float best;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void power_sums_kernel(PowerSumArgs a) {
     acc += part;
     acc = wave_sum(acc);
     bad = wave_or(bad);
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wid = wave_id();
     if (lane == 0) { s_z[wid] = acc; s_f[wid] = bad; }
     __syncthreads();
     if (threadIdx.x == 0) {

@@ -63,7 +63,7 @@ __device__ __forceinline__ int block_sum(int v, ChunkSmem& sm) {
 
 // Exclusive prefix of v over the threads of the block; the block total in *total.
 __device__ __forceinline__ int block_exclusive(int v, ChunkSmem& sm, int* total) {
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wid = wave_id();
     int incl = v;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -202,7 +202,7 @@ __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row
     using E = Elem<DT>;
     constexpr int EPV = E::kPerVec;
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    const int lane = tid & (kWave - 1), wid = wave_id();
     const int nvec = (len + EPV - 1) / EPV;
     float gmax[kSlots];
     float tmax = -INFINITY, tmin = INFINITY;

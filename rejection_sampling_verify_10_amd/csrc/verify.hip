@@ -151,7 +151,7 @@ __global__ __launch_bounds__(2 * kWave) void alpha_topk_kernel(AlphaArgs a) {
     __shared__ int32_t sidx[kWave];
     __shared__ double sp[kWave];
     __shared__ int32_t skd, sok;
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wid = wave_id();
     const long r = blockIdx.x;                                  // b*K + k
     const int b = static_cast<int>(r / a.K), k = static_cast<int>(r - static_cast<long>(b) * a.K);
     int it = kNoIndex, kt = 0;
