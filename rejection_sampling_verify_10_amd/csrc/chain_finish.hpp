@@ -162,8 +162,8 @@ struct FinishSmem {
 
 // Wave 0 of position (b, k)'s finisher: test k and the token to emit if k is
 // the first rejection (residual draw, or from p'_k when the residual has no
-// mass; bonus draw for k = K).  (it, pt, kt): the target's kept distribution,
-// ranked by value, one entry per lane; the draft's kept entries and the draft
+// mass; bonus draw for k = K).  (it, pt, kt): the target's kept distribution in
+// index order, one entry per lane; the draft's kept entries and the draft
 // probability at each target entry (fs.qpart, one part per wave) are in LDS.
 // Stores the position's record words.  (uk, uK, x): u_k, u_K and x_k (x unused
 // for k = K).
@@ -188,13 +188,15 @@ __device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, in
         const float q = fmaxf(fmaxf(fs.qpart[0][lane], fs.qpart[1][lane]), fmaxf(fs.qpart[2][lane], fs.qpart[3][lane]));
         r = lane < kt ? fmaxf(pt - q, 0.f) : 0.f;
     }
-    float S = wave_sum(r);
+    // inverse CDF in index order: S is the last inclusive prefix
+    float C = wave_inclusive_scan(r);
+    float S = bcast(C, kWave - 1);
     if (!(S > 0.f)) {                       // zero residual: draw from p'_k
         r = pt;
-        S = wave_sum(pt);
+        C = wave_inclusive_scan(r);
+        S = bcast(C, kWave - 1);
     }
-    r = lane_gather(r, wave_sort_indices(it));     // index order for the draw
-    const int src = lane_draw(r, lane < kt, uK * S);
+    const int src = lane_draw_scanned(r, C, lane < kt, uK * S);
     const int y = bcast(it, src);
     const float ry = bcast(r, src);
     if (lane < kRecWords) {
@@ -328,6 +330,7 @@ __device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, in
         kt = real < t.top_k ? real : t.top_k;
         ok = kept_dist32(key_val(key), key_idx(key), kt, done && !flagged, false,
                          static_cast<float>(1.4426950408889634 * t.invT), 0.f, false, it, pt) && done;
+        pt = lane_gather(pt, wave_sort_indices(it));     // index order
         fs.tidx[lane] = it;
     } else if (wid == 1 && k < K) {
         wave_merge_keys(key, fs.dkey[lane]);

@@ -214,6 +214,34 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 
 namespace sv {
 
+// ---- bitonic networks over one 32-bit key per lane ----
+
+// Keeps in this lane the larger (keep_large) or the smaller of {mine, lane^j's}.
+__device__ __forceinline__ uint32_t cx_u32(uint32_t k, int j, bool keep_large) {
+    const uint32_t o = xshfl(k, j);
+    return ((o > k) == keep_large) ? o : k;
+}
+// Sorts the wave's 64 keys, largest first.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t k) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int s = 2; s <= kWave; s <<= 1) {
+#pragma unroll
+        for (int j = s >> 1; j > 0; j >>= 1) {
+            const bool up = (lane & s) == 0 || s == kWave;
+            k = cx_u32(k, j, ((lane & j) == 0) == up);
+        }
+    }
+    return k;
+}
+// Sorts a bitonic sequence of 64 keys, largest first (desc) or smallest first.
+__device__ __forceinline__ uint32_t wave_bitonic_clean(uint32_t k, bool desc) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int j = kWave >> 1; j > 0; j >>= 1) k = cx_u32(k, j, ((lane & j) == 0) == desc);
+    return k;
+}
+
 // ---- wave-level bitonic networks over (value, index) pairs, one pair per lane ----
 //
 // Order: larger value first, lower index on equal values (a strict total order

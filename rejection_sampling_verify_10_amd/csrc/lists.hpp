@@ -134,12 +134,11 @@ __device__ __forceinline__ double lds_lookup(const int* sidx, const double* sp, 
     return (lo < n && sidx[lo] == x) ? sp[lo] : 0.0;
 }
 
-// Inverse-CDF draw over an index-sorted list of weights r (one per lane) with
-// target u*S: first lane whose inclusive prefix exceeds the target; rounding
-// fallback = last lane with a positive weight.  Returns the lane.
+// Inverse-CDF draw over an index-sorted list of weights r (one per lane), C their
+// inclusive prefix, with target u*S: first lane whose prefix exceeds the target;
+// rounding fallback = last lane with a positive weight.  Returns the lane.
 template <typename P>
-__device__ __forceinline__ int lane_draw(P r, bool have, P target) {
-    const P C = wave_inclusive_scan(r);
+__device__ __forceinline__ int lane_draw_scanned(P r, P C, bool have, P target) {
     const unsigned long long hit = __ballot(have && r > P(0) && target < C);
     if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
     const unsigned long long pos = __ballot(have && r > P(0));

@@ -47,7 +47,6 @@ struct ChunkSmem {
     int32_t red[kWaves];
     int32_t cnt;
     uint32_t flags, overflow;
-    float tau;
 };
 
 __device__ __forceinline__ int block_sum(int v, ChunkSmem& sm) {
@@ -233,34 +232,18 @@ __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row
     bad = wave_or(bad);
     if (tmax != tmax) tmax = -INFINITY;
 
-    // tau: the top_k-th largest of the 256 thread maxima, by bisection on their
-    // ordered keys in wave 0 (4 keys per lane; counts are ballot popcounts).
-    sm.tkey[tid] = order_key(tmax);
+    // tau: the top_k-th largest of the 256 thread maxima.  Each wave sorts its 64
+    // ordered keys; after one barrier every wave merges the four sorted lists
+    // itself (two bitonic merges, then one more), so no second barrier is needed.
+    sm.tkey[tid] = wave_sort_desc(order_key(tmax));
     if (tid == 0) { sm.cnt = 0; sm.flags = 0; sm.overflow = 0; }
     __syncthreads();
     if (lane == 0 && bad) atomicOr(&sm.flags, kFlagInvalid);
-    if (wid == 0) {
-        const uint32_t k0 = sm.tkey[lane], k1 = sm.tkey[lane + 64], k2 = sm.tkey[lane + 128], k3 = sm.tkey[lane + 192];
-        // Any key with at least top_k maxima at or above it is a valid threshold;
-        // the search runs between the smallest and largest maximum and stops as
-        // soon as exactly top_k qualify.
-        uint32_t lo = wave_min_u32(min(min(k0, k1), min(k2, k3)));
-        uint32_t hi = wave_max_u32(max(max(k0, k1), max(k2, k3)));
-        while (lo < hi) {
-            const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
-            const int c = __popcll(__ballot(k0 >= mid)) + __popcll(__ballot(k1 >= mid)) +
-                          __popcll(__ballot(k2 >= mid)) + __popcll(__ballot(k3 >= mid));
-            if (c >= top_k) {
-                lo = mid;
-                if (c == top_k) break;
-            } else {
-                hi = mid - 1u;
-            }
-        }
-        if (lane == 0) sm.tau = lo == 0u ? -INFINITY : order_value(lo);
-    }
-    __syncthreads();
-    const float tau = sm.tau;
+    uint32_t m01 = wave_bitonic_clean(max(sm.tkey[lane], sm.tkey[127 - lane]), true);
+    const uint32_t m23 = wave_bitonic_clean(max(sm.tkey[128 + lane], sm.tkey[255 - lane]), false);
+    m01 = wave_bitonic_clean(max(m01, m23), true);
+    const uint32_t kth = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(m01), top_k - 1));
+    const float tau = kth == 0u ? -INFINITY : order_value(kth);
 
     // Stage the vectors whose maximum reaches tau (about k + 10 per chunk) in
     // wave-private LDS, then let each lane check one staged vector's elements.
