@@ -45,7 +45,7 @@ WORKLOADS = {
             kernel="dense_walk_kernel", copies=64, oracle_rows=8, dtype="bf16 in, f32 exp, f64 draw"),
     2: dict(name="chain verify B=64 K=7 V=128256, bf16 target logits, fp32 draft probs, T=0.7, top_k=50",
             kernel="topk_chunk_kernel", copies=4, oracle_rows=64,
-            dtype="bf16/f32 in, f32 select, f64 probabilities"),
+            dtype="bf16/f32 in, f32 select, f32 probabilities"),
     3: dict(name="greedy static-tree verify B=32 N=27 (depth 5) V=32000, bf16 target logits",
             kernel="rowstats_kernel", copies=10, oracle_rows=32, dtype="bf16 in, exact argmax"),
     4: dict(name="chain verify B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
@@ -145,8 +145,8 @@ def read_probe_gbps(R, torch, dev) -> float:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
