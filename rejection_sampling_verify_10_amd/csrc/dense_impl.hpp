@@ -410,6 +410,158 @@ struct RowSmem {
     double before;
 };
 
+// Exact chunk sums of a draw row by a pass of its own (the slow path: a
+// normaliser outside its bracket or an overflowing list): sm.part[c] = the sum
+// of e_i (resid false) or of max(0, e_i/Zp - w_i/Zq) (true) over chunk c.
+template <int DT, bool VEC, bool TR>
+__device__ __forceinline__ void exact_chunk_sums(const ChainArgs& a, const char* zr, const float* qr, int C, ExpArg g,
+                                              const double* tbl, ExpConsts ek, bool resid, double invZp,
+                                              double invZq, RowSmem& sm) {
+    const int tid = threadIdx.x, V = a.V;
+#pragma unroll 1
+    for (int c = 0; c < C; ++c) {
+        double sc = 0.0;
+#pragma unroll 1
+        for (int s = 0; s < kSub; ++s) {
+            const int i0 = c * kDenseChunk + (s * kThreads + tid) * 8;
+            float z[8], q[8];
+            load8_z<DT, VEC, false>(zr, i0, V, z);
+            if (resid) load8_q<VEC, false>(qr, i0, V, q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double ex = exp_of(z[e], g, tbl, ek);
+                if (resid) {
+                    const double rr = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
+                    sc += rr > 0.0 ? rr : 0.0;
+                } else {
+                    sc += ex;
+                }
+            }
+        }
+        sc = block_sum(sc, sm.red);
+        if (tid == 0) sm.part[c] = sc;
+    }
+    __syncthreads();
+}
+
+// The draw of batch row b from its chunk weights sm.part[0..C) (total W): the
+// chunk holding u_K*W, rescanned element by element (weights e_i (residual false)
+// or max(0, e_i/Zp - w_i/Zq)), then the row's outputs.  S: the residual mass
+// reported in diag (residual rows).
+template <int DT, bool VEC, bool TR>
+__device__ __forceinline__ void draw_emit(const ChainArgs& a, int b, int j, const char* zr, const float* qr, int C,
+                                          ExpArg g, const double* tbl, const ExpConsts& ek, bool residual, double W,
+                                          double S, double invZp, double invZq, RowSmem& sm) {
+    const int K = a.K, V = a.V;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
+    const long rbase = static_cast<long>(b) * (K + 1);
+    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
+    const double target = static_cast<double>(a.u[rbase + K]) * W;
+    if (tid == 0) {
+        double before = 0.0;
+        int chunk = -1, last = 0;
+        for (int c = 0; c < C; ++c) {
+            const double pc = sm.part[c];
+            if (target < before + pc) { chunk = c; break; }
+            before += pc;
+            if (pc > 0.0) last = c;
+        }
+        sm.fallback = chunk < 0;     // rounding: u*W at or past the total
+        sm.chunk = chunk < 0 ? last : chunk;
+        sm.before = before;
+    }
+    __syncthreads();
+    const int chunk = sm.chunk;
+    const bool fallback = sm.fallback != 0;
+
+    // Weights of 8 consecutive elements from i0: exp (p' draw) or residual.
+    auto weights8 = [&](int i0, double wt[8]) {
+        float z[8], q[8];
+        load8_z<DT, VEC, false>(zr, i0, V, z);
+        if (residual) load8_q<VEC, false>(qr, i0, V, q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double ex = exp_of(z[e], g, tbl, ek);
+            double w = ex;
+            if (residual) {
+                w = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
+                w = w > 0.0 ? w : 0.0;
+            }
+            wt[e] = (i0 + e < V) ? w : 0.0;
+        }
+    };
+    // Thread t holds elements [t*8, t*8 + 8) of the chunk.  Two passes
+    // (recomputing beats holding 16 doubles): thread sums, then the crossing.
+    const int i0 = chunk * kDenseChunk + tid * kEPT;
+    double s = 0.0, wlast = 0.0;
+    int lastpos = -1;
+#pragma unroll 1
+    for (int sub = 0; sub < kSub; ++sub) {
+        double wt[8];
+        weights8(i0 + 8 * sub, wt);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s += wt[e];
+            if (wt[e] > 0.0) { lastpos = i0 + 8 * sub + e; wlast = wt[e]; }
+        }
+    }
+    double incl = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) sm.red[wid] = incl;
+    __syncthreads();
+    double cum = sm.before;
+    for (int x = 0; x < wid; ++x) cum += sm.red[x];
+    cum += incl - s;
+    int found = 0x7fffffff;
+    double wfound = 0.0;
+    // Threads whose span ends past u*W rescan; the smallest crossing wins.
+    if (!fallback && target < cum + s) {
+#pragma unroll 1
+        for (int sub = 0; sub < kSub && found == 0x7fffffff; ++sub) {
+            double wt[8];
+            weights8(i0 + 8 * sub, wt);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                cum += wt[e];
+                if (found == 0x7fffffff && wt[e] > 0.0 && target < cum) { found = i0 + 8 * sub + e; wfound = wt[e]; }
+            }
+        }
+    }
+    // Smallest crossing index; if rounding left none in the chunk, its last positive index.
+    int y = wave_min_int(found);
+    const int lp = wave_max_int(lastpos);
+    __syncthreads();
+    if (lane == 0) { sm.ired[wid] = y; sm.red[wid] = static_cast<double>(lp); }
+    __syncthreads();
+    y = sm.ired[0];
+    int lpb = static_cast<int>(sm.red[0]);
+#pragma unroll
+    for (int x = 1; x < kWaves; ++x) { y = min(y, sm.ired[x]); lpb = max(lpb, static_cast<int>(sm.red[x])); }
+    const bool crossed = y != 0x7fffffff;
+    if (!crossed) y = lpb;
+    const double my = crossed ? (found == y ? wfound : 0.0) : (lastpos == y ? wlast : 0.0);
+    const double wy = block_sum(my, sm.red);
+
+    for (int t = tid; t <= K; t += kThreads) {
+        int tok = -1;
+        if (t < j) tok = a.x[static_cast<long>(b) * K + t];
+        else if (t == j) tok = y;
+        a.out_tokens[rbase + t] = tok;
+    }
+    if (tid == 0) {
+        a.out_accept_len[b] = j;
+        if (diag) {
+            diag[2 * K] = static_cast<float>(residual ? S : 1.0);
+            diag[2 * K + 1] = static_cast<float>(wy / W);
+        }
+    }
+}
+
 // The final draw of batch row b (one workgroup): sm.j / sm.err set, sm.tbl
 // built, sm.n_list = sm.qbad = 0, all visible after a barrier; (m_j, Zp_ap):
 // the maximum and approximate normaliser of target row j.
@@ -595,33 +747,6 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
     else body(std::false_type{});
     __syncthreads();
 
-    // Exact chunk sums of e (RESID false) or of the residual (true) by a second pass.
-    auto exact_chunks = [&](bool resid, double invZp, double invZq) {
-#pragma unroll 1
-        for (int c = 0; c < C; ++c) {
-            double sc = 0.0;
-#pragma unroll 1
-            for (int s = 0; s < kSub; ++s) {
-                const int i0 = c * kDenseChunk + (s * kThreads + tid) * 8;
-                float z[8], q[8];
-                load8_z<DT, VEC, false>(zr, i0, V, z);
-                if (resid) load8_q<VEC, false>(qr, i0, V, q);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const double ex = exp_of(z[e], g, tbl, ek);
-                    if (resid) {
-                        const double rr = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
-                        sc += rr > 0.0 ? rr : 0.0;
-                    } else {
-                        sc += ex;
-                    }
-                }
-            }
-            sc = block_sum(sc, sm.red);
-            if (tid == 0) sm.part[c] = sc;
-        }
-        __syncthreads();
-    };
 
     double Zp = 0.0, Zq = 1.0, S = 0.0;
     bool residual = false;
@@ -665,126 +790,21 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
         } else {
             // A normaliser outside its bracket or the list overflowed: never expected,
             // always correct.
-            exact_chunks(true, invZp, invZq);
+            exact_chunk_sums<DT, VEC, TR>(a, zr, qr, C, g, tbl, ek, true, invZp, invZq, sm);
         }
         for (int c = 0; c < C; ++c) S += sm.part[c];
         __syncthreads();
         residual = S > 0.0;
         if (!residual) {
             // zero residual: the draw falls back to p'_j, whose chunk sums this pass skipped
-            exact_chunks(false, 0.0, 0.0);
+            exact_chunk_sums<DT, VEC, TR>(a, zr, qr, C, g, tbl, ek, false, 0.0, 0.0, sm);
             Zp = 0.0;
             for (int c = 0; c < C; ++c) Zp += sm.part[c];
         }
     }
     const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
 
-    // ---- draw: the chunk holding u*W, then its elements ----
-    const double W = residual ? S : Zp;
-    const double target = static_cast<double>(a.u[rbase + K]) * W;
-    if (tid == 0) {
-        double before = 0.0;
-        int chunk = -1, last = 0;
-        for (int c = 0; c < C; ++c) {
-            const double pc = sm.part[c];
-            if (target < before + pc) { chunk = c; break; }
-            before += pc;
-            if (pc > 0.0) last = c;
-        }
-        sm.fallback = chunk < 0;     // rounding: u*W at or past the total
-        sm.chunk = chunk < 0 ? last : chunk;
-        sm.before = before;
-    }
-    __syncthreads();
-    const int chunk = sm.chunk;
-    const bool fallback = sm.fallback != 0;
-
-    // Weights of 8 consecutive elements from i0: exp (p' draw) or residual.
-    auto weights8 = [&](int i0, double wt[8]) {
-        float z[8], q[8];
-        load8_z<DT, VEC, false>(zr, i0, V, z);
-        if (residual) load8_q<VEC, false>(qr, i0, V, q);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const double ex = exp_of(z[e], g, tbl, ek);
-            double w = ex;
-            if (residual) {
-                w = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
-                w = w > 0.0 ? w : 0.0;
-            }
-            wt[e] = (i0 + e < V) ? w : 0.0;
-        }
-    };
-    // Thread t holds elements [t*8, t*8 + 8) of the chunk.  Two passes
-    // (recomputing beats holding 16 doubles): thread sums, then the crossing.
-    const int i0 = chunk * kDenseChunk + tid * kEPT;
-    double s = 0.0, wlast = 0.0;
-    int lastpos = -1;
-#pragma unroll 1
-    for (int sub = 0; sub < kSub; ++sub) {
-        double wt[8];
-        weights8(i0 + 8 * sub, wt);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            s += wt[e];
-            if (wt[e] > 0.0) { lastpos = i0 + 8 * sub + e; wlast = wt[e]; }
-        }
-    }
-    double incl = s;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
-    __syncthreads();
-    if (lane == kWave - 1) sm.red[wid] = incl;
-    __syncthreads();
-    double cum = sm.before;
-    for (int x = 0; x < wid; ++x) cum += sm.red[x];
-    cum += incl - s;
-    int found = 0x7fffffff;
-    double wfound = 0.0;
-    // Threads whose span ends past u*W rescan; the smallest crossing wins.
-    if (!fallback && target < cum + s) {
-#pragma unroll 1
-        for (int sub = 0; sub < kSub && found == 0x7fffffff; ++sub) {
-            double wt[8];
-            weights8(i0 + 8 * sub, wt);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                cum += wt[e];
-                if (found == 0x7fffffff && wt[e] > 0.0 && target < cum) { found = i0 + 8 * sub + e; wfound = wt[e]; }
-            }
-        }
-    }
-    // Smallest crossing index; if rounding left none in the chunk, its last positive index.
-    int y = wave_min_int(found);
-    const int lp = wave_max_int(lastpos);
-    __syncthreads();
-    if (lane == 0) { sm.ired[wid] = y; sm.red[wid] = static_cast<double>(lp); }
-    __syncthreads();
-    y = sm.ired[0];
-    int lpb = static_cast<int>(sm.red[0]);
-#pragma unroll
-    for (int x = 1; x < kWaves; ++x) { y = min(y, sm.ired[x]); lpb = max(lpb, static_cast<int>(sm.red[x])); }
-    const bool crossed = y != 0x7fffffff;
-    if (!crossed) y = lpb;
-    const double my = crossed ? (found == y ? wfound : 0.0) : (lastpos == y ? wlast : 0.0);
-    const double wy = block_sum(my, sm.red);
-
-    for (int t = tid; t <= K; t += kThreads) {
-        int tok = -1;
-        if (t < j) tok = a.x[static_cast<long>(b) * K + t];
-        else if (t == j) tok = y;
-        a.out_tokens[rbase + t] = tok;
-    }
-    if (tid == 0) {
-        a.out_accept_len[b] = j;
-        if (diag) {
-            diag[2 * K] = static_cast<float>(residual ? S : 1.0);
-            diag[2 * K + 1] = static_cast<float>(wy / W);
-        }
-    }
+    draw_emit<DT, VEC, TR>(a, b, j, zr, qr, C, g, tbl, ek, residual, residual ? S : Zp, S, invZp, invZq, sm);
 }
 
 __device__ __forceinline__ void init_draw_smem(RowSmem& sm) {
@@ -878,21 +898,18 @@ __device__ __forceinline__ void row_reduce(const RowAcc<DT>& ra, double invT, Ro
     lds_barrier();                 // the slots are reused by the next row
 }
 
-// Chain verification with the draft used as given (T == 1, no top-k): one
-// workgroup per batch row walks the positions left to right ("064 · 投机解码",
-// section 三), reading target row k only once x_0..x_{k-1} are accepted: its
-// statistics, then test k from the gathered z[x_k] and q[x_k].  At the first
-// rejection (or at row K) it draws the emitted token as dense_row_kernel does.
-// The rows are one stream of tiles: the tile after the last of row k (the first
-// of row k+1) is in flight while row k is reduced and tested, and is dropped if
-// the walk stops.
-template <int DT, bool VEC, bool TAB>
-__global__ __launch_bounds__(kThreads, (min_waves<VEC, false>())) void dense_walk_kernel(ChainArgs a, double bracket,
-                                                                                         ExpConsts ek) {
+// The walk of batch row b with the draft used as given (T == 1, no top-k), one
+// workgroup: the positions left to right ("064 · 投机解码", section 三), reading
+// target row k only once x_0..x_{k-1} are accepted: its statistics, then test k
+// from the gathered z[x_k] and q[x_k].  Returns the first rejection j (K if
+// none), the error flag and the maximum and normaliser of target row j.  The
+// rows are one stream of tiles: the tile after the last of row k (the first of
+// row k+1) is in flight while row k is reduced and tested, and is dropped if the
+// walk stops.  sm.tbl must be built (init_draw_smem) before the call.
+template <int DT, bool VEC>
+__device__ __forceinline__ void walk_positions(const ChainArgs& a, int b, RowSmem& sm, int& j_out, bool& err_out,
+                                               float& mj_out, double& zj_out) {
     using E = Elem<DT>;
-    __shared__ RowSmem sm;
-    extern __shared__ double dyn_lds[];
-    const int b = blockIdx.x;
     const int K = a.K, V = a.V;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const long rbase = static_cast<long>(b) * (K + 1);
@@ -921,7 +938,6 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, false>())) void dense_wal
         bad = __ballot(bad) != 0ull;
         if (lane == 0) sm.err = bad;
     }
-    init_draw_smem(sm);
     __syncthreads();
     const float scale = static_cast<float>(1.4426950408889634 * a.invT);
     bool err = sm.err != 0;
@@ -1030,7 +1046,32 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, false>())) void dense_wal
     }
     if (diag && !err)
         for (int t = j + 1 + tid; t < K; t += kThreads) { diag[t] = NAN; diag[K + t] = NAN; }
-    if (tid == 0) { sm.j = j; sm.err = err; }
+    j_out = j;
+    err_out = err;
+    mj_out = mj;
+    zj_out = Zj;
+}
+
+// Chain verification with the draft used as given (T == 1, no top-k): one
+// workgroup per batch row walks the positions (walk_positions), then draws the
+// emitted token as dense_row_kernel does.
+template <int DT, bool VEC, bool TAB>
+__global__ __launch_bounds__(kThreads, (min_waves<VEC, false>())) void dense_walk_kernel(ChainArgs a, double bracket,
+                                                                                         ExpConsts ek) {
+    __shared__ RowSmem sm;
+    extern __shared__ double dyn_lds[];
+    const int b = blockIdx.x;
+    // The walks are the launch's critical path; a workgroup drawing its row
+    // shares the CU with one still walking: the walk takes issue precedence.
+    __builtin_amdgcn_s_setprio(2);
+    init_draw_smem(sm);
+    int j;
+    bool err;
+    float mj;
+    double Zj;
+    walk_positions<DT, VEC>(a, b, sm, j, err, mj, Zj);
+    __builtin_amdgcn_s_setprio(0);
+    if (threadIdx.x == 0) { sm.j = j; sm.err = err; }
     __syncthreads();
     final_draw<DT, VEC, false, TAB>(a, b, bracket, ek, sm, dyn_lds, mj, Zj);
 }
