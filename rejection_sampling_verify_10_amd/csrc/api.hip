@@ -145,6 +145,21 @@ double dense_bracket(bool transformed) {
     return transformed ? 3e-5 : 4e-6;
 }
 
+// Dense chains with the draft used as given (T == 1): the walk (one workgroup per
+// batch row reads target rows only up to the first rejection) or every row's
+// statistics at once followed by the tests and the draw.  The walk reads fewer
+// bytes but its rows are sequential; a small batch does not fill the GPU with
+// walks.  SPEC_VERIFY_DENSE_PATH=walk|rows overrides the choice.
+bool dense_walks(int B, int K, int V) {
+    const char* env = getenv("SPEC_VERIFY_DENSE_PATH");
+    if (env && !strcmp(env, "walk")) return true;
+    if (env && !strcmp(env, "rows")) return false;
+    // Measured crossover (K = 8, V = 128256): the all-rows route is faster up to
+    // B = 128 (93 against 109 us), the walk from B = 256 (117 against 143 us).
+    // Short rows (V = 1000) favour the walk's single launch.
+    return static_cast<long>(B) * (K + 1) > 1536 || V < 4096;
+}
+
 ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {
     ChainPlan p{};
     const size_t Rt = static_cast<size_t>(B) * (K + 1), Rd = static_cast<size_t>(B) * K;
@@ -310,8 +325,15 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
         fa.sel = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K + 1, p.tk);
         fa.ch = ca;
         SV_TRY(launch_chain_topk(fa, s, prof.timing()));
-    } else if (!ca.transformed) {
+    } else if (!ca.transformed && dense_walks(B, K, V)) {
         SV_TRY(launch_chain_walk(ca, dense_bracket(false), s, prof.timing()));
+    } else if (!ca.transformed) {
+        // every target row's statistics at once, then the tests and the draw per batch row
+        ca.st = p.st;
+        RowStatsArgs ra =
+            rowstats_args(target_logits, dtype, V, K + 1, K + 1, B, false, temperature, draft_tokens, K, p.st);
+        SV_TRY(launch_rowstats(ra, s));
+        SV_TRY(launch_chain_dense(ca, dense_bracket(false), s, prof.timing()));
     } else {
         ca.st = p.st;
         RowStatsArgs ra =

@@ -1078,17 +1078,17 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, false>())) void dense_wal
 
 #if SV_DENSE_TR
 template <int DT, bool VEC, bool TR>
-hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s) {
+hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s, Timing t) {
     const int C = (a.V + kDenseChunk - 1) / kDenseChunk;
     if constexpr (DT == 1 && VEC && !TR) {
         if (C <= kTabMaxChunks) {
-            hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR, true>), dim3(a.B), dim3(kThreads),
-                               static_cast<unsigned>(dense_dyn_lds(C, true)), s, a, bracket, exp_consts());
+            launch_timed(t, dense_row_kernel<DT, VEC, TR, true>, dim3(a.B), dim3(kThreads),
+                         static_cast<unsigned>(dense_dyn_lds(C, true)), s, a, bracket, exp_consts());
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((dense_row_kernel<DT, VEC, TR, false>), dim3(a.B), dim3(kThreads),
-                       static_cast<unsigned>(dense_dyn_lds(C, false)), s, a, bracket, exp_consts());
+    launch_timed(t, dense_row_kernel<DT, VEC, TR, false>, dim3(a.B), dim3(kThreads),
+                 static_cast<unsigned>(dense_dyn_lds(C, false)), s, a, bracket, exp_consts());
     return hipGetLastError();
 }
 #endif
@@ -1122,12 +1122,15 @@ hipError_t launch_chain_walk(const ChainArgs& a, double bracket, hipStream_t s, 
 #endif
 
 #if SV_DENSE_TR
-hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s) {
-    // transformed drafts only (T != 1 without top-k); T == 1 takes launch_chain_walk
+hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s, Timing t) {
     const int esz = a.dtype ? 2 : 4;
     const bool vec = vec_ok(a.logits, a.V, esz) && vec_ok(a.q, a.V, 4);
-    if (a.dtype == 1) return vec ? dense_launch<1, true, true>(a, bracket, s) : dense_launch<1, false, true>(a, bracket, s);
-    return vec ? dense_launch<0, true, true>(a, bracket, s) : dense_launch<0, false, true>(a, bracket, s);
+    if (a.transformed) {
+        if (a.dtype == 1) return vec ? dense_launch<1, true, true>(a, bracket, s, t) : dense_launch<1, false, true>(a, bracket, s, t);
+        return vec ? dense_launch<0, true, true>(a, bracket, s, t) : dense_launch<0, false, true>(a, bracket, s, t);
+    }
+    if (a.dtype == 1) return vec ? dense_launch<1, true, false>(a, bracket, s, t) : dense_launch<1, false, false>(a, bracket, s, t);
+    return vec ? dense_launch<0, true, false>(a, bracket, s, t) : dense_launch<0, false, false>(a, bracket, s, t);
 }
 #endif
 

@@ -151,7 +151,7 @@ hipError_t launch_chain_topk(const TopkChainArgs& a, hipStream_t s, Timing t = {
 hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
 // bracket: relative half-width of the brackets put around the row statistics'
 // normalisers (any value gives the same result; it sets how often the slow path runs)
-hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s);   // T != 1, statistics precomputed
+hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s, Timing t = {});   // statistics precomputed
 // T == 1 without top-k: the whole chain (row statistics of the rows the walk
 // reaches, tests, final draw) in one launch.
 hipError_t launch_chain_walk(const ChainArgs& a, double bracket, hipStream_t s, Timing t = {});

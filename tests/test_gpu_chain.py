@@ -64,6 +64,15 @@ def test_workload4_reduced_batch(R, orc):
     check(R, orc, W.config(4, 0, B=16), "c4 B=16")
 
 
+@pytest.mark.parametrize("path", ["walk", "rows"])
+def test_dense_paths(R, orc, path, monkeypatch):
+    """T = 1 without top-k: the walk and the all-rows route, each forced, on the same inputs."""
+    monkeypatch.setenv("SPEC_VERIFY_DENSE_PATH", path)
+    check(R, orc, W.config(1, 5), f"c1 via {path}")
+    check(R, orc, W.config(4, 3, B=12), f"c4 B=12 via {path}")
+    check(R, orc, W.config(0, 4, B=64), f"c0 B=64 via {path}")
+
+
 @pytest.mark.slow
 def test_workload4_full_sampled(R, orc):
     """B=512, K=8, V=128256: the full launch, checked on 48 sampled batch rows."""
@@ -113,7 +122,7 @@ def test_ties_at_topk_boundary_and_argmax(R, orc):
     check(R, orc, W.with_transform(ci, temperature=0.9, top_k=3), "ties top-3")
 
 
-def test_error_rows(R, orc):
+def test_error_rows(R, orc, monkeypatch):
     """E1-E5 as the left-to-right walk consults rows: errors in row 0 always count; an
     error in a later row counts only when the walk reaches it (position 0 forced to
     accept or to reject by construction)."""
@@ -149,8 +158,12 @@ def test_error_rows(R, orc):
     force(8, accept=False)
     q[8, 2, x[8, 2]] = np.nan        # draft entry at an untested position
     ci = dataclasses.replace(ci, logits=z, draft_probs=q, draft_tokens=x, uniforms=u)
-    for T, k in [(1.0, 0), (0.6, 0), (0.7, 8), (0.0, 0)]:
-        t, tok, alen = check(R, orc, W.with_transform(ci, temperature=T, top_k=k), f"errors T={T} k={k}")
+    for T, k, path in [(1.0, 0, "walk"), (1.0, 0, "rows"), (0.6, 0, ""), (0.7, 8, ""), (0.0, 0, "")]:
+        if path:
+            monkeypatch.setenv("SPEC_VERIFY_DENSE_PATH", path)
+        else:
+            monkeypatch.delenv("SPEC_VERIFY_DENSE_PATH", raising=False)
+        t, tok, alen = check(R, orc, W.with_transform(ci, temperature=T, top_k=k), f"errors T={T} k={k} {path}")
         assert alen[1] == -1 and alen[4] == -1
         if T != 0.0:
             assert np.all(alen[[1, 2, 3, 4, 5, 6]] == -1)
