@@ -26,10 +26,13 @@
  *   - `workspace` is device scratch of at least the size reported by the
  *     matching *_workspace_bytes function, 256-byte aligned.  It must be
  *     zero-filled before its first use (spec_workspace_init, or any zeroing
- *     allocation); every call leaves it in that reusable state (the hand-over
- *     words one call writes are cleared by the same call), so zeroing once is
- *     enough.  A workspace serves
- *     one call at a time: calls that may overlap need separate workspaces.
+ *     allocation).  A top-k chain call (temperature > 0, 0 < top_k < V)
+ *     needs the part it uses to be zero and leaves it zero (the hand-over
+ *     words one call writes are cleared by the same call), so a series of
+ *     such calls needs zeroing once.  Every other call leaves scratch data
+ *     behind: before a top-k chain call that follows a call of another kind
+ *     on the same workspace, zero it again.  A workspace serves one call at a
+ *     time: calls that may overlap need separate workspaces.
  *   - Logit rows are bfloat16 (SPEC_BF16, raw bits) or float32 (SPEC_F32).
  *     Draft probabilities are float32.  Uniforms are float32 in [0, 1).
  *   - Host-detectable argument errors return a negative code and launch
@@ -53,6 +56,11 @@
  *     Results do not depend on it; a normaliser outside its bracket only makes
  *     the draw recompute that row exactly (0 forces that path, for tests).
  *     Read on every call; unset or invalid values leave the built-in width.
+ *     SPEC_VERIFY_DENSE_PATH = walk | rows picks the route of a chain with
+ *     temperature 1 and top-k off: the walk (one workgroup per batch row reads
+ *     target rows only up to the first rejection) or every row's statistics
+ *     first; by default the walk when B*(K+1) > 1536 or V < 4096.  Results
+ *     are the same either way.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H

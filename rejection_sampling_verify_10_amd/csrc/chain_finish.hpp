@@ -10,14 +10,15 @@
 //
 // Hand-over without waiting on the producer side: a selection workgroup stores
 // its chunk list as 64 self-validating words (bit 0 set) with device-scope
-// stores and retires at once.  One finisher workgroup per batch row, placed
-// after every selection unit in the grid (so dispatched after all of them on
-// its XCD), polls the words of each position until all are valid, merges them,
-// clears them back to zero for the next call, runs test k and draws the token
-// that would be emitted if k were the first rejection.  Its waves then pick
-// the first rejection from the position records in LDS and write the row's
-// outputs.  The polls are bounded: a row whose lists never complete is
-// reported as failed instead of hanging the launch.
+// stores and retires at once.  One finisher workgroup per position (b, k),
+// placed after every selection unit in the grid (so dispatched after all of
+// them on its XCD), polls the position's words until all are valid, merges
+// them, runs test k and draws the token that would be emitted if k were the
+// first rejection, stores the position's record words and clears the list
+// words for the next call.  Wave 3 of position K's finisher polls the K+1
+// records, picks the first rejection and writes the row's outputs.  Every poll
+// is bounded: a row whose words never complete is reported as failed instead
+// of hanging the launch.
 #pragma once
 
 #include "common.hpp"
