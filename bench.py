@@ -263,17 +263,24 @@ def main() -> int:
     if not args.no_cpu_baseline:
         import oracle
         rows = min(wl["oracle_rows"], B)
+        # the sample is repeated until about 1.5 s of wall time (some 10-30 s of CPU work on
+        # the box's threads) so that the rate is stable; data generation is not timed
+        reps = 0
         t0 = time.perf_counter()
-        if tree:
-            oracle.verify_tree_greedy(ci.logits[:rows], ci.dtype, ci.node_tokens[:rows], ci.parents)
-        else:
-            oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
-                                ci.uniforms[:rows], T, top_k)
-        dt = time.perf_counter() - t0
-        cpu = {"value": rows * rows_per_step / B / dt, "unit": "token-rows/s", "cores": oracle.max_threads(),
+        while True:
+            if tree:
+                oracle.verify_tree_greedy(ci.logits[:rows], ci.dtype, ci.node_tokens[:rows], ci.parents)
+            else:
+                oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
+                                    ci.uniforms[:rows], T, top_k)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 1.5 or reps >= 200:
+                break
+        cpu = {"value": reps * rows * rows_per_step / B / dt, "unit": "token-rows/s", "cores": oracle.max_threads(),
                "kind": "oracle",
                "sample": f"first {rows} of {B} batch rows ({rows * rows_per_step // B} token-rows) of the same workload, "
-                         f"fp64 C oracle, OpenMP over batch rows, {dt:.2f} s wall"}
+                         f"{reps} passes, fp64 C oracle, OpenMP over batch rows, {dt:.2f} s wall"}
         log(f"oracle: {cpu['value']:.0f} token-rows/s on {cpu['cores']} threads")
 
     line = {
