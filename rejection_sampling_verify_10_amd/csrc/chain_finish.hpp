@@ -48,7 +48,7 @@ __device__ __forceinline__ pkey_t word_key(unsigned long long w) {
 // finisher's dispatch and the completion of the last selection unit.
 constexpr int kSpinLimit = 1 << 16;
 
-// Merges the C (<= 16) chunk lists of a row from their words (units unit0 ..
+// Merges the C (<= 64) chunk lists of a row from their words (units unit0 ..
 // unit0+C-1), polling until every word is valid.  Lane l ends with the l-th
 // ranked key of the union; returns false on a poll timeout.  flagged: some
 // chunk flagged the row.  The caller clears the words (clear_words) once it has

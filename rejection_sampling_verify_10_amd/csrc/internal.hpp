@@ -165,8 +165,10 @@ hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
 
 // Chunking of a row for the top-k selection kernel: chunks of at most
 // kChunkBytes, equal sizes rounded up to whole 16-byte vectors.
-constexpr int kChunkBytes = 64 * 1024;
+constexpr int kChunkBytes = 112 * 1024;
 constexpr int kMaxV = 1 << 20;
+static_assert((static_cast<long>(kMaxV) * 4 + kChunkBytes - 1) / kChunkBytes <= 64,
+              "a row's chunk lists are merged one count per lane");
 inline void topk_chunking(int V, int esz, int* nchunks, int* chunk_elems) {
     const int per_vec = 16 / esz;
     const long bytes = static_cast<long>(V) * esz;

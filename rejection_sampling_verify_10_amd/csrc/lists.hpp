@@ -11,10 +11,9 @@ namespace sv {
 __device__ __forceinline__ bool u_ok(float u) { return u >= 0.f && u < 1.f; }
 __device__ __forceinline__ bool q_ok(float v) { return v >= 0.f && v < INFINITY; }
 
-constexpr int kMaxRowChunks = 16;
 constexpr int kMergeBatch = 8;
 
-// Merges the C (<= 16) sorted chunk lists of a row (workspace units unit0 ..
+// Merges the C (<= 64) sorted chunk lists of a row (workspace units unit0 ..
 // unit0+C-1): lane l ends with the l-th ranked (value, index) of their union.
 // Up to kMergeBatch lists are loaded at once, every load issued before any is
 // used (a list owns all kTopkMax slots), and merged by a pairwise tree whose

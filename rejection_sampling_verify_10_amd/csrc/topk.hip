@@ -6,8 +6,9 @@
 // (z/T for logits, q^(1/T) for probabilities), so the kept set is selected on
 // the raw values and only the k survivors are ever exponentiated.
 //
-// topk_chunk_kernel: one workgroup per <= 64 KiB chunk of a target or draft row,
-// held in registers (16 x 16-byte non-temporal vectors per thread).  Per chunk:
+// topk_chunk_kernel: one workgroup per <= 112 KiB chunk of a target or draft row,
+// held in registers (28 x 16-byte non-temporal vectors per thread; three
+// workgroups per CU).  Per chunk:
 //   - Per vector, a NaN-propagating maximum (v_maximum3_f32): 1.5 VALU ops per
 //     bf16 element, 0.5 per fp32 element; the thread maximum carries NaN.
 //   - tau = the exact k-th largest of the 256 thread maxima (each wave sorts
@@ -32,10 +33,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kSlots = 16;
+constexpr int kSlots = 28;           // 16-byte vectors per thread: a chunk of up to 112 KiB
 constexpr int kCap = 1024;
 
 constexpr int kStage = kWave;             // staged (lane, vector) pairs per wave
+static_assert(kSlots * kThreads * 16 >= kChunkBytes, "a chunk fits the registers of one workgroup");
 static_assert(kWaves == kFinishWaves, "a finisher workgroup has the selection's block size");
 
 struct ChunkSmem {
@@ -328,7 +330,7 @@ __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row
 // FIN: a chain call; the grid holds B*Ub selection units followed by one
 // finisher workgroup per batch row (chain_finish.hpp).
 template <int DT, bool VEC, bool FIN>
-__global__ __launch_bounds__(kThreads, 4) void topk_chunk_kernel(TopkChainArgs fa) {
+__global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkChainArgs fa) {
     __shared__ union {
         ChunkSmem sel;
         FinishSmem fin;

@@ -64,7 +64,6 @@ def test_chain_argument_checks(L):
     assert _chain(L, K=64) == EUNSUPPORTED
     assert _chain(L, V=(1 << 20) + 1) == EUNSUPPORTED
     assert _chain(L, top_k=65, T=0.7) == EUNSUPPORTED
-    assert _chain(L, top_k=50, T=0.7, V=300000) == EUNSUPPORTED
     assert _chain(L, wsb=16) == EWORKSPACE
     assert _chain(L, ws=None) == EWORKSPACE
     assert _chain(L, ws=FAKE + 8) == EWORKSPACE
