@@ -83,6 +83,22 @@ def counter_traffic(workload: int):
     return float(m_b.group(1))
 
 
+SELECT_CHUNK_BYTES = 112 * 1024    # largest chunk of a row in the top-k selection kernel
+
+
+def select_chunks(V: int, esz: int) -> int:
+    """Chunks per row in the top-k selection: the fewest equal chunks of whole 16-byte
+    vectors that each fit SELECT_CHUNK_BYTES."""
+    per_vec = 16 // esz
+    c = max(1, -(-V * esz // SELECT_CHUNK_BYTES))
+    while True:
+        e = -(-V // c)
+        e = -(-e // per_vec) * per_vec
+        if e * esz <= SELECT_CHUNK_BYTES:
+            return -(-V // e)
+        c += 1
+
+
 def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_len=None, esz: int = 2) -> float:
     """Bytes the dominant kernel must move per launch (see the design notes).  For the tree,
     K is the node count N."""
@@ -92,7 +108,7 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
     if workload == 2:
         # every target row (bf16) and every draft row (fp32) once; per chunk a sorted list
         # of top_k (value, index) pairs plus count and flags written
-        chunks = B * (K + 1) * 4 + B * K * 8
+        chunks = B * (K + 1) * select_chunks(V, esz) + B * K * select_chunks(V, 4)
         return B * (K + 1) * V * 2 + B * K * V * 4 + chunks * (top_k * 8 + 8)
     j = [K] * B if accept_len is None else [int(a) for a in accept_len]
     if workload == 1:
