@@ -48,11 +48,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_verify_chain.argtypes = [P, I, P, P, P, I, I, I, D, I, P, P, P, P, P, P, P, P]
         L.oracle_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P]
         L.oracle_accept_rate.argtypes = [P, I, P, I, I, I, D, I, P]
+        L.oracle_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, D, I, P, P, P, P, P]
         L.oracle_target_dist.argtypes = [P, I, I, D, I, P]
         L.oracle_draft_dist.argtypes = [P, I, D, I, P]
         L.oracle_argmax_row.argtypes = [P, I, I]
         L.oracle_set_variant.argtypes = [I]
         for f in ("oracle_verify_chain", "oracle_verify_tree_greedy", "oracle_accept_rate",
+                  "oracle_verify_tree_sample",
                   "oracle_target_dist", "oracle_draft_dist", "oracle_argmax_row",
                   "oracle_max_threads"):
             getattr(L, f).restype = I
@@ -115,6 +117,35 @@ def verify_tree_greedy(logits, dtype, node_tokens, parents):
                                          _p(out["tokens"]), _p(out["accept_len"]))
     if rc != 0:
         raise ValueError(f"oracle_verify_tree_greedy rejected its arguments ({rc})")
+    return out
+
+
+def tree_depths(parents) -> np.ndarray:
+    par = np.asarray(parents, dtype=np.int64)
+    depth = np.zeros(par.shape[0], dtype=np.int64)
+    for n in range(1, par.shape[0]):
+        depth[n] = depth[par[n]] + 1
+    return depth
+
+
+def verify_tree_sample(logits, dtype, draft_probs, node_tokens, uniforms, parents, temperature, top_k):
+    """Sampling verification of a static tree (T > 0); returns path, tokens, accept_len,
+    m_test [B, N] and m_draw [B] (see spec_oracle.c)."""
+    z = _logits_arr(logits, dtype)
+    B, N, V = z.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    q = np.ascontiguousarray(draft_probs, dtype=np.float32).reshape(B, N, V)
+    tok = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(B, N)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, N)
+    D = int(tree_depths(par).max())
+    out = dict(path=np.empty((B, D + 1), np.int32), tokens=np.empty((B, D + 1), np.int32),
+               accept_len=np.empty(B, np.int32), m_test=np.empty((B, N)), m_draw=np.empty(B))
+    rc = lib().oracle_verify_tree_sample(_p(z), dtype, _p(q), _p(tok), _p(u), _p(par), B, N, V,
+                                         float(temperature), int(top_k), _p(out["path"]),
+                                         _p(out["tokens"]), _p(out["accept_len"]), _p(out["m_test"]),
+                                         _p(out["m_draw"]))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree_sample rejected its arguments ({rc})")
     return out
 
 

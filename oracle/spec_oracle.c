@@ -51,8 +51,9 @@
  *   E5 a uniform outside [0, 1) (sampling mode; all of them are checked).
  * The chain walk consults position k only when every earlier draft token was
  * accepted ([LEV] section 3): target rows 0..j and the draft rows / entries of
- * positions 0..j, j the first rejection (K if none).  Tree nodes are verified
- * together: every node row is consulted.
+ * positions 0..j, j the first rejection (K if none).  Greedy tree nodes are
+ * verified together: every node row is consulted.  The sampled tree walks from
+ * the root and consults the rows of the nodes it visits.
  */
 #include <math.h>
 #include <stdint.h>
@@ -68,7 +69,8 @@
 /* Deliberate-mistake switch used only by the tests that show the pins bite:
  * 0 = the method as stated; 1 = on rejection re-sample from p instead of the
  * residual (the "naive" variant of [LEV] section 二); 2 = bonus token drawn
- * from p_{K-1} instead of p_K; 3 = ratio written q/p instead of p/q. */
+ * from p_{K-1} instead of p_K; 3 = ratio written q/p instead of p/q;
+ * 4 = in the sampled tree, a rejected sibling leaves P as it was. */
 static int g_variant = 0;
 void oracle_set_variant(int v) { g_variant = v; }
 
@@ -441,5 +443,125 @@ int oracle_accept_rate(const void* logits, int dtype, const float* q, int B, int
             free(qq);
         }
     }
+    return 0;
+}
+
+/*
+ * Sampling verification of a static draft tree.  [EAG], the EAGLE part: with a
+ * tree of drafts, a rejected token does not end the step, the other branches
+ * are tried; [E2] section 2.1 and [LEV] section 三 give the single test
+ * (accept with probability min(1, p/q)) and the residual norm(max(0, p - q)).
+ *
+ * The pages give no rule for several branches; the reading taken here applies
+ * the chain's rule once per sibling.  At the current node c (the root first)
+ * P = p'_c, the target distribution of c's row, and Q = q'_c, the draft
+ * distribution at c from which c's children were drawn.  The children are
+ * tried in increasing node order: child n is accepted iff u[n] < min(1,
+ * P(x_n)/Q(x_n)) (the same q'=0 rule as the chain); an acceptance emits x_n and
+ * moves to n; a rejection replaces P by max(0, P - Q)/sum (P is kept when that
+ * has zero mass) and the next child is tried.  When no child is accepted, or c
+ * is a leaf, the token is drawn from P with u[0] (index-ascending inverse CDF,
+ * as in the chain).  With the children of c drawn independently from q'_c each
+ * round is one step of the chain's method, so the emitted tokens follow the
+ * target's law.
+ *
+ * Layouts: logits [B][N][V]; q [B][N][V] (row n: the draft distribution at
+ * node n; rows of leaves are never read); node_tokens [B][N] (entry 0
+ * ignored); u [B][N] (u[n], n >= 1: the test of node n; u[0]: the final draw);
+ * parents [N], parents[0] = -1, 0 <= parents[n] < n.  T > 0.
+ * Outputs: path and tokens [B][D+1] (-1 padded), accept_len [B] = depth of the
+ * last accepted node (-1 on error); m_test [B][N]: |u[n] - min(1, ratio)| for
+ * the tests performed (NaN otherwise); m_draw [B] as in the chain.
+ * Errors: E2 (every node token), E5 (every uniform), E1 for the rows of the
+ * nodes the walk visits, E3 / E4 for the draft rows it consults: the whole row
+ * when transformed or when a residual is formed, else the entries gathered.
+ */
+int oracle_verify_tree_sample(const void* logits, int dtype, const float* q, const int32_t* node_tokens,
+                              const float* u, const int32_t* parents, int B, int N, int V, double T,
+                              int top_k, int32_t* out_path, int32_t* out_tokens, int32_t* accept_len,
+                              double* m_test, double* m_draw) {
+    if (B <= 0 || N <= 0 || V <= 0 || !(T > 0.0) || isinf(T) || parents[0] != -1) return -1;
+    int D = 0;
+    int* depth = (int*)malloc(sizeof(int) * (size_t)N);
+    depth[0] = 0;
+    for (int n = 1; n < N; ++n) {
+        if (parents[n] < 0 || parents[n] >= n) { free(depth); return -1; }
+        depth[n] = depth[parents[n]] + 1;
+        if (depth[n] > D) D = depth[n];
+    }
+    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    const int transformed = !(T == 1.0 && !topk_enabled(top_k, V));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        const char* zb = (const char*)logits + (size_t)b * N * V * esz;
+        const float* qb = q + (size_t)b * N * V;
+        const int32_t* tk = node_tokens + (size_t)b * N;
+        const float* ub = u + (size_t)b * N;
+        int32_t* op = out_path + (size_t)b * (D + 1);
+        int32_t* ot = out_tokens + (size_t)b * (D + 1);
+        double* mt = m_test + (size_t)b * N;
+        for (int d = 0; d <= D; ++d) { op[d] = -1; ot[d] = -1; }
+        for (int n = 0; n < N; ++n) mt[n] = NAN;
+        accept_len[b] = -1;
+        m_draw[b] = NAN;
+        int err = 0;
+        for (int n = 1; n < N; ++n) if (tk[n] < 0 || tk[n] >= V) err = 1;        /* E2 */
+        for (int n = 0; n < N; ++n) if (!u_ok(ub[n])) err = 1;                    /* E5 */
+        if (err) continue;
+        double* P = (double*)malloc(sizeof(double) * (size_t)V);
+        double* Q = (double*)malloc(sizeof(double) * (size_t)V);
+        int c = 0, d = 0;
+        op[0] = 0;
+        for (;;) {
+            if (oracle_target_dist(zb + (size_t)c * V * esz, dtype, V, T, top_k, P)) { err = 1; break; }  /* E1 */
+            const float* qrow = qb + (size_t)c * V;
+            int accepted = -1, have_q = 0;
+            for (int n = c + 1; n < N && !err; ++n) {
+                if (parents[n] != c) continue;
+                if (!have_q && transformed) {
+                    if (oracle_draft_dist(qrow, V, T, top_k, Q)) { err = 1; break; }       /* E3, E4 */
+                    have_q = 1;
+                }
+                const int x = tk[n];
+                if (!have_q && !q_ok(qrow[x])) { err = 1; break; }                           /* E3 */
+                const double a = P[x], cq = have_q ? Q[x] : (double)qrow[x];
+                double ratio;
+                if (cq > 0.0) ratio = a / cq;
+                else ratio = a > 0.0 ? INFINITY : 0.0;
+                const double thr = ratio < 1.0 ? ratio : 1.0;
+                mt[n] = fabs((double)ub[n] - thr);
+                if ((double)ub[n] < thr) { accepted = n; break; }
+                if (g_variant == 4) continue;   /* planted mistake: the next sibling sees P again */
+                /* Rejected: the next sibling (or the final draw) sees the residual. */
+                if (!have_q) {
+                    for (int i = 0; i < V; ++i) if (!q_ok(qrow[i])) err = 1;                 /* E3 */
+                    if (err) break;
+                    for (int i = 0; i < V; ++i) Q[i] = (double)qrow[i];
+                    have_q = 1;
+                }
+                double S = 0.0;
+                for (int i = 0; i < V; ++i) { const double r = P[i] - Q[i]; S += r > 0.0 ? r : 0.0; }
+                if (S > 0.0)                                                                 /* [P10] */
+                    for (int i = 0; i < V; ++i) { const double r = P[i] - Q[i]; P[i] = (r > 0.0 ? r : 0.0) / S; }
+            }
+            if (err || accepted < 0) break;
+            ot[d] = tk[accepted];
+            c = accepted;
+            op[++d] = c;
+        }
+        if (!err) {
+            double S = 0.0, md;
+            for (int i = 0; i < V; ++i) S += P[i];
+            ot[d] = draw_index(P, V, S, (double)ub[0], &md);
+            accept_len[b] = d;
+            m_draw[b] = md;
+        } else {
+            for (int t = 0; t <= D; ++t) { op[t] = -1; ot[t] = -1; }
+            for (int n = 0; n < N; ++n) mt[n] = NAN;
+        }
+        free(P);
+        free(Q);
+    }
+    free(depth);
     return 0;
 }

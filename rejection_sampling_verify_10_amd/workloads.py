@@ -30,6 +30,13 @@ Trees (greedy verification) draw, per batch row: a permutation and noise
 for each of the N node rows as above, draft noise per node row, and give the
 children of node ``p`` the best draft tokens of ``zd_p`` in sibling order.
 
+Sampled trees draw, per batch row: target rows and draft noise for the N
+nodes as above, the draft probabilities ``q_n = softmax(zd_n)`` of every node
+(row ``n`` is the draft model's distribution at node ``n``, from which its
+children are drawn), then for each node ``p`` in order its children's tokens,
+independently, from the draft model's sampling distribution at ``p`` (step
+5), and last the N verification uniforms.
+
 The value distribution follows the workloads described for the method: a
 Zipf-like ``-1.1*ln(rank)`` prior plus Gaussian spread gives a long-tailed
 next-token distribution, and the draft is the same distribution seen through
@@ -212,7 +219,61 @@ def make_tree(B: int, V: int, *, parents: np.ndarray = EAGLE_TREE_PARENTS, dtype
     return TreeInputs(B, N, V, dtype, logits, tok, parents)
 
 
-# The five workloads, by index.  Each entry builds inputs for a seed, with
+@dataclasses.dataclass
+class SampledTreeInputs:
+    """Inputs of one batched sampling tree verification call."""
+    B: int
+    N: int
+    V: int
+    dtype: int
+    temperature: float
+    top_k: int
+    logits: np.ndarray         # [B, N, V] uint16 (bf16 bits) or float32
+    draft_probs: np.ndarray    # [B, N, V] float32, row n: the draft distribution at node n
+    node_tokens: np.ndarray    # [B, N] int32 (entry 0, the root, is -1)
+    uniforms: np.ndarray       # [B, N] float32: u[n] tests node n, u[0] drives the final draw
+    parents: np.ndarray        # [N] int32
+
+    def logits_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.logits) if self.dtype == DTYPE_BF16 else self.logits
+
+
+def make_tree_sampled(B: int, V: int, *, parents: np.ndarray = EAGLE_TREE_PARENTS, dtype: int = DTYPE_BF16,
+                      temperature: float = 1.0, top_k: int = 0, sigma: float = 0.5, config_id: int,
+                      seed: int, threads: Optional[int] = None) -> SampledTreeInputs:
+    """Draw one sampling tree-verification input set (children drawn independently from
+    the draft model's distribution at their parent)."""
+    parents = np.ascontiguousarray(parents, dtype=np.int32)
+    N = parents.shape[0]
+    log_rank = _log_rank_table(V)
+    logits = np.empty((B, N, V), dtype=np.uint16 if dtype == DTYPE_BF16 else np.float32)
+    q = np.empty((B, N, V), dtype=np.float32)
+    tok = np.full((B, N), -1, dtype=np.int32)
+    u = np.empty((B, N), dtype=np.float32)
+    children = [[c for c in range(N) if parents[c] == p] for p in range(N)]
+
+    def one(b: int) -> None:
+        rng = np.random.default_rng([config_id, seed, b])
+        z = _target_rows(rng, N, V, log_rank)
+        nd = rng.standard_normal((N, V), dtype=np.float32)
+        zd = z.astype(np.float64) + sigma * nd.astype(np.float64)
+        q[b] = _softmax64(zd).astype(np.float32)
+        for p in range(N):
+            if not children[p]:
+                continue
+            cdf = _draft_sampler_cdf(zd[p], temperature, top_k)
+            ud = rng.random(len(children[p]))
+            for r, c in enumerate(children[p]):
+                tok[b, c] = min(int(np.searchsorted(cdf, ud[r] * cdf[-1], side="right")), V - 1)
+        u[b] = rng.random(N, dtype=np.float32)
+        logits[b] = f32_to_bf16_bits(z) if dtype == DTYPE_BF16 else z
+
+    with ThreadPoolExecutor(threads or _workers()) as ex:
+        list(ex.map(one, range(B)))
+    return SampledTreeInputs(B, N, V, dtype, float(temperature), int(top_k), logits, q, tok, u, parents)
+
+
+# The workloads, by index.  Each entry builds inputs for a seed, with
 # optional size overrides used by the smaller parity cases.
 CONFIG_NAMES = {
     0: "chain B=1 K=4 V=1000 fp32 T=1",
@@ -220,12 +281,13 @@ CONFIG_NAMES = {
     2: "chain B=64 K=7 V=128256 bf16 T=0.7 top_k=50",
     3: "tree-greedy B=32 N=27 V=32000 bf16",
     4: "chain B=512 K=8 V=128256 bf16 T=1",
+    5: "tree-sample B=32 N=27 V=32000 bf16 T=1",
 }
 
 
 def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int] = None,
            V: Optional[int] = None, threads: Optional[int] = None):
-    """Inputs for workload ``cid`` (0..4), optionally with smaller B/K/V."""
+    """Inputs for workload ``cid`` (0..5), optionally with smaller B/K/V."""
     if cid == 0:
         return make_chain(B or 1, K or 4, V or 1000, dtype=DTYPE_F32, temperature=1.0, top_k=0,
                           sigma=sigma_const(0.5), config_id=0, seed=seed, threads=threads)
@@ -241,6 +303,9 @@ def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int]
     if cid == 4:
         return make_chain(B or 512, K or 8, V or 128256, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
                           sigma=sigma_uniform(0.2, 1.5), config_id=4, seed=seed, threads=threads)
+    if cid == 5:
+        return make_tree_sampled(B or 32, V or 32000, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
+                                 sigma=0.5, config_id=5, seed=seed, threads=threads)
     raise ValueError(f"unknown workload {cid}")
 
 
