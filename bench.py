@@ -50,6 +50,9 @@ WORKLOADS = {
             kernel="rowstats_kernel", copies=10, oracle_rows=32, dtype="bf16 in, exact argmax"),
     4: dict(name="chain verify B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
             kernel="dense_walk_kernel", copies=1, oracle_rows=32, dtype="bf16 in, f32 exp, f64 draw"),
+    5: dict(name="sampled static-tree verify B=32 N=27 (depth 5) V=32000, bf16 target logits, fp32 draft probs, "
+                 "T=1, no top-k",
+            kernel="tree_sample_kernel", copies=4, oracle_rows=32, dtype="bf16 in, f64 probabilities"),
 }
 
 
@@ -99,9 +102,40 @@ def select_chunks(V: int, esz: int) -> int:
         c += 1
 
 
-def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_len=None, esz: int = 2) -> float:
-    """Bytes the dominant kernel must move per launch (see the design notes).  For the tree,
+def tree_walk_rows(path, parents):
+    """Rows the sampled-tree walk reads from memory: per batch row, the target rows of the
+    nodes it visits and the draft rows of the visited nodes where a residual was formed (a
+    child other than the first accepted, or every child rejected)."""
+    first = {}
+    for n in range(1, len(parents)):
+        first.setdefault(int(parents[n]), n)
+    targets = drafts = tests = 0
+    for row in path:
+        nodes = [int(n) for n in row if n >= 0]
+        if not nodes:
+            continue
+        targets += len(nodes)
+        for i, c in enumerate(nodes):
+            if c not in first:
+                continue
+            nxt = nodes[i + 1] if i + 1 < len(nodes) else None
+            drafts += nxt != first[c]
+            kids = [n for n in range(1, len(parents)) if parents[n] == c]
+            tests += len(kids) if nxt is None else kids.index(nxt) + 1
+    return targets, drafts, tests
+
+
+def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_len=None, esz: int = 2,
+                      tree_path=None, parents=None) -> float:
+    """Bytes the dominant kernel must move per launch (see the design notes).  For the trees,
     K is the node count N."""
+    if workload == 5:
+        # the walk: each visited node's target row once, the draft row of each visited node
+        # where a residual was formed, z[x] and q[x] of every child tested, the tokens and
+        # uniforms read and the outputs written
+        targets, drafts, tests = tree_walk_rows(tree_path, parents)
+        D1 = tree_path.shape[1]
+        return targets * V * esz + drafts * V * 4 + tests * (esz + 4) + B * (K * 8 + D1 * 8 + 4)
     if workload == 3:
         # the row statistics: every node row once, argmax and flags written
         return B * K * V * esz + B * K * 12
@@ -196,6 +230,7 @@ def main() -> int:
     t0 = time.time()
     ci = W.config(args.workload, seed=args.seed)
     tree = args.workload == 3
+    sampled_tree = args.workload == 5
     log(f"workload {args.workload}: {wl['name']} (inputs drawn in {time.time() - t0:.1f} s)")
 
     def to_dev(a):
@@ -217,6 +252,18 @@ def main() -> int:
         ws = R.new_workspace(R.tree_workspace_bytes(B, K, V, ci.dtype), dev)
         parents = ci.parents.tolist()
         rows_per_step = B * K                  # node rows verified
+    elif sampled_tree:
+        B, K, V, T, top_k = ci.B, ci.N, ci.V, ci.temperature, ci.top_k
+        depth = [0] * K
+        for n in range(1, K):
+            depth[n] = depth[int(ci.parents[n])] + 1
+        D = max(depth)
+        base = [to_dev(ci.logits), to_dev(ci.draft_probs), to_dev(ci.node_tokens), to_dev(ci.uniforms)]
+        tok = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        parents = ci.parents.tolist()
+        rows_per_step = B * K                  # node rows verified
     else:
         B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
         base = [to_dev(ci.logits), to_dev(ci.draft_probs), to_dev(ci.draft_tokens), to_dev(ci.uniforms)]
@@ -232,6 +279,9 @@ def main() -> int:
         if tree:
             z, nt = sets[i % len(sets)]
             R.verify_tree_greedy(z, nt, parents, out=(path, tok, alen), workspace=ws)
+        elif sampled_tree:
+            z, q, nt, u = sets[i % len(sets)]
+            R.verify_tree_sample(z, q, nt, u, parents, T, top_k, out=(path, tok, alen))
         else:
             z, q, x, u = sets[i % len(sets)]
             R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
@@ -265,12 +315,13 @@ def main() -> int:
     k_ms = sum(a.elapsed_time(b) for a, b in zip(kstart, kstop)) / args.steps
     value = rows_per_step / (ms_step * 1e-3)
     al = alen.cpu().numpy()
-    alg = algorithmic_bytes(args.workload, B, K, V, top_k, al, esz)
+    alg = algorithmic_bytes(args.workload, B, K, V, top_k, al, esz,
+                            path.cpu().numpy() if sampled_tree else None, ci.parents if sampled_tree else None)
     achieved = alg / (k_ms * 1e-3) / 1e9
     step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak); accept_len histogram "
-        f"{np.bincount(al[al >= 0], minlength=(K + 1) if not tree else 1).tolist()}")
+        f"{np.bincount(al[al >= 0], minlength=(K + 1) if not (tree or sampled_tree) else 1).tolist()}")
     traffic = counter_traffic(args.workload)
     probe = read_probe_gbps(R, torch, dev)
     log(f"read probe {probe:.0f} GB/s; {wl['kernel']} at {100 * achieved / probe:.1f}% of it")
@@ -286,6 +337,9 @@ def main() -> int:
         while True:
             if tree:
                 oracle.verify_tree_greedy(ci.logits[:rows], ci.dtype, ci.node_tokens[:rows], ci.parents)
+            elif sampled_tree:
+                oracle.verify_tree_sample(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.node_tokens[:rows],
+                                          ci.uniforms[:rows], ci.parents, T, top_k)
             else:
                 oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
                                     ci.uniforms[:rows], T, top_k)
@@ -314,6 +368,8 @@ def main() -> int:
         "data": "synthetic",
         "config": ({"workload": wl["name"], "B": B, "N": K, "V": V, "input_copies": wl["copies"],
                     "parallelism": "single GPU"} if tree else
+                   {"workload": wl["name"], "B": B, "N": K, "V": V, "temperature": T, "top_k": top_k,
+                    "input_copies": wl["copies"], "parallelism": "single GPU"} if sampled_tree else
                    {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
                     "input_copies": wl["copies"], "parallelism": "single GPU"}),
         "step_algorithmic_GBps": step_alg_gbs,

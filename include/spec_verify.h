@@ -49,7 +49,8 @@
  *     (the left-to-right walk of the method): target rows 0..j, and for the
  *     draft, q[x_k] for k <= j (T == 1, no top-k) or whole rows 0..j (any
  *     other transform), plus row j itself for a residual draw; j = first
- *     rejection (K if none).  A tree consults every node row.
+ *     rejection (K if none).  A greedy tree consults every node row; a
+ *     sampled tree the rows of the nodes its walk visits.
  *   - Environment: SPEC_VERIFY_DENSE_BRACKET (a number in [0, 0.5)) sets the
  *     relative width of the bracket the dense final draw (temperature > 0,
  *     top-k off) puts around the normalisers taken from its row statistics.
@@ -164,6 +165,50 @@ int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype,
                             int B, int N, int V,
                             int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * spec_verify_tree_sample -- sampling verification of a static draft tree
+ * ("投机解码与 EAGLE", the EAGLE part: a rejected branch makes the verifier try
+ * the others; "064 · 投机解码", section 三, and "EAGLE-2: Faster Inference of
+ * Language Models with Dynamic Draft Trees", section 2.1, for the single test
+ * and the residual).
+ *
+ * Tree layout as in spec_verify_tree_greedy.  Row n of the logits is the
+ * target's distribution after the path to node n; row n of draft_probs is the
+ * draft model's distribution at node n, from which node n's children were
+ * drawn (independently of one another; rows of leaves are not read).
+ * p'_n and q'_n carry the temperature as in spec_verify_chain (T == 1: q as
+ * given).  For each batch row, from the root c = 0 with P = p'_c and Q = q'_c:
+ * the children of c are tried in increasing node order; child n is accepted
+ * iff u[n] < min(1, P(x_n)/Q(x_n)) (Q = 0 accepts iff P > 0), which emits x_n
+ * and moves to n; a rejection replaces P by max(0, P - Q)/S, S its mass (P is
+ * kept when S = 0), and the next child is tried.  When no child is accepted,
+ * or c is a leaf, a token is drawn from P with u[0] (index-ascending inverse
+ * CDF: the first y with u[0]*sum P < prefix_y, as in spec_verify_chain).
+ * This reading (the pages give no rule for several branches) keeps the
+ * emitted tokens distributed as the target's when children are independent
+ * draws from q'.  Computed in fp64.  The walk consults the target rows of the
+ * nodes it visits and, for a visited node with children, its draft row:
+ * q[x_n] of the tested children (T == 1), the whole row when T != 1 or once a
+ * residual is formed (E1, E3, E4); E2 and E5 cover every token and uniform.
+ *
+ *   target_logits [B][N][V]    dtype                   device, read
+ *   draft_probs   [B][N][V]    float32                 device, read
+ *   node_tokens   [B][N]       int32                   device, read ([b][0] ignored)
+ *   uniforms      [B][N]       float32                 device, read (u[n]: node n's test; u[0]: the draw)
+ *   parents_host  [N]          int32                   HOST, read during the call only
+ *   temperature   > 0 (greedy trees: spec_verify_tree_greedy); top_k must be
+ *                 off (<= 0 or >= V) in this build, else SPEC_EUNSUPPORTED
+ *   out_path      [B][D+1]     int32                   device, written: node ids root..last accepted, then -1
+ *   out_tokens    [B][D+1]     int32                   device, written: accepted tokens, the drawn one, then -1
+ *   out_accept_len[B]          int32                   device, written: depth reached, -1 on error
+ * Needs no workspace.
+ */
+int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                            const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
+                            int B, int N, int V, float temperature, int top_k,
+                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len,
+                            void* hip_stream);
 
 /*
  * spec_accept_rate -- alpha[b][k] = sum_i min(p'_k(i), q'_k(i)) for k < K, with

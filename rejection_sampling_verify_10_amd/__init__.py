@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_chain.restype = I
         L.spec_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, Z, P]
         L.spec_verify_tree_greedy.restype = I
+        L.spec_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P]
+        L.spec_verify_tree_sample.restype = I
         L.spec_accept_rate.argtypes = [P, I, P, I, I, I, F, I, P, P, Z, P]
         L.spec_accept_rate.restype = I
         L.spec_profile_events.argtypes = [P, P]
@@ -211,6 +213,50 @@ def verify_tree_greedy(target_logits: torch.Tensor, node_tokens: torch.Tensor, p
                                        _dev(node_tokens, "node_tokens", torch.int32), par, B, N, V,
                                        path.data_ptr(), toks.data_ptr(), alen.data_ptr(), wp, need, _stream(dev))
     _check(rc, "spec_verify_tree_greedy")
+    return path, toks, alen
+
+
+def verify_tree_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor, node_tokens: torch.Tensor,
+                       uniforms: torch.Tensor, parents: Sequence[int], temperature: float = 1.0, top_k: int = 0,
+                       *, out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """Sampling static-tree verification (``spec_verify_tree_sample``).
+
+    target_logits [B, N, V] bf16/f32, draft_probs [B, N, V] f32 (row n: the draft
+    distribution at node n), node_tokens [B, N] int32, uniforms [B, N] f32 (u[n] tests
+    node n, u[0] drives the final draw), parents: N host ints.  Returns (path [B, D+1],
+    tokens [B, D+1], accept_len [B]) int32 tensors; ``out`` reuses output tensors.
+    """
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    _shape(draft_probs, "draft_probs", (B, N, V))
+    _shape(node_tokens, "node_tokens", (B, N))
+    _shape(uniforms, "uniforms", (B, N))
+    if len(parents) != N:
+        raise ValueError(f"parents must have {N} entries")
+    par = (ctypes.c_int32 * N)(*[int(p) for p in parents])
+    depth = [0] * N
+    for n in range(1, N):
+        depth[n] = depth[int(parents[n])] + 1 if 0 <= int(parents[n]) < n else 0
+    D = max(depth)
+    if out is None:
+        path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        toks = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        path, toks, alen = out
+        _shape(path, "out path", (B, D + 1))
+        _shape(toks, "out tokens", (B, D + 1))
+        _shape(alen, "out accept_len", (B,))
+        for o, n in ((path, "out path"), (toks, "out tokens"), (alen, "out accept_len")):
+            _dev(o, n, torch.int32)
+    rc = lib().spec_verify_tree_sample(_dev(target_logits, "target_logits"), code,
+                                       _dev(draft_probs, "draft_probs", torch.float32),
+                                       _dev(node_tokens, "node_tokens", torch.int32),
+                                       _dev(uniforms, "uniforms", torch.float32), par, B, N, V,
+                                       float(temperature), int(top_k), path.data_ptr(), toks.data_ptr(),
+                                       alen.data_ptr(), _stream(dev))
+    _check(rc, "spec_verify_tree_sample")
     return path, toks, alen
 
 

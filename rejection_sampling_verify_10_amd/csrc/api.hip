@@ -396,6 +396,59 @@ int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype, const
     return SPEC_OK;
 }
 
+int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                            const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
+                            int B, int N, int V, float temperature, int top_k, int32_t* out_path,
+                            int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream) {
+    if (!target_logits || !draft_probs || !node_tokens || !uniforms || !parents_host || !out_path ||
+        !out_tokens || !out_accept_len)
+        return SPEC_EINVAL;
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EINVAL;
+    if (B < 1 || N < 1 || V < 1 || !(temperature > 0.f) || isinf(temperature)) return SPEC_EINVAL;
+    if (N > SPEC_MAX_NODES || V > SPEC_MAX_V || topk_active(top_k, V)) return SPEC_EUNSUPPORTED;
+    if (!aligned(target_logits, esz_of(dtype)) || !aligned(draft_probs, 4) || !aligned(node_tokens, 4) ||
+        !aligned(uniforms, 4) || !aligned(out_path, 4) || !aligned(out_tokens, 4) || !aligned(out_accept_len, 4))
+        return SPEC_EINVAL;
+    if (parents_host[0] != -1) return SPEC_EINVAL;
+    TreeSampleArgs ta{};
+    int depth[SPEC_MAX_NODES];
+    int last_child[SPEC_MAX_NODES];
+    depth[0] = 0;
+    int D = 0;
+    for (int n = 0; n < N; ++n) {
+        ta.first_child[n] = -1;
+        ta.next_sibling[n] = -1;
+        last_child[n] = -1;
+    }
+    for (int n = 1; n < N; ++n) {
+        const int p = parents_host[n];
+        if (p < 0 || p >= n) return SPEC_EINVAL;
+        depth[n] = depth[p] + 1;
+        if (depth[n] > D) D = depth[n];
+        // children are appended in increasing node order
+        if (last_child[p] < 0) ta.first_child[p] = static_cast<int8_t>(n);
+        else ta.next_sibling[last_child[p]] = static_cast<int8_t>(n);
+        last_child[p] = n;
+    }
+    ta.logits = target_logits;
+    ta.dtype = dtype;
+    ta.q = draft_probs;
+    ta.node_tokens = node_tokens;
+    ta.u = uniforms;
+    ta.B = B;
+    ta.N = N;
+    ta.V = V;
+    ta.D = D;
+    ta.invT = 1.0 / static_cast<double>(temperature);
+    ta.transformed = temperature != 1.f ? 1 : 0;
+    ta.out_path = out_path;
+    ta.out_tokens = out_tokens;
+    ta.out_accept_len = out_accept_len;
+    ProfileScope prof;
+    SV_TRY(launch_tree_sample(ta, static_cast<hipStream_t>(hip_stream), prof.timing()));
+    return SPEC_OK;
+}
+
 int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float* draft_probs, int B, int K,
                      int V, float temperature, int top_k, float* out_alpha, void* workspace,
                      size_t workspace_bytes, void* hip_stream) {

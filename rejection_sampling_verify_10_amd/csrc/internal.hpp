@@ -121,6 +121,25 @@ struct TreeArgs {
     int32_t* out_accept_len;
 };
 
+// Sampling verification of a static tree (tree_sample.hip): one workgroup per
+// batch row.  Children of a node, in increasing node order, are linked by
+// first_child / next_sibling (-1 ends a list).
+struct TreeSampleArgs {
+    const void* logits;     // [B][N][V] (dtype)
+    int dtype;
+    const float* q;         // [B][N][V]: row n = the draft distribution at node n
+    const int32_t* node_tokens;   // [B][N]
+    const float* u;         // [B][N]: u[n] tests node n, u[0] drives the final draw
+    int B, N, V, D;
+    double invT;
+    int transformed;        // T != 1: q'(v) = q_v^(1/T) / sum
+    int8_t first_child[64];
+    int8_t next_sibling[64];
+    int32_t* out_path;
+    int32_t* out_tokens;
+    int32_t* out_accept_len;
+};
+
 struct AlphaArgs {
     const void* logits;
     int dtype;
@@ -157,6 +176,7 @@ hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s,
 hipError_t launch_chain_walk(const ChainArgs& a, double bracket, hipStream_t s, Timing t = {});
 hipError_t launch_chain_greedy(const ChainArgs& a, hipStream_t s);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t s);
+hipError_t launch_tree_sample(const TreeSampleArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_alpha_greedy(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);

@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_symbols_exported(L):
     names = declared_functions()
-    assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_accept_rate"} <= set(names)
+    assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_tree_sample",
+            "spec_accept_rate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -80,6 +81,24 @@ def test_tree_argument_checks(L):
     assert call(bad2) == EINVAL
     assert call(par, B=0) == EINVAL
     assert call(par, wsb=8) == EWORKSPACE
+    big = (ctypes.c_int32 * 65)(*([-1] + list(range(64))))
+    assert call(big, N=65) == EUNSUPPORTED
+
+
+def test_tree_sample_argument_checks(L):
+    par = (ctypes.c_int32 * 4)(-1, 0, 0, 1)
+    bad = (ctypes.c_int32 * 4)(-1, 0, 3, 1)
+
+    def call(p=par, N=4, B=2, V=1000, T=1.0, top_k=0, q=FAKE, u=FAKE):
+        return L.spec_verify_tree_sample(FAKE, 1, q, FAKE, u, p, B, N, V, T, top_k, FAKE, FAKE, FAKE, None)
+    assert call(bad) == EINVAL
+    assert call(B=0) == EINVAL
+    assert call(T=0.0) == EINVAL                            # greedy trees have their own entry point
+    assert call(T=float("nan")) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(u=None) == EINVAL
+    assert call(top_k=50) == EUNSUPPORTED
+    assert call(V=(1 << 20) + 1) == EUNSUPPORTED
     big = (ctypes.c_int32 * 65)(*([-1] + list(range(64))))
     assert call(big, N=65) == EUNSUPPORTED
 
