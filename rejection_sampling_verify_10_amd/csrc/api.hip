@@ -416,6 +416,7 @@ int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const
     depth[0] = 0;
     int D = 0;
     for (int n = 0; n < N; ++n) {
+        ta.parent[n] = static_cast<int8_t>(parents_host[n] < 0 ? -1 : parents_host[n]);
         ta.first_child[n] = -1;
         ta.next_sibling[n] = -1;
         last_child[n] = -1;

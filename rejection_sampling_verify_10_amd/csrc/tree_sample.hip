@@ -17,16 +17,23 @@
 // prefix of P exceeds u[0]*sum P (rounding fallback: the last index with
 // P > 0).
 //
-// Every probability is fp64 (a draw over a wide distribution needs every weight
-// to fp64 accuracy).  The passes over a row recompute P(v) from the logit
-// (one table-driven fp64 exponential: the bf16 logits of a row take few
-// distinct values, looked up in an LDS table built per node) and the chain of
-// residual normalisers, instead of storing intermediate rows: the only
-// memory traffic is the rows themselves, re-read from L2 after the first pass.
-// Passes at node c: the row maximum (and E1 flags), the normalisers Z (and Sq
-// when the draft is transformed), one pass per rejected sibling (its S), and
-// for the final draw one pass of per-segment sums plus the rescan of the
-// segment that holds u*S.
+// Two precisions.  The tests along the walk take fp32 probabilities (one
+// v_exp_f32 per element, sums accumulated in fp64), as the chain's ratio tests
+// do: a test's outcome moves only where u lies within ~1e-6 of its threshold.
+// The final draw needs every weight to fp64 accuracy (a boundary of the inverse
+// CDF lies within 1e-5 of u*S for a good share of draws over a wide
+// distribution), so at the node where the walk stops the normalisers and the
+// residual masses are recomputed in fp64 (bf16 logits: one LDS table lookup of
+// an fp64 exponential per element), the last of those passes also leaving the
+// per-segment sums of the draw's weights; the draw then rescans one
+// 512-element segment.
+//
+// Rows.  A logit row of at most 64 KiB is copied into LDS when the walk
+// reaches its node (every load issued at once) and every pass reads it from
+// there; while a node is being tested, its first child's row -- the likeliest
+// next node -- is loaded into registers and parked in a second LDS buffer.
+// The draft row is streamed, each tile's loads issued one tile ahead.  Longer
+// rows are streamed (from L2 after the first pass).
 
 #include <math.h>
 
@@ -45,20 +52,27 @@ constexpr int kTsTile = 8 * kTsThreads;                     // elements per tile
 constexpr int kTsMaxTiles = (kMaxV + kTsTile - 1) / kTsTile;
 constexpr int kTsParts = kTsMaxTiles * kTsWaves;            // one 512-element segment per (tile, wave)
 constexpr int kTsMaxNodes = 64;
+constexpr int kTsRowBytes = 64 * 1024;                      // largest LDS-held logit row
+constexpr int kTsRowVecs = kTsRowBytes / 16 / kTsThreads;   // its 16-byte vectors per thread
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct TsSmem {
     double tbl[kTableSize];          // 2^(k/256) for the fp64 exponential
-    double part[kTsParts];           // segment sums of the draw pass, in index order
+    double part[kTsParts];           // segment sums of the draw's weights, in index order
     double red[kTsWaves];
     float fred[kTsWaves];
     int ired[kTsWaves];
-    double sinv[kTsMaxNodes];        // 1/S of each rejection at the current node (1 when kept)
-    int kept[kTsMaxNodes];           // 1: that rejection left P as it was (S = 0)
+    float sinv32[kTsMaxNodes];       // walk (fp32): 1/S of each rejection at the current node
+    int kept32[kTsMaxNodes];         //   1: that rejection left P as it was (S = 0)
+    double sinv[kTsMaxNodes];        // final node (fp64): the same
+    int kept[kTsMaxNodes];
     int path[kTsMaxNodes];
     int toks[kTsMaxNodes];
+    float gz[kTsMaxNodes];           // z[x_n] and q[x_n] of the current node's children n
+    float gq[kTsMaxNodes];
     int dec;                         // thread 0's decision: 0 reject, 1 accept, 2 error
     int seg;                         // draw: segment holding u*S, -1 for the fallback
-    double base;                     // draw: mass before that segment
+    double base;                     // draw: weight before that segment
 };
 
 // Eight consecutive logits from i0 (a multiple of 8), widened; -inf past V.
@@ -139,18 +153,112 @@ __device__ __forceinline__ int ts_block_max(int v, TsSmem& sm) {
     return t;
 }
 
-// Everything a pass needs to turn one (logit, draft probability) pair into the
-// current P(v) and Q(v).
+// The current node's logit row: from an LDS copy (LROW) or streamed.
+template <int DT, bool VEC, bool LROW>
+struct NodeRow {
+    static constexpr bool kVec = VEC;
+    const u32x4* zs;      // LDS copy (LROW)
+    const char* zr;
+    const float* qr;
+    int V;
+
+    __device__ __forceinline__ void get_z(int t, float out[8]) const {
+        const int i0 = t * kTsTile + 8 * static_cast<int>(threadIdx.x);
+        if constexpr (LROW) {
+            if (i0 >= V) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[e] = -INFINITY;
+                return;
+            }
+            if (DT == 1) {
+                const u32x4 v = zs[i0 / 8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[e] = Elem<1>::get(v, e);
+            } else {
+                const u32x4 v0 = zs[i0 / 4], v1 = zs[i0 / 4 + 1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { out[e] = __uint_as_float(v0[e]); out[4 + e] = __uint_as_float(v1[e]); }
+            }
+        } else {
+            ts_load_z<DT, VEC>(zr, i0, V, out);
+        }
+    }
+};
+
+// A row of at most kTsRowBytes (nvec 16-byte vectors): thread t's vectors t,
+// t + 1024, ... are loaded into v, then stored to an LDS buffer.
+__device__ __forceinline__ void row_issue(const char* row, int nvec, u32x4 (&v)[kTsRowVecs]) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+    for (int k = 0; k < kTsRowVecs; ++k) {
+        const int j = k * kTsThreads + static_cast<int>(threadIdx.x);
+        v[k] = p[j < nvec ? j : 0];
+    }
+}
+__device__ __forceinline__ void row_park(u32x4* dst, int nvec, const u32x4 (&v)[kTsRowVecs]) {
+#pragma unroll
+    for (int k = 0; k < kTsRowVecs; ++k) {
+        const int j = k * kTsThreads + static_cast<int>(threadIdx.x);
+        if (j < nvec) dst[j] = v[k];
+    }
+}
+
+// f(t, i0, z[8], q[8]) over the tiles in index order (q only when with_q).
+template <class Row, class F>
+__device__ __forceinline__ void for_tiles(const Row& r, int ntiles, bool with_q, F&& f) {
+    const int lo = 8 * static_cast<int>(threadIdx.x);
+    if constexpr (!Row::kVec) {
+        for (int t = 0; t < ntiles; ++t) {
+            const int i0 = t * kTsTile + lo;
+            float z[8], q[8];
+            if (with_q) ts_load_q<false>(r.qr, i0, r.V, q);
+            r.get_z(t, z);
+            f(t, i0, z, q);
+        }
+        return;
+    }
+    float qn[8];
+    if (with_q) ts_load_q<true>(r.qr, lo, r.V, qn);
+    for (int t = 0; t < ntiles; ++t) {
+        const int i0 = t * kTsTile + lo;
+        float z[8], q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = qn[e];
+        if (with_q && t + 1 < ntiles) ts_load_q<true>(r.qr, i0 + kTsTile, r.V, qn);
+        r.get_z(t, z);
+        f(t, i0, z, q);
+    }
+}
+
+// The walk's fp32 view of the current node.
+template <bool TR>
+struct Dist32 {
+    float m, k32;          // row maximum, log2(e)/T
+    float invT;
+    float invZ, invSq;
+    const float* sinv;
+    const int* kept;
+    __device__ __forceinline__ float e_of(float z) const { return __builtin_amdgcn_exp2f((z - m) * k32); }
+    __device__ __forceinline__ float w_of(float q) const {
+        if (!TR) return q;
+        return q > 0.f ? __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(q) * invT) : 0.f;
+    }
+    __device__ __forceinline__ float Q_of(float q) const { return TR ? w_of(q) * invSq : q; }
+    __device__ __forceinline__ float P_of(float e, float Q, int upto) const {
+        float P = e * invZ;
+        for (int j = 0; j < upto; ++j) P = kept[j] ? P : fmaxf(P - Q, 0.f) * sinv[j];
+        return P;
+    }
+};
+
+// The final node's fp64 view.
 template <int DT, bool TR>
-struct NodeDist {
-    const double* etab;    // bf16: exp of every tabulated logit value at this node
+struct Dist64 {
+    const double* etab;    // bf16: exp((z - m)/T) of every tabulated logit value
     const double* tbl;
     ExpArg g;
     ExpConsts ek;
-    double invZ;           // 1 / sum_v exp((z_v - m)/T)
-    double qk1;            // transformed draft: invT * 256/ln2
-    double invSq;          // transformed draft: 1 / sum_v q_v^(1/T)
-    int nrej;              // rejections so far at this node
+    double invZ, qk1, invSq;
     const double* sinv;
     const int* kept;
 
@@ -162,13 +270,11 @@ struct NodeDist {
         }
         return exp_of(z, g, tbl, ek);
     }
-    // q^(1/T) in fp64 (0 stays 0); as given when the draft is untransformed.
     __device__ __forceinline__ double w_of(float q) const {
         if (!TR) return static_cast<double>(q);
         return q > 0.f ? exp_scaled(log(static_cast<double>(q)) * qk1, tbl, ek) : 0.0;
     }
     __device__ __forceinline__ double Q_of(float q) const { return TR ? w_of(q) * invSq : static_cast<double>(q); }
-    // P(v) after the first `upto` rejections at this node.
     __device__ __forceinline__ double P_of(double e, double Q, int upto) const {
         double P = e * invZ;
         for (int j = 0; j < upto; ++j) P = kept[j] ? P : fmax(P - Q, 0.0) * sinv[j];
@@ -176,17 +282,20 @@ struct NodeDist {
     }
 };
 
-template <int DT, bool VEC, bool TR>
+template <int DT, bool VEC, bool TR, bool LROW>
 __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleArgs a, ExpConsts ek) {
-    extern __shared__ double etab[];
+    extern __shared__ double dyn[];
     __shared__ TsSmem sm;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
     const int b = blockIdx.x, N = a.N, V = a.V;
     const long esz = Elem<DT>::kBytes;
     const int ntiles = (V + kTsTile - 1) / kTsTile;
+    const int nvec = static_cast<int>(static_cast<long>(V) * esz / 16);
     for (int t = tid; t < kTableSize; t += kTsThreads) sm.tbl[t] = exp2(static_cast<double>(t) * (1.0 / kTableSize));
     const int32_t* tok = a.node_tokens + static_cast<long>(b) * N;
     const float* ub = a.u + static_cast<long>(b) * N;
+    const char* zbase = static_cast<const char*>(a.logits) + static_cast<long>(b) * N * V * esz;
+    const float* qbase = a.q + static_cast<long>(b) * N * V;
 
     // E2 (every node token) and E5 (every uniform).
     int bad = 0;
@@ -196,90 +305,131 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
     }
     int err = ts_block_or(bad, sm);
 
-    int c = 0, d = 0;
+    // LDS: two row buffers (LROW; the final node's fp64 table goes into the one
+    // not holding its row) or the table alone.
+    u32x4* buf_cur = reinterpret_cast<u32x4*>(dyn);
+    u32x4* buf_next = buf_cur + kTsRowBytes / 16;
+    bool have_next = false;
+
+    Dist32<TR> d32;
+    d32.k32 = kLog2e * static_cast<float>(a.invT);
+    d32.invT = static_cast<float>(a.invT);
+    d32.sinv = sm.sinv32;
+    d32.kept = sm.kept32;
+    NodeRow<DT, VEC, LROW> row;
+    row.V = V;
+    row.zs = buf_cur;
+    int c = 0, d = 0, nrej = 0;
+    float m = 0.f;
     if (tid == 0) sm.path[0] = 0;
-    NodeDist<DT, TR> nd;
-    nd.etab = etab;
-    nd.tbl = sm.tbl;
-    nd.ek = ek;
-    nd.qk1 = a.invT * ek.scale;
-    nd.sinv = sm.sinv;
-    nd.kept = sm.kept;
-    const char* zr = nullptr;
-    const float* qr = nullptr;
     while (!err) {
-        zr = static_cast<const char*>(a.logits) + (static_cast<long>(b) * N + c) * V * esz;
-        qr = a.q + (static_cast<long>(b) * N + c) * V;
-        // Row maximum; E1 for NaN, +inf or a row of -inf only.
-        float m = -INFINITY;
-        int rb = 0;
-        for (int t = 0; t < ntiles; ++t) {
-            float z[8];
-            ts_load_z<DT, VEC>(zr, t * kTsTile + 8 * tid, V, z);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                rb |= (z[e] != z[e]) || z[e] == INFINITY;
-                m = fmaxf(m, z[e]);
+        const char* zr = zbase + static_cast<long>(c) * V * esz;
+        const float* qr = qbase + static_cast<long>(c) * V;
+        row.zr = zr;
+        row.qr = qr;
+        const int first = a.first_child[c];
+        // Loads, in this order: the node's row unless parked already, the tested
+        // children's z[x_n] and q[x_n] (lanes of wave 0), then the first child's
+        // row.  The memory counter retires in order, so waiting for one set never
+        // waits for a later one.
+        u32x4 cur[kTsRowVecs], pf[kTsRowVecs];
+        if constexpr (LROW) {
+            if (have_next) {
+                u32x4* t = buf_cur;
+                buf_cur = buf_next;
+                buf_next = t;
+            } else {
+                row_issue(zr, nvec, cur);
             }
         }
-        m = wave_max(m);
-        if (lane == 0) sm.fred[wid] = m;
-        rb = ts_block_or(rb, sm);
-        m = sm.fred[0];
-#pragma unroll
-        for (int w = 1; w < kTsWaves; ++w) m = fmaxf(m, sm.fred[w]);
-        if (rb || m == -INFINITY) { err = 1; break; }
-        nd.g = exp_arg(static_cast<double>(m), a.invT, ek);
-        if (DT == 1) {
-            build_exp_table(etab, nd.g, sm.tbl, ek);
-            __syncthreads();
+        float gz = 0.f, gq = 0.f;
+        const bool gl = wid == 0 && lane > 0 && lane < N && a.parent[lane] == c;
+        if (gl) {
+            const int x = tok[lane];
+            gz = Elem<DT>::scalar(zr, x);
+            gq = qr[x];
         }
-        // Normalisers: Z of the target row, Sq of a transformed draft row (with E3).
-        const int first = a.first_child[c];
-        const bool need_q = TR && first >= 0;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LROW) {
+            if (first >= 0) row_issue(zbase + static_cast<long>(first) * V * esz, nvec, pf);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LROW) {
+            if (!have_next) row_park(buf_cur, nvec, cur);
+        }
+        if (gl) {
+            sm.gz[lane] = gz;
+            sm.gq[lane] = gq;
+        }
+        have_next = false;
+        row.zs = buf_cur;
+        __syncthreads();
+
+        // Row maximum; E1 for NaN, +inf or a row of -inf only.
+        float mx = -INFINITY;
+        for_tiles(row, ntiles, false, [&](int, int, const float* z, const float*) {
+            mx = maximum3(maximum3(mx, z[0], z[1]), maximum3(z[2], z[3], z[4]), maximum3(z[5], z[6], z[7]));
+        });
+        const unsigned long long rbw = __ballot(!(mx < INFINITY));     // NaN (propagated) or +inf
+        mx = wave_max(mx);
+        if (lane == 0) {
+            sm.fred[wid] = mx;
+            sm.ired[wid] = rbw != 0ull;
+        }
+        __syncthreads();
+        m = sm.fred[0];
+        int rb = sm.ired[0];
+#pragma unroll
+        for (int w = 1; w < kTsWaves; ++w) {
+            m = fmaxf(m, sm.fred[w]);
+            rb |= sm.ired[w];
+        }
+        __syncthreads();
+        if (rb || m == -INFINITY) { err = 1; break; }
+        nrej = 0;
+        if (first < 0) break;                                           // a leaf: the draw is here
+
+        // The walk's tests in fp32: normalisers, then the children in node order.
+        d32.m = m;
         double Z = 0.0, Sq = 0.0;
         int qb = 0;
-        for (int t = 0; t < ntiles; ++t) {
-            const int i0 = t * kTsTile + 8 * tid;
-            float z[8], q[8];
-            ts_load_z<DT, VEC>(zr, i0, V, z);
-            if (need_q) ts_load_q<VEC>(qr, i0, V, q);
+        for_tiles(row, ntiles, TR, [&](int, int, const float* z, const float* q) {
+            float s = 0.f, sq = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                Z += nd.e_of(z[e]);
-                if (need_q) {
+                s += d32.e_of(z[e]);
+                if (TR) {
                     qb |= !q_ok(q[e]);
-                    Sq += nd.w_of(q[e]);
+                    sq += d32.w_of(q[e]);
                 }
             }
-        }
+            Z += static_cast<double>(s);
+            if (TR) Sq += static_cast<double>(sq);
+        });
         Z = ts_block_sum(Z, sm);
-        if (need_q) {
+        if (TR) {
             Sq = ts_block_sum(Sq, sm);
             qb = ts_block_or(qb, sm);
-            if (qb || !(Sq > 0.0)) { err = 1; break; }                               // E3, E4
+            if (qb || !(Sq > 0.0)) { err = 1; break; }                  // E3, E4
         }
-        nd.invZ = 1.0 / Z;
-        nd.invSq = need_q ? 1.0 / Sq : 1.0;
-        nd.nrej = 0;
-        // Children in node order, each one round of the chain's test.
+        d32.invZ = static_cast<float>(1.0 / Z);
+        d32.invSq = TR ? static_cast<float>(1.0 / Sq) : 1.f;
         int accepted = -1, q_checked = 0;
         for (int n = first; n >= 0; n = a.next_sibling[n]) {
             if (tid == 0) {
-                const int x = tok[n];
-                const float zx = Elem<DT>::scalar(zr, x);
-                const float qx = qr[x];
+                const float zx = sm.gz[n];
+                const float qx = sm.gq[n];
                 int dec = 0;
                 if (!TR && !q_ok(qx)) {
-                    dec = 2;                                                             // E3
+                    dec = 2;                                                 // E3
                 } else {
-                    const double Qx = nd.Q_of(qx);
-                    const double Px = nd.P_of(nd.e_of(zx), Qx, nd.nrej);
-                    double ratio;
-                    if (Qx > 0.0) ratio = Px / Qx;
-                    else ratio = Px > 0.0 ? INFINITY : 0.0;
-                    const double thr = ratio < 1.0 ? ratio : 1.0;
-                    dec = static_cast<double>(ub[n]) < thr ? 1 : 0;
+                    const float Qx = d32.Q_of(qx);
+                    const float Px = d32.P_of(d32.e_of(zx), Qx, nrej);
+                    float ratio;
+                    if (Qx > 0.f) ratio = Px / Qx;
+                    else ratio = Px > 0.f ? INFINITY : 0.f;
+                    const float thr = ratio < 1.f ? ratio : 1.f;
+                    dec = ub[n] < thr ? 1 : 0;
                 }
                 sm.dec = dec;
             }
@@ -293,29 +443,34 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
             const bool check_q = !TR && !q_checked;
             double S = 0.0;
             qb = 0;
-            for (int t = 0; t < ntiles; ++t) {
-                const int i0 = t * kTsTile + 8 * tid;
-                float z[8], q[8];
-                ts_load_z<DT, VEC>(zr, i0, V, z);
-                ts_load_q<VEC>(qr, i0, V, q);
+            for_tiles(row, ntiles, true, [&](int, int, const float* z, const float* q) {
+                float s = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     if (check_q) qb |= !q_ok(q[e]);
-                    const double Qv = nd.Q_of(q[e]);
-                    S += fmax(nd.P_of(nd.e_of(z[e]), Qv, nd.nrej) - Qv, 0.0);
+                    const float Qv = d32.Q_of(q[e]);
+                    s += fmaxf(d32.P_of(d32.e_of(z[e]), Qv, nrej) - Qv, 0.f);
                 }
-            }
+                S += static_cast<double>(s);
+            });
             S = ts_block_sum(S, sm);
             if (check_q) {
                 q_checked = 1;
                 if (ts_block_or(qb, sm)) { err = 1; break; }
             }
             if (tid == 0) {
-                sm.kept[nd.nrej] = !(S > 0.0);
-                sm.sinv[nd.nrej] = S > 0.0 ? 1.0 / S : 1.0;
+                sm.kept32[nrej] = !(S > 0.0);
+                sm.sinv32[nrej] = S > 0.0 ? static_cast<float>(1.0 / S) : 1.f;
             }
             __syncthreads();
-            ++nd.nrej;
+            ++nrej;
+        }
+        if constexpr (LROW) {
+            // the next node's entry barrier orders these stores before any read
+            if (!err && first >= 0 && accepted == first) {
+                row_park(buf_next, nvec, pf);
+                have_next = true;
+            }
         }
         if (err || accepted < 0) break;
         ++d;
@@ -326,26 +481,92 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
         }
     }
 
-    // Final draw from P at node c with u[0]: segment sums in index order, the
-    // segment holding u*S, then that segment rescanned by the wave that owns it.
+    // The final node c, nrej rejections there: its normalisers and residual masses
+    // in fp64, the last pass leaving the segment sums of the draw's weights (e_v
+    // without a rejection, max(0, P(v) - Q(v)) of the last rejection otherwise),
+    // then the segment holding u*S, rescanned.
     int y = -1;
     if (!err) {
+        __syncthreads();                 // every thread is done with the walk's LDS rows
+        double* etab = LROW ? reinterpret_cast<double*>(buf_next) : dyn;
+        const float* qr = qbase + static_cast<long>(c) * V;
+        Dist64<DT, TR> d64;
+        d64.etab = etab;
+        d64.tbl = sm.tbl;
+        d64.ek = ek;
+        d64.g = exp_arg(static_cast<double>(m), a.invT, ek);
+        d64.qk1 = a.invT * ek.scale;
+        d64.sinv = sm.sinv;
+        d64.kept = sm.kept;
+        if (DT == 1) {
+            build_exp_table(etab, d64.g, sm.tbl, ek);
+            __syncthreads();
+        }
+        const bool with_q = nrej > 0;
+        const bool need_sq = TR && nrej > 0;
+        // mode 0: weights e_v, summed by the normaliser pass; 1: the last
+        // rejection's residual, summed by its pass; 2: P after a last rejection
+        // that kept P, summed by a pass of its own
+        int mode = nrej == 0 ? 0 : 1;
         int last = -1;
-        for (int t = 0; t < ntiles; ++t) {
-            const int i0 = t * kTsTile + 8 * tid;
-            float z[8], q[8];
-            ts_load_z<DT, VEC>(zr, i0, V, z);
-            if (nd.nrej > 0) ts_load_q<VEC>(qr, i0, V, q);
-            double s = 0.0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const double Qv = nd.nrej > 0 ? nd.Q_of(q[e]) : 0.0;
-                const double P = nd.P_of(nd.e_of(z[e]), Qv, nd.nrej);
-                s += P;
-                if (P > 0.0) last = i0 + e;
-            }
+        auto seg_sum = [&](int t, double s) {
             s = wave_sum(s);
             if (lane == 0) sm.part[t * kTsWaves + wid] = s;
+        };
+        double Z = 0.0, Sq = 0.0;
+        for_tiles(row, ntiles, need_sq, [&](int t, int i0, const float* z, const float* q) {
+            double s = 0.0, sq = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double ev = d64.e_of(z[e]);
+                s += ev;
+                if (ev > 0.0) last = i0 + e;
+                if (need_sq) sq += d64.w_of(q[e]);
+            }
+            Z += s;
+            Sq += sq;
+            if (mode == 0) seg_sum(t, s);
+        });
+        Z = ts_block_sum(Z, sm);
+        if (need_sq) Sq = ts_block_sum(Sq, sm);
+        d64.invZ = 1.0 / Z;
+        d64.invSq = need_sq ? 1.0 / Sq : 1.0;
+        for (int j = 0; j < nrej; ++j) {
+            const bool lastj = j == nrej - 1;
+            if (lastj) last = -1;
+            double S = 0.0;
+            for_tiles(row, ntiles, true, [&](int t, int i0, const float* z, const float* q) {
+                double s = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double Qv = d64.Q_of(q[e]);
+                    const double r = fmax(d64.P_of(d64.e_of(z[e]), Qv, j) - Qv, 0.0);
+                    s += r;
+                    if (lastj && r > 0.0) last = i0 + e;
+                }
+                S += s;
+                if (lastj) seg_sum(t, s);
+            });
+            S = ts_block_sum(S, sm);
+            if (tid == 0) {
+                sm.kept[j] = !(S > 0.0);
+                sm.sinv[j] = S > 0.0 ? 1.0 / S : 1.0;
+            }
+            __syncthreads();
+        }
+        if (nrej > 0 && sm.kept[nrej - 1]) {
+            mode = 2;
+            last = -1;
+            for_tiles(row, ntiles, true, [&](int t, int i0, const float* z, const float* q) {
+                double s = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double P = d64.P_of(d64.e_of(z[e]), d64.Q_of(q[e]), nrej);
+                    s += P;
+                    if (P > 0.0) last = i0 + e;
+                }
+                seg_sum(t, s);
+            });
         }
         last = ts_block_max(last, sm);       // (its barrier also publishes sm.part)
         const int nparts = ntiles * kTsWaves;
@@ -387,19 +608,24 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
         if (seg < 0) {
             y = last;                                   // rounding fallback
         } else if (wid == seg % kTsWaves) {
-            const int t = seg / kTsWaves;
-            const int i0 = t * kTsTile + 8 * tid;
+            const int ts = seg / kTsWaves;
+            const int i0 = ts * kTsTile + 8 * tid;
+            const double target = sm.red[0];
             float z[8], q[8];
-            ts_load_z<DT, VEC>(zr, i0, V, z);
-            if (nd.nrej > 0) ts_load_q<VEC>(qr, i0, V, q);
-            double P[8], s = 0.0;
+            row.get_z(ts, z);
+            if (with_q) ts_load_q<VEC>(qr, i0, V, q);
+            double w[8], s = 0.0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const double Qv = nd.nrej > 0 ? nd.Q_of(q[e]) : 0.0;
-                P[e] = nd.P_of(nd.e_of(z[e]), Qv, nd.nrej);
-                s += P[e];
+                const double ev = d64.e_of(z[e]);
+                if (mode == 0) {
+                    w[e] = ev;
+                } else {
+                    const double Qv = d64.Q_of(q[e]);
+                    w[e] = mode == 1 ? fmax(d64.P_of(ev, Qv, nrej - 1) - Qv, 0.0) : d64.P_of(ev, Qv, nrej);
+                }
+                s += w[e];
             }
-            const double target = sm.red[0];
             const double incl = sm.base + wave_inclusive_scan(s);
             const unsigned long long hit = __ballot(target < incl);
             int yy;
@@ -410,13 +636,13 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
                     double acc = incl - s;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        acc += P[e];
-                        if (pick < 0 && P[e] > 0.0 && target < acc) pick = i0 + e;
+                        acc += w[e];
+                        if (pick < 0 && w[e] > 0.0 && target < acc) pick = i0 + e;
                     }
                     if (pick < 0) {                      // rounding inside the lane: its last positive
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            if (P[e] > 0.0) pick = i0 + e;
+                            if (w[e] > 0.0) pick = i0 + e;
                     }
                 }
                 yy = bcast(pick, l);
@@ -425,7 +651,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
                 int lp = -1;
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (P[e] > 0.0) lp = i0 + e;
+                    if (w[e] > 0.0) lp = i0 + e;
                 yy = wave_max_int(lp);
             }
             if (lane == 0) sm.seg = yy;
@@ -444,10 +670,10 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
     if (tid == 0) a.out_accept_len[b] = err ? -1 : d;
 }
 
-template <int DT, bool VEC, bool TR>
+template <int DT, bool VEC, bool TR, bool LROW>
 hipError_t ts_launch(const TreeSampleArgs& a, hipStream_t s, Timing t) {
-    const unsigned lds = DT == 1 ? static_cast<unsigned>(kTabBytes) : 0u;
-    launch_timed(t, tree_sample_kernel<DT, VEC, TR>, dim3(a.B), dim3(kTsThreads), lds, s, a, exp_consts());
+    const unsigned lds = LROW ? 2u * kTsRowBytes : (DT == 1 ? static_cast<unsigned>(kTabBytes) : 0u);
+    launch_timed(t, tree_sample_kernel<DT, VEC, TR, LROW>, dim3(a.B), dim3(kTsThreads), lds, s, a, exp_consts());
     return hipGetLastError();
 }
 
@@ -455,9 +681,16 @@ template <int DT>
 hipError_t ts_dispatch(const TreeSampleArgs& a, hipStream_t s, Timing t) {
     // 16-byte vectors: 8 elements per load need V a multiple of 8 and aligned rows.
     const bool vec = a.V % 8 == 0 && vec_ok(a.logits, a.V, Elem<DT>::kBytes) && vec_ok(a.q, a.V, 4);
-    if (a.transformed) return vec ? ts_launch<DT, true, true>(a, s, t) : ts_launch<DT, false, true>(a, s, t);
-    return vec ? ts_launch<DT, true, false>(a, s, t) : ts_launch<DT, false, false>(a, s, t);
+    const bool lrow = vec && static_cast<long>(a.V) * Elem<DT>::kBytes <= kTsRowBytes;
+    if (a.transformed) {
+        if (lrow) return ts_launch<DT, true, true, true>(a, s, t);
+        return vec ? ts_launch<DT, true, true, false>(a, s, t) : ts_launch<DT, false, true, false>(a, s, t);
+    }
+    if (lrow) return ts_launch<DT, true, false, true>(a, s, t);
+    return vec ? ts_launch<DT, true, false, false>(a, s, t) : ts_launch<DT, false, false, false>(a, s, t);
 }
+
+static_assert(kTabBytes <= kTsRowBytes, "the final node's fp64 table fits the spare row buffer");
 
 }  // namespace
 
