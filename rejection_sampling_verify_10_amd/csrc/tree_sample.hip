@@ -56,10 +56,35 @@ constexpr int kTsRowBytes = 64 * 1024;                      // largest LDS-held 
 constexpr int kTsRowVecs = kTsRowBytes / 16 / kTsThreads;   // its 16-byte vectors per thread
 constexpr float kLog2e = 1.4426950408889634f;
 
+constexpr int kTsFastRej = 3;                               // rejections the one-pass final stage takes
+constexpr int kTsListCap = 256;                             // its undecided elements
+constexpr double kTsBracket = 1e-4;                         // relative bracket around the walk's fp32 points
+
+// A value every lane holds alike, moved to scalar registers.
+__device__ __forceinline__ double uniform_d(double v) {
+    const long long bits = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(bits));
+    const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(bits >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+// Segment-sum slots the LDS layout provides (two arrays of this many doubles).
+template <int DT, bool LROW> constexpr int ts_parts_cap() {
+    return LROW ? kTsRowBytes / Elem<DT>::kBytes / kTsTile * kTsWaves : kTsParts;
+}
+
 struct TsSmem {
     double tbl[kTableSize];          // 2^(k/256) for the fp64 exponential
-    double part[kTsParts];           // segment sums of the draw's weights, in index order
     double red[kTsWaves];
+    double redn[kTsWaves][2 + 2 * kTsFastRej];
+    int li_v[kTsListCap];            // undecided elements of the one-pass final stage: index,
+    int li_j[kTsListCap];            //   evaluation point, e_v and the draft weight y_v
+    double li_e[kTsListCap];
+    double li_y[kTsListCap];
+    int n_list;
+    int fast_ok;
+    double lam_last;                 // the exact point of the draw's residual
+    int last_list;                   // the largest listed index with a positive draw weight
     float fred[kTsWaves];
     int ired[kTsWaves];
     float sinv32[kTsMaxNodes];       // walk (fp32): 1/S of each rejection at the current node
@@ -230,25 +255,23 @@ __device__ __forceinline__ void for_tiles(const Row& r, int ntiles, bool with_q,
     }
 }
 
-// The walk's fp32 view of the current node.
+// The walk's fp32 view of the current node.  After rejections at the node,
+// P(v) = max(0, P_0(v) - cq Q(v)) * invD: each rejection with mass S > 0 adds
+// D to cq and multiplies D by S (a rejection with S = 0 changes nothing), which
+// is the residual recursion max(0, P - Q)/S unrolled.
 template <bool TR>
 struct Dist32 {
     float m, k32;          // row maximum, log2(e)/T
     float invT;
     float invZ, invSq;
-    const float* sinv;
-    const int* kept;
+    float cq, invD;
     __device__ __forceinline__ float e_of(float z) const { return __builtin_amdgcn_exp2f((z - m) * k32); }
     __device__ __forceinline__ float w_of(float q) const {
         if (!TR) return q;
         return q > 0.f ? __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(q) * invT) : 0.f;
     }
     __device__ __forceinline__ float Q_of(float q) const { return TR ? w_of(q) * invSq : q; }
-    __device__ __forceinline__ float P_of(float e, float Q, int upto) const {
-        float P = e * invZ;
-        for (int j = 0; j < upto; ++j) P = kept[j] ? P : fmaxf(P - Q, 0.f) * sinv[j];
-        return P;
-    }
+    __device__ __forceinline__ float P_of(float e, float Q) const { return fmaxf(e * invZ - cq * Q, 0.f) * invD; }
 };
 
 // The final node's fp64 view.
@@ -314,13 +337,12 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
     Dist32<TR> d32;
     d32.k32 = kLog2e * static_cast<float>(a.invT);
     d32.invT = static_cast<float>(a.invT);
-    d32.sinv = sm.sinv32;
-    d32.kept = sm.kept32;
     NodeRow<DT, VEC, LROW> row;
     row.V = V;
     row.zs = buf_cur;
     int c = 0, d = 0, nrej = 0;
     float m = 0.f;
+    double Zw = 1.0, Sqw = 1.0;      // the walk's normalisers at the current node (fp32 terms)
     if (tid == 0) sm.path[0] = 0;
     while (!err) {
         const char* zr = zbase + static_cast<long>(c) * V * esz;
@@ -406,6 +428,11 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
             Z += static_cast<double>(s);
             if (TR) Sq += static_cast<double>(sq);
         });
+        if constexpr (LROW) {
+            // park the first child's row (its loads have had the passes above to land);
+            // the barriers below order these stores before the next node reads them
+            if (first >= 0) row_park(buf_next, nvec, pf);
+        }
         Z = ts_block_sum(Z, sm);
         if (TR) {
             Sq = ts_block_sum(Sq, sm);
@@ -414,6 +441,11 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
         }
         d32.invZ = static_cast<float>(1.0 / Z);
         d32.invSq = TR ? static_cast<float>(1.0 / Sq) : 1.f;
+        d32.cq = 0.f;
+        d32.invD = 1.f;
+        double Dw = 1.0;                 // D of the closed form, kept in fp64
+        Zw = Z;
+        Sqw = TR ? Sq : 1.0;
         int accepted = -1, q_checked = 0;
         for (int n = first; n >= 0; n = a.next_sibling[n]) {
             if (tid == 0) {
@@ -424,7 +456,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
                     dec = 2;                                                 // E3
                 } else {
                     const float Qx = d32.Q_of(qx);
-                    const float Px = d32.P_of(d32.e_of(zx), Qx, nrej);
+                    const float Px = d32.P_of(d32.e_of(zx), Qx);
                     float ratio;
                     if (Qx > 0.f) ratio = Px / Qx;
                     else ratio = Px > 0.f ? INFINITY : 0.f;
@@ -449,7 +481,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
                 for (int e = 0; e < 8; ++e) {
                     if (check_q) qb |= !q_ok(q[e]);
                     const float Qv = d32.Q_of(q[e]);
-                    s += fmaxf(d32.P_of(d32.e_of(z[e]), Qv, nrej) - Qv, 0.f);
+                    s += fmaxf(d32.P_of(d32.e_of(z[e]), Qv) - Qv, 0.f);
                 }
                 S += static_cast<double>(s);
             });
@@ -462,16 +494,15 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
                 sm.kept32[nrej] = !(S > 0.0);
                 sm.sinv32[nrej] = S > 0.0 ? static_cast<float>(1.0 / S) : 1.f;
             }
+            if (S > 0.0) {                   // (S is the same in every thread)
+                d32.cq += static_cast<float>(Dw);
+                Dw *= S;
+                d32.invD = static_cast<float>(1.0 / Dw);
+            }
             __syncthreads();
             ++nrej;
         }
-        if constexpr (LROW) {
-            // the next node's entry barrier orders these stores before any read
-            if (!err && first >= 0 && accepted == first) {
-                row_park(buf_next, nvec, pf);
-                have_next = true;
-            }
-        }
+        if constexpr (LROW) have_next = !err && first >= 0 && accepted == first;
         if (err || accepted < 0) break;
         ++d;
         c = accepted;
@@ -481,15 +512,27 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
         }
     }
 
-    // The final node c, nrej rejections there: its normalisers and residual masses
-    // in fp64, the last pass leaving the segment sums of the draw's weights (e_v
-    // without a rejection, max(0, P(v) - Q(v)) of the last rejection otherwise),
-    // then the segment holding u*S, rescanned.
+    // The final node c, nrej = R rejections there, in fp64.  Without a kept step,
+    // after j rejections P_j(v) = max(0, P_0(v) - c_j Q_v) / D_j with c_0 = 0,
+    // D_0 = 1, c_{j+1} = c_j + D_j, D_{j+1} = D_j S_j, so every residual mass is a
+    // hinge sum of the node's first distribution:
+    //     S_j = sum_v max(0, e_v - lam_j y_v) / (Z D_j),   lam_j = (c_j + D_j) Z / Sq
+    // (e_v = exp((z_v - m)/T), y_v the draft weight, Sq its sum; Sq = 1 untransformed).
+    // The walk's fp32 S's give each lam_j to ~1e-6, so one pass sorts every element
+    // against lam_j (1 -+ kTsBracket): above (sum e_v and y_v), below (nothing), or
+    // between (listed).  The exact lam_j then follow in order from those sums, each
+    // checked to lie inside its bracket.  The same pass leaves the segment sums of the
+    // draw's weights: e_v (no rejection) or max(0, e_v - lam_{R-1} y_v).  A kept
+    // step, more than kTsFastRej rejections, a full list or a point outside its
+    // bracket take the multi-pass route instead (one fp64 pass per S_j).
     int y = -1;
     if (!err) {
         __syncthreads();                 // every thread is done with the walk's LDS rows
         double* etab = LROW ? reinterpret_cast<double*>(buf_next) : dyn;
+        double* partE = dyn + (LROW ? 2 * kTsRowBytes / 8 : (DT == 1 ? kTabBytes / 8 : 0));
+        double* partY = partE + ts_parts_cap<DT, LROW>();
         const float* qr = qbase + static_cast<long>(c) * V;
+        const int R = nrej;
         Dist64<DT, TR> d64;
         d64.etab = etab;
         d64.tbl = sm.tbl;
@@ -498,78 +541,218 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
         d64.qk1 = a.invT * ek.scale;
         d64.sinv = sm.sinv;
         d64.kept = sm.kept;
-        if (DT == 1) {
-            build_exp_table(etab, d64.g, sm.tbl, ek);
-            __syncthreads();
+        if (tid == 0) {
+            sm.n_list = 0;
+            sm.last_list = -1;
         }
-        const bool with_q = nrej > 0;
-        const bool need_sq = TR && nrej > 0;
-        // mode 0: weights e_v, summed by the normaliser pass; 1: the last
-        // rejection's residual, summed by its pass; 2: P after a last rejection
-        // that kept P, summed by a pass of its own
-        int mode = nrej == 0 ? 0 : 1;
-        int last = -1;
-        auto seg_sum = [&](int t, double s) {
-            s = wave_sum(s);
-            if (lane == 0) sm.part[t * kTsWaves + wid] = s;
-        };
-        double Z = 0.0, Sq = 0.0;
-        for_tiles(row, ntiles, need_sq, [&](int t, int i0, const float* z, const float* q) {
-            double s = 0.0, sq = 0.0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const double ev = d64.e_of(z[e]);
-                s += ev;
-                if (ev > 0.0) last = i0 + e;
-                if (need_sq) sq += d64.w_of(q[e]);
-            }
-            Z += s;
-            Sq += sq;
-            if (mode == 0) seg_sum(t, s);
-        });
-        Z = ts_block_sum(Z, sm);
-        if (need_sq) Sq = ts_block_sum(Sq, sm);
-        d64.invZ = 1.0 / Z;
-        d64.invSq = need_sq ? 1.0 / Sq : 1.0;
-        for (int j = 0; j < nrej; ++j) {
-            const bool lastj = j == nrej - 1;
-            if (lastj) last = -1;
-            double S = 0.0;
-            for_tiles(row, ntiles, true, [&](int t, int i0, const float* z, const float* q) {
-                double s = 0.0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const double Qv = d64.Q_of(q[e]);
-                    const double r = fmax(d64.P_of(d64.e_of(z[e]), Qv, j) - Qv, 0.0);
-                    s += r;
-                    if (lastj && r > 0.0) last = i0 + e;
-                }
-                S += s;
-                if (lastj) seg_sum(t, s);
-            });
-            S = ts_block_sum(S, sm);
-            if (tid == 0) {
-                sm.kept[j] = !(S > 0.0);
-                sm.sinv[j] = S > 0.0 ? 1.0 / S : 1.0;
-            }
-            __syncthreads();
-        }
-        if (nrej > 0 && sm.kept[nrej - 1]) {
-            mode = 2;
-            last = -1;
-            for_tiles(row, ntiles, true, [&](int t, int i0, const float* z, const float* q) {
-                double s = 0.0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const double P = d64.P_of(d64.e_of(z[e]), d64.Q_of(q[e]), nrej);
-                    s += P;
-                    if (P > 0.0) last = i0 + e;
-                }
-                seg_sum(t, s);
-            });
-        }
-        last = ts_block_max(last, sm);       // (its barrier also publishes sm.part)
+        if (DT == 1) build_exp_table(etab, d64.g, sm.tbl, ek);
+        __syncthreads();
+        const bool with_q = R > 0;
         const int nparts = ntiles * kTsWaves;
+        auto seg_sum = [&](double* part, int t, double v) {
+            v = wave_sum(v);
+            if (lane == 0) part[t * kTsWaves + wid] = v;
+        };
+        // The walk's points and their brackets (every thread computes the same).
+        bool fast = R <= kTsFastRej;
+        double lamLo[kTsFastRej], lamHi[kTsFastRej];
+        {
+            double cc = 0.0, DD = 1.0;
+#pragma unroll
+            for (int j = 0; j < kTsFastRej; ++j) {
+                lamLo[j] = lamHi[j] = 0.0;
+                if (j < R) {
+                    fast = fast && !sm.kept32[j];
+                    const double lam = (cc + DD) * Zw / Sqw;
+                    lamLo[j] = uniform_d(lam * (1.0 - kTsBracket));
+                    lamHi[j] = uniform_d(lam * (1.0 + kTsBracket));
+                    cc += DD;
+                    DD *= 1.0 / static_cast<double>(sm.sinv32[j]);
+                }
+            }
+        }
+        int mode = 0;            // draw weights: 0 e_v, 1 the hinge max(0, e_v - lam y_v), 2 and 3 the
+        int last = -1;           // multi-pass route's residual and kept P
+        if (fast) {
+            double Zs = 0.0, Sqs = 0.0, Ej[kTsFastRej], Yj[kTsFastRej];
+#pragma unroll
+            for (int j = 0; j < kTsFastRej; ++j) Ej[j] = Yj[j] = 0.0;
+            for_tiles(row, ntiles, with_q, [&](int t, int i0, const float* z, const float* q) {
+                double sE = 0.0, sY = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double ev = d64.e_of(z[e]);
+                    Zs += ev;
+                    if (R == 0) {
+                        sE += ev;
+                        if (ev > 0.0) last = i0 + e;
+                        continue;
+                    }
+                    const double yv = d64.w_of(q[e]);
+                    Sqs += yv;
+#pragma unroll
+                    for (int j = 0; j < kTsFastRej; ++j) {
+                        if (j >= R) continue;
+                        const bool pos = ev > lamHi[j] * yv;
+                        Ej[j] += pos ? ev : 0.0;
+                        Yj[j] += pos ? yv : 0.0;
+                        if (j == R - 1) {
+                            sE += pos ? ev : 0.0;
+                            sY += pos ? yv : 0.0;
+                            last = pos ? i0 + e : last;
+                        }
+                        const bool und = !pos && ev > lamLo[j] * yv;
+                        if (__ballot(und)) {             // rare: a few elements per row
+                            if (und) {
+                                const int k = atomicAdd(&sm.n_list, 1);
+                                if (k < kTsListCap) {
+                                    sm.li_v[k] = i0 + e;
+                                    sm.li_j[k] = j;
+                                    sm.li_e[k] = ev;
+                                    sm.li_y[k] = yv;
+                                }
+                            }
+                        }
+                    }
+                }
+                seg_sum(partE, t, sE);
+                if (R > 0) seg_sum(partY, t, sY);
+            });
+            // block sums of Z, Sq and the per-point sums in one exchange
+            {
+                double v[2 + 2 * kTsFastRej];
+                v[0] = Zs;
+                v[1] = Sqs;
+#pragma unroll
+                for (int j = 0; j < kTsFastRej; ++j) {
+                    v[2 + 2 * j] = Ej[j];
+                    v[3 + 2 * j] = Yj[j];
+                }
+#pragma unroll
+                for (int k = 0; k < 2 + 2 * kTsFastRej; ++k) {
+                    const double w = wave_sum(v[k]);
+                    if (lane == 0) sm.redn[wid][k] = w;
+                }
+            }
+            last = ts_block_max(last, sm);       // (its barriers also publish redn, the list and the parts)
+            if (wid == 0) {
+                // lane k sums value k over the waves; every lane then holds all of them
+                double tk = 0.0;
+                if (lane < 2 + 2 * kTsFastRej)
+                    for (int w = 0; w < kTsWaves; ++w) tk += sm.redn[w][lane];
+                double tot[2 + 2 * kTsFastRej];
+#pragma unroll
+                for (int k = 0; k < 2 + 2 * kTsFastRej; ++k) tot[k] = bcast(tk, k);
+                const double Z = tot[0];
+                const double Sq = TR && R > 0 ? tot[1] : 1.0;
+                const int nl = sm.n_list;
+                int ok = nl <= kTsListCap;
+                double cc = 0.0, DD = 1.0, lam = 0.0;
+#pragma unroll
+                for (int j = 0; j < kTsFastRej; ++j) {
+                    if (j >= R || !ok) continue;
+                    lam = (cc + DD) * Z / Sq;
+                    ok = lam >= lamLo[j] && lam <= lamHi[j];
+                    double G = tot[2 + 2 * j] - lam * tot[3 + 2 * j];
+                    for (int k = 0; k < nl; ++k)
+                        if (sm.li_j[k] == j) G += fmax(sm.li_e[k] - lam * sm.li_y[k], 0.0);
+                    const double S = G / (Z * DD);
+                    ok = ok && S > 0.0;
+                    cc += DD;
+                    DD *= S;
+                }
+                int ll = -1;
+                if (ok && R > 0) {
+                    for (int k = 0; k < nl; ++k)
+                        if (sm.li_j[k] == R - 1 && sm.li_e[k] - lam * sm.li_y[k] > 0.0) ll = max(ll, sm.li_v[k]);
+                }
+                if (lane == 0) {
+                    sm.fast_ok = ok;
+                    sm.lam_last = lam;
+                    sm.last_list = ll;
+                }
+            }
+            __syncthreads();
+            fast = sm.fast_ok != 0;
+            if (fast && R > 0) {
+                // the draw's segment sums at the exact point, then the listed elements
+                const double lam = sm.lam_last;
+                for (int p = tid; p < nparts; p += kTsThreads) partE[p] = partE[p] - lam * partY[p];
+                __syncthreads();
+                if (tid == 0) {
+                    const int nl = sm.n_list;
+                    for (int k = 0; k < nl; ++k) {
+                        if (sm.li_j[k] != R - 1) continue;
+                        const int v = sm.li_v[k];
+                        partE[(v / kTsTile) * kTsWaves + (v % kTsTile) / 8 / kWave] +=
+                            fmax(sm.li_e[k] - lam * sm.li_y[k], 0.0);
+                    }
+                }
+                last = max(last, sm.last_list);
+                mode = 1;
+            }
+        }
+        if (!fast) {
+            // Multi-pass route: the normalisers, then one pass per rejection.
+            mode = R == 0 ? 0 : 2;
+            last = -1;
+            double Z = 0.0, Sq = 0.0;
+            for_tiles(row, ntiles, TR && R > 0, [&](int t, int i0, const float* z, const float* q) {
+                double s = 0.0, sq = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double ev = d64.e_of(z[e]);
+                    s += ev;
+                    if (ev > 0.0) last = i0 + e;
+                    if (TR && R > 0) sq += d64.w_of(q[e]);
+                }
+                Z += s;
+                Sq += sq;
+                if (R == 0) seg_sum(partE, t, s);
+            });
+            Z = ts_block_sum(Z, sm);
+            if (TR && R > 0) Sq = ts_block_sum(Sq, sm);
+            d64.invZ = 1.0 / Z;
+            d64.invSq = TR && R > 0 ? 1.0 / Sq : 1.0;
+            for (int j = 0; j < R; ++j) {
+                const bool lastj = j == R - 1;
+                if (lastj) last = -1;
+                double S = 0.0;
+                for_tiles(row, ntiles, true, [&](int t, int i0, const float* z, const float* q) {
+                    double s = 0.0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const double Qv = d64.Q_of(q[e]);
+                        const double r = fmax(d64.P_of(d64.e_of(z[e]), Qv, j) - Qv, 0.0);
+                        s += r;
+                        if (lastj && r > 0.0) last = i0 + e;
+                    }
+                    S += s;
+                    if (lastj) seg_sum(partE, t, s);
+                });
+                S = ts_block_sum(S, sm);
+                if (tid == 0) {
+                    sm.kept[j] = !(S > 0.0);
+                    sm.sinv[j] = S > 0.0 ? 1.0 / S : 1.0;
+                }
+                __syncthreads();
+            }
+            if (R > 0 && sm.kept[R - 1]) {
+                mode = 3;
+                last = -1;
+                for_tiles(row, ntiles, true, [&](int t, int i0, const float* z, const float* q) {
+                    double s = 0.0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const double P = d64.P_of(d64.e_of(z[e]), d64.Q_of(q[e]), R);
+                        s += P;
+                        if (P > 0.0) last = i0 + e;
+                    }
+                    seg_sum(partE, t, s);
+                });
+            }
+        }
+        last = ts_block_max(last, sm);       // (its barrier also publishes the parts)
         if (wid == 0) {
             // Lane l sums a run of consecutive segments; an inclusive scan of the
             // runs, then a serial walk inside the run that crosses u*S.
@@ -577,7 +760,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
             double run = 0.0;
             for (int j = 0; j < per; ++j) {
                 const int p = lane * per + j;
-                if (p < nparts) run += sm.part[p];
+                if (p < nparts) run += partE[p];
             }
             const double incl = wave_inclusive_scan(run);
             const double S = bcast(incl, kWave - 1);
@@ -591,7 +774,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
                 for (int j = 0; j < per; ++j) {
                     const int p = l * per + j;
                     if (p >= nparts) break;
-                    const double nxt = acc + sm.part[p];
+                    const double nxt = acc + partE[p];
                     if (target < nxt) { seg = p; break; }
                     acc = nxt;
                 }
@@ -611,6 +794,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
             const int ts = seg / kTsWaves;
             const int i0 = ts * kTsTile + 8 * tid;
             const double target = sm.red[0];
+            const double lam = sm.lam_last;
             float z[8], q[8];
             row.get_z(ts, z);
             if (with_q) ts_load_q<VEC>(qr, i0, V, q);
@@ -620,9 +804,11 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
                 const double ev = d64.e_of(z[e]);
                 if (mode == 0) {
                     w[e] = ev;
+                } else if (mode == 1) {
+                    w[e] = fmax(ev - lam * d64.w_of(q[e]), 0.0);
                 } else {
                     const double Qv = d64.Q_of(q[e]);
-                    w[e] = mode == 1 ? fmax(d64.P_of(ev, Qv, nrej - 1) - Qv, 0.0) : d64.P_of(ev, Qv, nrej);
+                    w[e] = mode == 2 ? fmax(d64.P_of(ev, Qv, R - 1) - Qv, 0.0) : d64.P_of(ev, Qv, R);
                 }
                 s += w[e];
             }
@@ -672,7 +858,10 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
 
 template <int DT, bool VEC, bool TR, bool LROW>
 hipError_t ts_launch(const TreeSampleArgs& a, hipStream_t s, Timing t) {
-    const unsigned lds = LROW ? 2u * kTsRowBytes : (DT == 1 ? static_cast<unsigned>(kTabBytes) : 0u);
+    // LDS row buffers (or the fp64 table), then two arrays of segment sums
+    const unsigned parts = ts_parts_cap<DT, LROW>();
+    const unsigned lds = (LROW ? 2u * kTsRowBytes : (DT == 1 ? static_cast<unsigned>(kTabBytes) : 0u)) +
+                         2u * parts * static_cast<unsigned>(sizeof(double));
     launch_timed(t, tree_sample_kernel<DT, VEC, TR, LROW>, dim3(a.B), dim3(kTsThreads), lds, s, a, exp_consts());
     return hipGetLastError();
 }
