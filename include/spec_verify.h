@@ -57,6 +57,9 @@
  *     Results do not depend on it; a normaliser outside its bracket only makes
  *     the draw recompute that row exactly (0 forces that path, for tests).
  *     Read on every call; unset or invalid values leave the built-in width.
+ *     SPEC_VERIFY_TREE_ONEPASS = 0 makes spec_verify_tree_sample compute the
+ *     residual masses of the node it draws at with one pass each, instead of
+ *     one pass for all of them (the same results; for tests).
  *     SPEC_VERIFY_DENSE_PATH = walk | rows picks the route of a chain with
  *     temperature 1 and top-k off: the walk (one workgroup per batch row reads
  *     target rows only up to the first rejection) or every row's statistics

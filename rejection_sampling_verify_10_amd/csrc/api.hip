@@ -442,6 +442,8 @@ int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const
     ta.D = D;
     ta.invT = 1.0 / static_cast<double>(temperature);
     ta.transformed = temperature != 1.f ? 1 : 0;
+    const char* env = getenv("SPEC_VERIFY_TREE_ONEPASS");
+    ta.onepass = (env && env[0] == '0') ? 0 : 1;
     ta.out_path = out_path;
     ta.out_tokens = out_tokens;
     ta.out_accept_len = out_accept_len;

@@ -133,6 +133,7 @@ struct TreeSampleArgs {
     int B, N, V, D;
     double invT;
     int transformed;        // T != 1: q'(v) = q_v^(1/T) / sum
+    int onepass;            // 0: the drawing node's residual masses always take one pass each
     int8_t parent[64];      // parent[0] = -1
     int8_t first_child[64];
     int8_t next_sibling[64];

@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
             if (lane == 0) part[t * kTsWaves + wid] = v;
         };
         // The walk's points and their brackets (every thread computes the same).
-        bool fast = R <= kTsFastRej;
+        bool fast = a.onepass && R <= kTsFastRej;
         double lamLo[kTsFastRej], lamHi[kTsFastRej];
         {
             double cc = 0.0, DD = 1.0;

@@ -89,6 +89,15 @@ def test_workload5_full(R, orc):
     tally.check()
 
 
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_multipass_route(R, orc, monkeypatch, T):
+    """The drawing node's residual masses one pass each (the route taken when the
+    one-pass brackets do not hold): the same results."""
+    monkeypatch.setenv("SPEC_VERIFY_TREE_ONEPASS", "0")
+    ti = W.make_tree_sampled(32, 32000, temperature=T, config_id=5, seed=21)
+    run_case(R, orc, ti, f"multi-pass T={T}").check()
+
+
 @pytest.mark.parametrize("T", [0.7, 1.3])
 def test_transformed_full(R, orc, T):
     """Temperature applied to both distributions (q^(1/T) renormalised), full V."""
