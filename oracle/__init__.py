@@ -49,12 +49,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P]
         L.oracle_accept_rate.argtypes = [P, I, P, I, I, I, D, I, P]
         L.oracle_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, D, I, P, P, P, P, P]
+        L.oracle_tree_expand.argtypes = [P, P, I, I, I, I, I, P, P, P]
+        L.oracle_tree_rerank.argtypes = [P, P, I, I, I, P, P, P]
         L.oracle_target_dist.argtypes = [P, I, I, D, I, P]
         L.oracle_draft_dist.argtypes = [P, I, D, I, P]
         L.oracle_argmax_row.argtypes = [P, I, I]
         L.oracle_set_variant.argtypes = [I]
         for f in ("oracle_verify_chain", "oracle_verify_tree_greedy", "oracle_accept_rate",
-                  "oracle_verify_tree_sample",
+                  "oracle_verify_tree_sample", "oracle_tree_expand", "oracle_tree_rerank",
                   "oracle_target_dist", "oracle_draft_dist", "oracle_argmax_row",
                   "oracle_max_threads"):
             getattr(L, f).restype = I
@@ -146,6 +148,36 @@ def verify_tree_sample(logits, dtype, draft_probs, node_tokens, uniforms, parent
                                          _p(out["m_draw"]))
     if rc != 0:
         raise ValueError(f"oracle_verify_tree_sample rejected its arguments ({rc})")
+    return out
+
+
+def tree_expand(draft_probs, node_values, top_k, k_next):
+    """One EAGLE-2 expansion layer: child tokens [B,E,K], child values [B,E,K] (float32) and
+    the k_next flat child indices of highest value [B,k_next]."""
+    q = np.ascontiguousarray(draft_probs, dtype=np.float32)
+    B, E, V = q.shape
+    nv = np.ascontiguousarray(node_values, dtype=np.float32).reshape(B, E)
+    out = dict(tokens=np.empty((B, E, top_k), np.int32), values=np.empty((B, E, top_k), np.float32),
+               next=np.empty((B, k_next), np.int32))
+    rc = lib().oracle_tree_expand(_p(q), _p(nv), B, E, V, int(top_k), int(k_next), _p(out["tokens"]),
+                                  _p(out["values"]), _p(out["next"]))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_expand rejected its arguments ({rc})")
+    return out
+
+
+def tree_rerank(parents, values, m):
+    """EAGLE-2 reranking: kept nodes in flattened order [B,m], their parents' flattened
+    positions [B,m] (0 = root) and the ancestor mask [B,m+1,m+1] (uint8)."""
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    B, M = par.shape
+    v = np.ascontiguousarray(values, dtype=np.float32).reshape(B, M)
+    out = dict(nodes=np.empty((B, m), np.int32), parent_pos=np.empty((B, m), np.int32),
+               mask=np.empty((B, m + 1, m + 1), np.uint8))
+    rc = lib().oracle_tree_rerank(_p(par), _p(v), B, M, int(m), _p(out["nodes"]), _p(out["parent_pos"]),
+                                  _p(out["mask"]))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_rerank rejected its arguments ({rc})")
     return out
 
 

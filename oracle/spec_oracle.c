@@ -565,3 +565,160 @@ int oracle_verify_tree_sample(const void* logits, int dtype, const float* q, con
     free(depth);
     return 0;
 }
+
+/*
+ * EAGLE-2 draft-tree construction ([E2] section 4).  The value of a node is the
+ * product of the draft model's confidences along its path from the root
+ * (section 4.1; the printed formula is lost, the text states it); the
+ * expansion phase feeds the top-k nodes of the newest layer, by value, to the
+ * draft model, and each of them gets the draft's top-k tokens as children
+ * (section 4.1); the reranking phase keeps the m nodes of highest value over
+ * the whole tree, the shallower node first among equal values, which keeps the
+ * selection a connected tree, flattens it and masks each token to its ancestors
+ * (section 4.2).
+ *
+ * Readings (the pages fix none of these): values and their products are
+ * float32 (value_child = value_parent * q(token), one float32 multiply), so
+ * both implementations take every ordering decision on the same numbers; a
+ * node's children are its draft row's top_k tokens by probability, larger
+ * first, lower index on ties; among equal keys the lower index wins; the
+ * selection is flattened in its ranking order (parents come first: a child's
+ * value never exceeds its parent's and ties go to the shallower node).
+ */
+
+typedef struct { float v; int i; } fi_t;
+static int cmp_fdesc_then_index(const void* a, const void* b) {
+    const fi_t* x = (const fi_t*)a;
+    const fi_t* y = (const fi_t*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->i > y->i) - (x->i < y->i);
+}
+
+/*
+ * One expansion layer for B batch rows.  q [B][E][V]: the draft distribution at
+ * each of the E nodes being expanded; node_value [B][E].  Outputs:
+ * child_token [B][E][K] (the row's K most probable tokens), child_value
+ * [B][E][K] (node value times the token's probability, in float32), next
+ * [B][k_next] (flat indices e*K + i of the k_next children of highest value,
+ * lower flat index first among equals).  A row with a NaN, negative or +inf
+ * probability, or a node value that is NaN, negative or +inf, is an error: its
+ * outputs are all -1 (values NaN).
+ */
+int oracle_tree_expand(const float* q, const float* node_value, int B, int E, int V, int K, int k_next,
+                       int32_t* child_token, float* child_value, int32_t* next) {
+    if (B <= 0 || E <= 0 || V <= 0 || K <= 0 || K > V || k_next <= 0 || k_next > E * K) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        int err = 0;
+        fi_t* row = (fi_t*)malloc(sizeof(fi_t) * (size_t)V);
+        fi_t* kids = (fi_t*)malloc(sizeof(fi_t) * (size_t)E * K);
+        for (int e = 0; e < E && !err; ++e) {
+            const float* qr = q + ((size_t)b * E + e) * V;
+            const float nv = node_value[(size_t)b * E + e];
+            if (!q_ok(nv)) err = 1;
+            for (int i = 0; i < V; ++i) {
+                if (!q_ok(qr[i])) err = 1;
+                row[i].v = qr[i];
+                row[i].i = i;
+            }
+            if (err) break;
+            qsort(row, (size_t)V, sizeof(fi_t), cmp_fdesc_then_index);
+            for (int t = 0; t < K; ++t) {
+                const size_t o = ((size_t)b * E + e) * K + t;
+                child_token[o] = row[t].i;
+                volatile float prod = nv * row[t].v;          /* one float32 rounding */
+                child_value[o] = prod;
+                kids[e * K + t].v = prod;
+                kids[e * K + t].i = e * K + t;
+            }
+        }
+        if (err) {
+            for (int o = 0; o < E * K; ++o) {
+                child_token[(size_t)b * E * K + o] = -1;
+                child_value[(size_t)b * E * K + o] = NAN;
+            }
+            for (int t = 0; t < k_next; ++t) next[(size_t)b * k_next + t] = -1;
+        } else {
+            qsort(kids, (size_t)E * K, sizeof(fi_t), cmp_fdesc_then_index);
+            for (int t = 0; t < k_next; ++t) next[(size_t)b * k_next + t] = kids[t].i;
+        }
+        free(row);
+        free(kids);
+    }
+    return 0;
+}
+
+typedef struct { float v; int d; int i; } fdi_t;
+static int cmp_rerank(const void* a, const void* b) {
+    const fdi_t* x = (const fdi_t*)a;
+    const fdi_t* y = (const fdi_t*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    if (x->d != y->d) return x->d < y->d ? -1 : 1;
+    return (x->i > y->i) - (x->i < y->i);
+}
+
+/*
+ * Reranking for B batch rows of M candidate nodes (the root excluded).
+ * parent [B][M]: the parent's candidate index, -1 for a child of the root,
+ * else < the node's own index; value [B][M] (float32).  Keeps the m nodes
+ * first in the order (value descending, depth ascending, index ascending) and
+ * flattens them in that order after the root (position 0).  Outputs:
+ * node [B][m] (candidate index at flattened position p + 1), parent_pos [B][m]
+ * (the flattened position of its parent, 0 for the root), mask [B][m+1][m+1]
+ * (1 where the column is the row's own position or one of its ancestors').
+ * Errors (outputs -1, mask 0): a parent index out of range or not below the
+ * node's, a NaN value, or a kept node whose parent is not kept (values that
+ * grow along a path).
+ */
+int oracle_tree_rerank(const int32_t* parent, const float* value, int B, int M, int m,
+                       int32_t* node, int32_t* parent_pos, uint8_t* mask) {
+    if (B <= 0 || M <= 0 || m <= 0 || m > M) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        const int32_t* pr = parent + (size_t)b * M;
+        const float* vr = value + (size_t)b * M;
+        int32_t* on = node + (size_t)b * m;
+        int32_t* op = parent_pos + (size_t)b * m;
+        uint8_t* mk = mask + (size_t)b * (m + 1) * (m + 1);
+        int err = 0;
+        fdi_t* key = (fdi_t*)malloc(sizeof(fdi_t) * (size_t)M);
+        int* depth = (int*)malloc(sizeof(int) * (size_t)M);
+        int* pos = (int*)malloc(sizeof(int) * (size_t)M);
+        for (int i = 0; i < M; ++i) {
+            if (pr[i] < -1 || pr[i] >= i || isnan(vr[i])) { err = 1; break; }
+            depth[i] = pr[i] < 0 ? 1 : depth[pr[i]] + 1;
+            key[i].v = vr[i];
+            key[i].d = depth[i];
+            key[i].i = i;
+            pos[i] = -1;
+        }
+        memset(mk, 0, (size_t)(m + 1) * (m + 1));
+        if (!err) {
+            qsort(key, (size_t)M, sizeof(fdi_t), cmp_rerank);
+            for (int p = 0; p < m; ++p) pos[key[p].i] = p + 1;
+            for (int p = 0; p < m && !err; ++p) {
+                const int i = key[p].i;
+                on[p] = i;
+                op[p] = pr[i] < 0 ? 0 : pos[pr[i]];
+                if (op[p] < 0) err = 1;                       /* parent not kept */
+            }
+        }
+        if (!err) {
+            mk[0] = 1;
+            for (int p = 0; p < m; ++p) {
+                uint8_t* r = mk + (size_t)(p + 1) * (m + 1);
+                r[0] = 1;
+                for (int i = on[p]; i >= 0; i = pr[i]) r[pos[i]] = 1;
+            }
+        } else {
+            for (int p = 0; p < m; ++p) { on[p] = -1; op[p] = -1; }
+            memset(mk, 0, (size_t)(m + 1) * (m + 1));
+        }
+        free(key);
+        free(depth);
+        free(pos);
+    }
+    return 0;
+}

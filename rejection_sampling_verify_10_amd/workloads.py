@@ -37,6 +37,14 @@ children are drawn), then for each node ``p`` in order its children's tokens,
 independently, from the draft model's sampling distribution at ``p`` (step
 5), and last the N verification uniforms.
 
+Draft-tree construction (EAGLE-2) draws, per batch row: for an expansion
+layer, E draft rows as in step 3 (q = softmax(z + sigma*N(0,1)) of a fresh
+target-like row) and the E expanded nodes' values, sorted descending in
+(0.05, 1]; for reranking, a layered candidate tree -- each layer gives k
+children to k nodes picked at random from the layer before -- whose node
+values are the parent's value times a confidence in (0, 1] (float32; every
+fourth tree draws confidences from a coarse grid so that equal values occur).
+
 The value distribution follows the workloads described for the method: a
 Zipf-like ``-1.1*ln(rank)`` prior plus Gaussian spread gives a long-tailed
 next-token distribution, and the draft is the same distribution seen through
@@ -273,6 +281,79 @@ def make_tree_sampled(B: int, V: int, *, parents: np.ndarray = EAGLE_TREE_PARENT
     return SampledTreeInputs(B, N, V, dtype, float(temperature), int(top_k), logits, q, tok, u, parents)
 
 
+@dataclasses.dataclass
+class ExpandInputs:
+    """Inputs of one EAGLE-2 expansion layer."""
+    B: int
+    E: int
+    V: int
+    top_k: int
+    k_next: int
+    draft_probs: np.ndarray    # [B, E, V] float32
+    node_values: np.ndarray    # [B, E] float32
+
+
+@dataclasses.dataclass
+class RerankInputs:
+    """A batch of candidate draft trees for EAGLE-2 reranking (root excluded)."""
+    B: int
+    M: int
+    m: int
+    parents: np.ndarray        # [B, M] int32, -1 = child of the root, else < own index
+    values: np.ndarray         # [B, M] float32
+
+
+def make_expand(B: int, E: int, V: int, *, top_k: int, k_next: int, sigma: float = 0.5, config_id: int,
+                seed: int, threads: Optional[int] = None) -> ExpandInputs:
+    """Draw one expansion-layer input set (see the module docstring)."""
+    log_rank = _log_rank_table(V)
+    q = np.empty((B, E, V), dtype=np.float32)
+    nv = np.empty((B, E), dtype=np.float32)
+
+    def one(b: int) -> None:
+        rng = np.random.default_rng([config_id, seed, b])
+        z = _target_rows(rng, E, V, log_rank)
+        nd = rng.standard_normal((E, V), dtype=np.float32)
+        q[b] = _softmax64(z.astype(np.float64) + sigma * nd.astype(np.float64)).astype(np.float32)
+        nv[b] = np.sort(rng.uniform(0.05, 1.0, E))[::-1].astype(np.float32)
+
+    with ThreadPoolExecutor(threads or _workers()) as ex:
+        list(ex.map(one, range(B)))
+    return ExpandInputs(B, E, V, int(top_k), int(k_next), q, nv)
+
+
+def make_rerank(B: int, *, k: int, depth: int, m: int, config_id: int, seed: int) -> RerankInputs:
+    """Draw B layered candidate trees of k children per expanded node (see the module docstring)."""
+    M = k + (depth - 1) * k * k
+    par = np.empty((B, M), dtype=np.int32)
+    val = np.empty((B, M), dtype=np.float32)
+    for b in range(B):
+        rng = np.random.default_rng([config_id, seed, b])
+        coarse = b % 4 == 3
+
+        def conf(n):
+            if coarse:
+                return (rng.integers(1, 5, n) / 4.0).astype(np.float32)
+            return rng.uniform(1e-3, 1.0, n).astype(np.float32)
+
+        par[b, :k] = -1
+        val[b, :k] = conf(k)
+        layer = list(range(k))
+        nxt = k
+        for _ in range(depth - 1):
+            picked = rng.choice(layer, size=k, replace=False)
+            new = []
+            for p in picked:
+                c = conf(k)
+                for j in range(k):
+                    par[b, nxt] = p
+                    val[b, nxt] = np.float32(val[b, p]) * c[j]
+                    new.append(nxt)
+                    nxt += 1
+            layer = new
+    return RerankInputs(B, M, int(m), par, val)
+
+
 # The workloads, by index.  Each entry builds inputs for a seed, with
 # optional size overrides used by the smaller parity cases.
 CONFIG_NAMES = {
@@ -282,12 +363,13 @@ CONFIG_NAMES = {
     3: "tree-greedy B=32 N=27 V=32000 bf16",
     4: "chain B=512 K=8 V=128256 bf16 T=1",
     5: "tree-sample B=32 N=27 V=32000 bf16 T=1",
+    6: "eagle2-expand B=64 E=10 V=128256 top_k=10 k_next=10",
 }
 
 
 def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int] = None,
            V: Optional[int] = None, threads: Optional[int] = None):
-    """Inputs for workload ``cid`` (0..5), optionally with smaller B/K/V."""
+    """Inputs for workload ``cid`` (0..6), optionally with smaller B/K/V (K: expanded nodes for 6)."""
     if cid == 0:
         return make_chain(B or 1, K or 4, V or 1000, dtype=DTYPE_F32, temperature=1.0, top_k=0,
                           sigma=sigma_const(0.5), config_id=0, seed=seed, threads=threads)
@@ -306,6 +388,9 @@ def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int]
     if cid == 5:
         return make_tree_sampled(B or 32, V or 32000, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
                                  sigma=0.5, config_id=5, seed=seed, threads=threads)
+    if cid == 6:
+        return make_expand(B or 64, K or 10, V or 128256, top_k=10, k_next=10, sigma=0.5, config_id=6, seed=seed,
+                           threads=threads)
     raise ValueError(f"unknown workload {cid}")
 
 

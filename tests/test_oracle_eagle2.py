@@ -1,0 +1,113 @@
+"""Pins of the oracle's EAGLE-2 draft-tree construction ("EAGLE-2: Faster Inference
+of Language Models with Dynamic Draft Trees", section 4).
+
+Each pin restates a property the pages give, or reduces the step to a library
+routine, independently of the oracle's own code:
+- expansion: a node's children are its draft row's most probable tokens (a
+  stable sort), a child's value is its parent's value times the token's
+  probability (one float32 multiply, numpy's), the next layer is the
+  highest-valued children (a stable sort);
+- reranking: the kept nodes are the first m in (value descending, shallower
+  first, lower index), the selection stays a connected tree (the pages' reason
+  for the tie rule), it is flattened parents-first, and the mask holds exactly
+  each token's ancestors (a separate walk up the parents).
+"""
+
+import numpy as np
+import pytest
+
+from rejection_sampling_verify_10_amd import workloads as W
+
+
+@pytest.mark.parametrize("E,V,K,kn", [(1, 50, 4, 4), (3, 1000, 5, 7), (10, 2048, 10, 10), (4, 64, 64, 100)])
+def test_expand_is_sorts_and_float32_products(orc, E, V, K, kn):
+    e = W.make_expand(6, E, V, top_k=K, k_next=kn, config_id=31, seed=E)
+    q = e.draft_probs.copy()
+    q[2, 0, 7] = q[2, 0, 3]                       # a tie inside the top of a row
+    q[2, 0, [3, 7]] = q[2, 0].max()
+    o = orc.tree_expand(q, e.node_values, K, kn)
+    for b in range(e.B):
+        for n in range(E):
+            order = np.lexsort((np.arange(V), -q[b, n].astype(np.float64)))[:K]
+            assert np.array_equal(o["tokens"][b, n], order)
+            want = (np.float32(e.node_values[b, n]) * q[b, n, order]).astype(np.float32)
+            assert np.array_equal(o["values"][b, n].view(np.uint32), want.view(np.uint32))
+        flat = o["values"][b].reshape(-1).astype(np.float64)
+        nxt = np.lexsort((np.arange(E * K), -flat))[:kn]
+        assert np.array_equal(o["next"][b], nxt)
+    assert list(o["tokens"][2, 0, :2]) == [3, 7]   # equal probabilities: the lower index first
+
+
+def test_expand_error_rows(orc):
+    e = W.make_expand(5, 3, 300, top_k=4, k_next=3, config_id=32, seed=0)
+    q, nv = e.draft_probs.copy(), e.node_values.copy()
+    q[1, 2, 5] = np.nan
+    q[2, 0, 9] = -0.1
+    nv[3, 1] = np.inf
+    o = orc.tree_expand(q, nv, 4, 3)
+    for b in (1, 2, 3):
+        assert np.all(o["tokens"][b] == -1) and np.all(o["next"][b] == -1) and np.all(np.isnan(o["values"][b]))
+    for b in (0, 4):
+        assert np.all(o["tokens"][b] >= 0) and np.all(o["next"][b] >= 0)
+
+
+def _depths(par):
+    d = np.zeros(len(par), np.int64)
+    for i, p in enumerate(par):
+        d[i] = 1 if p < 0 else d[p] + 1
+    return d
+
+
+def _ancestors(par, i):
+    out = []
+    while i >= 0:
+        out.append(i)
+        i = par[i]
+    return out
+
+
+@pytest.mark.parametrize("k,depth,m", [(2, 3, 5), (4, 4, 10), (10, 6, 60), (8, 5, 200)])
+def test_rerank_is_a_sort_and_stays_connected(orc, k, depth, m):
+    r = W.make_rerank(8, k=k, depth=depth, m=m, config_id=33, seed=k)
+    o = orc.tree_rerank(r.parents, r.values, m)
+    for b in range(r.B):
+        par, val = r.parents[b], r.values[b]
+        d = _depths(par)
+        order = np.lexsort((np.arange(r.M), d, -val.astype(np.float64)))[:m]
+        assert np.array_equal(o["nodes"][b], order), b
+        pos = {int(n): p + 1 for p, n in enumerate(order)}
+        for p, n in enumerate(order):
+            want_parent = 0 if par[n] < 0 else pos[int(par[n])]   # KeyError = disconnected
+            assert o["parent_pos"][b, p] == want_parent and want_parent < p + 1
+            row = o["mask"][b, p + 1]
+            want = np.zeros(m + 1, np.uint8)
+            want[0] = 1
+            for a in _ancestors(par, int(n)):
+                want[pos[a]] = 1
+            assert np.array_equal(row, want)
+        assert o["mask"][b, 0, 0] == 1 and o["mask"][b, 0, 1:].sum() == 0
+
+
+def test_rerank_ties_go_to_the_shallower_node(orc):
+    """Every confidence 1: all values equal, so the kept nodes are the shallowest ones
+    (breadth-first), and the selection is connected whatever m is."""
+    r = W.make_rerank(3, k=3, depth=4, m=10, config_id=34, seed=0)
+    val = np.ones_like(r.values)
+    for m in (1, 3, 4, 10, r.M):
+        o = orc.tree_rerank(r.parents, val, m)
+        d = _depths(r.parents[0])
+        assert np.all(np.diff(d[o["nodes"][0]]) >= 0)
+        assert np.all(o["nodes"] >= 0)
+
+
+def test_rerank_error_rows(orc):
+    r = W.make_rerank(4, k=3, depth=3, m=6, config_id=35, seed=0)
+    par, val = r.parents.copy(), r.values.copy()
+    val[1, 3] = 0.999                 # a child above its parent (node 3's parent is a root child)
+    val[1, int(par[1, 3])] = 1e-6
+    par[2, 5] = 7                     # a parent index not below the node's
+    val[3, 0] = np.nan
+    o = orc.tree_rerank(par, val, 6)
+    for b in (1, 2, 3):
+        assert np.all(o["nodes"][b] == -1) and o["mask"][b].sum() == 0, b
+    assert np.all(o["nodes"][0] >= 0)
