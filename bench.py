@@ -53,6 +53,9 @@ WORKLOADS = {
     5: dict(name="sampled static-tree verify B=32 N=27 (depth 5) V=32000, bf16 target logits, fp32 draft probs, "
                  "T=1, no top-k",
             kernel="tree_sample_kernel", copies=4, oracle_rows=32, dtype="bf16 in, f64 probabilities"),
+    6: dict(name="EAGLE-2 expansion layer B=64 E=10 V=128256, fp32 draft probs, top_k=10 children per node, "
+                 "k_next=10 kept",
+            kernel="topk_chunk_kernel", copies=2, oracle_rows=8, dtype="f32 in, f32 select and value products"),
 }
 
 
@@ -129,6 +132,12 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
                       tree_path=None, parents=None) -> float:
     """Bytes the dominant kernel must move per launch (see the design notes).  For the trees,
     K is the node count N."""
+    if workload == 6:
+        # every draft row once; per chunk a sorted list of top_k (value, index) pairs plus count
+        # and flags written; the children (token, value) and the kept indices written
+        # (K is the number of expanded nodes E; the workload keeps k_next = top_k)
+        chunks = B * K * select_chunks(V, 4)
+        return B * K * V * 4 + chunks * (top_k * 8 + 8) + B * K * top_k * 8 + B * top_k * 4
     if workload == 5:
         # the walk: each visited node's target row once, the draft row of each visited node
         # where a residual was formed, z[x] and q[x] of every child tested, the tokens and
@@ -231,6 +240,7 @@ def main() -> int:
     ci = W.config(args.workload, seed=args.seed)
     tree = args.workload == 3
     sampled_tree = args.workload == 5
+    expand = args.workload == 6
     log(f"workload {args.workload}: {wl['name']} (inputs drawn in {time.time() - t0:.1f} s)")
 
     def to_dev(a):
@@ -238,7 +248,7 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    esz = 2 if ci.dtype == W.DTYPE_BF16 else 4
+    esz = 2 if getattr(ci, "dtype", W.DTYPE_F32) == W.DTYPE_BF16 else 4
     if tree:
         B, K, V, T, top_k = ci.B, ci.N, ci.V, 0.0, 0
         depth = [0] * K
@@ -252,6 +262,15 @@ def main() -> int:
         ws = R.new_workspace(R.tree_workspace_bytes(B, K, V, ci.dtype), dev)
         parents = ci.parents.tolist()
         rows_per_step = B * K                  # node rows verified
+    elif expand:
+        B, K, V, T, top_k = ci.B, ci.E, ci.V, 1.0, ci.top_k
+        base = [to_dev(ci.draft_probs), to_dev(ci.node_values)]
+        xt = torch.empty((B, K, top_k), dtype=torch.int32, device=dev)
+        xv = torch.empty((B, K, top_k), dtype=torch.float32, device=dev)
+        xn = torch.empty((B, ci.k_next), dtype=torch.int32, device=dev)
+        alen = torch.zeros((B,), dtype=torch.int32, device=dev)
+        ws = R.new_workspace(R.tree_expand_workspace_bytes(B, K, V, top_k), dev)
+        rows_per_step = B * K                  # draft rows expanded
     elif sampled_tree:
         B, K, V, T, top_k = ci.B, ci.N, ci.V, ci.temperature, ci.top_k
         depth = [0] * K
@@ -279,6 +298,9 @@ def main() -> int:
         if tree:
             z, nt = sets[i % len(sets)]
             R.verify_tree_greedy(z, nt, parents, out=(path, tok, alen), workspace=ws)
+        elif expand:
+            q, nv = sets[i % len(sets)]
+            R.tree_expand(q, nv, top_k, ci.k_next, out=(xt, xv, xn), workspace=ws)
         elif sampled_tree:
             z, q, nt, u = sets[i % len(sets)]
             R.verify_tree_sample(z, q, nt, u, parents, T, top_k, out=(path, tok, alen))
@@ -320,8 +342,9 @@ def main() -> int:
     achieved = alg / (k_ms * 1e-3) / 1e9
     step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
-        f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak); accept_len histogram "
-        f"{np.bincount(al[al >= 0], minlength=(K + 1) if not (tree or sampled_tree) else 1).tolist()}")
+        f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak)"
+        + ("" if expand else "; accept_len histogram "
+           f"{np.bincount(al[al >= 0], minlength=(K + 1) if not (tree or sampled_tree) else 1).tolist()}"))
     traffic = counter_traffic(args.workload)
     probe = read_probe_gbps(R, torch, dev)
     log(f"read probe {probe:.0f} GB/s; {wl['kernel']} at {100 * achieved / probe:.1f}% of it")
@@ -337,6 +360,8 @@ def main() -> int:
         while True:
             if tree:
                 oracle.verify_tree_greedy(ci.logits[:rows], ci.dtype, ci.node_tokens[:rows], ci.parents)
+            elif expand:
+                oracle.tree_expand(ci.draft_probs[:rows], ci.node_values[:rows], top_k, ci.k_next)
             elif sampled_tree:
                 oracle.verify_tree_sample(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.node_tokens[:rows],
                                           ci.uniforms[:rows], ci.parents, T, top_k)
@@ -370,6 +395,9 @@ def main() -> int:
                     "parallelism": "single GPU"} if tree else
                    {"workload": wl["name"], "B": B, "N": K, "V": V, "temperature": T, "top_k": top_k,
                     "input_copies": wl["copies"], "parallelism": "single GPU"} if sampled_tree else
+                   {"workload": wl["name"], "B": B, "E": K, "V": V, "top_k": top_k, "k_next": ci.k_next,
+                    "rows": "expanded draft rows", "input_copies": wl["copies"], "parallelism": "single GPU"}
+                   if expand else
                    {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
                     "input_copies": wl["copies"], "parallelism": "single GPU"}),
         "step_algorithmic_GBps": step_alg_gbs,

@@ -93,6 +93,8 @@ enum {
 #define SPEC_MAX_NODES 64
 #define SPEC_TOPK_MAX 64
 #define SPEC_MAX_V (1 << 20)
+#define SPEC_EXPAND_MAX 1024     /* children of one expansion layer, E * top_k */
+#define SPEC_RERANK_MAX 1024     /* candidate nodes of one reranking */
 
 /* Human-readable text for a return code (static storage). */
 const char* spec_error_string(int code);
@@ -102,6 +104,7 @@ const char* spec_error_string(int code);
 size_t spec_chain_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k);
 size_t spec_tree_workspace_bytes(int B, int N, int V, spec_dtype_t dtype);
 size_t spec_accept_rate_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k);
+size_t spec_tree_expand_workspace_bytes(int B, int E, int V, int top_k);
 
 /*
  * spec_verify_chain -- batched verification of B drafted chains of K tokens.
@@ -212,6 +215,59 @@ int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const
                             int B, int N, int V, float temperature, int top_k,
                             int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len,
                             void* hip_stream);
+
+/*
+ * EAGLE-2 draft-tree construction ("EAGLE-2: Faster Inference of Language
+ * Models with Dynamic Draft Trees", section 4).  A node's value is the product
+ * of the draft model's confidences along its path (section 4.1).  Values and
+ * their products are float32, and every ordering is decided on those float32
+ * numbers, the lower index first among equal keys.
+ *
+ * spec_tree_expand -- one expansion layer (section 4.1).  For each batch row,
+ * each of the E nodes being expanded gets its draft row's top_k most probable
+ * tokens as children (larger probability first, lower token index on ties);
+ * a child's value is the node's value times the token's probability (one
+ * float32 multiply); out_next lists the k_next children of highest value (flat
+ * index e*top_k + i), the lower flat index first among equal values -- the
+ * nodes to expand next.
+ *
+ *   draft_probs      [B][E][V]        float32   device, read: the draft distribution at each expanded node
+ *   node_values      [B][E]           float32   device, read: the expanded nodes' values
+ *   out_child_tokens [B][E][top_k]    int32     device, written
+ *   out_child_values [B][E][top_k]    float32   device, written
+ *   out_next         [B][k_next]      int32     device, written
+ *   1 <= top_k <= min(V, SPEC_TOPK_MAX), 1 <= k_next <= E*top_k <= SPEC_EXPAND_MAX.
+ *   workspace: spec_tree_expand_workspace_bytes(B, E, V, top_k) bytes (leaves
+ *   scratch behind, like the other non-top-k-chain calls).
+ * A batch row whose draft rows hold a NaN, negative or +inf probability, or
+ * whose node value is not a finite non-negative number, gets -1 tokens and
+ * next indices and NaN values.
+ */
+int spec_tree_expand(const float* draft_probs, const float* node_values, int B, int E, int V, int top_k,
+                     int k_next, int32_t* out_child_tokens, float* out_child_values, int32_t* out_next,
+                     void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * spec_tree_rerank -- reranking (section 4.2).  For each batch row, M
+ * candidate nodes (the root excluded) with parent indices (-1: a child of the
+ * root; otherwise below the node's own index) and values.  The m nodes first
+ * in (value descending, depth ascending, index ascending) are kept -- the
+ * shallower node wins among equal values, so with values that never grow
+ * along a path the kept nodes form a connected tree -- and flattened in that
+ * order after the root (position 0).
+ *
+ *   parents        [B][M]           int32     device, read
+ *   values         [B][M]           float32   device, read
+ *   out_nodes      [B][m]           int32     device, written: candidate index at position p + 1
+ *   out_parent_pos [B][m]           int32     device, written: the parent's position (0 = root)
+ *   out_mask       [B][m+1][m+1]    uint8     device, written: 1 where the column is the row's
+ *                                             own position or an ancestor's (the attention mask)
+ *   1 <= m <= M <= SPEC_RERANK_MAX.  Needs no workspace.
+ * A batch row with a parent index out of range, a NaN value, or a kept node
+ * whose parent is not kept gets -1 outputs and an all-zero mask.
+ */
+int spec_tree_rerank(const int32_t* parents, const float* values, int B, int M, int m, int32_t* out_nodes,
+                     int32_t* out_parent_pos, uint8_t* out_mask, void* hip_stream);
 
 /*
  * spec_accept_rate -- alpha[b][k] = sum_i min(p'_k(i), q'_k(i)) for k < K, with

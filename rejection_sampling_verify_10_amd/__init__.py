@@ -54,6 +54,12 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_tree_greedy.restype = I
         L.spec_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P]
         L.spec_verify_tree_sample.restype = I
+        L.spec_tree_expand_workspace_bytes.argtypes = [I, I, I, I]
+        L.spec_tree_expand_workspace_bytes.restype = Z
+        L.spec_tree_expand.argtypes = [P, P, I, I, I, I, I, P, P, P, P, Z, P]
+        L.spec_tree_expand.restype = I
+        L.spec_tree_rerank.argtypes = [P, P, I, I, I, P, P, P, P]
+        L.spec_tree_rerank.restype = I
         L.spec_accept_rate.argtypes = [P, I, P, I, I, I, F, I, P, P, Z, P]
         L.spec_accept_rate.restype = I
         L.spec_profile_events.argtypes = [P, P]
@@ -258,6 +264,59 @@ def verify_tree_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor, n
                                        alen.data_ptr(), _stream(dev))
     _check(rc, "spec_verify_tree_sample")
     return path, toks, alen
+
+
+def tree_expand_workspace_bytes(B: int, E: int, V: int, top_k: int) -> int:
+    return int(lib().spec_tree_expand_workspace_bytes(B, E, V, top_k))
+
+
+def tree_expand(draft_probs: torch.Tensor, node_values: torch.Tensor, top_k: int, k_next: int, *,
+                out: Optional[Tuple[torch.Tensor, ...]] = None, workspace: Optional[torch.Tensor] = None):
+    """One EAGLE-2 expansion layer (``spec_tree_expand``).
+
+    draft_probs [B, E, V] f32, node_values [B, E] f32.  Returns (child tokens [B, E, top_k]
+    int32, child values [B, E, top_k] f32, next [B, k_next] int32 flat child indices).
+    """
+    B, E, V = draft_probs.shape
+    dev = draft_probs.device
+    _shape(node_values, "node_values", (B, E))
+    if out is None:
+        toks = torch.empty((B, E, top_k), dtype=torch.int32, device=dev)
+        vals = torch.empty((B, E, top_k), dtype=torch.float32, device=dev)
+        nxt = torch.empty((B, k_next), dtype=torch.int32, device=dev)
+    else:
+        toks, vals, nxt = out
+        _shape(toks, "out tokens", (B, E, top_k))
+        _shape(vals, "out values", (B, E, top_k))
+        _shape(nxt, "out next", (B, k_next))
+        _dev(toks, "out tokens", torch.int32)
+        _dev(vals, "out values", torch.float32)
+        _dev(nxt, "out next", torch.int32)
+    need = tree_expand_workspace_bytes(B, E, V, top_k)
+    wp, ws = _workspace(need, dev, workspace)
+    rc = lib().spec_tree_expand(_dev(draft_probs, "draft_probs", torch.float32),
+                                _dev(node_values, "node_values", torch.float32), B, E, V, int(top_k), int(k_next),
+                                toks.data_ptr(), vals.data_ptr(), nxt.data_ptr(), wp, need, _stream(dev))
+    _check(rc, "spec_tree_expand")
+    return toks, vals, nxt
+
+
+def tree_rerank(parents: torch.Tensor, values: torch.Tensor, m: int):
+    """EAGLE-2 reranking (``spec_tree_rerank``).
+
+    parents [B, M] int32 (-1 = child of the root), values [B, M] f32.  Returns (nodes [B, m],
+    parent positions [B, m]) int32 and the ancestor mask [B, m+1, m+1] uint8.
+    """
+    B, M = parents.shape
+    dev = parents.device
+    _shape(values, "values", (B, M))
+    nodes = torch.empty((B, m), dtype=torch.int32, device=dev)
+    ppos = torch.empty((B, m), dtype=torch.int32, device=dev)
+    mask = torch.empty((B, m + 1, m + 1), dtype=torch.uint8, device=dev)
+    rc = lib().spec_tree_rerank(_dev(parents, "parents", torch.int32), _dev(values, "values", torch.float32), B, M,
+                                int(m), nodes.data_ptr(), ppos.data_ptr(), mask.data_ptr(), _stream(dev))
+    _check(rc, "spec_tree_rerank")
+    return nodes, ppos, mask
 
 
 def accept_rate(target_logits: torch.Tensor, draft_probs: torch.Tensor, temperature: float = 1.0,

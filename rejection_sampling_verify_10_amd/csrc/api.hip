@@ -81,6 +81,24 @@ TopkLists carve_topk(Carver& c, int dtype, int V, int B, int P, int K, int top_k
     return t;
 }
 
+// Per-chunk lists of E draft rows per batch row, no target rows (tree expansion).
+TopkLists carve_draft_lists(Carver& c, int V, int B, int E, int top_k) {
+    TopkLists t{};
+    t.Ct = 0;
+    t.chunk_t = 0;
+    topk_chunking(V, 4, &t.Cd, &t.chunk_d);
+    t.Ub = static_cast<long>(E) * t.Cd;
+    const size_t units = static_cast<size_t>(B) * t.Ub;
+    t.vals = c.take<float>(units * kTopkMax);
+    t.idx = c.take<int32_t>(units * kTopkMax);
+    t.cnt = c.take<int32_t>(units);
+    t.flags = c.take<uint32_t>(units);
+    t.top_k = top_k;
+    t.draft_identity = 1;
+    t.invT = 1.0;
+    return t;
+}
+
 TopkChunkArgs topk_chunk_args(const void* target, const float* draft, int dtype, int B, int K, int V, int P,
                               const TopkLists& t) {
     TopkChunkArgs a{};
@@ -95,7 +113,7 @@ TopkChunkArgs topk_chunk_args(const void* target, const float* draft, int dtype,
     return a;
 }
 
-// Chunks per row must fit the row-merge kernel (<= 16).
+// A row's chunk lists are merged one count per lane: at most 64 chunks.
 bool topk_shape_ok(int dtype, int V) {
     int c1, e1, c2, e2;
     topk_chunking(V, esz_of(dtype), &c1, &e1);
@@ -449,6 +467,67 @@ int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const
     ta.out_accept_len = out_accept_len;
     ProfileScope prof;
     SV_TRY(launch_tree_sample(ta, static_cast<hipStream_t>(hip_stream), prof.timing()));
+    return SPEC_OK;
+}
+
+size_t spec_tree_expand_workspace_bytes(int B, int E, int V, int top_k) {
+    if (B < 1 || E < 1 || V < 1 || V > SPEC_MAX_V || top_k < 1 || top_k > SPEC_TOPK_MAX) return 0;
+    Carver c(nullptr);
+    carve_draft_lists(c, V, B, E, top_k);
+    return (c.off + 255) & ~static_cast<size_t>(255);
+}
+
+int spec_tree_expand(const float* draft_probs, const float* node_values, int B, int E, int V, int top_k,
+                     int k_next, int32_t* out_child_tokens, float* out_child_values, int32_t* out_next,
+                     void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!draft_probs || !node_values || !out_child_tokens || !out_child_values || !out_next) return SPEC_EINVAL;
+    if (B < 1 || E < 1 || V < 1 || top_k < 1 || top_k > V || k_next < 1 ||
+        static_cast<long>(k_next) > static_cast<long>(E) * top_k)
+        return SPEC_EINVAL;
+    if (V > SPEC_MAX_V || top_k > SPEC_TOPK_MAX || static_cast<long>(E) * top_k > SPEC_EXPAND_MAX)
+        return SPEC_EUNSUPPORTED;
+    if (!aligned(draft_probs, 4) || !aligned(node_values, 4) || !aligned(out_child_tokens, 4) ||
+        !aligned(out_child_values, 4) || !aligned(out_next, 4))
+        return SPEC_EINVAL;
+    const size_t need = spec_tree_expand_workspace_bytes(B, E, V, top_k);
+    int rc = check_workspace(workspace, workspace_bytes, need);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfileScope prof;
+    Carver c(workspace);
+    TreeExpandArgs ea{};
+    ea.tk = carve_draft_lists(c, V, B, E, top_k);
+    // the draft rows only: E positions, each with a draft row and no target row
+    SV_TRY(launch_topk_chunks(topk_chunk_args(nullptr, draft_probs, SPEC_F32, B, E, V, E, ea.tk), s, prof.timing()));
+    ea.node_values = node_values;
+    ea.B = B;
+    ea.E = E;
+    ea.K = top_k;
+    ea.k_next = k_next;
+    ea.out_tokens = out_child_tokens;
+    ea.out_values = out_child_values;
+    ea.out_next = out_next;
+    SV_TRY(launch_tree_expand(ea, s));
+    return SPEC_OK;
+}
+
+int spec_tree_rerank(const int32_t* parents, const float* values, int B, int M, int m, int32_t* out_nodes,
+                     int32_t* out_parent_pos, uint8_t* out_mask, void* hip_stream) {
+    if (!parents || !values || !out_nodes || !out_parent_pos || !out_mask) return SPEC_EINVAL;
+    if (B < 1 || M < 1 || m < 1 || m > M) return SPEC_EINVAL;
+    if (M > SPEC_RERANK_MAX) return SPEC_EUNSUPPORTED;
+    if (!aligned(parents, 4) || !aligned(values, 4) || !aligned(out_nodes, 4) || !aligned(out_parent_pos, 4))
+        return SPEC_EINVAL;
+    TreeRerankArgs ra{};
+    ra.parents = parents;
+    ra.values = values;
+    ra.B = B;
+    ra.M = M;
+    ra.m = m;
+    ra.out_nodes = out_nodes;
+    ra.out_parent_pos = out_parent_pos;
+    ra.out_mask = out_mask;
+    SV_TRY(launch_tree_rerank(ra, static_cast<hipStream_t>(hip_stream)));
     return SPEC_OK;
 }
 

@@ -142,6 +142,26 @@ struct TreeSampleArgs {
     int32_t* out_accept_len;
 };
 
+// EAGLE-2 draft-tree construction (eagle2.hip).
+constexpr int kExpandMax = 1024;    // children of one expansion layer (E * K)
+constexpr int kRerankMax = 1024;    // candidate nodes of one reranking
+struct TreeExpandArgs {
+    const float* node_values;   // [B][E]
+    int B, E, K, k_next;
+    TopkLists tk;               // the draft rows' per-chunk lists (draft units only)
+    int32_t* out_tokens;        // [B][E][K]
+    float* out_values;          // [B][E][K]
+    int32_t* out_next;          // [B][k_next]
+};
+struct TreeRerankArgs {
+    const int32_t* parents;     // [B][M]
+    const float* values;        // [B][M]
+    int B, M, m;
+    int32_t* out_nodes;         // [B][m]
+    int32_t* out_parent_pos;    // [B][m]
+    uint8_t* out_mask;          // [B][m+1][m+1]
+};
+
 struct AlphaArgs {
     const void* logits;
     int dtype;
@@ -179,6 +199,8 @@ hipError_t launch_chain_walk(const ChainArgs& a, double bracket, hipStream_t s, 
 hipError_t launch_chain_greedy(const ChainArgs& a, hipStream_t s);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t s);
 hipError_t launch_tree_sample(const TreeSampleArgs& a, hipStream_t s, Timing t = {});
+hipError_t launch_tree_expand(const TreeExpandArgs& a, hipStream_t s);
+hipError_t launch_tree_rerank(const TreeRerankArgs& a, hipStream_t s);
 hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_alpha_greedy(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);

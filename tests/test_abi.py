@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_symbols_exported(L):
     names = declared_functions()
     assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_tree_sample",
-            "spec_accept_rate"} <= set(names)
+            "spec_tree_expand", "spec_tree_rerank", "spec_accept_rate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -101,6 +101,32 @@ def test_tree_sample_argument_checks(L):
     assert call(V=(1 << 20) + 1) == EUNSUPPORTED
     big = (ctypes.c_int32 * 65)(*([-1] + list(range(64))))
     assert call(big, N=65) == EUNSUPPORTED
+
+
+def test_tree_expand_and_rerank_argument_checks(L):
+    def ex(**kw):
+        a = dict(q=FAKE, nv=FAKE, B=2, E=3, V=1000, K=4, kn=5, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return L.spec_tree_expand(a["q"], a["nv"], a["B"], a["E"], a["V"], a["K"], a["kn"], FAKE, FAKE, FAKE,
+                                  a["ws"], a["wsb"], None)
+    assert ex(q=None) == EINVAL
+    assert ex(K=0) == EINVAL
+    assert ex(K=2000) == EINVAL                           # more children than tokens
+    assert ex(kn=13) == EINVAL                            # more than E*top_k
+    assert ex(K=65, V=5000) == EUNSUPPORTED
+    assert ex(E=64, K=32, kn=4) == EUNSUPPORTED           # E*top_k beyond the limit
+    assert ex(wsb=16) == EWORKSPACE
+    assert L.spec_tree_expand_workspace_bytes(2, 3, 1000, 4) > 0
+    assert L.spec_tree_expand_workspace_bytes(2, 3, 1000, 65) == 0
+
+    def rr(**kw):
+        a = dict(p=FAKE, v=FAKE, B=2, M=50, m=10)
+        a.update(kw)
+        return L.spec_tree_rerank(a["p"], a["v"], a["B"], a["M"], a["m"], FAKE, FAKE, FAKE, None)
+    assert rr(p=None) == EINVAL
+    assert rr(m=0) == EINVAL
+    assert rr(m=51) == EINVAL
+    assert rr(M=1025, m=10) == EUNSUPPORTED
 
 
 def test_accept_rate_argument_checks(L):
