@@ -217,6 +217,25 @@ int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const
                             void* hip_stream);
 
 /*
+ * Per-row trees (a dynamic draft tree differs from one batch row to the next,
+ * e.g. the output of spec_tree_rerank with the root at position 0):
+ * spec_verify_tree_greedy_rows and spec_verify_tree_sample_rows are the two
+ * calls above with `parents` a DEVICE array [B][N] (row b: parents[b][0] = -1,
+ * 0 <= parents[b][n] < n; a row that breaks this is an error row, accept_len
+ * -1) instead of parents_host, and out_path / out_tokens of N entries per batch
+ * row ([B][N], -1 padded).  Everything else is as above; the greedy call takes
+ * the workspace of spec_tree_workspace_bytes(B, N, V, dtype).
+ */
+int spec_verify_tree_greedy_rows(const void* target_logits, spec_dtype_t dtype, const int32_t* node_tokens,
+                                 const int32_t* parents, int B, int N, int V, int32_t* out_path,
+                                 int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+int spec_verify_tree_sample_rows(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                                 const int32_t* node_tokens, const float* uniforms, const int32_t* parents,
+                                 int B, int N, int V, float temperature, int top_k, int32_t* out_path,
+                                 int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream);
+
+/*
  * EAGLE-2 draft-tree construction ("EAGLE-2: Faster Inference of Language
  * Models with Dynamic Draft Trees", section 4).  A node's value is the product
  * of the draft model's confidences along its path (section 4.1).  Values and

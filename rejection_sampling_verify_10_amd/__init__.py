@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_tree_greedy.restype = I
         L.spec_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P]
         L.spec_verify_tree_sample.restype = I
+        L.spec_verify_tree_sample_rows.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P]
+        L.spec_verify_tree_sample_rows.restype = I
+        L.spec_verify_tree_greedy_rows.argtypes = [P, I, P, P, I, I, I, P, P, P, P, Z, P]
+        L.spec_verify_tree_greedy_rows.restype = I
         L.spec_tree_expand_workspace_bytes.argtypes = [I, I, I, I]
         L.spec_tree_expand_workspace_bytes.restype = Z
         L.spec_tree_expand.argtypes = [P, P, I, I, I, I, I, P, P, P, P, Z, P]
@@ -187,7 +191,8 @@ def verify_tree_greedy(target_logits: torch.Tensor, node_tokens: torch.Tensor, p
                        out: Optional[Tuple[torch.Tensor, ...]] = None, workspace: Optional[torch.Tensor] = None):
     """Greedy static-tree verification (``spec_verify_tree_greedy``).
 
-    target_logits [B, N, V], node_tokens [B, N] int32, parents: N host ints.
+    target_logits [B, N, V], node_tokens [B, N] int32, parents: N host ints (one static tree)
+    or a [B, N] int32 GPU tensor (a tree per batch row; then D = N - 1).
     Returns (path [B, D+1], tokens [B, D+1], accept_len [B]) int32 tensors.  ``out`` reuses
     output tensors and ``workspace`` a workspace, as for :func:`verify_chain`.
     """
@@ -195,30 +200,44 @@ def verify_tree_greedy(target_logits: torch.Tensor, node_tokens: torch.Tensor, p
     dev = target_logits.device
     code = _dtype_code(target_logits)
     _shape(node_tokens, "node_tokens", (B, N))
+    rows = isinstance(parents, torch.Tensor)
+    par, D = _tree_parents(parents, B, N)
+    path, toks, alen = _tree_outputs(out, B, D, dev)
+    need = tree_workspace_bytes(B, N, V, code)
+    wp, ws = _workspace(need, dev, workspace)
+    fn = lib().spec_verify_tree_greedy_rows if rows else lib().spec_verify_tree_greedy
+    rc = fn(_dev(target_logits, "target_logits"), code, _dev(node_tokens, "node_tokens", torch.int32), par, B, N, V,
+            path.data_ptr(), toks.data_ptr(), alen.data_ptr(), wp, need, _stream(dev))
+    _check(rc, "spec_verify_tree_greedy" + ("_rows" if rows else ""))
+    return path, toks, alen
+
+
+def _tree_parents(parents, B: int, N: int):
+    """A static tree (N host ints) -> (ctypes array, max depth); a tree per batch row
+    ([B, N] int32 GPU tensor) -> (its pointer, N - 1)."""
+    if isinstance(parents, torch.Tensor):
+        _shape(parents, "parents", (B, N))
+        return _dev(parents, "parents", torch.int32), N - 1
     if len(parents) != N:
         raise ValueError(f"parents must have {N} entries")
     par = (ctypes.c_int32 * N)(*[int(p) for p in parents])
     depth = [0] * N
     for n in range(1, N):
         depth[n] = depth[int(parents[n])] + 1 if 0 <= int(parents[n]) < n else 0
-    D = max(depth)
+    return par, max(depth)
+
+
+def _tree_outputs(out, B: int, D: int, dev):
     if out is None:
-        path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
-        toks = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
-        alen = torch.empty((B,), dtype=torch.int32, device=dev)
-    else:
-        path, toks, alen = out
-        _shape(path, "out path", (B, D + 1))
-        _shape(toks, "out tokens", (B, D + 1))
-        _shape(alen, "out accept_len", (B,))
-        for o, n in ((path, "out path"), (toks, "out tokens"), (alen, "out accept_len")):
-            _dev(o, n, torch.int32)
-    need = tree_workspace_bytes(B, N, V, code)
-    wp, ws = _workspace(need, dev, workspace)
-    rc = lib().spec_verify_tree_greedy(_dev(target_logits, "target_logits"), code,
-                                       _dev(node_tokens, "node_tokens", torch.int32), par, B, N, V,
-                                       path.data_ptr(), toks.data_ptr(), alen.data_ptr(), wp, need, _stream(dev))
-    _check(rc, "spec_verify_tree_greedy")
+        return (torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+                torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+                torch.empty((B,), dtype=torch.int32, device=dev))
+    path, toks, alen = out
+    _shape(path, "out path", (B, D + 1))
+    _shape(toks, "out tokens", (B, D + 1))
+    _shape(alen, "out accept_len", (B,))
+    for o, n in ((path, "out path"), (toks, "out tokens"), (alen, "out accept_len")):
+        _dev(o, n, torch.int32)
     return path, toks, alen
 
 
@@ -229,7 +248,8 @@ def verify_tree_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor, n
 
     target_logits [B, N, V] bf16/f32, draft_probs [B, N, V] f32 (row n: the draft
     distribution at node n), node_tokens [B, N] int32, uniforms [B, N] f32 (u[n] tests
-    node n, u[0] drives the final draw), parents: N host ints.  Returns (path [B, D+1],
+    node n, u[0] drives the final draw), parents: N host ints (one static tree) or a [B, N]
+    int32 GPU tensor (a tree per batch row; then D = N - 1).  Returns (path [B, D+1],
     tokens [B, D+1], accept_len [B]) int32 tensors; ``out`` reuses output tensors.
     """
     B, N, V = target_logits.shape
@@ -238,31 +258,14 @@ def verify_tree_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor, n
     _shape(draft_probs, "draft_probs", (B, N, V))
     _shape(node_tokens, "node_tokens", (B, N))
     _shape(uniforms, "uniforms", (B, N))
-    if len(parents) != N:
-        raise ValueError(f"parents must have {N} entries")
-    par = (ctypes.c_int32 * N)(*[int(p) for p in parents])
-    depth = [0] * N
-    for n in range(1, N):
-        depth[n] = depth[int(parents[n])] + 1 if 0 <= int(parents[n]) < n else 0
-    D = max(depth)
-    if out is None:
-        path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
-        toks = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
-        alen = torch.empty((B,), dtype=torch.int32, device=dev)
-    else:
-        path, toks, alen = out
-        _shape(path, "out path", (B, D + 1))
-        _shape(toks, "out tokens", (B, D + 1))
-        _shape(alen, "out accept_len", (B,))
-        for o, n in ((path, "out path"), (toks, "out tokens"), (alen, "out accept_len")):
-            _dev(o, n, torch.int32)
-    rc = lib().spec_verify_tree_sample(_dev(target_logits, "target_logits"), code,
-                                       _dev(draft_probs, "draft_probs", torch.float32),
-                                       _dev(node_tokens, "node_tokens", torch.int32),
-                                       _dev(uniforms, "uniforms", torch.float32), par, B, N, V,
-                                       float(temperature), int(top_k), path.data_ptr(), toks.data_ptr(),
-                                       alen.data_ptr(), _stream(dev))
-    _check(rc, "spec_verify_tree_sample")
+    rows = isinstance(parents, torch.Tensor)
+    par, D = _tree_parents(parents, B, N)
+    path, toks, alen = _tree_outputs(out, B, D, dev)
+    fn = lib().spec_verify_tree_sample_rows if rows else lib().spec_verify_tree_sample
+    rc = fn(_dev(target_logits, "target_logits"), code, _dev(draft_probs, "draft_probs", torch.float32),
+            _dev(node_tokens, "node_tokens", torch.int32), _dev(uniforms, "uniforms", torch.float32), par, B, N, V,
+            float(temperature), int(top_k), path.data_ptr(), toks.data_ptr(), alen.data_ptr(), _stream(dev))
+    _check(rc, "spec_verify_tree_sample" + ("_rows" if rows else ""))
     return path, toks, alen
 
 

@@ -414,12 +414,36 @@ int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype, const
     return SPEC_OK;
 }
 
+// Both tree-sample entry points: a static tree (host parents) or one per batch row (device).
+static int tree_sample_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                            const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
+                            const int32_t* parents_rows, int B, int N, int V, float temperature, int top_k,
+                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream);
+
 int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
                             const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
                             int B, int N, int V, float temperature, int top_k, int32_t* out_path,
                             int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream) {
-    if (!target_logits || !draft_probs || !node_tokens || !uniforms || !parents_host || !out_path ||
-        !out_tokens || !out_accept_len)
+    if (!parents_host) return SPEC_EINVAL;
+    return tree_sample_call(target_logits, dtype, draft_probs, node_tokens, uniforms, parents_host, nullptr, B, N,
+                            V, temperature, top_k, out_path, out_tokens, out_accept_len, hip_stream);
+}
+
+int spec_verify_tree_sample_rows(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                                 const int32_t* node_tokens, const float* uniforms, const int32_t* parents,
+                                 int B, int N, int V, float temperature, int top_k, int32_t* out_path,
+                                 int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream) {
+    if (!parents || !aligned(parents, 4)) return SPEC_EINVAL;
+    return tree_sample_call(target_logits, dtype, draft_probs, node_tokens, uniforms, nullptr, parents, B, N, V,
+                            temperature, top_k, out_path, out_tokens, out_accept_len, hip_stream);
+}
+
+static int tree_sample_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                            const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
+                            const int32_t* parents_rows, int B, int N, int V, float temperature, int top_k,
+                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream) {
+    if (!target_logits || !draft_probs || !node_tokens || !uniforms || !out_path || !out_tokens ||
+        !out_accept_len)
         return SPEC_EINVAL;
     if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EINVAL;
     if (B < 1 || N < 1 || V < 1 || !(temperature > 0.f) || isinf(temperature)) return SPEC_EINVAL;
@@ -427,28 +451,32 @@ int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const
     if (!aligned(target_logits, esz_of(dtype)) || !aligned(draft_probs, 4) || !aligned(node_tokens, 4) ||
         !aligned(uniforms, 4) || !aligned(out_path, 4) || !aligned(out_tokens, 4) || !aligned(out_accept_len, 4))
         return SPEC_EINVAL;
-    if (parents_host[0] != -1) return SPEC_EINVAL;
     TreeSampleArgs ta{};
-    int depth[SPEC_MAX_NODES];
-    int last_child[SPEC_MAX_NODES];
-    depth[0] = 0;
-    int D = 0;
-    for (int n = 0; n < N; ++n) {
-        ta.parent[n] = static_cast<int8_t>(parents_host[n] < 0 ? -1 : parents_host[n]);
-        ta.first_child[n] = -1;
-        ta.next_sibling[n] = -1;
-        last_child[n] = -1;
+    int D = N - 1;                     // per-row trees: outputs of N entries per batch row
+    if (parents_host) {
+        if (parents_host[0] != -1) return SPEC_EINVAL;
+        int depth[SPEC_MAX_NODES];
+        int last_child[SPEC_MAX_NODES];
+        depth[0] = 0;
+        D = 0;
+        for (int n = 0; n < N; ++n) {
+            ta.parent[n] = static_cast<int8_t>(parents_host[n] < 0 ? -1 : parents_host[n]);
+            ta.first_child[n] = -1;
+            ta.next_sibling[n] = -1;
+            last_child[n] = -1;
+        }
+        for (int n = 1; n < N; ++n) {
+            const int p = parents_host[n];
+            if (p < 0 || p >= n) return SPEC_EINVAL;
+            depth[n] = depth[p] + 1;
+            if (depth[n] > D) D = depth[n];
+            // children are appended in increasing node order
+            if (last_child[p] < 0) ta.first_child[p] = static_cast<int8_t>(n);
+            else ta.next_sibling[last_child[p]] = static_cast<int8_t>(n);
+            last_child[p] = n;
+        }
     }
-    for (int n = 1; n < N; ++n) {
-        const int p = parents_host[n];
-        if (p < 0 || p >= n) return SPEC_EINVAL;
-        depth[n] = depth[p] + 1;
-        if (depth[n] > D) D = depth[n];
-        // children are appended in increasing node order
-        if (last_child[p] < 0) ta.first_child[p] = static_cast<int8_t>(n);
-        else ta.next_sibling[last_child[p]] = static_cast<int8_t>(n);
-        last_child[p] = n;
-    }
+    ta.parents_rows = parents_rows;
     ta.logits = target_logits;
     ta.dtype = dtype;
     ta.q = draft_probs;
@@ -528,6 +556,42 @@ int spec_tree_rerank(const int32_t* parents, const float* values, int B, int M, 
     ra.out_parent_pos = out_parent_pos;
     ra.out_mask = out_mask;
     SV_TRY(launch_tree_rerank(ra, static_cast<hipStream_t>(hip_stream)));
+    return SPEC_OK;
+}
+
+int spec_verify_tree_greedy_rows(const void* target_logits, spec_dtype_t dtype, const int32_t* node_tokens,
+                                 const int32_t* parents, int B, int N, int V, int32_t* out_path,
+                                 int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+    if (!target_logits || !node_tokens || !parents || !out_path || !out_tokens || !out_accept_len)
+        return SPEC_EINVAL;
+    if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EINVAL;
+    if (B < 1 || N < 1 || V < 1) return SPEC_EINVAL;
+    if (N > SPEC_MAX_NODES || V > SPEC_MAX_V) return SPEC_EUNSUPPORTED;
+    if (!aligned(target_logits, esz_of(dtype)) || !aligned(node_tokens, 4) || !aligned(parents, 4) ||
+        !aligned(out_path, 4) || !aligned(out_tokens, 4) || !aligned(out_accept_len, 4))
+        return SPEC_EINVAL;
+    const size_t need = spec_tree_workspace_bytes(B, N, V, dtype);
+    int rc = check_workspace(workspace, workspace_bytes, need);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfileScope prof;
+    Carver c(workspace);
+    RowStats st = carve_rowstats(c, static_cast<size_t>(B) * N);
+    RowStatsArgs ra = rowstats_args(target_logits, dtype, V, N, N, B, true, 0.f, nullptr, 0, st);
+    SV_TRY(launch_rowstats(ra, s, prof.timing()));
+    TreeArgs ta{};
+    ta.node_tokens = node_tokens;
+    ta.B = B;
+    ta.N = N;
+    ta.V = V;
+    ta.D = N - 1;
+    ta.parents_rows = parents;
+    ta.st = st;
+    ta.out_path = out_path;
+    ta.out_tokens = out_tokens;
+    ta.out_accept_len = out_accept_len;
+    SV_TRY(launch_tree(ta, s));
     return SPEC_OK;
 }
 

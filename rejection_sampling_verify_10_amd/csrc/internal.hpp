@@ -113,8 +113,9 @@ struct TopkChainArgs {
 
 struct TreeArgs {
     const int32_t* node_tokens;
-    int B, N, V, D;
+    int B, N, V, D;             // per-row trees: D = N - 1 (the output stride is N)
     int16_t parents[64];
+    const int32_t* parents_rows;    // [B][N] device: a tree per batch row (parents unused), or null
     RowStats st;
     int32_t* out_path;
     int32_t* out_tokens;
@@ -137,6 +138,8 @@ struct TreeSampleArgs {
     int8_t parent[64];      // parent[0] = -1
     int8_t first_child[64];
     int8_t next_sibling[64];
+    const int32_t* parents_rows;    // [B][N] device: a tree per batch row (the arrays above unused;
+                                    // D = N - 1), or null
     int32_t* out_path;
     int32_t* out_tokens;
     int32_t* out_accept_len;

@@ -95,6 +95,9 @@ struct TsSmem {
     int toks[kTsMaxNodes];
     float gz[kTsMaxNodes];           // z[x_n] and q[x_n] of the current node's children n
     float gq[kTsMaxNodes];
+    int par[kTsMaxNodes];            // the batch row's tree: parent, first child, next sibling (-1: none)
+    int fch[kTsMaxNodes];
+    int nsib[kTsMaxNodes];
     int dec;                         // thread 0's decision: 0 reject, 1 accept, 2 error
     int seg;                         // draw: segment holding u*S, -1 for the fallback
     double base;                     // draw: weight before that segment
@@ -320,8 +323,32 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
     const char* zbase = static_cast<const char*>(a.logits) + static_cast<long>(b) * N * V * esz;
     const float* qbase = a.q + static_cast<long>(b) * N * V;
 
-    // E2 (every node token) and E5 (every uniform).
+    // The tree: the static one of the arguments, or the batch row's own, checked
+    // (parents[0] = -1, 0 <= parents[n] < n) and linked here.
     int bad = 0;
+    if (a.parents_rows) {
+        if (tid < N) {
+            const int p = a.parents_rows[static_cast<long>(b) * N + tid];
+            bad |= tid == 0 ? p != -1 : (p < 0 || p >= tid);
+            sm.par[tid] = p;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            // pushing children in decreasing node order leaves each list increasing
+            for (int n = 0; n < N; ++n) sm.fch[n] = sm.nsib[n] = -1;
+            for (int n = N - 1; n >= 1; --n) {
+                const int p = sm.par[n];
+                if (p < 0 || p >= n) continue;                  // (an error row)
+                sm.nsib[n] = sm.fch[p];
+                sm.fch[p] = n;
+            }
+        }
+    } else if (tid < N) {
+        sm.par[tid] = a.parent[tid];
+        sm.fch[tid] = a.first_child[tid];
+        sm.nsib[tid] = a.next_sibling[tid];
+    }
+    // E2 (every node token) and E5 (every uniform).
     if (tid < N) {
         bad |= !u_ok(ub[tid]);
         if (tid > 0) bad |= (tok[tid] < 0 || tok[tid] >= V);
@@ -349,7 +376,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
         const float* qr = qbase + static_cast<long>(c) * V;
         row.zr = zr;
         row.qr = qr;
-        const int first = a.first_child[c];
+        const int first = sm.fch[c];
         // Loads, in this order: the node's row unless parked already, the tested
         // children's z[x_n] and q[x_n] (lanes of wave 0), then the first child's
         // row.  The memory counter retires in order, so waiting for one set never
@@ -365,7 +392,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
             }
         }
         float gz = 0.f, gq = 0.f;
-        const bool gl = wid == 0 && lane > 0 && lane < N && a.parent[lane] == c;
+        const bool gl = wid == 0 && lane > 0 && lane < N && sm.par[lane] == c;
         if (gl) {
             const int x = tok[lane];
             gz = Elem<DT>::scalar(zr, x);
@@ -447,7 +474,7 @@ __global__ __launch_bounds__(kTsThreads, 1) void tree_sample_kernel(TreeSampleAr
         Zw = Z;
         Sqw = TR ? Sq : 1.0;
         int accepted = -1, q_checked = 0;
-        for (int n = first; n >= 0; n = a.next_sibling[n]) {
+        for (int n = first; n >= 0; n = sm.nsib[n]) {
             if (tid == 0) {
                 const float zx = sm.gz[n];
                 const float qx = sm.gq[n];

@@ -60,19 +60,31 @@ __global__ void chain_greedy_kernel(ChainArgs a) {
     if (diag) { diag[2 * K] = 1.f; diag[2 * K + 1] = 1.f; }
 }
 
-// Static tree, greedy: one wave per batch entry, one lane per node.
+// Tree, greedy: one wave per batch entry, one lane per node.  The tree is the
+// static one of the arguments, or the batch row's own (parents_rows), checked
+// here: parents[0] = -1 and 0 <= parents[n] < n, else the row is an error.
 __global__ __launch_bounds__(kWave) void tree_kernel(TreeArgs a) {
+    __shared__ int sp[kWave];
     const int b = blockIdx.x;
     const int n = threadIdx.x;
     const int N = a.N, D = a.D;
     const bool node = n < N;
     const long base = static_cast<long>(b) * N;
-    const int par = node ? a.parents[n] : -1;
+    bool bad = false;
+    if (a.parents_rows) {
+        int p = node ? a.parents_rows[base + n] : -1;
+        bad = node && (n == 0 ? p != -1 : (p < 0 || p >= n));
+        sp[n] = bad ? -1 : p;
+    } else {
+        sp[n] = node ? a.parents[n] : -1;
+    }
+    __syncthreads();
+    const int par = sp[n];
     int depth = 0;
-    for (int p = par; p >= 0; p = a.parents[p]) ++depth;
+    for (int p = par; p >= 0; p = sp[p]) ++depth;
     const int g = node ? a.st.arg[base + n] : -1;
     const int tok = (node && n > 0) ? a.node_tokens[base + n] : -1;
-    bool bad = node && a.st.flags[base + n] != 0u;
+    bad |= node && a.st.flags[base + n] != 0u;
     bad |= node && n > 0 && (tok < 0 || tok >= a.V);
     int32_t* op = a.out_path + static_cast<long>(b) * (D + 1);
     int32_t* ot = a.out_tokens + static_cast<long>(b) * (D + 1);
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(kWave) void tree_kernel(TreeArgs a) {
     __shared__ int path[kWave];
     if (n == 0) {
         int cur = best;
-        for (int t = dbest; t >= 0; --t) { path[t] = cur; cur = cur > 0 ? a.parents[cur] : 0; }
+        for (int t = dbest; t >= 0; --t) { path[t] = cur; cur = cur > 0 ? sp[cur] : 0; }
     }
     __syncthreads();
     if (n <= D) {

@@ -32,6 +32,7 @@ def declared_functions():
 def test_header_symbols_exported(L):
     names = declared_functions()
     assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_tree_sample",
+            "spec_verify_tree_greedy_rows", "spec_verify_tree_sample_rows",
             "spec_tree_expand", "spec_tree_rerank", "spec_accept_rate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n

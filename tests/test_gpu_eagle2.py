@@ -114,3 +114,81 @@ def test_two_layers_then_rerank(R, orc):
     r = W.RerankInputs(B, M, 16, par.astype(np.int32), val)
     o = run_rerank(R, orc, r, "two layers")
     assert np.all(o["nodes"] >= 0)
+
+
+def _row_oracle(orc, fn, B, N, parents_rows, *args):
+    """The oracle row by row with each row's own tree, outputs padded to N entries."""
+    path = np.full((B, N), -1, np.int32)
+    toks = np.full((B, N), -1, np.int32)
+    alen = np.full(B, -1, np.int32)
+    margins = []
+    for b in range(B):
+        par = parents_rows[b]
+        ok = par[0] == -1 and all(0 <= par[n] < n for n in range(1, N))
+        if not ok:
+            margins.append(None)
+            continue
+        o = fn(b, par, *args)
+        D1 = o["path"].shape[1]
+        path[b, :D1], toks[b, :D1], alen[b] = o["path"][0], o["tokens"][0], o["accept_len"][0]
+        margins.append(o)
+    return path, toks, alen, margins
+
+
+def _reranked_trees(R, B, N, seed):
+    """Per-row trees from the GPU's own reranking: parents[b][0] = -1, node p + 1's parent
+    is the kept node's parent position."""
+    import torch
+    r = W.make_rerank(B, k=4, depth=4, m=N - 1, config_id=66, seed=seed)
+    _, ppos, _ = R.tree_rerank(to_torch(r.parents), to_torch(r.values), N - 1)
+    torch.cuda.synchronize()
+    par = np.concatenate([np.full((B, 1), -1, np.int32), ppos.cpu().numpy()], axis=1)
+    return par
+
+
+def test_reranked_trees_verified_greedy(R, orc):
+    """Greedy verification with a tree per batch row (spec_verify_tree_greedy_rows), the
+    trees from spec_tree_rerank; one malformed row."""
+    import torch
+    B, N, V = 16, 21, 5000
+    par = _reranked_trees(R, B, N, 0)
+    par[5, 7] = 9                                    # a parent after its child: an error row
+    ti = W.make_tree(B, V, parents=W.EAGLE_TREE_PARENTS[:N], config_id=67, seed=0)
+    # node tokens: for half the nodes the argmax of the parent's row, so that paths go deep
+    z = ti.logits_f32()
+    tok = ti.node_tokens.copy()
+    for b in range(B):
+        for n in range(1, N):
+            p = par[b, n] if 0 <= par[b, n] < n else 0
+            tok[b, n] = int(np.argmax(z[b, p])) if (n + b) % 2 else (int(np.argmax(z[b, p])) + 1) % V
+    path, toks, alen = R.verify_tree_greedy(to_torch(ti.logits), to_torch(tok), torch.from_numpy(par).cuda())
+    torch.cuda.synchronize()
+    op, ot, oa, _ = _row_oracle(orc, lambda b, p: orc.verify_tree_greedy(ti.logits[b:b + 1], ti.dtype,
+                                                                        tok[b:b + 1], p), B, N, par)
+    assert np.array_equal(alen.cpu().numpy(), oa)
+    assert np.array_equal(path.cpu().numpy(), op) and np.array_equal(toks.cpu().numpy(), ot)
+    assert oa[5] == -1 and np.max(oa) >= 2
+
+
+def test_reranked_trees_verified_sampled(R, orc):
+    """Sampling verification with a tree per batch row (spec_verify_tree_sample_rows)."""
+    import torch
+    from parity import MARGIN
+    B, N, V = 24, 21, 8000
+    par = _reranked_trees(R, B, N, 1)
+    par[3, 0] = 0                                    # the root must have no parent: an error row
+    ts = W.make_tree_sampled(B, V, parents=W.EAGLE_TREE_PARENTS[:N], config_id=68, seed=0)
+    path, toks, alen = R.verify_tree_sample(to_torch(ts.logits), to_torch(ts.draft_probs), to_torch(ts.node_tokens),
+                                            to_torch(ts.uniforms), torch.from_numpy(par).cuda(), 1.0, 0)
+    torch.cuda.synchronize()
+    path, toks, alen = path.cpu().numpy(), toks.cpu().numpy(), alen.cpu().numpy()
+    op, ot, oa, outs = _row_oracle(
+        orc, lambda b, p: orc.verify_tree_sample(ts.logits[b:b + 1], ts.dtype, ts.draft_probs[b:b + 1],
+                                                 ts.node_tokens[b:b + 1], ts.uniforms[b:b + 1], p, 1.0, 0),
+        B, N, par)
+    assert alen[3] == -1 and oa[3] == -1
+    for b in range(B):
+        if np.array_equal(path[b], op[b]) and np.array_equal(toks[b], ot[b]):
+            continue
+        o = outs[b]                                  # a differing decision must sit on a tiny margin
+        assert o is not None and (np.nanmin(o["m_test"][0]) < MARGIN or o["m_draw"][0] < MARGIN), b
