@@ -46,6 +46,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(_LIB)
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         L.oracle_verify_chain.argtypes = [P, I, P, P, P, I, I, I, D, I, P, P, P, P, P, P, P, P]
+        L.oracle_verify_chain_p.argtypes = [P, I, P, P, P, I, I, I, D, I, D, P, P, P, P, P, P, P, P]
+        L.oracle_target_dist_p.argtypes = [P, I, I, D, I, D, P]
+        L.oracle_draft_dist_p.argtypes = [P, I, D, I, D, P]
         L.oracle_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P]
         L.oracle_accept_rate.argtypes = [P, I, P, I, I, I, D, I, P]
         L.oracle_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, D, I, P, P, P, P, P]
@@ -55,7 +58,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_draft_dist.argtypes = [P, I, D, I, P]
         L.oracle_argmax_row.argtypes = [P, I, I]
         L.oracle_set_variant.argtypes = [I]
-        for f in ("oracle_verify_chain", "oracle_verify_tree_greedy", "oracle_accept_rate",
+        for f in ("oracle_verify_chain", "oracle_verify_chain_p", "oracle_target_dist_p", "oracle_draft_dist_p",
+                  "oracle_verify_tree_greedy", "oracle_accept_rate",
                   "oracle_verify_tree_sample", "oracle_tree_expand", "oracle_tree_rerank",
                   "oracle_target_dist", "oracle_draft_dist", "oracle_argmax_row",
                   "oracle_max_threads"):
@@ -84,8 +88,9 @@ def max_threads() -> int:
     return int(lib().oracle_max_threads())
 
 
-def verify_chain(logits, dtype, draft_probs, draft_tokens, uniforms, temperature, top_k):
-    """Chain verification; returns a dict of numpy arrays (see spec_oracle.c)."""
+def verify_chain(logits, dtype, draft_probs, draft_tokens, uniforms, temperature, top_k, top_p=1.0):
+    """Chain verification (a nucleus cut at top_p < 1 after temperature and top-k); returns a
+    dict of numpy arrays (see spec_oracle.c)."""
     z = _logits_arr(logits, dtype)
     B, K1, V = z.shape
     K = K1 - 1
@@ -95,8 +100,8 @@ def verify_chain(logits, dtype, draft_probs, draft_tokens, uniforms, temperature
     out = dict(tokens=np.empty((B, K + 1), np.int32), accept_len=np.empty(B, np.int32),
                pk=np.empty((B, K)), qk=np.empty((B, K)), S=np.empty(B), py=np.empty(B),
                m_test=np.empty((B, K)), m_draw=np.empty(B))
-    rc = lib().oracle_verify_chain(_p(z), dtype, _p(q), _p(x), _p(u), B, K, V, float(temperature),
-                                   int(top_k), _p(out["tokens"]), _p(out["accept_len"]),
+    rc = lib().oracle_verify_chain_p(_p(z), dtype, _p(q), _p(x), _p(u), B, K, V, float(temperature),
+                                   int(top_k), float(top_p), _p(out["tokens"]), _p(out["accept_len"]),
                                    _p(out["pk"]), _p(out["qk"]), _p(out["S"]), _p(out["py"]),
                                    _p(out["m_test"]), _p(out["m_draw"]))
     if rc != 0:
@@ -193,19 +198,19 @@ def accept_rate(logits, dtype, draft_probs, temperature, top_k):
     return a
 
 
-def target_dist(row, dtype, temperature, top_k):
+def target_dist(row, dtype, temperature, top_k, top_p=1.0):
     """p' of one logit row (fp64, length V); None if the row is invalid."""
     z = _logits_arr(row, dtype).reshape(-1)
     p = np.empty(z.shape[0])
-    bad = lib().oracle_target_dist(_p(z), dtype, z.shape[0], float(temperature), int(top_k), _p(p))
+    bad = lib().oracle_target_dist_p(_p(z), dtype, z.shape[0], float(temperature), int(top_k), float(top_p), _p(p))
     return None if bad else p
 
 
-def draft_dist(row, temperature, top_k):
+def draft_dist(row, temperature, top_k, top_p=1.0):
     """q' of one row of draft probabilities (fp64); None if invalid."""
     q = np.ascontiguousarray(row, dtype=np.float32).reshape(-1)
     out = np.empty(q.shape[0])
-    bad = lib().oracle_draft_dist(_p(q), q.shape[0], float(temperature), int(top_k), _p(out))
+    bad = lib().oracle_draft_dist_p(_p(q), q.shape[0], float(temperature), int(top_k), float(top_p), _p(out))
     return None if bad else out
 
 

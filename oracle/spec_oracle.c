@@ -130,11 +130,35 @@ int oracle_argmax_row(const void* row, int dtype, int V) {
 
 int oracle_argmax_f32(const float* row, int V) { return oracle_argmax_row(row, ORC_F32, V); }
 
+/* Nucleus (top-p) cut of a distribution dist[0..V) in place: order the tokens
+ * by probability (larger first, lower index on ties), keep the shortest prefix
+ * whose mass reaches top_p, zero the rest and renormalise ([LEV] section 二:
+ * the sampling transforms travel with p and q).  top_p >= 1 keeps everything. */
+static void nucleus_cut(double* dist, int V, double top_p) {
+    if (!(top_p < 1.0)) return;
+    vi_t* tmp = (vi_t*)malloc(sizeof(vi_t) * (size_t)V);
+    for (int i = 0; i < V; ++i) { tmp[i].v = dist[i]; tmp[i].i = i; }
+    qsort(tmp, (size_t)V, sizeof(vi_t), cmp_desc_then_index);
+    double cum = 0.0;
+    int keep = 0;
+    while (keep < V && cum < top_p && tmp[keep].v > 0.0) { cum += tmp[keep].v; ++keep; }
+    for (int t = keep; t < V; ++t) dist[tmp[t].i] = 0.0;
+    double s = 0.0;
+    for (int i = 0; i < V; ++i) s += dist[i];
+    for (int i = 0; i < V; ++i) dist[i] /= s;
+    free(tmp);
+}
+
 /* Target distribution p' of one logit row under temperature T > 0 and top-k:
  * x = z/T, keep set S (all, or the top_k of x), p'_i = exp(x_i - m) / sum_S exp(x_j - m)
  * on S and 0 elsewhere ([LEV] section 二: p must already carry the temperature and
  * truncation).  Returns 0, or 1 when the row is invalid (E1). */
+int oracle_target_dist_p(const void* row, int dtype, int V, double T, int top_k, double top_p, double* p);
 int oracle_target_dist(const void* row, int dtype, int V, double T, int top_k, double* p) {
+    return oracle_target_dist_p(row, dtype, V, T, top_k, 1.0, p);
+}
+/* The same, then the nucleus cut at top_p. */
+int oracle_target_dist_p(const void* row, int dtype, int V, double T, int top_k, double top_p, double* p) {
     if (V <= 0 || !(T > 0.0)) return 1;
     double* x = (double*)malloc(sizeof(double) * (size_t)V);
     unsigned char* keep = (unsigned char*)malloc((size_t)V);
@@ -159,6 +183,7 @@ int oracle_target_dist(const void* row, int dtype, int V, double T, int top_k, d
             Z += p[i];
         }
         for (int i = 0; i < V; ++i) p[i] /= Z;
+        nucleus_cut(p, V, top_p);
     }
     free(x);
     free(keep);
@@ -169,13 +194,18 @@ int oracle_target_dist(const void* row, int dtype, int V, double T, int top_k, d
  * T == 1 and no top-k: q as given.  Otherwise w_i = q_i^(1/T), keep the top_k of w,
  * q' = w / sum_kept w ([LEV] section 二; temperature applied to both p and q).
  * Returns 0, or 1 when invalid (E3, E4). */
+int oracle_draft_dist_p(const float* q, int V, double T, int top_k, double top_p, double* out);
 int oracle_draft_dist(const float* q, int V, double T, int top_k, double* out) {
+    return oracle_draft_dist_p(q, V, T, top_k, 1.0, out);
+}
+/* The same, then the nucleus cut at top_p (a transformed draft whenever top_p < 1). */
+int oracle_draft_dist_p(const float* q, int V, double T, int top_k, double top_p, double* out) {
     if (V <= 0 || !(T > 0.0)) return 1;
     for (int i = 0; i < V; ++i) {
         double v = (double)q[i];
         if (isnan(v) || v < 0.0 || v == INFINITY) return 1;
     }
-    if (T == 1.0 && !topk_enabled(top_k, V)) {
+    if (T == 1.0 && !topk_enabled(top_k, V) && !(top_p < 1.0)) {
         for (int i = 0; i < V; ++i) out[i] = (double)q[i];
         return 0;
     }
@@ -187,8 +217,10 @@ int oracle_draft_dist(const float* q, int V, double T, int top_k, double* out) {
     double s = 0.0;
     for (int i = 0; i < V; ++i) s += keep[i] ? w[i] : 0.0;
     int bad = !(s > 0.0);
-    if (!bad)
+    if (!bad) {
         for (int i = 0; i < V; ++i) out[i] = keep[i] ? w[i] / s : 0.0;
+        nucleus_cut(out, V, top_p);
+    }
     free(w);
     free(keep);
     return bad;
@@ -228,14 +260,27 @@ static int q_ok(float v) { return !(isnan(v) || v < 0.0f || v == INFINITY); }
  * Greedy mode (T == 0): argmax comparisons; pk = 1 if x_k is the argmax else 0,
  * qk = NaN, S = py = 1, margins = +inf (the decisions are exact).
  */
+int oracle_verify_chain_p(const void* logits, int dtype, const float* q, const int32_t* x,
+                          const float* u, int B, int K, int V, double T, int top_k, double top_p,
+                          int32_t* tokens, int32_t* accept_len, double* pk, double* qk,
+                          double* S_out, double* py_out, double* m_test, double* m_draw);
 int oracle_verify_chain(const void* logits, int dtype, const float* q, const int32_t* x,
                         const float* u, int B, int K, int V, double T, int top_k,
                         int32_t* tokens, int32_t* accept_len, double* pk, double* qk,
                         double* S_out, double* py_out, double* m_test, double* m_draw) {
-    if (B <= 0 || K <= 0 || V <= 0 || !(T >= 0.0) || isinf(T)) return -1;
+    return oracle_verify_chain_p(logits, dtype, q, x, u, B, K, V, T, top_k, 1.0, tokens, accept_len, pk, qk,
+                                 S_out, py_out, m_test, m_draw);
+}
+/* The same with a nucleus cut at top_p (0 < top_p <= 1) on both distributions,
+ * after the temperature and top-k. */
+int oracle_verify_chain_p(const void* logits, int dtype, const float* q, const int32_t* x,
+                          const float* u, int B, int K, int V, double T, int top_k, double top_p,
+                          int32_t* tokens, int32_t* accept_len, double* pk, double* qk,
+                          double* S_out, double* py_out, double* m_test, double* m_draw) {
+    if (B <= 0 || K <= 0 || V <= 0 || !(T >= 0.0) || isinf(T) || !(top_p > 0.0)) return -1;
     const size_t esz = dtype == ORC_BF16 ? 2 : 4;
     const int greedy = (T == 0.0);
-    const int transformed = !(T == 1.0 && !topk_enabled(top_k, V));
+    const int transformed = !(T == 1.0 && !topk_enabled(top_k, V) && !(top_p < 1.0));
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
         const char* zb = (const char*)logits + (size_t)b * (K + 1) * V * esz;
@@ -282,13 +327,13 @@ int oracle_verify_chain(const void* logits, int dtype, const float* q, const int
         /* Ratio tests left to right, stop at the first rejection. */
         int j = K;
         for (int k = 0; k <= K; ++k) {
-            if (oracle_target_dist(zb + (size_t)k * V * esz, dtype, V, T, top_k, p + (size_t)k * V)) {
+            if (oracle_target_dist_p(zb + (size_t)k * V * esz, dtype, V, T, top_k, top_p, p + (size_t)k * V)) {
                 err = 1;                                                           /* E1 */
                 break;
             }
             if (k == K) break;
             if (transformed) {
-                if (oracle_draft_dist(qb + (size_t)k * V, V, T, top_k, qq + (size_t)k * V)) {
+                if (oracle_draft_dist_p(qb + (size_t)k * V, V, T, top_k, top_p, qq + (size_t)k * V)) {
                     err = 1;                                                       /* E3, E4 */
                     break;
                 }

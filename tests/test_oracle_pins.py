@@ -462,3 +462,57 @@ def test_error_rules(orc):
     x_g[6, 0] = int(np.argmax(z[6, 0]))
     og = orc.verify_chain(z, orc.F32, q, x_g, u, 0.0, 0)
     assert og["accept_len"][6] == -1    # consulted row 1 holds NaN
+
+
+# ---------------------------------------------------------------- nucleus (top-p)
+
+def lib_nucleus(p, top_p):
+    """The nucleus of a distribution by library routines: a stable sort by probability,
+    numpy's cumulative sum, the shortest prefix reaching top_p, renormalised."""
+    if top_p >= 1.0:
+        return p
+    order = np.lexsort((np.arange(p.shape[0]), -p))
+    cum = np.cumsum(p[order])
+    n = int(np.searchsorted(cum, top_p, side="left")) + 1
+    n = min(n, int(np.count_nonzero(p)))
+    out = np.zeros_like(p)
+    out[order[:n]] = p[order[:n]]
+    return out / out.sum()
+
+
+@pytest.mark.parametrize("T,top_k,top_p", [(1.0, 0, 0.9), (0.7, 50, 0.5), (1.3, 7, 0.95), (1.0, 0, 1e-6),
+                                           (0.8, 200, 0.999)])
+def test_nucleus_matches_library(orc, T, top_k, top_p):
+    """Temperature, then top-k, then the nucleus ("064 · 投机解码", section 二: the sampling
+    transforms are part of p and q), on both distributions."""
+    rng = np.random.default_rng([5, top_k])
+    V = 1000
+    for _ in range(4):
+        z = (2.0 * rng.standard_normal(V)).astype(np.float32)
+        q = scipy.special.softmax(2.0 * rng.standard_normal(V)).astype(np.float32)
+        p = orc.target_dist(z, orc.F32, T, top_k, top_p)
+        assert np.allclose(p, lib_nucleus(lib_target(z, T, top_k), top_p), rtol=0, atol=1e-12)
+        d = orc.draft_dist(q, T, top_k, top_p)
+        assert np.allclose(d, lib_nucleus(lib_draft(q, T, top_k), top_p), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("top_p", [0.6, 0.9])
+def test_nucleus_chain_law(orc, top_p):
+    """With the nucleus on both sides the chain's exact output law is the nucleus of p."""
+    V, K, T, top_k = 4, 2, 0.9, 3
+    z, q = _tiny_inputs(V, K, 11)
+    prop = np.stack([lib_nucleus(lib_draft(q[k], T, top_k), top_p) for k in range(K)])
+
+    def run(seqs, u):
+        S = seqs.shape[0]
+        Z = np.ascontiguousarray(np.broadcast_to(z, (S,) + z.shape))
+        Q = np.ascontiguousarray(np.broadcast_to(q, (S,) + q.shape))
+        o = orc.verify_chain(Z, orc.F32, Q, seqs, u, T, top_k, top_p)
+        return o["accept_len"], o["tokens"]
+
+    emit, reach = chain_law(run, K, V, prop)
+    for k in range(K + 1):
+        if reach[k] < 1e-9:
+            continue
+        want = lib_nucleus(lib_target(z[k], T, top_k), top_p)
+        assert np.allclose(emit[k] / reach[k], want, atol=2e-6), (k, emit[k] / reach[k], want)
