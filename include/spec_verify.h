@@ -149,6 +149,22 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * spec_verify_chain_topp -- spec_verify_chain with a nucleus (top-p) transform
+ * on both distributions ("064 · 投机解码", section 二: the sampling transforms
+ * are part of p and q).  After the temperature and top-k, each row keeps the
+ * shortest prefix of its kept tokens, in value order (lower index first on
+ * ties), whose probability mass reaches top_p, renormalised.  0 < top_p <= 1
+ * (1: spec_verify_chain); top_p < 1 needs temperature > 0 and top-k on
+ * (SPEC_EUNSUPPORTED otherwise).  The cut is decided on fp64 probabilities.
+ * Everything else, workspace included, is as for spec_verify_chain.
+ */
+int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                           const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                           float temperature, int top_k, float top_p, int32_t* out_tokens,
+                           int32_t* out_accept_len, float* out_diag, void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
+/*
  * spec_verify_tree_greedy -- greedy verification of a static draft tree.
  *
  * Node 0 is the root; parents_host[0] = -1 and 0 <= parents_host[n] < n

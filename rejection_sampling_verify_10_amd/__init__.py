@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.spec_accept_rate_workspace_bytes.restype = Z
         L.spec_verify_chain.argtypes = [P, I, P, P, P, I, I, I, F, I, P, P, P, P, Z, P]
         L.spec_verify_chain.restype = I
+        L.spec_verify_chain_topp.argtypes = [P, I, P, P, P, I, I, I, F, I, F, P, P, P, P, Z, P]
+        L.spec_verify_chain_topp.restype = I
         L.spec_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, Z, P]
         L.spec_verify_tree_greedy.restype = I
         L.spec_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P]
@@ -138,12 +140,13 @@ def accept_rate_workspace_bytes(B: int, K: int, V: int, dtype: int, temperature:
 
 def verify_chain(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor],
                  draft_tokens: torch.Tensor, uniforms: Optional[torch.Tensor],
-                 temperature: float = 1.0, top_k: int = 0, *, diag: bool = False,
+                 temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0, *, diag: bool = False,
                  out: Optional[Tuple[torch.Tensor, ...]] = None, workspace: Optional[torch.Tensor] = None):
     """Batched chain verification (``spec_verify_chain``).
 
     target_logits [B, K+1, V] bf16/f32, draft_probs [B, K, V] f32, draft_tokens [B, K] int32,
-    uniforms [B, K+1] f32.  Returns (tokens [B, K+1] int32, accept_len [B] int32) and, with
+    uniforms [B, K+1] f32; top_p < 1 adds the nucleus cut (top-k on, temperature > 0).
+    Returns (tokens [B, K+1] int32, accept_len [B] int32) and, with
     ``diag=True``, a third tensor [B, 2K+2] f32.  Asynchronous on the current stream.
     ``out`` reuses output tensors; ``workspace`` (uint8, zero-filled before its first
     use, at least the size reported by :func:`chain_workspace_bytes` + 256) avoids the
@@ -180,10 +183,16 @@ def verify_chain(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor
         dg = out[2] if diag else None
     need = chain_workspace_bytes(B, K, V, code, temperature, top_k)
     wp, ws = _workspace(need, dev, workspace)
-    rc = lib().spec_verify_chain(z, code, q, x, u, B, K, V, float(temperature), int(top_k),
-                                 tokens.data_ptr(), alen.data_ptr(), dg.data_ptr() if dg is not None else None,
-                                 wp, need, _stream(dev))
-    _check(rc, "spec_verify_chain")
+    if float(top_p) != 1.0:
+        rc = lib().spec_verify_chain_topp(z, code, q, x, u, B, K, V, float(temperature), int(top_k), float(top_p),
+                                          tokens.data_ptr(), alen.data_ptr(),
+                                          dg.data_ptr() if dg is not None else None, wp, need, _stream(dev))
+        _check(rc, "spec_verify_chain_topp")
+    else:
+        rc = lib().spec_verify_chain(z, code, q, x, u, B, K, V, float(temperature), int(top_k),
+                                     tokens.data_ptr(), alen.data_ptr(), dg.data_ptr() if dg is not None else None,
+                                     wp, need, _stream(dev))
+        _check(rc, "spec_verify_chain")
     return (tokens, alen, dg) if diag else (tokens, alen)
 
 

@@ -76,6 +76,7 @@ TopkLists carve_topk(Carver& c, int dtype, int V, int B, int P, int K, int top_k
         t.flags = c.take<uint32_t>(units);
     }
     t.top_k = top_k;
+    t.top_p = 1.f;
     t.draft_identity = (T == 1.f) ? 1 : 0;
     t.invT = T > 0.f ? 1.0 / static_cast<double>(T) : 0.0;
     return t;
@@ -290,9 +291,32 @@ size_t spec_accept_rate_workspace_bytes(int B, int K, int V, spec_dtype_t dtype,
     return (c.off + 255) & ~static_cast<size_t>(255);
 }
 
+static int chain_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                      float temperature, int top_k, float top_p, int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
                       const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
                       float temperature, int top_k, int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return chain_call(target_logits, dtype, draft_probs, draft_tokens, uniforms, B, K, V, temperature, top_k, 1.f,
+                      out_tokens, out_accept_len, out_diag, workspace, workspace_bytes, hip_stream);
+}
+
+int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                           const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                           float temperature, int top_k, float top_p, int32_t* out_tokens,
+                           int32_t* out_accept_len, float* out_diag, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+    if (!(top_p > 0.f && top_p <= 1.f)) return SPEC_EINVAL;
+    return chain_call(target_logits, dtype, draft_probs, draft_tokens, uniforms, B, K, V, temperature, top_k, top_p,
+                      out_tokens, out_accept_len, out_diag, workspace, workspace_bytes, hip_stream);
+}
+
+static int chain_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                      float temperature, int top_k, float top_p, int32_t* out_tokens, int32_t* out_accept_len,
                       float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream) {
     int rc = check_common(target_logits, dtype, B, K, V, temperature);
     if (rc) return rc;
@@ -306,6 +330,8 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
     if (!greedy && topk_active(top_k, V)) {
         if (top_k > SPEC_TOPK_MAX || !topk_shape_ok(dtype, V)) return SPEC_EUNSUPPORTED;
     }
+    // the nucleus is built on the top-k path's kept lists: it needs top-k and a temperature
+    if (top_p < 1.f && (greedy || !topk_active(top_k, V))) return SPEC_EUNSUPPORTED;
     const size_t need = spec_chain_workspace_bytes(B, K, V, dtype, temperature, top_k);
     rc = check_workspace(workspace, workspace_bytes, need);
     if (rc) return rc;
@@ -337,6 +363,7 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype, const float
         SV_TRY(launch_rowstats(ra, s, prof.timing()));
         SV_TRY(launch_chain_greedy(ca, s));
     } else if (p.mode == 1) {
+        p.tk.top_p = top_p;
         ca.tk = p.tk;
         ca.recw = p.recw;
         TopkChainArgs fa{};

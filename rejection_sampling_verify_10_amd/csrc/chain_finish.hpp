@@ -143,6 +143,27 @@ __device__ __forceinline__ bool kept_dist32(float v, int idx_in, int kk, bool va
     return ok;
 }
 
+// Nucleus cut of a row's kept entries (lane l = l-th largest, kk kept): the
+// length of the shortest prefix whose mass reaches top_p, the probabilities
+// taken in fp64 (exp((v - v0)/T) for the target, q^(1/T) for the draft) so that
+// the cut is decided on the same numbers to ~1e-16.  The nucleus keeps the
+// tokens whose preceding mass is below top_p (and whose probability is not 0).
+__device__ __forceinline__ int nucleus_count(float v, int kk, bool draft, double invT, bool identity, float top_p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool have = lane < kk;
+    const double v0 = static_cast<double>(bcast(v, 0));
+    double w = 0.0;
+    if (have) {
+        if (!draft) w = exp((static_cast<double>(v) - v0) * invT);
+        else if (v > 0.f) w = identity ? static_cast<double>(v) : pow(static_cast<double>(v), invT);
+    }
+    const double Z = wave_sum(w);
+    const double p = Z > 0.0 ? w / Z : 0.0;
+    const double incl = wave_inclusive_scan(p);
+    const bool keep = have && p > 0.0 && (incl - p) < static_cast<double>(top_p);
+    return static_cast<int>(__popcll(__ballot(keep)));
+}
+
 // ---- position records: kRecWords words per position (payload in bits 63..32,
 // bit 0 valid): y with accept (bit 2), rows unusable (bit 1: E1 / E3 / E4,
 // they count only if the walk reaches the position) and inputs invalid (bit 3:
@@ -329,6 +350,7 @@ __device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, in
         // real (non-empty) entries of the merged list; top_k of them are kept
         const int real = static_cast<int>(__popcll(__ballot(key_idx(key) != kNoIndex)));
         kt = real < t.top_k ? real : t.top_k;
+        if (t.top_p < 1.f) kt = nucleus_count(key_val(key), kt, false, t.invT, false, t.top_p);
         ok = kept_dist32(key_val(key), key_idx(key), kt, done && !flagged, false,
                          static_cast<float>(1.4426950408889634 * t.invT), 0.f, false, it, pt) && done;
         pt = lane_gather(pt, wave_sort_indices(it));     // index order
@@ -336,7 +358,8 @@ __device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, in
     } else if (wid == 1 && k < K) {
         wave_merge_keys(key, fs.dkey[lane]);
         const int real = static_cast<int>(__popcll(__ballot(key_idx(key) != kNoIndex)));
-        const int kd = real < t.top_k ? real : t.top_k;
+        int kd = real < t.top_k ? real : t.top_k;
+        if (t.top_p < 1.f) kd = nucleus_count(key_val(key), kd, true, t.invT, t.draft_identity != 0, t.top_p);
         int di;
         float dq;
         const bool okd = kept_dist32(key_val(key), key_idx(key), kd, done && !flagged && !fs.dbad, true, 0.f,

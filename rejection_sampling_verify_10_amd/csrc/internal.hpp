@@ -66,6 +66,7 @@ struct TopkLists {
     int chunk_t, chunk_d;   // elements per target / draft chunk
     long Ub;                // units per batch row
     int top_k;
+    float top_p;            // nucleus cut after top-k (chain finish; 1 = off)
     int draft_identity;     // T == 1: q^(1/T) = q exactly
     double invT;
     __host__ __device__ long unit_base(int b, int k) const {

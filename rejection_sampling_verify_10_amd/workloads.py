@@ -133,9 +133,17 @@ def _softmax64(a: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def _draft_sampler_cdf(zd_row: np.ndarray, T: float, top_k: int) -> np.ndarray:
-    """Cumulative sum of the draft model's own sampling distribution (float64)."""
+def _draft_sampler_cdf(zd_row: np.ndarray, T: float, top_k: int, top_p: float = 1.0) -> np.ndarray:
+    """Cumulative sum of the draft model's own sampling distribution (float64), with its
+    own nucleus when top_p < 1."""
     V = zd_row.shape[0]
+    if top_p < 1.0:
+        w = np.diff(_draft_sampler_cdf(zd_row, T, top_k), prepend=0.0)
+        order = np.argsort(-w, kind="stable")
+        n = int(np.searchsorted(np.cumsum(w[order]), top_p * w.sum(), side="left")) + 1
+        keep = np.zeros(V, dtype=bool)
+        keep[order[:n]] = True
+        return np.cumsum(np.where(keep, w, 0.0))
     if T == 0.0:                        # greedy draft: its argmax
         w = np.zeros(V, dtype=np.float64)
         w[int(np.argmax(zd_row))] = 1.0
@@ -170,7 +178,7 @@ def _workers() -> int:
 
 def make_chain(B: int, K: int, V: int, *, dtype: int, temperature: float, top_k: int,
                sigma: SigmaSpec, config_id: int, seed: int,
-               threads: Optional[int] = None) -> ChainInputs:
+               threads: Optional[int] = None, top_p: float = 1.0) -> ChainInputs:
     """Draw one chain-verification input set (see the module docstring for the recipe)."""
     log_rank = _log_rank_table(V)
     logits = np.empty((B, K + 1, V), dtype=np.uint16 if dtype == DTYPE_BF16 else np.float32)
@@ -189,7 +197,7 @@ def make_chain(B: int, K: int, V: int, *, dtype: int, temperature: float, top_k:
         q[b] = _softmax64(zd).astype(np.float32)
         ud = rng.random(K)
         for k in range(K):
-            cdf = _draft_sampler_cdf(zd[k], temperature, top_k)
+            cdf = _draft_sampler_cdf(zd[k], temperature, top_k, top_p)
             x[b, k] = min(int(np.searchsorted(cdf, ud[k] * cdf[-1], side="right")), V - 1)
         u[b] = rng.random(K + 1, dtype=np.float32)
         logits[b] = f32_to_bf16_bits(z) if dtype == DTYPE_BF16 else z

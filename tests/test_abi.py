@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_symbols_exported(L):
     names = declared_functions()
-    assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_tree_sample",
+    assert {"spec_verify_chain", "spec_verify_chain_topp", "spec_verify_tree_greedy", "spec_verify_tree_sample",
             "spec_verify_tree_greedy_rows", "spec_verify_tree_sample_rows",
             "spec_tree_expand", "spec_tree_rerank", "spec_accept_rate"} <= set(names)
     for n in names:
@@ -69,6 +69,20 @@ def test_chain_argument_checks(L):
     assert _chain(L, wsb=16) == EWORKSPACE
     assert _chain(L, ws=None) == EWORKSPACE
     assert _chain(L, ws=FAKE + 8) == EWORKSPACE
+
+
+def test_chain_topp_argument_checks(L):
+    def call(**kw):
+        a = dict(T=0.7, top_k=50, top_p=0.9, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return L.spec_verify_chain_topp(FAKE, 1, FAKE, FAKE, FAKE, 4, 3, 1000, a["T"], a["top_k"], a["top_p"],
+                                        FAKE, FAKE, None, a["ws"], a["wsb"], None)
+    assert call(top_p=0.0) == EINVAL
+    assert call(top_p=1.5) == EINVAL
+    assert call(top_p=float("nan")) == EINVAL
+    assert call(top_k=0) == EUNSUPPORTED             # the nucleus needs top-k
+    assert call(T=0.0) == EUNSUPPORTED               # and a temperature
+    assert call(wsb=16) == EWORKSPACE
 
 
 def test_tree_argument_checks(L):

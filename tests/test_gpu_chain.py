@@ -258,3 +258,23 @@ def test_dense_long_rows(R, orc, V, T):
     ci = W.make_chain(3, 3, V, dtype=W.DTYPE_BF16, temperature=T, top_k=0, sigma=W.sigma_const(0.6),
                       config_id=92, seed=V % 1000)
     check(R, orc, ci, f"dense V={V} T={T}")
+
+
+@pytest.mark.parametrize("top_p,nucleus_draft", [(0.9, True), (0.5, True), (0.99, False), (1e-6, False)])
+def test_topp_on_the_topk_path(R, orc, top_p, nucleus_draft):
+    """The nucleus (spec_verify_chain_topp) after temperature and top-k, on the c2 shape (a
+    reduced batch); drafts drawn from the draft's own nucleus, or from its top-k only (then
+    some drafted tokens lie outside the nucleus: q'(x) = 0)."""
+    import torch
+    ci = W.make_chain(16, 7, 128256, dtype=W.DTYPE_BF16, temperature=0.7, top_k=50,
+                      sigma=W.sigma_halves(0.3, 1.0), config_id=2, seed=40 + int(top_p * 100),
+                      top_p=top_p if nucleus_draft else 1.0)
+    print(f"[case] top_p={top_p} nucleus draft={nucleus_draft}: B={ci.B} K={ci.K} V={ci.V}", flush=True)
+    tok, alen, dg = R.verify_chain(to_torch(ci.logits), to_torch(ci.draft_probs), to_torch(ci.draft_tokens),
+                                   to_torch(ci.uniforms), ci.temperature, ci.top_k, top_p, diag=True)
+    torch.cuda.synchronize()
+    o = orc.verify_chain(ci.logits, ci.dtype, ci.draft_probs, ci.draft_tokens, ci.uniforms, ci.temperature,
+                         ci.top_k, top_p)
+    t = compare_chain(o, tok.cpu().numpy(), alen.cpu().numpy(), dg.cpu().numpy(), ci.K)
+    log_tally(f"top_p={top_p}", t)
+    t.check()
