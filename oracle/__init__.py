@@ -54,13 +54,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_verify_tree_sample.argtypes = [P, I, P, P, P, P, I, I, I, D, I, P, P, P, P, P]
         L.oracle_tree_expand.argtypes = [P, P, I, I, I, I, I, P, P, P]
         L.oracle_tree_rerank.argtypes = [P, P, I, I, I, P, P, P]
+        LL = ctypes.c_longlong
+        L.oracle_kv_commit.argtypes = [P, I, LL, I, LL, LL, I, P, P, I, I, P, P]
         L.oracle_target_dist.argtypes = [P, I, I, D, I, P]
         L.oracle_draft_dist.argtypes = [P, I, D, I, P]
         L.oracle_argmax_row.argtypes = [P, I, I]
         L.oracle_set_variant.argtypes = [I]
         for f in ("oracle_verify_chain", "oracle_verify_chain_p", "oracle_target_dist_p", "oracle_draft_dist_p",
                   "oracle_verify_tree_greedy", "oracle_accept_rate",
-                  "oracle_verify_tree_sample", "oracle_tree_expand", "oracle_tree_rerank",
+                  "oracle_verify_tree_sample", "oracle_tree_expand", "oracle_tree_rerank", "oracle_kv_commit",
                   "oracle_target_dist", "oracle_draft_dist", "oracle_argmax_row",
                   "oracle_max_threads"):
             getattr(L, f).restype = I
@@ -184,6 +186,22 @@ def tree_rerank(parents, values, m):
     if rc != 0:
         raise ValueError(f"oracle_tree_rerank rejected its arguments ({rc})")
     return out
+
+
+def kv_commit(kv, prefix, path, N, accept_len):
+    """KV commit on a copy of kv [planes, B, S, row] (any dtype): returns (new kv, new lengths)."""
+    out = np.ascontiguousarray(kv).copy()
+    planes, B, S = out.shape[:3]
+    row_bytes = out[0, 0, 0].nbytes
+    pre = np.ascontiguousarray(prefix, dtype=np.int32)
+    pth = np.ascontiguousarray(path, dtype=np.int32)
+    al = np.ascontiguousarray(accept_len, dtype=np.int32)
+    nl = np.empty(B, np.int32)
+    rc = lib().oracle_kv_commit(_p(out), planes, out[0].nbytes, B, out[0, 0].nbytes, row_bytes, row_bytes,
+                                _p(pre), _p(pth), pth.shape[1], int(N), _p(al), _p(nl))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_commit rejected its arguments ({rc})")
+    return out, nl
 
 
 def accept_rate(logits, dtype, draft_probs, temperature, top_k):

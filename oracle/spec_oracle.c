@@ -767,3 +767,38 @@ int oracle_tree_rerank(const int32_t* parent, const float* value, int B, int M, 
     }
     return 0;
 }
+
+/*
+ * KV commit after a tree verification ("Việc giải mã giả định và EAGLE-3",
+ * KV cache rollback: write the draft's entries to scratch and commit on
+ * acceptance, or keep a logical length and cut on rejection).  The verifier
+ * appended the N tree nodes' rows at positions prefix[b] + n; the accepted
+ * path root..n* (path[b][0..d], d = accept_len[b]) is moved to positions
+ * prefix[b] + 0..d in every plane, and the new logical length is
+ * prefix[b] + d + 1.  Layout: row (plane, b, s) at byte offset
+ * plane*plane_stride + b*batch_stride + s*pos_stride, row_bytes long.  Rows are
+ * moved in increasing t; since path is increasing and path[t] >= t, a row is
+ * never overwritten before it is read.  A row with accept_len < 0, or a path
+ * that is not 0 followed by increasing node indices below N, moves nothing and
+ * gets new length -1.
+ */
+int oracle_kv_commit(uint8_t* kv, int planes, long long plane_stride, int B, long long batch_stride,
+                     long long pos_stride, int row_bytes, const int32_t* prefix, const int32_t* path,
+                     int path_stride, int N, const int32_t* accept_len, int32_t* new_len) {
+    if (planes <= 0 || B <= 0 || row_bytes <= 0 || N <= 0 || path_stride <= 0) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int d = accept_len[b];
+        const int32_t* pb = path + (size_t)b * path_stride;
+        int ok = d >= 0 && d < path_stride && d < N && prefix[b] >= 0 && pb[0] == 0;
+        for (int t = 1; ok && t <= d; ++t) ok = pb[t] > pb[t - 1] && pb[t] < N;
+        if (!ok) { new_len[b] = -1; continue; }
+        for (int pl = 0; pl < planes; ++pl) {
+            uint8_t* base = kv + (size_t)pl * plane_stride + (size_t)b * batch_stride;
+            for (int t = 1; t <= d; ++t)
+                memmove(base + (size_t)(prefix[b] + t) * pos_stride, base + (size_t)(prefix[b] + pb[t]) * pos_stride,
+                        (size_t)row_bytes);
+        }
+        new_len[b] = prefix[b] + d + 1;
+    }
+    return 0;
+}

@@ -37,6 +37,10 @@ children are drawn), then for each node ``p`` in order its children's tokens,
 independently, from the draft model's sampling distribution at ``p`` (step
 5), and last the N verification uniforms.
 
+A KV commit draws random cache contents (bf16 bits), a prefix length per
+batch row and the path from the root to a node of the tree picked at a
+uniformly drawn depth.
+
 Draft-tree construction (EAGLE-2) draws, per batch row: for an expansion
 layer, E draft rows as in step 3 (q = softmax(z + sigma*N(0,1)) of a fresh
 target-like row) and the E expanded nodes' values, sorted descending in
@@ -362,6 +366,47 @@ def make_rerank(B: int, *, k: int, depth: int, m: int, config_id: int, seed: int
     return RerankInputs(B, M, int(m), par, val)
 
 
+@dataclasses.dataclass
+class KVCommitInputs:
+    """A KV cache holding each batch row's prefix and its N tree nodes, and the accepted paths."""
+    B: int
+    planes: int
+    S: int
+    row: int                   # elements (bf16 bits, uint16) per row
+    N: int
+    kv: np.ndarray             # [planes, B, S, row] uint16
+    prefix: np.ndarray         # [B] int32: where node 0 sits
+    path: np.ndarray           # [B, D+1] int32: node ids root..n*, -1 padded
+    accept_len: np.ndarray     # [B] int32: depth of n*
+
+
+def make_kv_commit(B: int, *, planes: int, row: int, parents: np.ndarray = EAGLE_TREE_PARENTS, max_prefix: int,
+                   config_id: int, seed: int) -> KVCommitInputs:
+    """Random cache contents; per batch row a prefix length in [0, max_prefix] and the path to a
+    random node of the tree (deeper nodes about as likely as shallow ones)."""
+    rng = np.random.default_rng([config_id, seed])
+    parents = np.asarray(parents, dtype=np.int32)
+    N = parents.shape[0]
+    depth = np.zeros(N, np.int64)
+    for n in range(1, N):
+        depth[n] = depth[parents[n]] + 1
+    D = int(depth.max())
+    S = max_prefix + N
+    kv = rng.integers(0, 1 << 16, (planes, B, S, row), dtype=np.uint16)
+    prefix = rng.integers(0, max_prefix + 1, B).astype(np.int32)
+    path = np.full((B, D + 1), -1, np.int32)
+    alen = np.empty(B, np.int32)
+    for b in range(B):
+        d = int(rng.integers(0, D + 1))
+        cands = np.flatnonzero(depth == d)
+        n = int(rng.choice(cands))
+        alen[b] = d
+        for t in range(d, -1, -1):
+            path[b, t] = n
+            n = parents[n] if n > 0 else 0
+    return KVCommitInputs(B, planes, S, row, N, kv, prefix, path, alen)
+
+
 # The workloads, by index.  Each entry builds inputs for a seed, with
 # optional size overrides used by the smaller parity cases.
 CONFIG_NAMES = {
@@ -372,12 +417,13 @@ CONFIG_NAMES = {
     4: "chain B=512 K=8 V=128256 bf16 T=1",
     5: "tree-sample B=32 N=27 V=32000 bf16 T=1",
     6: "eagle2-expand B=64 E=10 V=128256 top_k=10 k_next=10",
+    7: "kv-commit B=64 planes=64 row=2KiB N=27",
 }
 
 
 def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int] = None,
            V: Optional[int] = None, threads: Optional[int] = None):
-    """Inputs for workload ``cid`` (0..6), optionally with smaller B/K/V (K: expanded nodes for 6)."""
+    """Inputs for workload ``cid`` (0..7), optionally with smaller B/K/V (K: expanded nodes for 6)."""
     if cid == 0:
         return make_chain(B or 1, K or 4, V or 1000, dtype=DTYPE_F32, temperature=1.0, top_k=0,
                           sigma=sigma_const(0.5), config_id=0, seed=seed, threads=threads)
@@ -396,6 +442,8 @@ def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int]
     if cid == 5:
         return make_tree_sampled(B or 32, V or 32000, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
                                  sigma=0.5, config_id=5, seed=seed, threads=threads)
+    if cid == 7:
+        return make_kv_commit(B or 64, planes=64, row=1024, max_prefix=64, config_id=7, seed=seed)
     if cid == 6:
         return make_expand(B or 64, K or 10, V or 128256, top_k=10, k_next=10, sigma=0.5, config_id=6, seed=seed,
                            threads=threads)

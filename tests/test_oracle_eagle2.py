@@ -10,7 +10,10 @@ routine, independently of the oracle's own code:
 - reranking: the kept nodes are the first m in (value descending, shallower
   first, lower index), the selection stays a connected tree (the pages' reason
   for the tie rule), it is flattened parents-first, and the mask holds exactly
-  each token's ancestors (a separate walk up the parents).
+  each token's ancestors (a separate walk up the parents);
+- KV commit ("Việc giải mã giả định và EAGLE-3", KV cache rollback): the
+  in-place move of the accepted path's rows equals a gather of the original
+  rows, and malformed rows move nothing.
 """
 
 import numpy as np
@@ -111,3 +114,39 @@ def test_rerank_error_rows(orc):
     for b in (1, 2, 3):
         assert np.all(o["nodes"][b] == -1) and o["mask"][b].sum() == 0, b
     assert np.all(o["nodes"][0] >= 0)
+
+
+# ---------------------------------------------------------------- KV commit
+
+def test_kv_commit_is_a_gather_of_the_original_rows(orc):
+    """In place, rows moved in increasing order, the result equals a gather of the ORIGINAL
+    rows (numpy fancy indexing on a copy): no row is overwritten before it is read, also for
+    paths like 0, 2, 3 where a destination is another move's source."""
+    k = W.make_kv_commit(16, planes=3, row=8, max_prefix=10, config_id=71, seed=0)
+    k.path[0, :4] = [0, 2, 3, 7]
+    k.path[0, 4:] = -1
+    k.accept_len[0] = 3
+    out, nl = orc.kv_commit(k.kv, k.prefix, k.path, k.N, k.accept_len)
+    want = k.kv.copy()
+    for b in range(k.B):
+        d = k.accept_len[b]
+        src = k.prefix[b] + k.path[b, :d + 1]
+        want[:, b, k.prefix[b]:k.prefix[b] + d + 1] = k.kv[:, b, src]
+        assert nl[b] == k.prefix[b] + d + 1
+    assert np.array_equal(out, want)
+
+
+def test_kv_commit_error_rows_move_nothing(orc):
+    k = W.make_kv_commit(6, planes=2, row=4, max_prefix=5, config_id=72, seed=0)
+    path, al = k.path.copy(), k.accept_len.copy()
+    al[0] = -1
+    path[1, 0] = 1                     # must start at the root
+    if al[2] < 2:
+        al[2] = 2
+        path[2, :3] = [0, 1, 4]
+    path[2, 2] = path[2, 1]            # not increasing
+    path[3, 1] = k.N                   # out of range
+    al[3] = max(al[3], 1)
+    out, nl = orc.kv_commit(k.kv, k.prefix, path, k.N, al)
+    for b in range(4):
+        assert nl[b] == -1 and np.array_equal(out[:, b], k.kv[:, b])
