@@ -53,6 +53,9 @@ WORKLOADS = {
     5: dict(name="sampled static-tree verify B=32 N=27 (depth 5) V=32000, bf16 target logits, fp32 draft probs, "
                  "T=1, no top-k",
             kernel="tree_sample_kernel", copies=4, oracle_rows=32, dtype="bf16 in, f64 probabilities"),
+    7: dict(name="KV commit of accepted tree paths B=64, 64 planes (32 layers x K/V), 2 KiB rows (8 heads x 128 "
+                 "x bf16), 27-node tree, prefix <= 16",
+            kernel="kv_commit_kernel", copies=8, oracle_rows=64, dtype="bytes (bf16 rows)"),
     6: dict(name="EAGLE-2 expansion layer B=64 E=10 V=128256, fp32 draft probs, top_k=10 children per node, "
                  "k_next=10 kept",
             kernel="topk_chunk_kernel", copies=2, oracle_rows=8, dtype="f32 in, f32 select and value products"),
@@ -132,6 +135,12 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
                       tree_path=None, parents=None) -> float:
     """Bytes the dominant kernel must move per launch (see the design notes).  For the trees,
     K is the node count N."""
+    if workload == 7:
+        # every moving row read and written once (rows 1..d of each path, in every plane), the
+        # path, prefix and length read and the new length written
+        planes, rb = K, top_k
+        moved = sum(int(d) for d in accept_len if d > 0)
+        return 2 * planes * moved * rb + B * (8 + 4) + B * 6 * 4
     if workload == 6:
         # every draft row once; per chunk a sorted list of top_k (value, index) pairs plus count
         # and flags written; the children (token, value) and the kept indices written
@@ -241,6 +250,7 @@ def main() -> int:
     tree = args.workload == 3
     sampled_tree = args.workload == 5
     expand = args.workload == 6
+    kvc = args.workload == 7
     log(f"workload {args.workload}: {wl['name']} (inputs drawn in {time.time() - t0:.1f} s)")
 
     def to_dev(a):
@@ -262,6 +272,14 @@ def main() -> int:
         ws = R.new_workspace(R.tree_workspace_bytes(B, K, V, ci.dtype), dev)
         parents = ci.parents.tolist()
         rows_per_step = B * K                  # node rows verified
+    elif kvc:
+        # K: planes, top_k: bytes per row (for the algorithmic byte count)
+        B, K, V, T, top_k = ci.B, ci.planes, ci.S, 1.0, ci.row * 2
+        kv0 = torch.from_numpy(ci.kv.view(np.int16)).to(dev)
+        base = [kv0, to_dev(ci.prefix), to_dev(ci.path), to_dev(ci.accept_len)]
+        alen = to_dev(ci.accept_len)
+        xn = torch.empty((B,), dtype=torch.int32, device=dev)
+        rows_per_step = B                      # accepted paths committed
     elif expand:
         B, K, V, T, top_k = ci.B, ci.E, ci.V, 1.0, ci.top_k
         base = [to_dev(ci.draft_probs), to_dev(ci.node_values)]
@@ -298,6 +316,9 @@ def main() -> int:
         if tree:
             z, nt = sets[i % len(sets)]
             R.verify_tree_greedy(z, nt, parents, out=(path, tok, alen), workspace=ws)
+        elif kvc:
+            kv, pre, pth, al = sets[i % len(sets)]
+            R.kv_commit(kv, pre, pth, al, ci.N, out_len=xn)
         elif expand:
             q, nv = sets[i % len(sets)]
             R.tree_expand(q, nv, top_k, ci.k_next, out=(xt, xv, xn), workspace=ws)
@@ -343,7 +364,7 @@ def main() -> int:
     step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak)"
-        + ("" if expand else "; accept_len histogram "
+        + ("" if (expand or kvc) else "; accept_len histogram "
            f"{np.bincount(al[al >= 0], minlength=(K + 1) if not (tree or sampled_tree) else 1).tolist()}"))
     traffic = counter_traffic(args.workload)
     probe = read_probe_gbps(R, torch, dev)
@@ -360,6 +381,8 @@ def main() -> int:
         while True:
             if tree:
                 oracle.verify_tree_greedy(ci.logits[:rows], ci.dtype, ci.node_tokens[:rows], ci.parents)
+            elif kvc:
+                oracle.kv_commit(ci.kv[:, :rows], ci.prefix[:rows], ci.path[:rows], ci.N, ci.accept_len[:rows])
             elif expand:
                 oracle.tree_expand(ci.draft_probs[:rows], ci.node_values[:rows], top_k, ci.k_next)
             elif sampled_tree:
@@ -398,6 +421,9 @@ def main() -> int:
                    {"workload": wl["name"], "B": B, "E": K, "V": V, "top_k": top_k, "k_next": ci.k_next,
                     "rows": "expanded draft rows", "input_copies": wl["copies"], "parallelism": "single GPU"}
                    if expand else
+                   {"workload": wl["name"], "B": B, "planes": K, "S": V, "row_bytes": top_k, "tree_nodes": ci.N,
+                    "rows": "committed paths", "input_copies": wl["copies"], "parallelism": "single GPU"}
+                   if kvc else
                    {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
                     "input_copies": wl["copies"], "parallelism": "single GPU"}),
         "step_algorithmic_GBps": step_alg_gbs,

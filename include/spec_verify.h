@@ -305,6 +305,33 @@ int spec_tree_rerank(const int32_t* parents, const float* values, int B, int M, 
                      int32_t* out_parent_pos, uint8_t* out_mask, void* hip_stream);
 
 /*
+ * spec_kv_commit -- KV commit of an accepted tree path ("Việc giải mã giả
+ * định và EAGLE-3", KV cache rollback: write the draft's entries to scratch,
+ * commit on acceptance).  The verifier appended the N tree nodes' KV rows at
+ * positions prefix[b] + n; the accepted path path[b][0..d] (d = accept_len[b],
+ * the out_path / out_accept_len of a tree verification) moves to positions
+ * prefix[b] + 0..d in every plane, in place, and out_len[b] = prefix[b] + d + 1.
+ * Rows move in increasing order; as the path increases from node 0, no row is
+ * overwritten before it is read.
+ *
+ *   kv          device, read and written: row (plane, b, s) at byte offset
+ *               plane*plane_stride + b*batch_stride + s*pos_stride, row_bytes
+ *               long (e.g. planes = layers x {K, V}, a row = heads x head_dim);
+ *               16-byte aligned layouts move with 16-byte accesses
+ *   prefix      [B] int32 device; path [B][path_stride] int32 device;
+ *   accept_len  [B] int32 device; out_len [B] int32 device, written
+ *   N           tree nodes (path entries must be below N)
+ * A row with accept_len < 0, or a path that is not node 0 followed by
+ * increasing node indices below N, moves nothing and gets out_len -1.
+ * Rows must not overlap (pos_stride >= row_bytes); B <= 65535 and
+ * path_stride <= SPEC_MAX_NODES (a path is at most one tree's nodes), else
+ * SPEC_EUNSUPPORTED.
+ */
+int spec_kv_commit(void* kv, int planes, long long plane_stride, int B, long long batch_stride,
+                   long long pos_stride, int row_bytes, const int32_t* prefix, const int32_t* path, int path_stride,
+                   int N, const int32_t* accept_len, int32_t* out_len, void* hip_stream);
+
+/*
  * spec_accept_rate -- alpha[b][k] = sum_i min(p'_k(i), q'_k(i)) for k < K, with
  * p' and q' transformed as in spec_verify_chain (rows 0..K-1 of the logits are
  * read; row K is not).  Greedy (temperature == 0): 1 if the argmax of target

@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.spec_tree_expand.restype = I
         L.spec_tree_rerank.argtypes = [P, P, I, I, I, P, P, P, P]
         L.spec_tree_rerank.restype = I
+        LL = ctypes.c_longlong
+        L.spec_kv_commit.argtypes = [P, I, LL, I, LL, LL, I, P, P, I, I, P, P, P]
+        L.spec_kv_commit.restype = I
         L.spec_accept_rate.argtypes = [P, I, P, I, I, I, F, I, P, P, Z, P]
         L.spec_accept_rate.restype = I
         L.spec_profile_events.argtypes = [P, P]
@@ -329,6 +332,34 @@ def tree_rerank(parents: torch.Tensor, values: torch.Tensor, m: int):
                                 int(m), nodes.data_ptr(), ppos.data_ptr(), mask.data_ptr(), _stream(dev))
     _check(rc, "spec_tree_rerank")
     return nodes, ppos, mask
+
+
+def kv_commit(kv: torch.Tensor, prefix: torch.Tensor, path: torch.Tensor, accept_len: torch.Tensor, N: int,
+              *, out_len: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """KV commit of accepted tree paths (``spec_kv_commit``), in place.
+
+    kv [planes, B, S, ...] on the GPU, rows = the trailing dimensions (contiguous within a
+    row; planes, batch and positions may be strided); prefix [B], path [B, D+1] and
+    accept_len [B] int32.  Returns the new lengths [B] int32.
+    """
+    planes, B, S = kv.shape[:3]
+    if not kv.is_cuda:
+        raise ValueError("kv must be a GPU tensor")
+    row = kv[0, 0, 0]
+    if not row.is_contiguous():
+        raise ValueError("a KV row must be contiguous")
+    es = kv.element_size()
+    _shape(prefix, "prefix", (B,))
+    _shape(accept_len, "accept_len", (B,))
+    if path.dim() != 2 or path.shape[0] != B:
+        raise ValueError("path must be [B, D+1]")
+    nl = out_len if out_len is not None else torch.empty((B,), dtype=torch.int32, device=kv.device)
+    rc = lib().spec_kv_commit(kv.data_ptr(), planes, kv.stride(0) * es, B, kv.stride(1) * es, kv.stride(2) * es,
+                              row.numel() * es, _dev(prefix, "prefix", torch.int32), _dev(path, "path", torch.int32),
+                              path.shape[1], int(N), _dev(accept_len, "accept_len", torch.int32),
+                              _dev(nl, "out_len", torch.int32), _stream(kv.device))
+    _check(rc, "spec_kv_commit")
+    return nl
 
 
 def accept_rate(target_logits: torch.Tensor, draft_probs: torch.Tensor, temperature: float = 1.0,

@@ -622,6 +622,35 @@ int spec_verify_tree_greedy_rows(const void* target_logits, spec_dtype_t dtype, 
     return SPEC_OK;
 }
 
+int spec_kv_commit(void* kv, int planes, long long plane_stride, int B, long long batch_stride,
+                   long long pos_stride, int row_bytes, const int32_t* prefix, const int32_t* path, int path_stride,
+                   int N, const int32_t* accept_len, int32_t* out_len, void* hip_stream) {
+    if (!kv || !prefix || !path || !accept_len || !out_len) return SPEC_EINVAL;
+    if (planes < 1 || B < 1 || row_bytes < 1 || path_stride < 1 || N < 1 || plane_stride < 0 || batch_stride < 0 ||
+        pos_stride < row_bytes)
+        return SPEC_EINVAL;
+    if (B > 65535 || path_stride > SPEC_MAX_NODES) return SPEC_EUNSUPPORTED;
+    if (!aligned(prefix, 4) || !aligned(path, 4) || !aligned(accept_len, 4) || !aligned(out_len, 4))
+        return SPEC_EINVAL;
+    KVCommitArgs ka{};
+    ka.kv = static_cast<uint8_t*>(kv);
+    ka.plane_stride = plane_stride;
+    ka.batch_stride = batch_stride;
+    ka.pos_stride = pos_stride;
+    ka.planes = planes;
+    ka.B = B;
+    ka.row_bytes = row_bytes;
+    ka.prefix = prefix;
+    ka.path = path;
+    ka.path_stride = path_stride;
+    ka.N = N;
+    ka.accept_len = accept_len;
+    ka.new_len = out_len;
+    ProfileScope prof;
+    SV_TRY(launch_kv_commit(ka, static_cast<hipStream_t>(hip_stream), prof.timing()));
+    return SPEC_OK;
+}
+
 int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float* draft_probs, int B, int K,
                      int V, float temperature, int top_k, float* out_alpha, void* workspace,
                      size_t workspace_bytes, void* hip_stream) {

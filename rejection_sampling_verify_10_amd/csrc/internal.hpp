@@ -166,6 +166,18 @@ struct TreeRerankArgs {
     uint8_t* out_mask;          // [B][m+1][m+1]
 };
 
+// KV commit of an accepted tree path (kv_commit.hip).
+struct KVCommitArgs {
+    uint8_t* kv;                    // row (plane, b, s) at plane*plane_stride + b*batch_stride + s*pos_stride
+    long long plane_stride, batch_stride, pos_stride;
+    int planes, B, row_bytes;
+    const int32_t* prefix;          // [B]
+    const int32_t* path;            // [B][path_stride]
+    int path_stride, N;
+    const int32_t* accept_len;      // [B]
+    int32_t* new_len;               // [B]
+};
+
 struct AlphaArgs {
     const void* logits;
     int dtype;
@@ -205,6 +217,7 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t s);
 hipError_t launch_tree_sample(const TreeSampleArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_tree_expand(const TreeExpandArgs& a, hipStream_t s);
 hipError_t launch_tree_rerank(const TreeRerankArgs& a, hipStream_t s);
+hipError_t launch_kv_commit(const KVCommitArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_alpha_greedy(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);

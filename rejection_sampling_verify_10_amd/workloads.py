@@ -443,7 +443,7 @@ def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int]
         return make_tree_sampled(B or 32, V or 32000, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
                                  sigma=0.5, config_id=5, seed=seed, threads=threads)
     if cid == 7:
-        return make_kv_commit(B or 64, planes=64, row=1024, max_prefix=64, config_id=7, seed=seed)
+        return make_kv_commit(B or 64, planes=64, row=1024, max_prefix=16, config_id=7, seed=seed)
     if cid == 6:
         return make_expand(B or 64, K or 10, V or 128256, top_k=10, k_next=10, sigma=0.5, config_id=6, seed=seed,
                            threads=threads)

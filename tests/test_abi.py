@@ -33,7 +33,7 @@ def test_header_symbols_exported(L):
     names = declared_functions()
     assert {"spec_verify_chain", "spec_verify_chain_topp", "spec_verify_tree_greedy", "spec_verify_tree_sample",
             "spec_verify_tree_greedy_rows", "spec_verify_tree_sample_rows",
-            "spec_tree_expand", "spec_tree_rerank", "spec_accept_rate"} <= set(names)
+            "spec_tree_expand", "spec_tree_rerank", "spec_kv_commit", "spec_accept_rate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -142,6 +142,20 @@ def test_tree_expand_and_rerank_argument_checks(L):
     assert rr(m=0) == EINVAL
     assert rr(m=51) == EINVAL
     assert rr(M=1025, m=10) == EUNSUPPORTED
+
+
+def test_kv_commit_argument_checks(L):
+    def call(**kw):
+        a = dict(kv=FAKE, planes=4, ps=1 << 20, B=2, bs=1 << 16, pos=2048, row=2048, ps_=6, N=27)
+        a.update(kw)
+        return L.spec_kv_commit(a["kv"], a["planes"], a["ps"], a["B"], a["bs"], a["pos"], a["row"], FAKE, FAKE,
+                                a["ps_"], a["N"], FAKE, FAKE, None)
+    assert call(kv=None) == EINVAL
+    assert call(planes=0) == EINVAL
+    assert call(pos=1024) == EINVAL                      # rows would overlap
+    assert call(N=0) == EINVAL
+    assert call(B=70000) == EUNSUPPORTED
+    assert call(ps_=65) == EUNSUPPORTED                   # a path longer than a tree
 
 
 def test_accept_rate_argument_checks(L):
