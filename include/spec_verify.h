@@ -323,7 +323,10 @@ int spec_tree_rerank(const int32_t* parents, const float* values, int B, int M, 
  *   N           tree nodes (path entries must be below N)
  * A row with accept_len < 0, or a path that is not node 0 followed by
  * increasing node indices below N, moves nothing and gets out_len -1.
- * Rows must not overlap (pos_stride >= row_bytes); B <= 65535 and
+ * Rows must not overlap: pos_stride >= row_bytes, and no two (plane, b,
+ * position) rows may share bytes (a zero plane_stride with planes > 1, or a
+ * zero batch_stride with B > 1, is SPEC_EINVAL; other overlaps are the
+ * caller's to avoid and give undefined contents).  B <= 65535 and
  * path_stride <= SPEC_MAX_NODES (a path is at most one tree's nodes), else
  * SPEC_EUNSUPPORTED.
  */

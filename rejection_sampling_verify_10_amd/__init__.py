@@ -348,6 +348,8 @@ def kv_commit(kv: torch.Tensor, prefix: torch.Tensor, path: torch.Tensor, accept
     row = kv[0, 0, 0]
     if not row.is_contiguous():
         raise ValueError("a KV row must be contiguous")
+    if any(kv.stride(d) == 0 and kv.shape[d] > 1 for d in range(3)):
+        raise ValueError("kv planes, batch rows and positions must not share memory (an expanded view)")
     es = kv.element_size()
     _shape(prefix, "prefix", (B,))
     _shape(accept_len, "accept_len", (B,))

@@ -629,6 +629,8 @@ int spec_kv_commit(void* kv, int planes, long long plane_stride, int B, long lon
     if (planes < 1 || B < 1 || row_bytes < 1 || path_stride < 1 || N < 1 || plane_stride < 0 || batch_stride < 0 ||
         pos_stride < row_bytes)
         return SPEC_EINVAL;
+    // planes or batch rows that share memory would be moved by several workgroups at once
+    if ((planes > 1 && plane_stride == 0) || (B > 1 && batch_stride == 0)) return SPEC_EINVAL;
     if (B > 65535 || path_stride > SPEC_MAX_NODES) return SPEC_EUNSUPPORTED;
     if (!aligned(prefix, 4) || !aligned(path, 4) || !aligned(accept_len, 4) || !aligned(out_len, 4))
         return SPEC_EINVAL;

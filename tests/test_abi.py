@@ -153,6 +153,8 @@ def test_kv_commit_argument_checks(L):
     assert call(kv=None) == EINVAL
     assert call(planes=0) == EINVAL
     assert call(pos=1024) == EINVAL                      # rows would overlap
+    assert call(ps=0) == EINVAL                          # every plane on the same memory
+    assert call(bs=0) == EINVAL                          # every batch row on the same memory
     assert call(N=0) == EINVAL
     assert call(B=70000) == EUNSUPPORTED
     assert call(ps_=65) == EUNSUPPORTED                   # a path longer than a tree
