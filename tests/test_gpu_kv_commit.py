@@ -61,3 +61,18 @@ def test_strided_planes_overlapping_paths_and_errors(R, orc):
     path[3, 1] = k.N
     alen[3] = max(alen[3], 1)
     run(R, orc, k, "strided, overlapping, errors", path=path, alen=alen, layout="batch-first")
+
+
+@pytest.mark.parametrize("row", [8, 1024])
+def test_longest_paths(R, orc, row):
+    """A 64-node path tree (the most nodes a tree has): paths of every depth up to 63, so the
+    path check uses every lane; 16-byte rows are staged whole, 2 KiB rows past 8 moving rows
+    move one at a time."""
+    k = W.make_kv_commit(96, planes=2, row=row, parents=np.arange(-1, 63, dtype=np.int32), max_prefix=3,
+                         config_id=75, seed=row)
+    assert k.path.shape[1] == 64 and k.accept_len.max() >= 60
+    alen = k.accept_len.copy()
+    path = k.path.copy()
+    alen[0] = 63
+    path[0] = np.arange(64, dtype=np.int32)          # the whole tree accepted: nothing moves
+    run(R, orc, k, f"longest paths row={row}", path=path, alen=alen)
