@@ -21,11 +21,14 @@ namespace sv {
 
 namespace {
 
-constexpr int kKvThreads = 256;
-constexpr int kStageVecs = 4;
+// Two waves per block and eight waves per SIMD: the whole grid of a 64-plane,
+// 64-row commit is resident at once, each block one round trip to memory (256
+// threads x 4 vectors and 64 x 16 measured 10% and 4% slower).
+constexpr int kKvThreads = 128;
+constexpr int kStageVecs = 8;
 
 template <int MODE>   // 0: 16-byte vectors, 1: 4-byte words, 2: bytes
-__global__ __launch_bounds__(kKvThreads) void kv_commit_kernel(KVCommitArgs a) {
+__global__ __launch_bounds__(kKvThreads, 8) void kv_commit_kernel(KVCommitArgs a) {
     const int pl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & (kWave - 1);
     // the row's path, checked by every wave: node 0, then increasing nodes below N
     const int d = a.accept_len[b];
@@ -42,24 +45,24 @@ __global__ __launch_bounds__(kKvThreads) void kv_commit_kernel(KVCommitArgs a) {
     uint8_t* base = a.kv + static_cast<long>(pl) * a.plane_stride + static_cast<long>(b) * a.batch_stride;
     if (MODE == 0) {
         const int rv = a.row_bytes / 16;                 // vectors per row
-        const long nv = static_cast<long>(d) * rv;       // vectors that move (rows 1..d)
-        if (nv <= static_cast<long>(kStageVecs) * kKvThreads) {
-            // every read first, then every write
+        if (static_cast<long>(d) * rv <= kStageVecs * kKvThreads) {
+            // every read first, then every write; indices fit 32 bits here
+            const int nv = d * rv;                       // vectors that move (rows 1..d)
             u32x4 v[kStageVecs];
 #pragma unroll
             for (int k = 0; k < kStageVecs; ++k) {
-                const long j = static_cast<long>(k) * kKvThreads + tid;
-                const int t = j < nv ? 1 + static_cast<int>(j / rv) : 0;
+                const int j = k * kKvThreads + tid;
+                const int t = j < nv ? 1 + j / rv : 0;
                 const int src = __shfl(pt, t, kWave);
-                if (j < nv) v[k] = reinterpret_cast<const u32x4*>(base + (pre + src) * a.pos_stride)[j % rv];
+                if (j < nv) v[k] = reinterpret_cast<const u32x4*>(base + (pre + src) * a.pos_stride)[j - (t - 1) * rv];
             }
             __syncthreads();
 #pragma unroll
             for (int k = 0; k < kStageVecs; ++k) {
-                const long j = static_cast<long>(k) * kKvThreads + tid;
+                const int j = k * kKvThreads + tid;
                 if (j < nv) {
-                    const int t = 1 + static_cast<int>(j / rv);
-                    reinterpret_cast<u32x4*>(base + (pre + t) * a.pos_stride)[j % rv] = v[k];
+                    const int t = 1 + j / rv;
+                    reinterpret_cast<u32x4*>(base + (pre + t) * a.pos_stride)[j - (t - 1) * rv] = v[k];
                 }
             }
         } else {
