@@ -136,11 +136,14 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
     """Bytes the dominant kernel must move per launch (see the design notes).  For the trees,
     K is the node count N."""
     if workload == 7:
-        # every moving row read and written once (rows 1..d of each path, in every plane), the
-        # path, prefix and length read and the new length written
+        # every row that moves read and written once (rows t = 1..d of each path with
+        # path[t] != t, in every plane), the path, prefix and length read and the new length
+        # written; tree_path is the committed path array [B, D+1]
+        import numpy as np
         planes, rb = K, top_k
-        moved = sum(int(d) for d in accept_len if d > 0)
-        return 2 * planes * moved * rb + B * (8 + 4) + B * 6 * 4
+        moved = sum(int(np.count_nonzero(tree_path[b, 1:d + 1] != np.arange(1, d + 1)))
+                    for b, d in enumerate(accept_len) if d > 0)
+        return 2 * planes * moved * rb + B * (8 + 4) + B * tree_path.shape[1] * 4
     if workload == 6:
         # every draft row once; per chunk a sorted list of top_k (value, index) pairs plus count
         # and flags written; the children (token, value) and the kept indices written
@@ -361,7 +364,8 @@ def main() -> int:
         args.workload, "token-rows/s")
     al = alen.cpu().numpy()
     alg = algorithmic_bytes(args.workload, B, K, V, top_k, al, esz,
-                            path.cpu().numpy() if sampled_tree else None, ci.parents if sampled_tree else None)
+                            path.cpu().numpy() if sampled_tree else ci.path if kvc else None,
+                            ci.parents if sampled_tree else None)
     achieved = alg / (k_ms * 1e-3) / 1e9
     step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "

@@ -48,22 +48,24 @@ __global__ __launch_bounds__(kKvThreads, 8) void kv_commit_kernel(KVCommitArgs a
         if (static_cast<long>(d) * rv <= kStageVecs * kKvThreads) {
             // every read first, then every write; indices fit 32 bits here
             const int nv = d * rv;                       // vectors that move (rows 1..d)
+            // (a row already in place, path[t] == t, is neither read nor written)
             u32x4 v[kStageVecs];
 #pragma unroll
             for (int k = 0; k < kStageVecs; ++k) {
                 const int j = k * kKvThreads + tid;
                 const int t = j < nv ? 1 + j / rv : 0;
                 const int src = __shfl(pt, t, kWave);
-                if (j < nv) v[k] = reinterpret_cast<const u32x4*>(base + (pre + src) * a.pos_stride)[j - (t - 1) * rv];
+                if (j < nv && src != t)
+                    v[k] = reinterpret_cast<const u32x4*>(base + (pre + src) * a.pos_stride)[j - (t - 1) * rv];
             }
             __syncthreads();
 #pragma unroll
             for (int k = 0; k < kStageVecs; ++k) {
                 const int j = k * kKvThreads + tid;
-                if (j < nv) {
-                    const int t = 1 + j / rv;
+                const int t = j < nv ? 1 + j / rv : 0;
+                const int src = __shfl(pt, t, kWave);
+                if (j < nv && src != t)
                     reinterpret_cast<u32x4*>(base + (pre + t) * a.pos_stride)[j - (t - 1) * rv] = v[k];
-                }
             }
         } else {
             for (int t = 1; t <= d; ++t) {

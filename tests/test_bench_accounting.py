@@ -1,0 +1,32 @@
+"""The algorithmic byte counts behind bench.py's roofline figures, checked against
+independent counts (not the formulas themselves)."""
+
+import numpy as np
+
+import bench
+from rejection_sampling_verify_10_amd import workloads as W
+
+
+def test_chain_topk_bytes():
+    """The headline workload: every target row (bf16) and every draft row (fp32) once, plus a
+    sorted list of 50 (value, index) pairs with its count word per selection chunk."""
+    B, K, V, k = 64, 7, 128256, 50
+    chunks_t, chunks_d = bench.select_chunks(V, 2), bench.select_chunks(V, 4)
+    assert (chunks_t, chunks_d) == (3, 5)          # 112 KiB chunks: 85504 B and 102608 B
+    rows = B * (K + 1) * V * 2 + B * K * V * 4
+    lists = B * ((K + 1) * chunks_t + K * chunks_d) * (k * 8 + 8)
+    assert bench.algorithmic_bytes(2, B, K, V, k) == rows + lists == 362_709_504
+
+
+def test_kv_commit_bytes_are_the_rows_that_change(orc):
+    """Workload 7's count equals twice the bytes of the cache rows the oracle's commit changes
+    (random contents: a moved row differs from the one it replaces), plus the small arrays."""
+    k = W.make_kv_commit(64, planes=3, row=32, max_prefix=16, config_id=7, seed=0)
+    out, _ = orc.kv_commit(k.kv, k.prefix, k.path, k.N, k.accept_len)
+    changed = int(np.count_nonzero(np.any(out != k.kv, axis=3)))
+    row_bytes = k.row * 2
+    small = k.B * (8 + 4) + k.B * k.path.shape[1] * 4
+    got = bench.algorithmic_bytes(7, k.B, k.planes, k.S, row_bytes, k.accept_len, tree_path=k.path)
+    assert got == 2 * changed * row_bytes + small
+    # node 1 (the root's first child) sits in place: such rows are not counted
+    assert any(k.path[b, 1] == 1 for b in range(k.B) if k.accept_len[b] >= 1)
