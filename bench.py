@@ -1,24 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the speculative-decoding verification step on one MI355X.
 
-A step is one spec_verify_chain call (spec_verify_tree_greedy for --workload 3)
-over one batch of synthetic inputs that already sit in HBM.  The default
+A step is one call of the workload's entry point over one batch of synthetic
+inputs that already sit in HBM: spec_verify_chain (workloads 0, 1, 2, 4),
+spec_verify_tree_greedy (3), spec_verify_tree_sample (5), one EAGLE-2
+expansion layer, spec_tree_expand (6), or spec_kv_commit (7).  The default
 workload is the chain verification with B=64, K=7, V=128256 (bf16 target
 logits, fp32 draft probabilities, temperature 0.7, top-k 50 on both
 distributions).  Several copies of the inputs are rotated so that the working
 set exceeds the 256 MB Infinity Cache.
 
-Prints ONE JSON line: verified token-rows/s (B*(K+1) per step; B*N node rows
-for the tree) and the step
-time from K timed steps with nothing else on the stream; the dominant kernel's
-achieved HBM bandwidth against the 8 TB/s peak, timed live with HIP events that
-the library attaches to that kernel's dispatch on the call's stream during a
-second pass of K steps (events between kernels add several microseconds of
-queue latency, so they stay out of the step timing); the
-hardware-counter traffic recorded under profiles/ when it matches the current
-kernel source; and the CPU oracle's throughput on the host cores.
+Prints ONE JSON line: the workload's rows per second (verified token rows
+B*(K+1) for a chain, node rows B*N for a tree, expanded draft rows B*E,
+committed paths B) and the step time from K timed steps with nothing else on
+the stream; the dominant kernel's achieved HBM bandwidth against the 8 TB/s
+peak, timed live with HIP events that the library attaches to that kernel's
+dispatch on the call's stream during a second pass of K steps (events between
+kernels add several microseconds of queue latency, so they stay out of the
+step timing); the hardware-counter traffic recorded under profiles/ when it
+matches the current kernel source; and the CPU oracle's throughput on the host
+cores.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 0|1|2|3|4]
+    python bench.py [--gpus 1] [--steps 400] [--warmup 40] [--workload 0..7]
 """
 
 from __future__ import annotations
