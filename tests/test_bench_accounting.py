@@ -30,3 +30,11 @@ def test_kv_commit_bytes_are_the_rows_that_change(orc):
     assert got == 2 * changed * row_bytes + small
     # node 1 (the root's first child) sits in place: such rows are not counted
     assert any(k.path[b, 1] == 1 for b in range(k.B) if k.accept_len[b] >= 1)
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py --gpus 2 exits with a message before touching torch or a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
