@@ -38,3 +38,26 @@ def test_more_than_one_gpu_is_refused():
     import sys
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_sampled_tree_rows_match_the_oracles_tests(orc):
+    """The sampled-tree walk's row counts (bench.tree_walk_rows, from the tree's shape and the
+    accepted paths) equal counts taken from the oracle's own record of which children it
+    tested (a finite test margin): target rows = visited nodes, tests = tested children,
+    draft rows = visited nodes where some tested child was rejected."""
+    ti = W.make_tree_sampled(24, 1000, config_id=5, seed=3)
+    o = orc.verify_tree_sample(ti.logits, ti.dtype, ti.draft_probs, ti.node_tokens, ti.uniforms, ti.parents,
+                               ti.temperature, ti.top_k)
+    assert np.all(o["accept_len"] >= 0)
+    targets = drafts = tests = 0
+    for b in range(ti.B):
+        visited = [int(n) for n in o["path"][b] if n >= 0]
+        targets += len(visited)
+        tested = np.flatnonzero(~np.isnan(o["m_test"][b]))
+        tests += len(tested)
+        for i, c in enumerate(visited):
+            mine = [n for n in tested if ti.parents[n] == c]
+            accepted = 1 if i + 1 < len(visited) else 0
+            drafts += len(mine) - accepted > 0
+    assert bench.tree_walk_rows(o["path"], ti.parents) == (targets, drafts, tests)
+    assert drafts > 0 and tests > targets - ti.B
