@@ -61,3 +61,22 @@ def test_sampled_tree_rows_match_the_oracles_tests(orc):
             drafts += len(mine) - accepted > 0
     assert bench.tree_walk_rows(o["path"], ti.parents) == (targets, drafts, tests)
     assert drafts > 0 and tests > targets - ti.B
+
+
+def test_dense_walk_rows_match_the_oracles_tests(orc):
+    """The T = 1 walk's count (target rows 0..j, the draft row j when j < K) equals a count
+    from the oracle's record: one target row per ratio test it made (a finite margin), plus
+    row K when every test passed (the bonus draw), and one draft row when a test failed (the
+    residual draw at that row)."""
+    c = W.config(4, 1, B=12, V=2000)
+    o = orc.verify_chain(c.logits, c.dtype, c.draft_probs, c.draft_tokens, c.uniforms, c.temperature, c.top_k)
+    K, V = c.K, c.V
+    tested = (~np.isnan(o["m_test"])).sum(axis=1)          # tests made: j + 1 if j < K, else K
+    j = o["accept_len"]
+    assert np.all(j >= 0)
+    rows = int(np.sum(tested + (tested == j)))             # every test's row; row K for a bonus draw
+    drafts = int(np.sum(tested > j))                        # a failed test: its draft row, residual draw
+    B = c.B
+    want = rows * V * 2 + drafts * V * 4 + B * (K * 12 + (K + 1) * 4 + (K + 2) * 4)
+    assert bench.algorithmic_bytes(4, B, K, V, 0, j) == want
+    assert 0 < drafts < B
