@@ -70,7 +70,9 @@
  * 0 = the method as stated; 1 = on rejection re-sample from p instead of the
  * residual (the "naive" variant of [LEV] section 二); 2 = bonus token drawn
  * from p_{K-1} instead of p_K; 3 = ratio written q/p instead of p/q;
- * 4 = in the sampled tree, a rejected sibling leaves P as it was. */
+ * 4 = in the sampled tree, a rejected sibling leaves P as it was;
+ * 5 = the draw's margin left in units of mass (not divided by S);
+ * 6 = a test's margin measured against the ratio instead of min(1, ratio). */
 static int g_variant = 0;
 void oracle_set_variant(int v) { g_variant = v; }
 
@@ -234,7 +236,7 @@ static int draw_index(const double* r, int V, double S, double u, double* margin
         c += r[i];
         if (t < c) {
             double a = t - prev, b = c - t;
-            *margin = (a < b ? a : b) / S;
+            *margin = (a < b ? a : b) / (g_variant == 5 ? 1.0 : S);
             return i;
         }
     }
@@ -348,7 +350,7 @@ int oracle_verify_chain_p(const void* logits, int dtype, const float* q, const i
             if (c > 0.0) ratio = a / c;
             else ratio = a > 0.0 ? INFINITY : 0.0;
             double thr = ratio < 1.0 ? ratio : 1.0;
-            mtb[k] = fabs((double)ub[k] - thr);
+            mtb[k] = fabs((double)ub[k] - (g_variant == 6 ? ratio : thr));
             if (!((double)ub[k] < thr)) { j = k; break; }
         }
         if (!err) {
@@ -778,19 +780,23 @@ int oracle_tree_rerank(const int32_t* parent, const float* value, int B, int M, 
  * prefix[b] + d + 1.  Layout: row (plane, b, s) at byte offset
  * plane*plane_stride + b*batch_stride + s*pos_stride, row_bytes long.  Rows are
  * moved in increasing t; since path is increasing and path[t] >= t, a row is
- * never overwritten before it is read.  A row with accept_len < 0, or a path
- * that is not 0 followed by increasing node indices below N, moves nothing and
- * gets new length -1.
+ * never overwritten before it is read.  Positions 0 .. capacity-1 exist in every
+ * (plane, b) row.  A row with accept_len < 0, a negative prefix, a path that is
+ * not 0 followed by increasing node indices below N, or a path reaching past the
+ * capacity (prefix + path[t] >= capacity), moves nothing and gets new length -1.
  */
 int oracle_kv_commit(uint8_t* kv, int planes, long long plane_stride, int B, long long batch_stride,
-                     long long pos_stride, int row_bytes, const int32_t* prefix, const int32_t* path,
+                     long long pos_stride, int row_bytes, int capacity, const int32_t* prefix, const int32_t* path,
                      int path_stride, int N, const int32_t* accept_len, int32_t* new_len) {
-    if (planes <= 0 || B <= 0 || row_bytes <= 0 || N <= 0 || path_stride <= 0) return -1;
+    if (planes <= 0 || B <= 0 || row_bytes <= 0 || N <= 0 || path_stride <= 0 || capacity <= 0) return -1;
     for (int b = 0; b < B; ++b) {
         const int d = accept_len[b];
         const int32_t* pb = path + (size_t)b * path_stride;
         int ok = d >= 0 && d < path_stride && d < N && prefix[b] >= 0 && pb[0] == 0;
         for (int t = 1; ok && t <= d; ++t) ok = pb[t] > pb[t - 1] && pb[t] < N;
+        /* every row read (prefix + path[t]) and written (prefix + t <= prefix + path[t])
+         * must exist in the cache */
+        for (int t = 0; ok && t <= d; ++t) ok = (long long)prefix[b] + pb[t] < (long long)capacity;
         if (!ok) { new_len[b] = -1; continue; }
         for (int pl = 0; pl < planes; ++pl) {
             uint8_t* base = kv + (size_t)pl * plane_stride + (size_t)b * batch_stride;
