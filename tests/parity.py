@@ -44,8 +44,10 @@ def to_torch(arr, device="cuda"):
 
 
 def compare_chain(orc: dict, tokens: np.ndarray, alen: np.ndarray, diag, K: int, greedy: bool = False,
-                  rows=None) -> Tally:
-    """Compare GPU outputs (numpy) with an oracle result dict for the given batch rows."""
+                  rows=None, V=None, draft_tokens=None) -> Tally:
+    """Compare GPU outputs (numpy) with an oracle result dict for the given batch rows.
+    V and draft_tokens ([B, K], GPU row order), when given, let a row admitted on a
+    small margin be checked for range and for the draft tokens it accepted."""
     t = Tally()
     B = alen.shape[0]
     rows = range(B) if rows is None else rows
@@ -72,7 +74,6 @@ def compare_chain(orc: dict, tokens: np.ndarray, alen: np.ndarray, diag, K: int,
                     assert abs(diag[b, 2 * K] - orc["S"][i]) <= PROB_TOL, f"row {b} S"
                     assert abs(diag[b, 2 * K + 1] - orc["py"][i]) <= PROB_TOL, f"row {b} p(y)"
                 continue
-            assert np.array_equal(tokens[b, :oa], ot[:oa])
             m = orc["m_draw"][i]
             assert m < MARGIN, f"row {b}: draw differs (gpu {tokens[b, oa]}, oracle {ot[oa]}) at margin {m}"
             t.admissible += 1
@@ -81,7 +82,21 @@ def compare_chain(orc: dict, tokens: np.ndarray, alen: np.ndarray, diag, K: int,
             m = orc["m_test"][i, k]
             assert m < MARGIN, f"row {b}: test {k} differs (gpu len {ga}, oracle {oa}) at margin {m}"
             t.admissible += 1
+        _check_admitted_row(tokens[b], ot, ga, oa, V, None if draft_tokens is None else draft_tokens[b], b)
     return t
+
+
+def _check_admitted_row(gt: np.ndarray, ot: np.ndarray, ga: int, oa: int, V, xb, b: int) -> None:
+    """A row whose last decision differs within the margin must still be well formed: the
+    accepted draft tokens (those both sides accepted equal the oracle's; all of them equal
+    the row's draft tokens when given), one emitted token in [0, V), then -1 padding."""
+    k = min(ga, oa)
+    assert np.array_equal(gt[:k], ot[:k]), f"row {b}: accepted draft tokens differ"
+    if xb is not None:
+        assert np.array_equal(gt[:ga], np.asarray(xb)[:ga]), f"row {b}: accepted tokens are not the draft's"
+    y = int(gt[ga])
+    assert 0 <= y and (V is None or y < V), f"row {b}: emitted token {y} out of range"
+    assert np.all(gt[ga + 1:] == -1), f"row {b}: padding after the emitted token"
 
 
 def oracle_rows(ci, rows):
