@@ -17,14 +17,17 @@
  * Conventions shared by every entry point
  *   - All array arguments except `parents_host` are DEVICE pointers, row-major
  *     and contiguous.  Every buffer is owned by the caller; the library
- *     allocates nothing, keeps no pointer after returning and holds no global
- *     mutable state (calls on different streams may run concurrently as long as
- *     they use different workspaces).
+ *     allocates nothing and keeps no pointer after returning.  Calls on
+ *     different streams may run concurrently as long as they use different
+ *     workspaces.  The library's own state is: a process-wide atomic counter
+ *     that gives every top-k chain call its tag (see the hand-over below) and
+ *     the per-thread request of spec_profile_events.
  *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  Inputs must stay valid and
  *     outputs must not be read until the stream has reached the call.
  *   - `workspace` is device scratch of at least the size reported by the
- *     matching *_workspace_bytes function, 256-byte aligned.  It must be
+ *     matching *_workspace_bytes function (or spec_workspace_bytes, which
+ *     covers every call of a shape), 256-byte aligned.  It must be
  *     zero-filled before its first use (spec_workspace_init, or any zeroing
  *     allocation).  A top-k chain call (temperature > 0, 0 < top_k < V)
  *     needs the part it uses to be zero and leaves it zero (the hand-over
@@ -33,6 +36,19 @@
  *     behind: before a top-k chain call that follows a call of another kind
  *     on the same workspace, zero it again.  A workspace serves one call at a
  *     time: calls that may overlap need separate workspaces.
+ *   - Hand-over inside a top-k chain launch: the finisher workgroups of a
+ *     batch row wait, with a bounded poll, for the words the selection
+ *     workgroups of the same launch store.  Finishers come after every
+ *     selection workgroup in the grid, and the GPU dispatches a launch's
+ *     workgroups in grid order within each XCD, so a finisher only waits for
+ *     workgroups that are running or done; progress relies on that order.
+ *     If words still have not arrived after about 0.1 s (another process
+ *     holding the GPU's compute units), the row gets accept_len =
+ *     SPEC_ROW_TIMED_OUT and -1 tokens, and the launch still ends.  Words
+ *     carry the call's tag, so a word a late workgroup stores after its
+ *     call gave up is ignored by later calls.  A graph replay reuses the tag
+ *     of the captured call: after a replay that reports a timed-out row, zero
+ *     the workspace before the next replay.
  *   - Logit rows are bfloat16 (SPEC_BF16, raw bits) or float32 (SPEC_F32).
  *     Draft probabilities are float32.  Uniforms are float32 in [0, 1).
  *   - Host-detectable argument errors return a negative code and launch
@@ -65,6 +81,9 @@
  *     target rows only up to the first rejection) or every row's statistics
  *     first; by default the walk when B*(K+1) > 1536 or V < 4096.  Results
  *     are the same either way.
+ *     SPEC_VERIFY_SPIN_LIMIT (an integer in [0, 65536]) lowers the number of
+ *     polls a top-k chain finisher makes before it gives up (tests of the
+ *     timed-out path); read on every call.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -86,6 +105,9 @@ enum {
     SPEC_EUNSUPPORTED = -4   /* valid request outside this build's limits */
 };
 
+/* accept_len of a batch row whose top-k chain hand-over timed out (see above). */
+#define SPEC_ROW_TIMED_OUT (-2)
+
 /* Limits of this build: K <= SPEC_MAX_K draft positions, N <= SPEC_MAX_NODES
  * tree nodes, top_k <= SPEC_TOPK_MAX when top-k is active, V < 2^24 and V <=
  * SPEC_MAX_V. */
@@ -99,6 +121,14 @@ enum {
 /* Human-readable text for a return code (static storage). */
 const char* spec_error_string(int code);
 
+/* One workspace size (bytes) that serves every spec_verify_chain,
+ * spec_verify_chain_topp and spec_accept_rate call with B batch rows and K =
+ * K_or_N draft positions, and every spec_verify_tree_greedy(_rows) call with
+ * N = K_or_N tree nodes, over V tokens with this top_k, whatever the dtype and
+ * temperature; 0 if no such call is valid (B, K_or_N or V below 1, V above
+ * SPEC_MAX_V).  It is the largest of the per-call sizes below. */
+size_t spec_workspace_bytes(int B, int K_or_N, int V, int top_k);
+
 /* Workspace sizes (bytes) for the calls below with the same arguments; 0 if the
  * arguments are invalid.  Sizes depend only on the arguments. */
 size_t spec_chain_workspace_bytes(int B, int K, int V, spec_dtype_t dtype, float temperature, int top_k);
@@ -108,6 +138,12 @@ size_t spec_tree_expand_workspace_bytes(int B, int E, int V, int top_k);
 
 /*
  * spec_verify_chain -- batched verification of B drafted chains of K tokens.
+ * "064 · 投机解码", section 二 (the test min(1, p/q), the residual
+ * norm(max(0, p - q)), p and q carrying the temperature and top-k) and section
+ * 三 (the left-to-right loop, the residual draw at the first rejection, the
+ * bonus draw from p_{K+1}); "投机解码与 EAGLE", section 二 (greedy mode);
+ * "Việc giải mã giả định và EAGLE-3", step 2 of the residual routine (zero
+ * residual mass: draw from the target).
  *
  * For each batch row b (independently):
  *   p'_k = softmax(z_k / T) over the top_k largest logits of row k (all V when
@@ -131,7 +167,8 @@ size_t spec_tree_expand_workspace_bytes(int B, int E, int V, int top_k);
  *   uniforms      [B][K+1]     float32 in [0,1)        device, read
  *   temperature   >= 0, finite (0 = greedy); top_k <= 0 or >= V disables top-k
  *   out_tokens    [B][K+1]     int32                   device, written: x_0..x_{j-1}, y, then -1
- *   out_accept_len[B]          int32                   device, written: j in [0,K], -1 on error
+ *   out_accept_len[B]          int32                   device, written: j in [0,K], -1 on error,
+ *                                                      SPEC_ROW_TIMED_OUT (top-k mode only, see above)
  *   out_diag      [B][2K+2]    float32, may be NULL    device, written:
  *                 [k] = p'_k(x_k), [K+k] = q'_k(x_k) for the tested
  *                 positions k <= j, k < K (NaN for k > j; greedy: [k] = 1 if
@@ -166,6 +203,11 @@ int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const 
 
 /*
  * spec_verify_tree_greedy -- greedy verification of a static draft tree.
+ * "EAGLE-2: Faster Inference of Language Models with Dynamic Draft Trees",
+ * section 2.2 (every branch of the draft tree verified in one target pass, the
+ * longest accepted branch kept); "投机解码与 EAGLE", section 二 (temperature 0:
+ * a draft token is accepted when it is the target's argmax) and its EAGLE part
+ * (tree drafts).
  *
  * Node 0 is the root; parents_host[0] = -1 and 0 <= parents_host[n] < n
  * (nodes in topological, e.g. breadth-first, order).  Row n of the logits is
@@ -318,11 +360,16 @@ int spec_tree_rerank(const int32_t* parents, const float* values, int B, int M, 
  *               plane*plane_stride + b*batch_stride + s*pos_stride, row_bytes
  *               long (e.g. planes = layers x {K, V}, a row = heads x head_dim);
  *               16-byte aligned layouts move with 16-byte accesses
+ *   capacity    positions s = 0 .. capacity-1 that exist in every (plane, b)
+ *               row of the cache (>= 1)
  *   prefix      [B] int32 device; path [B][path_stride] int32 device;
  *   accept_len  [B] int32 device; out_len [B] int32 device, written
  *   N           tree nodes (path entries must be below N)
- * A row with accept_len < 0, or a path that is not node 0 followed by
- * increasing node indices below N, moves nothing and gets out_len -1.
+ * A row with accept_len < 0, a negative prefix, a path that is not node 0
+ * followed by increasing node indices below N, or a path whose last (largest)
+ * node lies past the cache (prefix[b] + path[b][d] >= capacity) moves nothing
+ * and gets out_len -1; the check covers every row the move would touch before
+ * any byte of the batch row moves.
  * Rows must not overlap: pos_stride >= row_bytes, and no two (plane, b,
  * position) rows may share bytes (a zero plane_stride with planes > 1, or a
  * zero batch_stride with B > 1, is SPEC_EINVAL; other overlaps are the
@@ -331,11 +378,13 @@ int spec_tree_rerank(const int32_t* parents, const float* values, int B, int M, 
  * SPEC_EUNSUPPORTED.
  */
 int spec_kv_commit(void* kv, int planes, long long plane_stride, int B, long long batch_stride,
-                   long long pos_stride, int row_bytes, const int32_t* prefix, const int32_t* path, int path_stride,
-                   int N, const int32_t* accept_len, int32_t* out_len, void* hip_stream);
+                   long long pos_stride, int row_bytes, int capacity, const int32_t* prefix, const int32_t* path,
+                   int path_stride, int N, const int32_t* accept_len, int32_t* out_len, void* hip_stream);
 
 /*
- * spec_accept_rate -- alpha[b][k] = sum_i min(p'_k(i), q'_k(i)) for k < K, with
+ * spec_accept_rate -- "064 · 投机解码", section 二: the chance that one drafted
+ * token is accepted is the overlap of the two distributions,
+ * alpha[b][k] = sum_i min(p'_k(i), q'_k(i)) for k < K, with
  * p' and q' transformed as in spec_verify_chain (rows 0..K-1 of the logits are
  * read; row K is not).  Greedy (temperature == 0): 1 if the argmax of target
  * row k equals the argmax of draft row k, else 0.  An invalid row gives NaN.
@@ -354,7 +403,8 @@ int spec_workspace_init(void* workspace, size_t workspace_bytes, void* hip_strea
 /*
  * Instrumentation.
  *
- * spec_profile_events: the next verification call made BY THIS HOST THREAD
+ * spec_profile_events (the library's one per-thread state): the next
+ * verification call made BY THIS HOST THREAD
  * launches its dominant (vocabulary-streaming) kernel with `start_event` and
  * `stop_event` attached to the dispatch (hipExtLaunchKernel), so that they hold
  * that kernel's own start and end times; both are hipEvent_t created by the

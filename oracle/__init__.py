@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_tree_expand.argtypes = [P, P, I, I, I, I, I, P, P, P]
         L.oracle_tree_rerank.argtypes = [P, P, I, I, I, P, P, P]
         LL = ctypes.c_longlong
-        L.oracle_kv_commit.argtypes = [P, I, LL, I, LL, LL, I, P, P, I, I, P, P]
+        L.oracle_kv_commit.argtypes = [P, I, LL, I, LL, LL, I, I, P, P, I, I, P, P]
         L.oracle_target_dist.argtypes = [P, I, I, D, I, P]
         L.oracle_draft_dist.argtypes = [P, I, D, I, P]
         L.oracle_argmax_row.argtypes = [P, I, I]
@@ -188,16 +188,18 @@ def tree_rerank(parents, values, m):
     return out
 
 
-def kv_commit(kv, prefix, path, N, accept_len):
-    """KV commit on a copy of kv [planes, B, S, row] (any dtype): returns (new kv, new lengths)."""
+def kv_commit(kv, prefix, path, N, accept_len, capacity=None):
+    """KV commit on a copy of kv [planes, B, S, row] (any dtype): returns (new kv, new lengths).
+    capacity (positions per (plane, b) row) defaults to S."""
     out = np.ascontiguousarray(kv).copy()
     planes, B, S = out.shape[:3]
+    cap = S if capacity is None else int(capacity)
     row_bytes = out[0, 0, 0].nbytes
     pre = np.ascontiguousarray(prefix, dtype=np.int32)
     pth = np.ascontiguousarray(path, dtype=np.int32)
     al = np.ascontiguousarray(accept_len, dtype=np.int32)
     nl = np.empty(B, np.int32)
-    rc = lib().oracle_kv_commit(_p(out), planes, out[0].nbytes, B, out[0, 0].nbytes, row_bytes, row_bytes,
+    rc = lib().oracle_kv_commit(_p(out), planes, out[0].nbytes, B, out[0, 0].nbytes, row_bytes, row_bytes, cap,
                                 _p(pre), _p(pth), pth.shape[1], int(N), _p(al), _p(nl))
     if rc != 0:
         raise ValueError(f"oracle_kv_commit rejected its arguments ({rc})")

@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
         P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.spec_error_string.argtypes = [I]
         L.spec_error_string.restype = ctypes.c_char_p
+        L.spec_workspace_bytes.argtypes = [I, I, I, I]
+        L.spec_workspace_bytes.restype = Z
         L.spec_chain_workspace_bytes.argtypes = [I, I, I, I, F, I]
         L.spec_chain_workspace_bytes.restype = Z
         L.spec_tree_workspace_bytes.argtypes = [I, I, I, I]
@@ -67,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.spec_tree_rerank.argtypes = [P, P, I, I, I, P, P, P, P]
         L.spec_tree_rerank.restype = I
         LL = ctypes.c_longlong
-        L.spec_kv_commit.argtypes = [P, I, LL, I, LL, LL, I, P, P, I, I, P, P, P]
+        L.spec_kv_commit.argtypes = [P, I, LL, I, LL, LL, I, I, P, P, I, I, P, P, P]
         L.spec_kv_commit.restype = I
         L.spec_accept_rate.argtypes = [P, I, P, I, I, I, F, I, P, P, Z, P]
         L.spec_accept_rate.restype = I
@@ -127,6 +129,11 @@ def _workspace(nbytes: int, device: torch.device,
     ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
     p = ws.data_ptr()
     return (p + 255) // 256 * 256, ws
+
+
+def workspace_bytes(B: int, K_or_N: int, V: int, top_k: int = 0) -> int:
+    """One workspace size for every chain, acceptance-rate and greedy-tree call of this shape."""
+    return int(lib().spec_workspace_bytes(B, K_or_N, V, int(top_k)))
 
 
 def chain_workspace_bytes(B: int, K: int, V: int, dtype: int, temperature: float, top_k: int) -> int:
@@ -335,14 +342,19 @@ def tree_rerank(parents: torch.Tensor, values: torch.Tensor, m: int):
 
 
 def kv_commit(kv: torch.Tensor, prefix: torch.Tensor, path: torch.Tensor, accept_len: torch.Tensor, N: int,
-              *, out_len: Optional[torch.Tensor] = None) -> torch.Tensor:
+              *, out_len: Optional[torch.Tensor] = None, capacity: Optional[int] = None) -> torch.Tensor:
     """KV commit of accepted tree paths (``spec_kv_commit``), in place.
 
     kv [planes, B, S, ...] on the GPU, rows = the trailing dimensions (contiguous within a
     row; planes, batch and positions may be strided); prefix [B], path [B, D+1] and
-    accept_len [B] int32.  Returns the new lengths [B] int32.
+    accept_len [B] int32.  capacity (positions per (plane, b) row, at most S) defaults to S;
+    a batch row whose path would reach past it moves nothing.  Returns the new lengths [B]
+    int32 (-1 for such rows and malformed ones).
     """
     planes, B, S = kv.shape[:3]
+    cap = S if capacity is None else int(capacity)
+    if not 1 <= cap <= S:
+        raise ValueError(f"capacity must lie in [1, {S}]")
     if not kv.is_cuda:
         raise ValueError("kv must be a GPU tensor")
     row = kv[0, 0, 0]
@@ -357,7 +369,8 @@ def kv_commit(kv: torch.Tensor, prefix: torch.Tensor, path: torch.Tensor, accept
         raise ValueError("path must be [B, D+1]")
     nl = out_len if out_len is not None else torch.empty((B,), dtype=torch.int32, device=kv.device)
     rc = lib().spec_kv_commit(kv.data_ptr(), planes, kv.stride(0) * es, B, kv.stride(1) * es, kv.stride(2) * es,
-                              row.numel() * es, _dev(prefix, "prefix", torch.int32), _dev(path, "path", torch.int32),
+                              row.numel() * es, cap, _dev(prefix, "prefix", torch.int32),
+                              _dev(path, "path", torch.int32),
                               path.shape[1], int(N), _dev(accept_len, "accept_len", torch.int32),
                               _dev(nl, "out_len", torch.int32), _stream(kv.device))
     _check(rc, "spec_kv_commit")

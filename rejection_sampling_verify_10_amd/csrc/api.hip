@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/spec_verify.h"
 #include "common.hpp"
 #include "internal.hpp"
@@ -15,6 +17,22 @@ namespace {
 
 static_assert(SPEC_TOPK_MAX == kTopkMax, "top-k list width");
 static_assert(SPEC_MAX_V == kMaxV, "vocabulary limit");
+
+// Tags the hand-over words of each top-k chain call (9 bits of them are used),
+// so that a finisher never merges a word an earlier call left in its slot.
+std::atomic<uint32_t> g_chain_calls{0};
+
+// Polls before a top-k chain finisher gives up on words that have not arrived;
+// SPEC_VERIFY_SPIN_LIMIT (a non-negative integer) lowers it, for tests that
+// force the give-up path.
+int spin_limit() {
+    const char* env = getenv("SPEC_VERIFY_SPIN_LIMIT");
+    if (env && *env) {
+        const long v = atol(env);
+        if (v >= 0 && v <= kDefaultSpinLimit) return static_cast<int>(v);
+    }
+    return kDefaultSpinLimit;
+}
 
 thread_local hipEvent_t t_prof_start = nullptr;
 thread_local hipEvent_t t_prof_stop = nullptr;
@@ -291,6 +309,28 @@ size_t spec_accept_rate_workspace_bytes(int B, int K, int V, spec_dtype_t dtype,
     return (c.off + 255) & ~static_cast<size_t>(255);
 }
 
+size_t spec_workspace_bytes(int B, int K_or_N, int V, int top_k) {
+    if (B < 1 || K_or_N < 1 || V < 1 || V > SPEC_MAX_V) return 0;
+    size_t need = 0;
+    const spec_dtype_t dtypes[2] = {SPEC_F32, SPEC_BF16};
+    // temperature 0 (greedy), 1 (draft as given) and any other value (transformed
+    // draft) select the three workspace layouts; 0.5 stands for the last
+    const float temps[3] = {0.f, 1.f, 0.5f};
+    for (spec_dtype_t dt : dtypes) {
+        if (K_or_N <= SPEC_MAX_K) {
+            for (float T : temps) {
+                const size_t c = spec_chain_workspace_bytes(B, K_or_N, V, dt, T, top_k);
+                const size_t a = spec_accept_rate_workspace_bytes(B, K_or_N, V, dt, T, top_k);
+                need = c > need ? c : need;
+                need = a > need ? a : need;
+            }
+        }
+        const size_t t = spec_tree_workspace_bytes(B, K_or_N, V, dt);
+        need = t > need ? t : need;
+    }
+    return need;
+}
+
 static int chain_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
                       const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
                       float temperature, int top_k, float top_p, int32_t* out_tokens, int32_t* out_accept_len,
@@ -364,6 +404,8 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
         SV_TRY(launch_chain_greedy(ca, s));
     } else if (p.mode == 1) {
         p.tk.top_p = top_p;
+        p.tk.tag = g_chain_calls.fetch_add(1, std::memory_order_relaxed) + 1u;
+        p.tk.spin_limit = spin_limit();
         ca.tk = p.tk;
         ca.recw = p.recw;
         TopkChainArgs fa{};
@@ -623,11 +665,11 @@ int spec_verify_tree_greedy_rows(const void* target_logits, spec_dtype_t dtype, 
 }
 
 int spec_kv_commit(void* kv, int planes, long long plane_stride, int B, long long batch_stride,
-                   long long pos_stride, int row_bytes, const int32_t* prefix, const int32_t* path, int path_stride,
-                   int N, const int32_t* accept_len, int32_t* out_len, void* hip_stream) {
+                   long long pos_stride, int row_bytes, int capacity, const int32_t* prefix, const int32_t* path,
+                   int path_stride, int N, const int32_t* accept_len, int32_t* out_len, void* hip_stream) {
     if (!kv || !prefix || !path || !accept_len || !out_len) return SPEC_EINVAL;
     if (planes < 1 || B < 1 || row_bytes < 1 || path_stride < 1 || N < 1 || plane_stride < 0 || batch_stride < 0 ||
-        pos_stride < row_bytes)
+        pos_stride < row_bytes || capacity < 1)
         return SPEC_EINVAL;
     // planes or batch rows that share memory would be moved by several workgroups at once
     if ((planes > 1 && plane_stride == 0) || (B > 1 && batch_stride == 0)) return SPEC_EINVAL;
@@ -642,6 +684,7 @@ int spec_kv_commit(void* kv, int planes, long long plane_stride, int B, long lon
     ka.planes = planes;
     ka.B = B;
     ka.row_bytes = row_bytes;
+    ka.capacity = capacity;
     ka.prefix = prefix;
     ka.path = path;
     ka.path_stride = path_stride;

@@ -27,26 +27,36 @@
 
 namespace sv {
 
-// ---- list words: (value, index, chunk flag, valid) in 64 bits ----
-// bits 63..32: order_key(value); bits 31..2: index; bit 1: the chunk's invalid
-// flag; bit 0: valid.  Zero = not yet written in this call.
-constexpr uint32_t kWordNoIndex = 0x3fffffffu;
-__device__ __forceinline__ unsigned long long list_word(pkey_t key, bool flagged) {
+// ---- list words: (value, index, chunk flag, call tag, valid) in 64 bits ----
+// bits 63..32: order_key(value); bits 31..23: the call's tag; bits 22..2: index
+// (V <= 2^20, so 21 bits hold every index and the no-index code); bit 1: the
+// chunk's invalid flag; bit 0: valid.  A word counts only with the valid bit
+// and this call's tag: a word a late selection unit of an earlier call stored
+// after that call's finisher gave up and cleared its slot is ignored.
+constexpr uint32_t kWordNoIndex = 0x1fffffu;
+constexpr int kTagShift = 23;
+constexpr uint32_t kTagMask = 0x1ffu;
+static_assert(kMaxV <= static_cast<int>(kWordNoIndex), "word index field");
+__device__ __forceinline__ unsigned long long list_word(pkey_t key, bool flagged, uint32_t tag) {
     const int i = key_idx(key);
     const uint32_t idx = (i < 0 || i >= static_cast<int>(kWordNoIndex)) ? kWordNoIndex : static_cast<uint32_t>(i);
-    return (key & 0xffffffff00000000ull) | (static_cast<unsigned long long>(idx) << 2) |
-           (flagged ? 2ull : 0ull) | 1ull;
+    return (key & 0xffffffff00000000ull) | (static_cast<unsigned long long>(tag & kTagMask) << kTagShift) |
+           (static_cast<unsigned long long>(idx) << 2) | (flagged ? 2ull : 0ull) | 1ull;
 }
 __device__ __forceinline__ pkey_t word_key(unsigned long long w) {
-    const uint32_t idx = static_cast<uint32_t>(w) >> 2;
+    const uint32_t idx = (static_cast<uint32_t>(w) >> 2) & kWordNoIndex;
     const int i = idx == kWordNoIndex ? kNoIndex : static_cast<int>(idx);
     return (w & 0xffffffff00000000ull) | (0xffffffffu - static_cast<uint32_t>(i));
 }
+// A list or record word written by this call (valid bit and tag).
+__device__ __forceinline__ bool word_here(unsigned long long w, uint32_t tag) {
+    return (w & 1ull) != 0ull && ((static_cast<uint32_t>(w) >> kTagShift) & kTagMask) == (tag & kTagMask);
+}
 
 // Polls per list batch before a row is given up (each poll sleeps ~256 cycles
-// and waits for a load): about 0.1 s, thousands of times the time between a
-// finisher's dispatch and the completion of the last selection unit.
-constexpr int kSpinLimit = 1 << 16;
+// and waits for a load): about 0.1 s by default (TopkLists::spin_limit),
+// thousands of times the time between a finisher's dispatch and the completion
+// of the last selection unit.
 
 // Merges the C (<= 64) chunk lists of a row from their words (units unit0 ..
 // unit0+C-1), polling until every word is valid.  Lane l ends with the l-th
@@ -55,7 +65,7 @@ constexpr int kSpinLimit = 1 << 16;
 // no more loads to wait for: the vector memory counter retires in order, so a
 // load issued after these stores would wait for their write-through.
 __device__ __forceinline__ bool merge_words(unsigned long long* words, long unit0, int C, pkey_t& out,
-                                            bool& flagged) {
+                                            bool& flagged, uint32_t tag, int spin_limit) {
     const int lane = threadIdx.x & (kWave - 1);
     pkey_t acc = empty_key();
     bool ok = true;
@@ -73,21 +83,22 @@ __device__ __forceinline__ bool merge_words(unsigned long long* words, long unit
             bool missing = false;
 #pragma unroll
             for (int c = 0; c < kMergeBatch; ++c)
-                if (base + c < C) missing |= (w[c] & 1ull) == 0ull;
+                if (base + c < C) missing |= !word_here(w[c], tag);
             if (!__ballot(missing)) break;
-            if (tries >= kSpinLimit) { ok = false; break; }
+            if (tries >= spin_limit) { ok = false; break; }
             __builtin_amdgcn_s_sleep(4);
 #pragma unroll
             for (int c = 0; c < kMergeBatch; ++c)
-                if (base + c < C && (w[c] & 1ull) == 0ull) w[c] = ld_agent64(p + c * kTopkMax);
+                if (base + c < C && !word_here(w[c], tag)) w[c] = ld_agent64(p + c * kTopkMax);
         }
         bool fl = false;
         pkey_t k[kMergeBatch];
 #pragma unroll
         for (int c = 0; c < kMergeBatch; ++c) {
             if (base + c < C) {
-                fl |= (w[c] & 2ull) != 0ull;
-                k[c] = (w[c] & 1ull) ? word_key(w[c]) : empty_key();
+                const bool here = word_here(w[c], tag);
+                fl |= here && (w[c] & 2ull) != 0ull;
+                k[c] = here ? word_key(w[c]) : empty_key();
             }
         }
         flagged |= __ballot(fl) != 0ull;
@@ -165,10 +176,11 @@ __device__ __forceinline__ int nucleus_count(float v, int kk, bool draft, double
 }
 
 // ---- position records: kRecWords words per position (payload in bits 63..32,
-// bit 0 valid): y with accept (bit 2), rows unusable (bit 1: E1 / E3 / E4,
-// they count only if the walk reaches the position) and inputs invalid (bit 3:
-// E2 / E5, they always count); then p'_k(x_k), q'_k(x_k), the draw's mass S
-// and the drawn token's probability.  Zero between calls.
+// the call's tag in bits 31..23 as in the list words, bit 0 valid): y with
+// accept (bit 2), rows unusable (bit 1: E1 / E3 / E4, they count only if the
+// walk reaches the position) and inputs invalid (bit 3: E2 / E5, they always
+// count); then p'_k(x_k), q'_k(x_k), the draw's mass S and the drawn token's
+// probability.  Zero between calls.
 static_assert(kRecWords == 5, "record layout");
 
 constexpr int kFinishWaves = 4;
@@ -180,6 +192,7 @@ struct FinishSmem {
     int32_t tidx[kWave];           // the target's kept indices, value order
     float qpart[kFinishWaves][kWave];   // q'_k at those indices, from wave w's draft entries
     int32_t dkd, dok, dbad;
+    int32_t dlate, dlate1;         // lists of wave 2's draft half, of either half, did not arrive
 };
 
 // Wave 0 of position (b, k)'s finisher: test k and the token to emit if k is
@@ -190,7 +203,8 @@ struct FinishSmem {
 // Stores the position's record words.  (uk, uK, x): u_k, u_K and x_k (x unused
 // for k = K).
 __device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, int k, int it, float pt, int kt,
-                                                   bool ok, const FinishSmem& fs, float uk, float uK, int x) {
+                                                   bool ok, bool late, const FinishSmem& fs, float uk, float uK,
+                                                   int x) {
     const int K = a.K, V = a.V;
     const int lane = threadIdx.x & (kWave - 1);
     const long rbase = static_cast<long>(b) * (K + 1);
@@ -223,10 +237,10 @@ __device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, in
     const float ry = bcast(r, src);
     if (lane < kRecWords) {
         uint32_t hi;
-        uint32_t lo = 1u;
+        uint32_t lo = 1u | ((a.tk.tag & kTagMask) << kTagShift);
         if (lane == 0) {
             hi = static_cast<uint32_t>(y);
-            lo |= (accept ? 4u : 0u) | (ok ? 0u : 2u) | (inputs_ok ? 0u : 8u);
+            lo |= (accept ? 4u : 0u) | (ok ? 0u : 2u) | (inputs_ok ? 0u : 8u) | (late ? 16u : 0u);
         } else if (lane == 1) {
             hi = __float_as_uint(px);
         } else if (lane == 2) {
@@ -242,7 +256,9 @@ __device__ __forceinline__ void position_test_draw(const ChainArgs& a, int b, in
 
 // One wave: batch row b from the K+1 position records (lane k = position k,
 // K <= 63), polled until complete and then cleared: first rejection j, emitted
-// tokens x_0..x_{j-1}, y_j, accept_len = j.
+// tokens x_0..x_{j-1}, y_j, accept_len = j.  A row whose records (or, through a
+// finisher's flag, whose lists) did not arrive within the poll limit gets
+// accept_len = kTimedOut and -1 tokens.
 __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
     const int K = a.K;
     const int lane = threadIdx.x & (kWave - 1);
@@ -252,25 +268,28 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
     // the draft tokens, loaded before any store of this wave (see merge_words)
     const int xl = lane < K ? a.x[static_cast<long>(b) * K + lane] : -1;
     unsigned long long w[kRecWords];
+    const uint32_t tag = a.tk.tag;
+    const unsigned long long filler = 1ull | (static_cast<unsigned long long>(tag & kTagMask) << kTagShift);
 #pragma unroll
-    for (int i = 0; i < kRecWords; ++i) w[i] = have ? ld_agent64(pw + i) : 1ull;
+    for (int i = 0; i < kRecWords; ++i) w[i] = have ? ld_agent64(pw + i) : filler;
     bool timeout = false;
 #pragma unroll 1
     for (int tries = 0;; ++tries) {
         bool missing = false;
 #pragma unroll
-        for (int i = 0; i < kRecWords; ++i) missing |= (w[i] & 1ull) == 0ull;
+        for (int i = 0; i < kRecWords; ++i) missing |= !word_here(w[i], tag);
         if (!__ballot(missing)) break;
-        if (tries >= kSpinLimit) { timeout = true; break; }
+        if (tries >= a.tk.spin_limit) { timeout = true; break; }
         __builtin_amdgcn_s_sleep(4);
 #pragma unroll
         for (int i = 0; i < kRecWords; ++i)
-            if ((w[i] & 1ull) == 0ull) w[i] = ld_agent64(pw + i);
+            if (!word_here(w[i], tag)) w[i] = ld_agent64(pw + i);
     }
     const int y = static_cast<int>(w[0] >> 32);
     const bool acc = (w[0] & 4ull) != 0ull;
     const bool bad = (w[0] & 2ull) != 0ull;
     const bool inputs_bad = (w[0] & 8ull) != 0ull;
+    const bool late = (w[0] & 16ull) != 0ull;       // a finisher gave up on its lists
     const float pk = __uint_as_float(static_cast<uint32_t>(w[1] >> 32));
     const float qk = __uint_as_float(static_cast<uint32_t>(w[2] >> 32));
     const float S = __uint_as_float(static_cast<uint32_t>(w[3] >> 32));
@@ -279,7 +298,10 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
     // whose draft token is rejected; invalid tokens or uniforms count anywhere.
     const unsigned long long stop = __ballot(have && (bad || (lane < K && !acc)));
     const int j = stop ? __ffsll(static_cast<long long>(stop)) - 1 : K;
-    const bool err = timeout || __ballot(have && inputs_bad) != 0ull || (stop && bcast(static_cast<int>(bad), j));
+    // a position whose lists never arrived is unusable wherever it lies: the row
+    // cannot be decided, and it is reported as timed out rather than as bad data
+    const bool timed_out = timeout || __ballot(have && late) != 0ull;
+    const bool err = timed_out || __ballot(have && inputs_bad) != 0ull || (stop && bcast(static_cast<int>(bad), j));
     const int yj = bcast(y, j);
     const float Sj = bcast(S, j), pyj = bcast(py, j);
     if (have) {
@@ -293,7 +315,7 @@ __device__ __forceinline__ void chain_combine(const ChainArgs& a, int b) {
         diag[K + lane] = (err || lane > j) ? NAN : qk;
     }
     if (lane == 0) {
-        a.out_accept_len[b] = err ? -1 : j;
+        a.out_accept_len[b] = timed_out ? kTimedOut : (err ? -1 : j);
         if (diag) {
             diag[2 * K] = err ? NAN : Sj;
             diag[2 * K + 1] = err ? NAN : pyj;
@@ -332,14 +354,14 @@ __device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, in
         uk = a.u[rbase + k];                 // issued before the merges
         uK = a.u[rbase + K];
         if (k < K) x = a.x[static_cast<long>(b) * K + k];
-        done = merge_words(t.words, unit0, t.Ct, key, flagged);
+        done = merge_words(t.words, unit0, t.Ct, key, flagged, t.tag, t.spin_limit);
     } else if (wid <= 2 && k < K) {
         const int c0 = wid == 1 ? 0 : half;
         const int cn = wid == 1 ? half : t.Cd - half;
-        if (cn > 0) done = merge_words(t.words, unit0 + t.Ct + c0, cn, key, flagged);
+        if (cn > 0) done = merge_words(t.words, unit0 + t.Ct + c0, cn, key, flagged, t.tag, t.spin_limit);
         if (wid == 2) {
             fs.dkey[lane] = key;
-            if (lane == 0) fs.dbad = flagged || !done;
+            if (lane == 0) { fs.dbad = flagged || !done; fs.dlate = !done; }
         }
     }
     __syncthreads();
@@ -364,6 +386,7 @@ __device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, in
         float dq;
         const bool okd = kept_dist32(key_val(key), key_idx(key), kd, done && !flagged && !fs.dbad, true, 0.f,
                                      static_cast<float>(t.invT), t.draft_identity != 0, di, dq);
+        if (lane == 0) fs.dlate1 = !done || fs.dlate;
         fs.didx[lane] = di;
         fs.dq[lane] = dq;
         if (lane == 0) { fs.dkd = kd; fs.dok = okd; }
@@ -389,7 +412,8 @@ __device__ __forceinline__ void chain_finish_group(const ChainArgs& a, int b, in
         __syncthreads();
     }
     if (wid == 0) {
-        position_test_draw(a, b, k, it, pt, kt, ok && (k == K || fs.dok != 0), fs, uk, uK, x);
+        const bool late = !done || (k < K && fs.dlate1 != 0);
+        position_test_draw(a, b, k, it, pt, kt, ok && (k == K || fs.dok != 0), late, fs, uk, uK, x);
         clear_words(t.words, unit0, t.Ct);
     } else if (wid <= 2 && k < K) {
         const int c0 = wid == 1 ? 0 : half;

@@ -69,6 +69,8 @@ struct TopkLists {
     float top_p;            // nucleus cut after top-k (chain finish; 1 = off)
     int draft_identity;     // T == 1: q^(1/T) = q exactly
     double invT;
+    uint32_t tag;           // chain calls: this call's tag in the list and record words
+    int spin_limit;         // chain calls: polls before a finisher gives up on missing words
     __host__ __device__ long unit_base(int b, int k) const {
         return static_cast<long>(b) * Ub + static_cast<long>(k) * (Ct + Cd);
     }
@@ -106,6 +108,8 @@ struct ChainArgs {
 // A top-k chain in one launch (topk.hip): B*Ub selection units, then the
 // finisher workgroups, finish_groups(K) per batch row (chain_finish.hpp).
 constexpr int kRecWords = 5;    // 64-bit words of a position record
+constexpr int kTimedOut = -2;   // accept_len of a row whose hand-over words did not arrive in time
+constexpr int kDefaultSpinLimit = 1 << 16;
 struct TopkChainArgs {
     TopkChunkArgs sel;
     ChainArgs ch;
@@ -171,6 +175,7 @@ struct KVCommitArgs {
     uint8_t* kv;                    // row (plane, b, s) at plane*plane_stride + b*batch_stride + s*pos_stride
     long long plane_stride, batch_stride, pos_stride;
     int planes, B, row_bytes;
+    int capacity;                   // positions 0 .. capacity-1 exist in every (plane, b) row
     const int32_t* prefix;          // [B]
     const int32_t* path;            // [B][path_stride]
     int path_stride, N;

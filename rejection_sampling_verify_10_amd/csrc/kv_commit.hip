@@ -3,7 +3,8 @@
 // acceptance).  The verifier appended the N tree nodes' rows at positions
 // prefix[b] + n; the accepted path root..n* (path[b][0..d]) moves to positions
 // prefix[b] + 0..d in every plane (layer x K/V), and the logical length becomes
-// prefix[b] + d + 1.
+// prefix[b] + d + 1.  A batch row whose path or prefix is malformed, or whose
+// last path node lies past the cache's capacity, moves nothing.
 //
 // One workgroup per (plane, batch row).  The path increases and path[t] >= t,
 // so a destination row prefix + t can only be the source of an earlier move
@@ -37,7 +38,11 @@ __global__ __launch_bounds__(kKvThreads, 8) void kv_commit_kernel(KVCommitArgs a
     const int pt = lane < a.path_stride ? pb[lane] : -1;
     const int prev = __shfl_up(pt, 1, kWave);
     const bool lane_bad = lane <= d && (lane == 0 ? pt != 0 : (pt <= prev || pt >= a.N));
-    const bool ok = d >= 0 && d < a.path_stride && d < a.N && pre >= 0 && __ballot(lane_bad) == 0ull;
+    // the path increases, so its last node is the farthest row read (every row
+    // written lies below it): that row must exist in the cache
+    const long last = pre + __shfl(pt, d >= 0 && d < kWave ? d : 0, kWave);
+    const bool ok = d >= 0 && d < a.path_stride && d < a.N && pre >= 0 && last < a.capacity &&
+                    __ballot(lane_bad) == 0ull;
     if (!ok) {
         if (pl == 0 && tid == 0) a.new_len[b] = -1;
         return;

@@ -199,7 +199,8 @@ __device__ __forceinline__ void load_chunk(const char* row, long start, int len,
 template <int DT, bool VEC, bool WORDS>
 __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row, long start, int len, int top_k,
                                              bool is_draft, float* ov, int32_t* oi, int32_t* ocnt,
-                                             uint32_t* oflag, unsigned long long* ow, ChunkSmem& sm) {
+                                             uint32_t* oflag, unsigned long long* ow, uint32_t tag,
+                                             ChunkSmem& sm) {
     using E = Elem<DT>;
     constexpr int EPV = E::kPerVec;
     const int tid = threadIdx.x;
@@ -316,7 +317,7 @@ __device__ __forceinline__ void select_chunk(u32x4 (&d)[kSlots], const char* row
     }
     const int kk = n < top_k ? n : top_k;
     if constexpr (WORDS) {
-        st_agent64(ow + lane, list_word(lane < kk ? key : empty_key(), sm.flags != 0u));
+        st_agent64(ow + lane, list_word(lane < kk ? key : empty_key(), sm.flags != 0u, tag));
     } else {
         ov[lane] = key_val(key);            // every slot: past kk the entries are ignored
         oi[lane] = key_idx(key);
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkChainArgs f
         const int len = static_cast<int>(min(static_cast<long>(t.chunk_t), a.V - start));
         load_chunk<DT, VEC>(row, start, len, d);
         select_chunk<DT, VEC, FIN>(d, row, start, len, t.top_k, false, ov, oi, t.cnt + unit, t.flags + unit,
-                                   t.words + unit * kTopkMax, sm);
+                                   t.words + unit * kTopkMax, t.tag, sm);
     } else {
         const int c = within - t.Ct;
         const char* row = reinterpret_cast<const char*>(a.draft + (static_cast<long>(b) * a.K + k) * a.V);
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkChainArgs f
         const int len = static_cast<int>(min(static_cast<long>(t.chunk_d), a.V - start));
         load_chunk<0, VEC>(row, start, len, d);
         select_chunk<0, VEC, FIN>(d, row, start, len, t.top_k, true, ov, oi, t.cnt + unit, t.flags + unit,
-                                  t.words + unit * kTopkMax, sm);
+                                  t.words + unit * kTopkMax, t.tag, sm);
     }
 }
 

@@ -146,11 +146,13 @@ def test_tree_expand_and_rerank_argument_checks(L):
 
 def test_kv_commit_argument_checks(L):
     def call(**kw):
-        a = dict(kv=FAKE, planes=4, ps=1 << 20, B=2, bs=1 << 16, pos=2048, row=2048, ps_=6, N=27)
+        a = dict(kv=FAKE, planes=4, ps=1 << 20, B=2, bs=1 << 16, pos=2048, row=2048, cap=32, ps_=6, N=27)
         a.update(kw)
-        return L.spec_kv_commit(a["kv"], a["planes"], a["ps"], a["B"], a["bs"], a["pos"], a["row"], FAKE, FAKE,
-                                a["ps_"], a["N"], FAKE, FAKE, None)
+        return L.spec_kv_commit(a["kv"], a["planes"], a["ps"], a["B"], a["bs"], a["pos"], a["row"], a["cap"],
+                                FAKE, FAKE, a["ps_"], a["N"], FAKE, FAKE, None)
     assert call(kv=None) == EINVAL
+    assert call(cap=0) == EINVAL                         # a cache with no positions
+    assert call(cap=-5) == EINVAL
     assert call(planes=0) == EINVAL
     assert call(pos=1024) == EINVAL                      # rows would overlap
     assert call(ps=0) == EINVAL                          # every plane on the same memory
@@ -183,6 +185,28 @@ def test_workspace_sizes(L):
     assert R.chain_workspace_bytes(8, 5, 32000, 1, 0.0, 0) > 0
     assert R.tree_workspace_bytes(32, 27, 32000, 1) > 0
     assert R.accept_rate_workspace_bytes(8, 5, 32000, 1, 0.7, 50) > 0
+
+
+def test_one_workspace_bound_covers_every_call(L):
+    """spec_workspace_bytes(B, K_or_N, V, top_k) bounds the workspace of every chain,
+    acceptance-rate and greedy-tree call of that shape, whatever the dtype and temperature."""
+    L.spec_workspace_bytes.argtypes = [ctypes.c_int] * 4
+    L.spec_workspace_bytes.restype = ctypes.c_size_t
+    import rejection_sampling_verify_10_amd as R
+    for B, K, V, top_k in [(1, 4, 1000, 0), (8, 5, 32000, 0), (64, 7, 128256, 50), (512, 8, 128256, 0),
+                           (512, 8, 128256, 64), (3, 63, 1001, 7), (32, 26, 32000, 0), (5, 1, 1, 0)]:
+        bound = L.spec_workspace_bytes(B, K, V, top_k)
+        assert bound > 0 and bound % 256 == 0
+        for dtype in (0, 1):
+            for T in (0.0, 1.0, 0.7, 1.9):
+                assert R.chain_workspace_bytes(B, K, V, dtype, T, top_k) <= bound, (B, K, V, dtype, T, top_k)
+                assert R.accept_rate_workspace_bytes(B, K, V, dtype, T, top_k) <= bound
+            assert R.tree_workspace_bytes(B, K, V, dtype) <= bound
+    assert L.spec_workspace_bytes(0, 4, 1000, 0) == 0
+    assert L.spec_workspace_bytes(4, 0, 1000, 0) == 0
+    assert L.spec_workspace_bytes(4, 4, (1 << 20) + 1, 0) == 0
+    # a node count past the chain limit still bounds the tree call
+    assert L.spec_workspace_bytes(4, 64, 1000, 0) >= R.tree_workspace_bytes(4, 64, 1000, 1) > 0
 
 
 def test_binding_rejects_cpu_tensors():

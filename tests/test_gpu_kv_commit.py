@@ -18,22 +18,44 @@ def R():
     return R
 
 
-def run(R, orc, k, name, kv=None, path=None, alen=None, layout="planes-first"):
+def run(R, orc, k, name, kv=None, path=None, alen=None, layout="planes-first", prefix=None, capacity=None):
     import torch
     kv = k.kv if kv is None else kv
     path = k.path if path is None else path
     alen = k.accept_len if alen is None else alen
+    prefix = k.prefix if prefix is None else prefix
     print(f"[case] kv commit {name}: B={k.B} planes={kv.shape[0]} S={kv.shape[2]} row={kv.shape[3:]} {layout}",
           flush=True)
-    want, want_len = orc.kv_commit(kv, k.prefix, path, k.N, alen)
+    want, want_len = orc.kv_commit(kv, prefix, path, k.N, alen, capacity=capacity)
     if layout == "batch-first":                      # planes strided over the batch: [B, planes, S, row] memory
         dev = torch.from_numpy(np.ascontiguousarray(kv.swapaxes(0, 1))).cuda().transpose(0, 1)
     else:
         dev = torch.from_numpy(np.ascontiguousarray(kv)).cuda()
-    nl = R.kv_commit(dev, to_torch(k.prefix), to_torch(path), to_torch(alen), k.N)
+    nl = R.kv_commit(dev, to_torch(prefix), to_torch(path), to_torch(alen), k.N, capacity=capacity)
     torch.cuda.synchronize()
     assert np.array_equal(nl.cpu().numpy(), want_len), name
     assert np.array_equal(dev.cpu().numpy(), want), name
+    return want_len
+
+
+@pytest.mark.parametrize("row", [1024, 10])
+def test_rows_past_the_capacity(R, orc, row):
+    """Batch rows whose path reaches past the cache (prefix + path[d] >= capacity, or a prefix
+    beyond it) are error rows that move nothing; the check runs before any load, so the
+    kernel never touches memory past the cache.  A path ending on the last position moves."""
+    k = W.make_kv_commit(16, planes=3, row=row, max_prefix=6, config_id=77, seed=row)
+    S = k.kv.shape[2]
+    pre = k.prefix.copy()
+    last = k.path[np.arange(k.B), k.accept_len]
+    pre[0] = S - 1 - last[0]                          # exactly fits
+    pre[1] = S - last[1]                              # one row past the end
+    pre[2] = 2 ** 30                                  # far past the end
+    pre[3] = S - 1 - last[3]
+    nl = run(R, orc, k, f"capacity row={row}", prefix=pre)
+    assert nl[0] >= 0 and nl[1] == -1 and nl[2] == -1
+    cap = S - 3
+    nl = run(R, orc, k, f"capacity {cap} row={row}", prefix=pre, capacity=cap)
+    assert nl[0] == -1 and nl[3] == -1
 
 
 def test_workload7_full(R, orc):

@@ -150,3 +150,35 @@ def test_kv_commit_error_rows_move_nothing(orc):
     out, nl = orc.kv_commit(k.kv, k.prefix, path, k.N, al)
     for b in range(4):
         assert nl[b] == -1 and np.array_equal(out[:, b], k.kv[:, b])
+
+
+def test_kv_commit_rows_past_the_capacity_move_nothing(orc):
+    """A batch row whose path would read or write a position at or past the cache's capacity
+    is an error row (new length -1, nothing moved); a path that ends exactly at the last
+    position moves as usual.  The expected result is a numpy gather on a copy."""
+    k = W.make_kv_commit(8, planes=2, row=4, max_prefix=4, config_id=76, seed=0)
+    S = k.kv.shape[2]
+    path, al, pre = k.path.copy(), k.accept_len.copy(), k.prefix.copy()
+    for b in range(4):                                # paths 0, 1, 4 of depth 2
+        al[b] = 2
+        path[b, :3] = [0, 1, 4]
+        path[b, 3:] = -1
+    pre[0] = S - 5                                    # last row read at S - 1: fits
+    pre[1] = S - 4                                    # last row read at S: past the cache
+    pre[2] = S + 3                                    # prefix itself past the cache
+    pre[3] = S - 5
+    cap = np.full(8, S)
+    out, nl = orc.kv_commit(k.kv, pre, path, k.N, al)
+    out_small, nl_small = orc.kv_commit(k.kv, pre, path, k.N, al, capacity=S - 1)
+    for b in range(8):
+        d = al[b]
+        fits = pre[b] + path[b, d] < cap[b]
+        if not fits:
+            assert nl[b] == -1 and np.array_equal(out[:, b], k.kv[:, b]), b
+            continue
+        want = k.kv[:, b].copy()
+        want[:, pre[b]:pre[b] + d + 1] = k.kv[:, b, pre[b] + path[b, :d + 1]]
+        assert nl[b] == pre[b] + d + 1 and np.array_equal(out[:, b], want), b
+    assert nl[0] == S - 5 + 3 and nl[1] == -1 and nl[2] == -1
+    # one position less: row 0's last read (S - 1) no longer exists
+    assert nl_small[0] == -1 and np.array_equal(out_small[:, 0], k.kv[:, 0])
