@@ -354,10 +354,12 @@ int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const 
                       out_tokens, out_accept_len, out_diag, workspace, workspace_bytes, hip_stream);
 }
 
-static int chain_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
-                      const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
-                      float temperature, int top_k, float top_p, int32_t* out_tokens, int32_t* out_accept_len,
-                      float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream) {
+// Host checks of a chain call's arguments (workspace aside); the workspace size
+// it needs goes to *need.
+static int chain_check(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                       const int32_t* draft_tokens, const float* uniforms, int B, int K, int V, float temperature,
+                       int top_k, float top_p, int32_t* out_tokens, int32_t* out_accept_len, float* out_diag,
+                       size_t* need) {
     int rc = check_common(target_logits, dtype, B, K, V, temperature);
     if (rc) return rc;
     const bool greedy = temperature == 0.f;
@@ -372,9 +374,21 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
     }
     // the nucleus is built on the top-k path's kept lists: it needs top-k and a temperature
     if (top_p < 1.f && (greedy || !topk_active(top_k, V))) return SPEC_EUNSUPPORTED;
-    const size_t need = spec_chain_workspace_bytes(B, K, V, dtype, temperature, top_k);
+    *need = spec_chain_workspace_bytes(B, K, V, dtype, temperature, top_k);
+    return SPEC_OK;
+}
+
+static int chain_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                      float temperature, int top_k, float top_p, int32_t* out_tokens, int32_t* out_accept_len,
+                      float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    size_t need = 0;
+    int rc = chain_check(target_logits, dtype, draft_probs, draft_tokens, uniforms, B, K, V, temperature, top_k,
+                         top_p, out_tokens, out_accept_len, out_diag, &need);
+    if (rc) return rc;
     rc = check_workspace(workspace, workspace_bytes, need);
     if (rc) return rc;
+    const bool greedy = temperature == 0.f;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     ProfileScope prof;
