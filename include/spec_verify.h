@@ -20,8 +20,9 @@
  *     allocates nothing and keeps no pointer after returning.  Calls on
  *     different streams may run concurrently as long as they use different
  *     workspaces.  The library's own state is: a process-wide atomic counter
- *     that gives every top-k chain call its tag (see the hand-over below) and
- *     the per-thread request of spec_profile_events.
+ *     that gives every top-k chain call its tag (see the hand-over below),
+ *     the per-thread request of spec_profile_events, and the device scratch
+ *     of spec_verify_chain_noalloc (one array per GPU, looked up on first use).
  *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  Inputs must stay valid and
  *     outputs must not be read until the stream has reached the call.
@@ -102,7 +103,8 @@ enum {
     SPEC_EINVAL = -1,        /* bad sizes, pointers, dtype, temperature, parents */
     SPEC_EWORKSPACE = -2,    /* workspace missing, misaligned or too small */
     SPEC_ELAUNCH = -3,       /* a kernel launch failed (hipGetLastError) */
-    SPEC_EUNSUPPORTED = -4   /* valid request outside this build's limits */
+    SPEC_EUNSUPPORTED = -4,  /* valid request outside this build's limits */
+    SPEC_ESCRATCH = -5       /* spec_verify_chain_noalloc: more scratch needed than it holds */
 };
 
 /* accept_len of a batch row whose top-k chain hand-over timed out (see above). */
@@ -200,6 +202,27 @@ int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const 
                            float temperature, int top_k, float top_p, int32_t* out_tokens,
                            int32_t* out_accept_len, float* out_diag, void* workspace, size_t workspace_bytes,
                            void* hip_stream);
+
+/*
+ * spec_verify_chain_noalloc -- spec_verify_chain for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and kernels, no
+ * workspace: the call uses a device array of SPEC_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends, and calls
+ * no hipMalloc, hipFree or other allocating routine.  A call whose workspace
+ * (spec_chain_workspace_bytes) would exceed that size returns SPEC_ESCRATCH
+ * and launches nothing.  The first call on a device looks the array up (with
+ * that device current); the array is zero-filled by a fill kernel on the
+ * call's stream before a top-k call whenever another kind of call used it
+ * since.  Every call on a GPU shares that GPU's array: calls that may overlap
+ * (different streams, or several host threads, without ordering between them)
+ * race and give undefined results; order them on one stream.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (32u << 20)
+int spec_verify_chain_noalloc(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                              const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                              float temperature, int top_k, int32_t* out_tokens, int32_t* out_accept_len,
+                              float* out_diag, void* hip_stream);
 
 /*
  * spec_verify_tree_greedy -- greedy verification of a static draft tree.

@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.spec_accept_rate_workspace_bytes.restype = Z
         L.spec_verify_chain.argtypes = [P, I, P, P, P, I, I, I, F, I, P, P, P, P, Z, P]
         L.spec_verify_chain.restype = I
+        L.spec_verify_chain_noalloc.argtypes = [P, I, P, P, P, I, I, I, F, I, P, P, P, P]
+        L.spec_verify_chain_noalloc.restype = I
         L.spec_verify_chain_topp.argtypes = [P, I, P, P, P, I, I, I, F, I, F, P, P, P, P, Z, P]
         L.spec_verify_chain_topp.restype = I
         L.spec_verify_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, Z, P]
@@ -203,6 +205,45 @@ def verify_chain(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor
                                      tokens.data_ptr(), alen.data_ptr(), dg.data_ptr() if dg is not None else None,
                                      wp, need, _stream(dev))
         _check(rc, "spec_verify_chain")
+    return (tokens, alen, dg) if diag else (tokens, alen)
+
+
+def verify_chain_noalloc(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor],
+                         draft_tokens: torch.Tensor, uniforms: Optional[torch.Tensor],
+                         temperature: float = 1.0, top_k: int = 0, *, diag: bool = False,
+                         out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """``spec_verify_chain_noalloc``: :func:`verify_chain` on the library's own device
+    scratch (no workspace; with ``out`` given the call allocates nothing at all).
+    Calls that may overlap on one GPU race."""
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    _shape(draft_probs, "draft_probs", (B, K, V))
+    _shape(draft_tokens, "draft_tokens", (B, K))
+    _shape(uniforms, "uniforms", (B, K + 1))
+    if float(temperature) != 0.0 and (draft_probs is None or uniforms is None):
+        raise ValueError("sampling verification needs draft_probs and uniforms")
+    if out is None:
+        tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        dg = torch.empty((B, 2 * K + 2), dtype=torch.float32, device=dev) if diag else None
+    else:
+        tokens, alen = out[0], out[1]
+        dg = out[2] if diag else None
+        _shape(tokens, "out tokens", (B, K + 1))
+        _shape(alen, "out accept_len", (B,))
+        if diag:
+            _shape(dg, "out diag", (B, 2 * K + 2))
+    rc = lib().spec_verify_chain_noalloc(
+        _dev(target_logits, "target_logits"), code,
+        _dev(draft_probs, "draft_probs", torch.float32) if draft_probs is not None else None,
+        _dev(draft_tokens, "draft_tokens", torch.int32),
+        _dev(uniforms, "uniforms", torch.float32) if uniforms is not None else None,
+        B, K, V, float(temperature), int(top_k), _dev(tokens, "out tokens", torch.int32),
+        _dev(alen, "out accept_len", torch.int32), _dev(dg, "out diag", torch.float32) if dg is not None else None,
+        _stream(dev))
+    _check(rc, "spec_verify_chain_noalloc")
     return (tokens, alen, dg) if diag else (tokens, alen)
 
 

@@ -6,12 +6,16 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/spec_verify.h"
 #include "common.hpp"
 #include "internal.hpp"
 
 using namespace sv;
+
+// Device scratch of spec_verify_chain_noalloc (see ScratchSlot below).
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -265,6 +269,22 @@ RowStatsArgs rowstats_args(const void* base, int dtype, int V, int rows_per_batc
     return a;
 }
 
+// ---- device scratch of spec_verify_chain_noalloc (for callers that cannot
+// allocate).  Each GPU the library runs on holds its own copy of this array
+// until the process ends.  In host code `scratch` only names the symbol: its
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is ever handed to a kernel or a fill.
+constexpr size_t kScratchBytes = SPEC_NOALLOC_SCRATCH_BYTES;
+
+constexpr int kScratchDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;           // the device address of `scratch` on this device
+    hipError_t err = hipSuccess;
+    std::atomic<bool> zeroed{false};   // no call other than a top-k chain has written it since it was zeroed
+};
+ScratchSlot g_scratch[kScratchDevices];
+
 #define SV_TRY(expr)                                  \
     do {                                              \
         if ((expr) != hipSuccess) return SPEC_ELAUNCH; \
@@ -281,6 +301,7 @@ const char* spec_error_string(int code) {
         case SPEC_EWORKSPACE: return "workspace missing, misaligned or too small";
         case SPEC_ELAUNCH: return "kernel launch failed";
         case SPEC_EUNSUPPORTED: return "outside the limits of this build";
+        case SPEC_ESCRATCH: return "the call needs more device scratch than the no-allocation entry point holds";
         default: return "unknown error";
     }
 }
@@ -352,6 +373,46 @@ int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const 
     if (!(top_p > 0.f && top_p <= 1.f)) return SPEC_EINVAL;
     return chain_call(target_logits, dtype, draft_probs, draft_tokens, uniforms, B, K, V, temperature, top_k, top_p,
                       out_tokens, out_accept_len, out_diag, workspace, workspace_bytes, hip_stream);
+}
+
+static int chain_check(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                       const int32_t* draft_tokens, const float* uniforms, int B, int K, int V, float temperature,
+                       int top_k, float top_p, int32_t* out_tokens, int32_t* out_accept_len, float* out_diag,
+                       size_t* need);
+
+int spec_verify_chain_noalloc(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                              const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                              float temperature, int top_k, int32_t* out_tokens, int32_t* out_accept_len,
+                              float* out_diag, void* hip_stream) {
+    size_t need = 0;
+    int rc = chain_check(target_logits, dtype, draft_probs, draft_tokens, uniforms, B, K, V, temperature, top_k,
+                         1.f, out_tokens, out_accept_len, out_diag, &need);
+    if (rc) return rc;
+    if (need > kScratchBytes) return SPEC_ESCRATCH;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return SPEC_ELAUNCH;
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] {
+        slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess && slot.ptr == nullptr) slot.err = hipErrorInvalidSymbol;
+    });
+    if (slot.err != hipSuccess) return SPEC_ELAUNCH;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    // A top-k chain call needs the words it uses to be zero and leaves them zero;
+    // every other call leaves scratch data behind.  The array is zero-filled (a
+    // fill kernel on the caller's stream, no memset node) before its first top-k
+    // chain call and again after any other call used it.
+    const bool topk = temperature != 0.f && topk_active(top_k, V);
+    if (topk) {
+        if (!slot.zeroed.load(std::memory_order_acquire)) {
+            if (launch_zero_fill(slot.ptr, kScratchBytes, s) != hipSuccess) return SPEC_ELAUNCH;
+            slot.zeroed.store(true, std::memory_order_release);
+        }
+    } else if (need > 0) {
+        slot.zeroed.store(false, std::memory_order_release);
+    }
+    return chain_call(target_logits, dtype, draft_probs, draft_tokens, uniforms, B, K, V, temperature, top_k, 1.f,
+                      out_tokens, out_accept_len, out_diag, slot.ptr, kScratchBytes, hip_stream);
 }
 
 // Host checks of a chain call's arguments (workspace aside); the workspace size
