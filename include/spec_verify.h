@@ -96,7 +96,11 @@
 extern "C" {
 #endif
 
-typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+/* Element type of logit rows.  A plain integer, so that a value outside the two
+ * below is an argument error the library reports (SPEC_EINVAL), not an
+ * out-of-range enumeration. */
+typedef int32_t spec_dtype_t;
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
 
 enum {
     SPEC_OK = 0,

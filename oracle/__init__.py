@@ -39,11 +39,14 @@ def build(force: bool = True) -> str:
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library; ORACLE_LIBRARY names another build of the same source (the
+    sanitizer build of the host-side tests)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("ORACLE_LIBRARY") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         L.oracle_verify_chain.argtypes = [P, I, P, P, P, I, I, I, D, I, P, P, P, P, P, P, P, P]
         L.oracle_verify_chain_p.argtypes = [P, I, P, P, P, I, I, I, D, I, D, P, P, P, P, P, P, P, P]
@@ -60,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_draft_dist.argtypes = [P, I, D, I, P]
         L.oracle_argmax_row.argtypes = [P, I, I]
         L.oracle_set_variant.argtypes = [I]
+        L.oracle_set_threads.argtypes = [I]
+        L.oracle_set_threads.restype = None
         for f in ("oracle_verify_chain", "oracle_verify_chain_p", "oracle_target_dist_p", "oracle_draft_dist_p",
                   "oracle_verify_tree_greedy", "oracle_accept_rate",
                   "oracle_verify_tree_sample", "oracle_tree_expand", "oracle_tree_rerank", "oracle_kv_commit",
@@ -84,6 +89,11 @@ def _logits_arr(logits: np.ndarray, dtype: int) -> np.ndarray:
 def set_variant(v: int) -> None:
     """Plant a deliberate mistake (tests of the pins only); 0 restores the method."""
     lib().oracle_set_variant(int(v))
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's loops over batch rows."""
+    lib().oracle_set_threads(int(n))
 
 
 def max_threads() -> int:

@@ -76,6 +76,15 @@
 static int g_variant = 0;
 void oracle_set_variant(int v) { g_variant = v; }
 
+/* Threads of the OpenMP loops over batch rows (the benchmark times one and all). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -32,13 +32,15 @@ class SpecError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """Load the HIP library (raises if it has not been built)."""
+    """Load the HIP library (raises if it has not been built).  SPEC_VERIFY_LIBRARY names
+    another build of the same sources to load instead (e.g. a host-sanitizer build)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise SpecError(f"{LIB_PATH} is missing: build it with "
+        path = os.environ.get("SPEC_VERIFY_LIBRARY") or LIB_PATH
+        if not os.path.exists(path):
+            raise SpecError(f"{path} is missing: build it with "
                             "`python -m rejection_sampling_verify_10_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.spec_error_string.argtypes = [I]
         L.spec_error_string.restype = ctypes.c_char_p
