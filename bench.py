@@ -4,7 +4,8 @@
 A step is one call of the workload's entry point over one batch of synthetic
 inputs that already sit in HBM: spec_verify_chain (workloads 0, 1, 2, 4),
 spec_verify_tree_greedy (3), spec_verify_tree_sample (5), one EAGLE-2
-expansion layer, spec_tree_expand (6), or spec_kv_commit (7).  The default
+expansion layer, spec_tree_expand (6), spec_kv_commit (7), or spec_accept_rate
+on the inputs of workload 4 (8).  The default
 workload is the chain verification with B=64, K=7, V=128256 (bf16 target
 logits, fp32 draft probabilities, temperature 0.7, top-k 50 on both
 distributions).  Several copies of the inputs are rotated so that the working
@@ -21,7 +22,7 @@ step timing); the hardware-counter traffic recorded under profiles/ when it
 matches the current kernel source; and the CPU oracle's throughput on the host
 cores.
 
-    python bench.py [--gpus 1] [--steps 400] [--warmup 40] [--workload 0..7]
+    python bench.py [--gpus 1] [--steps 400] [--warmup 40] [--workload 0..8]
 """
 
 from __future__ import annotations
@@ -60,6 +61,9 @@ WORKLOADS = {
     7: dict(name="KV commit of accepted tree paths B=64, 64 planes (32 layers x K/V), 2 KiB rows (8 heads x 128 "
                  "x bf16), 27-node tree, prefix <= 16",
             kernel="kv_commit_kernel", copies=8, oracle_rows=64, dtype="bytes (bf16 rows)"),
+    8: dict(name="acceptance rate B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
+            kernel="alpha_row_kernel", copies=1, oracle_rows=32, single_kernel=True,
+            dtype="bf16 in, f32 exp and terms, f64 sums"),
     6: dict(name="EAGLE-2 expansion layer B=64 E=10 V=128256, fp32 draft probs, top_k=10 children per node, "
                  "k_next=10 kept",
             kernel="topk_chunk_kernel", copies=2, oracle_rows=8, dtype="f32 in, f32 select and value products"),
@@ -139,6 +143,9 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
                       tree_path=None, parents=None) -> float:
     """Bytes the dominant kernel must move per launch (see the design notes).  For the trees,
     K is the node count N."""
+    if workload == 8:
+        # target rows 0..K-1 and every draft row once, alpha written
+        return B * K * V * (esz + 4) + B * K * 4
     if workload == 7:
         # every row that moves read and written once (rows t = 1..d of each path with
         # path[t] != t, in every plane), the path, prefix and length read and the new length
@@ -262,6 +269,7 @@ def main() -> int:
     t0 = time.time()
     ci = W.config(args.workload, seed=args.seed)
     tree = args.workload == 3
+    arate = args.workload == 8
     sampled_tree = args.workload == 5
     expand = args.workload == 6
     kvc = args.workload == 7
@@ -315,6 +323,13 @@ def main() -> int:
         alen = torch.empty((B,), dtype=torch.int32, device=dev)
         parents = ci.parents.tolist()
         rows_per_step = B * K                  # node rows verified
+    elif arate:
+        B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
+        base = [to_dev(ci.logits), to_dev(ci.draft_probs)]
+        alpha_out = torch.empty((B, K), dtype=torch.float32, device=dev)
+        alen = torch.zeros((B,), dtype=torch.int32, device=dev)
+        ws = R.new_workspace(R.accept_rate_workspace_bytes(B, K, V, ci.dtype, T, top_k), dev)
+        rows_per_step = B * K                  # (target, draft) row pairs compared
     else:
         B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
         base = [to_dev(ci.logits), to_dev(ci.draft_probs), to_dev(ci.draft_tokens), to_dev(ci.uniforms)]
@@ -339,6 +354,9 @@ def main() -> int:
         elif sampled_tree:
             z, q, nt, u = sets[i % len(sets)]
             R.verify_tree_sample(z, q, nt, u, parents, T, top_k, out=(path, tok, alen))
+        elif arate:
+            z, q = sets[i % len(sets)]
+            R.accept_rate(z, q, T, top_k, out=alpha_out, workspace=ws)
         else:
             z, q, x, u = sets[i % len(sets)]
             R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
@@ -375,8 +393,8 @@ def main() -> int:
         # the kernel is the whole call: its time cannot exceed the step time of the timed pass
         k_ms = min(k_ms, ms_step)
     value = rows_per_step / (ms_step * 1e-3)
-    unit = {3: "node-rows/s", 5: "node-rows/s", 6: "expanded draft rows/s", 7: "committed paths/s"}.get(
-        args.workload, "token-rows/s")
+    unit = {3: "node-rows/s", 5: "node-rows/s", 6: "expanded draft rows/s", 7: "committed paths/s",
+            8: "row pairs/s"}.get(args.workload, "token-rows/s")
     al = alen.cpu().numpy()
     alg = algorithmic_bytes(args.workload, B, K, V, top_k, al, esz,
                             path.cpu().numpy() if sampled_tree else ci.path if kvc else None,
@@ -385,7 +403,7 @@ def main() -> int:
     step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak)"
-        + ("" if (expand or kvc) else "; accept_len histogram "
+        + ("" if (expand or kvc or arate) else "; accept_len histogram "
            f"{np.bincount(al[al >= 0], minlength=(K + 1) if not (tree or sampled_tree) else 1).tolist()}"))
     traffic = counter_traffic(args.workload)
     probe = read_probe_gbps(R, torch, dev)
@@ -410,6 +428,8 @@ def main() -> int:
                 elif sampled_tree:
                     oracle.verify_tree_sample(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows],
                                               ci.node_tokens[:rows], ci.uniforms[:rows], ci.parents, T, top_k)
+                elif arate:
+                    oracle.accept_rate(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], T, top_k)
                 else:
                     oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
                                         ci.uniforms[:rows], T, top_k)
@@ -459,9 +479,12 @@ def main() -> int:
                     "rows": "committed paths", "input_copies": wl["copies"], "parallelism": "single GPU"}
                    if kvc else
                    {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
+                    "rows": "(target, draft) row pairs", "input_copies": wl["copies"], "parallelism": "single GPU"}
+                   if arate else
+                   {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
                     "input_copies": wl["copies"], "parallelism": "single GPU"}),
         "step_algorithmic_GBps": step_alg_gbs,
-        "emitted_tokens_per_s": float(np.sum(al[al >= 0] + 1)) / (ms_step * 1e-3),
+        "emitted_tokens_per_s": None if arate else float(np.sum(al[al >= 0] + 1)) / (ms_step * 1e-3),
         "roofline": {"bound": "hbm", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg,

@@ -421,16 +421,23 @@ def kv_commit(kv: torch.Tensor, prefix: torch.Tensor, path: torch.Tensor, accept
 
 
 def accept_rate(target_logits: torch.Tensor, draft_probs: torch.Tensor, temperature: float = 1.0,
-                top_k: int = 0) -> torch.Tensor:
-    """alpha[b, k] = sum min(p'_k, q'_k) (``spec_accept_rate``); returns [B, K] f32."""
+                top_k: int = 0, *, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """alpha[b, k] = sum min(p'_k, q'_k) (``spec_accept_rate``); returns [B, K] f32.
+    ``out`` reuses the output tensor and ``workspace`` a workspace, as for :func:`verify_chain`."""
     B, K1, V = target_logits.shape
     K = K1 - 1
     dev = target_logits.device
     code = _dtype_code(target_logits)
     _shape(draft_probs, "draft_probs", (B, K, V))
-    alpha = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if out is None:
+        alpha = torch.empty((B, K), dtype=torch.float32, device=dev)
+    else:
+        _shape(out, "out alpha", (B, K))
+        _dev(out, "out alpha", torch.float32)
+        alpha = out
     need = accept_rate_workspace_bytes(B, K, V, code, temperature, top_k)
-    wp, ws = _workspace(need, dev)
+    wp, ws = _workspace(need, dev, workspace)
     rc = lib().spec_accept_rate(_dev(target_logits, "target_logits"), code,
                                 _dev(draft_probs, "draft_probs", torch.float32), B, K, V,
                                 float(temperature), int(top_k), alpha.data_ptr(), wp, need, _stream(dev))

@@ -813,6 +813,9 @@ int spec_accept_rate(const void* target_logits, spec_dtype_t dtype, const float*
         SV_TRY(launch_topk_chunks(ta, s, prof.timing()));
         aa.tk = p.tk;
         SV_TRY(launch_alpha_topk(aa, s));
+    } else if (alpha_rows_fit(aa)) {
+        // every target and draft row read once, in one launch
+        SV_TRY(launch_alpha_rows(aa, s, prof.timing()));
     } else {
         SV_TRY(launch_rowstats(
             rowstats_args(target_logits, dtype, V, K, K + 1, B, false, temperature, nullptr, 0, p.st), s, prof.timing()));

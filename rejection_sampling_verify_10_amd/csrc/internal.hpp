@@ -224,6 +224,9 @@ hipError_t launch_tree_expand(const TreeExpandArgs& a, hipStream_t s);
 hipError_t launch_tree_rerank(const TreeRerankArgs& a, hipStream_t s);
 hipError_t launch_kv_commit(const KVCommitArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s);
+// Dense acceptance rate in one pass per row (alpha.hip), for rows that fit its registers.
+bool alpha_rows_fit(const AlphaArgs& a);
+hipError_t launch_alpha_rows(const AlphaArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_alpha_greedy(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, void* sink, hipStream_t s);

@@ -120,8 +120,10 @@ __global__ __launch_bounds__(kWave) void tree_kernel(TreeArgs a) {
     if (n == 0) a.out_accept_len[b] = dbest;
 }
 
-// alpha = sum_i min(p'_i, q'_i) over dense rows (fp32 terms, fp64 sums).
-template <int DT, bool VEC>
+// alpha = sum_i min(p'_i, q'_i) over dense rows (fp32 terms, fp64 sums), from
+// precomputed row statistics: the route for rows too long for the one-pass
+// kernel (alpha.hip) or not 16-byte aligned, hence element loads.
+template <int DT>
 __global__ __launch_bounds__(256) void alpha_dense_kernel(AlphaArgs a) {
     __shared__ double red[4];
     __shared__ uint32_t fred[4];
@@ -206,8 +208,8 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t s) {
 
 hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s) {
     const int R = a.B * a.K;
-    if (a.dtype == 1) hipLaunchKernelGGL((alpha_dense_kernel<1, false>), dim3(R), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((alpha_dense_kernel<0, false>), dim3(R), dim3(256), 0, s, a);
+    if (a.dtype == 1) hipLaunchKernelGGL(alpha_dense_kernel<1>, dim3(R), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(alpha_dense_kernel<0>, dim3(R), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

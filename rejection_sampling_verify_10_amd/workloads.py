@@ -418,12 +418,13 @@ CONFIG_NAMES = {
     5: "tree-sample B=32 N=27 V=32000 bf16 T=1",
     6: "eagle2-expand B=64 E=10 V=128256 top_k=10 k_next=10",
     7: "kv-commit B=64 planes=64 row=2KiB N=27",
+    8: "accept-rate B=512 K=8 V=128256 bf16 T=1 (the inputs of workload 4)",
 }
 
 
 def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int] = None,
            V: Optional[int] = None, threads: Optional[int] = None):
-    """Inputs for workload ``cid`` (0..7), optionally with smaller B/K/V (K: expanded nodes for 6)."""
+    """Inputs for workload ``cid`` (0..8), optionally with smaller B/K/V (K: expanded nodes for 6)."""
     if cid == 0:
         return make_chain(B or 1, K or 4, V or 1000, dtype=DTYPE_F32, temperature=1.0, top_k=0,
                           sigma=sigma_const(0.5), config_id=0, seed=seed, threads=threads)
@@ -436,7 +437,7 @@ def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int]
     if cid == 3:
         return make_tree(B or 32, V or 32000, dtype=DTYPE_BF16, sigma=0.5, config_id=3, seed=seed,
                          threads=threads)
-    if cid == 4:
+    if cid in (4, 8):
         return make_chain(B or 512, K or 8, V or 128256, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
                           sigma=sigma_uniform(0.2, 1.5), config_id=4, seed=seed, threads=threads)
     if cid == 5:

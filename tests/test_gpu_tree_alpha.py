@@ -121,3 +121,30 @@ def test_mean_accept_len_matches_alpha_products(R, orc):
     alen = alen.cpu().numpy()
     expect = np.sum(np.cumprod(alpha.cpu().numpy()[0].astype(np.float64)))
     assert abs(alen.mean() - expect) <= 4 * alen.std() / np.sqrt(n)
+
+
+@pytest.mark.parametrize("V,dtype", [(4096, 1), (4096, 0), (65536, 0), (65540, 0), (131072, 1), (131080, 1),
+                                     (1000, 0)])
+@pytest.mark.parametrize("T", [1.0, 0.6])
+def test_accept_rate_one_pass_limits_and_errors(R, orc, V, dtype, T):
+    """The one-pass kernel (a whole logit row in registers: up to 65536 fp32 or 131072 bf16
+    logits) at and just past its limits (the longer rows take the two-kernel route), with
+    unusable rows planted: NaN, +inf and all -inf logits, a NaN or negative draft entry, and
+    (T != 1) an all-zero draft row."""
+    ci = W.make_chain(6, 2, V, dtype=dtype, temperature=T, top_k=0, sigma=W.sigma_const(0.5),
+                      config_id=95, seed=V % 997)
+    z = ci.logits.copy()
+    q = ci.draft_probs.copy()
+    nan_bits = 0x7FC0 if dtype == W.DTYPE_BF16 else np.float32(np.nan)
+    inf_bits = 0x7F80 if dtype == W.DTYPE_BF16 else np.float32(np.inf)
+    ninf_bits = 0xFF80 if dtype == W.DTYPE_BF16 else np.float32(-np.inf)
+    z[0, 0, V - 1] = nan_bits
+    z[1, 1, 7] = inf_bits
+    z[2, 0, :] = ninf_bits
+    q[3, 1, V // 2] = np.nan
+    q[4, 0, 3] = -0.5
+    q[5, 1, :] = 0.0
+    ci = dataclasses.replace(ci, logits=z, draft_probs=q)
+    a = run_alpha(R, orc, ci, f"alpha one-pass V={V} dtype={dtype} T={T}")
+    assert np.isnan(a[0, 0]) and np.isnan(a[1, 1]) and np.isnan(a[2, 0]) and np.isnan(a[3, 1]) and np.isnan(a[4, 0])
+    assert np.isfinite(a[0, 1]) and np.isfinite(a[5, 0])
