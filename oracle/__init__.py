@@ -26,6 +26,7 @@ _lib: Optional[ctypes.CDLL] = None
 
 F32 = 0
 BF16 = 1
+F64 = 2      # fp64 logit rows (the logits lm_head_logits forms)
 
 
 def build(force: bool = True) -> str:
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
         LL = ctypes.c_longlong
         L.oracle_kv_commit.argtypes = [P, I, LL, I, LL, LL, I, I, P, P, I, I, P, P]
         L.oracle_target_dist.argtypes = [P, I, I, D, I, P]
+        L.oracle_lm_head_logits.argtypes = [P, P, I, I, I, P]
         L.oracle_draft_dist.argtypes = [P, I, D, I, P]
         L.oracle_argmax_row.argtypes = [P, I, I]
         L.oracle_set_variant.argtypes = [I]
@@ -68,7 +70,7 @@ def lib() -> ctypes.CDLL:
         for f in ("oracle_verify_chain", "oracle_verify_chain_p", "oracle_target_dist_p", "oracle_draft_dist_p",
                   "oracle_verify_tree_greedy", "oracle_accept_rate",
                   "oracle_verify_tree_sample", "oracle_tree_expand", "oracle_tree_rerank", "oracle_kv_commit",
-                  "oracle_target_dist", "oracle_draft_dist", "oracle_argmax_row",
+                  "oracle_target_dist", "oracle_draft_dist", "oracle_argmax_row", "oracle_lm_head_logits",
                   "oracle_max_threads"):
             getattr(L, f).restype = I
         L.oracle_set_variant.restype = None
@@ -82,7 +84,7 @@ def _p(a: np.ndarray) -> int:
 
 
 def _logits_arr(logits: np.ndarray, dtype: int) -> np.ndarray:
-    want = np.uint16 if dtype == BF16 else np.float32
+    want = np.uint16 if dtype == BF16 else np.float64 if dtype == F64 else np.float32
     return np.ascontiguousarray(logits, dtype=want)
 
 
@@ -214,6 +216,21 @@ def kv_commit(kv, prefix, path, N, accept_len, capacity=None):
     if rc != 0:
         raise ValueError(f"oracle_kv_commit rejected its arguments ({rc})")
     return out, nl
+
+
+def lm_head_logits(hidden_bits, weight_bits) -> np.ndarray:
+    """fp64 logits hidden @ W^T of bf16 hidden states [..., H] and head weights [V, H] (raw
+    bits, uint16); shape [..., V]."""
+    h = np.ascontiguousarray(hidden_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(weight_bits, dtype=np.uint16)
+    H = h.shape[-1]
+    V = w.shape[0]
+    assert w.shape[1] == H
+    R = h.size // H
+    z = np.empty((R, V))
+    if lib().oracle_lm_head_logits(_p(h), _p(w), R, V, H, _p(z)) != 0:
+        raise ValueError("oracle_lm_head_logits rejected its arguments")
+    return z.reshape(h.shape[:-1] + (V,))
 
 
 def accept_rate(logits, dtype, draft_probs, temperature, top_k):

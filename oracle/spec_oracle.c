@@ -65,6 +65,7 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2      /* fp64 logit rows, e.g. the logits oracle_lm_head_logits forms */
 
 /* Deliberate-mistake switch used only by the tests that show the pins bite:
  * 0 = the method as stated; 1 = on rejection re-sample from p instead of the
@@ -93,7 +94,10 @@ int oracle_max_threads(void) {
 #endif
 }
 
+static size_t logit_size(int dtype) { return dtype == ORC_BF16 ? 2 : dtype == ORC_F64 ? 8 : 4; }
+
 static double load_logit(const void* row, int dtype, int i) {
+    if (dtype == ORC_F64) return ((const double*)row)[i];
     if (dtype == ORC_BF16) {
         uint32_t bits = ((uint32_t)((const uint16_t*)row)[i]) << 16;
         float f;
@@ -237,6 +241,27 @@ int oracle_draft_dist_p(const float* q, int V, double T, int top_k, double top_p
     return bad;
 }
 
+/* Logits of an LM head with no bias: z[r][v] = sum_h hidden[r][h] * W[v][h], both
+ * operands bfloat16 (raw bits), every product exact in fp64 and the sum taken in
+ * fp64 in index order.  This is the target pass that yields the distributions
+ * p[1..gamma+1] the verification consumes ("064 · 投机解码", section 三), done
+ * here so that the verification can be checked from hidden states and head
+ * weights.  hidden [R][H], W [V][H] row-major, z [R][V]. */
+int oracle_lm_head_logits(const uint16_t* hidden, const uint16_t* W, int R, int V, int H, double* z) {
+    if (R <= 0 || V <= 0 || H <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < R; ++r) {
+        const uint16_t* hr = hidden + (size_t)r * H;
+        for (int v = 0; v < V; ++v) {
+            const uint16_t* wv = W + (size_t)v * H;
+            double s = 0.0;
+            for (int h = 0; h < H; ++h) s += load_logit(hr, ORC_BF16, h) * load_logit(wv, ORC_BF16, h);
+            z[(size_t)r * V + v] = s;
+        }
+    }
+    return 0;
+}
+
 /* Inverse-CDF draw over r[0..V) with total S (index-ascending). */
 static int draw_index(const double* r, int V, double S, double u, double* margin) {
     double t = u * S, c = 0.0, prev = 0.0;
@@ -289,7 +314,7 @@ int oracle_verify_chain_p(const void* logits, int dtype, const float* q, const i
                           int32_t* tokens, int32_t* accept_len, double* pk, double* qk,
                           double* S_out, double* py_out, double* m_test, double* m_draw) {
     if (B <= 0 || K <= 0 || V <= 0 || !(T >= 0.0) || isinf(T) || !(top_p > 0.0)) return -1;
-    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    const size_t esz = logit_size(dtype);
     const int greedy = (T == 0.0);
     const int transformed = !(T == 1.0 && !topk_enabled(top_k, V) && !(top_p < 1.0));
 #pragma omp parallel for schedule(dynamic, 1)
@@ -426,7 +451,7 @@ int oracle_verify_tree_greedy(const void* logits, int dtype, const int32_t* node
         depth[n] = depth[parents[n]] + 1;
         if (depth[n] > D) D = depth[n];
     }
-    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    const size_t esz = logit_size(dtype);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
         const char* zb = (const char*)logits + (size_t)b * N * V * esz;
@@ -472,7 +497,7 @@ int oracle_verify_tree_greedy(const void* logits, int dtype, const int32_t* node
 int oracle_accept_rate(const void* logits, int dtype, const float* q, int B, int K, int V,
                        double T, int top_k, double* alpha) {
     if (B <= 0 || K <= 0 || V <= 0 || !(T >= 0.0) || isinf(T)) return -1;
-    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    const size_t esz = logit_size(dtype);
 #pragma omp parallel for schedule(dynamic, 1) collapse(2)
     for (int b = 0; b < B; ++b) {
         for (int k = 0; k < K; ++k) {
@@ -545,7 +570,7 @@ int oracle_verify_tree_sample(const void* logits, int dtype, const float* q, con
         depth[n] = depth[parents[n]] + 1;
         if (depth[n] > D) D = depth[n];
     }
-    const size_t esz = dtype == ORC_BF16 ? 2 : 4;
+    const size_t esz = logit_size(dtype);
     const int transformed = !(T == 1.0 && !topk_enabled(top_k, V));
 #pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {

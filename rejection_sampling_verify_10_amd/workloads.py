@@ -407,6 +407,77 @@ def make_kv_commit(B: int, *, planes: int, row: int, parents: np.ndarray = EAGLE
     return KVCommitInputs(B, planes, S, row, N, kv, prefix, path, alen)
 
 
+@dataclasses.dataclass
+class LMHeadInputs:
+    """A chain verification fed by hidden states and LM-head weights instead of logits."""
+    B: int
+    K: int
+    V: int
+    H: int
+    temperature: float
+    top_k: int
+    hidden: np.ndarray         # [B, K+1, H] uint16 (bf16 bits): last hidden states of the target
+    weight: np.ndarray         # [V, H] uint16 (bf16 bits): the LM head (no bias)
+    draft_probs: np.ndarray    # [B, K, V] float32
+    draft_tokens: np.ndarray   # [B, K] int32
+    uniforms: np.ndarray       # [B, K+1] float32
+
+
+def make_lm_head(B: int, K: int, V: int, H: int, *, temperature: float, top_k: int, sigma: SigmaSpec,
+                 config_id: int, seed: int, threads: Optional[int] = None) -> LMHeadInputs:
+    """Hidden states and head weights whose logits follow the chain recipe in shape.
+
+    The head is drawn once per (config, seed): a permutation ``rank`` of 1..V, and row v of
+    W = [g_v * 3/sqrt(H-1), -1.1*ln(rank_v)] with g_v ~ N(0, I) in H-1 dimensions; hidden
+    states are [n, 1] with n ~ N(0, I), so that a logit is 3*N(0,1) - 1.1*ln(rank) as in
+    step 2 of the chain recipe (the Zipf-like prior is the model's, shared by every row).
+    Both are stored as bfloat16.  The draft sees the target's logits (float32 products of
+    the rounded operands, in numpy) through noise as in step 3; its tokens and the
+    verification uniforms follow steps 5 and 6."""
+    rng0 = np.random.default_rng([config_id, seed, 1 << 30])
+    rank = rng0.permutation(V) + 1
+    bias = (-1.1 * np.log(rank.astype(np.float64))).astype(np.float32)
+    weight = np.empty((V, H), dtype=np.uint16)
+    rows = 8192
+    scale = np.float32(3.0 / math.sqrt(H - 1))
+
+    def wchunk(c: int) -> None:
+        r = np.random.default_rng([config_id, seed, 1 << 30, c])
+        v0, v1 = c * rows, min(V, (c + 1) * rows)
+        g = r.standard_normal((v1 - v0, H - 1), dtype=np.float32) * scale
+        weight[v0:v1, :H - 1] = f32_to_bf16_bits(g)
+        weight[v0:v1, H - 1] = f32_to_bf16_bits(bias[v0:v1])
+
+    with ThreadPoolExecutor(threads or _workers()) as ex:
+        list(ex.map(wchunk, range((V + rows - 1) // rows)))
+    hidden = np.empty((B, K + 1, H), dtype=np.uint16)
+    q = np.empty((B, K, V), dtype=np.float32)
+    x = np.empty((B, K), dtype=np.int32)
+    u = np.empty((B, K + 1), dtype=np.float32)
+    wf = bf16_bits_to_f32(weight)
+
+    def one(b: int) -> None:
+        rng = np.random.default_rng([config_id, seed, b])
+        h = np.ones((K + 1, H), dtype=np.float32)
+        h[:, :H - 1] = rng.standard_normal((K + 1, H - 1), dtype=np.float32)
+        hb = f32_to_bf16_bits(h)
+        hidden[b] = hb
+        z = bf16_bits_to_f32(hb)[:K] @ wf.T
+        nd = rng.standard_normal((K, V), dtype=np.float32)
+        s = sigma(rng, b, B)
+        zd = z.astype(np.float64) + s * nd.astype(np.float64)
+        q[b] = _softmax64(zd).astype(np.float32)
+        ud = rng.random(K)
+        for k in range(K):
+            cdf = _draft_sampler_cdf(zd[k], temperature, top_k)
+            x[b, k] = min(int(np.searchsorted(cdf, ud[k] * cdf[-1], side="right")), V - 1)
+        u[b] = rng.random(K + 1, dtype=np.float32)
+
+    with ThreadPoolExecutor(threads or _workers()) as ex:
+        list(ex.map(one, range(B)))
+    return LMHeadInputs(B, K, V, H, float(temperature), int(top_k), hidden, weight, q, x, u)
+
+
 # The workloads, by index.  Each entry builds inputs for a seed, with
 # optional size overrides used by the smaller parity cases.
 CONFIG_NAMES = {
@@ -419,12 +490,13 @@ CONFIG_NAMES = {
     6: "eagle2-expand B=64 E=10 V=128256 top_k=10 k_next=10",
     7: "kv-commit B=64 planes=64 row=2KiB N=27",
     8: "accept-rate B=512 K=8 V=128256 bf16 T=1 (the inputs of workload 4)",
+    9: "lm-head-fused chain B=64 K=7 V=128256 H=4096 bf16 T=0.7 top_k=50",
 }
 
 
 def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int] = None,
            V: Optional[int] = None, threads: Optional[int] = None):
-    """Inputs for workload ``cid`` (0..8), optionally with smaller B/K/V (K: expanded nodes for 6)."""
+    """Inputs for workload ``cid`` (0..9), optionally with smaller B/K/V (K: expanded nodes for 6)."""
     if cid == 0:
         return make_chain(B or 1, K or 4, V or 1000, dtype=DTYPE_F32, temperature=1.0, top_k=0,
                           sigma=sigma_const(0.5), config_id=0, seed=seed, threads=threads)
@@ -443,6 +515,9 @@ def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int]
     if cid == 5:
         return make_tree_sampled(B or 32, V or 32000, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
                                  sigma=0.5, config_id=5, seed=seed, threads=threads)
+    if cid == 9:
+        return make_lm_head(B or 64, K or 7, V or 128256, 4096, temperature=0.7, top_k=50,
+                            sigma=sigma_halves(0.3, 1.0), config_id=9, seed=seed, threads=threads)
     if cid == 7:
         return make_kv_commit(B or 64, planes=64, row=1024, max_prefix=16, config_id=7, seed=seed)
     if cid == 6:
