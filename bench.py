@@ -37,6 +37,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0     # dense bf16 matrix-core peak
 METRIC = "verified token-rows/s and achieved HBM GB/s (% of peak), V=128256, B=64, K=7"
 
 # The default is the headline workload (2); 0, 1 and 3 are the small configurations, bound by
@@ -61,6 +62,10 @@ WORKLOADS = {
     7: dict(name="KV commit of accepted tree paths B=64, 64 planes (32 layers x K/V), 2 KiB rows (8 heads x 128 "
                  "x bf16), 27-node tree, prefix <= 16",
             kernel="kv_commit_kernel", copies=8, oracle_rows=64, dtype="bytes (bf16 rows)"),
+    9: dict(name="LM head fused with chain verify B=64 K=7 V=128256 H=4096, bf16 hidden states and head, fp32 draft "
+                 "probs, T=0.7, top_k=50",
+            kernel="lmhead_tile_kernel", copies=1, oracle_rows=4, bound="mfma",
+            dtype="bf16 MFMA with f32 accumulation, f32 select, f32 probabilities"),
     8: dict(name="acceptance rate B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
             kernel="alpha_row_kernel", copies=1, oracle_rows=32, single_kernel=True,
             dtype="bf16 in, f32 exp and terms, f64 sums"),
@@ -217,6 +222,36 @@ def copy_probe(R, torch, args) -> int:
     return 0
 
 
+def unfused_baseline(R, torch, ci, inputs, T, top_k, args) -> dict:
+    """The same step without the fusion, for context: the library GEMM of torch (F.linear,
+    bf16 logits written to memory), then spec_verify_chain on those logits."""
+    h, w, q, x, u = inputs
+    B, K1, H = h.shape
+    K = K1 - 1
+    dev = h.device
+    tok = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = R.new_workspace(R.chain_workspace_bytes(B, K, w.shape[0], 1, T, top_k), dev)
+    h2 = h.reshape(B * K1, H)
+
+    def one():
+        z = torch.nn.functional.linear(h2, w).reshape(B, K1, -1)
+        R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
+
+    n = max(10, args.steps // 4)
+    for _ in range(5):
+        one()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": a.elapsed_time(b) / n, "steps": n,
+            "what": "torch F.linear (bf16 logits [B, K+1, V] written to HBM) + spec_verify_chain"}
+
+
 def read_probe_gbps(R, torch, dev) -> float:
     """Achievable streaming-read bandwidth: the library's read-only probe over 1 GiB
     (four times the Infinity Cache), 20 launches timed together."""
@@ -273,6 +308,7 @@ def main() -> int:
     sampled_tree = args.workload == 5
     expand = args.workload == 6
     kvc = args.workload == 7
+    fused = args.workload == 9
     log(f"workload {args.workload}: {wl['name']} (inputs drawn in {time.time() - t0:.1f} s)")
 
     def to_dev(a):
@@ -323,6 +359,15 @@ def main() -> int:
         alen = torch.empty((B,), dtype=torch.int32, device=dev)
         parents = ci.parents.tolist()
         rows_per_step = B * K                  # node rows verified
+    elif fused:
+        B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
+        Hd = ci.H
+        base = [to_dev(ci.hidden), to_dev(ci.weight), to_dev(ci.draft_probs), to_dev(ci.draft_tokens),
+                to_dev(ci.uniforms)]
+        tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        ws = R.new_workspace(R.chain_fused_workspace_bytes(B, K, V, Hd, T, top_k), dev)
+        rows_per_step = B * (K + 1)            # token rows verified
     elif arate:
         B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
         base = [to_dev(ci.logits), to_dev(ci.draft_probs)]
@@ -357,6 +402,9 @@ def main() -> int:
         elif arate:
             z, q = sets[i % len(sets)]
             R.accept_rate(z, q, T, top_k, out=alpha_out, workspace=ws)
+        elif fused:
+            h, w, q, x, u = sets[i % len(sets)]
+            R.verify_chain_fused(h, w, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
         else:
             z, q, x, u = sets[i % len(sets)]
             R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
@@ -396,18 +444,33 @@ def main() -> int:
     unit = {3: "node-rows/s", 5: "node-rows/s", 6: "expanded draft rows/s", 7: "committed paths/s",
             8: "row pairs/s"}.get(args.workload, "token-rows/s")
     al = alen.cpu().numpy()
-    alg = algorithmic_bytes(args.workload, B, K, V, top_k, al, esz,
-                            path.cpu().numpy() if sampled_tree else ci.path if kvc else None,
-                            ci.parents if sampled_tree else None)
-    achieved = alg / (k_ms * 1e-3) / 1e9
+    extra = {}
+    if fused:
+        # the dominant kernel is the GEMM: 2*R*V*H flops on the matrix cores; the bytes
+        # every step must read are the head, the hidden states and the draft rows
+        flops = 2.0 * B * (K + 1) * V * Hd
+        alg = V * Hd * 2 + B * (K + 1) * Hd * 2 + B * K * V * 4
+        achieved = flops / (k_ms * 1e-3) / 1e12
+        log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} TFLOP/s "
+            f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of the bf16 peak); accept_len histogram "
+            f"{np.bincount(al[al >= 0], minlength=K + 1).tolist()}")
+        extra["unfused"] = unfused_baseline(R, torch, ci, sets[0], T, top_k, args)
+        log(f"unfused (library GEMM to bf16 logits, then spec_verify_chain): "
+            f"{extra['unfused']['ms_per_step'] * 1e3:.1f} us per step")
+        probe = None
+    else:
+        alg = algorithmic_bytes(args.workload, B, K, V, top_k, al, esz,
+                                path.cpu().numpy() if sampled_tree else ci.path if kvc else None,
+                                ci.parents if sampled_tree else None)
+        achieved = alg / (k_ms * 1e-3) / 1e9
+        log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
+            f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak)"
+            + ("" if (expand or kvc or arate) else "; accept_len histogram "
+               f"{np.bincount(al[al >= 0], minlength=(K + 1) if not (tree or sampled_tree) else 1).tolist()}"))
+        probe = read_probe_gbps(R, torch, dev)
+        log(f"read probe {probe:.0f} GB/s; {wl['kernel']} at {100 * achieved / probe:.1f}% of it")
     step_alg_gbs = alg / (ms_step * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us, {wl['kernel']} {k_ms * 1e3:.1f} us -> {achieved:.0f} GB/s "
-        f"({100 * achieved / PEAK_HBM_GBS:.1f}% of peak)"
-        + ("" if (expand or kvc or arate) else "; accept_len histogram "
-           f"{np.bincount(al[al >= 0], minlength=(K + 1) if not (tree or sampled_tree) else 1).tolist()}"))
     traffic = counter_traffic(args.workload)
-    probe = read_probe_gbps(R, torch, dev)
-    log(f"read probe {probe:.0f} GB/s; {wl['kernel']} at {100 * achieved / probe:.1f}% of it")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -430,6 +493,10 @@ def main() -> int:
                                               ci.node_tokens[:rows], ci.uniforms[:rows], ci.parents, T, top_k)
                 elif arate:
                     oracle.accept_rate(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], T, top_k)
+                elif fused:
+                    z64 = oracle.lm_head_logits(ci.hidden[:rows], ci.weight)
+                    oracle.verify_chain(z64, oracle.F64, ci.draft_probs[:rows], ci.draft_tokens[:rows],
+                                        ci.uniforms[:rows], T, top_k)
                 else:
                     oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
                                         ci.uniforms[:rows], T, top_k)
@@ -481,20 +548,29 @@ def main() -> int:
                    {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
                     "rows": "(target, draft) row pairs", "input_copies": wl["copies"], "parallelism": "single GPU"}
                    if arate else
+                   {"workload": wl["name"], "B": B, "K": K, "V": V, "H": Hd, "temperature": T, "top_k": top_k,
+                    "input_copies": wl["copies"], "parallelism": "single GPU"}
+                   if fused else
                    {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
                     "input_copies": wl["copies"], "parallelism": "single GPU"}),
         "step_algorithmic_GBps": step_alg_gbs,
         "emitted_tokens_per_s": None if arate else float(np.sum(al[al >= 0] + 1)) / (ms_step * 1e-3),
-        "roofline": {"bound": "hbm", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg,
-                     "kernel_timing": "HIP events attached to the kernel's dispatch (hipExtLaunchKernel) on "
-                                      "the call's stream, second pass of the same number of steps"
-                                      + (", capped by the timed pass's step time (the kernel is the whole call)"
-                                         if single_kernel else ""),
-                     "read_probe_GBps": probe, "frac_of_read_probe": achieved / probe},
+        "roofline": ({"bound": "mfma", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                      "kernel_us": k_ms * 1e3, "flops": 2.0 * B * (K + 1) * V * Hd,
+                      "kernel_timing": "HIP events attached to the GEMM kernel's dispatch on the call's stream, "
+                                       "second pass of the same number of steps"} if fused else
+                     {"bound": "hbm", "kernel": wl["kernel"], "achieved": achieved, "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                      "kernel_us": k_ms * 1e3, "algorithmic_bytes": alg,
+                      "kernel_timing": "HIP events attached to the kernel's dispatch (hipExtLaunchKernel) on "
+                                       "the call's stream, second pass of the same number of steps"
+                                       + (", capped by the timed pass's step time (the kernel is the whole call)"
+                                          if single_kernel else ""),
+                      "read_probe_GBps": probe, "frac_of_read_probe": achieved / probe}),
         "cpu_baseline": cpu,
     }
+    line.update(extra)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -229,6 +229,39 @@ int spec_verify_chain_noalloc(const void* target_logits, spec_dtype_t dtype, con
                               float* out_diag, void* hip_stream);
 
 /*
+ * spec_verify_chain_fused -- spec_verify_chain with the target's LM head in
+ * front of it, so that the logits never reach memory ("064 · 投机解码", section
+ * 三: one target pass yields the K+1 distributions the verification consumes;
+ * "Việc giải mã giả định và EAGLE-3": decoding is bound by memory bandwidth).
+ * The logits are z[b][k][v] = sum_h hidden[b][k][h] * head_weight[v][h]
+ * (bfloat16 operands, fp32 accumulation on the matrix cores); the verification
+ * is then exactly spec_verify_chain's on those logits, for the two modes whose
+ * selection runs in the GEMM's epilogue: greedy (temperature == 0) and top-k
+ * (temperature > 0, 0 < top_k < V, top_k <= SPEC_TOPK_MAX).  Without top-k the
+ * residual draw needs whole logit rows: SPEC_EUNSUPPORTED.
+ *
+ *   hidden        [B][K+1][H]  bfloat16 (raw bits)     device, read; 16-byte aligned
+ *   head_weight   [V][H]       bfloat16 (raw bits)     device, read; 16-byte aligned (no bias)
+ *   H             hidden size, a multiple of 16
+ *   draft_probs, draft_tokens, uniforms, temperature, top_k, out_tokens,
+ *   out_accept_len, out_diag: as for spec_verify_chain (the logit rows are the
+ *   fp32 logits above; a NaN logit makes its row unusable, E1).
+ *   workspace     spec_chain_fused_workspace_bytes(B, K, V, H, temperature, top_k)
+ *                 bytes, 256-byte aligned, zero-filled before its first use; a
+ *                 top-k call leaves its hand-over words zero, as a top-k chain does,
+ *                 and a greedy call leaves scratch behind (zero the workspace before
+ *                 a top-k call that follows one on it).
+ * Precision: the verification is exact on the fp32 logits the matrix cores
+ * produce; they differ from exact logits by the rounding of fp32 accumulation
+ * over H/16 steps (a few 1e-6 at |z| ~ 20, H = 4096).
+ */
+size_t spec_chain_fused_workspace_bytes(int B, int K, int V, int H, float temperature, int top_k);
+int spec_verify_chain_fused(const void* hidden, const void* head_weight, const float* draft_probs,
+                            const int32_t* draft_tokens, const float* uniforms, int B, int K, int V, int H,
+                            float temperature, int top_k, int32_t* out_tokens, int32_t* out_accept_len,
+                            float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * spec_verify_tree_greedy -- greedy verification of a static draft tree.
  * "EAGLE-2: Faster Inference of Language Models with Dynamic Draft Trees",
  * section 2.2 (every branch of the draft tree verified in one target pass, the

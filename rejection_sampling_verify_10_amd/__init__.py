@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.spec_accept_rate_workspace_bytes.restype = Z
         L.spec_verify_chain.argtypes = [P, I, P, P, P, I, I, I, F, I, P, P, P, P, Z, P]
         L.spec_verify_chain.restype = I
+        L.spec_chain_fused_workspace_bytes.argtypes = [I, I, I, I, F, I]
+        L.spec_chain_fused_workspace_bytes.restype = Z
+        L.spec_verify_chain_fused.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, P, P, Z, P]
+        L.spec_verify_chain_fused.restype = I
         L.spec_verify_chain_noalloc.argtypes = [P, I, P, P, P, I, I, I, F, I, P, P, P, P]
         L.spec_verify_chain_noalloc.restype = I
         L.spec_verify_chain_topp.argtypes = [P, I, P, P, P, I, I, I, F, I, F, P, P, P, P, Z, P]
@@ -207,6 +211,57 @@ def verify_chain(target_logits: torch.Tensor, draft_probs: Optional[torch.Tensor
                                      tokens.data_ptr(), alen.data_ptr(), dg.data_ptr() if dg is not None else None,
                                      wp, need, _stream(dev))
         _check(rc, "spec_verify_chain")
+    return (tokens, alen, dg) if diag else (tokens, alen)
+
+
+def chain_fused_workspace_bytes(B: int, K: int, V: int, H: int, temperature: float, top_k: int) -> int:
+    return int(lib().spec_chain_fused_workspace_bytes(B, K, V, H, float(temperature), int(top_k)))
+
+
+def verify_chain_fused(hidden: torch.Tensor, head_weight: torch.Tensor, draft_probs: Optional[torch.Tensor],
+                       draft_tokens: torch.Tensor, uniforms: Optional[torch.Tensor], temperature: float = 1.0,
+                       top_k: int = 0, *, diag: bool = False, out: Optional[Tuple[torch.Tensor, ...]] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """``spec_verify_chain_fused``: the chain verification fed by the target's last hidden
+    states and LM head instead of logits (the logits stay on the chip).
+
+    hidden [B, K+1, H] bf16, head_weight [V, H] bf16, draft_probs [B, K, V] f32,
+    draft_tokens [B, K] int32, uniforms [B, K+1] f32; greedy (temperature 0) or top-k.
+    Returns what :func:`verify_chain` returns."""
+    B, K1, H = hidden.shape
+    K = K1 - 1
+    V = head_weight.shape[0]
+    dev = hidden.device
+    if hidden.dtype != torch.bfloat16 or head_weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and head_weight must be bfloat16")
+    _shape(head_weight, "head_weight", (V, H))
+    _shape(draft_probs, "draft_probs", (B, K, V))
+    _shape(draft_tokens, "draft_tokens", (B, K))
+    _shape(uniforms, "uniforms", (B, K + 1))
+    if float(temperature) != 0.0 and (draft_probs is None or uniforms is None):
+        raise ValueError("sampling verification needs draft_probs and uniforms")
+    if out is None:
+        tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        alen = torch.empty((B,), dtype=torch.int32, device=dev)
+        dg = torch.empty((B, 2 * K + 2), dtype=torch.float32, device=dev) if diag else None
+    else:
+        tokens, alen = out[0], out[1]
+        dg = out[2] if diag else None
+        _shape(tokens, "out tokens", (B, K + 1))
+        _shape(alen, "out accept_len", (B,))
+        if diag:
+            _shape(dg, "out diag", (B, 2 * K + 2))
+    need = chain_fused_workspace_bytes(B, K, V, H, temperature, top_k)
+    wp, ws = _workspace(need, dev, workspace)
+    rc = lib().spec_verify_chain_fused(
+        _dev(hidden, "hidden"), _dev(head_weight, "head_weight"),
+        _dev(draft_probs, "draft_probs", torch.float32) if draft_probs is not None else None,
+        _dev(draft_tokens, "draft_tokens", torch.int32),
+        _dev(uniforms, "uniforms", torch.float32) if uniforms is not None else None,
+        B, K, V, H, float(temperature), int(top_k), _dev(tokens, "out tokens", torch.int32),
+        _dev(alen, "out accept_len", torch.int32), _dev(dg, "out diag", torch.float32) if dg is not None else None,
+        wp, need, _stream(dev))
+    _check(rc, "spec_verify_chain_fused")
     return (tokens, alen, dg) if diag else (tokens, alen)
 
 

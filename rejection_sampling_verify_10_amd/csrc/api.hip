@@ -222,6 +222,41 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
     return p;
 }
 
+// The fused LM-head chain: per-unit candidates, then the top-k chain's lists
+// with the target rows pre-listed (one list per row) or the greedy statistics.
+struct FusedPlan {
+    bool greedy;
+    unsigned long long* cand;
+    uint32_t* cflag;
+    RowStats st;
+    TopkLists tk;
+    unsigned long long* recw;
+};
+
+FusedPlan plan_fused(Carver& c, int B, int K, int V, float T, int top_k) {
+    FusedPlan p{};
+    const size_t R = static_cast<size_t>(B) * (K + 1);
+    const size_t units = static_cast<size_t>(lmhead_units(V));
+    p.greedy = T == 0.f;
+    p.cand = c.take<unsigned long long>(R * units * (p.greedy ? 1 : 4));
+    p.cflag = c.take<uint32_t>(R * units);
+    if (p.greedy) {
+        p.st = carve_rowstats(c, R);
+    } else {
+        p.tk.Ct = 1;                   // the target row's list, written by the merge
+        p.tk.chunk_t = V;
+        topk_chunking(V, 4, &p.tk.Cd, &p.tk.chunk_d);
+        p.tk.Ub = static_cast<long>(K + 1) * p.tk.Ct + static_cast<long>(K) * p.tk.Cd;
+        p.tk.words = c.take<unsigned long long>(static_cast<size_t>(B) * p.tk.Ub * kTopkMax);
+        p.tk.top_k = top_k;
+        p.tk.top_p = 1.f;
+        p.tk.draft_identity = (T == 1.f) ? 1 : 0;
+        p.tk.invT = 1.0 / static_cast<double>(T);
+        p.recw = c.take<unsigned long long>(R * kRecWords);
+    }
+    return p;
+}
+
 struct AlphaPlan {
     int mode;   // 0 dense, 1 top-k, 2 greedy
     RowStats st, qst;
@@ -506,6 +541,89 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
         ca.qsum = p.qsum;
         ca.qflags = p.qflags;
         SV_TRY(launch_chain_dense(ca, dense_bracket(true), s));
+    }
+    return SPEC_OK;
+}
+
+size_t spec_chain_fused_workspace_bytes(int B, int K, int V, int H, float temperature, int top_k) {
+    if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V || H < 16 || H % 16 != 0) return 0;
+    if (!(temperature >= 0.f) || isinf(temperature)) return 0;
+    if (temperature != 0.f && !(topk_active(top_k, V) && top_k <= SPEC_TOPK_MAX)) return 0;
+    Carver c(nullptr);
+    plan_fused(c, B, K, V, temperature, top_k);
+    return (c.off + 255) & ~static_cast<size_t>(255);
+}
+
+int spec_verify_chain_fused(const void* hidden, const void* head_weight, const float* draft_probs,
+                            const int32_t* draft_tokens, const float* uniforms, int B, int K, int V, int H,
+                            float temperature, int top_k, int32_t* out_tokens, int32_t* out_accept_len,
+                            float* out_diag, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!hidden || !head_weight || !draft_tokens || !out_tokens || !out_accept_len) return SPEC_EINVAL;
+    if (B < 1 || K < 1 || V < 1 || H < 1 || !(temperature >= 0.f) || isinf(temperature)) return SPEC_EINVAL;
+    const bool greedy = temperature == 0.f;
+    if (!greedy && (!draft_probs || !uniforms)) return SPEC_EINVAL;
+    if (K > SPEC_MAX_K || V > SPEC_MAX_V || H % 16 != 0) return SPEC_EUNSUPPORTED;
+    if (static_cast<long>(B) * (K + 1) > (1L << 24)) return SPEC_EUNSUPPORTED;
+    // the fused call serves the modes whose selection fits in the GEMM's epilogue:
+    // greedy and top-k; the dense draw needs whole logit rows
+    if (!greedy && !(topk_active(top_k, V) && top_k <= SPEC_TOPK_MAX)) return SPEC_EUNSUPPORTED;
+    if (!greedy && !topk_shape_ok(SPEC_F32, V)) return SPEC_EUNSUPPORTED;
+    if (!aligned(hidden, 16) || !aligned(head_weight, 16) || !aligned(draft_tokens, 4) || !aligned(out_tokens, 4) ||
+        !aligned(out_accept_len, 4) || (draft_probs && !aligned(draft_probs, 4)) || (uniforms && !aligned(uniforms, 4)) ||
+        (out_diag && !aligned(out_diag, 4)))
+        return SPEC_EINVAL;
+    const size_t need = spec_chain_fused_workspace_bytes(B, K, V, H, temperature, top_k);
+    int rc = check_workspace(workspace, workspace_bytes, need);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    ProfileScope prof;
+    Carver c(workspace);
+    FusedPlan p = plan_fused(c, B, K, V, temperature, top_k);
+
+    LMHeadArgs la{};
+    la.hidden = static_cast<const uint16_t*>(hidden);
+    la.weight = static_cast<const uint16_t*>(head_weight);
+    la.R = B * (K + 1);
+    la.V = V;
+    la.H = H;
+    la.K = K;
+    la.units = lmhead_units(V);
+    la.top_k = greedy ? 1 : top_k;
+    la.cand = p.cand;
+    la.cflag = p.cflag;
+
+    ChainArgs ca{};
+    ca.logits = nullptr;
+    ca.dtype = SPEC_F32;
+    ca.q = draft_probs;
+    ca.x = draft_tokens;
+    ca.u = uniforms;
+    ca.B = B;
+    ca.K = K;
+    ca.V = V;
+    ca.T = temperature;
+    ca.invT = greedy ? 0.0 : 1.0 / static_cast<double>(temperature);
+    ca.out_tokens = out_tokens;
+    ca.out_accept_len = out_accept_len;
+    ca.out_diag = out_diag;
+    if (greedy) {
+        la.greedy_arg = p.st.arg;
+        la.greedy_flags = p.st.flags;
+        SV_TRY(launch_lmhead(la, s, prof.timing()));
+        ca.st = p.st;
+        SV_TRY(launch_chain_greedy(ca, s));
+    } else {
+        p.tk.tag = g_chain_calls.fetch_add(1, std::memory_order_relaxed) + 1u;
+        p.tk.spin_limit = spin_limit();
+        la.words = p.tk.words;
+        la.tk = p.tk;
+        SV_TRY(launch_lmhead(la, s, prof.timing()));
+        ca.tk = p.tk;
+        ca.recw = p.recw;
+        TopkChainArgs fa{};
+        fa.sel = topk_chunk_args(nullptr, draft_probs, SPEC_F32, B, K, V, K + 1, p.tk);
+        fa.ch = ca;
+        SV_TRY(launch_chain_topk(fa, s));
     }
     return SPEC_OK;
 }

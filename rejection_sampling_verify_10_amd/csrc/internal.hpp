@@ -116,6 +116,25 @@ struct TopkChainArgs {
 };
 
 
+// LM head fused with the selection (lmhead.hip): logits = hidden @ W^T never
+// leave the GEMM's registers; per (row, unit of 128 columns) the epilogue keeps
+// candidates, and a merge writes each row's exact top-k as one list into the
+// hand-over words of a top-k chain launch (targets pre-listed: Ct = 1), or its
+// argmax for the greedy chain.
+struct LMHeadArgs {
+    const uint16_t* hidden;     // [R][H] bf16 bits, R = B*(K+1)
+    const uint16_t* weight;     // [V][H] bf16 bits
+    int R, V, H, K;
+    int units;                  // ceil(V / 128)
+    int top_k;
+    unsigned long long* cand;   // [R][units][4] keys (top-k) or [R][units] (greedy)
+    uint32_t* cflag;            // [R][units]: a NaN logit in the unit
+    int32_t* greedy_arg;        // greedy: [R] argmax, else null
+    uint32_t* greedy_flags;     // greedy: [R]
+    unsigned long long* words;  // top-k: the chain's list words
+    TopkLists tk;               // top-k: the chain's unit layout and tag
+};
+
 struct TreeArgs {
     const int32_t* node_tokens;
     int B, N, V, D;             // per-row trees: D = N - 1 (the output stride is N)
@@ -228,6 +247,8 @@ hipError_t launch_alpha_dense(const AlphaArgs& a, hipStream_t s);
 bool alpha_rows_fit(const AlphaArgs& a);
 hipError_t launch_alpha_rows(const AlphaArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_alpha_greedy(const AlphaArgs& a, hipStream_t s);
+hipError_t launch_lmhead(const LMHeadArgs& a, hipStream_t s, Timing t = {});   // tiles + merge
+int lmhead_units(int V);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_read_probe(const void* src, size_t bytes, void* sink, hipStream_t s);
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);

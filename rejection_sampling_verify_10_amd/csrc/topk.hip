@@ -359,6 +359,9 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkChainArgs f
     int32_t* oi = t.idx + unit * kTopkMax;
     u32x4 d[kSlots];
     if (within < t.Ct) {
+        // no target logits: the target rows' lists were written before the launch
+        // (the LM-head fusion), only the draft rows are selected here
+        if (a.target == nullptr) return;
         const char* row = static_cast<const char*>(a.target) + (static_cast<long>(b) * (a.K + 1) + k) * a.V * Elem<DT>::kBytes;
         const long start = static_cast<long>(within) * t.chunk_t;
         const int len = static_cast<int>(min(static_cast<long>(t.chunk_t), a.V - start));
