@@ -8,9 +8,11 @@
 // GEMM: C[r][v] = sum_h A[r][h] * W[v][h], A = hidden states [R][H], W = head
 // [V][H], both bfloat16 and contiguous along h, fp32 accumulation with the
 // gfx950 v_mfma_f32_32x32x16_bf16 instruction.  A lane's operand fragment is 8
-// consecutive h of one row (16 bytes), so every fragment is one 16-byte load
-// straight from memory (L2 serves the reuse).  A workgroup of 4 waves computes
-// a 128 x 256 tile; each wave a 64 x 128 sub-tile, 2 x 4 blocks of 32 x 32.  The
+// consecutive h of one row (16 bytes).  A workgroup of 4 waves computes a 128 x
+// 256 tile; each wave a 64 x 128 sub-tile, 2 x 4 blocks of 32 x 32.  The
+// workgroup stages 32 h of its 128 hidden rows and 256 head rows at a time in
+// LDS (double-buffered, the next step's global loads in flight during this
+// step's 16 MFMAs per wave), and every wave reads its fragments from there.  The
 // M tiles that share one N tile of W are dispatched back to back on the same
 // XCD, so that they read that slice of W through one L2.  Every 32 x 32 block
 // accumulates k = 0, 16, 32, ... in order from zero, and a row's results do not
@@ -121,26 +123,102 @@ __device__ __forceinline__ TileId tile_of(int block, int mtiles) {
     return t;
 }
 
+// The workgroup's operands per step of 32 h: rows of 32 bf16 (64 bytes, 4
+// chunks of 16) padded to 80 bytes, so that consecutive rows of a fragment read
+// start 20 banks apart and 16 of them hit 16 different groups of 4 banks.
+constexpr int kKS = 32;                          // h per staged step (two MFMA steps)
+constexpr int kRowC = 5;                         // 16-byte chunks per staged row (4 + 1 of padding)
+struct GemmStage {
+    u32x4 a[2][kTileM * kRowC];                  // double-buffered hidden-state rows
+    u32x4 b[2][kTileN * kRowC];                  // double-buffered head rows
+};
+union TileSmem {
+    GemmStage g;
+    float stage[4][32 * kLdsStride];             // the epilogue's per-wave slabs
+};
+
 template <bool GREEDY>
 __global__ __launch_bounds__(kLmThreads, 2) void lmhead_tile_kernel(LMHeadArgs a) {
-    __shared__ float stage[4][32 * kLdsStride];
+    __shared__ TileSmem sm;
     const int mtiles = (a.R + kTileM - 1) / kTileM;
     const TileId t = tile_of(blockIdx.x, mtiles);
     if (t.n * kTileN >= a.V) return;
-    const int lane = threadIdx.x & (kWave - 1), wid = wave_id();
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wid = wave_id();
     const int wm = wid >> 1, wn = wid & 1;
     const int m0 = t.m * kTileM + wm * 64, n0 = t.n * kTileN + wn * kUnit;
-    int arow[kMB], wrow[kNB];
+    const int H = a.H;
+
+    // global -> LDS copy of one step: 16-byte chunks, A 2 per thread, B 4 per thread
+    const uint16_t* ga[2];
+    const uint16_t* gb[4];
+    int la[2], lb[4];
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) arow[i] = min(m0 + 32 * i + (lane & 31), a.R - 1);
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * kLmThreads, row = c >> 2, part = c & 3;
+        ga[i] = a.hidden + static_cast<long>(min(t.m * kTileM + row, a.R - 1)) * H + part * 8;
+        la[i] = row * kRowC + part;
+    }
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) wrow[j] = min(n0 + 32 * j + (lane & 31), a.V - 1);
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + i * kLmThreads, row = c >> 2, part = c & 3;
+        gb[i] = a.weight + static_cast<long>(min(t.n * kTileN + row, a.V - 1)) * H + part * 8;
+        lb[i] = row * kRowC + part;
+    }
+    u32x4 ra[2], rb[4];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + k0);
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sm.g.a[buf][la[i]] = ra[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.g.b[buf][lb[i]] = rb[i];
+    };
+    // this lane's fragment chunks within a staged step (chunk 2*ks + lane/32 of its row)
+    const int koff = lane >> 5;
+    int fa[kMB], fb[kNB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) fa[i] = (wm * 64 + 32 * i + (lane & 31)) * kRowC + koff;
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) fb[j] = (wn * kUnit + 32 * j + (lane & 31)) * kRowC + koff;
+
     f32x16 acc[kMB][kNB];
-    mma_blocks<kMB, kNB>(a.hidden, a.weight, arow, wrow, a.H, acc);
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) acc[i][j] = f32x16{};
+    const int steps = H / kKS;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int s = 0; s < steps; ++s) {
+        const int cur = s & 1;
+        const bool more = s + 1 < steps;
+        if (more) fetch((s + 1) * kKS);           // next step's operands in flight
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 xa[kMB], xb[kNB];
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) xa[i] = __builtin_bit_cast(bf16x8, sm.g.a[cur][fa[i] + 2 * ks]);
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) xb[j] = __builtin_bit_cast(bf16x8, sm.g.b[cur][fb[j] + 2 * ks]);
+#pragma unroll
+            for (int i = 0; i < kMB; ++i)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) stash(cur ^ 1);
+        __syncthreads();
+    }
 
     // Epilogue: one 32-row block at a time through this wave's LDS slab; lane l
     // then scans half of row l % 32 (64 columns) and the two halves combine.
-    float* slab = stage[wid];
+    float* slab = sm.stage[wid];
     const int unit = n0 / kUnit;
     const int rr = lane & 31, half = lane >> 5;
 #pragma unroll
