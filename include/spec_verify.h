@@ -242,7 +242,7 @@ int spec_verify_chain_noalloc(const void* target_logits, spec_dtype_t dtype, con
  *
  *   hidden        [B][K+1][H]  bfloat16 (raw bits)     device, read; 16-byte aligned
  *   head_weight   [V][H]       bfloat16 (raw bits)     device, read; 16-byte aligned (no bias)
- *   H             hidden size, a multiple of 32
+ *   H             hidden size, a multiple of 64 (V*H and B*(K+1)*H below 2^31)
  *   draft_probs, draft_tokens, uniforms, temperature, top_k, out_tokens,
  *   out_accept_len, out_diag: as for spec_verify_chain (the logit rows are the
  *   fp32 logits above; a NaN logit makes its row unusable, E1).

@@ -546,7 +546,7 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
 }
 
 size_t spec_chain_fused_workspace_bytes(int B, int K, int V, int H, float temperature, int top_k) {
-    if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V || H < 32 || H % 32 != 0) return 0;
+    if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V || H < 64 || H % 64 != 0) return 0;
     if (!(temperature >= 0.f) || isinf(temperature)) return 0;
     if (temperature != 0.f && !(topk_active(top_k, V) && top_k <= SPEC_TOPK_MAX)) return 0;
     Carver c(nullptr);
@@ -562,7 +562,10 @@ int spec_verify_chain_fused(const void* hidden, const void* head_weight, const f
     if (B < 1 || K < 1 || V < 1 || H < 1 || !(temperature >= 0.f) || isinf(temperature)) return SPEC_EINVAL;
     const bool greedy = temperature == 0.f;
     if (!greedy && (!draft_probs || !uniforms)) return SPEC_EINVAL;
-    if (K > SPEC_MAX_K || V > SPEC_MAX_V || H % 32 != 0) return SPEC_EUNSUPPORTED;
+    if (K > SPEC_MAX_K || V > SPEC_MAX_V || H % 64 != 0) return SPEC_EUNSUPPORTED;
+    // 32-bit element offsets into the head and the hidden states
+    if (static_cast<long>(V) * H >= (1L << 31) || static_cast<long>(B) * (K + 1) * H >= (1L << 31))
+        return SPEC_EUNSUPPORTED;
     if (static_cast<long>(B) * (K + 1) > (1L << 24)) return SPEC_EUNSUPPORTED;
     // the fused call serves the modes whose selection fits in the GEMM's epilogue:
     // greedy and top-k; the dense draw needs whole logit rows

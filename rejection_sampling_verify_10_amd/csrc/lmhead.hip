@@ -10,9 +10,9 @@
 // gfx950 v_mfma_f32_32x32x16_bf16 instruction.  A lane's operand fragment is 8
 // consecutive h of one row (16 bytes).  A workgroup of 4 waves computes a 128 x
 // 256 tile; each wave a 64 x 128 sub-tile, 2 x 4 blocks of 32 x 32.  The
-// workgroup stages 32 h of its 128 hidden rows and 256 head rows at a time in
-// LDS (double-buffered, the next step's global loads in flight during this
-// step's 16 MFMAs per wave), and every wave reads its fragments from there.  The
+// workgroup stages 64 h of its 128 hidden rows and 256 head rows at a time in
+// LDS (the next step's global loads in flight during this step's 32 MFMAs per
+// wave), and every wave reads its fragments from there.  The
 // M tiles that share one N tile of W are dispatched back to back on the same
 // XCD, so that they read that slice of W through one L2.  Every 32 x 32 block
 // accumulates k = 0, 16, 32, ... in order from zero, and a row's results do not
@@ -123,14 +123,15 @@ __device__ __forceinline__ TileId tile_of(int block, int mtiles) {
     return t;
 }
 
-// The workgroup's operands per step of 32 h: rows of 32 bf16 (64 bytes, 4
-// chunks of 16) padded to 80 bytes, so that consecutive rows of a fragment read
-// start 20 banks apart and 16 of them hit 16 different groups of 4 banks.
-constexpr int kKS = 32;                          // h per staged step (two MFMA steps)
-constexpr int kRowC = 5;                         // 16-byte chunks per staged row (4 + 1 of padding)
+// The workgroup's operands per step of 64 h: rows of 64 bf16 (128 bytes, 8
+// chunks of 16) padded to 144 bytes, so that consecutive rows of a fragment
+// read start 36 banks apart and 16 of them hit 16 different groups of 4 banks.
+// One LDS buffer (two workgroups per CU fit); the next step waits in registers.
+constexpr int kKS = 64;                          // h per staged step (four MFMA steps)
+constexpr int kRowC = 9;                         // 16-byte chunks per staged row (8 + 1 of padding)
 struct GemmStage {
-    u32x4 a[2][kTileM * kRowC];                  // double-buffered hidden-state rows
-    u32x4 b[2][kTileN * kRowC];                  // double-buffered head rows
+    u32x4 a[kTileM * kRowC];                     // hidden-state rows
+    u32x4 b[kTileN * kRowC];                     // head rows
 };
 union TileSmem {
     GemmStage g;
@@ -149,42 +150,32 @@ __global__ __launch_bounds__(kLmThreads, 2) void lmhead_tile_kernel(LMHeadArgs a
     const int m0 = t.m * kTileM + wm * 64, n0 = t.n * kTileN + wn * kUnit;
     const int H = a.H;
 
-    // global -> LDS copy of one step: 16-byte chunks, A 2 per thread, B 4 per thread
-    const uint16_t* ga[2];
-    const uint16_t* gb[4];
-    int la[2], lb[4];
+    // global -> LDS copy of one step: thread t moves chunk (t % 8) of rows t / 8 + 32 i,
+    // 4 rows of hidden states and 8 of the head
+    constexpr int kRA = kTileM / 32, kRB = kTileN / 32;
+    const int part = tid & 7, r0 = tid >> 3;
+    int oa[kRA], ob[kRB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = tid + i * kLmThreads, row = c >> 2, part = c & 3;
-        ga[i] = a.hidden + static_cast<long>(min(t.m * kTileM + row, a.R - 1)) * H + part * 8;
-        la[i] = row * kRowC + part;
-    }
+    for (int i = 0; i < kRA; ++i) oa[i] = min(t.m * kTileM + r0 + 32 * i, a.R - 1) * H + part * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + i * kLmThreads, row = c >> 2, part = c & 3;
-        gb[i] = a.weight + static_cast<long>(min(t.n * kTileN + row, a.V - 1)) * H + part * 8;
-        lb[i] = row * kRowC + part;
-    }
-    u32x4 ra[2], rb[4];
+    for (int i = 0; i < kRB; ++i) ob[i] = min(t.n * kTileN + r0 + 32 * i, a.V - 1) * H + part * 8;
+    u32x4 ra[kRA], rb[kRB];
     auto fetch = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ga[i] + k0);
+        for (int i = 0; i < kRA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a.hidden + static_cast<long>(oa[i]) + k0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const u32x4*>(gb[i] + k0);
+        for (int i = 0; i < kRB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(a.weight + static_cast<long>(ob[i]) + k0);
     };
-    auto stash = [&](int buf) {
+    const int ls = r0 * kRowC + part;
+    auto stash = [&]() {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) sm.g.a[buf][la[i]] = ra[i];
+        for (int i = 0; i < kRA; ++i) sm.g.a[ls + 32 * kRowC * i] = ra[i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.g.b[buf][lb[i]] = rb[i];
+        for (int i = 0; i < kRB; ++i) sm.g.b[ls + 32 * kRowC * i] = rb[i];
     };
-    // this lane's fragment chunks within a staged step (chunk 2*ks + lane/32 of its row)
-    const int koff = lane >> 5;
-    int fa[kMB], fb[kNB];
-#pragma unroll
-    for (int i = 0; i < kMB; ++i) fa[i] = (wm * 64 + 32 * i + (lane & 31)) * kRowC + koff;
-#pragma unroll
-    for (int j = 0; j < kNB; ++j) fb[j] = (wn * kUnit + 32 * j + (lane & 31)) * kRowC + koff;
+    // this lane's fragment chunks within a staged step: chunk 2*ks + lane/32 of its row
+    const int fa0 = (wm * 64 + (lane & 31)) * kRowC + (lane >> 5);
+    const int fb0 = (wn * kUnit + (lane & 31)) * kRowC + (lane >> 5);
 
     f32x16 acc[kMB][kNB];
 #pragma unroll
@@ -193,26 +184,28 @@ __global__ __launch_bounds__(kLmThreads, 2) void lmhead_tile_kernel(LMHeadArgs a
         for (int j = 0; j < kNB; ++j) acc[i][j] = f32x16{};
     const int steps = H / kKS;
     fetch(0);
-    stash(0);
+    stash();
     __syncthreads();
     for (int s = 0; s < steps; ++s) {
-        const int cur = s & 1;
         const bool more = s + 1 < steps;
-        if (more) fetch((s + 1) * kKS);           // next step's operands in flight
+        if (more) fetch((s + 1) * kKS);           // the next step's operands in flight
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < kKS / 16; ++ks) {
             bf16x8 xa[kMB], xb[kNB];
 #pragma unroll
-            for (int i = 0; i < kMB; ++i) xa[i] = __builtin_bit_cast(bf16x8, sm.g.a[cur][fa[i] + 2 * ks]);
+            for (int i = 0; i < kMB; ++i) xa[i] = __builtin_bit_cast(bf16x8, sm.g.a[fa0 + 32 * kRowC * i + 2 * ks]);
 #pragma unroll
-            for (int j = 0; j < kNB; ++j) xb[j] = __builtin_bit_cast(bf16x8, sm.g.b[cur][fb[j] + 2 * ks]);
+            for (int j = 0; j < kNB; ++j) xb[j] = __builtin_bit_cast(bf16x8, sm.g.b[fb0 + 32 * kRowC * j + 2 * ks]);
 #pragma unroll
             for (int i = 0; i < kMB; ++i)
 #pragma unroll
                 for (int j = 0; j < kNB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], xb[j], acc[i][j], 0, 0, 0);
         }
-        if (more) stash(cur ^ 1);
+        if (more) {
+            __syncthreads();                      // every wave is done with this step
+            stash();
+        }
         __syncthreads();
     }
 
