@@ -321,6 +321,8 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_merge_kernel(LMHeadArgs a) 
     const long total = static_cast<long>(a.units) * ncand;
     for (long base = static_cast<long>(wid) * kWave; base < total; base += 4 * kWave) {
         pkey_t k = base + lane < total ? cand[base + lane] : empty_key();
+        // a batch with nothing above the running 64th key changes nothing
+        if (__ballot(k > __shfl(acc, kWave - 1, kWave)) == 0ull) continue;
         wave_sort_keys(k);
         wave_merge_keys(acc, k);
     }
