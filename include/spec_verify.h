@@ -196,9 +196,13 @@ int spec_verify_chain(const void* target_logits, spec_dtype_t dtype,
  * on both distributions ("064 · 投机解码", section 二: the sampling transforms
  * are part of p and q).  After the temperature and top-k, each row keeps the
  * shortest prefix of its kept tokens, in value order (lower index first on
- * ties), whose probability mass reaches top_p, renormalised.  0 < top_p <= 1
- * (1: spec_verify_chain); top_p < 1 needs temperature > 0 and top-k on
- * (SPEC_EUNSUPPORTED otherwise).  The cut is decided on fp64 probabilities.
+ * ties), whose probability mass reaches top_p, renormalised; a token of zero
+ * probability is never kept.  0 < top_p <= 1 (1: spec_verify_chain); top_p < 1
+ * needs temperature > 0 (SPEC_EUNSUPPORTED otherwise).  With top-k on, the cut
+ * runs over the kept top-k entries; with top-k off, over whole rows (every
+ * target and draft row's cut is found first, by a radix select on the values
+ * with the masses summed exactly in fixed point, then the tests and the
+ * residual draw run in fp64).  The cut is decided on fp64 probabilities.
  * Everything else, workspace included, is as for spec_verify_chain.
  */
 int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,

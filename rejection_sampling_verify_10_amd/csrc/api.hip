@@ -165,6 +165,8 @@ int check_workspace(void* ws, size_t have, size_t need) {
 struct ChainPlan {
     int mode;   // 0 dense, 1 top-k, 2 greedy
     RowStats st;
+    NucleusRow* nt;             // dense with a nucleus: the target rows' cuts [B][K+1]
+    NucleusRow* nd;             //                        the draft rows' cuts [B][K]
     double* qsum;
     uint32_t* qflags;
     TopkLists tk;
@@ -218,6 +220,8 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
             p.qsum = c.take<double>(Rd);
             p.qflags = c.take<uint32_t>(Rd);
         }
+        p.nt = c.take<NucleusRow>(Rt);
+        p.nd = c.take<NucleusRow>(Rd);
     }
     return p;
 }
@@ -468,8 +472,8 @@ static int chain_check(const void* target_logits, spec_dtype_t dtype, const floa
     if (!greedy && topk_active(top_k, V)) {
         if (top_k > SPEC_TOPK_MAX || !topk_shape_ok(dtype, V)) return SPEC_EUNSUPPORTED;
     }
-    // the nucleus is built on the top-k path's kept lists: it needs top-k and a temperature
-    if (top_p < 1.f && (greedy || !topk_active(top_k, V))) return SPEC_EUNSUPPORTED;
+    // the nucleus needs a temperature (greedy decoding has no distribution to cut)
+    if (top_p < 1.f && greedy) return SPEC_EUNSUPPORTED;
     *need = spec_chain_workspace_bytes(B, K, V, dtype, temperature, top_k);
     return SPEC_OK;
 }
@@ -522,6 +526,26 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
         fa.sel = topk_chunk_args(target_logits, draft_probs, dtype, B, K, V, K + 1, p.tk);
         fa.ch = ca;
         SV_TRY(launch_chain_topk(fa, s, prof.timing()));
+    } else if (top_p < 1.f) {
+        // the nucleus on whole rows: every row's cut, then the tests and the draw
+        NucleusArgs na{};
+        na.logits = target_logits;
+        na.q = draft_probs;
+        na.dtype = dtype;
+        na.V = V;
+        na.invT = ca.invT;
+        na.plain = temperature == 1.f ? 1 : 0;
+        na.top_p = top_p;
+        na.out = p.nt;
+        SV_TRY(launch_nucleus_rows(na, B * (K + 1), false, s));
+        na.out = p.nd;
+        SV_TRY(launch_nucleus_rows(na, B * K, true, s));
+        NucleusChainArgs nc{};
+        nc.ch = ca;
+        nc.trow = p.nt;
+        nc.drow = p.nd;
+        nc.plain = na.plain;
+        SV_TRY(launch_nucleus_chain(nc, s, prof.timing()));
     } else if (!ca.transformed && dense_walks(B, K, V)) {
         SV_TRY(launch_chain_walk(ca, dense_bracket(false), s, prof.timing()));
     } else if (!ca.transformed) {

@@ -105,6 +105,36 @@ struct ChainArgs {
     float* out_diag;
 };
 
+// The nucleus (top-p) cut of a dense row (nucleus.hip): tokens whose order key
+// exceeds `key`, or equals it at an index <= tie_last, are kept; their nucleus
+// probability is (weight / norm) / kept.
+struct NucleusRow {
+    float m;            // target rows: the maximum logit
+    uint32_t key;       // order key of the boundary value
+    int32_t tie_last;   // last kept index among the boundary value's elements
+    uint32_t flags;     // nonzero: the row is unusable (E1 target; E3, E4 draft)
+    double norm;        // target: sum exp((z - m)/T); draft: sum q^(1/T)
+    double kept;        // the kept probability mass
+};
+struct NucleusArgs {
+    const void* logits;     // target rows [R][V] (dtype), or
+    const float* q;         // draft rows [R][V]
+    int dtype;
+    int V;
+    double invT;
+    int plain;              // draft used as given (T == 1)
+    float top_p;
+    NucleusRow* out;        // [R]
+};
+struct NucleusChainArgs {
+    ChainArgs ch;
+    const NucleusRow* trow;     // [B][K+1]
+    const NucleusRow* drow;     // [B][K]
+    int plain;
+};
+hipError_t launch_nucleus_rows(const NucleusArgs& a, int rows, bool draft, hipStream_t s);
+hipError_t launch_nucleus_chain(const NucleusChainArgs& a, hipStream_t s, Timing t = {});
+
 // A top-k chain in one launch (topk.hip): B*Ub selection units, then the
 // finisher workgroups, finish_groups(K) per batch row (chain_finish.hpp).
 constexpr int kRecWords = 5;    // 64-bit words of a position record

@@ -80,8 +80,8 @@ def test_chain_topp_argument_checks(L):
     assert call(top_p=0.0) == EINVAL
     assert call(top_p=1.5) == EINVAL
     assert call(top_p=float("nan")) == EINVAL
-    assert call(top_k=0) == EUNSUPPORTED             # the nucleus needs top-k
-    assert call(T=0.0) == EUNSUPPORTED               # and a temperature
+    assert call(top_k=0, wsb=16) == EWORKSPACE       # whole rows (top-k off) pass the argument checks
+    assert call(T=0.0) == EUNSUPPORTED               # the nucleus needs a temperature
     assert call(wsb=16) == EWORKSPACE
 
 
