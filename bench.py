@@ -69,6 +69,10 @@ WORKLOADS = {
     8: dict(name="acceptance rate B=512 K=8 V=128256, bf16 target logits, fp32 draft probs, T=1, no top-k",
             kernel="alpha_row_kernel", copies=1, oracle_rows=32, single_kernel=True,
             dtype="bf16 in, f32 exp and terms, f64 sums"),
+    10: dict(name="chain verify with the nucleus on whole rows B=64 K=7 V=128256, bf16 target logits, fp32 draft "
+                  "probs, T=0.7, top_p=0.9, no top-k",
+             kernel="nucleus_row_kernel", copies=4, oracle_rows=16, top_p=0.9,
+             dtype="bf16/f32 in, f64 probabilities, fixed-point cut masses"),
     6: dict(name="EAGLE-2 expansion layer B=64 E=10 V=128256, fp32 draft probs, top_k=10 children per node, "
                  "k_next=10 kept",
             kernel="topk_chunk_kernel", copies=2, oracle_rows=8, dtype="f32 in, f32 select and value products"),
@@ -176,6 +180,10 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
     if workload == 3:
         # the row statistics: every node row once, argmax and flags written
         return B * K * V * esz + B * K * 12
+    if workload == 10:
+        # the cut of every row needs every target row (bf16) and every draft row (fp32): each
+        # once, and the cuts written
+        return B * (K + 1) * V * 2 + B * K * V * 4 + B * (2 * K + 1) * 32
     if workload == 2:
         # every target row (bf16) and every draft row (fp32) once.  The chunk lists the
         # selection hands to the finishers (64 words of 8 bytes per chunk) are written and
@@ -303,6 +311,7 @@ def main() -> int:
 
     t0 = time.time()
     ci = W.config(args.workload, seed=args.seed)
+    top_p = wl.get("top_p", 1.0)
     tree = args.workload == 3
     arate = args.workload == 8
     sampled_tree = args.workload == 5
@@ -407,7 +416,7 @@ def main() -> int:
             R.verify_chain_fused(h, w, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
         else:
             z, q, x, u = sets[i % len(sets)]
-            R.verify_chain(z, q, x, u, T, top_k, out=(tok, alen), workspace=ws)
+            R.verify_chain(z, q, x, u, T, top_k, top_p, out=(tok, alen), workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -499,7 +508,7 @@ def main() -> int:
                                         ci.uniforms[:rows], T, top_k)
                 else:
                     oracle.verify_chain(ci.logits[:rows], ci.dtype, ci.draft_probs[:rows], ci.draft_tokens[:rows],
-                                        ci.uniforms[:rows], T, top_k)
+                                        ci.uniforms[:rows], T, top_k, top_p)
                 reps += 1
                 dt = time.perf_counter() - t0
                 if dt >= budget_s or reps >= 200:
@@ -552,6 +561,7 @@ def main() -> int:
                     "input_copies": wl["copies"], "parallelism": "single GPU"}
                    if fused else
                    {"workload": wl["name"], "B": B, "K": K, "V": V, "temperature": T, "top_k": top_k,
+                    **({"top_p": top_p} if top_p < 1.0 else {}),
                     "input_copies": wl["copies"], "parallelism": "single GPU"}),
         "step_algorithmic_GBps": step_alg_gbs,
         "emitted_tokens_per_s": None if arate else float(np.sum(al[al >= 0] + 1)) / (ms_step * 1e-3),

@@ -536,16 +536,17 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
         na.invT = ca.invT;
         na.plain = temperature == 1.f ? 1 : 0;
         na.top_p = top_p;
-        na.out = p.nt;
-        SV_TRY(launch_nucleus_rows(na, B * (K + 1), false, s));
-        na.out = p.nd;
-        SV_TRY(launch_nucleus_rows(na, B * K, true, s));
+        na.rows_t = B * (K + 1);
+        na.rows_d = B * K;
+        na.out_t = p.nt;
+        na.out_d = p.nd;
+        SV_TRY(launch_nucleus_rows(na, s, prof.timing()));
         NucleusChainArgs nc{};
         nc.ch = ca;
         nc.trow = p.nt;
         nc.drow = p.nd;
         nc.plain = na.plain;
-        SV_TRY(launch_nucleus_chain(nc, s, prof.timing()));
+        SV_TRY(launch_nucleus_chain(nc, s));
     } else if (!ca.transformed && dense_walks(B, K, V)) {
         SV_TRY(launch_chain_walk(ca, dense_bracket(false), s, prof.timing()));
     } else if (!ca.transformed) {

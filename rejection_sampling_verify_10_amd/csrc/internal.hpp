@@ -117,14 +117,16 @@ struct NucleusRow {
     double kept;        // the kept probability mass
 };
 struct NucleusArgs {
-    const void* logits;     // target rows [R][V] (dtype), or
-    const float* q;         // draft rows [R][V]
+    const void* logits;     // target rows [rows_t][V] (dtype)
+    const float* q;         // draft rows [rows_d][V]
+    int rows_t, rows_d;
     int dtype;
     int V;
     double invT;
     int plain;              // draft used as given (T == 1)
     float top_p;
-    NucleusRow* out;        // [R]
+    NucleusRow* out_t;      // [rows_t]
+    NucleusRow* out_d;      // [rows_d]
 };
 struct NucleusChainArgs {
     ChainArgs ch;
@@ -132,7 +134,7 @@ struct NucleusChainArgs {
     const NucleusRow* drow;     // [B][K]
     int plain;
 };
-hipError_t launch_nucleus_rows(const NucleusArgs& a, int rows, bool draft, hipStream_t s);
+hipError_t launch_nucleus_rows(const NucleusArgs& a, hipStream_t s, Timing t = {});
 hipError_t launch_nucleus_chain(const NucleusChainArgs& a, hipStream_t s, Timing t = {});
 
 // A top-k chain in one launch (topk.hip): B*Ub selection units, then the

@@ -80,22 +80,17 @@ __device__ __forceinline__ double block_sum_d(double v, NucSmem& sm) {
     return t;
 }
 
-// The row's element i: its value, order key and fp64 probability (given the
-// normaliser's inverse).
+// A row's values and their unnormalised weights: exp((z - m)/T) for a target
+// row, q^(1/T) for a draft row (q as given at T == 1; 0 for q <= 0).
 template <int DT, bool DRAFT>
 struct RowView {
-    const void* row;
+    const char* row;
     int V;
     double invT;
-    bool plain;          // draft used as given (T == 1)
+    bool plain;
     ExpArg g;
     const double* tbl;
     ExpConsts ek;
-    __device__ __forceinline__ float value(int i) const {
-        if (DRAFT) return static_cast<const float*>(row)[i];
-        return Elem<DT>::scalar(row, i);
-    }
-    // unnormalised weight: exp((z - m)/T), or q^(1/T)
     __device__ __forceinline__ double weight(float v) const {
         if (DRAFT) {
             if (!(v > 0.f)) return 0.0;
@@ -103,12 +98,37 @@ struct RowView {
         }
         return exp_of(v, g, tbl, ek);
     }
+    // f(i, v) for the elements of this thread, chunk by chunk: with VEC thread t
+    // takes the 16-byte vector t of each chunk of kNT vectors (so its elements
+    // within a chunk are contiguous and follow those of thread t - 1); else one
+    // element per thread per chunk.  Every thread runs the same chunks; f may
+    // return true to end the loop after the current chunk (a block-uniform
+    // decision, taken through `stop`).
+    template <bool VEC, typename F>
+    __device__ __forceinline__ void each(F f) const {
+        constexpr int EPV = DRAFT ? 4 : Elem<DT>::kPerVec;
+        if constexpr (VEC) {
+            const int nvec = V / EPV;
+            const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+            for (int c = 0; c < nvec; c += kNT) {
+                const int g = c + static_cast<int>(threadIdx.x);
+                if (g < nvec) {
+                    const u32x4 w = load_stream(rv + g);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e)
+                        f(g * EPV + e, DRAFT ? __uint_as_float(w[e]) : Elem<DT>::get(w, e));
+                }
+            }
+        } else {
+            for (int i = threadIdx.x; i < V; i += kNT)
+                f(i, DRAFT ? reinterpret_cast<const float*>(row)[i] : Elem<DT>::scalar(row, i));
+        }
+    }
 };
 
-template <int DT, bool DRAFT>
-__global__ __launch_bounds__(kNT, 1) void nucleus_row_kernel(NucleusArgs a, ExpConsts ek) {
-    __shared__ NucSmem sm;
-    const int r = blockIdx.x;
+// The cut of target row r (DRAFT false) or draft row r.
+template <int DT, bool DRAFT, bool VEC>
+__device__ void nucleus_row(const NucleusArgs& a, const ExpConsts& ek, int r, NucleusRow* outp, NucSmem& sm) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
     const int V = a.V;
     const char* rowp = static_cast<const char*>(DRAFT ? static_cast<const void*>(a.q) : a.logits) +
@@ -119,15 +139,14 @@ __global__ __launch_bounds__(kNT, 1) void nucleus_row_kernel(NucleusArgs a, ExpC
     RowView<DT, DRAFT> rv{rowp, V, a.invT, a.plain != 0, ExpArg{0.0, 0.0}, sm.tbl, ek};
     NucleusRow out{};
 
-    // 1. maximum (targets) and the validity of the row
+    // 1. the row's validity, maximum (targets) and normaliser
     float mx = -INFINITY;
     bool bad = false;
-    for (int i = tid; i < V; i += kNT) {
-        const float v = rv.value(i);
+    rv.template each<VEC>([&](int, float v) {
         if (DRAFT) bad |= !q_ok(v);
         else bad |= !(v < INFINITY);                 // NaN or +inf (E1)
         mx = fmaxf(mx, v);
-    }
+    });
     mx = wave_max(mx);
     if (lane == 0) sm.fred[wid] = mx;
     if (__ballot(bad) && lane == 0) atomicOr(&sm.bad, 1u);
@@ -135,27 +154,38 @@ __global__ __launch_bounds__(kNT, 1) void nucleus_row_kernel(NucleusArgs a, ExpC
     float M = sm.fred[0];
 #pragma unroll
     for (int w = 1; w < kNW; ++w) M = fmaxf(M, sm.fred[w]);
-    if (!DRAFT && M == -INFINITY) bad = true;        // only -inf (E1)
-    bad = bad || sm.bad != 0u;
+    bad = sm.bad != 0u || (!DRAFT && M == -INFINITY);    // only -inf (E1)
     if (!DRAFT) rv.g = exp_arg(static_cast<double>(M), a.invT, ek);
     double norm = 0.0;
     if (!bad) {
         double s = 0.0;
-        for (int i = tid; i < V; i += kNT) s += rv.weight(rv.value(i));
+        rv.template each<VEC>([&](int, float v) { s += rv.weight(v); });
         norm = block_sum_d(s, sm);
         if (!(norm > 0.0 && norm < INFINITY)) bad = true;     // E4 (drafts), or an overflow
     }
     if (bad) {
         if (tid == 0) {
             out.flags = 1u;
-            a.out[r] = out;
+            outp[r] = out;
         }
         return;
     }
     const double invN = 1.0 / norm;
 
-    // 2. radix select of the boundary key
+    // 2. radix select of the boundary key.  Tokens of probability below
+    // tau = (1 - top_p) / (2V) hold less than (1 - top_p)/2 together, so the mass
+    // taken from the top reaches top_p before them: they are left out (their
+    // value lies below the boundary).  A value threshold skips their weights.
     const unsigned long long target = max(fixp(static_cast<double>(a.top_p)), 1ull);   // at least the top token
+    const double tau = (1.0 - static_cast<double>(a.top_p)) / (2.0 * V);
+    float vskip;                                  // values strictly below it have p < tau
+    if (DRAFT) {
+        const double qt = a.plain ? tau * norm : pow(tau * norm, 1.0 / a.invT);
+        vskip = static_cast<float>(qt * (1.0 - 1e-9));
+    } else {
+        vskip = static_cast<float>(static_cast<double>(M) + log(tau * norm) / a.invT - 1e-6 * (1.0 + fabs(M)));
+    }
+    if (!(tau > 0.0)) vskip = -INFINITY;
     if (tid == 0) { sm.prefix = 0u; sm.above = 0ull; sm.goal = target; }
     int last_cnt = 0;
     for (int l = 0; l < kLevels; ++l) {
@@ -164,15 +194,16 @@ __global__ __launch_bounds__(kNT, 1) void nucleus_row_kernel(NucleusArgs a, ExpC
         for (int t = tid; t < nb; t += kNT) { sm.cnt[t] = 0u; sm.mass[t] = 0ull; }
         __syncthreads();
         const uint32_t prefix = sm.prefix;
-        for (int i = tid; i < V; i += kNT) {
-            const float v = rv.value(i);
+        rv.template each<VEC>([&](int, float v) {
+            if (!(v >= vskip)) return;
             const uint32_t key = order_key(v);
-            if (l > 0 && (key >> psh) != prefix) continue;
+            if (l > 0 && (key >> psh) != prefix) return;
+            const double p = rv.weight(v) * invN;
+            if (!(p > 0.0)) return;
             const int bin = static_cast<int>((key >> sh) & static_cast<uint32_t>(nb - 1));
             atomicAdd(&sm.cnt[bin], 1u);
-            const double p = rv.weight(v) * invN;
-            if (p > 0.0) atomicAdd(&sm.mass[bin], fixp(p));
-        }
+            atomicAdd(&sm.mass[bin], fixp(p));
+        });
         __syncthreads();
         // Bins from the top: thread t holds bins nb-1-per*t .. nb-per-per*t.
         const int per = (nb + kNT - 1) / kNT;
@@ -182,7 +213,7 @@ __global__ __launch_bounds__(kNT, 1) void nucleus_row_kernel(NucleusArgs a, ExpC
             if (bin >= 0) mine += sm.mass[bin];
         }
         // exclusive sums from the top, by waves of 64 threads (a sequential pass over
-        // the 16 wave totals, then lane scans): integers, so exact in any order
+        // the wave totals, then lane scans): integers, so exact in any order
         unsigned long long incl = mine;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
@@ -236,55 +267,75 @@ __global__ __launch_bounds__(kNT, 1) void nucleus_row_kernel(NucleusArgs a, ExpC
         n = n < 1 ? 1 : (n > last_cnt ? last_cnt : n);
     }
 
-    // 3. the last kept element of the boundary value (index order) and the kept mass
-    double kept = 0.0;
-    long long seen = 0;                               // boundary elements before this chunk
-    constexpr int kE = 4;                             // contiguous elements per thread per chunk
-    for (int base = 0; base < V; base += kNT * kE) {
-        int ties = 0;
-        const int i0 = base + tid * kE;
-        for (int e = 0; e < kE; ++e) {
-            const int i = i0 + e;
-            if (i >= V) break;
-            const float v = rv.value(i);
-            const uint32_t key = order_key(v);
-            if (key > bkey) kept += rv.weight(v) * invN;
-            else if (key == bkey) ++ties;
-        }
-        int incl = ties;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int tv = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += tv;
-        }
-        __syncthreads();
-        if (lane == kWave - 1) sm.ired[wid] = incl;
-        __syncthreads();
-        long long rank = seen + incl - ties;
-        for (int w = 0; w < wid; ++w) rank += sm.ired[w];
-        long long chunk_ties = 0;
-        for (int w = 0; w < kNW; ++w) chunk_ties += sm.ired[w];
-        if (ties > 0 && rank < n && rank + ties >= n) {
-            // the n-th boundary element lies in this thread's span
-            long long rr = rank;
-            for (int e = 0; e < kE; ++e) {
+    // 3. The last kept element of the boundary value in index order (a scan of tie
+    // counts, ended once it is found; every one of them when all are kept), and
+    // the kept mass: the elements above the boundary from their exact fixed-point
+    // sum, plus n times the boundary probability.
+    if (n >= last_cnt) {
+        if (tid == 0) sm.tie_last = V;
+    } else {
+        long long seen = 0;                       // boundary elements before this chunk
+        constexpr int EPT = VEC ? (DRAFT ? 4 : Elem<DT>::kPerVec) : 1;
+        const int step = kNT * EPT;
+        for (int base = 0; base < V; base += step) {
+            const int i0 = base + tid * EPT;
+            int ties = 0;
+            for (int e = 0; e < EPT; ++e) {
                 const int i = i0 + e;
-                if (i >= V) break;
-                if (order_key(rv.value(i)) == bkey && ++rr == n) { sm.tie_last = i; break; }
+                if (i < V && order_key(DRAFT ? reinterpret_cast<const float*>(rowp)[i]
+                                             : Elem<DT>::scalar(rowp, i)) == bkey)
+                    ++ties;
             }
+            int incl = ties;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int tv = __shfl_up(incl, o, kWave);
+                if (lane >= o) incl += tv;
+            }
+            __syncthreads();
+            if (lane == kWave - 1) sm.ired[wid] = incl;
+            __syncthreads();
+            long long rank = seen + incl - ties;
+            for (int w = 0; w < wid; ++w) rank += sm.ired[w];
+            long long chunk_ties = 0;
+            for (int w = 0; w < kNW; ++w) chunk_ties += sm.ired[w];
+            if (ties > 0 && rank < n && rank + ties >= n) {
+                long long rr = rank;
+                for (int e = 0; e < EPT; ++e) {
+                    const int i = i0 + e;
+                    if (i >= V) break;
+                    if (order_key(DRAFT ? reinterpret_cast<const float*>(rowp)[i] : Elem<DT>::scalar(rowp, i)) ==
+                            bkey &&
+                        ++rr == n) {
+                        sm.tie_last = i;
+                        break;
+                    }
+                }
+            }
+            seen += chunk_ties;
+            if (seen >= n) break;                 // block-uniform: every thread has the same `seen`
         }
-        seen += chunk_ties;
     }
-    kept = block_sum_d(kept, sm);
+    __syncthreads();
     if (tid == 0) {
         out.m = M;
         out.key = bkey;
         out.tie_last = sm.tie_last;
         out.flags = 0u;
         out.norm = norm;
-        out.kept = kept + static_cast<double>(n) * pb;
-        a.out[r] = out;
+        out.kept = static_cast<double>(above) * 0x1p-62 + static_cast<double>(n) * pb;
+        outp[r] = out;
     }
+}
+
+// One launch for every row of a call: the rows_t target rows first, then the
+// draft rows.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kNT, 1) void nucleus_row_kernel(NucleusArgs a, ExpConsts ek) {
+    __shared__ NucSmem sm;
+    const int r = blockIdx.x;
+    if (r < a.rows_t) nucleus_row<DT, false, VEC>(a, ek, r, a.out_t, sm);
+    else nucleus_row<0, true, VEC>(a, ek, r - a.rows_t, a.out_d, sm);
 }
 
 // ---- the chain ----
@@ -507,13 +558,19 @@ __global__ __launch_bounds__(kCT) void nucleus_chain_kernel(NucleusChainArgs na,
 
 }  // namespace
 
-hipError_t launch_nucleus_rows(const NucleusArgs& a, int rows, bool draft, hipStream_t s) {
+hipError_t launch_nucleus_rows(const NucleusArgs& a, hipStream_t s, Timing t) {
+    const int rows = a.rows_t + a.rows_d;
     if (rows <= 0) return hipSuccess;
     const ExpConsts ek = exp_consts();
-    const Timing none{};
-    if (draft) launch_timed(none, nucleus_row_kernel<0, true>, dim3(rows), dim3(kNT), 0, s, a, ek);
-    else if (a.dtype == 1) launch_timed(none, nucleus_row_kernel<1, false>, dim3(rows), dim3(kNT), 0, s, a, ek);
-    else launch_timed(none, nucleus_row_kernel<0, false>, dim3(rows), dim3(kNT), 0, s, a, ek);
+    // 16-byte loads when every target and draft row starts 16-byte aligned
+    const bool vec = vec_ok(a.logits, a.V, a.dtype == 1 ? 2 : 4) && vec_ok(a.q, a.V, 4);
+    if (a.dtype == 1) {
+        if (vec) launch_timed(t, nucleus_row_kernel<1, true>, dim3(rows), dim3(kNT), 0, s, a, ek);
+        else launch_timed(t, nucleus_row_kernel<1, false>, dim3(rows), dim3(kNT), 0, s, a, ek);
+    } else {
+        if (vec) launch_timed(t, nucleus_row_kernel<0, true>, dim3(rows), dim3(kNT), 0, s, a, ek);
+        else launch_timed(t, nucleus_row_kernel<0, false>, dim3(rows), dim3(kNT), 0, s, a, ek);
+    }
     return hipGetLastError();
 }
 

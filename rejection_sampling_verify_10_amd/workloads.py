@@ -496,7 +496,7 @@ CONFIG_NAMES = {
 
 def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int] = None,
            V: Optional[int] = None, threads: Optional[int] = None):
-    """Inputs for workload ``cid`` (0..9), optionally with smaller B/K/V (K: expanded nodes for 6)."""
+    """Inputs for workload ``cid`` (0..10), optionally with smaller B/K/V (K: expanded nodes for 6)."""
     if cid == 0:
         return make_chain(B or 1, K or 4, V or 1000, dtype=DTYPE_F32, temperature=1.0, top_k=0,
                           sigma=sigma_const(0.5), config_id=0, seed=seed, threads=threads)
@@ -515,6 +515,10 @@ def config(cid: int, seed: int = 0, *, B: Optional[int] = None, K: Optional[int]
     if cid == 5:
         return make_tree_sampled(B or 32, V or 32000, dtype=DTYPE_BF16, temperature=1.0, top_k=0,
                                  sigma=0.5, config_id=5, seed=seed, threads=threads)
+    if cid == 10:
+        # the benchmark's shape with the nucleus on whole rows: drafts from the draft's own nucleus
+        return make_chain(B or 64, K or 7, V or 128256, dtype=DTYPE_BF16, temperature=0.7, top_k=0,
+                          sigma=sigma_halves(0.3, 1.0), config_id=10, seed=seed, threads=threads, top_p=0.9)
     if cid == 9:
         return make_lm_head(B or 64, K or 7, V or 128256, 4096, temperature=0.7, top_k=50,
                             sigma=sigma_halves(0.3, 1.0), config_id=9, seed=seed, threads=threads)
