@@ -314,6 +314,7 @@ struct RowSmem {
     int ired[kWaves];
     int n_list, j, err, chunk, fallback;
     uint32_t qbad;
+    uint32_t zbad;                     // the bonus row holds NaN or +inf
     double before;
 };
 
@@ -518,6 +519,8 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
     // ---- one pass over row j ----
     double sq_tot = 0.0;                   // transformed draft: sum w over the thread's elements
     double se_tot = 0.0;                   // residual rows: sum e over the thread's elements
+    float zmax = -INFINITY;                // bonus rows: the maximum and any NaN or +inf
+    bool zbad = false;
     auto body = [&](auto res_tag) {
         constexpr bool RES = decltype(res_tag)::value;
         using Buf = Raw8<DT>[kSub];
@@ -545,6 +548,11 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
                 auto one = [&](int e) {
                     const double ex = TAB ? ext[e] : exp_of(rb[s].zf(e), g, tbl, ek);
                     se += ex;
+                    if (!RES) {
+                        const float zf = rb[s].zf(e);
+                        zmax = fmaxf(zmax, zf);
+                        zbad |= !(zf < INFINITY);
+                    }
                     if (RES) {
                         const float qv = rb[s].qf(e);
                         const double w = draft_w<TR>(qv, a.invT);
@@ -657,7 +665,19 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
 
     double Zp = 0.0, Zq = 1.0, S = 0.0;
     bool residual = false;
+    ExpArg gd = g;                          // the draw's exponents
     if (!res) {
+        // The bonus row's validity (E1) and maximum: the walk leaves row K to this pass.
+        {
+            const float wz = wave_max(zmax);
+            if (lane == 0) sm.wmax[wid] = wz;
+            if (__ballot(zbad) && lane == 0) atomicOr(&sm.zbad, 1u);
+        }
+        __syncthreads();
+        float zm = sm.wmax[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) zm = fmaxf(zm, sm.wmax[w]);
+        if (sm.zbad || zm == -INFINITY) { fail_row(); return; }
         for (int c = tid; c < C; c += kThreads) {
             double e = 0.0;
 #pragma unroll
@@ -666,6 +686,15 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
         }
         __syncthreads();
         for (int c = 0; c < C; ++c) Zp += sm.part[c];
+        if (!(Zp > 0.0 && Zp < INFINITY) || fabs((static_cast<double>(zm) - m_j) * a.invT) > 600.0) {
+            // exponents too far from the reference (overflow or underflow risk): again
+            // against the row's own maximum
+            gd = exp_arg(static_cast<double>(zm), a.invT, ek);
+            __syncthreads();
+            exact_chunk_sums<DT, VEC, TR>(a, zr, qr, C, gd, tbl, ek, false, 0.0, 0.0, sm);
+            Zp = 0.0;
+            for (int c = 0; c < C; ++c) Zp += sm.part[c];
+        }
     } else {
         Zp = block_sum(se_tot, sm.red);
         if (TR) Zq = block_sum(sq_tot, sm.red);      // exact normaliser of the transformed draft
@@ -711,12 +740,12 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
     }
     const double invZp = 1.0 / Zp, invZq = 1.0 / Zq;
 
-    draw_emit<DT, VEC, TR>(a, b, j, zr, qr, C, g, tbl, ek, residual, residual ? S : Zp, S, invZp, invZq, sm);
+    draw_emit<DT, VEC, TR>(a, b, j, zr, qr, C, gd, tbl, ek, residual, residual ? S : Zp, S, invZp, invZq, sm);
 }
 
 __device__ __forceinline__ void init_draw_smem(RowSmem& sm) {
     for (int t = threadIdx.x; t < kTableSize; t += kThreads) sm.tbl[t] = exp2(static_cast<double>(t) * (1.0 / kTableSize));
-    if (threadIdx.x == 0) { sm.n_list = 0; sm.qbad = 0; }
+    if (threadIdx.x == 0) { sm.n_list = 0; sm.qbad = 0; sm.zbad = 0; }
 }
 
 // All rows' statistics precomputed (rowstats_kernel): ratio tests in one wave,
@@ -910,6 +939,14 @@ __device__ __forceinline__ void walk_positions(const ChainArgs& a, int b, RowSme
                 row_reduce<DT>(ra, a.invT, sm, M, Z);
                 if (test(k, M, Z)) return true;
                 ++k;
+                if (k == K) {
+                    // Every draft token passed: row K feeds only the bonus draw, whose fp64
+                    // pass takes the row's validity and maximum itself.  Its exponents are
+                    // taken against row K-1's maximum (mj), a common factor of every weight
+                    // that cancels in the draw.
+                    j = K;
+                    return true;
+                }
                 t = 0;
                 ra = RowAcc<DT>();
                 return false;
