@@ -222,7 +222,9 @@ int spec_verify_chain_topp(const void* target_logits, spec_dtype_t dtype, const 
  * and launches nothing.  The first call on a device looks the array up (with
  * that device current); the array is zero-filled by a fill kernel on the
  * call's stream before a top-k call whenever another kind of call used it
- * since.  Every call on a GPU shares that GPU's array: calls that may overlap
+ * since; that decision is taken when a call is issued, so a graph that
+ * captured a top-k call replays without it: between its replays, run no call
+ * that leaves scratch behind.  Every call on a GPU shares that GPU's array: calls that may overlap
  * (different streams, or several host threads, without ordering between them)
  * race and give undefined results; order them on one stream.
  */
