@@ -580,6 +580,14 @@ def main() -> int:
                       "read_probe_GBps": probe, "frac_of_read_probe": achieved / probe}),
         "cpu_baseline": cpu,
     }
+    if args.workload == 4:
+        # The walk reads target rows only up to the first rejection.  The bytes of the
+        # route that reduces every row first (every target row once, plus the draft row of
+        # each residual draw) put its step time beside a full read of the batch.
+        drafts = int(np.sum((al >= 0) & (al < K)))
+        all_rows = B * (K + 1) * V * esz + drafts * V * 4
+        line["roofline"]["all_rows_bytes"] = all_rows
+        line["roofline"]["all_rows_equivalent_frac"] = all_rows / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS
     line.update(extra)
     print(json.dumps(line), flush=True)
     return 0
