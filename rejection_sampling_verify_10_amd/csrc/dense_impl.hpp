@@ -545,16 +545,19 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
                 }
                 double ext[8];
                 if constexpr (TAB) exp8_table(rb[s], etab, g, tbl, ek, ext);
+                // (the transformed draft's loop is not unrolled, to keep one copy of the
+                // power function: its element index is a run-time value, read through
+                // selects rather than by indexing the registers)
                 auto one = [&](int e) {
-                    const double ex = TAB ? ext[e] : exp_of(rb[s].zf(e), g, tbl, ek);
+                    const float zf = TR ? rb[s].zf_at(e) : rb[s].zf(e);
+                    const double ex = TAB ? ext[e] : exp_of(zf, g, tbl, ek);
                     se += ex;
                     if (!RES) {
-                        const float zf = rb[s].zf(e);
                         zmax = fmaxf(zmax, zf);
                         zbad |= !(zf < INFINITY);
                     }
                     if (RES) {
-                        const float qv = rb[s].qf(e);
+                        const float qv = TR ? rb[s].qf_at(e) : rb[s].qf(e);
                         const double w = draft_w<TR>(qv, a.invT);
                         if (TR) sq_tot += w;
                         const double wq = TR ? w * iq : w;
