@@ -64,6 +64,52 @@ __device__ __forceinline__ double exp_of(float z, const ExpArg& g, const double*
     return exp_scaled(fma(static_cast<double>(z), g.k1, g.mk1), tbl, k);
 }
 
+// q^(1/T) for a float32 q > 0 in fp64, as 2^(log2(q)/T): the logarithm by Tang's
+// table-driven method (ACM TOMS 16(4), 1990), the power of two by exp_scaled.
+// With q = 2^e * m, m in [1, 2), and c_j = 1 + j/128 the table point nearest m
+// (j = 0..128), log2 q = e - log2(inv_j) + log2(1 + r), where inv_j is the fp64
+// value of 1/c_j and r = m*inv_j - 1 (one fma; |r| <= 1/256).  Using log2 of the
+// stored inv_j rather than of c_j cancels the rounding of inv_j exactly.
+// ln(1 + r) is its Taylor series to r^6 (truncation < 2e-18).  Relative error
+// about 3e-15 where the result exceeds 1e-6 of the largest weight (the rounding
+// of the scaled argument, as in exp_of), up to 1e-13 for results below that;
+// q = 2^e gives 2^(e/T) to the last bit of exp_scaled (r = 0).
+constexpr int kLogTab = 129;
+struct LogEntry {
+    double inv;       // 1 / (1 + j/128), rounded
+    double lg;        // -log2(inv)
+};
+__device__ __forceinline__ void build_log_table(LogEntry* lt) {
+    for (int j = threadIdx.x; j < kLogTab; j += blockDim.x) {
+        const double inv = 1.0 / (1.0 + static_cast<double>(j) * (1.0 / 128));
+        lt[j] = LogEntry{inv, -log2(inv)};
+    }
+}
+// y = A*log2(q) + ... in exp_scaled's units: A = 256/T, B = A/ln2.
+struct PowArg {
+    double A, B;
+};
+__device__ __forceinline__ PowArg pow_arg(double invT, const ExpConsts& k) {
+    return PowArg{256.0 * invT, invT * k.scale};
+}
+__device__ __forceinline__ double pow_q(float q, const PowArg& pa, const LogEntry* lt, const double* tbl,
+                                        const ExpConsts& k) {
+    const double d = static_cast<double>(q);
+    const int hi = __double2hiint(d), lo = __double2loint(d);
+    const int e = ((hi >> 20) & 0x7ff) - 1023;
+    const int j = (((hi >> 12) & 0xff) + 1) >> 1;
+    const double m = __hiloint2double((hi & 0x000fffff) | 0x3ff00000, lo);
+    const LogEntry c = lt[j];
+    const double r = fma(m, c.inv, -1.0);
+    double t = fma(r, -1.0 / 6, 1.0 / 5);
+    t = fma(t, r, -0.25);
+    t = fma(t, r, 1.0 / 3);
+    t = fma(t, r, -0.5);
+    t *= r;
+    const double l1p = fma(t, r, r);                        // ln(1 + r)
+    return exp_scaled(fma(pa.A, static_cast<double>(e) + c.lg, pa.B * l1p), tbl, k);
+}
+
 // bfloat16 logits take few distinct values: the pass looks exp((z - m)/T) up in
 // a per-row LDS table holding exp_of of every bf16 value with 2^-20 <= |z| < 256
 // (28 binades of 128 values per sign), so the result is the one exp_of gives.
