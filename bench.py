@@ -58,7 +58,7 @@ WORKLOADS = {
             dtype="bf16 in, f32 exp, f64 draw"),
     5: dict(name="sampled static-tree verify B=32 N=27 (depth 5) V=32000, bf16 target logits, fp32 draft probs, "
                  "T=1, no top-k",
-            kernel="tree_sample_kernel", copies=4, oracle_rows=32, dtype="bf16 in, f64 probabilities"),
+            kernel="tree_cluster_kernel", copies=4, oracle_rows=32, dtype="bf16 in, f64 probabilities"),
     7: dict(name="KV commit of accepted tree paths B=64, 64 planes (32 layers x K/V), 2 KiB rows (8 heads x 128 "
                  "x bf16), 27-node tree, prefix <= 16",
             kernel="kv_commit_kernel", copies=8, oracle_rows=64, dtype="bytes (bf16 rows)"),
@@ -368,6 +368,7 @@ def main() -> int:
         alen = torch.empty((B,), dtype=torch.int32, device=dev)
         parents = ci.parents.tolist()
         rows_per_step = B * K                  # node rows verified
+        ws = R.new_workspace(R.tree_sample_workspace_bytes(B, K), dev)
     elif fused:
         B, K, V, T, top_k = ci.B, ci.K, ci.V, ci.temperature, ci.top_k
         Hd = ci.H
@@ -407,7 +408,7 @@ def main() -> int:
             R.tree_expand(q, nv, top_k, ci.k_next, out=(xt, xv, xn), workspace=ws)
         elif sampled_tree:
             z, q, nt, u = sets[i % len(sets)]
-            R.verify_tree_sample(z, q, nt, u, parents, T, top_k, out=(path, tok, alen))
+            R.verify_tree_sample(z, q, nt, u, parents, T, top_k, out=(path, tok, alen), workspace=ws)
         elif arate:
             z, q = sets[i % len(sets)]
             R.accept_rate(z, q, T, top_k, out=alpha_out, workspace=ws)

@@ -360,6 +360,38 @@ int spec_verify_tree_sample_rows(const void* target_logits, spec_dtype_t dtype, 
                                  int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream);
 
 /*
+ * spec_verify_tree_sample_ws, spec_verify_tree_sample_rows_ws -- the two
+ * sampled-tree calls above (same method, pages and arguments), given a
+ * workspace of spec_tree_sample_workspace_bytes(B, N) bytes (256-byte
+ * aligned; SPEC_EWORKSPACE if smaller).  With it, a batch of B <= 128 rows
+ * shares each row's walk among min(8, 256/B) workgroups, each summing a slice
+ * of the vocabulary, which exchange their sums through the workspace; this
+ * needs V a multiple of 8, 16-byte aligned rows and V <= 8192 * min(8, 256/B)
+ * (4096 * min(8, 256/B) when temperature != 1), else (and for B > 128, where
+ * the size is 0) the call runs as without one.
+ * Same results as the calls above, up to the rounding order of the sums.
+ *
+ * The workspace must be zero-filled before its first use; every call leaves
+ * it zero, so it can be reused, including by replays of a captured graph.
+ * Calls that overlap on one workspace race.  The members of a batch row wait
+ * for one another's words; this relies on workgroups being dispatched in
+ * order (a row's members are consecutive), as the top-k chain does.  A wait
+ * that exceeds the spin limit (SPEC_VERIFY_SPIN_LIMIT, above) gives up: that
+ * batch row's accept_len is SPEC_ROW_TIMED_OUT and its outputs -1.
+ */
+size_t spec_tree_sample_workspace_bytes(int B, int N);
+int spec_verify_tree_sample_ws(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                               const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
+                               int B, int N, int V, float temperature, int top_k, int32_t* out_path,
+                               int32_t* out_tokens, int32_t* out_accept_len, void* workspace, size_t workspace_bytes,
+                               void* hip_stream);
+int spec_verify_tree_sample_rows_ws(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                                    const int32_t* node_tokens, const float* uniforms, const int32_t* parents, int B,
+                                    int N, int V, float temperature, int top_k, int32_t* out_path,
+                                    int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream);
+
+/*
  * EAGLE-2 draft-tree construction ("EAGLE-2: Faster Inference of Language
  * Models with Dynamic Draft Trees", section 4).  A node's value is the product
  * of the draft model's confidences along its path (section 4.1).  Values and

@@ -68,6 +68,12 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_tree_sample.restype = I
         L.spec_verify_tree_sample_rows.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P]
         L.spec_verify_tree_sample_rows.restype = I
+        L.spec_tree_sample_workspace_bytes.argtypes = [I, I]
+        L.spec_tree_sample_workspace_bytes.restype = Z
+        L.spec_verify_tree_sample_ws.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P, Z, P]
+        L.spec_verify_tree_sample_ws.restype = I
+        L.spec_verify_tree_sample_rows_ws.argtypes = [P, I, P, P, P, P, I, I, I, F, I, P, P, P, P, Z, P]
+        L.spec_verify_tree_sample_rows_ws.restype = I
         L.spec_verify_tree_greedy_rows.argtypes = [P, I, P, P, I, I, I, P, P, P, P, Z, P]
         L.spec_verify_tree_greedy_rows.restype = I
         L.spec_tree_expand_workspace_bytes.argtypes = [I, I, I, I]
@@ -358,16 +364,23 @@ def _tree_outputs(out, B: int, D: int, dev):
     return path, toks, alen
 
 
+def tree_sample_workspace_bytes(B: int, N: int) -> int:
+    return int(lib().spec_tree_sample_workspace_bytes(B, N))
+
+
 def verify_tree_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor, node_tokens: torch.Tensor,
                        uniforms: torch.Tensor, parents: Sequence[int], temperature: float = 1.0, top_k: int = 0,
-                       *, out: Optional[Tuple[torch.Tensor, ...]] = None):
-    """Sampling static-tree verification (``spec_verify_tree_sample``).
+                       *, out: Optional[Tuple[torch.Tensor, ...]] = None, workspace=None):
+    """Sampling static-tree verification (``spec_verify_tree_sample_ws``).
 
     target_logits [B, N, V] bf16/f32, draft_probs [B, N, V] f32 (row n: the draft
     distribution at node n), node_tokens [B, N] int32, uniforms [B, N] f32 (u[n] tests
     node n, u[0] drives the final draw), parents: N host ints (one static tree) or a [B, N]
     int32 GPU tensor (a tree per batch row; then D = N - 1).  Returns (path [B, D+1],
     tokens [B, D+1], accept_len [B]) int32 tensors; ``out`` reuses output tensors.
+    ``workspace``: a zeroed uint8 tensor of at least tree_sample_workspace_bytes(B, N)
+    (left zero by the call), None for a fresh one, or False for the call without a
+    workspace (``spec_verify_tree_sample``: one workgroup per batch row).
     """
     B, N, V = target_logits.shape
     dev = target_logits.device
@@ -378,11 +391,18 @@ def verify_tree_sample(target_logits: torch.Tensor, draft_probs: torch.Tensor, n
     rows = isinstance(parents, torch.Tensor)
     par, D = _tree_parents(parents, B, N)
     path, toks, alen = _tree_outputs(out, B, D, dev)
-    fn = lib().spec_verify_tree_sample_rows if rows else lib().spec_verify_tree_sample
-    rc = fn(_dev(target_logits, "target_logits"), code, _dev(draft_probs, "draft_probs", torch.float32),
+    args = (_dev(target_logits, "target_logits"), code, _dev(draft_probs, "draft_probs", torch.float32),
             _dev(node_tokens, "node_tokens", torch.int32), _dev(uniforms, "uniforms", torch.float32), par, B, N, V,
-            float(temperature), int(top_k), path.data_ptr(), toks.data_ptr(), alen.data_ptr(), _stream(dev))
-    _check(rc, "spec_verify_tree_sample" + ("_rows" if rows else ""))
+            float(temperature), int(top_k), path.data_ptr(), toks.data_ptr(), alen.data_ptr())
+    name = "spec_verify_tree_sample" + ("_rows" if rows else "")
+    if workspace is False:
+        rc = getattr(lib(), name)(*args, _stream(dev))
+    else:
+        need = tree_sample_workspace_bytes(B, N)
+        wp, _ws = _workspace(need, dev, workspace)
+        name += "_ws"
+        rc = getattr(lib(), name)(*args, wp, need, _stream(dev))
+    _check(rc, name)
     return path, toks, alen
 
 

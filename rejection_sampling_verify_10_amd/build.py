@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspecverify.so")
 SOURCES = ["alpha.hip", "api.hip", "dense_tr.hip", "dense_walk.hip", "eagle2.hip", "kv_commit.hip", "lmhead.hip", "nucleus.hip", "rowstats.hip",
-           "topk.hip", "tree_sample.hip", "verify.hip"]
+           "topk.hip", "tree_cluster.hip", "tree_sample.hip", "verify.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

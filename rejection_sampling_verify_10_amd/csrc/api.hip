@@ -708,7 +708,31 @@ int spec_verify_tree_greedy(const void* target_logits, spec_dtype_t dtype, const
 static int tree_sample_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
                             const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
                             const int32_t* parents_rows, int B, int N, int V, float temperature, int top_k,
-                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream);
+                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                            size_t workspace_bytes, bool with_ws, void* hip_stream);
+
+// Exchange words of the clustered walk: [B][2N+2][G][kTcWords] words, then [B] counters.
+struct TcPlan {
+    unsigned long long* words;
+    unsigned* done;
+    int G, R;
+};
+static TcPlan plan_tree_cluster(Carver& c, int B, int N) {
+    TcPlan p{};
+    p.G = tree_cluster_members(B);
+    p.R = 2 * N + 2;
+    if (p.G < 2) return p;
+    p.words = c.take<unsigned long long>(static_cast<size_t>(B) * p.R * p.G * kTcWords);
+    p.done = c.take<unsigned>(static_cast<size_t>(B));
+    return p;
+}
+
+size_t spec_tree_sample_workspace_bytes(int B, int N) {
+    if (B < 1 || N < 1 || N > SPEC_MAX_NODES) return 0;
+    Carver c(nullptr);
+    plan_tree_cluster(c, B, N);
+    return (c.off + 255) & ~static_cast<size_t>(255);
+}
 
 int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
                             const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
@@ -716,7 +740,18 @@ int spec_verify_tree_sample(const void* target_logits, spec_dtype_t dtype, const
                             int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream) {
     if (!parents_host) return SPEC_EINVAL;
     return tree_sample_call(target_logits, dtype, draft_probs, node_tokens, uniforms, parents_host, nullptr, B, N,
-                            V, temperature, top_k, out_path, out_tokens, out_accept_len, hip_stream);
+                            V, temperature, top_k, out_path, out_tokens, out_accept_len, nullptr, 0, false, hip_stream);
+}
+
+int spec_verify_tree_sample_ws(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                               const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
+                               int B, int N, int V, float temperature, int top_k, int32_t* out_path,
+                               int32_t* out_tokens, int32_t* out_accept_len, void* workspace, size_t workspace_bytes,
+                               void* hip_stream) {
+    if (!parents_host) return SPEC_EINVAL;
+    return tree_sample_call(target_logits, dtype, draft_probs, node_tokens, uniforms, parents_host, nullptr, B, N,
+                            V, temperature, top_k, out_path, out_tokens, out_accept_len, workspace, workspace_bytes,
+                            true, hip_stream);
 }
 
 int spec_verify_tree_sample_rows(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
@@ -725,13 +760,25 @@ int spec_verify_tree_sample_rows(const void* target_logits, spec_dtype_t dtype, 
                                  int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream) {
     if (!parents || !aligned(parents, 4)) return SPEC_EINVAL;
     return tree_sample_call(target_logits, dtype, draft_probs, node_tokens, uniforms, nullptr, parents, B, N, V,
-                            temperature, top_k, out_path, out_tokens, out_accept_len, hip_stream);
+                            temperature, top_k, out_path, out_tokens, out_accept_len, nullptr, 0, false, hip_stream);
+}
+
+int spec_verify_tree_sample_rows_ws(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
+                                    const int32_t* node_tokens, const float* uniforms, const int32_t* parents, int B,
+                                    int N, int V, float temperature, int top_k, int32_t* out_path,
+                                    int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream) {
+    if (!parents || !aligned(parents, 4)) return SPEC_EINVAL;
+    return tree_sample_call(target_logits, dtype, draft_probs, node_tokens, uniforms, nullptr, parents, B, N, V,
+                            temperature, top_k, out_path, out_tokens, out_accept_len, workspace, workspace_bytes,
+                            true, hip_stream);
 }
 
 static int tree_sample_call(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,
                             const int32_t* node_tokens, const float* uniforms, const int32_t* parents_host,
                             const int32_t* parents_rows, int B, int N, int V, float temperature, int top_k,
-                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len, void* hip_stream) {
+                            int32_t* out_path, int32_t* out_tokens, int32_t* out_accept_len, void* workspace,
+                            size_t workspace_bytes, bool with_ws, void* hip_stream) {
     if (!target_logits || !draft_probs || !node_tokens || !uniforms || !out_path || !out_tokens ||
         !out_accept_len)
         return SPEC_EINVAL;
@@ -784,6 +831,24 @@ static int tree_sample_call(const void* target_logits, spec_dtype_t dtype, const
     ta.out_tokens = out_tokens;
     ta.out_accept_len = out_accept_len;
     ProfileScope prof;
+    if (with_ws) {
+        const int rc = check_workspace(workspace, workspace_bytes, spec_tree_sample_workspace_bytes(B, N));
+        if (rc) return rc;
+        if (tree_cluster_fits(B, N, V, target_logits, dtype, draft_probs, ta.transformed != 0)) {
+            // each batch row's walk shared by a cluster of workgroups
+            Carver c(workspace);
+            const TcPlan p = plan_tree_cluster(c, B, N);
+            TcArgs ca{};
+            ca.t = ta;
+            ca.words = p.words;
+            ca.done = p.done;
+            ca.G = p.G;
+            ca.R = p.R;
+            ca.spin_limit = spin_limit();
+            SV_TRY(launch_tree_cluster(ca, static_cast<hipStream_t>(hip_stream), prof.timing()));
+            return SPEC_OK;
+        }
+    }
     SV_TRY(launch_tree_sample(ta, static_cast<hipStream_t>(hip_stream), prof.timing()));
     return SPEC_OK;
 }

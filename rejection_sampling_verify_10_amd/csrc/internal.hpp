@@ -201,6 +201,23 @@ struct TreeSampleArgs {
     int32_t* out_accept_len;
 };
 
+// The sampled tree with each batch row's walk shared by a cluster of G
+// workgroups (tree_cluster.hip), exchanging per-slice sums through words.
+constexpr int kTcMaxG = 8;       // members per batch row
+constexpr int kTcWords = 8;      // 64-bit words per (batch row, round, member)
+struct TcArgs {
+    TreeSampleArgs t;
+    unsigned long long* words;   // [B][R][G][kTcWords], zero before and after a call
+    unsigned* done;              // [B] members finished, zero before and after a call
+    int G;                       // members per batch row
+    int L;                       // elements per member slice (set by the launcher)
+    int R;                       // exchange rounds per batch row (2N + 2)
+    int spin_limit;              // polls before a wait gives up
+};
+int tree_cluster_members(int B);   // G for a batch of B rows (< 2: no cluster)
+bool tree_cluster_fits(int B, int N, int V, const void* logits, int dtype, const float* q, bool transformed);
+hipError_t launch_tree_cluster(TcArgs a, hipStream_t s, Timing t = {});
+
 // EAGLE-2 draft-tree construction (eagle2.hip).
 constexpr int kExpandMax = 1024;    // children of one expansion layer (E * K)
 constexpr int kRerankMax = 1024;    // candidate nodes of one reranking

@@ -118,6 +118,33 @@ def test_tree_sample_argument_checks(L):
     assert call(big, N=65) == EUNSUPPORTED
 
 
+def test_tree_sample_ws_argument_checks(L):
+    """The workspace variants: the same argument checks, then the workspace (none is
+    needed for B > 128, where the cluster route does not apply)."""
+    par = (ctypes.c_int32 * 4)(-1, 0, 0, 1)
+    bad = (ctypes.c_int32 * 4)(-1, 0, 3, 1)
+    need = L.spec_tree_sample_workspace_bytes(2, 4)
+    assert need > 0 and need % 256 == 0
+    assert L.spec_tree_sample_workspace_bytes(128, 64) > 0
+    assert L.spec_tree_sample_workspace_bytes(129, 4) == 0
+    assert L.spec_tree_sample_workspace_bytes(2, 65) == 0
+    assert L.spec_tree_sample_workspace_bytes(0, 4) == 0
+
+    def call(p=par, N=4, B=2, V=1000, T=1.0, top_k=0, ws=FAKE, wsb=1 << 30):
+        return L.spec_verify_tree_sample_ws(FAKE, 1, FAKE, FAKE, FAKE, p, B, N, V, T, top_k, FAKE, FAKE, FAKE, ws, wsb,
+                                            None)
+    assert call(bad) == EINVAL
+    assert call(B=0) == EINVAL
+    assert call(T=0.0) == EINVAL
+    assert call(top_k=50) == EUNSUPPORTED
+    assert call(wsb=need - 1) == EWORKSPACE
+    assert call(ws=None) == EWORKSPACE
+    assert call(ws=FAKE + 8) == EWORKSPACE                  # not 256-byte aligned
+    rows = L.spec_verify_tree_sample_rows_ws
+    assert rows(FAKE, 1, FAKE, FAKE, FAKE, None, 2, 4, 1000, 1.0, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
+    assert rows(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 4, 1000, 1.0, 0, FAKE, FAKE, FAKE, FAKE, 16, None) == EWORKSPACE
+
+
 def test_tree_expand_and_rerank_argument_checks(L):
     def ex(**kw):
         a = dict(q=FAKE, nv=FAKE, B=2, E=3, V=1000, K=4, kn=5, ws=FAKE, wsb=1 << 30)

@@ -123,3 +123,48 @@ def test_noalloc_graph_replays(R, T, top_k, B, cid):
         torch.cuda.synchronize()
         assert same(got, want_g), f"eager call after replay {rep} differs"
     print(f"[graph] {REPLAYS} no-allocation replays match", flush=True)
+
+
+def test_tree_sample_ws_graph_replays(R):
+    """spec_verify_tree_sample_ws (each batch row's walk shared by a cluster of workgroups
+    exchanging words through the workspace) captured once and replayed: the words are left
+    zero by every call, so every replay reproduces the eager result."""
+    import torch
+    dev = torch.device("cuda")
+    ti, other = W.config(5, 90), W.config(5, 91)
+
+    def args(t):
+        return [to_torch(a) for a in (t.logits, t.draft_probs, t.node_tokens, t.uniforms)]
+
+    a0, a1 = args(ti), args(other)
+    B, N = ti.B, ti.N
+    par = ti.parents.tolist()
+    need = R.tree_sample_workspace_bytes(B, N)
+    ws, ws_other = R.new_workspace(need, dev), R.new_workspace(need, dev)
+    want = R.verify_tree_sample(*a0, par, ti.temperature, 0, workspace=R.new_workspace(need, dev))
+    want_other = R.verify_tree_sample(*a1, par, other.temperature, 0, workspace=R.new_workspace(need, dev))
+    D = want[0].shape[1] - 1
+    out = (torch.full((B, D + 1), -7, dtype=torch.int32, device=dev),
+           torch.full((B, D + 1), -7, dtype=torch.int32, device=dev),
+           torch.full((B,), -7, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    print(f"[case] tree-sample graph capture B={B} N={N}", flush=True)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            R.verify_tree_sample(*a0, par, ti.temperature, 0, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        for o in out:
+            o.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert same(out, want), f"replay {rep} differs from the eager call"
+        assert int(torch.count_nonzero(ws)) == 0
+        got = R.verify_tree_sample(*a1, par, other.temperature, 0, workspace=ws_other)
+        torch.cuda.synchronize()
+        assert same(got, want_other), f"eager call after replay {rep} differs"
+    print(f"[graph] {REPLAYS} tree-sample replays match", flush=True)

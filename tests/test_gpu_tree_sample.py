@@ -1,5 +1,9 @@
 """Parity of spec_verify_tree_sample with the CPU oracle, and its exact output law.
 
+Two routes: with a workspace (spec_verify_tree_sample_ws; for B <= 128 each batch
+row's walk is shared by a cluster of workgroups exchanging their sums through the
+workspace) and without one (one workgroup per batch row); the main cases run both.
+
 Paths, tokens and depths must equal the oracle's, except where the oracle's own
 margin for the decision that differs is below MARGIN (the tolerance rule of
 the chain tests); such cases are counted against the same 1e-4 budget.
@@ -29,10 +33,15 @@ def R():
     return R
 
 
-def gpu_tree_sample(R, ti):
+ROUTES = ["cluster", "single"]
+
+
+def gpu_tree_sample(R, ti, route="cluster", workspace=None):
     import torch
+    ws = False if route == "single" else workspace
     path, toks, alen = R.verify_tree_sample(to_torch(ti.logits), to_torch(ti.draft_probs), to_torch(ti.node_tokens),
-                                            to_torch(ti.uniforms), ti.parents.tolist(), ti.temperature, ti.top_k)
+                                            to_torch(ti.uniforms), ti.parents.tolist(), ti.temperature, ti.top_k,
+                                            workspace=ws)
     torch.cuda.synchronize()
     return path.cpu().numpy(), toks.cpu().numpy(), alen.cpu().numpy()
 
@@ -70,9 +79,9 @@ def compare(o, path, toks, alen, parents) -> Tally:
     return t
 
 
-def run_case(R, orc, ti, name) -> Tally:
-    print(f"[case] {name}: B={ti.B} N={ti.N} V={ti.V} T={ti.temperature} dtype={ti.dtype}", flush=True)
-    path, toks, alen = gpu_tree_sample(R, ti)
+def run_case(R, orc, ti, name, route="cluster") -> Tally:
+    print(f"[case] {name} ({route}): B={ti.B} N={ti.N} V={ti.V} T={ti.temperature} dtype={ti.dtype}", flush=True)
+    path, toks, alen = gpu_tree_sample(R, ti, route)
     o = orc.verify_tree_sample(ti.logits, ti.dtype, ti.draft_probs, ti.node_tokens, ti.uniforms, ti.parents,
                                ti.temperature, ti.top_k)
     t = compare(o, path, toks, alen, ti.parents)
@@ -81,11 +90,12 @@ def run_case(R, orc, ti, name) -> Tally:
     return t
 
 
-def test_workload5_full(R, orc):
-    """B=32, the 27-node tree, V=32000 bf16, T=1: the launch bench.py times."""
+@pytest.mark.parametrize("route", ROUTES)
+def test_workload5_full(R, orc, route):
+    """B=32, the 27-node tree, V=32000 bf16, T=1: the launch bench.py times (cluster route)."""
     tally = Tally()
     for seed in range(3):
-        tally.add(run_case(R, orc, W.config(5, seed), f"tree-sample seed {seed}"))
+        tally.add(run_case(R, orc, W.config(5, seed), f"tree-sample seed {seed}", route))
     tally.check()
 
 
@@ -95,19 +105,22 @@ def test_multipass_route(R, orc, monkeypatch, T):
     one-pass brackets do not hold): the same results."""
     monkeypatch.setenv("SPEC_VERIFY_TREE_ONEPASS", "0")
     ti = W.make_tree_sampled(32, 32000, temperature=T, config_id=5, seed=21)
-    run_case(R, orc, ti, f"multi-pass T={T}").check()
+    run_case(R, orc, ti, f"multi-pass T={T}", "single").check()
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("T", [0.7, 1.3])
-def test_transformed_full(R, orc, T):
+def test_transformed_full(R, orc, T, route):
     """Temperature applied to both distributions (q^(1/T) renormalised), full V."""
     ti = W.make_tree_sampled(32, 32000, temperature=T, config_id=5, seed=11)
-    run_case(R, orc, ti, f"tree-sample T={T}").check()
+    run_case(R, orc, ti, f"tree-sample T={T}", route).check()
 
 
-def test_many_small_cases(R, orc):
+@pytest.mark.parametrize("route", ROUTES)
+def test_many_small_cases(R, orc, route):
     """Small vocabularies (vector and scalar loads, f32 and bf16 rows), several shapes of
-    tree, many rows: the admissible-disagreement budget over all of them."""
+    tree, many rows: the admissible-disagreement budget over all of them (B = 48: clusters
+    of 5 workgroups, the slices of V = 1000 and 4104 uneven; V = 999 takes the single route)."""
     tally = Tally()
     shapes = {"eagle": W.EAGLE_TREE_PARENTS, "root": np.array([-1], np.int32),
               "path": np.arange(-1, 63, dtype=np.int32), "wide": np.array([-1] + [0] * 63, np.int32),
@@ -119,12 +132,14 @@ def test_many_small_cases(R, orc):
             seed += 1
             ti = W.make_tree_sampled(48, V, parents=parents, dtype=dtype, temperature=T, sigma=0.7,
                                      config_id=55, seed=seed)
-            tally.add(run_case(R, orc, ti, f"{name} V={V} T={T}"))
+            tally.add(run_case(R, orc, ti, f"{name} V={V} T={T}", route))
     tally.check()
 
 
-def test_error_rows(R, orc):
-    """E1-E5 as the walk consults rows: the oracle's error cases, on the GPU."""
+@pytest.mark.parametrize("route", ROUTES)
+def test_error_rows(R, orc, route):
+    """E1-E5 as the walk consults rows: the oracle's error cases, on the GPU (V = 40 over
+    clusters of 8: slices of 8 values, three members empty)."""
     rng = np.random.default_rng(83)
     parents = np.array([-1, 0, 0, 1, 2], np.int32)
     B, N, V = 10, 5, 40
@@ -162,7 +177,8 @@ def test_error_rows(R, orc):
     z[9, 0, 11] = np.inf                 # +inf at the root
     for T in (1.0, 0.7):
         ti = W.SampledTreeInputs(B, N, V, W.DTYPE_F32, T, 0, z, q, tok, u, parents)
-        path, toks, alen = gpu_tree_sample(R, ti)
+        print(f"[case] error rows T={T} ({route})", flush=True)
+        path, toks, alen = gpu_tree_sample(R, ti, route)
         o = orc.verify_tree_sample(z, W.DTYPE_F32, q, tok, u, parents, T, 0)
         assert np.array_equal(alen, o["accept_len"]), (T, alen, o["accept_len"])
         assert np.array_equal(path, o["path"]) and np.array_equal(toks, o["tokens"]), T
@@ -207,3 +223,42 @@ def test_gpu_output_law_is_the_target(R, tree, V, T):
         if reach[n] < 1e-6:
             continue
         assert np.allclose(law[n] / reach[n], lib_target(z[n], T, 0), atol=3e-6), n
+
+
+def test_cluster_workspace_left_zero_and_reused(R, orc):
+    """The exchange words are zero after every call, so one workspace serves a series of
+    calls of different shapes (B = 1, 5, 32, 128: clusters of 8, 8, 8 and 2)."""
+    import torch
+    ws = R.new_workspace(R.tree_sample_workspace_bytes(128, 27), torch.device("cuda"))
+    for B, seed in ((32, 1), (1, 2), (5, 3), (128, 4), (32, 5)):
+        ti = W.make_tree_sampled(B, 32000, config_id=57, seed=seed)
+        print(f"[case] reused workspace B={B}", flush=True)
+        path, toks, alen = gpu_tree_sample(R, ti, "cluster", ws)
+        o = orc.verify_tree_sample(ti.logits, ti.dtype, ti.draft_probs, ti.node_tokens, ti.uniforms, ti.parents,
+                                   ti.temperature, ti.top_k)
+        compare(o, path, toks, alen, ti.parents).check()
+        assert int(torch.count_nonzero(ws)) == 0, f"words left behind after B={B}"
+
+
+def test_cluster_forced_timeout(R, orc, monkeypatch):
+    """A spin limit of 0 (read from the host) makes a member give up on words not yet
+    there: such rows report SPEC_ROW_TIMED_OUT with -1 outputs, never a wrong token, and
+    the launch ends.  The words are still cleared, so the next call on the workspace
+    matches the oracle."""
+    import torch
+    ti = W.make_tree_sampled(32, 32000, config_id=58, seed=0)
+    ws = R.new_workspace(R.tree_sample_workspace_bytes(32, 27), torch.device("cuda"))
+    o = orc.verify_tree_sample(ti.logits, ti.dtype, ti.draft_probs, ti.node_tokens, ti.uniforms, ti.parents,
+                               ti.temperature, ti.top_k)
+    monkeypatch.setenv("SPEC_VERIFY_SPIN_LIMIT", "0")
+    print("[case] tree cluster, spin limit 0", flush=True)
+    path, toks, alen = gpu_tree_sample(R, ti, "cluster", ws)
+    late = alen == -2
+    print(f"[tree-sample] timed-out rows: {int(late.sum())} of {ti.B}", flush=True)
+    assert np.all(path[late] == -1) and np.all(toks[late] == -1)
+    ok = ~late
+    compare({k: v[ok] for k, v in o.items()}, path[ok], toks[ok], alen[ok], ti.parents).check()
+    assert int(torch.count_nonzero(ws)) == 0
+    monkeypatch.delenv("SPEC_VERIFY_SPIN_LIMIT")
+    path, toks, alen = gpu_tree_sample(R, ti, "cluster", ws)
+    compare(o, path, toks, alen, ti.parents).check()
