@@ -83,7 +83,8 @@
  *     first; by default the walk when B*(K+1) > 1536 or V < 4096.  Results
  *     are the same either way.
  *     SPEC_VERIFY_SPIN_LIMIT (an integer in [0, 65536]) lowers the number of
- *     polls a top-k chain finisher makes before it gives up (tests of the
+ *     polls a top-k chain finisher, or a member of a sampled tree's cluster
+ *     (spec_verify_tree_sample_ws), makes before it gives up (tests of the
  *     timed-out path); read on every call.
  */
 #ifndef SPEC_VERIFY_H
@@ -374,10 +375,13 @@ int spec_verify_tree_sample_rows(const void* target_logits, spec_dtype_t dtype, 
  * The workspace must be zero-filled before its first use; every call leaves
  * it zero, so it can be reused, including by replays of a captured graph.
  * Calls that overlap on one workspace race.  The members of a batch row wait
- * for one another's words; this relies on workgroups being dispatched in
- * order (a row's members are consecutive), as the top-k chain does.  A wait
- * that exceeds the spin limit (SPEC_VERIFY_SPIN_LIMIT, above) gives up: that
- * batch row's accept_len is SPEC_ROW_TIMED_OUT and its outputs -1.
+ * for one another's words.  A row's members are consecutive workgroups, so they
+ * sit on different XCDs, and each XCD dispatches its workgroups in grid order:
+ * on every XCD the rows already dispatched form a prefix, and every row below
+ * the shortest prefix has all its members running and finishes, so progress
+ * relies on that order, as the top-k chain's hand-over does.  A wait that
+ * exceeds the spin limit (SPEC_VERIFY_SPIN_LIMIT, above) gives up: that batch
+ * row's accept_len is SPEC_ROW_TIMED_OUT and its outputs -1.
  */
 size_t spec_tree_sample_workspace_bytes(int B, int N);
 int spec_verify_tree_sample_ws(const void* target_logits, spec_dtype_t dtype, const float* draft_probs,

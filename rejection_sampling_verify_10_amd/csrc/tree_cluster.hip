@@ -33,9 +33,11 @@
 // atomic) and a zero word is not yet written.  A member writes its words, then
 // polls the other members' words of the same round.  The last member of a row
 // to finish zeroes the row's words, so every call finds them zero.  Members of
-// a row are consecutive workgroups; with workgroups dispatched in order and at
-// least G of them resident, every member of a row runs, so every wait ends.
-// A wait that passes the spin limit ends the row as timed out.
+// a row are G <= 8 consecutive workgroups, so they sit on different XCDs, and
+// each XCD dispatches its workgroups in grid order: on every XCD the rows
+// dispatched form a prefix, and every row below the shortest prefix has all
+// its members running, so it finishes and makes room.  A wait that passes the
+// spin limit ends the row as timed out.
 
 #include <math.h>
 
