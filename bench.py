@@ -47,7 +47,7 @@ WORKLOADS = {
     0: dict(name="chain verify B=1 K=4 V=1000, fp32 target logits, fp32 draft probs, T=1, no top-k",
             kernel="dense_walk_kernel", copies=1, oracle_rows=1, dtype="f32 in, f32 exp, f64 draw"),
     1: dict(name="chain verify B=8 K=5 V=32000, bf16 target logits, fp32 draft probs, T=1, no top-k",
-            kernel="dense_row_kernel", copies=64, oracle_rows=8, dtype="bf16 in, f32 exp, f64 draw"),
+            kernel="draw_part_kernel", copies=64, oracle_rows=8, dtype="bf16 in, f32 exp, f64 draw"),
     2: dict(name="chain verify B=64 K=7 V=128256, bf16 target logits, fp32 draft probs, T=0.7, top_k=50",
             kernel="topk_chunk_kernel", copies=4, oracle_rows=64, single_kernel=True,
             dtype="bf16/f32 in, f32 select, f32 probabilities"),
@@ -192,8 +192,10 @@ def algorithmic_bytes(workload: int, B: int, K: int, V: int, top_k: int, accept_
         return B * (K + 1) * V * 2 + B * K * V * 4
     j = [K] * B if accept_len is None else [int(a) for a in accept_len]
     if workload == 1:
-        # the all-rows route's draw kernel: target row j of each batch row and the draft row j
-        # when j < K, plus the row statistics of rows 0..j and the tokens and uniforms read
+        # the all-rows route's draw, split over several workgroups per batch row: target row j
+        # of each batch row and the draft row j when j < K, plus the row statistics of rows
+        # 0..j and the tokens and uniforms read (the slices' partial sums, a few KB per batch
+        # row written and read back by the finishing launch, are not counted)
         drafts = sum(1 for a in j if 0 <= a < K)
         return sum(1 for a in j if a >= 0) * V * esz + drafts * V * 4 + B * ((K + 1) * 24 + K * 8 + (K + 1) * 4)
     # the walk: target rows 0..j of each batch row once, the draft row j when j < K, the

@@ -171,6 +171,7 @@ struct ChainPlan {
     uint32_t* qflags;
     TopkLists tk;
     unsigned long long* recw;
+    unsigned char* split;       // dense: the split draw's partial sums (dense_split_bytes)
 };
 
 // Relative half-width of the brackets the dense draw puts around the row
@@ -222,8 +223,18 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
         }
         p.nt = c.take<NucleusRow>(Rt);
         p.nd = c.take<NucleusRow>(Rd);
+        p.split = c.take<unsigned char>(dense_split_bytes(B, V));
     }
     return p;
+}
+
+// The all-rows route's draw split over several workgroups per batch row (rows of
+// the split's partial sums carved from `split`), unless the environment variable
+// SPEC_VERIFY_DENSE_SPLIT is 0, which keeps one workgroup per batch row.
+void plan_dense_split(ChainArgs& ca, unsigned char* split, int B, int V) {
+    const char* env = getenv("SPEC_VERIFY_DENSE_SPLIT");
+    const int S = (env && !strcmp(env, "0")) ? 1 : dense_split_slices(B, V, ca.transformed != 0);
+    if (S > 1) dense_split_plan(ca, split, B, V, S);
 }
 
 // The fused LM-head chain: per-unit candidates, then the top-k chain's lists
@@ -552,6 +563,7 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
     } else if (!ca.transformed) {
         // every target row's statistics at once, then the tests and the draw per batch row
         ca.st = p.st;
+        plan_dense_split(ca, p.split, B, V);
         RowStatsArgs ra =
             rowstats_args(target_logits, dtype, V, K + 1, K + 1, B, false, temperature, draft_tokens, K, p.st);
         SV_TRY(launch_rowstats(ra, s));
@@ -565,6 +577,7 @@ static int chain_call(const void* target_logits, spec_dtype_t dtype, const float
         SV_TRY(launch_power_sums(pa, s));
         ca.qsum = p.qsum;
         ca.qflags = p.qflags;
+        plan_dense_split(ca, p.split, B, V);
         SV_TRY(launch_chain_dense(ca, dense_bracket(true), s));
     }
     return SPEC_OK;

@@ -470,57 +470,61 @@ __device__ __forceinline__ void draw_emit(const ChainArgs& a, int b, int j, cons
     }
 }
 
-// The final draw of batch row b (one workgroup): sm.j / sm.err set, sm.tbl
-// built, sm.n_list = sm.qbad = 0, all visible after a barrier; (m_j, Zp_ap):
-// the maximum and approximate normaliser of target row j.
-template <int DT, bool VEC, bool TR, bool TAB>
-__device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bracket, const ExpConsts& ek,
-                                           RowSmem& sm, double* dyn_lds, float m_j, double Zp_row) {
-    static_assert(!TAB || DT == 1, "the exponential table is for bf16 logits");
+// The draw of batch row b from row j (j < K: the residual max(0, p'_j - q'_j);
+// j = K: p'_K), around the row statistics' maximum m_j and normaliser Zp_row.
+struct DrawCtx {
+    int j, C, C_full, nslots;
+    bool res;
+    const char* zr;
+    const float* qr;
+    long qrow;
+    ExpArg g;
+    double Zp_ap, Zq_ap, iz, iq, tol2;
+};
+template <int DT, bool TR>
+__device__ __forceinline__ DrawCtx draw_ctx(const ChainArgs& a, int b, int j, double bracket, const ExpConsts& ek,
+                                            float m_j, double Zp_row) {
     const int K = a.K, V = a.V;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
-    const int C = (V + kDenseChunk - 1) / kDenseChunk;
-    const int C_full = V / kDenseChunk;              // chunks wholly inside the row
-    const int nslots = dense_slots(C);
-    double* etab = dyn_lds;                          // TAB: [kTabSize] exponentials
-    double* pr = dyn_lds + (TAB ? kTabSize : 0);     // [C][nslots]: R (residual rows) or E
-    float* pp = reinterpret_cast<float*>(pr + static_cast<long>(C) * nslots);        // [C][nslots]: P
-    const long rbase = static_cast<long>(b) * (K + 1);
-    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
-    const int j = sm.j;
-    auto fail_row = [&]() {
-        for (int t = tid; t <= K; t += kThreads) a.out_tokens[rbase + t] = -1;
-        if (tid == 0) a.out_accept_len[b] = -1;
-        if (diag)
-            for (int t = tid; t < 2 * K + 2; t += kThreads) diag[t] = NAN;
-    };
-    if (sm.err) { fail_row(); return; }
-
-    const bool res = j < K;
-    const long zrow = rbase + j;
-    const long qrow = static_cast<long>(b) * K + (res ? j : 0);
-    const char* zr = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
-    const float* qr = a.q + qrow * V;
-    const double* tbl = sm.tbl;
-    const ExpArg g = exp_arg(static_cast<double>(m_j), a.invT, ek);
-    const double Zp_ap = Zp_row;
-    const double Zq_ap = (TR && res) ? a.qsum[qrow] : 1.0;
-    const double iz = 1.0 / Zp_ap, iq = TR ? 1.0 / Zq_ap : 1.0;
+    DrawCtx d;
+    d.j = j;
+    d.C = (V + kDenseChunk - 1) / kDenseChunk;
+    d.C_full = V / kDenseChunk;                      // chunks wholly inside the row
+    d.nslots = dense_slots(d.C);
+    d.res = j < K;
+    const long zrow = static_cast<long>(b) * (K + 1) + j;
+    d.qrow = static_cast<long>(b) * K + (d.res ? j : 0);
+    d.zr = static_cast<const char*>(a.logits) + zrow * V * Elem<DT>::kBytes;
+    d.qr = a.q + d.qrow * V;
+    d.g = exp_arg(static_cast<double>(m_j), a.invT, ek);
+    d.Zp_ap = Zp_row;
+    d.Zq_ap = (TR && d.res) ? a.qsum[d.qrow] : 1.0;
+    d.iz = 1.0 / d.Zp_ap;
+    d.iq = TR ? 1.0 / d.Zq_ap : 1.0;
     // |d| > tol*(e*iz + w') (w' = w*iq, tol >= delta/(1 - delta) plus rounding room)
     // fixes the sign of the residual over the brackets; since e*iz = d + w' this
     // holds whenever |d| > tol2*w'.
     const double tol = bracket * (1.0 + 2.0 * bracket) + 1e-12;
-    const double tol2 = 2.0 * tol / (1.0 - tol);
-    if constexpr (TAB) {
-        build_exp_table(etab, g, tbl, ek);
-        __syncthreads();
-    }
+    d.tol2 = 2.0 * tol / (1.0 - tol);
+    return d;
+}
 
-    // ---- one pass over row j ----
-    double sq_tot = 0.0;                   // transformed draft: sum w over the thread's elements
-    double se_tot = 0.0;                   // residual rows: sum e over the thread's elements
-    float zmax = -INFINITY;                // bonus rows: the maximum and any NaN or +inf
-    bool zbad = false;
+// The draw's pass over chunks [c_begin, c_end) of row j: per chunk the slot partials
+// pr (R on residual rows, else E) and pp (P) at [c][slot]; per thread se_tot (sum
+// e, residual rows), sq_tot (sum w, transformed draft), zmax / zbad (bonus rows);
+// undecided elements into sm's list, a bad draft value into sm.qbad.
+template <int DT, bool VEC, bool TR, bool TAB>
+__device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, int c_begin, int c_end,
+                                          const double* etab, const double* tbl, const ExpConsts& ek, double* pr,
+                                          float* pp, RowSmem& sm, double& se_tot, double& sq_tot, float& zmax,
+                                          bool& zbad) {
+    const int V = a.V;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
+    const int C = d.C, C_full = d.C_full, nslots = d.nslots;
+    const bool res = d.res;
+    const char* zr = d.zr;
+    const float* qr = d.qr;
+    const ExpArg g = d.g;
+    const double iz = d.iz, iq = d.iq, tol2 = d.tol2;
     auto body = [&](auto res_tag) {
         constexpr bool RES = decltype(res_tag)::value;
         using Buf = Raw8<DT>[kSub];
@@ -643,20 +647,21 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
         // last chunk comes after.
         constexpr int kRing = ring_depth<VEC, TR>();
         Buf ring[kRing];
-        if (C_full > 0) {
+        const int f_end = min(c_end, C_full);          // full chunks of the range: [c_begin, f_end)
+        if (c_begin < f_end) {
 #pragma unroll
-            for (int r = 0; r < kRing - 1; ++r) load(min(r, C_full - 1), ring[r], std::false_type{});
+            for (int r = 0; r < kRing - 1; ++r) load(min(c_begin + r, f_end - 1), ring[r], std::false_type{});
         }
 #pragma unroll 1
-        for (int c = 0; c < C_full; c += kRing) {
+        for (int c = c_begin; c < f_end; c += kRing) {
 #pragma unroll
             for (int st = 0; st < kRing; ++st) {
-                load(min(c + st + kRing - 1, C_full - 1), ring[(st + kRing - 1) % kRing], std::false_type{});
+                load(min(c + st + kRing - 1, f_end - 1), ring[(st + kRing - 1) % kRing], std::false_type{});
                 __builtin_amdgcn_sched_barrier(0);     // keep the prefetch ahead of the compute
-                if (st == 0 || c + st < C_full) compute(c + st, ring[st]);
+                if (st == 0 || c + st < f_end) compute(c + st, ring[st]);
             }
         }
-        if (C_full < C) {
+        if (C_full < C && c_end == C) {
             load(C_full, ring[0], std::true_type{});
             compute(C_full, ring[0]);
         }
@@ -664,6 +669,35 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
     if (res) body(std::true_type{});
     else body(std::false_type{});
     __syncthreads();
+}
+
+// Everything after the pass: the bracket check (or exact sums), the chunk weights and
+// the draw.  pr / pp hold every chunk's slot partials; se_tot, sq_tot, zmax, zbad are
+// this thread's parts of the pass's sums.
+template <int DT, bool VEC, bool TR>
+__device__ __forceinline__ void draw_finish(const ChainArgs& a, int b, const DrawCtx& d, double bracket,
+                                            const ExpConsts& ek, RowSmem& sm, const double* pr, const float* pp,
+                                            float m_j, double se_tot, double sq_tot, float zmax, bool zbad) {
+    const int K = a.K;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
+    const int j = d.j, C = d.C, nslots = d.nslots;
+    const bool res = d.res;
+    const char* zr = d.zr;
+    const float* qr = d.qr;
+    const long qrow = d.qrow;
+    const double* tbl = sm.tbl;
+    const ExpArg g = d.g;
+    const double Zp_ap = d.Zp_ap, Zq_ap = d.Zq_ap, iz = d.iz, iq = d.iq, tol2 = d.tol2;
+    (void)tol2;
+    (void)qrow;
+    const long rbase = static_cast<long>(b) * (K + 1);
+    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
+    auto fail_row = [&]() {
+        for (int t = tid; t <= K; t += kThreads) a.out_tokens[rbase + t] = -1;
+        if (tid == 0) a.out_accept_len[b] = -1;
+        if (diag)
+            for (int t = tid; t < 2 * K + 2; t += kThreads) diag[t] = NAN;
+    };
 
 
     double Zp = 0.0, Zq = 1.0, S = 0.0;
@@ -746,6 +780,40 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
     draw_emit<DT, VEC, TR>(a, b, j, zr, qr, C, gd, tbl, ek, residual, residual ? S : Zp, S, invZp, invZq, sm);
 }
 
+
+// The final draw of batch row b (one workgroup): sm.j / sm.err set, sm.tbl
+// built, sm.n_list = sm.qbad = 0, all visible after a barrier; (m_j, Zp_ap):
+// the maximum and approximate normaliser of target row j.
+template <int DT, bool VEC, bool TR, bool TAB>
+__device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bracket, const ExpConsts& ek,
+                                           RowSmem& sm, double* dyn_lds, float m_j, double Zp_row) {
+    static_assert(!TAB || DT == 1, "the exponential table is for bf16 logits");
+    const int K = a.K;
+    const int tid = threadIdx.x;
+    if (sm.err) {
+        const long rbase = static_cast<long>(b) * (K + 1);
+        float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
+        for (int t = tid; t <= K; t += kThreads) a.out_tokens[rbase + t] = -1;
+        if (tid == 0) a.out_accept_len[b] = -1;
+        if (diag)
+            for (int t = tid; t < 2 * K + 2; t += kThreads) diag[t] = NAN;
+        return;
+    }
+    const DrawCtx d = draw_ctx<DT, TR>(a, b, sm.j, bracket, ek, m_j, Zp_row);
+    double* etab = dyn_lds;                          // TAB: [kTabSize] exponentials
+    double* pr = dyn_lds + (TAB ? kTabSize : 0);     // [C][nslots]: R (residual rows) or E
+    float* pp = reinterpret_cast<float*>(pr + static_cast<long>(d.C) * d.nslots);        // [C][nslots]: P
+    if constexpr (TAB) {
+        build_exp_table(etab, d.g, sm.tbl, ek);
+        __syncthreads();
+    }
+    double se_tot = 0.0, sq_tot = 0.0;
+    float zmax = -INFINITY;
+    bool zbad = false;
+    draw_pass<DT, VEC, TR, TAB>(a, d, 0, d.C, etab, sm.tbl, ek, pr, pp, sm, se_tot, sq_tot, zmax, zbad);
+    draw_finish<DT, VEC, TR>(a, b, d, bracket, ek, sm, pr, pp, m_j, se_tot, sq_tot, zmax, zbad);
+}
+
 __device__ __forceinline__ void init_draw_smem(RowSmem& sm) {
     for (int t = threadIdx.x; t < kTableSize; t += kThreads) sm.tbl[t] = exp2(static_cast<double>(t) * (1.0 / kTableSize));
     if (threadIdx.x == 0) { sm.n_list = 0; sm.qbad = 0; sm.zbad = 0; }
@@ -769,6 +837,138 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_ke
     __syncthreads();
     const long zrow = static_cast<long>(b) * (a.K + 1) + sm.j;
     final_draw<DT, VEC, TR, TAB>(a, b, bracket, ek, sm, dyn_lds, a.st.m[zrow], a.st.Z[zrow]);
+}
+
+// ---- the draw split over several workgroups per batch row (all-rows route) ----
+//
+// With the statistics of every row precomputed, a batch row's draw is one pass
+// over its row j plus a short finish; a small batch then leaves most CUs idle while
+// B workgroups draw.  The split: slice s of S workgroups of the row runs the ratio
+// tests itself (a few gathers), takes chunks [s*P, (s+1)*P) of the pass and stores
+// their slot partials and its own sums and undecided elements; a second launch, one
+// workgroup per row, gathers them and finishes exactly as the single workgroup does.
+
+struct SliceRec {
+    double E, Q;            // sums of e (residual rows) and of the draft weights (transformed)
+    float zmax;             // bonus rows: the slice's maximum logit
+    uint32_t flags;         // bit 0: a bad draft value; bit 1: a NaN or +inf logit
+    int n;                  // undecided elements found (more than kListCap: overflow)
+    int32_t li[kListCap];
+    double le[kListCap], lw[kListCap];
+};
+__host__ __device__ inline int split_chunks(int V) { return (V + kDenseChunk - 1) / kDenseChunk; }
+
+template <int DT, bool VEC, bool TR>
+__global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void draw_part_kernel(ChainArgs a, double bracket,
+                                                                                     ExpConsts ek) {
+    __shared__ RowSmem sm;
+    const int s = blockIdx.x, b = blockIdx.y, S = a.split_S;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
+    if (tid < kWave) {
+        int j;
+        bool err;
+        first_reject<TR>(a, b, nullptr, j, err);
+        if (tid == 0) { sm.j = j; sm.err = err; }
+    }
+    init_draw_smem(sm);
+    __syncthreads();
+    if (sm.err) return;                              // the finish writes the error row
+    const long zrow = static_cast<long>(b) * (a.K + 1) + sm.j;
+    const DrawCtx d = draw_ctx<DT, TR>(a, b, sm.j, bracket, ek, a.st.m[zrow], a.st.Z[zrow]);
+    const int per = (d.C + S - 1) / S;
+    const int c0 = min(d.C, s * per), c1 = min(d.C, c0 + per);
+    double* pr = a.split_pr + static_cast<long>(b) * d.C * d.nslots;
+    float* pp = a.split_pp + static_cast<long>(b) * d.C * d.nslots;
+    double se = 0.0, sq = 0.0;
+    float zmax = -INFINITY;
+    bool zbad = false;
+    if (c0 < c1) draw_pass<DT, VEC, TR, false>(a, d, c0, c1, nullptr, sm.tbl, ek, pr, pp, sm, se, sq, zmax, zbad);
+    se = block_sum(se, sm.red);
+    if (TR) sq = block_sum(sq, sm.red);
+    const float wz = wave_max(zmax);
+    const bool wb = __ballot(zbad) != 0ull;
+    __syncthreads();
+    if (lane == 0) { sm.wmax[wid] = wz; if (wb) atomicOr(&sm.zbad, 1u); }
+    __syncthreads();
+    SliceRec* rec = reinterpret_cast<SliceRec*>(a.split_rec) + static_cast<long>(b) * kSplitMax + s;
+    const int n = sm.n_list;
+    if (tid == 0) {
+        float zm = sm.wmax[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) zm = fmaxf(zm, sm.wmax[w]);
+        rec->E = se;
+        rec->Q = sq;
+        rec->zmax = zm;
+        rec->flags = (sm.qbad ? 1u : 0u) | (sm.zbad ? 2u : 0u);
+        rec->n = n;
+    }
+    for (int t = tid; t < min(n, kListCap); t += kThreads) {
+        rec->li[t] = sm.li[t];
+        rec->le[t] = sm.le[t];
+        rec->lw[t] = sm.lw[t];
+    }
+}
+
+template <int DT, bool VEC, bool TR>
+__global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void draw_combine_kernel(ChainArgs a, double bracket,
+                                                                                        ExpConsts ek) {
+    __shared__ RowSmem sm;
+    extern __shared__ double dyn_lds[];
+    const int b = blockIdx.x, S = a.split_S;
+    const int K = a.K, tid = threadIdx.x;
+    float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
+    if (tid < kWave) {
+        int j;
+        bool err;
+        first_reject<TR>(a, b, diag, j, err);
+        if (tid == 0) { sm.j = j; sm.err = err; }
+    }
+    init_draw_smem(sm);
+    __syncthreads();
+    if (sm.err) {
+        const long rbase = static_cast<long>(b) * (K + 1);
+        for (int t = tid; t <= K; t += kThreads) a.out_tokens[rbase + t] = -1;
+        if (tid == 0) a.out_accept_len[b] = -1;
+        if (diag)
+            for (int t = tid; t < 2 * K + 2; t += kThreads) diag[t] = NAN;
+        return;
+    }
+    const long zrow = static_cast<long>(b) * (K + 1) + sm.j;
+    const float m_j = a.st.m[zrow];
+    const DrawCtx d = draw_ctx<DT, TR>(a, b, sm.j, bracket, ek, m_j, a.st.Z[zrow]);
+    const int ns = d.C * d.nslots;
+    double* pr = dyn_lds;
+    float* pp = reinterpret_cast<float*>(pr + ns);
+    const double* gpr = a.split_pr + static_cast<long>(b) * ns;
+    const float* gpp = a.split_pp + static_cast<long>(b) * ns;
+    for (int t = tid; t < ns; t += kThreads) {
+        pr[t] = gpr[t];
+        pp[t] = gpp[t];
+    }
+    const SliceRec* rec = reinterpret_cast<const SliceRec*>(a.split_rec) + static_cast<long>(b) * kSplitMax;
+    // every slice's sums as one thread's part; the lists in slice order
+    const double se = tid < S ? rec[tid].E : 0.0;
+    const double sq = tid < S ? rec[tid].Q : 0.0;
+    const float zmax = tid < S ? rec[tid].zmax : -INFINITY;
+    const bool zbad = tid < S && (rec[tid].flags & 2u) != 0u;
+    if (tid < S && (rec[tid].flags & 1u)) atomicOr(&sm.qbad, 1u);
+    if (tid == 0) {
+        int n = 0;
+        for (int s = 0; s < S; ++s) n += rec[s].n;
+        sm.n_list = n;
+    }
+    __syncthreads();
+    if (sm.n_list <= kListCap && tid < S) {
+        int off = 0;
+        for (int s = 0; s < tid; ++s) off += rec[s].n;
+        for (int t = 0; t < rec[tid].n; ++t) {
+            sm.li[off + t] = rec[tid].li[t];
+            sm.le[off + t] = rec[tid].le[t];
+            sm.lw[off + t] = rec[tid].lw[t];
+        }
+    }
+    __syncthreads();
+    draw_finish<DT, VEC, TR>(a, b, d, bracket, ek, sm, pr, pp, m_j, se, sq, zmax, zbad);
 }
 
 // ---- the walk: statistics of target rows 0, 1, ... until the first rejection ----
@@ -1027,6 +1227,16 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, false>())) void dense_wal
 template <int DT, bool VEC, bool TR>
 hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s, Timing t) {
     const int C = (a.V + kDenseChunk - 1) / kDenseChunk;
+    if (a.split_S > 1) {
+        launch_timed(t, draw_part_kernel<DT, VEC, TR>, dim3(a.split_S, a.B), dim3(kThreads), 0u, s, a, bracket,
+                     exp_consts());
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const size_t lds = static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float));
+        launch_timed(Timing{}, draw_combine_kernel<DT, VEC, TR>, dim3(a.B), dim3(kThreads), static_cast<unsigned>(lds),
+                     s, a, bracket, exp_consts());
+        return hipGetLastError();
+    }
     if constexpr (DT == 1 && VEC && !TR) {
         if (C <= kTabMaxChunks) {
             launch_timed(t, dense_row_kernel<DT, VEC, TR, true>, dim3(a.B), dim3(kThreads),
@@ -1069,6 +1279,41 @@ hipError_t launch_chain_walk(const ChainArgs& a, double bracket, hipStream_t s, 
 #endif
 
 #if SV_DENSE_TR
+size_t dense_split_bytes(int B, int V) {
+    const int C = split_chunks(V);
+    const size_t per = static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float)) +
+                       kSplitMax * sizeof(SliceRec);
+    return static_cast<size_t>(B) * per + 2 * 256;
+}
+void dense_split_plan(ChainArgs& a, unsigned char* base, int B, int V, int S) {
+    const int C = split_chunks(V);
+    const size_t slots = static_cast<size_t>(C) * dense_slots(C);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        off = (off + 255) & ~static_cast<size_t>(255);
+        unsigned char* p = base + off;
+        off += bytes;
+        return p;
+    };
+    a.split_pr = reinterpret_cast<double*>(take(static_cast<size_t>(B) * slots * sizeof(double)));
+    a.split_pp = reinterpret_cast<float*>(take(static_cast<size_t>(B) * slots * sizeof(float)));
+    a.split_rec = take(static_cast<size_t>(B) * kSplitMax * sizeof(SliceRec));
+    a.split_S = S;
+}
+// Enough slices to put about two workgroups on every CU, at least one chunk each.
+// Measured (K = 8, V = 128256; µs per call, split / one workgroup per row): T = 1:
+// B = 32 48.0 / 60.2, B = 64 62.8 / 72.7, B = 96 84.7 / 86.0, B = 128 99.4 / 97.8;
+// transformed (T = 0.7): B = 64 369 / 546, B = 128 489 / 604, B = 256 721 / 706.
+// Larger batches keep one workgroup per row (their draws already fill the GPU).
+int dense_split_slices(int B, int V, bool transformed) {
+    if (B > (transformed ? 160 : 64)) return 1;
+    const int C = split_chunks(V);
+    int S = (512 + B - 1) / B;
+    if (S > C) S = C;
+    if (S > kSplitMax) S = kSplitMax;
+    return S < 1 ? 1 : S;
+}
+
 hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s, Timing t) {
     const int esz = a.dtype ? 2 : 4;
     const bool vec = vec_ok(a.logits, a.V, esz) && vec_ok(a.q, a.V, 4);

@@ -100,6 +100,12 @@ struct ChainArgs {
     const uint32_t* qflags;
     TopkLists tk;           // top-k path
     unsigned long long* recw;   // top-k chain: [B][K+1][kRecWords] position record words, zero between calls
+    // dense all-rows route with each batch row's draw split over split_S workgroups
+    // (0: one workgroup draws), their partial sums in the workspace
+    double* split_pr;           // [B][chunks][slots]
+    float* split_pp;            // [B][chunks][slots]
+    unsigned char* split_rec;   // [B][kSplitMax] slice records
+    int split_S;
     int32_t* out_tokens;
     int32_t* out_accept_len;
     float* out_diag;
@@ -282,6 +288,14 @@ hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
 // bracket: relative half-width of the brackets put around the row statistics'
 // normalisers (any value gives the same result; it sets how often the slow path runs)
 hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s, Timing t = {});   // statistics precomputed
+// The dense draw split over several workgroups per batch row: at most kSplitMax slices
+// of a row; the workspace bytes of the split for B batch rows of V, and the slice count
+// the launch uses (1: no split).
+constexpr int kSplitMax = 16;
+size_t dense_split_bytes(int B, int V);
+int dense_split_slices(int B, int V, bool transformed);
+// Points a's split fields into `base` (dense_split_bytes(B, V) bytes) for S slices.
+void dense_split_plan(ChainArgs& a, unsigned char* base, int B, int V, int S);
 // T == 1 without top-k: the whole chain (row statistics of the rows the walk
 // reaches, tests, final draw) in one launch.
 hipError_t launch_chain_walk(const ChainArgs& a, double bracket, hipStream_t s, Timing t = {});

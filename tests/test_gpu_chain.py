@@ -91,6 +91,23 @@ def test_greedy_chain_at_v128256(R, orc):
     check(R, orc, W.with_transform(W.config(4, 5, B=16), temperature=0.0, top_k=0), "greedy V=128256 c4 rows")
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("dtype", [1, 0])
+def test_maximum_vocabulary(R, orc, monkeypatch, dtype):
+    """V = 2^20, the largest vocabulary the library accepts (SPEC_MAX_V), in every chain mode:
+    the dense walk and the all-rows route, a transformed draft, top-k (the most selection
+    chunks a row can have: 19 per bf16 target row, 38 per draft row) and greedy."""
+    V = 1 << 20
+    base = W.make_chain(3, 2, V, dtype=dtype, temperature=1.0, top_k=0, sigma=W.sigma_const(0.7),
+                        config_id=94, seed=dtype)
+    for path in ("walk", "rows"):
+        monkeypatch.setenv("SPEC_VERIFY_DENSE_PATH", path)
+        check(R, orc, base, f"V=2^20 dtype={dtype} T=1 via {path}")
+    monkeypatch.delenv("SPEC_VERIFY_DENSE_PATH")
+    for T, k in [(0.8, 0), (0.7, 50), (0.0, 0)]:
+        check(R, orc, W.with_transform(base, temperature=T, top_k=k), f"V=2^20 dtype={dtype} T={T} k={k}")
+
+
 # ------------------------------------------------------------------ modes and shapes
 
 @pytest.mark.parametrize("T,top_k", [(0.0, 0), (0.5, 0), (1.7, 0), (1.0, 20), (0.7, 64), (1.3, 1)])
@@ -258,6 +275,42 @@ def test_dense_draw_bracket_widths(R, orc, bracket, monkeypatch):
     check(R, orc, W.config(4, 3, B=12), f"c4 B=12 bracket {bracket}")
     check(R, orc, W.with_transform(W.config(1, 6, B=6, V=20000), temperature=0.6, top_k=0),
           f"T=0.6 bracket {bracket}")
+
+
+@pytest.mark.parametrize("bracket", ["", "0", "0.3"])
+def test_split_draw_matches_one_workgroup(R, orc, monkeypatch, bracket):
+    """The all-rows route's draw split over several workgroups per batch row against the
+    oracle and against one workgroup per row (SPEC_VERIFY_DENSE_SPLIT=0): untransformed and
+    transformed drafts, a zero residual over several chunks, error rows, and brackets that
+    force the exact path (0) or overflow the undecided lists (0.3)."""
+    monkeypatch.setenv("SPEC_VERIFY_DENSE_PATH", "rows")
+    if bracket:
+        monkeypatch.setenv("SPEC_VERIFY_DENSE_BRACKET", bracket)
+    V, K, B = 20000, 3, 16
+    rng = np.random.default_rng(11)
+    z = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    p = np.exp(z - z.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    q = (1.5 * p[:, :K]).astype(np.float32)          # a rejection leaves a zero residual
+    x = np.stack([[rng.choice(V, p=p[b, k]) for k in range(K)] for b in range(B)]).astype(np.int32)
+    u = rng.random((B, K + 1), dtype=np.float32)
+    zero_res = W.ChainInputs(B, K, V, W.DTYPE_F32, 1.0, 0, z, q, x, u, np.zeros(B))
+    c1 = W.config(1, 12)
+    bad = W.make_chain(8, 3, 24000, dtype=W.DTYPE_BF16, temperature=1.0, top_k=0, sigma=W.sigma_const(0.5),
+                       config_id=95, seed=1)
+    zb, qb = bad.logits.copy(), bad.draft_probs.copy()
+    zb[1, 0, 17] = 0x7FC0                            # NaN in row 0
+    zb[2, 0, :] = 0xFF80                             # a row of -inf
+    qb[3, :, 5] = -1.0                               # a negative draft value in every draft row
+    bad = dataclasses.replace(bad, logits=zb, draft_probs=qb)
+    cases = [(c1, "c1"), (W.with_transform(c1, temperature=0.8, top_k=0), "c1 T=0.8"), (zero_res, "zero residual"),
+             (bad, "error rows"), (W.with_transform(bad, temperature=0.6, top_k=0), "error rows T=0.6")]
+    for ci, name in cases:
+        monkeypatch.delenv("SPEC_VERIFY_DENSE_SPLIT", raising=False)
+        _, tok_s, alen_s = check(R, orc, ci, f"{name} split bracket={bracket or 'default'}")
+        monkeypatch.setenv("SPEC_VERIFY_DENSE_SPLIT", "0")
+        _, tok_1, alen_1 = check(R, orc, ci, f"{name} one workgroup bracket={bracket or 'default'}")
+        assert np.array_equal(alen_s, alen_1) and np.array_equal(tok_s, tok_1), name
 
 
 @pytest.mark.parametrize("V,T", [(600000, 1.0), (600000, 0.8), (524288, 1.0)])
