@@ -254,11 +254,23 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
     return t;
 }
 
-// Draft weight w_i: q_i, or q_i^(1/T) when the draft is transformed (0 stays 0).
+// Draft weight w_i: q_i, or q_i^(1/T) when the draft is transformed (0 stays 0), by
+// the table-driven fp64 power (Tang's logarithm and exponential, within 3e-15 of the
+// exact power wherever the weight exceeds 1e-6 of the largest): every weight of a row,
+// in the pass and in the rescan, comes from this one function.
+// The power's logarithm table lives outside RowSmem, at namespace scope, so that
+// only the kernels of transformed drafts (the ones that read it) are given its LDS.
+__shared__ LogEntry dense_log_tab[kLogTab];
+struct PowCtx {
+    PowArg pa;
+    const LogEntry* lt;
+    const double* tbl;
+    ExpConsts ek;
+};
 template <bool TR>
-__device__ __forceinline__ double draft_w(float q, double invT) {
+__device__ __forceinline__ double draft_w(float q, const PowCtx& pw) {
     if (!TR) return static_cast<double>(q);
-    return q > 0.f ? pow(static_cast<double>(q), invT) : 0.0;
+    return q > 0.f ? pow_q(q, pw.pa, pw.lt, pw.tbl, pw.ek) : 0.0;
 }
 
 // True when Z lies strictly inside Zapprox(1 -+ delta), with room for rounding.
@@ -297,8 +309,8 @@ __host__ __device__ inline int dense_slots(int C) { return C <= 128 ? kRowSlots 
 inline size_t dense_dyn_lds(int C, bool tab) {
     return (tab ? kTabBytes : 0) + static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float));
 }
-// The exponential table is used when two workgroups still fit a CU's 160 KiB of
-// LDS (bf16 rows of up to 48 chunks).
+// The exponential table is used for bf16 rows of up to 48 chunks: two workgroups
+// share a CU's 160 KiB of LDS up to 47 chunks, one at 48.
 constexpr int kTabMaxChunks = 48;
 
 struct RowSmem {
@@ -326,6 +338,7 @@ __device__ __forceinline__ void exact_chunk_sums(const ChainArgs& a, const char*
                                               const double* tbl, ExpConsts ek, bool resid, double invZp,
                                               double invZq, RowSmem& sm) {
     const int tid = threadIdx.x, V = a.V;
+    const PowCtx pw{pow_arg(a.invT, ek), dense_log_tab, tbl, ek};
 #pragma unroll 1
     for (int c = 0; c < C; ++c) {
         double sc = 0.0;
@@ -339,7 +352,7 @@ __device__ __forceinline__ void exact_chunk_sums(const ChainArgs& a, const char*
             for (int e = 0; e < 8; ++e) {
                 const double ex = exp_of(z[e], g, tbl, ek);
                 if (resid) {
-                    const double rr = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
+                    const double rr = ex * invZp - draft_w<TR>(q[e], pw) * invZq;
                     sc += rr > 0.0 ? rr : 0.0;
                 } else {
                     sc += ex;
@@ -365,6 +378,7 @@ __device__ __forceinline__ void draw_emit(const ChainArgs& a, int b, int j, cons
     const long rbase = static_cast<long>(b) * (K + 1);
     float* diag = a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * K + 2) : nullptr;
     const double target = static_cast<double>(a.u[rbase + K]) * W;
+    const PowCtx pw{pow_arg(a.invT, ek), dense_log_tab, tbl, ek};
     if (tid == 0) {
         double before = 0.0;
         int chunk = -1, last = 0;
@@ -392,7 +406,7 @@ __device__ __forceinline__ void draw_emit(const ChainArgs& a, int b, int j, cons
             const double ex = exp_of(z[e], g, tbl, ek);
             double w = ex;
             if (residual) {
-                w = ex * invZp - draft_w<TR>(q[e], a.invT) * invZq;
+                w = ex * invZp - draft_w<TR>(q[e], pw) * invZq;
                 w = w > 0.0 ? w : 0.0;
             }
             wt[e] = (i0 + e < V) ? w : 0.0;
@@ -525,6 +539,7 @@ __device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, 
     const float* qr = d.qr;
     const ExpArg g = d.g;
     const double iz = d.iz, iq = d.iq, tol2 = d.tol2;
+    const PowCtx pw{pow_arg(a.invT, ek), dense_log_tab, tbl, ek};
     auto body = [&](auto res_tag) {
         constexpr bool RES = decltype(res_tag)::value;
         using Buf = Raw8<DT>[kSub];
@@ -562,7 +577,7 @@ __device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, 
                     }
                     if (RES) {
                         const float qv = TR ? rb[s].qf_at(e) : rb[s].qf(e);
-                        const double w = draft_w<TR>(qv, a.invT);
+                        const double w = draft_w<TR>(qv, pw);
                         if (TR) sq_tot += w;
                         const double wq = TR ? w * iq : w;
                         const double dd = fma(ex, iz, -wq);
@@ -609,7 +624,7 @@ __device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, 
                         const int i = c * kDenseChunk + ((k >> 3) * kThreads + tid) * 8 + (k & 7);
                         if (i >= V) break;
                         const double ex = exp_of(Elem<DT>::scalar(zr, i), g, tbl, ek);
-                        const double w = draft_w<TR>(qr[i], a.invT);
+                        const double w = draft_w<TR>(qr[i], pw);
                         const double wq = TR ? w * iq : w;
                         const double dd = fma(ex, iz, -wq);
                         if (fabs(dd) <= tol2 * wq) {
@@ -814,8 +829,10 @@ __device__ __forceinline__ void final_draw(const ChainArgs& a, int b, double bra
     draw_finish<DT, VEC, TR>(a, b, d, bracket, ek, sm, pr, pp, m_j, se_tot, sq_tot, zmax, zbad);
 }
 
+template <bool TR = false>
 __device__ __forceinline__ void init_draw_smem(RowSmem& sm) {
     for (int t = threadIdx.x; t < kTableSize; t += kThreads) sm.tbl[t] = exp2(static_cast<double>(t) * (1.0 / kTableSize));
+    if (TR) build_log_table(dense_log_tab);
     if (threadIdx.x == 0) { sm.n_list = 0; sm.qbad = 0; sm.zbad = 0; }
 }
 
@@ -833,7 +850,7 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void dense_row_ke
         first_reject<TR>(a, b, a.out_diag ? a.out_diag + static_cast<long>(b) * (2 * a.K + 2) : nullptr, j, err);
         if (threadIdx.x == 0) { sm.j = j; sm.err = err; }
     }
-    init_draw_smem(sm);
+    init_draw_smem<TR>(sm);
     __syncthreads();
     const long zrow = static_cast<long>(b) * (a.K + 1) + sm.j;
     final_draw<DT, VEC, TR, TAB>(a, b, bracket, ek, sm, dyn_lds, a.st.m[zrow], a.st.Z[zrow]);
@@ -870,7 +887,7 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void draw_part_ke
         first_reject<TR>(a, b, nullptr, j, err);
         if (tid == 0) { sm.j = j; sm.err = err; }
     }
-    init_draw_smem(sm);
+    init_draw_smem<TR>(sm);
     __syncthreads();
     if (sm.err) return;                              // the finish writes the error row
     const long zrow = static_cast<long>(b) * (a.K + 1) + sm.j;
@@ -923,7 +940,7 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void draw_combine
         first_reject<TR>(a, b, diag, j, err);
         if (tid == 0) { sm.j = j; sm.err = err; }
     }
-    init_draw_smem(sm);
+    init_draw_smem<TR>(sm);
     __syncthreads();
     if (sm.err) {
         const long rbase = static_cast<long>(b) * (K + 1);

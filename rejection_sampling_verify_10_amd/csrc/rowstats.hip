@@ -219,21 +219,62 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowStatsArgs a) {
 }
 
 // sum_i q_i^(1/T) of a draft-probability row, plus validity (E3, E4).
+// Sum of q^(1/T) (fp32 terms, 64-term fp32 groups added in fp64) and the E3 check
+// of one draft row.  VEC: the row is read as 16-byte vectors, two tiles of four
+// per thread in flight (the next tile loaded while this one is summed).
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void power_sums_kernel(PowerSumArgs a) {
     __shared__ double s_z[kThreads / kWave];
     __shared__ uint32_t s_f[kThreads / kWave];
     const float* row = a.q + static_cast<long>(blockIdx.x) * a.V;
     double acc = 0.0;
-    float part = 0.f;
     uint32_t bad = 0;
-    int n = 0;
-    for (int i = threadIdx.x; i < a.V; i += kThreads) {
-        const float v = row[i];
+    auto term = [&](float v) -> float {
         bad |= !(v >= 0.f && v < INFINITY);
-        part += (v > 0.f) ? __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(v) * a.invT) : 0.f;
-        if (++n == 64) { acc += part; part = 0.f; n = 0; }
+        return (v > 0.f) ? __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(v) * a.invT) : 0.f;
+    };
+    if constexpr (VEC) {
+        const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+        const int nvec = a.V / 4;
+        constexpr int kTileV = kThreads * kUnroll;
+        // vectors past the row load the row's last vector and count as zero
+        auto load = [&](int base, u32x4 (&v)[kUnroll]) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = base + u * kThreads + static_cast<int>(threadIdx.x);
+                v[u] = load_stream(rv + (i < nvec ? i : nvec - 1));
+            }
+        };
+        auto sum = [&](int base, const u32x4 (&v)[kUnroll]) {
+            float part = 0.f;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const bool in = base + u * kThreads + static_cast<int>(threadIdx.x) < nvec;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) part += in ? term(__uint_as_float(v[u][e])) : 0.f;
+            }
+            acc += part;
+        };
+        u32x4 va[kUnroll], vb[kUnroll];
+        load(0, va);
+#pragma unroll 1
+        for (int base = 0; base < nvec; base += 2 * kTileV) {
+            load(base + kTileV, vb);
+            __builtin_amdgcn_sched_barrier(0);
+            sum(base, va);
+            load(base + 2 * kTileV, va);
+            __builtin_amdgcn_sched_barrier(0);
+            if (base + kTileV < nvec) sum(base + kTileV, vb);
+        }
+    } else {
+        float part = 0.f;
+        int n = 0;
+        for (int i = threadIdx.x; i < a.V; i += kThreads) {
+            part += term(row[i]);
+            if (++n == 64) { acc += part; part = 0.f; n = 0; }
+        }
+        acc += part;
     }
-    acc += part;
     acc = wave_sum(acc);
     bad = wave_or(bad);
     const int lane = threadIdx.x & (kWave - 1), wid = wave_id();
@@ -320,7 +361,8 @@ hipError_t launch_rowstats(const RowStatsArgs& a, hipStream_t s, Timing t) {
 }
 
 hipError_t launch_power_sums(const PowerSumArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(power_sums_kernel, dim3(a.R), dim3(kThreads), 0, s, a);
+    if (vec_ok(a.q, a.V, 4)) hipLaunchKernelGGL(power_sums_kernel<true>, dim3(a.R), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(power_sums_kernel<false>, dim3(a.R), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
