@@ -2,10 +2,11 @@
 """Throughput of the speculative-decoding verification step on one MI355X.
 
 A step is one call of the workload's entry point over one batch of synthetic
-inputs that already sit in HBM: spec_verify_chain (workloads 0, 1, 2, 4),
-spec_verify_tree_greedy (3), spec_verify_tree_sample (5), one EAGLE-2
-expansion layer, spec_tree_expand (6), spec_kv_commit (7), or spec_accept_rate
-on the inputs of workload 4 (8).  The default
+inputs that already sit in HBM: spec_verify_chain (workloads 0, 1, 2, 4, and 10
+with the nucleus on whole rows), spec_verify_tree_greedy (3),
+spec_verify_tree_sample (5), one EAGLE-2 expansion layer, spec_tree_expand (6),
+spec_kv_commit (7), spec_accept_rate on the inputs of workload 4 (8), or
+spec_verify_chain_fused, the LM head with the verification in its epilogue (9).  The default
 workload is the chain verification with B=64, K=7, V=128256 (bf16 target
 logits, fp32 draft probabilities, temperature 0.7, top-k 50 on both
 distributions).  Several copies of the inputs are rotated so that the working
@@ -22,7 +23,10 @@ step timing); the hardware-counter traffic recorded under profiles/ when it
 matches the current kernel source; and the CPU oracle's throughput on the host
 cores.
 
-    python bench.py [--gpus 1] [--steps 400] [--warmup 40] [--workload 0..8]
+    python bench.py [--gpus 1] [--steps 400] [--warmup 40] [--workload 0..10] [--no-c4]
+
+The default line (workload 2) also carries, under "c4", the step time, rows/s and
+walk-kernel roofline of workload 4, measured in a child process.
 """
 
 from __future__ import annotations
@@ -289,6 +293,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-c4", action="store_true",
+                    help="skip the B=512 K=8 chain (workload 4) that the default line carries under \"c4\"")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time the library's plain copy kernel on 512 MiB instead (counter calibration)")
     args = ap.parse_args()
@@ -592,8 +598,31 @@ def main() -> int:
         line["roofline"]["all_rows_bytes"] = all_rows
         line["roofline"]["all_rows_equivalent_frac"] = all_rows / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS
     line.update(extra)
+    if args.workload == 2 and not args.no_c4:
+        line["c4"] = c4_line(args)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def c4_line(args) -> dict | None:
+    """Workload 4 (the dense chain B=512 K=8 V=128256, T=1) in a child process with the
+    same steps and warmup: its step time, rows/s and the walk kernel's roofline, so the
+    default line carries the large dense batch beside the headline top-k chain."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", "4", "--no-cpu-baseline",
+           "--steps", str(args.steps), "--warmup", str(args.warmup), "--seed", str(args.seed)]
+    log("workload 4 in a child process for the c4 keys")
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
+    if r.returncode != 0:
+        log(f"workload 4 failed with status {r.returncode}")
+        return None
+    c4 = json.loads(r.stdout.strip().splitlines()[-1])
+    keep = ("workload", "B", "K", "V", "temperature", "top_k")
+    return {"workload": {k: c4["config"][k] for k in keep}, "value": c4["value"], "unit": c4["unit"],
+            "ms_per_step": c4["ms_per_step"], "emitted_tokens_per_s": c4["emitted_tokens_per_s"],
+            "roofline": {k: c4["roofline"][k] for k in
+                         ("bound", "kernel", "achieved", "peak", "unit", "frac", "traffic", "kernel_us",
+                          "algorithmic_bytes", "all_rows_bytes", "all_rows_equivalent_frac")}}
 
 
 if __name__ == "__main__":

@@ -229,11 +229,15 @@ ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top
 }
 
 // The all-rows route's draw split over several workgroups per batch row (rows of
-// the split's partial sums carved from `split`), unless the environment variable
-// SPEC_VERIFY_DENSE_SPLIT is 0, which keeps one workgroup per batch row.
+// the split's partial sums carved from `split`).  The environment variable
+// SPEC_VERIFY_DENSE_SPLIT overrides the slice count: 0 keeps one workgroup per batch
+// row, N >= 2 asks for N slices at any batch size (clamped to the row's chunks and
+// to 16).
 void plan_dense_split(ChainArgs& ca, unsigned char* split, int B, int V) {
     const char* env = getenv("SPEC_VERIFY_DENSE_SPLIT");
-    const int S = (env && !strcmp(env, "0")) ? 1 : dense_split_slices(B, V, ca.transformed != 0);
+    const int forced = env ? atoi(env) : 0;
+    const int S = (env && forced == 0 && !strcmp(env, "0")) ? 1
+                                                            : dense_split_slices(B, V, ca.transformed != 0, forced);
     if (S > 1) dense_split_plan(ca, split, B, V, S);
 }
 

@@ -1319,13 +1319,14 @@ void dense_split_plan(ChainArgs& a, unsigned char* base, int B, int V, int S) {
 }
 // Enough slices to put about two workgroups on every CU, at least one chunk each.
 // Measured (K = 8, V = 128256; µs per call, split / one workgroup per row): T = 1:
-// B = 32 48.0 / 60.2, B = 64 62.8 / 72.7, B = 96 84.7 / 86.0, B = 128 99.4 / 97.8;
-// transformed (T = 0.7): B = 64 369 / 546, B = 128 489 / 604, B = 256 721 / 706.
+// B = 32 48.0 / 60.2, B = 64 62.8 / 72.7, B = 96 84.0 / 83.0, B = 128 96-99 / 96-98;
+// transformed (T = 0.7): B = 64 (K = 7) 118.8 / 178.6, B = 128 219.3 / 259.9,
+// B = 192 322 (S = 2) to 315 (S = 8) / 328, B = 256 397-420 / 398.
 // Larger batches keep one workgroup per row (their draws already fill the GPU).
-int dense_split_slices(int B, int V, bool transformed) {
-    if (B > (transformed ? 160 : 64)) return 1;
+int dense_split_slices(int B, int V, bool transformed, int forced) {
+    if (forced <= 0 && B > (transformed ? 160 : 64)) return 1;
     const int C = split_chunks(V);
-    int S = (512 + B - 1) / B;
+    int S = forced > 0 ? forced : (512 + B - 1) / B;
     if (S > C) S = C;
     if (S > kSplitMax) S = kSplitMax;
     return S < 1 ? 1 : S;

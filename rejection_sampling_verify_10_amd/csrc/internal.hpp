@@ -290,10 +290,11 @@ hipError_t launch_alpha_topk(const AlphaArgs& a, hipStream_t s);
 hipError_t launch_chain_dense(const ChainArgs& a, double bracket, hipStream_t s, Timing t = {});   // statistics precomputed
 // The dense draw split over several workgroups per batch row: at most kSplitMax slices
 // of a row; the workspace bytes of the split for B batch rows of V, and the slice count
-// the launch uses (1: no split).
+// the launch uses (1: no split; forced > 0 asks for that many, clamped to the row's
+// chunks and kSplitMax).
 constexpr int kSplitMax = 16;
 size_t dense_split_bytes(int B, int V);
-int dense_split_slices(int B, int V, bool transformed);
+int dense_split_slices(int B, int V, bool transformed, int forced = 0);
 // Points a's split fields into `base` (dense_split_bytes(B, V) bytes) for S slices.
 void dense_split_plan(ChainArgs& a, unsigned char* base, int B, int V, int S);
 // T == 1 without top-k: the whole chain (row statistics of the rows the walk
