@@ -313,6 +313,31 @@ def test_split_draw_matches_one_workgroup(R, orc, monkeypatch, bracket):
         assert np.array_equal(alen_s, alen_1) and np.array_equal(tok_s, tok_1), name
 
 
+@pytest.mark.parametrize("S", ["2", "7", "16"])
+def test_forced_split_counts(R, orc, monkeypatch, S):
+    """SPEC_VERIFY_DENSE_SPLIT=N forces N slices at any batch size (clamped to the row's
+    chunks and 16): a batch above the default split limit, a row of fewer chunks than
+    slices, rows of more than 128 chunks, transformed drafts; every case against the
+    oracle and against one workgroup per row."""
+    monkeypatch.setenv("SPEC_VERIFY_DENSE_PATH", "rows")
+    cases = [
+        (W.make_chain(96, 2, 128256, dtype=W.DTYPE_BF16, temperature=1.0, top_k=0, sigma=W.sigma_const(0.5),
+                      config_id=91, seed=3), "B=96 T=1"),
+        (W.make_chain(96, 2, 50000, dtype=W.DTYPE_BF16, temperature=0.7, top_k=0, sigma=W.sigma_const(0.5),
+                      config_id=91, seed=4), "B=96 T=0.7"),
+        (W.make_chain(5, 3, 9000, dtype=W.DTYPE_F32, temperature=1.3, top_k=0, sigma=W.sigma_const(0.8),
+                      config_id=91, seed=5), "V=9000 (3 chunks) fp32 T=1.3"),
+        (W.make_chain(2, 2, 600000, dtype=W.DTYPE_BF16, temperature=0.9, top_k=0, sigma=W.sigma_const(0.6),
+                      config_id=91, seed=6), "V=600000 T=0.9"),
+    ]
+    for ci, name in cases:
+        monkeypatch.setenv("SPEC_VERIFY_DENSE_SPLIT", S)
+        _, tok_s, alen_s = check(R, orc, ci, f"{name} S={S}")
+        monkeypatch.setenv("SPEC_VERIFY_DENSE_SPLIT", "0")
+        _, tok_1, alen_1 = check(R, orc, ci, f"{name} one workgroup")
+        assert np.array_equal(alen_s, alen_1) and np.array_equal(tok_s, tok_1), name
+
+
 @pytest.mark.parametrize("V,T", [(600000, 1.0), (600000, 0.8), (524288, 1.0)])
 def test_dense_long_rows(R, orc, V, T):
     """Rows of more than 128 dense chunks (wave-level chunk partials) and exactly 128."""
