@@ -45,10 +45,13 @@ def same(a, b):
     return all(np.array_equal(x.cpu().numpy(), y.cpu().numpy(), equal_nan=True) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("T,top_k,B,cid", [(0.7, 50, 16, 2), (1.0, 0, 512, 4), (0.0, 0, 16, 2)])
+@pytest.mark.parametrize("T,top_k,B,cid", [(0.7, 50, 16, 2), (1.0, 0, 512, 4), (0.0, 0, 16, 2), (1.0, 0, 8, 1),
+                                           (0.8, 0, 8, 1)])
 def test_chain_graph_replays(R, T, top_k, B, cid):
     """spec_verify_chain on a workspace zeroed once: top-k chain (tags reused by every
-    replay), the dense walk (T = 1, B*(K+1) > 1536) and greedy."""
+    replay), the dense walk (T = 1, B*(K+1) > 1536), greedy, and the all-rows route with
+    its draw split over several workgroups per row (c1's shape, T = 1 and a transformed
+    draft: statistics, power sums, draw slices and their combine in one graph)."""
     import torch
     dev = torch.device("cuda")
     ci = W.with_transform(W.config(cid, 80, B=B), temperature=T, top_k=top_k)
