@@ -194,6 +194,35 @@ def test_error_rows(R, orc, monkeypatch):
             assert alen[7] == 0 and alen[8] == 0
 
 
+@pytest.mark.parametrize("dtype", [1, 0])
+def test_walk_rows_far_above_their_first_tile(R, orc, monkeypatch, dtype):
+    """The walk sums each thread's part of a row against the largest value of the
+    thread's first tile of that row.  A logit far above it later in the row (the fp32
+    sum overflows), huge logits, a +inf late in a row and first tiles that hold only
+    -inf make it take the other branches (the row summed again against a running
+    maximum; the reference 0): both dense routes against the oracle."""
+    V = 40000 if dtype == W.DTYPE_BF16 else 20000         # several tiles of the walk
+    ci = W.make_chain(7, 3, V, dtype=dtype, temperature=1.0, top_k=0, sigma=W.sigma_const(0.5),
+                      config_id=93, seed=dtype)
+    zf = W.bf16_bits_to_f32(ci.logits) if dtype == W.DTYPE_BF16 else ci.logits.copy()
+    q = ci.draft_probs.copy()
+    x = ci.draft_tokens.copy()
+    zf[0, 0, V - 7] = 150.0                  # late, 150 above the first tiles: overflow
+    zf[1, 0, V - 3] = np.inf                 # +inf late in row 0: E1
+    zf[2, :2] *= 1.0e6                       # huge logits (a reference beyond 2^24)
+    zf[3, 1, V - 5] = 200.0                  # overflow in row 1, reached after accepting x_0
+    x[3, 0] = int(np.argmax(zf[3, 0]))
+    q[3, 0] = 1.0 / V
+    zf[4, 0, : V // 2] = -np.inf             # first tiles of -inf, finite values after
+    zf[5, 0, V - 1] = 90.0                   # just below the overflow
+    z = W.f32_to_bf16_bits(zf) if dtype == W.DTYPE_BF16 else zf.astype(np.float32)
+    ci = dataclasses.replace(ci, logits=z, draft_probs=q, draft_tokens=x)
+    for path in ["walk", "rows"]:
+        monkeypatch.setenv("SPEC_VERIFY_DENSE_PATH", path)
+        t, tok, alen = check(R, orc, ci, f"late large logits dtype={dtype} {path}")
+        assert alen[1] == -1 and alen[0] >= 0 and alen[2] >= 0 and alen[3] >= 1
+
+
 def test_zero_residual_falls_back_to_target(R, orc):
     """q = 1.5 p' everywhere: a rejection leaves max(0, p' - q) = 0, so the draw uses p'."""
     V, K, B = 512, 2, 64
