@@ -85,6 +85,29 @@ def test_workload4_full(R, orc):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("T", [0.7, 1.0])
+def test_benchmark_shape_without_topk(R, orc, T):
+    """The benchmark's shape (B=64, K=7, V=128256) with top-k off: the all-rows route with
+    each row's draw split over 8 workgroups, T = 0.7 (transformed draft: power sums and
+    the table-driven power) and T = 1; every batch row against the oracle."""
+    check(R, orc, W.with_transform(W.config(2, 7), temperature=T, top_k=0), f"c2 shape T={T} no top-k")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", [0.7, 1.3])
+def test_workload4_full_transformed(R, orc, T):
+    """B=512, K=8, V=128256 with a transformed draft (T != 1, top-k off): every row's
+    statistics, every draft row's power sum, one draw workgroup per batch row (the
+    batch is above the split limit); 64 batch rows spread over the batch against the
+    oracle."""
+    ci = W.with_transform(W.config(4, 6), temperature=T, top_k=0)
+    rows = list(range(0, 512, 8))
+    t, _, alen = check(R, orc, ci, f"c4 full T={T}", rows=rows)
+    hist = np.bincount(alen[alen >= 0], minlength=9)
+    print(f"[c4 T={T}] accept_len histogram {hist.tolist()}", flush=True)
+
+
+@pytest.mark.slow
 def test_greedy_chain_at_v128256(R, orc):
     """Greedy (temperature 0) chains at the benchmark vocabulary, V=128256 bf16."""
     check(R, orc, W.with_transform(W.config(2, 0, B=8), temperature=0.0, top_k=0), "greedy V=128256")
