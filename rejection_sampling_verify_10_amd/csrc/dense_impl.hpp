@@ -564,9 +564,9 @@ __device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, 
                 }
                 double ext[8];
                 if constexpr (TAB) exp8_table(rb[s], etab, g, tbl, ek, ext);
-                // (the transformed draft's loop is not unrolled, to keep one copy of the
-                // power function: its element index is a run-time value, read through
-                // selects rather than by indexing the registers)
+                // (the transformed draft's loop is unrolled only by two, to keep two
+                // copies of the power function: its element index is a run-time value,
+                // read through selects rather than by indexing the registers)
                 auto one = [&](int e) {
                     const float zf = TR ? rb[s].zf_at(e) : rb[s].zf(e);
                     const double ex = TAB ? ext[e] : exp_of(zf, g, tbl, ek);
@@ -587,8 +587,12 @@ __device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, 
                     }
                 };
                 if (TR) {
+                    // two elements per turn: two independent fp64 chains in flight
 #pragma unroll 1
-                    for (int e = 0; e < 8; ++e) one(e);
+                    for (int e = 0; e < 8; e += 2) {
+                        one(e);
+                        one(e + 1);
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) one(e);
