@@ -310,7 +310,8 @@ inline size_t dense_dyn_lds(int C, bool tab) {
     return (tab ? kTabBytes : 0) + static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float));
 }
 // The exponential table is used for bf16 rows of up to 48 chunks: two workgroups
-// share a CU's 160 KiB of LDS up to 47 chunks, one at 48.
+// share a CU's 160 KiB of LDS up to 47 chunks (42 with a transformed draft, whose
+// kernels also hold the power's logarithm table), one beyond.
 constexpr int kTabMaxChunks = 48;
 
 struct RowSmem {
@@ -564,9 +565,10 @@ __device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, 
                 }
                 double ext[8];
                 if constexpr (TAB) exp8_table(rb[s], etab, g, tbl, ek, ext);
-                // (the transformed draft's loop is unrolled only by two, to keep two
-                // copies of the power function: its element index is a run-time value,
-                // read through selects rather than by indexing the registers)
+                // (without the table the transformed draft's loop is unrolled only by
+                // two, to keep two copies of the power function: its element index is a
+                // run-time value, read through selects rather than by indexing the
+                // registers; with the table it is unrolled whole, as ext[] must be)
                 auto one = [&](int e) {
                     const float zf = TR ? rb[s].zf_at(e) : rb[s].zf(e);
                     const double ex = TAB ? ext[e] : exp_of(zf, g, tbl, ek);
@@ -586,7 +588,7 @@ __device__ __forceinline__ void draw_pass(const ChainArgs& a, const DrawCtx& d, 
                         und |= fabs(dd) <= tol2 * wq;
                     }
                 };
-                if (TR) {
+                if (TR && !TAB) {
                     // two elements per turn: two independent fp64 chains in flight
 #pragma unroll 1
                     for (int e = 0; e < 8; e += 2) {
@@ -1258,7 +1260,7 @@ hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s, Timin
                      s, a, bracket, exp_consts());
         return hipGetLastError();
     }
-    if constexpr (DT == 1 && VEC && !TR) {
+    if constexpr (DT == 1 && VEC) {
         if (C <= kTabMaxChunks) {
             launch_timed(t, dense_row_kernel<DT, VEC, TR, true>, dim3(a.B), dim3(kThreads),
                          static_cast<unsigned>(dense_dyn_lds(C, true)), s, a, bracket, exp_consts());
