@@ -52,6 +52,9 @@
 #include "internal.hpp"
 #include "lists.hpp"
 
+#ifndef SV_SPLIT_TAB_CHUNKS
+#define SV_SPLIT_TAB_CHUNKS 3
+#endif
 #ifndef SV_DENSE_THREADS
 #error "define SV_DENSE_THREADS before including dense_impl.hpp"
 #endif
@@ -313,6 +316,8 @@ inline size_t dense_dyn_lds(int C, bool tab) {
 // share a CU's 160 KiB of LDS up to 47 chunks (42 with a transformed draft, whose
 // kernels also hold the power's logarithm table), one beyond.
 constexpr int kTabMaxChunks = 48;
+// A slice of the split draw builds the table when it has at least this many chunks.
+constexpr int kSplitTabChunks = SV_SPLIT_TAB_CHUNKS;
 
 struct RowSmem {
     float wq[kWave];                   // walk: q[x_k], lane k
@@ -881,10 +886,11 @@ struct SliceRec {
 };
 __host__ __device__ inline int split_chunks(int V) { return (V + kDenseChunk - 1) / kDenseChunk; }
 
-template <int DT, bool VEC, bool TR>
+template <int DT, bool VEC, bool TR, bool TAB>
 __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void draw_part_kernel(ChainArgs a, double bracket,
                                                                                      ExpConsts ek) {
     __shared__ RowSmem sm;
+    extern __shared__ double dyn_lds[];
     const int s = blockIdx.x, b = blockIdx.y, S = a.split_S;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = wave_id();
     if (tid < kWave) {
@@ -905,7 +911,13 @@ __global__ __launch_bounds__(kThreads, (min_waves<VEC, TR>())) void draw_part_ke
     double se = 0.0, sq = 0.0;
     float zmax = -INFINITY;
     bool zbad = false;
-    if (c0 < c1) draw_pass<DT, VEC, TR, false>(a, d, c0, c1, nullptr, sm.tbl, ek, pr, pp, sm, se, sq, zmax, zbad);
+    const double* etab = nullptr;
+    if constexpr (TAB) {
+        build_exp_table(dyn_lds, d.g, sm.tbl, ek);
+        __syncthreads();
+        etab = dyn_lds;
+    }
+    if (c0 < c1) draw_pass<DT, VEC, TR, TAB>(a, d, c0, c1, etab, sm.tbl, ek, pr, pp, sm, se, sq, zmax, zbad);
     se = block_sum(se, sm.red);
     if (TR) sq = block_sum(sq, sm.red);
     const float wz = wave_max(zmax);
@@ -1251,8 +1263,18 @@ template <int DT, bool VEC, bool TR>
 hipError_t dense_launch(const ChainArgs& a, double bracket, hipStream_t s, Timing t) {
     const int C = (a.V + kDenseChunk - 1) / kDenseChunk;
     if (a.split_S > 1) {
-        launch_timed(t, draw_part_kernel<DT, VEC, TR>, dim3(a.split_S, a.B), dim3(kThreads), 0u, s, a, bracket,
-                     exp_consts());
+        // bf16 slices of at least kSplitTabChunks chunks tabulate the exponentials first
+        bool tab = false;
+        if constexpr (DT == 1 && VEC) {
+            if ((C + a.split_S - 1) / a.split_S >= kSplitTabChunks) {
+                tab = true;
+                launch_timed(t, draw_part_kernel<DT, VEC, TR, true>, dim3(a.split_S, a.B), dim3(kThreads),
+                             static_cast<unsigned>(kTabBytes), s, a, bracket, exp_consts());
+            }
+        }
+        if (!tab)
+            launch_timed(t, draw_part_kernel<DT, VEC, TR, false>, dim3(a.split_S, a.B), dim3(kThreads), 0u, s, a,
+                         bracket, exp_consts());
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const size_t lds = static_cast<size_t>(C) * dense_slots(C) * (sizeof(double) + sizeof(float));
