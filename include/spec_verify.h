@@ -86,7 +86,7 @@
  *     draw on the every-row-first route (temperature > 0, top-k off): 0 keeps
  *     one per row, N >= 2 asks for N (at most 16 and the row's 4096-token
  *     chunks) at any batch size; unset, the library splits batches of up to
- *     64 rows (160 with a transformed draft).  Results are the same.
+ *     192 rows (160 with a transformed draft).  Results are the same.
  *     SPEC_VERIFY_SPIN_LIMIT (an integer in [0, 65536]) lowers the number of
  *     polls a top-k chain finisher, or a member of a sampled tree's cluster
  *     (spec_verify_tree_sample_ws), makes before it gives up (tests of the

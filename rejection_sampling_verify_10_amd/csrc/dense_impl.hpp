@@ -1345,16 +1345,18 @@ void dense_split_plan(ChainArgs& a, unsigned char* base, int B, int V, int S) {
     a.split_rec = take(static_cast<size_t>(B) * kSplitMax * sizeof(SliceRec));
     a.split_S = S;
 }
-// Enough slices to put about two workgroups on every CU, at least one chunk each.
+// Enough slices to put about two workgroups on every CU, at least one chunk each;
+// two per row for untransformed batches of 65 to 192 rows.
 // Measured (K = 8, V = 128256; µs per call, split / one workgroup per row): T = 1:
-// B = 32 48.0 / 60.2, B = 64 62.8 / 72.7, B = 96 84.0 / 83.0, B = 128 96-99 / 96-98;
+// B = 32 48.0 / 60.2, B = 64 62.8 / 72.7, B = 96 79.3 (S = 2) / 83.1,
+// B = 128 91.2 (S = 2) / 95.7;
 // transformed (T = 0.7): B = 64 (K = 7) 118.8 / 178.6, B = 128 219.3 / 259.9,
 // B = 192 322 (S = 2) to 315 (S = 8) / 328, B = 256 397-420 / 398.
 // Larger batches keep one workgroup per row (their draws already fill the GPU).
 int dense_split_slices(int B, int V, bool transformed, int forced) {
-    if (forced <= 0 && B > (transformed ? 160 : 64)) return 1;
+    if (forced <= 0 && B > (transformed ? 160 : 192)) return 1;
     const int C = split_chunks(V);
-    int S = forced > 0 ? forced : (512 + B - 1) / B;
+    int S = forced > 0 ? forced : (!transformed && B > 64) ? 2 : (512 + B - 1) / B;
     if (S > C) S = C;
     if (S > kSplitMax) S = kSplitMax;
     return S < 1 ? 1 : S;
