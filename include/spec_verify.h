@@ -80,7 +80,7 @@
  *     SPEC_VERIFY_DENSE_PATH = walk | rows picks the route of a chain with
  *     temperature 1 and top-k off: the walk (one workgroup per batch row reads
  *     target rows only up to the first rejection) or every row's statistics
- *     first; by default the walk when B*(K+1) > 1536 or V < 4096.  Results
+ *     first; by default the walk when B*(K+1) > 1344 or V < 4096.  Results
  *     are the same either way.
  *     SPEC_VERIFY_DENSE_SPLIT sets how many workgroups share each batch row's
  *     draw on the every-row-first route (temperature > 0, top-k off): 0 keeps

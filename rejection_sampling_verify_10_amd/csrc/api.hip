@@ -198,10 +198,11 @@ bool dense_walks(int B, int K, int V) {
     const char* env = getenv("SPEC_VERIFY_DENSE_PATH");
     if (env && !strcmp(env, "walk")) return true;
     if (env && !strcmp(env, "rows")) return false;
-    // Measured crossover (K = 8, V = 128256): the all-rows route is faster up to
-    // B = 128 (93 against 109 us), the walk from B = 256 (117 against 143 us).
-    // Short rows (V = 1000) favour the walk's single launch.
-    return static_cast<long>(B) * (K + 1) > 1536 || V < 4096;
+    // Measured crossover (K = 8, V = 128256, the all-rows draw split): the all-rows
+    // route is faster at B = 128 (90.7 against 107.0 us), the walk from B = 160
+    // (111.9 against 115.0 us; B = 256: 118.5 against 149.3).  Short rows (V = 1000)
+    // favour the walk's single launch.
+    return static_cast<long>(B) * (K + 1) > 1344 || V < 4096;
 }
 
 ChainPlan plan_chain(Carver& c, int B, int K, int V, int dtype, float T, int top_k) {

@@ -49,7 +49,7 @@ def same(a, b):
                                            (0.8, 0, 8, 1)])
 def test_chain_graph_replays(R, T, top_k, B, cid):
     """spec_verify_chain on a workspace zeroed once: top-k chain (tags reused by every
-    replay), the dense walk (T = 1, B*(K+1) > 1536), greedy, and the all-rows route with
+    replay), the dense walk (T = 1, B*(K+1) > 1344), greedy, and the all-rows route with
     its draw split over several workgroups per row (c1's shape, T = 1 and a transformed
     draft: statistics, power sums, draw slices and their combine in one graph)."""
     import torch
