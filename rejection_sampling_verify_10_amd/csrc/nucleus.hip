@@ -503,7 +503,7 @@ __device__ __forceinline__ void nucleus_row(const NucleusArgs& a, const ExpConst
                 if (p > 0.0) add(order_key(v), p);
             }
         } else if (l == 0) {
-            rv.template each_at_least<VEC, kBatchList>(vskip, [&](int i, float v) {
+            rv.template each_at_least<VEC, kBatchList>(vskip, [&](int, float v) {
                 const double p = rv.weight(v) * invN;
                 if (!(p > 0.0)) return;
                 add(order_key(v), p);
